@@ -1,0 +1,646 @@
+"""Plain CPU oracle of the TurboQuant / SpectralQuant codec (fp64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's
+``cpu_baseline`` leg use it.  It shares no code, tables or constants with the
+HIP library; the two meet only through the seeded input generators in
+``synth`` and through the record layout, which both implement from its
+written specification.
+
+What it computes, step by step, and where the pages define it:
+
+* Random rotation Pi (seeded Haar orthogonal, QR of a Gaussian matrix) and the
+  Gaussian sketch S -- TurboQuant paper review, "Method"; the launch kit names
+  the dense-QR rotation mode (OnlyTerp/turboquant LAUNCH.md, Show HN post).
+* Lloyd-Max scalar codebook for the post-rotation coordinate law (a Beta law,
+  about N(0, 1/d)) -- paper review, "Method" and the summary under the title.
+* TurboQuant-mse: store ||x||, rotate x/||x||, quantize every coordinate to the
+  nearest centroid -- paper review, "Method" and "Limitations" (norms stored
+  separately).
+* TurboQuant-prod: b-1 bits of mse codes, then a 1-bit QJL sketch sign(S r) of
+  the residual r with the unbiased estimator
+  ||r|| sqrt(pi/2)/m <S q', sign(S r)> -- paper review, "Method", "Key idea",
+  "Results" (exactly unbiased); the news article on the KV-cache debate calls
+  the residual stage a one-bit Johnson-Lindenstrauss transform.
+* SpectralQuant: eigenbasis of the calibrated key covariance as the rotation,
+  water-filled bits on the top dims, QJL signs on the 4 signal dims only --
+  SpectralQuant thread, tweets 4, 5 and 6.
+* Scoring, decode attention (softmax(q.k / sqrt(d)) . v over the compressed
+  cache) and top-k search -- paper review, "Background", "Validation" and the
+  "Sparks" list (rotation and codebook lookup fused into attention).
+
+Readings where the pages are silent (each also listed in the design doc):
+the generator of Pi and S (Philox4x32-10 + Box-Muller, below); fp16 norms;
+ties go to the upper cell; sign(0) = +1; the sketch acts on the rotated
+residual, so the query sketch is S (Pi q); the record layout of the library.
+
+The codec's parameters (Pi, S, centroids, boundaries) are stored in fp32 by
+the library, so the oracle evaluates with the fp32-rounded parameters in fp64
+arithmetic.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+from scipy import special
+
+# ---------------------------------------------------------------------------
+# Counter-based generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+# "Parallel random numbers: as easy as 1, 2, 3", SC'11).  Written here from
+# that published definition; the library carries its own implementation.
+# ---------------------------------------------------------------------------
+_MASK32 = np.uint64(0xFFFFFFFF)
+_PHILOX_M0 = np.uint64(0xD2511F53)
+_PHILOX_M1 = np.uint64(0xCD9E8D57)
+_PHILOX_W0 = np.uint64(0x9E3779B9)
+_PHILOX_W1 = np.uint64(0xBB67AE85)
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32 with 10 rounds.  counter: (..., 4) uint32, key: (2,) or (..., 2) uint32.
+
+    Returns (..., 4) uint32.
+    """
+    c = np.asarray(counter, dtype=np.uint64)
+    k = np.asarray(key, dtype=np.uint64)
+    c0, c1, c2, c3 = (c[..., i] for i in range(4))
+    k0, k1 = k[..., 0], k[..., 1]
+    for rnd in range(10):
+        if rnd:
+            k0 = (k0 + _PHILOX_W0) & _MASK32
+            k1 = (k1 + _PHILOX_W1) & _MASK32
+        p0 = _PHILOX_M0 * c0          # < 2^64: exact in uint64
+        p1 = _PHILOX_M1 * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+STREAM_ROTATION = 1
+STREAM_SKETCH = 2
+
+
+def philox_normals(seed: int, stream: int, count: int) -> np.ndarray:
+    """count standard normals from (seed, stream).
+
+    Block i uses counter (i mod 2^32, i div 2^32, stream, 0) and key
+    (seed mod 2^32, seed div 2^32).  Each block's four words (w0..w3) give four
+    normals by Box-Muller: with u(w) = (w + 1/2) / 2^32,
+    rho = sqrt(-2 ln u(w0)), theta = 2 pi u(w1): rho cos theta, rho sin theta,
+    and likewise from (w2, w3).
+    """
+    nblk = (count + 3) // 4
+    i = np.arange(nblk, dtype=np.uint64)
+    ctr = np.stack([i & _MASK32, i >> np.uint64(32),
+                    np.full(nblk, stream, np.uint64), np.zeros(nblk, np.uint64)], axis=-1)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    w = philox4x32_10(ctr, key).astype(np.float64)
+    u = (w + 0.5) * 2.0 ** -32
+    out = np.empty((nblk, 4))
+    for a, b in ((0, 1), (2, 3)):
+        rho = np.sqrt(-2.0 * np.log(u[:, a]))
+        th = 2.0 * math.pi * u[:, b]
+        out[:, a] = rho * np.cos(th)
+        out[:, b] = rho * np.sin(th)
+    return out.reshape(-1)[:count]
+
+
+def haar_rotation(d: int, seed: int) -> np.ndarray:
+    """Seeded Haar-distributed orthogonal d x d matrix (fp64).
+
+    G has i.i.d. N(0,1) entries (row-major from the rotation stream); with
+    G = QR, Pi = Q diag(sign(R_ii)) (Mezzadri's sign fix makes the law Haar).
+    The codec rotates with y = Pi u.
+    """
+    g = philox_normals(seed, STREAM_ROTATION, d * d).reshape(d, d)
+    q, r = np.linalg.qr(g)
+    return q * np.sign(np.diag(r))[None, :]
+
+
+def gaussian_sketch(m: int, seed: int) -> np.ndarray:
+    """Seeded m x m matrix with i.i.d. N(0, 1) entries (fp64), row-major from the sketch stream."""
+    return philox_normals(seed, STREAM_SKETCH, m * m).reshape(m, m)
+
+
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebooks.  The coordinate T of a uniformly random unit vector in
+# R^d has density f_d(t) = (1 - t^2)^((d-3)/2) / B(1/2, (d-1)/2) on [-1, 1],
+# i.e. (T+1)/2 ~ Beta((d-1)/2, (d-1)/2): the "known Beta distribution" of the
+# paper review's "Method", which tends to N(0, 1/d).  The cell moments are
+# written in closed form (regularised incomplete beta function).
+# ---------------------------------------------------------------------------
+def beta_cell_moments(a, b, d: int):
+    """Return (P, M1, M2) = integrals of (1, t, t^2) f_d(t) over [a, b]."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    al = (d - 1) / 2.0
+    sa, sb = (a + 1) / 2, (b + 1) / 2
+    p = special.betainc(al, al, sb) - special.betainc(al, al, sa)
+    # t (1-t^2)^k has antiderivative -(1-t^2)^(k+1) / (2(k+1)), k = (d-3)/2.
+    logb = special.betaln(0.5, al)
+
+    def anti(t):
+        with np.errstate(divide="ignore"):
+            v = -np.exp(al * np.log1p(-t * t) - logb) / (2 * al)
+        return np.where(np.abs(t) >= 1.0, 0.0, v)
+
+    m1 = anti(b) - anti(a)
+    # By parts: int t^2 f_d = [-t (1-t^2) f_d(t) / (d-1)] + (1/d) P_{d+2}, where
+    # P_{d+2} is the cell mass under the law at dimension d+2 (Beta(al+1, al+1)).
+    def edge(t):
+        with np.errstate(divide="ignore"):
+            v = t * np.exp(al * np.log1p(-t * t) - logb) / (d - 1)
+        return np.where(np.abs(t) >= 1.0, 0.0, v)
+
+    p2 = special.betainc(al + 1, al + 1, sb) - special.betainc(al + 1, al + 1, sa)
+    m2 = edge(a) - edge(b) + p2 / d
+    return p, m1, m2
+
+
+def gaussian_cell_moments(a, b):
+    """(P, M1, M2) of the standard normal over [a, b] (closed forms)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    phi = lambda t: np.where(np.isinf(t), 0.0, np.exp(-0.5 * np.where(np.isinf(t), 0.0, t) ** 2)
+                             / math.sqrt(2 * math.pi))
+    p = special.ndtr(b) - special.ndtr(a)
+    m1 = phi(a) - phi(b)
+    ta = np.where(np.isinf(a), 0.0, a)
+    tb = np.where(np.isinf(b), 0.0, b)
+    m2 = p + ta * phi(a) - tb * phi(b)
+    return p, m1, m2
+
+
+@dataclass
+class LloydMax:
+    centroids: np.ndarray      # fp64, ascending, length L
+    boundaries: np.ndarray     # fp64, length L-1 (midpoints)
+    mse: float                 # E[(T - Q(T))^2] per coordinate
+    iterations: int
+
+
+def lloyd_max(moments, lo: float, hi: float, levels: int, init: np.ndarray,
+              rtol: float = 1e-13, max_iter: int = 200000, patience: int = 500) -> LloydMax:
+    """Lloyd's iteration for a scalar law on [lo, hi]: boundaries at centroid
+    midpoints, centroids at the conditional mean of their cell ("continuous 1-D
+    k-means", paper review, "Method").  Stops when the largest centroid move is
+    below rtol * max|c|, or when the move has not reached a new minimum for
+    ``patience`` steps (the rounding floor of the moments, ~1e-14).  The result
+    is made exactly symmetric."""
+    c = np.array(init, dtype=np.float64)
+    it, best, best_it = 0, np.inf, 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[1:] + c[:-1])
+        edges = np.concatenate([[lo], t, [hi]])
+        p, m1, _ = moments(edges[:-1], edges[1:])
+        new = m1 / p
+        delta = np.max(np.abs(new - c))
+        c = new
+        if delta < best:
+            best, best_it = delta, it
+        if delta < rtol * np.max(np.abs(c)) or it - best_it > patience:
+            break
+    c = 0.5 * (c - c[::-1])                      # symmetric law -> symmetric codebook
+    t = 0.5 * (c[1:] + c[:-1])
+    if levels % 2 == 0:
+        t[levels // 2 - 1] = 0.0
+    edges = np.concatenate([[lo], t, [hi]])
+    p, m1, m2 = moments(edges[:-1], edges[1:])
+    mse = float(np.sum(m2 - 2 * c * m1 + c * c * p))
+    return LloydMax(c, t, mse, it)
+
+
+def beta_codebook(d: int, bits: int) -> LloydMax:
+    """Lloyd-Max codebook with 2^bits levels for the rotated-coordinate law at dimension d."""
+    levels = 1 << bits
+    sigma = 1.0 / math.sqrt(d)
+    q = special.ndtri((np.arange(levels) + 0.5) / levels) * sigma
+    init = np.clip(q, -0.999, 0.999)
+    return lloyd_max(lambda a, b: beta_cell_moments(a, b, d), -1.0, 1.0, levels, init)
+
+
+def gaussian_codebook(bits: int) -> LloydMax:
+    """Lloyd-Max codebook with 2^bits levels for N(0, 1)."""
+    levels = 1 << bits
+    init = special.ndtri((np.arange(levels) + 0.5) / levels)
+    return lloyd_max(gaussian_cell_moments, -np.inf, np.inf, levels, init)
+
+
+# ---------------------------------------------------------------------------
+# SpectralQuant calibration: eigenbasis of the centred key covariance, sorted
+# so that dim 0 carries the largest eigenvalue (SpectralQuant thread, tweet 4).
+# ---------------------------------------------------------------------------
+def eigenbasis(calib: np.ndarray):
+    """Rows of the returned matrix are eigenvectors of the centred sample
+    covariance (divisor n), eigenvalues descending; each row is flipped so that
+    its entry of largest magnitude (first such index) is positive."""
+    x = np.asarray(calib, dtype=np.float64)
+    xc = x - x.mean(axis=0, keepdims=True)
+    cov = xc.T @ xc / x.shape[0]
+    lam, vec = np.linalg.eigh(cov)
+    order = np.argsort(-lam, kind="stable")
+    lam, vec = lam[order], vec[:, order]
+    rows = vec.T.copy()
+    for i in range(rows.shape[0]):
+        j = int(np.argmax(np.abs(rows[i])))
+        if rows[i, j] < 0:
+            rows[i] = -rows[i]
+    return lam, rows
+
+
+# ---------------------------------------------------------------------------
+# Codebook objects
+# ---------------------------------------------------------------------------
+@dataclass
+class Codec:
+    d: int
+    mode: str                          # "mse" or "prod"
+    bits: np.ndarray                   # per-dim index bits, shape [d]
+    m: int                             # sketch dims (rotated dims 0..m-1); 0 for mse
+    layout: str                        # "row" or "col"
+    rot: np.ndarray                    # [H][d][d] fp32 values held in fp64
+    sketch: Optional[np.ndarray]       # [m][m] fp32 values held in fp64
+    centroids: List[List[np.ndarray]]  # [H][d] -> fp32 values held in fp64
+    boundaries: List[List[np.ndarray]] # [H][d]
+    uniform: bool = True
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def heads(self) -> int:
+        return self.rot.shape[0]
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def turboquant_codec(d: int, bits: int, mode: str, rot_seed: int, sketch_seed: int = 0,
+                     layout: str = "row") -> Codec:
+    """TurboQuant-mse (bits per coordinate) or TurboQuant-prod (bits-1 mse bits +
+    1 QJL bit, sketch over all d rotated dims); paper review, "Method"."""
+    mse_bits = bits - 1 if mode == "prod" else bits
+    if mse_bits < 1:
+        raise ValueError("prod needs bits >= 2 here (at least one mse bit)")
+    lm = beta_codebook(d, mse_bits)
+    rot = _f32(haar_rotation(d, rot_seed))[None]
+    m = d if mode == "prod" else 0
+    sk = _f32(gaussian_sketch(m, sketch_seed)) if mode == "prod" else None
+    c, t = _f32(lm.centroids), _f32(lm.boundaries)
+    return Codec(d, mode, np.full(d, mse_bits), m, layout, rot, sk,
+                 [[c] * d], [[t] * d], True, {"lloyd_max": lm})
+
+
+def spectralquant_codec(calib: np.ndarray, bitmap, m: int, sketch_seed: int,
+                        layout: str = "row") -> Codec:
+    """SpectralQuant keys: per-head eigenbasis rotation, water-filled bit map
+    (e.g. [5,3,2,2] on the top-4 dims, 1 bit elsewhere) and QJL on the first m
+    rotated dims (SpectralQuant thread, tweets 4, 5, 6).
+
+    Per-dim codebook: Gaussian Lloyd-Max with b_i bits scaled by sigma_i, the RMS
+    of the i-th rotated coordinate of the normalised calibration vectors.
+
+    calib: [H][n][d] calibration keys.
+    """
+    calib = np.asarray(calib, dtype=np.float64)
+    heads, _, d = calib.shape
+    bits = np.asarray(bitmap, dtype=np.int64)
+    books = {b: gaussian_codebook(int(b)) for b in set(bits.tolist())}
+    rots, cents, bnds, sig = [], [], [], []
+    for h in range(heads):
+        _, rows = eigenbasis(calib[h])
+        p = _f32(rows)
+        x = calib[h]
+        u = x / np.linalg.norm(x, axis=1, keepdims=True)
+        y = u @ p.T
+        sigma = np.sqrt(np.mean(y * y, axis=0))
+        rots.append(p)
+        sig.append(sigma)
+        cents.append([_f32(books[int(bits[i])].centroids * sigma[i]) for i in range(d)])
+        bnds.append([_f32(books[int(bits[i])].boundaries * sigma[i]) for i in range(d)])
+    sk = _f32(gaussian_sketch(m, sketch_seed))
+    return Codec(d, "prod", bits, m, layout, np.stack(rots), sk, cents, bnds, False,
+                 {"sigma": np.stack(sig)})
+
+
+# ---------------------------------------------------------------------------
+# Encode
+# ---------------------------------------------------------------------------
+@dataclass
+class Encoded:
+    idx: np.ndarray                 # [n][d] int
+    signs: Optional[np.ndarray]     # [n][m] bool (True = z >= 0)
+    nx: np.ndarray                  # [n] fp16
+    nr: Optional[np.ndarray]        # [n] fp16
+    y: np.ndarray                   # [n][d] rotated unit vectors (fp64), for band checks
+    z: Optional[np.ndarray]         # [n][m] sketch values (fp64)
+
+
+def quantize(codec: Codec, y: np.ndarray, head: int) -> np.ndarray:
+    """idx_i = number of boundaries t with t <= y_i (ties go to the upper cell)."""
+    n, d = y.shape
+    idx = np.empty((n, d), dtype=np.int64)
+    if codec.uniform:
+        idx[:] = np.searchsorted(codec.boundaries[head][0], y, side="right")
+    else:
+        for i in range(d):
+            idx[:, i] = np.searchsorted(codec.boundaries[head][i], y[:, i], side="right")
+    return idx
+
+
+def dequantize(codec: Codec, idx: np.ndarray, head: int) -> np.ndarray:
+    n, d = idx.shape
+    if codec.uniform:
+        return codec.centroids[head][0][idx]
+    out = np.empty((n, d))
+    for i in range(d):
+        out[:, i] = codec.centroids[head][i][idx[:, i]]
+    return out
+
+
+def encode(codec: Codec, x: np.ndarray, head: int = 0, round_norms: bool = True) -> Encoded:
+    """TurboQuant encode of the rows of x (paper review, "Method").
+
+    Norms are stored as fp16 (round to nearest even); round_norms=False keeps
+    them in fp64 for statistical checks of the estimator itself."""
+    x = np.asarray(x, dtype=np.float64)
+    nx = np.sqrt(np.sum(x * x, axis=1))
+    safe = np.where(nx > 0, nx, 1.0)
+    u = np.where(nx[:, None] > 0, x / safe[:, None], 0.0)
+    y = u @ codec.rot[head].T                     # y = Pi u
+    idx = quantize(codec, y, head)
+    store = (lambda v: v.astype(np.float16)) if round_norms else (lambda v: v)
+    if codec.mode == "mse":
+        return Encoded(idx, None, store(nx), None, y, None)
+    m = codec.m
+    chat = dequantize(codec, idx, head)
+    r = y[:, :m] - chat[:, :m]                   # residual of the mse stage
+    nr = np.sqrt(np.sum(r * r, axis=1))
+    z = r @ codec.sketch.T                       # S r
+    return Encoded(idx, z >= 0, store(nx), store(nr), y, z)
+
+
+def boundary_distance(codec: Codec, y: np.ndarray, head: int = 0) -> np.ndarray:
+    """min_t |y_i - t| over the decision boundaries of dim i."""
+    n, d = y.shape
+    out = np.full((n, d), np.inf)
+    for i in range(d):
+        t = codec.boundaries[head][0 if codec.uniform else i]
+        if len(t):
+            out[:, i] = np.min(np.abs(y[:, i:i + 1] - t[None, :]), axis=1)
+        if codec.uniform:
+            out[:] = np.min(np.abs(y[:, :, None] - t[None, None, :]), axis=2)
+            break
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Scoring (two independent paths) and decode attention
+# ---------------------------------------------------------------------------
+QJL_CONST = math.sqrt(math.pi / 2)
+
+
+def prepare_query(codec: Codec, q: np.ndarray, head: int = 0):
+    """q' = Pi q and (prod) q_s = S q'[0:m]."""
+    q = np.asarray(q, dtype=np.float64)
+    qr = q @ codec.rot[head].T
+    qs = qr[:, :codec.m] @ codec.sketch.T if codec.mode == "prod" else None
+    return qr, qs
+
+
+def score(codec: Codec, q: np.ndarray, enc: Encoded, head: int = 0) -> np.ndarray:
+    """s = n_x (sum_i q'_i c[idx_i] + n_r sqrt(pi/2)/m sum_j q_s,j (2 bit_j - 1)).
+
+    [nq][n] scores with the stored (fp16) norms."""
+    qr, qs = prepare_query(codec, q, head)
+    chat = dequantize(codec, enc.idx, head)
+    nx = enc.nx.astype(np.float64)
+    s = qr @ chat.T
+    if codec.mode == "prod":
+        pm = np.where(enc.signs, 1.0, -1.0)
+        s = s + (qs @ pm.T) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[None, :]
+    return s * nx[None, :]
+
+
+def reconstruct(codec: Codec, enc: Encoded, head: int = 0) -> np.ndarray:
+    """x_hat = n_x Pi^T (c[idx] + n_r sqrt(pi/2)/m [S^T sign ; 0])."""
+    chat = dequantize(codec, enc.idx, head)
+    if codec.mode == "prod":
+        pm = np.where(enc.signs, 1.0, -1.0)
+        corr = (pm @ codec.sketch) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[:, None]
+        chat = chat.copy()
+        chat[:, :codec.m] += corr
+    return (chat @ codec.rot[head]) * enc.nx.astype(np.float64)[:, None]
+
+
+def score_via_reconstruction(codec: Codec, q: np.ndarray, enc: Encoded, head: int = 0):
+    """Second scoring path: <q, x_hat>."""
+    return np.asarray(q, dtype=np.float64) @ reconstruct(codec, enc, head).T
+
+
+def decode_attention(kcodec: Codec, vcodec: Codec, q: np.ndarray, kenc: List[Encoded],
+                     venc: List[Encoded], scale: float, kv_heads_rot: bool = True) -> np.ndarray:
+    """One decode step of grouped-query attention over a compressed cache.
+
+    q: [Hq][d]; kenc/venc: one Encoded per KV head.  Query head h reads KV head
+    h // (Hq / Hkv).  logits = scale * score; softmax over tokens; the output is
+    sum_t p_t v_hat_t with v_hat the mse reconstruction."""
+    hq = q.shape[0]
+    hkv = len(kenc)
+    group = hq // hkv
+    out = np.zeros((hq, q.shape[1]))
+    for h in range(hq):
+        g = h // group
+        kh = g if kcodec.heads > 1 else 0
+        vh = g if vcodec.heads > 1 else 0
+        s = score(kcodec, q[h:h + 1], kenc[g], kh)[0] * scale
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[h] = p @ reconstruct(vcodec, venc[g], vh)
+    return out
+
+
+def topk(scores: np.ndarray, k: int):
+    """Per row the k largest scores, descending; equal scores go to the smaller id."""
+    nq, n = scores.shape
+    ids = np.empty((nq, k), dtype=np.int64)
+    for i in range(nq):
+        order = np.lexsort((np.arange(n), -scores[i]))
+        ids[i] = order[:k]
+    return np.take_along_axis(scores, ids, axis=1), ids
+
+
+# ---------------------------------------------------------------------------
+# Record layout (the library's specification; the pages give none).
+#
+# Records are grouped in tiles of 64 vectors.  Fields of a tile, in order:
+#   codes, signs (prod only), n_x (fp16 x 64), n_r (fp16 x 64, prod only).
+# Row layout: a vector's code bits form one bit string, plane by plane (plane p
+#   holds bit p of the index of every dim with more than p bits, dims
+#   ascending); bit k is bit (k mod 8) of byte k div 8.  Its C = ceil(B/8) bytes
+#   are cut into 16-byte chunks (the last may be shorter); chunk j of the tile
+#   is stored as [64 vectors][width_j] bytes.  Sign bits (bit j = [z_j >= 0])
+#   are packed and chunked the same way.
+# Col layout: for every plane p and every dim i of that plane, one little-endian
+#   64-bit word whose bit v is bit p of the index of vector v of the tile; then
+#   one 64-bit word per sketch dim j.
+# Slots of a partly filled last tile are zero.
+# ---------------------------------------------------------------------------
+TILE = 64
+
+
+def plane_dims(bits: np.ndarray):
+    return [np.nonzero(bits > p)[0] for p in range(int(bits.max()))]
+
+
+def _chunks(nbytes: int):
+    out, off = [], 0
+    while off < nbytes:
+        w = min(16, nbytes - off)
+        out.append((off, w))
+        off += w
+    return out
+
+
+def tile_fields(codec: Codec):
+    """(field name, byte offset in tile, bytes) for every field of a tile."""
+    fields, off = [], 0
+    total_bits = int(codec.bits.sum())
+    if codec.layout == "row":
+        for j, (o, w) in enumerate(_chunks((total_bits + 7) // 8)):
+            fields.append((f"code{j}", off, TILE * w))
+            off += TILE * w
+        if codec.mode == "prod":
+            for j, (o, w) in enumerate(_chunks((codec.m + 7) // 8)):
+                fields.append((f"sign{j}", off, TILE * w))
+                off += TILE * w
+    else:
+        fields.append(("codes", off, 8 * total_bits))
+        off += 8 * total_bits
+        if codec.mode == "prod":
+            fields.append(("signs", off, 8 * codec.m))
+            off += 8 * codec.m
+    fields.append(("nx", off, 2 * TILE))
+    off += 2 * TILE
+    if codec.mode == "prod":
+        fields.append(("nr", off, 2 * TILE))
+        off += 2 * TILE
+    return fields
+
+
+def tile_bytes(codec: Codec) -> int:
+    f = tile_fields(codec)
+    return f[-1][1] + f[-1][2]
+
+
+def _row_bitstrings(codec: Codec, idx: np.ndarray) -> np.ndarray:
+    planes = []
+    for p, dims in enumerate(plane_dims(codec.bits)):
+        planes.append(((idx[:, dims] >> p) & 1).astype(np.uint8))
+    return np.concatenate(planes, axis=1)
+
+
+def pack(codec: Codec, enc: Encoded) -> np.ndarray:
+    """Bytes of ceil(n/64) tiles holding the records of enc."""
+    n = enc.idx.shape[0]
+    ntile = (n + TILE - 1) // TILE
+    tb = tile_bytes(codec)
+    buf = np.zeros(ntile * tb, dtype=np.uint8)
+    fields = dict((f[0], (f[1], f[2])) for f in tile_fields(codec))
+    pad = ntile * TILE - n
+    idx = np.concatenate([enc.idx, np.zeros((pad, codec.d), np.int64)])
+    sg = None
+    if codec.mode == "prod":
+        sg = np.concatenate([enc.signs, np.zeros((pad, codec.m), bool)]).astype(np.uint8)
+    nx = np.concatenate([enc.nx, np.zeros(pad, np.float16)])
+    nr = np.concatenate([enc.nr, np.zeros(pad, np.float16)]) if codec.mode == "prod" else None
+    for t in range(ntile):
+        base = t * tb
+        rows = slice(t * TILE, (t + 1) * TILE)
+        if codec.layout == "row":
+            cbytes = np.packbits(_row_bitstrings(codec, idx[rows]), axis=1, bitorder="little")
+            for j, (o, w) in enumerate(_chunks(cbytes.shape[1])):
+                fo, _ = fields[f"code{j}"]
+                buf[base + fo: base + fo + TILE * w] = cbytes[:, o:o + w].reshape(-1)
+            if sg is not None:
+                sbytes = np.packbits(sg[rows], axis=1, bitorder="little")
+                for j, (o, w) in enumerate(_chunks(sbytes.shape[1])):
+                    fo, _ = fields[f"sign{j}"]
+                    buf[base + fo: base + fo + TILE * w] = sbytes[:, o:o + w].reshape(-1)
+        else:
+            words = []
+            for p, dims in enumerate(plane_dims(codec.bits)):
+                for i in dims:
+                    words.append(np.packbits(((idx[rows, i] >> p) & 1).astype(np.uint8),
+                                             bitorder="little"))
+            fo, fl = fields["codes"]
+            buf[base + fo: base + fo + fl] = np.concatenate(words)
+            if sg is not None:
+                fo, fl = fields["signs"]
+                buf[base + fo: base + fo + fl] = np.concatenate(
+                    [np.packbits(sg[rows, j], bitorder="little") for j in range(codec.m)])
+        fo, _ = fields["nx"]
+        buf[base + fo: base + fo + 2 * TILE] = nx[rows].view(np.uint8)
+        if nr is not None:
+            fo, _ = fields["nr"]
+            buf[base + fo: base + fo + 2 * TILE] = nr[rows].view(np.uint8)
+    return buf
+
+
+def unpack(codec: Codec, buf: np.ndarray, n: int) -> Encoded:
+    """Inverse of pack (y and z are not stored and come back as None)."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    ntile = (n + TILE - 1) // TILE
+    tb = tile_bytes(codec)
+    fields = dict((f[0], (f[1], f[2])) for f in tile_fields(codec))
+    d = codec.d
+    idx = np.zeros((ntile * TILE, d), dtype=np.int64)
+    sg = np.zeros((ntile * TILE, codec.m), dtype=bool) if codec.mode == "prod" else None
+    nx = np.zeros(ntile * TILE, np.float16)
+    nr = np.zeros(ntile * TILE, np.float16) if codec.mode == "prod" else None
+    pdims = plane_dims(codec.bits)
+    total_bits = int(codec.bits.sum())
+    for t in range(ntile):
+        base = t * tb
+        rows = slice(t * TILE, (t + 1) * TILE)
+        if codec.layout == "row":
+            nbytes = (total_bits + 7) // 8
+            cb = np.zeros((TILE, nbytes), np.uint8)
+            for j, (o, w) in enumerate(_chunks(nbytes)):
+                fo, _ = fields[f"code{j}"]
+                cb[:, o:o + w] = buf[base + fo: base + fo + TILE * w].reshape(TILE, w)
+            bitsarr = np.unpackbits(cb, axis=1, bitorder="little")[:, :total_bits].astype(np.int64)
+            k = 0
+            for p, dims in enumerate(pdims):
+                idx[rows, dims] |= bitsarr[:, k:k + len(dims)] << p
+                k += len(dims)
+            if sg is not None:
+                nb = (codec.m + 7) // 8
+                sb = np.zeros((TILE, nb), np.uint8)
+                for j, (o, w) in enumerate(_chunks(nb)):
+                    fo, _ = fields[f"sign{j}"]
+                    sb[:, o:o + w] = buf[base + fo: base + fo + TILE * w].reshape(TILE, w)
+                sg[rows] = np.unpackbits(sb, axis=1, bitorder="little")[:, :codec.m].astype(bool)
+        else:
+            fo, fl = fields["codes"]
+            words = buf[base + fo: base + fo + fl].reshape(-1, 8)
+            k = 0
+            for p, dims in enumerate(pdims):
+                for i in dims:
+                    idx[rows, i] |= np.unpackbits(words[k], bitorder="little").astype(np.int64) << p
+                    k += 1
+            if sg is not None:
+                fo, fl = fields["signs"]
+                words = buf[base + fo: base + fo + fl].reshape(-1, 8)
+                for j in range(codec.m):
+                    sg[rows, j] = np.unpackbits(words[j], bitorder="little").astype(bool)
+        fo, _ = fields["nx"]
+        nx[rows] = buf[base + fo: base + fo + 2 * TILE].view(np.float16)
+        if nr is not None:
+            fo, _ = fields["nr"]
+            nr[rows] = buf[base + fo: base + fo + 2 * TILE].view(np.float16)
+    return Encoded(idx[:n], None if sg is None else sg[:n], nx[:n],
+                   None if nr is None else nr[:n], None, None)

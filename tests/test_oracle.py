@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself:
+published known-answer vectors, closed forms, textbook tables, the pages'
+bounds and claims, brute force and Monte Carlo.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, special, stats
+
+from oracle import tq_oracle as o
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# --------------------------------------------------------------------- RNG
+def test_philox_known_answers():
+    for r in _rows("philox4x32_10_kat.txt"):
+        v = [int(x, 16) for x in r]
+        out = o.philox4x32_10(np.array(v[:4], np.uint32), np.array(v[4:6], np.uint32))
+        assert [int(x) for x in out] == v[6:]
+
+
+def test_philox_normals_law():
+    z = o.philox_normals(12345, o.STREAM_ROTATION, 200000)
+    assert abs(z.mean()) < 0.01 and abs(z.var() - 1) < 0.01
+    assert stats.kstest(z, "norm").pvalue > 1e-3
+    # streams and seeds give different numbers
+    assert not np.allclose(z[:8], o.philox_normals(12345, o.STREAM_SKETCH, 8))
+    assert not np.allclose(z[:8], o.philox_normals(12346, o.STREAM_ROTATION, 8))
+
+
+# ---------------------------------------------------------------- rotation
+@pytest.mark.parametrize("d", [8, 128])
+def test_haar_orthogonal(d):
+    p = o.haar_rotation(d, 7)
+    assert np.max(np.abs(p.T @ p - np.eye(d))) < 1e-12
+    assert abs(abs(np.linalg.det(p)) - 1) < 1e-10
+    p32 = p.astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(p32.T @ p32 - np.eye(d))) < 1e-6
+
+
+def test_haar_entries_and_rotated_coordinate_law():
+    d = 64
+    ent, coords = [], []
+    u = np.zeros(d)
+    u[0], u[5] = 0.6, 0.8
+    for s in range(60):
+        p = o.haar_rotation(d, 1000 + s)
+        ent.append(p.ravel() * math.sqrt(d))
+        coords.append(p @ u)
+    ent = np.concatenate(ent)
+    assert abs(ent.mean()) < 0.01 and abs(ent.var() - 1) < 0.02
+    # coordinates of Pi u follow the Beta law of the paper review's "Method"
+    al = (d - 1) / 2
+    cdf = lambda t: special.betainc(al, al, (np.clip(t, -1, 1) + 1) / 2)
+    assert stats.kstest(np.concatenate(coords), cdf).pvalue > 1e-3
+
+
+# --------------------------------------------------------------- codebooks
+def _density(d):
+    z = math.exp(special.betaln(0.5, (d - 1) / 2))
+    return lambda t: (1 - t * t) ** ((d - 3) / 2) / z
+
+
+@pytest.mark.parametrize("d", [8, 128, 1536])
+def test_beta_one_bit_closed_form(d):
+    # +-E|T| with E|T| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2)); total MSE 1 - d E|T|^2
+    e = math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    lm = o.beta_codebook(d, 1)
+    # lgamma near 770 carries ~1e-13 absolute error, so ~1e-12 relative here
+    assert np.allclose(lm.centroids, [-e, e], rtol=1e-11, atol=0)
+    assert lm.boundaries[0] == 0.0
+    assert abs(lm.mse * d - (1 - d * e * e)) < 1e-10
+
+
+def test_beta_one_bit_values():
+    # numeric values of the closed form at the dims used here
+    for d, c, dm in ((8, 0.291026, 0.32243), (128, 0.0706616, 0.36089), (1536, 0.0203618, 0.36317)):
+        lm = o.beta_codebook(d, 1)
+        assert abs(lm.centroids[1] - c) < 1e-6 and abs(lm.mse * d - dm) < 1e-5
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
+def test_beta_d3_is_uniform_quantizer(bits):
+    # d = 3: the law is uniform on [-1, 1], whose optimum quantizer is the
+    # uniform one; total MSE 4^-b equals the lower bound exactly.
+    lm = o.beta_codebook(3, bits)
+    L = 1 << bits
+    assert np.allclose(lm.centroids, -1 + (2 * np.arange(L) + 1) / L, atol=1e-9)
+    assert abs(lm.mse * 3 - 4.0 ** -bits) < 1e-12
+
+
+def test_gaussian_lloyd_max_matches_max_1960():
+    for r in _rows("lloyd_max_gaussian_max1960.txt"):
+        L = int(r[0])
+        pos = [float(x) for x in r[1:-1]]
+        lm = o.gaussian_codebook(int(math.log2(L)))
+        assert np.allclose(lm.centroids[L // 2:], pos, rtol=0, atol=6e-4)
+        assert abs(lm.mse - float(r[-1])) < 6e-5
+
+
+def test_beta_tends_to_gaussian():
+    for b in (1, 2, 3):
+        g = o.gaussian_codebook(b)
+        lm = o.beta_codebook(1536, b)
+        assert np.allclose(lm.centroids * math.sqrt(1536), g.centroids, rtol=2e-3)
+        assert abs(lm.mse * 1536 / g.mse - 1) < 2e-3
+
+
+@pytest.mark.parametrize("d,bits", [(8, 2), (8, 3), (128, 2), (128, 4), (1536, 3)])
+def test_lloyd_max_fixed_point_by_quadrature(d, bits):
+    # Independent of the closed forms: adaptive quadrature of the density.
+    f = _density(d)
+    lm = o.beta_codebook(d, bits)
+    edges = np.concatenate([[-1.0], lm.boundaries, [1.0]])
+    s = 1 / math.sqrt(d)
+    tot = 0.0
+    for k in range(len(lm.centroids)):
+        a, b = max(edges[k], -40 * s), min(edges[k + 1], 40 * s)
+        pts = [x for x in (0.0,) if a < x < b]
+        p = integrate.quad(f, a, b, epsabs=1e-15, epsrel=1e-13, limit=200, points=pts or None)[0]
+        m1 = integrate.quad(lambda t: t * f(t), a, b, epsabs=1e-16, epsrel=1e-13, limit=200,
+                            points=pts or None)[0]
+        assert abs(m1 / p - lm.centroids[k]) < 1e-10 * max(1.0, s)
+        tot += p
+    assert abs(tot - 1) < 1e-10
+    assert np.allclose(lm.boundaries, 0.5 * (lm.centroids[1:] + lm.centroids[:-1]), atol=1e-15)
+    assert np.array_equal(lm.centroids, -lm.centroids[::-1])
+    var = integrate.quad(lambda t: t * t * f(t), -1, 1, epsabs=1e-16, epsrel=1e-12, limit=400,
+                         points=[0.0])[0]
+    assert abs(var - 1 / d) < 1e-10
+
+
+@pytest.mark.parametrize("d", [8, 128, 1536])
+def test_mse_falls_with_bits_and_stays_within_bounds(d):
+    # Paper review, "Validation"/"Results": total MSE of a unit vector at b bits
+    # per coordinate lies between the lower bound 4^-b and (sqrt(3) pi / 2) 4^-b.
+    prev = math.inf
+    for b in range(1, 6):
+        D = o.beta_codebook(d, b).mse * d
+        assert D < prev
+        assert 4.0 ** -b <= D <= math.sqrt(3) * math.pi / 2 * 4.0 ** -b
+        prev = D
+
+
+def test_quantize_matches_brute_force_d8():
+    codec = o.turboquant_codec(8, 3, "mse", rot_seed=5)
+    rng = np.random.default_rng(0)
+    y = rng.normal(size=(5000, 8)) / math.sqrt(8)
+    idx = o.quantize(codec, y, 0)
+    c = codec.centroids[0][0]
+    brute = np.argmin(np.abs(y[:, :, None] - c[None, None, :]), axis=2)
+    dist = o.boundary_distance(codec, y)
+    ok = dist > 1e-12
+    assert np.array_equal(idx[ok], brute[ok])
+
+
+def test_empirical_mse_matches_codebook():
+    d, b = 128, 2
+    codec = o.turboquant_codec(d, b, "mse", rot_seed=11)
+    x = np.random.default_rng(1).normal(size=(20000, d))
+    enc = o.encode(codec, x, round_norms=False)
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    err = np.sum((u - o.reconstruct(codec, enc) / enc.nx[:, None]) ** 2, axis=1)
+    D = codec.extra["lloyd_max"].mse * d
+    assert abs(err.mean() - D) < 4 * err.std() / math.sqrt(len(err)) + 2e-6
+
+
+# ------------------------------------------------------------------ scoring
+def test_two_scoring_paths_agree():
+    d = 128
+    codec = o.turboquant_codec(d, 3, "prod", rot_seed=13, sketch_seed=14)
+    rng = np.random.default_rng(2)
+    x, q = rng.normal(size=(300, d)), rng.normal(size=(7, d))
+    enc = o.encode(codec, x)
+    s1 = o.score(codec, q, enc)
+    s2 = o.score_via_reconstruction(codec, q, enc)
+    assert np.max(np.abs(s1 - s2)) < 1e-12 * np.max(np.abs(s1))
+
+
+def _prod_mc(d, m_codec, x, q, seeds):
+    vals = []
+    for s in seeds:
+        codec = m_codec(s)
+        enc = o.encode(codec, x[None], round_norms=False)
+        vals.append(o.score(codec, q[None], enc)[0, 0])
+    return np.array(vals), codec, enc
+
+
+def test_prod_estimator_unbiased_over_sketch():
+    # Paper review, "Results": the prod variant is exactly unbiased.  Fixed x, q
+    # and Pi; the mean over independent sketches S must equal <q, x>.
+    d = 64
+    rng = np.random.default_rng(3)
+    x, q = rng.normal(size=d), rng.normal(size=d)
+    codec0 = o.turboquant_codec(d, 3, "prod", rot_seed=21, sketch_seed=0)
+
+    def mk(s):
+        c = o.Codec(**{**codec0.__dict__})
+        c.sketch = o._f32(o.gaussian_sketch(d, 5000 + s))
+        return c
+
+    v, codec, enc = _prod_mc(d, mk, x, q, range(3000))
+    se = v.std(ddof=1) / math.sqrt(len(v))
+    assert abs(v.mean() - q @ x) < 4 * se
+    # variance of the QJL term: (n_r^2/m) ((pi/2) |q'|^2 - <q', r_hat>^2) n_x^2
+    qr = codec.rot[0] @ q
+    y = enc.y[0]
+    r = y - o.dequantize(codec, enc.idx, 0)[0]
+    nr = np.linalg.norm(r)
+    var = (nr ** 2 / d) * ((math.pi / 2) * qr @ qr - (qr @ (r / nr)) ** 2) * float(enc.nx[0]) ** 2
+    assert abs(v.var(ddof=1) / var - 1) < 0.1
+
+
+def test_mse_inner_product_is_biased():
+    # Paper review, "Problem": mse-optimal quantizers give biased inner products.
+    # At 1 bit and large d the mean of <q, x_hat> over random rotations is
+    # (2/pi) <q, x> (derived: E|T| sqrt(2/pi) sqrt(d) -> 2/pi).
+    d = 128
+    rng = np.random.default_rng(4)
+    x, q = rng.normal(size=d), rng.normal(size=d)
+    q = q + 2 * x
+    lm = o.beta_codebook(d, 1)
+    ratios = []
+    for s in range(300):
+        c = o.Codec(d, "mse", np.full(d, 1), 0, "row", o._f32(o.haar_rotation(d, 9000 + s))[None],
+                    None, [[o._f32(lm.centroids)] * d], [[o._f32(lm.boundaries)] * d])
+        enc = o.encode(c, x[None], round_norms=False)
+        ratios.append(o.score(c, q[None], enc)[0, 0] / (q @ x))
+    assert abs(np.mean(ratios) - 2 / math.pi) < 0.02
+
+
+def test_scores_converge_with_bits():
+    d = 128
+    rng = np.random.default_rng(5)
+    x, q = rng.normal(size=(400, d)), rng.normal(size=(5, d))
+    errs = []
+    for b in (2, 3, 4, 5):
+        c = o.turboquant_codec(d, b, "mse", rot_seed=31)
+        errs.append(np.abs(o.score(c, q, o.encode(c, x)) - q @ x.T).mean())
+    assert all(a > b for a, b in zip(errs, errs[1:]))
+
+
+def test_zero_vector_scores_zero():
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=1, sketch_seed=2)
+    enc = o.encode(codec, np.zeros((1, 128)))
+    assert float(enc.nx[0]) == 0.0
+    assert o.score(codec, np.ones((1, 128)), enc)[0, 0] == 0.0
+
+
+# ----------------------------------------------------------------- layout
+@pytest.mark.parametrize("layout", ["row", "col"])
+def test_layout_worked_example(layout):
+    codec = o.Codec(8, "mse", np.full(8, 2), 0, layout, np.eye(8)[None], None,
+                    [[np.zeros(4)] * 8], [[np.zeros(3)] * 8])
+    idx = np.array([[0, 1, 2, 3, 3, 2, 1, 0], [3] * 8])
+    enc = o.Encoded(idx, None, np.array([1.0, 2.0], np.float16), None, None, None)
+    buf = o.pack(codec, enc)
+    rows = {tuple(r[:2]): [int(v, 16) for v in r[2:]] for r in _rows("record_layout_example.txt")}
+    assert len(buf) == 256
+    if layout == "row":
+        assert list(buf[:4]) == rows[("row", "code0")]
+        assert list(buf[128:132]) == rows[("row", "nx")]
+    else:
+        words = buf[:128].reshape(16, 8)
+        assert list(words[:8, 0]) == rows[("col", "plane0")]
+        assert list(words[8:, 0]) == rows[("col", "plane1")]
+        assert not words[:, 1:].any()
+        assert list(buf[128:132]) == rows[("col", "nx")]
+    back = o.unpack(codec, buf, 2)
+    assert np.array_equal(back.idx, idx)
+
+
+@pytest.mark.parametrize("layout", ["row", "col"])
+@pytest.mark.parametrize("n", [1, 64, 100])
+def test_pack_roundtrip(layout, n):
+    rng = np.random.default_rng(n)
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=3, sketch_seed=4, layout=layout)
+    enc = o.encode(codec, rng.normal(size=(n, 128)))
+    back = o.unpack(codec, o.pack(codec, enc), n)
+    assert np.array_equal(back.idx, enc.idx) and np.array_equal(back.signs, enc.signs)
+    assert np.array_equal(back.nx, enc.nx) and np.array_equal(back.nr, enc.nr)
+    assert len(o.pack(codec, enc)) == ((n + 63) // 64) * o.tile_bytes(codec)
+
+
+def test_record_sizes():
+    k = o.turboquant_codec(128, 3, "prod", rot_seed=1, sketch_seed=2)
+    v = o.turboquant_codec(128, 4, "mse", rot_seed=1, layout="col")
+    assert o.tile_bytes(k) == 64 * 52 and o.tile_bytes(v) == 64 * 66
+
+
+# -------------------------------------------------------------- attention
+def test_attention_is_softmax_over_reconstructions():
+    d, hq, hkv, T = 128, 8, 2, 200
+    rng = np.random.default_rng(6)
+    kc = o.turboquant_codec(d, 3, "prod", rot_seed=41, sketch_seed=42)
+    vc = o.turboquant_codec(d, 4, "mse", rot_seed=41, layout="col")
+    K, V = rng.normal(size=(hkv, T, d)), rng.normal(size=(hkv, T, d))
+    q = rng.normal(size=(hq, d))
+    ke = [o.encode(kc, K[h]) for h in range(hkv)]
+    ve = [o.encode(vc, V[h]) for h in range(hkv)]
+    scale = 1 / math.sqrt(d)
+    out = o.decode_attention(kc, vc, q, ke, ve, scale)
+    for h in range(hq):
+        g = h // (hq // hkv)
+        kh = o.reconstruct(kc, ke[g])
+        w = special.softmax(scale * (kh @ q[h]))
+        assert np.allclose(out[h], w @ o.reconstruct(vc, ve[g]), atol=1e-12)
+
+
+def test_attention_equal_logits_give_mean_value():
+    d = 128
+    kc = o.turboquant_codec(d, 3, "prod", rot_seed=1, sketch_seed=2)
+    vc = o.turboquant_codec(d, 4, "mse", rot_seed=1, layout="col")
+    rng = np.random.default_rng(7)
+    K = np.repeat(rng.normal(size=(1, d)), 50, axis=0)
+    V = rng.normal(size=(50, d))
+    out = o.decode_attention(kc, vc, rng.normal(size=(1, d)), [o.encode(kc, K)],
+                             [o.encode(vc, V)], 0.1)
+    assert np.allclose(out[0], o.reconstruct(vc, o.encode(vc, V)).mean(0), atol=1e-12)
+
+
+# ------------------------------------------------------------------ top-k
+def test_topk_brute_force_and_ties():
+    s = np.array([[0.5, 0.9, 0.9, 0.1, 0.7]])
+    v, i = o.topk(s, 3)
+    assert i.tolist() == [[1, 2, 4]] and v.tolist() == [[0.9, 0.9, 0.7]]
+    rng = np.random.default_rng(8)
+    s = rng.normal(size=(4, 1000))
+    v, i = o.topk(s, 10)
+    for r in range(4):
+        assert set(i[r]) == set(np.argsort(-s[r])[:10])
+
+
+# ----------------------------------------------------------- SpectralQuant
+def test_eigenbasis_and_spectrum():
+    import synth
+    law = synth.KVLaw(2, 128, 405)
+    calib = np.stack([law.sample(h, 2048, __import__("torch").Generator().manual_seed(h), "cpu")
+                      .float().numpy() for h in range(2)]).astype(np.float64)
+    for h in range(2):
+        lam, rows = o.eigenbasis(calib[h])
+        xc = calib[h] - calib[h].mean(0)
+        cov = xc.T @ xc / xc.shape[0]
+        assert np.max(np.abs(rows @ rows.T - np.eye(128))) < 1e-12
+        assert np.max(np.abs(cov @ rows.T - rows.T * lam[None, :])) < 1e-9 * lam[0]
+        assert np.all(np.diff(lam) <= 0)
+        frac = lam[:4].sum() / lam.sum()
+        # "~80% of the variance lives in 4 of 128 dimensions" (SpectralQuant thread, tweet 2)
+        assert 0.75 < frac < 0.95
+
+
+def test_selective_qjl_unbiased_on_signal_dims():
+    # QJL on the first m=4 rotated dims only (SpectralQuant thread, tweet 5): the
+    # sign term estimates <q'_{0..3}, r_{0..3}> without bias over random S.
+    d, m = 128, 4
+    rng = np.random.default_rng(9)
+    calib = rng.normal(size=(1, 512, d)) * np.linspace(3, 0.1, d)[None, None, :]
+    bitmap = [5, 3, 2, 2] + [1] * (d - 4)
+    base = o.spectralquant_codec(calib, bitmap, m, sketch_seed=1)
+    x, q = calib[0, 7], rng.normal(size=d)
+    vals = []
+    for s in range(4000):
+        c = o.Codec(**{**base.__dict__})
+        c.sketch = o._f32(o.gaussian_sketch(m, 777 + s))
+        enc = o.encode(c, x[None], round_norms=False)
+        qr, qs = o.prepare_query(c, q[None])
+        vals.append(float(enc.nr[0]) * o.QJL_CONST / m * (qs[0] @ np.where(enc.signs[0], 1, -1)))
+    r = enc.y[0, :m] - o.dequantize(c, enc.idx, 0)[0, :m]
+    target = qr[0, :m] @ r
+    vals = np.array(vals)
+    assert abs(vals.mean() - target) < 4 * vals.std(ddof=1) / math.sqrt(len(vals))
