@@ -184,11 +184,12 @@ class LloydMax:
 
 
 def lloyd_max(moments, lo: float, hi: float, levels: int, init: np.ndarray,
-              rtol: float = 1e-13, max_iter: int = 200000, patience: int = 500) -> LloydMax:
+              rtol: float = 1e-16, max_iter: int = 200000, patience: int = 500) -> LloydMax:
     """Lloyd's iteration for a scalar law on [lo, hi]: boundaries at centroid
     midpoints, centroids at the conditional mean of their cell ("continuous 1-D
     k-means", paper review, "Method").  Stops when the largest centroid move is
-    below rtol * max|c|, or when the move has not reached a new minimum for
+    below rtol * max|c| (1e-16: in practice the rounding floor), or when the
+    move has not reached a new minimum for
     ``patience`` steps (the rounding floor of the moments, ~1e-14).  The result
     is made exactly symmetric."""
     c = np.array(init, dtype=np.float64)
