@@ -1,0 +1,229 @@
+/*
+ * tq.h -- C ABI of the TurboQuant / SpectralQuant codec for MI355X (gfx950).
+ *
+ * The library quantizes vectors online (TurboQuant: store ||x||, rotate
+ * x/||x|| by a seeded random orthogonal Pi, quantize each rotated coordinate
+ * with a precomputed Lloyd-Max codebook for the known post-rotation law; the
+ * prod variant adds a 1-bit QJL sketch of the residual) and scores queries
+ * directly against the compressed records (inner products, fused decode
+ * attention, top-k search).
+ *
+ * Sources of the operations (web pages, cited by title and section):
+ *   [TQ]  "TurboQuant: Online Vector Quantization with Near-optimal Distortion
+ *         Rate" -- paper review (Zandieh et al., ICLR 2026): sections
+ *         "Method", "Key idea", "Results", "Limitations", "Sparks".
+ *   [SQ]  SpectralQuant thread (Ashwin Gopinath, tweet index), tweets 2-6.
+ *   [LK]  OnlyTerp/turboquant LAUNCH.md (launch kit): dense-QR rotation mode.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments named as device buffers are device pointers on the
+ *     codebook's device; host pointers are marked "host".
+ *   - The caller owns every buffer.  Only tq_codebook_build allocates (device
+ *     tables of the codebook) and tq_codebook_free releases them.
+ *   - Argument, shape and alignment checks run before any launch; on error
+ *     nothing is launched and nothing is written.  Kernel launches are
+ *     asynchronous on `stream` (a hipStream_t, NULL = default stream); launch
+ *     failures return TQ_EDEVICE, faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - Codebooks are immutable after build and may be shared across streams.
+ *   - No function prints, throws or calls exit.
+ *
+ * Record layout (the pages define none; this is the library's own format).
+ * Records are grouped in TILES of 64 consecutive vectors; a buffer holding n
+ * records is ceil(n/64) tiles of tq_codebook_info.tile_bytes bytes.  Fields of
+ * a tile, in order: codes, signs (prod only), n_x (64 x fp16), n_r (64 x fp16,
+ * prod only).  Norms are fp16, round to nearest even.
+ *   ROW layout (for keys and database vectors, read one vector per lane):
+ *     a vector's index bits form one bit string, plane by plane (plane p holds
+ *     bit p of the index of every dim with more than p bits, dims ascending);
+ *     bit k of the string is bit (k mod 8) of byte (k div 8).  Its
+ *     C = ceil(B/8) bytes are cut into 16-byte chunks (the last may be
+ *     shorter); chunk j of the tile is stored as [64 vectors][width_j] bytes.
+ *     Sign bits (bit j = [z_j >= 0]) are packed and chunked the same way.
+ *   COL layout (for values, read one coordinate per lane across the tile):
+ *     for every plane p and every dim i of that plane, a little-endian 64-bit
+ *     word whose bit v is bit p of the index of vector v of the tile.
+ *   Slots past the last vector of a partly filled tile are written as zero.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* bad argument: null pointer, non-positive size, bad enum  */
+  TQ_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. d)    */
+  TQ_EALIGN = 3,        /* a pointer or stride violates the stated alignment       */
+  TQ_ENOMEM = 4,        /* device or host allocation failed (codebook build only)  */
+  TQ_EWORKSPACE = 5,    /* workspace missing or smaller than tq_workspace_size     */
+  TQ_EDEVICE = 6        /* a HIP runtime call or kernel launch failed              */
+} tq_status;
+
+enum { TQ_MSE = 0, TQ_PROD = 1 };                 /* [TQ] "Method"                  */
+enum { TQ_F32 = 0, TQ_BF16 = 1 };                 /* element types of x and q       */
+enum { TQ_ROT_HAAR = 0, TQ_ROT_GIVEN = 1, TQ_ROT_CALIBRATE = 2 };
+enum { TQ_LAYOUT_ROW = 0, TQ_LAYOUT_COL = 1 };
+
+#define TQ_TILE 64          /* vectors per record tile                         */
+#define TQ_MAX_BITS 5       /* max index bits per coordinate (32 levels)       */
+#define TQ_MAX_LEVELS 32
+
+typedef struct tq_codebook tq_codebook;
+
+/* Description of a codec.
+ *   d          dimension; the GPU kernels support d = 128 (KV heads) and any
+ *              multiple of 128 up to 4096 for scoring/search (d = 1536 is the
+ *              vector-search size).
+ *   mode       TQ_MSE: `bits` index bits per coordinate.  TQ_PROD: bits-1 index
+ *              bits plus a 1-bit QJL sketch of the residual ([TQ] "Method").
+ *   bits       total bits per coordinate (TQ_PROD needs bits >= 2).
+ *   bitmap     optional host array [d] of per-dim index bits (1..5) replacing the
+ *              uniform bits (SpectralQuant water-filled map, e.g. 5,3,2,2,1,..;
+ *              [SQ] tweet 6); NULL = uniform.
+ *   qjl_dims   m, TQ_PROD only: the sketch S (m x m, i.i.d. N(0,1)) acts on
+ *              rotated dims 0..m-1 ([SQ] tweet 5); 0 means m = d (TurboQuant).
+ *   rotation   TQ_ROT_HAAR: Pi is Haar from seed_rotation ([TQ] "Method",
+ *              [LK] dense QR); codebooks are Lloyd-Max for the rotated-
+ *              coordinate Beta law at dimension d.
+ *              TQ_ROT_GIVEN: Pi taken from `given` (host, [num_heads][d][d]
+ *              fp32, row i = i-th basis vector), Beta-law codebooks.
+ *              TQ_ROT_CALIBRATE: per head, Pi = eigenvectors of the centred
+ *              covariance of `calib` (host, [num_heads][calib_n][d] of
+ *              calib_dtype), eigenvalues descending, each row signed so its
+ *              largest-magnitude entry is positive ([SQ] tweet 4); per-dim
+ *              codebook = Gaussian Lloyd-Max with b_i levels scaled by sigma_i,
+ *              the RMS of rotated coordinate i of the normalised calibration
+ *              vectors.
+ *   num_heads  rotations held by the codebook (one per KV head for
+ *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN); TQ_ROT_HAAR uses 1.
+ *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map).
+ *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1) and S
+ *              (stream 2).
+ *   device     HIP device ordinal that holds the codebook's tables.
+ */
+typedef struct {
+  int32_t d;
+  int32_t mode;
+  int32_t bits;
+  const uint8_t* bitmap;
+  int32_t qjl_dims;
+  int32_t rotation;
+  int32_t num_heads;
+  int32_t layout;
+  uint64_t seed_rotation;
+  uint64_t seed_sketch;
+  const float* given;
+  const void* calib;
+  int64_t calib_n;
+  int32_t calib_dtype;
+  int32_t device;
+} tq_codebook_desc;
+
+/* Sizes of a codec's records. */
+typedef struct {
+  int32_t d, mode, m, layout, num_heads, uniform;
+  int32_t index_bits_total;   /* B = sum of per-dim index bits                 */
+  int32_t code_bytes;         /* per vector, ceil(B/8)                          */
+  int32_t sign_bytes;         /* per vector, ceil(m/8) (0 for mse)              */
+  int32_t norms;              /* fp16 norms per vector: 1 (mse) or 2 (prod)     */
+  int64_t tile_bytes;         /* bytes of one 64-vector tile                    */
+  int64_t off_signs, off_nx, off_nr;  /* byte offsets of the fields in a tile  */
+} tq_codebook_info;
+
+/* Build a codebook (host math once, then device tables on desc->device).
+ * Synchronous.  [TQ] "Method": codebooks are solved once, offline. */
+tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out);
+tq_status tq_codebook_free(tq_codebook* cb);
+tq_status tq_codebook_get_info(const tq_codebook* cb, tq_codebook_info* info);
+
+/* Copy a codebook's parameters to host memory (any pointer may be NULL):
+ *   rot [d][d] fp32 of head `head`; sketch [m][m] fp32;
+ *   centroids [d][TQ_MAX_LEVELS] and boundaries [d][TQ_MAX_LEVELS-1] fp64 of
+ *   head `head` (unused entries 0); levels [d] = 2^(bits of dim i).
+ *   The fp64 values are those of the Lloyd-Max solution; kernels use them
+ *   rounded to fp32. */
+tq_status tq_codebook_export(const tq_codebook* cb, int32_t head, float* rot, float* sketch,
+                             double* centroids, double* boundaries, int32_t* levels);
+
+/* Bytes of the record tiles holding n vectors. */
+int64_t tq_records_bytes(const tq_codebook* cb, int64_t n);
+
+/* Encode a batch of vector sets.  [TQ] "Method": n_x = ||x||, y = Pi x/n_x,
+ * idx_i = #{boundaries t of dim i with t <= y_i} (ties to the upper cell); prod:
+ * r = y - c[idx] on dims 0..m-1, n_r = ||r||, bit_j = [(S r)_j >= 0].  A zero
+ * vector encodes y = 0 and stores n_x = 0.
+ *   x        device, element (b, h, t, i) at x[b*xs_b + h*xs_h + t*xs_t + i] of
+ *            type x_dtype (TQ_F32 or TQ_BF16); row starts 16-byte aligned.
+ *   batch, heads, tokens   sizes; `heads` indexes the codebook's rotation when
+ *            it holds num_heads > 1 (must then equal num_heads).
+ *   records  device; the tiles of set (b, h) start at
+ *            records + b*rs_b + h*rs_h bytes (16-byte aligned) and hold
+ *            ceil(tokens/64) tiles.
+ * Supported: d = 128 (any codec) and d multiple of 128 up to 4096 with a
+ * uniform ROW codec. */
+tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
+                    int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
+                    void* records, int64_t rs_b, int64_t rs_h, void* stream);
+
+/* Inner-product scores of nq queries against n ROW records of head `head`:
+ *   scores[i][t] = n_x (sum_j q'_j c[idx_j] + n_r sqrt(pi/2)/m sum_j qs_j (2 bit_j - 1)),
+ *   q' = Pi q, qs = S q'[0:m] ([TQ] "Method"; estimator of <q, x>).
+ *   q        device fp32 [nq][d];  scores device fp32 [nq][n].
+ *   workspace >= tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0) bytes (device). */
+tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t head,
+                   const void* records, int64_t n, float* scores, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Compressed KV cache of one layer, records as written by tq_encode.  Set
+ * (b, h) of the keys starts at k_records + b*k_stride_seq + h*k_stride_head
+ * bytes; likewise for values. */
+typedef struct {
+  const void* k_records;
+  const void* v_records;
+  int64_t k_stride_seq, k_stride_head;
+  int64_t v_stride_seq, v_stride_head;
+  int32_t max_tokens;         /* tokens stored per (b, h)                       */
+  const int32_t* seq_lens;    /* device [B] valid tokens per sequence, or NULL  */
+} tq_kv_view;
+
+/* One decode step of grouped-query attention over a compressed cache ([TQ]
+ * "Sparks": rotation and codebook lookup fused into attention):
+ *   logit_{b,h,t} = softmax_scale * score(q_{b,h}, k_{b,g,t}), g = h / (Hq/Hkv),
+ *   out_{b,h} = sum_t softmax_t(logit) * v_hat_{b,g,t},
+ *   v_hat = n_v Pi_v^T c_v[idx] (mse reconstruction of the value).
+ *   kcb      ROW codec of the keys (num_heads 1 or Hkv);
+ *   vcb      COL mse codec of the values (num_heads 1 or Hkv); same d = 128.
+ *   q        device [B][Hq][d] of q_dtype;  out device fp32 [B][Hq][d].
+ *   workspace >= tq_workspace_size(kcb, TQ_OP_DECODE, B*Hq, max_tokens, Hkv). */
+tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                           int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                           const tq_kv_view* kv, float softmax_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Top-k inner-product search over n ROW records ([TQ] "Validation": vector
+ * search with TurboQuant codes).  For each query the k largest scores
+ * (as tq_score), descending; equal scores go to the smaller id.
+ *   top_scores device fp32 [nq][k]; top_ids device int64 [nq][k]; 1 <= k <= 64.
+ *   workspace >= tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k). */
+tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
+                         const void* records, int64_t n, int32_t k, float* top_scores,
+                         int64_t* top_ids, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+enum { TQ_OP_SCORE = 0, TQ_OP_DECODE = 1, TQ_OP_TOPK = 2 };
+
+/* Device workspace bytes an operation needs (0 on bad arguments). */
+size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b, int64_t c);
+
+const char* tq_status_string(tq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,538 @@
+// C-ABI layer of the codec library: argument validation, codebook build
+// (host math + device tables) and kernel dispatch.  Every check runs before
+// any launch; errors return a tq_status and leave outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "tq_internal.h"
+#include "tq_kernels.h"
+
+using namespace tq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+template <class T>
+tq_status upload(T** dst, const T* src, size_t count) {
+  if (hipMalloc(reinterpret_cast<void**>(dst), count * sizeof(T)) != hipSuccess) return TQ_ENOMEM;
+  if (hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice) != hipSuccess) return TQ_EDEVICE;
+  return TQ_OK;
+}
+
+void free_device(tq_codebook* cb) {
+  DeviceTables& t = cb->dev;
+  void* ptrs[] = {t.rot, t.rot_hi, t.rot_lo, t.sketch, t.sketch_hi, t.sketch_lo,
+                  t.thr, t.cen, t.bitpos, t.dim_bits};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+  t = DeviceTables{};
+}
+
+void fill_info(tq_codebook* cb) {
+  tq_codebook_info& in = cb->info;
+  const int d = cb->desc.d;
+  in.d = d;
+  in.mode = cb->desc.mode;
+  in.m = cb->m;
+  in.layout = cb->desc.layout;
+  in.num_heads = int(cb->rot32.size() / (size_t(d) * d));
+  in.uniform = cb->uniform ? 1 : 0;
+  int total = 0;
+  for (uint8_t b : cb->bits) total += b;
+  in.index_bits_total = total;
+  in.code_bytes = (total + 7) / 8;
+  in.sign_bytes = cb->desc.mode == TQ_PROD ? (cb->m + 7) / 8 : 0;
+  in.norms = cb->desc.mode == TQ_PROD ? 2 : 1;
+  int64_t off = 0;
+  off += int64_t(kTile) * in.code_bytes;  // both layouts: 64 vectors x code bytes
+  in.off_signs = off;
+  off += int64_t(kTile) * in.sign_bytes;
+  in.off_nx = off;
+  off += 2 * kTile;
+  in.off_nr = cb->desc.mode == TQ_PROD ? off : -1;
+  if (cb->desc.mode == TQ_PROD) off += 2 * kTile;
+  in.tile_bytes = off;
+}
+
+tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
+  const int d = ds.d;
+  // ---------------------------------------------------------------- bits
+  cb->bits.assign(d, 0);
+  const int ub = ds.mode == TQ_PROD ? ds.bits - 1 : ds.bits;
+  if (ds.bitmap) {
+    for (int i = 0; i < d; ++i) {
+      if (ds.bitmap[i] < 1 || ds.bitmap[i] > kMaxBits) return TQ_EINVAL;
+      cb->bits[i] = ds.bitmap[i];
+    }
+  } else {
+    if (ub < 1 || ub > kMaxBits) return TQ_EINVAL;
+    std::fill(cb->bits.begin(), cb->bits.end(), uint8_t(ub));
+  }
+  cb->uniform = std::all_of(cb->bits.begin(), cb->bits.end(), [&](uint8_t b) { return b == cb->bits[0]; });
+  cb->ubits = cb->uniform ? cb->bits[0] : 0;
+  if (ds.layout == TQ_LAYOUT_COL && !cb->uniform) return TQ_EUNSUPPORTED;
+  cb->m = ds.mode == TQ_PROD ? (ds.qjl_dims > 0 ? ds.qjl_dims : d) : 0;
+  if (cb->m > d) return TQ_EINVAL;
+
+  // ----------------------------------------------------------- rotations
+  int heads = 1;
+  if (ds.rotation == TQ_ROT_HAAR) {
+    std::vector<double> g(size_t(d) * d);
+    philox_normals(ds.seed_rotation, 1, int64_t(d) * d, g.data());
+    cb->rot64.resize(size_t(d) * d);
+    haar_from_gaussian(d, g.data(), cb->rot64.data());
+  } else if (ds.rotation == TQ_ROT_GIVEN) {
+    if (!ds.given) return TQ_EINVAL;
+    heads = std::max(1, ds.num_heads);
+    cb->rot64.assign(ds.given, ds.given + size_t(heads) * d * d);
+  } else if (ds.rotation == TQ_ROT_CALIBRATE) {
+    if (!ds.calib || ds.calib_n < 2) return TQ_EINVAL;
+    if (ds.calib_dtype != TQ_F32 && ds.calib_dtype != TQ_BF16) return TQ_EINVAL;
+    heads = std::max(1, ds.num_heads);
+    cb->rot64.resize(size_t(heads) * d * d);
+    std::vector<double> x(size_t(ds.calib_n) * d), cov(size_t(d) * d), lam(d);
+    for (int h = 0; h < heads; ++h) {
+      for (int64_t t = 0; t < ds.calib_n; ++t)
+        for (int i = 0; i < d; ++i) {
+          const size_t e = (size_t(h) * ds.calib_n + t) * d + i;
+          x[size_t(t) * d + i] = ds.calib_dtype == TQ_F32
+                                     ? double(static_cast<const float*>(ds.calib)[e])
+                                     : double(bf16_to_f32(static_cast<const uint16_t*>(ds.calib)[e]));
+        }
+      std::vector<double> mean(d, 0.0);
+      for (int64_t t = 0; t < ds.calib_n; ++t)
+        for (int i = 0; i < d; ++i) mean[i] += x[size_t(t) * d + i];
+      for (int i = 0; i < d; ++i) mean[i] /= double(ds.calib_n);
+      std::fill(cov.begin(), cov.end(), 0.0);
+      for (int64_t t = 0; t < ds.calib_n; ++t) {
+        const double* r = &x[size_t(t) * d];
+        for (int i = 0; i < d; ++i) {
+          const double a = r[i] - mean[i];
+          for (int k = 0; k < d; ++k) cov[size_t(i) * d + k] += a * (r[k] - mean[k]);
+        }
+      }
+      for (double& c : cov) c /= double(ds.calib_n);
+      symmetric_eigen(d, cov.data(), lam.data(), &cb->rot64[size_t(h) * d * d]);
+    }
+  } else {
+    return TQ_EINVAL;
+  }
+  cb->rot32.resize(cb->rot64.size());
+  for (size_t e = 0; e < cb->rot64.size(); ++e) cb->rot32[e] = float(cb->rot64[e]);
+
+  // -------------------------------------------------------------- sketch
+  if (ds.mode == TQ_PROD) {
+    std::vector<double> s(size_t(cb->m) * cb->m);
+    philox_normals(ds.seed_sketch, 2, int64_t(cb->m) * cb->m, s.data());
+    cb->sketch32.resize(s.size());
+    for (size_t e = 0; e < s.size(); ++e) cb->sketch32[e] = float(s[e]);
+  }
+
+  // ----------------------------------------------------------- codebooks
+  cb->cen64.assign(size_t(heads) * d * kMaxLevels, 0.0);
+  cb->thr64.assign(size_t(heads) * d * (kMaxLevels - 1), 0.0);
+  cb->cen32.assign(size_t(heads) * d * kMaxLevels, 0.f);
+  cb->thr32.assign(size_t(heads) * d * kMaxLevels, INFINITY);
+  LloydMaxResult books[kMaxBits + 1];
+  bool have[kMaxBits + 1] = {};
+  for (int i = 0; i < d; ++i) {
+    const int b = cb->bits[i];
+    if (!have[b]) {
+      books[b] = ds.rotation == TQ_ROT_CALIBRATE ? lloyd_max_gaussian(b) : lloyd_max_sphere(d, b);
+      have[b] = true;
+    }
+  }
+  for (int h = 0; h < heads; ++h) {
+    std::vector<double> sigma(d, 1.0);
+    if (ds.rotation == TQ_ROT_CALIBRATE) {
+      // sigma_i: RMS of rotated coordinate i of the normalised calibration vectors
+      std::vector<double> acc(d, 0.0), u(d);
+      const float* p = &cb->rot32[size_t(h) * d * d];
+      for (int64_t t = 0; t < ds.calib_n; ++t) {
+        double nn = 0;
+        for (int i = 0; i < d; ++i) {
+          const size_t e = (size_t(h) * ds.calib_n + t) * d + i;
+          u[i] = ds.calib_dtype == TQ_F32 ? double(static_cast<const float*>(ds.calib)[e])
+                                          : double(bf16_to_f32(static_cast<const uint16_t*>(ds.calib)[e]));
+          nn += u[i] * u[i];
+        }
+        nn = std::sqrt(nn);
+        for (int i = 0; i < d; ++i) u[i] = nn > 0 ? u[i] / nn : 0.0;
+        for (int i = 0; i < d; ++i) {
+          double y = 0;
+          for (int k = 0; k < d; ++k) y += double(p[size_t(i) * d + k]) * u[k];
+          acc[i] += y * y;
+        }
+      }
+      for (int i = 0; i < d; ++i) sigma[i] = std::sqrt(acc[i] / double(ds.calib_n));
+    }
+    for (int i = 0; i < d; ++i) {
+      const LloydMaxResult& lm = books[cb->bits[i]];
+      const int L = 1 << cb->bits[i];
+      for (int k = 0; k < L; ++k) {
+        const double c = lm.centroids[k] * sigma[i];
+        cb->cen64[(size_t(h) * d + i) * kMaxLevels + k] = c;
+        cb->cen32[(size_t(h) * d + i) * kMaxLevels + k] = float(c);
+      }
+      for (int k = 0; k + 1 < L; ++k) {
+        const double t = lm.boundaries[k] * sigma[i];
+        cb->thr64[(size_t(h) * d + i) * (kMaxLevels - 1) + k] = t;
+        cb->thr32[(size_t(h) * d + i) * kMaxLevels + k] = float(t);
+      }
+    }
+  }
+  // bit positions of the row-layout bit string
+  cb->bitpos.assign(size_t(kMaxBits) * d, -1);
+  int pos = 0;
+  for (int p = 0; p < kMaxBits; ++p)
+    for (int i = 0; i < d; ++i)
+      if (cb->bits[i] > p) cb->bitpos[size_t(p) * d + i] = int16_t(pos++);
+  fill_info(cb);
+  cb->info.num_heads = heads;
+  return TQ_OK;
+}
+
+tq_status build_device(tq_codebook* cb) {
+  const int d = cb->desc.d;
+  if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
+  const size_t nr = cb->rot32.size();
+  std::vector<uint16_t> hi(nr), lo(nr);
+  for (size_t e = 0; e < nr; ++e) {
+    hi[e] = f32_to_bf16_rne(cb->rot32[e]);
+    lo[e] = f32_to_bf16_rne(cb->rot32[e] - bf16_to_f32(hi[e]));
+  }
+  tq_status st;
+  if ((st = upload(&cb->dev.rot, cb->rot32.data(), nr)) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.rot_hi, hi.data(), nr)) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.rot_lo, lo.data(), nr)) != TQ_OK) return st;
+  if (!cb->sketch32.empty()) {
+    const size_t ns = cb->sketch32.size();
+    std::vector<uint16_t> shi(ns), slo(ns);
+    for (size_t e = 0; e < ns; ++e) {
+      shi[e] = f32_to_bf16_rne(cb->sketch32[e]);
+      slo[e] = f32_to_bf16_rne(cb->sketch32[e] - bf16_to_f32(shi[e]));
+    }
+    if ((st = upload(&cb->dev.sketch, cb->sketch32.data(), ns)) != TQ_OK) return st;
+    if ((st = upload(&cb->dev.sketch_hi, shi.data(), ns)) != TQ_OK) return st;
+    if ((st = upload(&cb->dev.sketch_lo, slo.data(), ns)) != TQ_OK) return st;
+  }
+  if ((st = upload(&cb->dev.thr, cb->thr32.data(), cb->thr32.size())) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.cen, cb->cen32.data(), cb->cen32.size())) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.bitpos, cb->bitpos.data(), cb->bitpos.size())) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.dim_bits, cb->bits.data(), size_t(d))) != TQ_OK) return st;
+  return TQ_OK;
+}
+
+bool on_device(const tq_codebook* cb) { return cb && cb->device >= 0 && cb->dev.rot; }
+
+tq_status map_hip(hipError_t e) {
+  if (e == hipSuccess) return TQ_OK;
+  if (e == hipErrorNotSupported) return TQ_EUNSUPPORTED;
+  return TQ_EDEVICE;
+}
+
+int64_t decode_nsplit(int64_t max_tokens) {
+  const int64_t ntiles = (max_tokens + kTile - 1) / kTile;
+  return std::max<int64_t>(1, (ntiles + 7) / 8);
+}
+constexpr int kDecodeChunkTiles = 8;
+
+int64_t topk_nseg(int64_t n) {
+  return std::max<int64_t>(1, std::min<int64_t>(1024, (n + 4095) / 4096));
+}
+
+bool supported_query_d(int d) { return d % 64 == 0 && d >= 64 && d <= 4096; }
+
+}  // namespace
+
+CodecView tq::make_view(const tq_codebook* cb) {
+  CodecView v{};
+  v.d = cb->desc.d;
+  v.mode = cb->desc.mode;
+  v.m = cb->m;
+  v.layout = cb->desc.layout;
+  v.uniform = cb->uniform ? 1 : 0;
+  v.ubits = cb->ubits;
+  v.heads = cb->info.num_heads;
+  v.code_bytes = cb->info.code_bytes;
+  v.sign_bytes = cb->info.sign_bytes;
+  v.tile_bytes = int(cb->info.tile_bytes);
+  v.off_signs = int(cb->info.off_signs);
+  v.off_nx = int(cb->info.off_nx);
+  v.off_nr = int(cb->info.off_nr);
+  v.tail_bits = cb->info.index_bits_total - cb->desc.d;
+  v.rot = cb->dev.rot;
+  v.rot_hi = cb->dev.rot_hi;
+  v.rot_lo = cb->dev.rot_lo;
+  v.sketch = cb->dev.sketch;
+  v.sk_hi = cb->dev.sketch_hi;
+  v.sk_lo = cb->dev.sketch_lo;
+  v.thr = cb->dev.thr;
+  v.cen = cb->dev.cen;
+  v.bitpos = cb->dev.bitpos;
+  v.dim_bits = cb->dev.dim_bits;
+  for (int k = 0; k < kMaxLevels; ++k) {
+    v.uthr[k] = cb->thr32[k];
+    v.ucen[k] = cb->cen32[k];
+  }
+  return v;
+}
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported configuration";
+    case TQ_EALIGN: return "misaligned pointer or stride";
+    case TQ_ENOMEM: return "out of memory";
+    case TQ_EWORKSPACE: return "workspace too small";
+    case TQ_EDEVICE: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
+  if (!desc || !out) return TQ_EINVAL;
+  *out = nullptr;
+  const tq_codebook_desc& ds = *desc;
+  if (ds.d < 2 || ds.d > 4096) return TQ_EINVAL;
+  if (ds.mode != TQ_MSE && ds.mode != TQ_PROD) return TQ_EINVAL;
+  if (ds.mode == TQ_PROD && !ds.bitmap && ds.bits < 2) return TQ_EINVAL;
+  if (ds.layout != TQ_LAYOUT_ROW && ds.layout != TQ_LAYOUT_COL) return TQ_EINVAL;
+  if (ds.qjl_dims < 0 || ds.num_heads < 0) return TQ_EINVAL;
+  if (ds.rotation == TQ_ROT_HAAR && ds.num_heads > 1) return TQ_EINVAL;
+  tq_codebook* cb = new (std::nothrow) tq_codebook();
+  if (!cb) return TQ_ENOMEM;
+  cb->desc = ds;
+  cb->device = ds.device;
+  tq_status st;
+  try {
+    st = build_host(cb, ds);
+  } catch (const std::bad_alloc&) {
+    st = TQ_ENOMEM;
+  }
+  // the caller's host arrays are not kept
+  cb->desc.bitmap = nullptr;
+  cb->desc.given = nullptr;
+  cb->desc.calib = nullptr;
+  if (st == TQ_OK && cb->device >= 0) st = build_device(cb);
+  if (st != TQ_OK) {
+    free_device(cb);
+    delete cb;
+    return st;
+  }
+  *out = cb;
+  return TQ_OK;
+}
+
+tq_status tq_codebook_free(tq_codebook* cb) {
+  if (!cb) return TQ_EINVAL;
+  if (cb->device >= 0) (void)hipSetDevice(cb->device);
+  free_device(cb);
+  delete cb;
+  return TQ_OK;
+}
+
+tq_status tq_codebook_get_info(const tq_codebook* cb, tq_codebook_info* info) {
+  if (!cb || !info) return TQ_EINVAL;
+  *info = cb->info;
+  return TQ_OK;
+}
+
+tq_status tq_codebook_export(const tq_codebook* cb, int32_t head, float* rot, float* sketch,
+                             double* centroids, double* boundaries, int32_t* levels) {
+  if (!cb) return TQ_EINVAL;
+  const int d = cb->desc.d;
+  if (head < 0 || head >= cb->info.num_heads) return TQ_EINVAL;
+  if (rot) std::memcpy(rot, &cb->rot32[size_t(head) * d * d], sizeof(float) * d * d);
+  if (sketch && !cb->sketch32.empty())
+    std::memcpy(sketch, cb->sketch32.data(), sizeof(float) * cb->sketch32.size());
+  if (centroids)
+    std::memcpy(centroids, &cb->cen64[size_t(head) * d * kMaxLevels], sizeof(double) * d * kMaxLevels);
+  if (boundaries)
+    std::memcpy(boundaries, &cb->thr64[size_t(head) * d * (kMaxLevels - 1)],
+                sizeof(double) * d * (kMaxLevels - 1));
+  if (levels)
+    for (int i = 0; i < d; ++i) levels[i] = 1 << cb->bits[i];
+  return TQ_OK;
+}
+
+int64_t tq_records_bytes(const tq_codebook* cb, int64_t n) {
+  if (!cb || n < 0) return -1;
+  return ((n + kTile - 1) / kTile) * cb->info.tile_bytes;
+}
+
+tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
+                    int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
+                    void* records, int64_t rs_b, int64_t rs_h, void* stream) {
+  if (!cb || !x || !records) return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  if (batch < 0 || heads < 0 || tokens < 0 || xs_b < 0 || xs_h < 0 || xs_t < cb->desc.d)
+    return TQ_EINVAL;
+  if (batch * heads > 65535) return TQ_EUNSUPPORTED;
+  if (!on_device(cb)) return TQ_EINVAL;
+  if (cb->info.num_heads > 1 && heads != cb->info.num_heads) return TQ_EINVAL;
+  if (cb->desc.d != 128) return TQ_EUNSUPPORTED;
+  const int64_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  if (!aligned16(x) || !aligned16(records) || (xs_t * esz) % 16 || (xs_h * esz) % 16 ||
+      (xs_b * esz) % 16 || rs_b % 16 || rs_h % 16)
+    return TQ_EALIGN;
+  if (batch == 0 || heads == 0 || tokens == 0) return TQ_OK;
+  if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
+  EncodeArgs a{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
+               static_cast<uint8_t*>(records), rs_b, rs_h};
+  return map_hip(launch_encode_d128(make_view(cb), a, static_cast<hipStream_t>(stream)));
+}
+
+size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b, int64_t c) {
+  if (!cb || a < 0 || b < 0) return 0;
+  const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
+  const size_t qprep = size_t(a) * (d + m) * 4;
+  auto round = [](size_t v) { return (v + 255) & ~size_t(255); };
+  switch (op) {
+    case TQ_OP_SCORE: return round(qprep);
+    case TQ_OP_DECODE: {
+      if (c <= 0) return 0;
+      const size_t part = size_t(a) * size_t(decode_nsplit(b)) * (2 + d) * 4;
+      return round(qprep) + round(part);
+    }
+    case TQ_OP_TOPK: {
+      if (c <= 0 || c > 16) return 0;
+      const size_t sc = size_t(a) * size_t(b) * 4;
+      const size_t ps = size_t(a) * size_t(topk_nseg(b)) * size_t(c);
+      return round(qprep) + round(sc) + round(ps * 4) + round(ps * 8);
+    }
+  }
+  return 0;
+}
+
+tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t head,
+                   const void* records, int64_t n, float* scores, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!cb || !q || !records || !scores) return TQ_EINVAL;
+  if (nq < 0 || n < 0 || head < 0 || head >= cb->info.num_heads) return TQ_EINVAL;
+  if (!on_device(cb)) return TQ_EINVAL;
+  if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d)) return TQ_EUNSUPPORTED;
+  if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
+  if (nq == 0 || n == 0) return TQ_OK;
+  if (nq > int64_t(65535) * 16) return TQ_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0)) return TQ_EWORKSPACE;
+  if (!aligned16(workspace)) return TQ_EALIGN;
+  if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CodecView cv = make_view(cb);
+  float* qr = static_cast<float*>(workspace);
+  float* qs = qr + nq * cb->desc.d;
+  QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
+  tq_status st = map_hip(launch_query_prep(cv, qa, s));
+  if (st != TQ_OK) return st;
+  return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s));
+}
+
+tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                           int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                           const tq_kv_view* kv, float softmax_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!kcb || !vcb || !q || !kv || !out || !kv->k_records || !kv->v_records) return TQ_EINVAL;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || kv->max_tokens < 0) return TQ_EINVAL;
+  if (!on_device(kcb) || !on_device(vcb) || kcb->device != vcb->device) return TQ_EINVAL;
+  if (kcb->desc.d != 128 || vcb->desc.d != 128) return TQ_EUNSUPPORTED;
+  if (kcb->desc.layout != TQ_LAYOUT_ROW || vcb->desc.layout != TQ_LAYOUT_COL ||
+      vcb->desc.mode != TQ_MSE || !vcb->uniform || vcb->ubits > 4)
+    return TQ_EUNSUPPORTED;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_EUNSUPPORTED;
+  if (kcb->info.num_heads > 1 && kcb->info.num_heads != Hkv) return TQ_EINVAL;
+  if (vcb->info.num_heads > 1 && vcb->info.num_heads != Hkv) return TQ_EINVAL;
+  if (kcb->desc.mode == TQ_PROD && kcb->m != 128 && kcb->m > 8) return TQ_EUNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return TQ_EINVAL;
+  if (!aligned16(kv->k_records) || !aligned16(kv->v_records) || kv->k_stride_seq % 16 ||
+      kv->k_stride_head % 16 || kv->v_stride_seq % 16 || kv->v_stride_head % 16 || !aligned16(q))
+    return TQ_EALIGN;
+  if (B == 0) return TQ_OK;
+  if (B > 65535) return TQ_EUNSUPPORTED;
+  const int64_t nqt = int64_t(B) * Hq;
+  if (!workspace || workspace_bytes < tq_workspace_size(kcb, TQ_OP_DECODE, nqt, kv->max_tokens, Hkv))
+    return TQ_EWORKSPACE;
+  if (!aligned16(workspace)) return TQ_EALIGN;
+  if (hipSetDevice(kcb->device) != hipSuccess) return TQ_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CodecView kc = make_view(kcb), vc = make_view(vcb);
+  const size_t d = 128, m = size_t(std::max(kcb->m, 1));
+  float* qr = static_cast<float*>(workspace);
+  float* qs = qr + nqt * d;
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         ((size_t(nqt) * (d + m) * 4 + 255) & ~size_t(255)));
+  QueryPrepArgs qa{q, q_dtype == TQ_BF16, nqt, G, Hkv, 0, qr, qs};
+  tq_status st = map_hip(launch_query_prep(kc, qa, s));
+  if (st != TQ_OK) return st;
+  DecodeArgs da{};
+  da.qr = qr;
+  da.qs = qs;
+  da.B = B;
+  da.Hq = Hq;
+  da.Hkv = Hkv;
+  da.krec = static_cast<const uint8_t*>(kv->k_records);
+  da.vrec = static_cast<const uint8_t*>(kv->v_records);
+  da.ks_seq = kv->k_stride_seq;
+  da.ks_head = kv->k_stride_head;
+  da.vs_seq = kv->v_stride_seq;
+  da.vs_head = kv->v_stride_head;
+  da.max_tokens = kv->max_tokens;
+  da.seq_lens = kv->seq_lens;
+  da.scale = softmax_scale;
+  da.chunk_tiles = kDecodeChunkTiles;
+  da.nsplit = int(decode_nsplit(kv->max_tokens));
+  da.part = part;
+  da.out = out;
+  return map_hip(launch_decode(kc, vc, da, s));
+}
+
+tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
+                         const void* records, int64_t n, int32_t k, float* top_scores,
+                         int64_t* top_ids, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!cb || !q || !records || !top_scores || !top_ids) return TQ_EINVAL;
+  if (nq < 0 || n < 0 || k < 1) return TQ_EINVAL;
+  if (k > 16) return TQ_EUNSUPPORTED;
+  if (!on_device(cb)) return TQ_EINVAL;
+  if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d) || cb->info.num_heads != 1)
+    return TQ_EUNSUPPORTED;
+  if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
+  if (nq == 0) return TQ_OK;
+  if (n < k) return TQ_EINVAL;
+  if (nq > 65535) return TQ_EUNSUPPORTED;
+  if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k)) return TQ_EWORKSPACE;
+  if (!aligned16(workspace)) return TQ_EALIGN;
+  if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const CodecView cv = make_view(cb);
+  const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
+  auto round = [](size_t v) { return (v + 255) & ~size_t(255); };
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  float* qr = reinterpret_cast<float*>(w);
+  float* qs = qr + nq * d;
+  w += round(size_t(nq) * (d + m) * 4);
+  float* sc = reinterpret_cast<float*>(w);
+  w += round(size_t(nq) * size_t(n) * 4);
+  const int nseg = int(topk_nseg(n));
+  const size_t ps = size_t(nq) * nseg * k;
+  float* pss = reinterpret_cast<float*>(w);
+  w += round(ps * 4);
+  int64_t* psi = reinterpret_cast<int64_t*>(w);
+  QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
+  tq_status st = map_hip(launch_query_prep(cv, qa, s));
+  if (st != TQ_OK) return st;
+  return map_hip(launch_topk(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, k, top_scores,
+                             top_ids, sc, pss, psi, nseg, s));
+}
+
+}  // extern "C"

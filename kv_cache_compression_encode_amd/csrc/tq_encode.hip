@@ -1,0 +1,461 @@
+// Fused TurboQuant encode for d = 128 on CDNA4 (gfx950).
+//
+// One wavefront encodes one 64-vector record tile.  Per tile:
+//   1. 128-bit loads of the input rows (lane = vector, half-wave = 64 coords),
+//      n_x = ||x|| in fp32;
+//   2. rotation Y^T = Pi X^T as 32x32x16 bf16 MFMAs with Pi split into
+//      bf16 hi + lo parts (fp32 inputs are split too), i.e. fp32-accurate y;
+//      Pi hi/lo staged once per workgroup in LDS;
+//   3. quantize: idx = #{t_k : t_k * n_x <= y_k * n_x} against the Lloyd-Max
+//      boundaries (TurboQuant paper review, "Method"), codes packed as bit
+//      planes (lane-local for the row layout, wavefront ballot for the col
+//      layout);
+//   4. prod: residual r = y - c[idx] kept in the MFMA accumulator layout, which
+//      is exactly the B-operand layout of the next product, so the QJL sketch
+//      Z^T = S R^T runs on MFMA without any transpose (S columns are permuted
+//      once when staged); sign bits = [z >= 0];
+//   5. fp16 norms n_x and n_r = ||r||.
+// The 32x32 accumulator of v_mfma_f32_32x32x16 holds, in lane l and register
+// r, row 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+#include <hip/hip_runtime.h>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int LDS_ROW = D + 8;  // bf16 elements per staged row (16-byte pad)
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)x));
+}
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Pack 8 floats into bf16 hi and lo fragments (x ~= hi + lo).
+__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits(v[2 * i]), h1 = bf16_bits(v[2 * i + 1]);
+    const uint32_t l0 = bf16_bits(v[2 * i] - bf16_val(h0));
+    const uint32_t l1 = bf16_bits(v[2 * i + 1] - bf16_val(h1));
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = l0 | (l1 << 16);
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ uint32_t xor32(uint32_t v) {
+  return __shfl_xor((int)v, 32, 64);
+}
+__device__ __forceinline__ float xor32f(float v) { return __shfl_xor(v, 32, 64); }
+
+__device__ __forceinline__ uint16_t f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Stage a [128][128] bf16 matrix into LDS rows of LDS_ROW elements; with
+// `perm` the column index has bits 2 and 3 swapped (sketch operand order).
+__device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool perm) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < D * D / 4; e += blockDim.x) {
+    const int row = e / (D / 4), grp = e % (D / 4);
+    const int col = grp * 4;
+    const int dst = perm ? ((col & ~15) | (((col >> 2) & 1) << 3) | (((col >> 3) & 1) << 2)) : col;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(g + row * D + col);
+    *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + dst) = v;
+  }
+}
+
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
+__global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
+  // MODE: 0 mse, 1 prod with a full 128-dim MFMA sketch, 2 prod with a small
+  // (m <= 4) sketch on rotated dims 0..m-1 (SpectralQuant selective QJL).
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* sPiHi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sPiLo = sPiHi + D * LDS_ROW;
+  uint16_t* sSkHi = sPiLo + D * LDS_ROW;
+  uint16_t* sSkLo = sSkHi + D * LDS_ROW;
+  float* sThr = reinterpret_cast<float*>(MODE == 1 ? (uint8_t*)(sSkLo + D * LDS_ROW)
+                                                   : (uint8_t*)sSkHi);
+  float* sCen = sThr + D * kMaxLevels;
+
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.heads, h = bh % a.heads;
+  const int hc = cv.heads > 1 ? int(h) : 0;
+
+  stage_matrix(sPiHi, cv.rot_hi + size_t(hc) * D * D, false);
+  stage_matrix(sPiLo, cv.rot_lo + size_t(hc) * D * D, false);
+  if (MODE == 1) {
+    stage_matrix(sSkHi, cv.sk_hi, true);
+    stage_matrix(sSkLo, cv.sk_lo, true);
+  }
+  if (!UNIFORM) {
+    for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
+      sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
+      sCen[e] = cv.cen[size_t(hc) * D * kMaxLevels + e];
+    }
+  }
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int j = lane & 31, hh = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = (a.tokens + kTile - 1) / kTile;
+  const uint8_t* xbase = static_cast<const uint8_t*>(a.x) +
+                         (b * a.xs_b + h * a.xs_h) * (BF16IN ? 2 : 4);
+  uint8_t* rbase = a.rec + b * a.rs_b + h * a.rs_h;
+
+  constexpr int NSUB = 2 / NB;            // sub-tiles of 32*NB vectors per tile
+  constexpr int NPL = UNIFORM ? UB : 1;   // planes held in the word arrays
+  constexpr int LV = 1 << (UNIFORM ? UB : 1);
+
+  for (int64_t tile = int64_t(blockIdx.x) * 4 + wave; tile < ntiles; tile += int64_t(gridDim.x) * 4) {
+    uint8_t* trec = rbase + tile * cv.tile_bytes;
+    for (int sub = 0; sub < NSUB; ++sub) {
+      // ---------------------------------------------------------- load X
+      u32x4 xh[NB][8], xl[NB][8];
+      float sx[NB], nxv[NB];
+      bool valid[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int slot = sub * 32 * NB + nb * 32 + j;
+        const int64_t t = tile * kTile + slot;
+        valid[nb] = t < a.tokens;
+        float ss = 0.f;
+        if (BF16IN) {
+          const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            u32x4 v = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+            xh[nb][c] = v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+              ss = fmaf(lo, lo, ss);
+              ss = fmaf(hi, hi, ss);
+            }
+          }
+        } else {
+          const float* row = reinterpret_cast<const float*>(xbase) + t * a.xs_t + 64 * hh;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float v[8];
+            if (valid[nb]) {
+              const float4 p0 = *reinterpret_cast<const float4*>(row + 8 * c);
+              const float4 p1 = *reinterpret_cast<const float4*>(row + 8 * c + 4);
+              v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+              v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+            split8(v, xh[nb][c], xl[nb][c]);
+          }
+        }
+        ss += xor32f(ss);
+        nxv[nb] = sqrtf(ss);
+        // A zero vector encodes y = 0: thresholds and residual in unit scale.
+        sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
+      }
+
+      // scaled boundaries / centroids (uniform codec)
+      float T[NB][LV > 1 ? LV - 1 : 1], C[NB][LV];
+      if (UNIFORM) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * sx[nb];
+#pragma unroll
+          for (int k = 0; k < LV; ++k) C[nb][k] = cv.ucen[k] * sx[nb];
+        }
+      }
+
+      uint32_t cw[NB][NPL];      // code words of the current 32-dim block, plane p
+      uint32_t tailw[NB];        // non-uniform row layout: bits beyond plane 0
+      uint32_t sw[NB][4];        // sign words (row layout)
+      float rr[NB];
+      f32x16 z[NB][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        rr[nb] = 0.f;
+        tailw[nb] = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sw[nb][q] = 0;
+          if (MODE == 1) z[nb][q] = f32x16{};
+        }
+      }
+      float zsmall[NB][4];
+      float rsmall[NB][4];
+
+#pragma unroll 1
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int p = 0; p < NPL; ++p) cw[nb][p] = 0;
+        // ------------------------------------------------ rotation block
+        f32x16 acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
+          const u32x4 ah = *reinterpret_cast<const u32x4*>(sPiHi + off);
+          const u32x4 al = *reinterpret_cast<const u32x4*>(sPiLo + off);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            acc[nb] = mfma32(ah, xh[nb][c], acc[nb]);
+            acc[nb] = mfma32(al, xh[nb][c], acc[nb]);
+            if (!BF16IN) acc[nb] = mfma32(ah, xl[nb][c], acc[nb]);
+          }
+        }
+        // ------------------------------------------------ quantize block
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int bit = 8 * (r >> 2) + 4 * hh + (r & 3);  // dim within block
+            const int dim = 32 * mb + bit;
+            const float v = acc[nb][r];
+            int idx = 0;
+            float chat = 0.f;
+            if (UNIFORM) {
+              chat = C[nb][0];
+#pragma unroll
+              for (int k = 0; k < LV - 1; ++k) {
+                const bool ge = v >= T[nb][k];
+                idx += ge ? 1 : 0;
+                chat = ge ? C[nb][k + 1] : chat;
+              }
+            } else {
+              const int L = 1 << cv.dim_bits[dim];
+              chat = sCen[dim * kMaxLevels] * sx[nb];
+              for (int k = 0; k < L - 1; ++k) {
+                const bool ge = v >= sThr[dim * kMaxLevels + k] * sx[nb];
+                idx += ge ? 1 : 0;
+                chat = ge ? sCen[dim * kMaxLevels + k + 1] * sx[nb] : chat;
+              }
+            }
+            if (!valid[nb]) idx = 0;
+            if (!COL) {
+              if (UNIFORM) {
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) cw[nb][p] |= uint32_t((idx >> p) & 1) << bit;
+              } else {
+                cw[nb][0] |= uint32_t(idx & 1) << bit;
+                for (int p = 1; p < kMaxBits; ++p) {
+                  const int pos = cv.bitpos[p * D + dim];
+                  if (pos >= 0) tailw[nb] |= uint32_t((idx >> p) & 1) << (pos - D);
+                }
+              }
+            } else {
+              // col layout: ballot over lanes = vectors; lanes 0..31 carry dim
+              // (32mb + 8(r/4) + r%4), lanes 32..63 the dim 4 higher.
+#pragma unroll
+              for (int p = 0; p < NPL; ++p) {
+                const uint64_t m = __ballot(((idx >> p) & 1) != 0);
+                const int k0 = 8 * (r >> 2) + (r & 3);
+                cw[nb][p] = (lane == k0 ? uint32_t(m) : cw[nb][p]);
+                cw[nb][p] = (lane == k0 + 4 ? uint32_t(m >> 32) : cw[nb][p]);
+              }
+            }
+            const float res = v - chat;
+            if (MODE == 1) {
+              rr[nb] = fmaf(res, res, rr[nb]);
+              acc[nb][r] = res;
+            } else if (MODE == 2) {
+              if (mb == 0 && hh == 0 && r < 4) {
+                rsmall[nb][r] = dim < cv.m ? res : 0.f;
+                if (dim < cv.m) rr[nb] = fmaf(res, res, rr[nb]);
+              }
+            }
+          }
+          if (!COL) {
+            // row layout: the two half-waves hold complementary bits of each word
+            const int slot = sub * 32 * NB + nb * 32 + j;
+#pragma unroll
+            for (int p = 0; p < NPL; ++p) {
+              const uint32_t w = cw[nb][p] | xor32(cw[nb][p]);
+              if (hh == 0) *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
+            }
+          }
+          if (COL) {
+            // store the 32 dims x 32 vectors of this block: lane k < 32 holds dim 32mb+k
+#pragma unroll
+            for (int p = 0; p < NPL; ++p) {
+              if (lane < 32) {
+                uint8_t* w = trec + (size_t(p) * D + 32 * mb + lane) * 8;
+                const uint32_t val = cw[nb][p];
+                const int half = sub * NB + nb;  // which 32-vector half of the 64-bit word
+                *reinterpret_cast<uint32_t*>(w + 4 * half) = val;
+              }
+            }
+          }
+        }
+        // ------------------------------------------------ sketch block
+        if (MODE == 1) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            u32x4 rh[NB], rl[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              float v[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i];
+              split8(v, rh[nb], rl[nb]);
+            }
+            const int chunk = 2 * mb + q;
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms) {
+              const int off = (32 * ms + j) * LDS_ROW + 16 * chunk + 8 * hh;
+              const u32x4 sh = *reinterpret_cast<const u32x4*>(sSkHi + off);
+              const u32x4 sl = *reinterpret_cast<const u32x4*>(sSkLo + off);
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                z[nb][ms] = mfma32(sh, rh[nb], z[nb][ms]);
+                z[nb][ms] = mfma32(sl, rh[nb], z[nb][ms]);
+                z[nb][ms] = mfma32(sh, rl[nb], z[nb][ms]);
+              }
+            }
+          }
+        }
+      }
+
+      // ---------------------------------------------------- signs, norms
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int slot = sub * 32 * NB + nb * 32 + j;
+        if (MODE == 1) {
+          rr[nb] += xor32f(rr[nb]);
+#pragma unroll
+          for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int bit = 8 * (r >> 2) + 4 * hh + (r & 3);
+              const bool s = z[nb][ms][r] >= 0.f && valid[nb];
+              if (!COL) {
+                sw[nb][ms] |= uint32_t(s) << bit;
+              } else {
+                const uint64_t m = __ballot(s);
+                const int k0 = 8 * (r >> 2) + (r & 3);
+                sw[nb][0] = (lane == k0 ? uint32_t(m) : sw[nb][0]);
+                sw[nb][0] = (lane == k0 + 4 ? uint32_t(m >> 32) : sw[nb][0]);
+              }
+            }
+        } else if (MODE == 2) {
+          if (hh == 0) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              if (jj < cv.m) {
+                float zz = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (i < cv.m) zz = fmaf(cv.sketch[jj * cv.m + i], rsmall[nb][i], zz);
+                zsmall[nb][jj] = zz;
+                if (zz >= 0.f && valid[nb]) sw[nb][0] |= 1u << jj;
+              }
+            }
+          }
+        }
+        // combine the two half-waves' bits (row layout)
+        if (!COL) {
+          if (!UNIFORM) tailw[nb] |= xor32(tailw[nb]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sw[nb][q] |= xor32(sw[nb][q]);
+          if (!UNIFORM) {
+            const int tb = cv.code_bytes - 16;  // tail bytes per vector (1..4)
+            if (hh == 0)
+              for (int k = 0; k < tb; ++k)
+                trec[size_t(kTile) * 16 + size_t(slot) * tb + k] = uint8_t(tailw[nb] >> (8 * k));
+          }
+          if (MODE == 1) {
+            uint8_t* dst = trec + cv.off_signs + slot * 16 + 8 * hh;
+            *reinterpret_cast<u32x2*>(dst) = hh ? u32x2{sw[nb][2], sw[nb][3]}
+                                                : u32x2{sw[nb][0], sw[nb][1]};
+          } else if (MODE == 2) {
+            if (hh == 0)
+              for (int k = 0; k < cv.sign_bytes; ++k)
+                trec[cv.off_signs + size_t(slot) * cv.sign_bytes + k] = uint8_t(sw[nb][0] >> (8 * k));
+          }
+        }
+        if (hh == 0) {
+          const float nx = valid[nb] ? nxv[nb] : 0.f;
+          *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nx);
+          if (MODE != 0) {
+            const float nr = valid[nb] ? sqrtf(rr[nb]) / sx[nb] : 0.f;
+            *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = f16_bits(nr);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
+hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
+  auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB>;
+  size_t lds = size_t(2) * D * LDS_ROW * 2;
+  if (MODE == 1) lds += size_t(2) * D * LDS_ROW * 2;
+  if (!UNIFORM) lds += size_t(2) * D * kMaxLevels * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (a.tokens + kTile - 1) / kTile;
+  const int64_t sets = a.batch * a.heads;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  int64_t gx = (ntiles + 3) / 4;
+  const int64_t want = std::max<int64_t>(1, (2 * int64_t(cus) + sets - 1) / sets);
+  gx = std::max<int64_t>(1, std::min(gx, want));
+  const dim3 grid{unsigned(gx), unsigned(sets), 1u};
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, cv, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
+  const bool col = cv.layout == TQ_LAYOUT_COL;
+  if (!cv.uniform) {
+    // SpectralQuant keys: row layout, small sketch
+    if (col || cv.mode != TQ_PROD || cv.m > 4 || !a.x_bf16) return hipErrorNotSupported;
+    return launch_one<2, true, 2, false, false, 1>(cv, a, s);
+  }
+  const int mode = cv.mode == TQ_MSE ? 0 : (cv.m == D ? 1 : 2);
+  if (mode == 2) return hipErrorNotSupported;
+#define TQ_DISPATCH_UB(NB, BF, MODE, COL)                                   \
+  switch (cv.ubits) {                                                       \
+    case 1: return launch_one<NB, BF, MODE, COL, true, 1>(cv, a, s);        \
+    case 2: return launch_one<NB, BF, MODE, COL, true, 2>(cv, a, s);        \
+    case 3: return launch_one<NB, BF, MODE, COL, true, 3>(cv, a, s);        \
+    case 4: return launch_one<NB, BF, MODE, COL, true, 4>(cv, a, s);        \
+    default: return hipErrorNotSupported;                                   \
+  }
+  if (a.x_bf16) {
+    if (mode == 0) { if (col) { TQ_DISPATCH_UB(2, true, 0, true) } else { TQ_DISPATCH_UB(2, true, 0, false) } }
+    else { if (col) return hipErrorNotSupported; TQ_DISPATCH_UB(1, true, 1, false) }
+  } else {
+    if (mode == 0) { if (col) { TQ_DISPATCH_UB(1, false, 0, true) } else { TQ_DISPATCH_UB(1, false, 0, false) } }
+    else { if (col) return hipErrorNotSupported; TQ_DISPATCH_UB(1, false, 1, false) }
+  }
+#undef TQ_DISPATCH_UB
+}
+
+}  // namespace tq

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host builder, the C-ABI layer and the
+// HIP kernels of the codec library.  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kTile = TQ_TILE;
+constexpr int kMaxLevels = TQ_MAX_LEVELS;
+constexpr int kMaxBits = TQ_MAX_BITS;
+
+// ---------------------------------------------------------------- host math
+// Philox4x32-10 (Salmon et al., SC'11) and Box-Muller normals.
+void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+void philox_normals(uint64_t seed, uint32_t stream, int64_t count, double* out);
+
+// Householder QR of a square matrix g (row-major n x n); returns
+// Pi = Q diag(sign(R_ii)) row-major.
+void haar_from_gaussian(int n, const double* g, double* pi);
+
+// Lloyd-Max solution of a symmetric scalar law.
+struct LloydMaxResult {
+  std::vector<double> centroids, boundaries;
+  double mse = 0;
+  int iterations = 0;
+};
+// Law of one coordinate of a uniformly random unit vector in R^d.
+LloydMaxResult lloyd_max_sphere(int d, int bits);
+// Standard normal law.
+LloydMaxResult lloyd_max_gaussian(int bits);
+
+// Symmetric eigendecomposition (cyclic Jacobi).  a: n x n row-major symmetric.
+// Returns eigenvalues descending and eigenvectors as rows (row i <-> lambda_i),
+// each row signed so that its largest-magnitude entry (first on ties) is > 0.
+void symmetric_eigen(int n, const double* a, double* lambda, double* rows);
+
+uint16_t f32_to_bf16_rne(float x);
+float bf16_to_f32(uint16_t h);
+
+// --------------------------------------------------------- kernel parameters
+// Device tables of a codebook.
+struct DeviceTables {
+  float* rot = nullptr;          // [H][d][d] fp32, row i = basis vector i
+  uint16_t* rot_hi = nullptr;    // [H][d][d] bf16 high part
+  uint16_t* rot_lo = nullptr;    // [H][d][d] bf16 residual part
+  float* sketch = nullptr;       // [m][m] fp32
+  uint16_t* sketch_hi = nullptr; // [m][m] bf16
+  uint16_t* sketch_lo = nullptr; // [m][m] bf16
+  float* thr = nullptr;          // [H][d][kMaxLevels] boundaries (unused = +inf)
+  float* cen = nullptr;          // [H][d][kMaxLevels] centroids
+  int16_t* bitpos = nullptr;     // [kMaxBits][d] bit position in the ROW bit string, -1 if absent
+  uint8_t* dim_bits = nullptr;   // [d]
+};
+
+}  // namespace tq
+
+struct tq_codebook {
+  tq_codebook_desc desc{};
+  tq_codebook_info info{};
+  int device = 0;
+  int m = 0;
+  bool uniform = true;
+  int ubits = 0;  // index bits when uniform
+  std::vector<uint8_t> bits;                 // [d]
+  std::vector<double> rot64;                 // [H][d][d] (fp64 before rounding)
+  std::vector<float> rot32;                  // [H][d][d]
+  std::vector<float> sketch32;               // [m][m]
+  std::vector<double> cen64, thr64;          // [H][d][kMaxLevels], [H][d][kMaxLevels-1]
+  std::vector<float> cen32, thr32;           // [H][d][kMaxLevels]
+  std::vector<int16_t> bitpos;               // [kMaxBits][d]
+  tq::DeviceTables dev;
+};

@@ -1,0 +1,84 @@
+// Launch interfaces of the HIP kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+// Everything the kernels read of a codebook, by value.
+struct CodecView {
+  int d, mode, m, layout, uniform, ubits, heads;
+  int code_bytes, sign_bytes, tile_bytes;
+  int off_signs, off_nx, off_nr;
+  int tail_bits;  // ROW, non-uniform: index bits beyond plane 0 (<= 32)
+  const float* rot;
+  const uint16_t* rot_hi;
+  const uint16_t* rot_lo;
+  const float* sketch;
+  const uint16_t* sk_hi;
+  const uint16_t* sk_lo;
+  const float* thr;
+  const float* cen;
+  const int16_t* bitpos;
+  const uint8_t* dim_bits;
+  float uthr[kMaxLevels];
+  float ucen[kMaxLevels];
+};
+
+CodecView make_view(const tq_codebook* cb);
+
+struct EncodeArgs {
+  const void* x;
+  int x_bf16;
+  int64_t batch, heads, tokens, xs_b, xs_h, xs_t;
+  uint8_t* rec;
+  int64_t rs_b, rs_h;
+};
+
+hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s);
+
+// q' = Pi_h q and qs = S q'[0:m] for nq queries; head_of_query maps query ->
+// rotation head (NULL: all head 0; else head = (query / group) % hkv ...).
+struct QueryPrepArgs {
+  const void* q;
+  int q_bf16;
+  int64_t nq;
+  int q_per_head;   // queries sharing one codebook head, consecutive (GQA group); 0 = fixed head
+  int hkv;          // number of KV heads in the cycle (for [B][Hq] layouts)
+  int fixed_head;
+  float* qr;        // [nq][d]
+  float* qs;        // [nq][m]
+};
+hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStream_t s);
+
+hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
+                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s);
+
+struct DecodeArgs {
+  const float* qr;     // [B][Hq][d]
+  const float* qs;     // [B][Hq][mk]
+  int B, Hq, Hkv;
+  const uint8_t* krec;
+  const uint8_t* vrec;
+  int64_t ks_seq, ks_head, vs_seq, vs_head;
+  int max_tokens;
+  const int32_t* seq_lens;
+  float scale;
+  int chunk_tiles;     // tiles per split
+  int nsplit;
+  float* part;         // workspace partials
+  float* out;          // [B][Hq][d]
+};
+hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
+                         hipStream_t s);
+
+hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
+                       const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,
+                       float* ws_scores, float* ws_part_s, int64_t* ws_part_i, int nsplit,
+                       hipStream_t s);
+
+}  // namespace tq

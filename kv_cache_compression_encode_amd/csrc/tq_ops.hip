@@ -1,0 +1,508 @@
+// Query preparation, compressed-key scoring, fused decode attention and top-k
+// search over TurboQuant records (gfx950).
+//
+// Scoring follows the TurboQuant paper review ("Method"): with q' = Pi q and
+// qs = S q'[0:m], a record (idx, signs, n_x, n_r) scores
+//   s = n_x ( sum_i q'_i c_i[idx_i] + n_r sqrt(pi/2)/m sum_j qs_j (2 bit_j - 1) ).
+// Decode attention applies softmax(scale * s) over the tokens of a KV head
+// and accumulates p * n_v * c_v[idx_v] in the rotated value domain; the single
+// inverse rotation Pi_v^T is applied once per query head after the split-K
+// merge (rotation and codebook lookup fused into attention: paper review,
+// "Sparks").
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return float(__builtin_bit_cast(_Float16, h));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ----------------------------------------------------------- query prep
+// Block: up to QB queries; thread i computes rotated coordinates i, i+256, ...
+__global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrepArgs a, int qb) {
+  extern __shared__ float sq[];  // [qb][d]
+  const int d = cv.d;
+  const int64_t q0 = int64_t(blockIdx.x) * qb;
+  const int nqb = int(min<int64_t>(qb, a.nq - q0));
+  for (int e = threadIdx.x; e < nqb * d; e += blockDim.x) {
+    const int64_t qi = q0 + e / d;
+    const int i = e % d;
+    float v;
+    if (a.q_bf16)
+      v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * d + i]) << 16);
+    else
+      v = static_cast<const float*>(a.q)[qi * d + i];
+    sq[e] = v;
+  }
+  __syncthreads();
+  for (int qq = 0; qq < nqb; ++qq) {
+    const int64_t qi = q0 + qq;
+    int head = a.fixed_head;
+    if (a.q_per_head > 0) head = int((qi / a.q_per_head) % a.hkv);
+    if (cv.heads == 1) head = 0;
+    const float* rot = cv.rot + size_t(head) * d * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      const float* row = rot + size_t(i) * d;
+      float acc = 0.f;
+      for (int k = 0; k < d; ++k) acc = fmaf(row[k], sq[qq * d + k], acc);
+      a.qr[qi * d + i] = acc;
+    }
+  }
+  if (cv.mode != TQ_PROD) return;
+  __syncthreads();  // qr of this block visible (global, same block)
+  __threadfence_block();
+  for (int qq = 0; qq < nqb; ++qq) {
+    const int64_t qi = q0 + qq;
+    for (int jrow = threadIdx.x; jrow < cv.m; jrow += blockDim.x) {
+      const float* srow = cv.sketch + size_t(jrow) * cv.m;
+      float acc = 0.f;
+      for (int k = 0; k < cv.m; ++k) acc = fmaf(srow[k], a.qr[qi * d + k], acc);
+      a.qs[qi * cv.m + jrow] = acc;
+    }
+  }
+}
+
+// Index of dim `dim` of the vector in the 16-byte code chunks of a ROW
+// record (uniform codec: plane p occupies bits [p*d, (p+1)*d)).
+__device__ __forceinline__ int row_index_uniform(const uint8_t* tile, int slot, int dim, int d,
+                                                 int ubits) {
+  int idx = 0;
+  for (int p = 0; p < ubits; ++p) {
+    const int bitpos = p * d + dim;
+    const int chunk = bitpos >> 7, inchunk = bitpos & 127;
+    const uint8_t byte = tile[size_t(chunk) * kTile * 16 + size_t(slot) * 16 + (inchunk >> 3)];
+    idx |= ((byte >> (inchunk & 7)) & 1) << p;
+  }
+  return idx;
+}
+
+// ------------------------------------------------------------------ score
+// Block = 4 waves, each wave one record tile (lane = vector); a block of QB
+// queries (q' and qs) in LDS, read as broadcasts.
+template <int QB>
+__global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* qr, const float* qs,
+                                                    int64_t nq, const uint8_t* rec, int64_t n,
+                                                    float* scores) {
+  extern __shared__ float sm[];
+  const int d = cv.d, m = cv.m;
+  float* sqr = sm;                 // [QB][d]
+  float* sqs = sqr + QB * d;       // [QB][m]
+  float* scen = sqs + QB * m;      // [d][kMaxLevels] (non-uniform) or [kMaxLevels]
+  const int64_t q0 = int64_t(blockIdx.y) * QB;
+  const int nqb = int(min<int64_t>(QB, nq - q0));
+  for (int e = threadIdx.x; e < QB * d; e += blockDim.x)
+    sqr[e] = e / d < nqb ? qr[(q0 + e / d) * d + e % d] : 0.f;
+  for (int e = threadIdx.x; e < QB * m; e += blockDim.x)
+    sqs[e] = e / m < nqb ? qs[(q0 + e / m) * m + e % m] : 0.f;
+  const int ncen = cv.uniform ? kMaxLevels : d * kMaxLevels;
+  for (int e = threadIdx.x; e < ncen; e += blockDim.x) scen[e] = cv.uniform ? cv.ucen[e] : cv.cen[e];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tile = int64_t(blockIdx.x) * 4 + wave;
+  const int64_t v = tile * kTile + lane;
+  if (tile * kTile >= n) return;
+  const uint8_t* trec = rec + tile * cv.tile_bytes;
+  float acc[QB], sacc[QB];
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq) acc[qq] = sacc[qq] = 0.f;
+  for (int dim = 0; dim < d; ++dim) {
+    int idx;
+    float c;
+    if (cv.uniform) {
+      idx = row_index_uniform(trec, lane, dim, d, cv.ubits);
+      c = scen[idx];
+    } else {
+      idx = (trec[size_t(lane) * 16 + (dim >> 3)] >> (dim & 7)) & 1;
+      for (int p = 1; p < kMaxBits; ++p) {
+        const int pos = cv.bitpos[p * d + dim];
+        if (pos >= 0) {
+          const int tb = cv.code_bytes - 16, t = pos - d;
+          idx |= ((trec[size_t(kTile) * 16 + size_t(lane) * tb + (t >> 3)] >> (t & 7)) & 1) << p;
+        }
+      }
+      c = scen[dim * kMaxLevels + idx];
+    }
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq) acc[qq] = fmaf(sqr[qq * d + dim], c, acc[qq]);
+  }
+  if (cv.mode == TQ_PROD) {
+    for (int jrow = 0; jrow < m; ++jrow) {
+      int bit;
+      if (m == d || m > 8) {
+        const int chunk = jrow >> 7, in = jrow & 127;
+        const int w = min(16, cv.sign_bytes - chunk * 16);
+        bit = (trec[cv.off_signs + size_t(chunk) * kTile * 16 + size_t(lane) * w + (in >> 3)] >> (in & 7)) & 1;
+      } else {
+        bit = (trec[cv.off_signs + size_t(lane) * cv.sign_bytes + (jrow >> 3)] >> (jrow & 7)) & 1;
+      }
+      const float sgn = bit ? 1.f : -1.f;
+#pragma unroll
+      for (int qq = 0; qq < QB; ++qq) sacc[qq] = fmaf(sqs[qq * m + jrow], sgn, sacc[qq]);
+    }
+  }
+  if (v >= n) return;
+  const float nx = f16_to_f32(*reinterpret_cast<const uint16_t*>(trec + cv.off_nx + 2 * lane));
+  const float nr = cv.mode == TQ_PROD
+                       ? f16_to_f32(*reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * lane))
+                       : 0.f;
+  const float coef = cv.mode == TQ_PROD ? nr * kQjl / float(m) : 0.f;
+#pragma unroll
+  for (int qq = 0; qq < QB; ++qq)
+    if (qq < nqb) scores[(q0 + qq) * n + v] = nx * (acc[qq] + coef * sacc[qq]);
+}
+
+// ------------------------------------------------------------ decode
+constexpr int kMaxG = 8;
+
+// Split-K partial: block (split, kv head g, sequence b), 4 waves each taking
+// tiles of the split in turn.  Partial record per (b, g, split):
+// [G] max, [G] sum, [G][128] accumulator.
+template <int G>
+__global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float sqr[G][D];
+  __shared__ float sqs[G][D];
+  __shared__ float skcen[D * kMaxLevels];
+  __shared__ float svcen[kMaxLevels];
+  __shared__ float spw[4][G][kTile];
+  __shared__ float sm_m[4][G], sm_l[4][G];
+  __shared__ float sacc[4][G][D];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int mk = kc.mode == TQ_PROD ? kc.m : 0;
+  const int hk = kc.heads > 1 ? g : 0, hv = vc.heads > 1 ? g : 0;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int gg = e / D, i = e % D;
+    const int64_t qi = (int64_t(b) * a.Hq + g * G + gg);
+    sqr[gg][i] = a.qr[qi * D + i];
+    sqs[gg][i] = i < mk ? a.qs[qi * mk + i] : 0.f;
+  }
+  if (kc.uniform) {
+    for (int e = threadIdx.x; e < kMaxLevels; e += blockDim.x) skcen[e] = kc.ucen[e];
+  } else {
+    for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x)
+      skcen[e] = kc.cen[size_t(hk) * D * kMaxLevels + e];
+  }
+  for (int e = threadIdx.x; e < kMaxLevels; e += blockDim.x)
+    svcen[e] = vc.uniform ? vc.ucen[e] : vc.cen[size_t(hv) * D * kMaxLevels + e];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
+  const int ntiles = (len + kTile - 1) / kTile;
+  const uint8_t* kbase = a.krec + int64_t(b) * a.ks_seq + int64_t(g) * a.ks_head;
+  const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
+
+  float mrun[G], lrun[G], acc0[G], acc1[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) { mrun[gg] = -INFINITY; lrun[gg] = 0.f; acc0[gg] = acc1[gg] = 0.f; }
+
+  const int t_begin = split * a.chunk_tiles;
+  const int t_end = min(ntiles, t_begin + a.chunk_tiles);
+  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
+    const uint8_t* kt = kbase + int64_t(tile) * kc.tile_bytes;
+    const uint8_t* vt = vbase + int64_t(tile) * vc.tile_bytes;
+    const int tok = tile * kTile + lane;
+    const bool valid = tok < len;
+    // ---- scores (lane = token)
+    float s[G], sg[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) s[gg] = sg[gg] = 0.f;
+    for (int dim = 0; dim < D; ++dim) {
+      int idx;
+      float c;
+      if (kc.uniform) {
+        idx = row_index_uniform(kt, lane, dim, D, kc.ubits);
+        c = skcen[idx];
+      } else {
+        idx = (kt[size_t(lane) * 16 + (dim >> 3)] >> (dim & 7)) & 1;
+        for (int p = 1; p < kMaxBits; ++p) {
+          const int pos = kc.bitpos[p * D + dim];
+          if (pos >= 0) {
+            const int tb = kc.code_bytes - 16, t = pos - D;
+            idx |= ((kt[size_t(kTile) * 16 + size_t(lane) * tb + (t >> 3)] >> (t & 7)) & 1) << p;
+          }
+        }
+        c = skcen[dim * kMaxLevels + idx];
+      }
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) s[gg] = fmaf(sqr[gg][dim], c, s[gg]);
+    }
+    float coef = 0.f;
+    if (kc.mode == TQ_PROD) {
+      for (int jrow = 0; jrow < mk; ++jrow) {
+        int bit;
+        if (mk > 8)
+          bit = (kt[kc.off_signs + size_t(lane) * 16 + (jrow >> 3)] >> (jrow & 7)) & 1;
+        else
+          bit = (kt[kc.off_signs + size_t(lane) * kc.sign_bytes] >> jrow) & 1;
+        const float sgn = bit ? 1.f : -1.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) sg[gg] = fmaf(sqs[gg][jrow], sgn, sg[gg]);
+      }
+      coef = f16_to_f32(*reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * lane)) * kQjl / float(mk);
+    }
+    const float nx = f16_to_f32(*reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * lane));
+    const float nv = f16_to_f32(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * lane));
+    // ---- online softmax
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float logit = valid ? a.scale * nx * (s[gg] + coef * sg[gg]) : -INFINITY;
+      const float mt = wave_max(logit);
+      const float mnew = fmaxf(mrun[gg], mt);
+      const float alpha = mrun[gg] == -INFINITY ? 0.f : __expf(mrun[gg] - mnew);
+      const float p = valid ? __expf(logit - mnew) : 0.f;
+      lrun[gg] = lrun[gg] * alpha + wave_sum(p);
+      acc0[gg] *= alpha;
+      acc1[gg] *= alpha;
+      mrun[gg] = mnew;
+      spw[wave][gg][lane] = p * nv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- values (lane = dims lane, lane + 64; col layout words)
+    uint64_t w0[4], w1[4];
+    const int vb = vc.ubits;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      w0[p] = p < vb ? *reinterpret_cast<const uint64_t*>(vt + (size_t(p) * D + lane) * 8) : 0;
+      w1[p] = p < vb ? *reinterpret_cast<const uint64_t*>(vt + (size_t(p) * D + lane + 64) * 8) : 0;
+    }
+    for (int t = 0; t < kTile; ++t) {
+      int i0 = 0, i1 = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        i0 |= int((w0[p] >> t) & 1) << p;
+        i1 |= int((w1[p] >> t) & 1) << p;
+      }
+      const float c0 = svcen[i0], c1 = svcen[i1];
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        const float w = spw[wave][gg][t];
+        acc0[gg] = fmaf(w, c0, acc0[gg]);
+        acc1[gg] = fmaf(w, c1, acc1[gg]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // ---- merge the 4 waves
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    if (lane == 0) { sm_m[wave][gg] = mrun[gg]; sm_l[wave][gg] = lrun[gg]; }
+    sacc[wave][gg][lane] = acc0[gg];
+    sacc[wave][gg][lane + 64] = acc1[gg];
+  }
+  __syncthreads();
+  float* out = a.part + ((int64_t(b) * a.Hkv + g) * a.nsplit + split) * (G * (2 + D));
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int gg = e / D, i = e % D;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
+    float accv = 0.f, l = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = sm_m[w][gg] == -INFINITY ? 0.f : __expf(sm_m[w][gg] - M);
+      accv += f * sacc[w][gg][i];
+      l += f * sm_l[w][gg];
+    }
+    out[2 * G + gg * D + i] = accv;
+    if (i == 0) { out[gg] = M; out[G + gg] = l; }
+  }
+}
+
+// Merge of the splits and inverse value rotation: block (query head, b).
+template <int G>
+__global__ __launch_bounds__(128) void decode_combine_kernel(CodecView vc, DecodeArgs a) {
+  constexpr int D = 128;
+  __shared__ float sy[D];
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int g = hq / G, gg = hq % G;
+  const float* part = a.part + (int64_t(b) * a.Hkv + g) * a.nsplit * (G * (2 + D));
+  const int i = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * G * (2 + D) + gg]);
+  float accv = 0.f, l = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* ps = part + s * G * (2 + D);
+    const float f = ps[gg] == -INFINITY ? 0.f : __expf(ps[gg] - M);
+    accv += f * ps[2 * G + gg * D + i];
+    l += f * ps[G + gg];
+  }
+  sy[i] = l > 0.f ? accv / l : 0.f;
+  __syncthreads();
+  const int hv = vc.heads > 1 ? g : 0;
+  const float* rot = vc.rot + size_t(hv) * D * D;
+  float o = 0.f;
+  for (int k = 0; k < D; ++k) o = fmaf(rot[k * D + i], sy[k], o);
+  a.out[(int64_t(b) * a.Hq + hq) * D + i] = o;
+}
+
+// ------------------------------------------------------------------ top-k
+constexpr int kTopMax = 16;
+
+__device__ __forceinline__ bool better(float s1, int64_t i1, float s2, int64_t i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// Block (segment, query): per-thread top-16 of a strided subset, then k rounds
+// of a block-wide arg-max over the thread heads.
+__global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, int64_t n, int k,
+                                                           int nseg, float* ps, int64_t* pi) {
+  __shared__ float rs[256];
+  __shared__ int64_t ri[256];
+  __shared__ int rt[256];
+  const int seg = blockIdx.x;
+  const int64_t qi = blockIdx.y;
+  const int64_t per = (n + nseg - 1) / nseg;
+  const int64_t lo = seg * per, hi = min(n, lo + per);
+  float ls[kTopMax];
+  int64_t li[kTopMax];
+#pragma unroll
+  for (int r = 0; r < kTopMax; ++r) { ls[r] = -INFINITY; li[r] = INT64_MAX; }
+  const float* row = scores + qi * n;
+  for (int64_t t = lo + threadIdx.x; t < hi; t += blockDim.x) {
+    float s = row[t];
+    int64_t id = t;
+    if (!better(s, id, ls[kTopMax - 1], li[kTopMax - 1])) continue;
+#pragma unroll
+    for (int r = 0; r < kTopMax; ++r) {
+      if (better(s, id, ls[r], li[r])) {
+        const float ts = ls[r];
+        const int64_t ti = li[r];
+        ls[r] = s; li[r] = id;
+        s = ts; id = ti;
+      }
+    }
+  }
+  int head = 0;
+  for (int round = 0; round < k; ++round) {
+    float hs = -INFINITY;
+    int64_t hid = INT64_MAX;
+#pragma unroll
+    for (int r = 0; r < kTopMax; ++r)
+      if (r == head) { hs = ls[r]; hid = li[r]; }
+    rs[threadIdx.x] = hs; ri[threadIdx.x] = hid; rt[threadIdx.x] = threadIdx.x;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+      if (threadIdx.x < o) {
+        const int a2 = threadIdx.x + o;
+        if (better(rs[a2], ri[a2], rs[threadIdx.x], ri[threadIdx.x])) {
+          rs[threadIdx.x] = rs[a2]; ri[threadIdx.x] = ri[a2]; rt[threadIdx.x] = rt[a2];
+        }
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      ps[(qi * nseg + seg) * k + round] = rs[0];
+      pi[(qi * nseg + seg) * k + round] = ri[0];
+    }
+    if (threadIdx.x == rt[0]) ++head;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* ps, const int64_t* pi,
+                                                        int nseg, int k, float* out_s,
+                                                        int64_t* out_i) {
+  const int64_t qi = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  // segments hold sorted lists; k-way merge by repeated selection
+  int heads[1024];
+  for (int s = 0; s < nseg; ++s) heads[s] = 0;
+  for (int r = 0; r < k; ++r) {
+    int bs = -1;
+    float best_s = -INFINITY;
+    int64_t best_i = INT64_MAX;
+    for (int s = 0; s < nseg; ++s) {
+      if (heads[s] >= k) continue;
+      const float v = ps[(qi * nseg + s) * k + heads[s]];
+      const int64_t id = pi[(qi * nseg + s) * k + heads[s]];
+      if (bs < 0 || better(v, id, best_s, best_i)) { bs = s; best_s = v; best_i = id; }
+    }
+    out_s[qi * k + r] = best_s;
+    out_i[qi * k + r] = best_i;
+    if (bs >= 0) ++heads[bs];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStream_t s) {
+  const int qb = std::max(1, std::min(16, 16384 / cv.d));
+  const unsigned blocks = unsigned((a.nq + qb - 1) / qb);
+  hipLaunchKernelGGL(query_prep_kernel, dim3(blocks), dim3(256), size_t(qb) * cv.d * 4, s, cv, a, qb);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
+                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s) {
+  constexpr int QB = 16;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  dim3 grid(unsigned((ntiles + 3) / 4), unsigned((nq + QB - 1) / QB));
+  const size_t lds = (size_t(QB) * cv.d + size_t(QB) * std::max(cv.m, 1) +
+                      (cv.uniform ? kMaxLevels : size_t(cv.d) * kMaxLevels)) * 4;
+  auto kern = score_kernel<QB>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, cv, qr, qs, nq, rec, n, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
+                         hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
+  switch (G) {
+    case 1: hipLaunchKernelGGL(decode_partial_kernel<1>, grid, dim3(256), 0, s, kv, vv, a); break;
+    case 2: hipLaunchKernelGGL(decode_partial_kernel<2>, grid, dim3(256), 0, s, kv, vv, a); break;
+    case 4: hipLaunchKernelGGL(decode_partial_kernel<4>, grid, dim3(256), 0, s, kv, vv, a); break;
+    case 8: hipLaunchKernelGGL(decode_partial_kernel<8>, grid, dim3(256), 0, s, kv, vv, a); break;
+    default: return hipErrorNotSupported;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(unsigned(a.Hq), unsigned(a.B));
+  switch (G) {
+    case 1: hipLaunchKernelGGL(decode_combine_kernel<1>, g2, dim3(128), 0, s, vv, a); break;
+    case 2: hipLaunchKernelGGL(decode_combine_kernel<2>, g2, dim3(128), 0, s, vv, a); break;
+    case 4: hipLaunchKernelGGL(decode_combine_kernel<4>, g2, dim3(128), 0, s, vv, a); break;
+    case 8: hipLaunchKernelGGL(decode_combine_kernel<8>, g2, dim3(128), 0, s, vv, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
+                       const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,
+                       float* ws_scores, float* ws_part_s, int64_t* ws_part_i, int nsplit,
+                       hipStream_t s) {
+  hipError_t e = launch_score(cv, qr, qs, nq, rec, n, ws_scores, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_segment_kernel, dim3(unsigned(nsplit), unsigned(nq)), dim3(256), 0, s,
+                     ws_scores, n, k, nsplit, ws_part_s, ws_part_i);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(nq)), dim3(64), 0, s, ws_part_s, ws_part_i,
+                     nsplit, k, top_s, top_i);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,214 @@
+"""Parity of the HIP path against the CPU oracle on seeded synthetic inputs
+(MI355X).  Every call goes through the C ABI via the thin binding."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_encode_amd as tq
+import synth
+from oracle import tq_oracle as o
+from tests.parity import check_encoded, check_scores
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def up(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def gpu_records(cb, x, **kw):
+    rec = tq.encode(cb, x.to(DEV), **kw)
+    torch.cuda.synchronize()
+    return rec.cpu().numpy()
+
+
+# ------------------------------------------------ plain TurboQuant-prod, d=128
+@pytest.mark.parametrize("n", [4096, 1, 63, 65, 1000])
+def test_encode_prod_fp32_d128(n):
+    say(f"encode prod b=3 fp32 n={n}")
+    x = synth.iid_gaussian(n, 128, synth.seed(1, "data"))
+    cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=103, seed_sketch=104)
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=103, sketch_seed=104)
+    buf = gpu_records(cb, x)
+    assert len(buf) == cb.records_bytes(n)
+    ref = o.encode(codec, x.double().numpy())
+    got = o.unpack(codec, buf, n)
+    say(check_encoded(codec, ref, got))
+    # slots past n in the last tile are zero
+    assert np.array_equal(o.pack(codec, got), buf)
+
+
+def test_score_prod_d128():
+    say("score 16 x 4096")
+    x = synth.iid_gaussian(4096, 128, synth.seed(1, "data"))
+    q = synth.iid_gaussian(16, 128, synth.seed(1, "queries"))
+    cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=103, seed_sketch=104)
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=103, sketch_seed=104)
+    ref = o.encode(codec, x.double().numpy())
+    s = tq.score(cb, q.to(DEV), up(o.pack(codec, ref)), 4096).cpu().numpy()
+    r = check_scores(s, o.score(codec, q.double().numpy(), ref), q.numpy(), ref.nx)
+    say("max scaled error", r)
+
+
+@pytest.mark.parametrize("bits,mode", [(2, tq.TQ_MSE), (4, tq.TQ_MSE), (2, tq.TQ_PROD), (5, tq.TQ_PROD)])
+def test_encode_and_score_other_bits(bits, mode):
+    say(f"bits={bits} mode={mode}")
+    n = 777
+    x = synth.iid_gaussian(n, 128, 7)
+    q = synth.iid_gaussian(5, 128, 8)
+    mname = "prod" if mode == tq.TQ_PROD else "mse"
+    cb = tq.Codebook(128, mode, bits, seed_rotation=9, seed_sketch=10)
+    codec = o.turboquant_codec(128, bits, mname, rot_seed=9, sketch_seed=10)
+    ref = o.encode(codec, x.double().numpy())
+    say(check_encoded(codec, ref, o.unpack(codec, gpu_records(cb, x), n)))
+    s = tq.score(cb, q.to(DEV), up(o.pack(codec, ref)), n).cpu().numpy()
+    check_scores(s, o.score(codec, q.double().numpy(), ref), q.numpy(), ref.nx)
+
+
+def test_zero_vectors_and_empty():
+    cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=1, seed_sketch=2)
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=1, sketch_seed=2)
+    x = torch.zeros(70, 128)
+    x[5] = 1.0
+    buf = gpu_records(cb, x)
+    got = o.unpack(codec, buf, 70)
+    ref = o.encode(codec, x.double().numpy())
+    assert float(got.nx[0]) == 0.0
+    # y = 0 lies on the middle boundary: codes there are in the band by rule;
+    # the stored record must still score exactly 0
+    s = tq.score(cb, torch.ones(1, 128, device=DEV), torch.from_numpy(buf).to(DEV), 70).cpu().numpy()
+    assert s[0, 0] == 0.0
+    assert np.all(got.nx[[i for i in range(70) if i != 5]] == 0)
+    out = tq.encode(cb, torch.zeros(0, 128, device=DEV), records=torch.zeros(16, dtype=torch.uint8, device=DEV))
+    assert out.shape[0] == 16
+
+
+# --------------------------------------------------------- bf16 KV workload
+def kv_inputs(heads, tokens, seed):
+    law = synth.KVLaw(heads, 128, synth.seed(2, "calibration"))
+    k = synth.kv_cache(1, heads, tokens, 128, seed, law)[0]
+    v = synth.kv_cache(1, heads, tokens, 128, seed + 50, law)[0]
+    return law, k, v
+
+
+def test_encode_kv_bf16():
+    say("kv encode bf16 K prod b=3 row, V mse b=4 col")
+    H, T = 2, 1000
+    law, k, v = kv_inputs(H, T, synth.seed(2, "data"))
+    kcb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204)
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL)
+    kc = o.turboquant_codec(128, 3, "prod", rot_seed=203, sketch_seed=204)
+    vc = o.turboquant_codec(128, 4, "mse", rot_seed=203, layout="col")
+    kb, vb = gpu_records(kcb, k), gpu_records(vcb, v)
+    per_k, per_v = kcb.records_bytes(T), vcb.records_bytes(T)
+    for h in range(H):
+        rk = o.encode(kc, k[h].double().numpy())
+        rv = o.encode(vc, v[h].double().numpy())
+        say("K", check_encoded(kc, rk, o.unpack(kc, kb[h * per_k:(h + 1) * per_k], T)))
+        say("V", check_encoded(vc, rv, o.unpack(vc, vb[h * per_v:(h + 1) * per_v], T)))
+
+
+def _decode_case(B, Hq, Hkv, T, seq_lens=None, sq=False):
+    law = synth.KVLaw(Hkv, 128, 205)
+    K = synth.kv_cache(B, Hkv, T, 128, 201, law)
+    V = synth.kv_cache(B, Hkv, T, 128, 251, law)
+    q = synth.kv_queries(B, Hq, Hkv, 128, 202, law)
+    if sq:
+        calib = torch.stack([law.sample(h, 2048, torch.Generator().manual_seed(405 + h), "cpu")
+                             for h in range(Hkv)])
+        bitmap = [5, 3, 2, 2] + [1] * 124
+        kcb = tq.Codebook(128, tq.TQ_PROD, 0, bitmap=bitmap, qjl_dims=4,
+                          rotation=tq.TQ_ROT_CALIBRATE, num_heads=Hkv, seed_sketch=404, calib=calib)
+        kc = o.spectralquant_codec(calib.float().numpy().astype(np.float64), bitmap, 4, sketch_seed=404)
+    else:
+        kcb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204)
+        kc = o.turboquant_codec(128, 3, "prod", rot_seed=203, sketch_seed=204)
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=207, layout=tq.TQ_LAYOUT_COL)
+    vc = o.turboquant_codec(128, 4, "mse", rot_seed=207, layout="col")
+    kbuf, vbuf, outs = [], [], []
+    ke_all, ve_all = [], []
+    for b in range(B):
+        ke = [o.encode(kc, K[b, g].double().numpy(), head=g if sq else 0) for g in range(Hkv)]
+        ve = [o.encode(vc, V[b, g].double().numpy()) for g in range(Hkv)]
+        ke_all.append(ke)
+        ve_all.append(ve)
+        kbuf += [o.pack(kc, e) for e in ke]
+        vbuf += [o.pack(vc, e) for e in ve]
+    scale = 1 / math.sqrt(128)
+    lens = seq_lens if seq_lens is not None else [T] * B
+    ref = np.zeros((B, Hq, 128))
+    for b in range(B):
+        L_ = lens[b]
+        kk = [o.Encoded(e.idx[:L_], None if e.signs is None else e.signs[:L_], e.nx[:L_],
+                        None if e.nr is None else e.nr[:L_], None, None) for e in ke_all[b]]
+        vv = [o.Encoded(e.idx[:L_], None, e.nx[:L_], None, None, None) for e in ve_all[b]]
+        if L_ > 0:
+            ref[b] = o.decode_attention(kc, vc, q[b].double().numpy(), kk, vv, scale)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV) if seq_lens is not None else None
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), up(np.concatenate(kbuf)), up(np.concatenate(vbuf)),
+                           T, Hkv, scale, seq_lens=sl).cpu().numpy()
+    nvmax = max(float(np.max(e.nx.astype(np.float64))) for ve in ve_all for e in ve)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"decode B={B} Hq={Hq} Hkv={Hkv} T={T} sq={sq}: max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3
+
+
+def test_decode_attend_small():
+    _decode_case(1, 8, 2, 1000)
+
+
+def test_decode_attend_gqa_batch_and_seq_lens():
+    _decode_case(3, 16, 4, 300, seq_lens=[300, 1, 129])
+
+
+def test_decode_attend_spectralquant():
+    _decode_case(2, 8, 2, 500, sq=True)
+
+
+def test_encode_spectralquant():
+    Hkv, T = 2, 700
+    law = synth.KVLaw(Hkv, 128, 405)
+    K = synth.kv_cache(1, Hkv, T, 128, 401, law)[0]
+    calib = torch.stack([law.sample(h, 2048, torch.Generator().manual_seed(405 + h), "cpu")
+                         for h in range(Hkv)])
+    bitmap = [5, 3, 2, 2] + [1] * 124
+    kcb = tq.Codebook(128, tq.TQ_PROD, 0, bitmap=bitmap, qjl_dims=4, rotation=tq.TQ_ROT_CALIBRATE,
+                      num_heads=Hkv, seed_sketch=404, calib=calib)
+    kc = o.spectralquant_codec(calib.float().numpy().astype(np.float64), bitmap, 4, sketch_seed=404)
+    buf = gpu_records(kcb, K)
+    per = kcb.records_bytes(T)
+    for h in range(Hkv):
+        ref = o.encode(kc, K[h].double().numpy(), head=h)
+        say("SQ K", check_encoded(kc, ref, o.unpack(kc, buf[h * per:(h + 1) * per], T)))
+
+
+# ------------------------------------------------------------------- top-k
+def test_search_topk_small():
+    n, d, nq, k = 20000, 128, 8, 10
+    x = synth.iid_gaussian(n, d, 501)
+    x = x / x.norm(dim=1, keepdim=True)
+    q = synth.iid_gaussian(nq, d, 502)
+    cb = tq.Codebook(d, tq.TQ_PROD, 2, seed_rotation=503, seed_sketch=504)
+    codec = o.turboquant_codec(d, 2, "prod", rot_seed=503, sketch_seed=504)
+    ref = o.encode(codec, x.double().numpy())
+    rec = up(o.pack(codec, ref))
+    s, i = tq.search_topk(cb, q.to(DEV), rec, n, k)
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    full = o.score(codec, q.double().numpy(), ref)
+    rs, ri = o.topk(full, k)
+    for r in range(nq):
+        kth = rs[r, -1]
+        near = np.abs(full[r] - kth) <= 1e-3 * np.linalg.norm(q[r].numpy())
+        got_set, ref_set = set(i[r].tolist()), set(ri[r].tolist())
+        diff = got_set ^ ref_set
+        assert all(near[j] for j in diff), f"query {r}: top-k differs beyond near-ties"
+        assert np.all(np.diff(s[r]) <= 0)
