@@ -202,9 +202,12 @@ tq_status build_device(tq_codebook* cb) {
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   const size_t nr = cb->rot32.size();
   std::vector<uint16_t> hi(nr), lo(nr);
+  // fp16 hi + lo parts of 16 Pi (the factor keeps the lo parts normal); the
+  // encode kernel divides it out with the per-vector scale
   for (size_t e = 0; e < nr; ++e) {
-    hi[e] = f32_to_bf16_rne(cb->rot32[e]);
-    lo[e] = f32_to_bf16_rne(cb->rot32[e] - bf16_to_f32(hi[e]));
+    const float v = 16.f * cb->rot32[e];
+    hi[e] = f32_to_f16_rne(v);
+    lo[e] = f32_to_f16_rne(v - f16_to_f32(hi[e]));
   }
   tq_status st;
   if ((st = upload(&cb->dev.rot, cb->rot32.data(), nr)) != TQ_OK) return st;
@@ -214,8 +217,8 @@ tq_status build_device(tq_codebook* cb) {
     const size_t ns = cb->sketch32.size();
     std::vector<uint16_t> shi(ns), slo(ns);
     for (size_t e = 0; e < ns; ++e) {
-      shi[e] = f32_to_bf16_rne(cb->sketch32[e]);
-      slo[e] = f32_to_bf16_rne(cb->sketch32[e] - bf16_to_f32(shi[e]));
+      shi[e] = f32_to_f16_rne(cb->sketch32[e]);
+      slo[e] = f32_to_f16_rne(cb->sketch32[e] - f16_to_f32(shi[e]));
     }
     if ((st = upload(&cb->dev.sketch, cb->sketch32.data(), ns)) != TQ_OK) return st;
     if ((st = upload(&cb->dev.sketch_hi, shi.data(), ns)) != TQ_OK) return st;
@@ -372,10 +375,12 @@ int64_t tq_records_bytes(const tq_codebook* cb, int64_t n) {
 tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
                     int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
                     void* records, int64_t rs_b, int64_t rs_h, void* stream) {
-  if (!cb || !x || !records) return TQ_EINVAL;
+  if (!cb) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
-  if (batch < 0 || heads < 0 || tokens < 0 || xs_b < 0 || xs_h < 0 || xs_t < cb->desc.d)
-    return TQ_EINVAL;
+  if (batch < 0 || heads < 0 || tokens < 0) return TQ_EINVAL;
+  if (batch == 0 || heads == 0 || tokens == 0) return TQ_OK;  // nothing to encode
+  if (!x || !records) return TQ_EINVAL;
+  if (xs_b < 0 || xs_h < 0 || xs_t < cb->desc.d) return TQ_EINVAL;
   if (batch * heads > 65535) return TQ_EUNSUPPORTED;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->info.num_heads > 1 && heads != cb->info.num_heads) return TQ_EINVAL;
@@ -384,7 +389,6 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
   if (!aligned16(x) || !aligned16(records) || (xs_t * esz) % 16 || (xs_h * esz) % 16 ||
       (xs_b * esz) % 16 || rs_b % 16 || rs_h % 16)
     return TQ_EALIGN;
-  if (batch == 0 || heads == 0 || tokens == 0) return TQ_OK;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   EncodeArgs a{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
                static_cast<uint8_t*>(records), rs_b, rs_h};
@@ -416,12 +420,13 @@ size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b
 tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t head,
                    const void* records, int64_t n, float* scores, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  if (!cb || !q || !records || !scores) return TQ_EINVAL;
+  if (!cb) return TQ_EINVAL;
   if (nq < 0 || n < 0 || head < 0 || head >= cb->info.num_heads) return TQ_EINVAL;
+  if (nq == 0 || n == 0) return TQ_OK;
+  if (!q || !records || !scores) return TQ_EINVAL;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d)) return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
-  if (nq == 0 || n == 0) return TQ_OK;
   if (nq > int64_t(65535) * 16) return TQ_EUNSUPPORTED;
   if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0)) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;

@@ -3,9 +3,12 @@
 // One wavefront encodes one 64-vector record tile.  Per tile:
 //   1. 128-bit loads of the input rows (lane = vector, half-wave = 64 coords),
 //      n_x = ||x|| in fp32;
-//   2. rotation Y^T = Pi X^T as 32x32x16 bf16 MFMAs with Pi split into
-//      bf16 hi + lo parts (fp32 inputs are split too), i.e. fp32-accurate y;
-//      Pi hi/lo staged once per workgroup in LDS;
+//   2. rotation Y^T = Pi X^T as 32x32x16 f16 MFMAs: 16 Pi is split into fp16
+//      hi + lo parts (staged once per workgroup in LDS) and each input vector
+//      is scaled by a power of two into the fp16 range (bf16 inputs are then
+//      exact in fp16; fp32 inputs are split into hi + lo too), so y carries
+//      ~2^-22 relative error, well inside the 1e-5 decision band even after
+//      the sketch amplifies it by ||S_j|| ~ sqrt(m);
 //   3. quantize: idx = #{t_k : t_k * n_x <= y_k * n_x} against the Lloyd-Max
 //      boundaries (TurboQuant paper review, "Method"), codes packed as bit
 //      planes (lane-local for the row layout, wavefront ballot for the col
@@ -13,7 +16,8 @@
 //   4. prod: residual r = y - c[idx] kept in the MFMA accumulator layout, which
 //      is exactly the B-operand layout of the next product, so the QJL sketch
 //      Z^T = S R^T runs on MFMA without any transpose (S columns are permuted
-//      once when staged); sign bits = [z >= 0];
+//      once when staged); S and 32 r are split into fp16 hi + lo parts (three
+//      32x32x16 f16 MFMAs, ~2^-22 relative); sign bits = [z >= 0];
 //   5. fp16 norms n_x and n_r = ||r||.
 // The 32x32 accumulator of v_mfma_f32_32x32x16 holds, in lane l and register
 // r, row 8*(r/4) + 4*(l/32) + r%4 and column l%32.
@@ -35,6 +39,32 @@ constexpr int LDS_ROW = D + 8;  // bf16 elements per staged row (16-byte pad)
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+
+__device__ __forceinline__ f32x16 mfma32h(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t f16b(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)x));
+}
+__device__ __forceinline__ float f16v(uint32_t h) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(h)));
+}
+
+// Pack 8 floats into fp16 hi and lo fragments (x ~= hi + lo to ~2^-22).
+__device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = f16b(v[2 * i]), h1 = f16b(v[2 * i + 1]);
+    const uint32_t l0 = f16b(v[2 * i] - f16v(h0));
+    const uint32_t l1 = f16b(v[2 * i + 1] - f16v(h1));
+    hi[i] = h0 | (h1 << 16);
+    lo[i] = l0 | (l1 << 16);
+  }
 }
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
@@ -125,51 +155,68 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
     uint8_t* trec = rbase + tile * cv.tile_bytes;
     for (int sub = 0; sub < NSUB; ++sub) {
       // ---------------------------------------------------------- load X
+      // xh/xl: fp16 hi/lo fragments of x * 2^e, e chosen per vector so that
+      // max|x| * 2^e lies in [2^14, 2^15); w = 16 * 2^e * s_x is the factor
+      // between the accumulator and the rotated unit vector y.
       u32x4 xh[NB][8], xl[NB][8];
-      float sx[NB], nxv[NB];
+      float sx[NB], nxv[NB], wsc[NB];
       bool valid[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int slot = sub * 32 * NB + nb * 32 + j;
         const int64_t t = tile * kTile + slot;
         valid[nb] = t < a.tokens;
-        float ss = 0.f;
+        float ss = 0.f, mx = 0.f;
+        float v[8][8];
         if (BF16IN) {
           const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            u32x4 v = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
-            xh[nb][c] = v;
+            const u32x4 r = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
-              ss = fmaf(lo, lo, ss);
-              ss = fmaf(hi, hi, ss);
+              v[c][2 * i] = __uint_as_float(r[i] << 16);
+              v[c][2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
             }
           }
         } else {
           const float* row = reinterpret_cast<const float*>(xbase) + t * a.xs_t + 64 * hh;
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            float v[8];
             if (valid[nb]) {
               const float4 p0 = *reinterpret_cast<const float4*>(row + 8 * c);
               const float4 p1 = *reinterpret_cast<const float4*>(row + 8 * c + 4);
-              v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-              v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+              v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
+              v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
             } else {
 #pragma unroll
-              for (int i = 0; i < 8; ++i) v[i] = 0.f;
+              for (int i = 0; i < 8; ++i) v[c][i] = 0.f;
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
-            split8(v, xh[nb][c], xl[nb][c]);
           }
         }
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ss = fmaf(v[c][i], v[c][i], ss);
+            mx = fmaxf(mx, fabsf(v[c][i]));
+          }
         ss += xor32f(ss);
+        mx = fmaxf(mx, xor32f(mx));
+        // 2^(14 - floor(log2 mx)) from the exponent field of mx
+        const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+        const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float sc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc[i] = v[c][i] * p2;
+          split8h(sc, xh[nb][c], xl[nb][c]);
+        }
         nxv[nb] = sqrtf(ss);
         // A zero vector encodes y = 0: thresholds and residual in unit scale.
         sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
+        wsc[nb] = 16.f * p2 * sx[nb];
       }
 
       // scaled boundaries / centroids (uniform codec)
@@ -178,9 +225,9 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * sx[nb];
+          for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * wsc[nb];
 #pragma unroll
-          for (int k = 0; k < LV; ++k) C[nb][k] = cv.ucen[k] * sx[nb];
+          for (int k = 0; k < LV; ++k) C[nb][k] = cv.ucen[k] * wsc[nb];
         }
       }
 
@@ -219,9 +266,9 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
           const u32x4 al = *reinterpret_cast<const u32x4*>(sPiLo + off);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            acc[nb] = mfma32(ah, xh[nb][c], acc[nb]);
-            acc[nb] = mfma32(al, xh[nb][c], acc[nb]);
-            if (!BF16IN) acc[nb] = mfma32(ah, xl[nb][c], acc[nb]);
+            acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
+            acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
+            if (!BF16IN) acc[nb] = mfma32h(ah, xl[nb][c], acc[nb]);
           }
         }
         // ------------------------------------------------ quantize block
@@ -244,11 +291,11 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
               }
             } else {
               const int L = 1 << cv.dim_bits[dim];
-              chat = sCen[dim * kMaxLevels] * sx[nb];
+              chat = sCen[dim * kMaxLevels] * wsc[nb];
               for (int k = 0; k < L - 1; ++k) {
-                const bool ge = v >= sThr[dim * kMaxLevels + k] * sx[nb];
+                const bool ge = v >= sThr[dim * kMaxLevels + k] * wsc[nb];
                 idx += ge ? 1 : 0;
-                chat = ge ? sCen[dim * kMaxLevels + k + 1] * sx[nb] : chat;
+                chat = ge ? sCen[dim * kMaxLevels + k + 1] * wsc[nb] : chat;
               }
             }
             if (!valid[nb]) idx = 0;
@@ -314,10 +361,12 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
             u32x4 rh[NB], rl[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
+              // residual in unit-vector scale times 32 keeps both fp16 parts normal
+              const float rs = 32.f / wsc[nb];
               float v[8];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i];
-              split8(v, rh[nb], rl[nb]);
+              for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i] * rs;
+              split8h(v, rh[nb], rl[nb]);
             }
             const int chunk = 2 * mb + q;
 #pragma unroll
@@ -327,9 +376,9 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
               const u32x4 sl = *reinterpret_cast<const u32x4*>(sSkLo + off);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) {
-                z[nb][ms] = mfma32(sh, rh[nb], z[nb][ms]);
-                z[nb][ms] = mfma32(sl, rh[nb], z[nb][ms]);
-                z[nb][ms] = mfma32(sh, rl[nb], z[nb][ms]);
+                z[nb][ms] = mfma32h(sh, rh[nb], z[nb][ms]);
+                z[nb][ms] = mfma32h(sl, rh[nb], z[nb][ms]);
+                z[nb][ms] = mfma32h(sh, rl[nb], z[nb][ms]);
               }
             }
           }
@@ -397,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
           const float nx = valid[nb] ? nxv[nb] : 0.f;
           *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nx);
           if (MODE != 0) {
-            const float nr = valid[nb] ? sqrtf(rr[nb]) / sx[nb] : 0.f;
+            const float nr = valid[nb] ? sqrtf(rr[nb]) / wsc[nb] : 0.f;
             *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = f16_bits(nr);
           }
         }

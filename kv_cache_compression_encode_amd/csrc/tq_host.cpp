@@ -355,6 +355,42 @@ uint16_t f32_to_bf16_rne(float x) {
   return uint16_t(u >> 16);
 }
 
+// IEEE binary16 with round-to-nearest-even (finite inputs; overflow -> inf).
+uint16_t f32_to_f16_rne(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x7f800000u) return uint16_t(sign | 0x7c00u | (a > 0x7f800000u ? 0x200u : 0));
+  const int e = int(a >> 23) - 127;
+  if (e > 15) return uint16_t(sign | 0x7c00u);
+  uint32_t mant = (a & 0x7fffffu) | 0x800000u;  // 24-bit significand
+  int shift;                                     // bits dropped from the 24-bit significand
+  uint32_t expo;
+  if (e >= -14) { shift = 13; expo = uint32_t(e + 15); }
+  else { shift = 13 + (-14 - e); expo = 0; if (shift > 24) return uint16_t(sign); }
+  const uint32_t keep = mant >> shift, rest = mant & ((1u << shift) - 1), half = 1u << (shift - 1);
+  uint32_t r = keep + ((rest > half || (rest == half && (keep & 1))) ? 1 : 0);
+  uint32_t bits;
+  if (expo == 0) bits = r;                                   // subnormal (r may carry into normal)
+  else bits = (expo << 10) + (r - 0x400u);                   // r in [0x400, 0x800]
+  return uint16_t(sign | bits);
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = uint32_t(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1f, m = h & 0x3ff;
+  float v;
+  if (e == 0) v = std::ldexp(float(m), -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = std::ldexp(float(m | 0x400u), int(e) - 25);
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  u |= sign;
+  std::memcpy(&v, &u, 4);
+  return v;
+}
+
 float bf16_to_f32(uint16_t h) {
   const uint32_t u = uint32_t(h) << 16;
   float f;

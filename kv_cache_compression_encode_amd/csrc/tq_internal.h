@@ -40,16 +40,18 @@ void symmetric_eigen(int n, const double* a, double* lambda, double* rows);
 
 uint16_t f32_to_bf16_rne(float x);
 float bf16_to_f32(uint16_t h);
+uint16_t f32_to_f16_rne(float x);
+float f16_to_f32(uint16_t h);
 
 // --------------------------------------------------------- kernel parameters
 // Device tables of a codebook.
 struct DeviceTables {
   float* rot = nullptr;          // [H][d][d] fp32, row i = basis vector i
-  uint16_t* rot_hi = nullptr;    // [H][d][d] bf16 high part
-  uint16_t* rot_lo = nullptr;    // [H][d][d] bf16 residual part
+  uint16_t* rot_hi = nullptr;    // [H][d][d] fp16 high part of 16 Pi
+  uint16_t* rot_lo = nullptr;    // [H][d][d] fp16 residual part of 16 Pi
   float* sketch = nullptr;       // [m][m] fp32
-  uint16_t* sketch_hi = nullptr; // [m][m] bf16
-  uint16_t* sketch_lo = nullptr; // [m][m] bf16
+  uint16_t* sketch_hi = nullptr; // [m][m] fp16 high part
+  uint16_t* sketch_lo = nullptr; // [m][m] fp16 residual part
   float* thr = nullptr;          // [H][d][kMaxLevels] boundaries (unused = +inf)
   float* cen = nullptr;          // [H][d][kMaxLevels] centroids
   int16_t* bitpos = nullptr;     // [kMaxBits][d] bit position in the ROW bit string, -1 if absent

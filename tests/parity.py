@@ -37,7 +37,8 @@ def check_encoded(codec, ref, got, band=BAND):
         ok = ~vflip
         smis = (got.signs != ref.signs) & ok[:, None]
         smis_far = smis & (np.abs(ref.z) >= band)
-        assert not smis_far.any(), f"{int(smis_far.sum())} sign bit(s) differ with |z| >= {band}"
+        assert not smis_far.any(), f"{int(smis_far.sum())} sign bit(s) differ with |z| >= {band}: " \
+                                   f"|z| = {np.abs(ref.z[smis_far])[:5].tolist()}"
         assert np.all(fp16_ulps(got.nr[ok], ref.nr[ok]) <= 1), "n_r differs by more than 1 fp16 ulp"
         stats["band_sign_flips"] = int(smis.sum())
     return stats
