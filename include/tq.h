@@ -40,9 +40,12 @@
  *     C = ceil(B/8) bytes are cut into 16-byte chunks (the last may be
  *     shorter); chunk j of the tile is stored as [64 vectors][width_j] bytes.
  *     Sign bits (bit j = [z_j >= 0]) are packed and chunked the same way.
- *   COL layout (for values, read one coordinate per lane across the tile):
- *     for every plane p and every dim i of that plane, a little-endian 64-bit
- *     word whose bit v is bit p of the index of vector v of the tile.
+ *   COL layout (for values, read one coordinate per lane across the tile;
+ *     uniform codecs only): for every dim i, ascending, a field of 8*b bytes
+ *     holding the b-bit indices of the tile's 64 vectors, vector v at bits
+ *     [b*v, b*v + b) (bit k of the field is bit k mod 8 of byte k div 8); then
+ *     (prod) one little-endian 64-bit word per sketch dim j, bit v = sign bit
+ *     of vector v.
  *   Slots past the last vector of a partly filled tile are written as zero.
  */
 #ifndef TQ_H
@@ -102,7 +105,8 @@ typedef struct tq_codebook tq_codebook;
  *              vectors.
  *   num_heads  rotations held by the codebook (one per KV head for
  *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN); TQ_ROT_HAAR uses 1.
- *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map).
+ *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map;
+ *              the GPU encode writes COL records for 1, 2 or 4 index bits).
  *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1) and S
  *              (stream 2).
  *   device     HIP device ordinal that holds the codebook's tables.

@@ -1,0 +1,297 @@
+// Fused decode attention over a compressed KV cache on MFMA (gfx950), d = 128.
+//
+// Keys: TurboQuant-prod row records with 1 or 2 index bits.  A symmetric
+// Lloyd-Max codebook with 4 levels is exactly linear in the two bit planes
+// written as signs s = 2b - 1:  c(idx) = alpha s1 + beta s0 with
+// alpha = (c3 + c2)/2, beta = (c3 - c2)/2 (2 levels: c(idx) = c1 s0).  So the
+// score of a query against a key,
+//   n_x ( <q', c(idx)> + n_r sqrt(pi/2)/m <qs, sign> ),
+// is one contraction over K = [plane 0 | plane 1 | signs] (3 x 128) of +-1
+// values with the weighted query: a single chain of 16x16x32 f16 MFMAs per 16
+// keys.  Rows 0..7 carry the code part of 4 queries (fp16 hi and lo parts of
+// w_p q'), rows 8..15 the sign part (hi and lo of qs); the +-1 operands are
+// built from the key bits with one shift and one and-or per fp16 pair.
+//
+// Values: TurboQuant-mse col records with 4 index bits: 8 consecutive tokens
+// of one coordinate are one dword; a 256-entry LDS table maps each byte (two
+// tokens) to the fp16 pair of their centroids, giving the B operand of
+// P V_hat directly (P = softmax weights times n_v, fp16, rows = queries).
+//
+// Online softmax per query over 64-token tiles; split-K over tiles with the
+// same partial format as the generic kernel, merged by decode_combine.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;
+constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t f16b(float x) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)x));
+}
+__device__ __forceinline__ float f16v(uint32_t h) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(h)));
+}
+__device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+
+// 8 bits -> 8 fp16 values +1 (bit set) / -1 (bit clear), element k from bit k.
+__device__ __forceinline__ u32x4 expand_pm1(uint32_t byte) {
+  const uint32_t nb = (~byte) & 0xffu;       // sign bit = NOT bit
+  const uint32_t x2 = nb | (nb << 15);       // bit k at k and k + 15
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sp = x2 << (15 - 2 * j);  // bit 2j -> 15, bit 2j+1 -> 31
+    r[j] = (sp & 0x80008000u) | 0x3C003C00u;
+  }
+  return r;
+}
+
+template <int G>
+__device__ __forceinline__ float grp_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float grp_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <int G, int UB>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
+  static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
+  __shared__ float sqr[4][D];
+  __shared__ float sqs[4][D];
+  __shared__ uint32_t slut[256];
+  __shared__ __align__(16) uint16_t sP[4][16][64];  // per wave: [query row][token] fp16 weights
+  __shared__ float sm_m[4][4], sm_l[4][4];
+  __shared__ float sacc[4][4][D];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+    const int gg = e / D, i = e % D;
+    const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
+    sqr[gg][i] = gg < G ? a.qr[qi * D + i] : 0.f;
+    sqs[gg][i] = gg < G ? a.qs[qi * kc.m + i] : 0.f;
+  }
+  {
+    const int t = threadIdx.x;  // 256 threads: one table entry each
+    slut[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+  }
+  for (int e = threadIdx.x; e < 4 * 16 * 64; e += blockDim.x) (&sP[0][0][0])[e] = 0;
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g16 = lane >> 4;
+
+  // ---- score A fragments: chunk (p, c): lane row r = n, dims 32 g16 + 8c + s
+  float wp[2];
+  if (UB == 2) {
+    wp[0] = 0.5f * (kc.ucen[3] - kc.ucen[2]);
+    wp[1] = 0.5f * (kc.ucen[3] + kc.ucen[2]);
+  } else {
+    wp[0] = kc.ucen[1];
+    wp[1] = 0.f;
+  }
+  constexpr int NP = UB + 1;  // planes incl. signs
+  u32x4 A[NP][4];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool sign_part = p == NP - 1;
+      const int r = n;
+      const bool rowsig = r >= 8;
+      const int gq = (r & 7) >> 1, lo = r & 1;
+      float v[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int dim = 32 * g16 + 8 * c + s;
+        float x = 0.f;
+        if (gq < G) {
+          if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
+          if (rowsig && sign_part) x = sqs[gq][dim];
+        }
+        const float hi = f16v(f16b(x));
+        v[s] = lo ? x - hi : x;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) A[p][c][s2] = f16b(v[2 * s2]) | (f16b(v[2 * s2 + 1]) << 16);
+    }
+
+  const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
+  const int ntiles = (len + kTile - 1) / kTile;
+  const uint8_t* kbase = a.krec + int64_t(b) * a.ks_seq + int64_t(g) * a.ks_head;
+  const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
+  const float coef_scale = kQjl / float(kc.m);
+
+  // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  f32x4 accv[8];
+#pragma unroll
+  for (int vb = 0; vb < 8; ++vb) accv[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int t_begin = split * a.chunk_tiles;
+  const int t_end = min(ntiles, t_begin + a.chunk_tiles);
+  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
+    const uint8_t* kt = kbase + int64_t(tile) * kc.tile_bytes;
+    const uint8_t* vt = vbase + int64_t(tile) * vc.tile_bytes;
+    // ---- loads: key planes/signs (dword g16 of token 16nb+n), value fields
+    uint32_t kw[4][NP];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int tok = 16 * nb + n;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int off = p < UB ? p * kTile * 16 : kc.off_signs;
+        kw[nb][p] = *reinterpret_cast<const uint32_t*>(kt + off + tok * 16 + 4 * g16);
+      }
+    }
+    uint32_t vw[8][2];
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2)
+        vw[vb][kc2] = *reinterpret_cast<const uint32_t*>(vt + (16 * vb + n) * 32 + 16 * kc2 + 4 * g16);
+    float nx[4], nr[4], nv[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int tok = 16 * nb + n;
+      nx[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * tok));
+      nr[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * tok));
+      nv[nb] = h2f(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok));
+    }
+    // ---- scores
+    float lg[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc = mfma16(A[p][c], expand_pm1((kw[nb][p] >> (8 * c)) & 0xffu), acc);
+      const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
+      const float sa = __shfl_xor(xa, 32, 64), sb = __shfl_xor(xb, 32, 64);
+      const int tok = tile * kTile + 16 * nb + n;
+      const bool valid = tok < len;
+      const float coef = nr[nb] * coef_scale;
+      lg[nb][0] = valid ? a.scale * nx[nb] * (xa + coef * sa) : -INFINITY;
+      lg[nb][1] = valid ? a.scale * nx[nb] * (xb + coef * sb) : -INFINITY;
+    }
+    // ---- online softmax (lanes of group 0: queries 0,1; group 1: queries 2,3)
+    float alpha[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float mt = fmaxf(fmaxf(lg[0][k], lg[1][k]), fmaxf(lg[2][k], lg[3][k]));
+      mt = grp_max<G>(mt);
+      const float mnew = fmaxf(mrun[k], mt);
+      alpha[k] = mrun[k] == -INFINITY ? 0.f : __expf(mrun[k] - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const float p = mnew == -INFINITY ? 0.f : __expf(lg[nb][k] - mnew);
+        ps += p;
+        const int q = 2 * g16 + k;
+        if (g16 < 2 && q < G) sP[wave][q][16 * nb + n] = uint16_t(f16b(p * nv[nb]));
+      }
+      lrun[k] = lrun[k] * alpha[k] + grp_sum(ps);
+      mrun[k] = mnew;
+    }
+    // rescale: accumulator rows = queries 0..3 in lane group 0
+    const float al01 = alpha[0], al11 = alpha[1];
+    const float al2 = __shfl_xor(al01, 16, 64), al3 = __shfl_xor(al11, 16, 64);
+    __builtin_amdgcn_wave_barrier();
+    // ---- P V_hat
+    u32x4 Ap[2];
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2)
+      Ap[kc2] = *reinterpret_cast<const u32x4*>(&sP[wave][n][32 * kc2 + 8 * g16]);
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      accv[vb][0] *= al01;
+      accv[vb][1] *= al11;
+      accv[vb][2] *= al2;
+      accv[vb][3] *= al3;
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const uint32_t w = vw[vb][kc2];
+        u32x4 B;
+        B[0] = slut[w & 0xffu];
+        B[1] = slut[(w >> 8) & 0xffu];
+        B[2] = slut[(w >> 16) & 0xffu];
+        B[3] = slut[w >> 24];
+        accv[vb] = mfma16(Ap[kc2], B, accv[vb]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // ---- merge the 4 waves: group-0 lanes hold rows (queries) 0..3 of coord 16vb+n
+  if (g16 < 2 && n == 0) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      sm_m[wave][2 * g16 + k] = mrun[k];
+      sm_l[wave][2 * g16 + k] = lrun[k];
+    }
+  }
+  if (g16 == 0) {
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sacc[wave][q][16 * vb + n] = accv[vb][q];
+  }
+  __syncthreads();
+  float* out = a.part + ((int64_t(b) * a.Hkv + g) * a.nsplit + split) * (G * (2 + D));
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int gg = e / D, i = e % D;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
+    float accs = 0.f, l = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = sm_m[w][gg] == -INFINITY ? 0.f : __expf(sm_m[w][gg] - M);
+      accs += f * sacc[w][gg][i];
+      l += f * sm_l[w][gg];
+    }
+    out[2 * G + gg * D + i] = accs;
+    if (i == 0) { out[gg] = M; out[G + gg] = l; }
+  }
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G) {
+  return kv.d == D && vv.d == D && kv.uniform && kv.mode == TQ_PROD && kv.m == D &&
+         kv.layout == TQ_LAYOUT_ROW && (kv.ubits == 1 || kv.ubits == 2) && vv.uniform &&
+         vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL && vv.ubits == 4 &&
+         (G == 1 || G == 2 || G == 4);
+}
+
+hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
+                              hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
+#define TQ_LAUNCH(GG, UU) hipLaunchKernelGGL((decode_mfma_kernel<GG, UU>), grid, dim3(256), 0, s, kv, vv, a)
+  if (kv.ubits == 2) {
+    if (G == 4) TQ_LAUNCH(4, 2); else if (G == 2) TQ_LAUNCH(2, 2); else TQ_LAUNCH(1, 2);
+  } else {
+    if (G == 4) TQ_LAUNCH(4, 1); else if (G == 2) TQ_LAUNCH(2, 1); else TQ_LAUNCH(1, 1);
+  }
+#undef TQ_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace tq

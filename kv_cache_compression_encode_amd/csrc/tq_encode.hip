@@ -11,8 +11,8 @@
 //      the sketch amplifies it by ||S_j|| ~ sqrt(m);
 //   3. quantize: idx = #{t_k : t_k * n_x <= y_k * n_x} against the Lloyd-Max
 //      boundaries (TurboQuant paper review, "Method"), codes packed as bit
-//      planes (lane-local for the row layout, wavefront ballot for the col
-//      layout);
+//      planes (row layout: lane-local bits) or index-major col fields
+//      (lanes OR-ed together by a butterfly, or a wavefront ballot at 1 bit);
 //   4. prod: residual r = y - c[idx] kept in the MFMA accumulator layout, which
 //      is exactly the B-operand layout of the next product, so the QJL sketch
 //      Z^T = S R^T runs on MFMA without any transpose (S columns are permuted
@@ -310,15 +310,24 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
                   if (pos >= 0) tailw[nb] |= uint32_t((idx >> p) & 1) << (pos - D);
                 }
               }
+            } else if (UB == 1) {
+              // col layout, 1 bit: ballot over lanes = vectors; lanes 0..31
+              // carry dim (32mb + 8(r/4) + r%4), lanes 32..63 the dim 4 higher.
+              const uint64_t m = __ballot((idx & 1) != 0);
+              const int k0 = 8 * (r >> 2) + (r & 3);
+              cw[nb][0] = (lane == k0 ? uint32_t(m) : cw[nb][0]);
+              cw[nb][0] = (lane == k0 + 4 ? uint32_t(m >> 32) : cw[nb][0]);
             } else {
-              // col layout: ballot over lanes = vectors; lanes 0..31 carry dim
-              // (32mb + 8(r/4) + r%4), lanes 32..63 the dim 4 higher.
+              // col layout, UB bits: the 32/UB vectors of a dword are OR-ed
+              // together across their lanes (butterfly); the group's first lane
+              // stores the dword of dim `dim`.
+              constexpr int VPD = 32 / UB;
+              uint32_t w = uint32_t(idx) << (UB * (j & (VPD - 1)));
 #pragma unroll
-              for (int p = 0; p < NPL; ++p) {
-                const uint64_t m = __ballot(((idx >> p) & 1) != 0);
-                const int k0 = 8 * (r >> 2) + (r & 3);
-                cw[nb][p] = (lane == k0 ? uint32_t(m) : cw[nb][p]);
-                cw[nb][p] = (lane == k0 + 4 ? uint32_t(m >> 32) : cw[nb][p]);
+              for (int o = 1; o < VPD; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o, 64));
+              if ((j & (VPD - 1)) == 0) {
+                const int word = (sub * NB * 32 + nb * 32 + j) / VPD;
+                *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = w;
               }
             }
             const float res = v - chat;
@@ -341,16 +350,12 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
               if (hh == 0) *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
             }
           }
-          if (COL) {
+          if (COL && UB == 1) {
             // store the 32 dims x 32 vectors of this block: lane k < 32 holds dim 32mb+k
-#pragma unroll
-            for (int p = 0; p < NPL; ++p) {
-              if (lane < 32) {
-                uint8_t* w = trec + (size_t(p) * D + 32 * mb + lane) * 8;
-                const uint32_t val = cw[nb][p];
-                const int half = sub * NB + nb;  // which 32-vector half of the 64-bit word
-                *reinterpret_cast<uint32_t*>(w + 4 * half) = val;
-              }
+            if (lane < 32) {
+              uint8_t* w = trec + (size_t(32) * mb + lane) * 8;
+              const int half = sub * NB + nb;  // which 32-vector half of the 64-bit word
+              *reinterpret_cast<uint32_t*>(w + 4 * half) = cw[nb][0];
             }
           }
         }
@@ -497,6 +502,7 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
     case 4: return launch_one<NB, BF, MODE, COL, true, 4>(cv, a, s);        \
     default: return hipErrorNotSupported;                                   \
   }
+  if (col && cv.ubits == 3) return hipErrorNotSupported;
   if (a.x_bf16) {
     if (mode == 0) { if (col) { TQ_DISPATCH_UB(2, true, 0, true) } else { TQ_DISPATCH_UB(2, true, 0, false) } }
     else { if (col) return hipErrorNotSupported; TQ_DISPATCH_UB(1, true, 1, false) }

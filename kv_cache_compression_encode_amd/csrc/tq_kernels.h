@@ -75,6 +75,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
                          hipStream_t s);
+// MFMA decode partial kernel (d = 128, prod keys with 1-2 index bits and a
+// full sketch, mse values with 4 bits in col layout, 1-4 query heads per KV head).
+bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G);
+hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
+                              hipStream_t s);
 
 hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
                        const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,

@@ -37,10 +37,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ----------------------------------------------------------- query prep
-// Block: up to QB queries; thread i computes rotated coordinates i, i+256, ...
+// Block: qb consecutive queries (same rotation head); q in LDS, thread i
+// computes rotated coordinates i, i + 256, ... for all qb queries, so each
+// Pi element read from L2 serves qb queries; then qs = S q'[0:m] from LDS.
 __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrepArgs a, int qb) {
-  extern __shared__ float sq[];  // [qb][d]
+  extern __shared__ float sq[];  // [qb][d] input, then [qb][d] rotated
   const int d = cv.d;
+  float* sr = sq + qb * d;
   const int64_t q0 = int64_t(blockIdx.x) * qb;
   const int nqb = int(min<int64_t>(qb, a.nq - q0));
   for (int e = threadIdx.x; e < nqb * d; e += blockDim.x) {
@@ -54,30 +57,43 @@ __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrep
     sq[e] = v;
   }
   __syncthreads();
-  for (int qq = 0; qq < nqb; ++qq) {
-    const int64_t qi = q0 + qq;
-    int head = a.fixed_head;
-    if (a.q_per_head > 0) head = int((qi / a.q_per_head) % a.hkv);
-    if (cv.heads == 1) head = 0;
-    const float* rot = cv.rot + size_t(head) * d * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      const float* row = rot + size_t(i) * d;
-      float acc = 0.f;
-      for (int k = 0; k < d; ++k) acc = fmaf(row[k], sq[qq * d + k], acc);
-      a.qr[qi * d + i] = acc;
+  int head = a.fixed_head;
+  if (a.q_per_head > 0) head = int((q0 / a.q_per_head) % a.hkv);
+  if (cv.heads == 1) head = 0;
+  const float* rot = cv.rot + size_t(head) * d * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    const float* row = rot + size_t(i) * d;
+    float acc[8];
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq) acc[qq] = 0.f;
+    for (int k = 0; k < d; k += 4) {
+      const float4 r = *reinterpret_cast<const float4*>(row + k);
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        if (qq < nqb) {
+          const float* x = sq + qq * d + k;
+          acc[qq] = fmaf(r.x, x[0], acc[qq]);
+          acc[qq] = fmaf(r.y, x[1], acc[qq]);
+          acc[qq] = fmaf(r.z, x[2], acc[qq]);
+          acc[qq] = fmaf(r.w, x[3], acc[qq]);
+        }
+      }
     }
+#pragma unroll
+    for (int qq = 0; qq < 8; ++qq)
+      if (qq < nqb) {
+        sr[qq * d + i] = acc[qq];
+        a.qr[(q0 + qq) * d + i] = acc[qq];
+      }
   }
   if (cv.mode != TQ_PROD) return;
-  __syncthreads();  // qr of this block visible (global, same block)
-  __threadfence_block();
-  for (int qq = 0; qq < nqb; ++qq) {
-    const int64_t qi = q0 + qq;
-    for (int jrow = threadIdx.x; jrow < cv.m; jrow += blockDim.x) {
-      const float* srow = cv.sketch + size_t(jrow) * cv.m;
-      float acc = 0.f;
-      for (int k = 0; k < cv.m; ++k) acc = fmaf(srow[k], a.qr[qi * d + k], acc);
-      a.qs[qi * cv.m + jrow] = acc;
-    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nqb * cv.m; e += blockDim.x) {
+    const int qq = e / cv.m, jrow = e % cv.m;
+    const float* srow = cv.sketch + size_t(jrow) * cv.m;
+    float acc = 0.f;
+    for (int k = 0; k < cv.m; ++k) acc = fmaf(srow[k], sr[qq * d + k], acc);
+    a.qs[(q0 + qq) * cv.m + jrow] = acc;
   }
 }
 
@@ -279,21 +295,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
       spw[wave][gg][lane] = p * nv;
     }
     __builtin_amdgcn_wave_barrier();
-    // ---- values (lane = dims lane, lane + 64; col layout words)
-    uint64_t w0[4], w1[4];
+    // ---- values (lane = dims lane, lane + 64; index-major col fields)
     const int vb = vc.ubits;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      w0[p] = p < vb ? *reinterpret_cast<const uint64_t*>(vt + (size_t(p) * D + lane) * 8) : 0;
-      w1[p] = p < vb ? *reinterpret_cast<const uint64_t*>(vt + (size_t(p) * D + lane + 64) * 8) : 0;
-    }
+    const uint8_t* f0 = vt + size_t(lane) * 8 * vb;
+    const uint8_t* f1 = vt + size_t(lane + 64) * 8 * vb;
     for (int t = 0; t < kTile; ++t) {
-      int i0 = 0, i1 = 0;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        i0 |= int((w0[p] >> t) & 1) << p;
-        i1 |= int((w1[p] >> t) & 1) << p;
-      }
+      const int bit = vb * t;
+      const int i0 = int(((uint32_t(f0[bit >> 3]) | (uint32_t(f0[min((bit >> 3) + 1, 8 * vb - 1)]) << 8)) >> (bit & 7)) & ((1u << vb) - 1));
+      const int i1 = int(((uint32_t(f1[bit >> 3]) | (uint32_t(f1[min((bit >> 3) + 1, 8 * vb - 1)]) << 8)) >> (bit & 7)) & ((1u << vb) - 1));
       const float c0 = svcen[i0], c1 = svcen[i1];
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
@@ -446,9 +455,12 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* ps, const i
 }  // namespace
 
 hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStream_t s) {
-  const int qb = std::max(1, std::min(16, 16384 / cv.d));
+  // enough blocks to spread over the chip, up to 8 queries per Pi read
+  int qb = int(std::max<int64_t>(1, std::min<int64_t>(8, a.nq / 512)));
+  if (a.q_per_head > 0) qb = std::min(qb, a.q_per_head);  // one rotation head per block
+  while (qb > 1 && size_t(2) * qb * cv.d * 4 > 64 * 1024) --qb;
   const unsigned blocks = unsigned((a.nq + qb - 1) / qb);
-  hipLaunchKernelGGL(query_prep_kernel, dim3(blocks), dim3(256), size_t(qb) * cv.d * 4, s, cv, a, qb);
+  hipLaunchKernelGGL(query_prep_kernel, dim3(blocks), dim3(256), size_t(2) * qb * cv.d * 4, s, cv, a, qb);
   return hipGetLastError();
 }
 
@@ -471,14 +483,19 @@ hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeA
                          hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
-  switch (G) {
-    case 1: hipLaunchKernelGGL(decode_partial_kernel<1>, grid, dim3(256), 0, s, kv, vv, a); break;
-    case 2: hipLaunchKernelGGL(decode_partial_kernel<2>, grid, dim3(256), 0, s, kv, vv, a); break;
-    case 4: hipLaunchKernelGGL(decode_partial_kernel<4>, grid, dim3(256), 0, s, kv, vv, a); break;
-    case 8: hipLaunchKernelGGL(decode_partial_kernel<8>, grid, dim3(256), 0, s, kv, vv, a); break;
-    default: return hipErrorNotSupported;
+  hipError_t e;
+  if (decode_mfma_supported(kv, vv, G)) {
+    e = launch_decode_mfma(kv, vv, a, s);
+  } else {
+    switch (G) {
+      case 1: hipLaunchKernelGGL(decode_partial_kernel<1>, grid, dim3(256), 0, s, kv, vv, a); break;
+      case 2: hipLaunchKernelGGL(decode_partial_kernel<2>, grid, dim3(256), 0, s, kv, vv, a); break;
+      case 4: hipLaunchKernelGGL(decode_partial_kernel<4>, grid, dim3(256), 0, s, kv, vv, a); break;
+      case 8: hipLaunchKernelGGL(decode_partial_kernel<8>, grid, dim3(256), 0, s, kv, vv, a); break;
+      default: return hipErrorNotSupported;
+    }
+    e = hipGetLastError();
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(unsigned(a.Hq), unsigned(a.B));
   switch (G) {

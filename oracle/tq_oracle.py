@@ -485,9 +485,10 @@ def topk(scores: np.ndarray, k: int):
 #   are cut into 16-byte chunks (the last may be shorter); chunk j of the tile
 #   is stored as [64 vectors][width_j] bytes.  Sign bits (bit j = [z_j >= 0])
 #   are packed and chunked the same way.
-# Col layout: for every plane p and every dim i of that plane, one little-endian
-#   64-bit word whose bit v is bit p of the index of vector v of the tile; then
-#   one 64-bit word per sketch dim j.
+# Col layout (uniform codecs, b index bits): for every dim i, ascending, a field
+#   of 8*b bytes holding the b-bit indices of the tile's 64 vectors, vector v at
+#   bits [b*v, b*v + b) (bit k of the field is bit k mod 8 of byte k div 8);
+#   then one 64-bit word per sketch dim j (bit v = sign bit of vector v).
 # Slots of a partly filled last tile are zero.
 # ---------------------------------------------------------------------------
 TILE = 64
@@ -572,13 +573,14 @@ def pack(codec: Codec, enc: Encoded) -> np.ndarray:
                     fo, _ = fields[f"sign{j}"]
                     buf[base + fo: base + fo + TILE * w] = sbytes[:, o:o + w].reshape(-1)
         else:
-            words = []
-            for p, dims in enumerate(plane_dims(codec.bits)):
-                for i in dims:
-                    words.append(np.packbits(((idx[rows, i] >> p) & 1).astype(np.uint8),
-                                             bitorder="little"))
+            b = int(codec.bits[0])
+            fields_i = []
+            for i in range(codec.d):
+                # bit (b*v + k) of the field = bit k of the index of vector v
+                bits = ((idx[rows, i][:, None] >> np.arange(b)[None, :]) & 1).astype(np.uint8)
+                fields_i.append(np.packbits(bits.reshape(-1), bitorder="little"))
             fo, fl = fields["codes"]
-            buf[base + fo: base + fo + fl] = np.concatenate(words)
+            buf[base + fo: base + fo + fl] = np.concatenate(fields_i)
             if sg is not None:
                 fo, fl = fields["signs"]
                 buf[base + fo: base + fo + fl] = np.concatenate(
@@ -626,13 +628,12 @@ def unpack(codec: Codec, buf: np.ndarray, n: int) -> Encoded:
                     sb[:, o:o + w] = buf[base + fo: base + fo + TILE * w].reshape(TILE, w)
                 sg[rows] = np.unpackbits(sb, axis=1, bitorder="little")[:, :codec.m].astype(bool)
         else:
+            b = int(codec.bits[0])
             fo, fl = fields["codes"]
-            words = buf[base + fo: base + fo + fl].reshape(-1, 8)
-            k = 0
-            for p, dims in enumerate(pdims):
-                for i in dims:
-                    idx[rows, i] |= np.unpackbits(words[k], bitorder="little").astype(np.int64) << p
-                    k += 1
+            per_dim = buf[base + fo: base + fo + fl].reshape(codec.d, 8 * b)
+            for i in range(codec.d):
+                bits = np.unpackbits(per_dim[i], bitorder="little").reshape(TILE, b).astype(np.int64)
+                idx[rows, i] = (bits << np.arange(b)[None, :]).sum(axis=1)
             if sg is not None:
                 fo, fl = fields["signs"]
                 words = buf[base + fo: base + fo + fl].reshape(-1, 8)

@@ -212,3 +212,44 @@ def test_search_topk_small():
         diff = got_set ^ ref_set
         assert all(near[j] for j in diff), f"query {r}: top-k differs beyond near-ties"
         assert np.all(np.diff(s[r]) <= 0)
+
+
+# -------------------------------------------- full-size decode layer (8B GQA)
+def test_gqa_layer_full_size():
+    """One decode layer at its full size: 32 q / 8 kv heads, 32768 tokens."""
+    Hq, Hkv, T = 32, 8, 32768
+    say("full GQA layer: generate")
+    law = synth.KVLaw(Hkv, 128, 205)
+    K = synth.kv_cache(1, Hkv, T, 128, 201, law)[0]
+    V = synth.kv_cache(1, Hkv, T, 128, 251, law)[0]
+    q = synth.kv_queries(1, Hq, Hkv, 128, 202, law)
+    kcb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204)
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL)
+    kc = o.turboquant_codec(128, 3, "prod", rot_seed=203, sketch_seed=204)
+    vc = o.turboquant_codec(128, 4, "mse", rot_seed=203, layout="col")
+    say("full GQA layer: encode parity")
+    kb, vb = gpu_records(kcb, K), gpu_records(vcb, V)
+    per_k, per_v = kcb.records_bytes(T), vcb.records_bytes(T)
+    ke, ve, kp, vp = [], [], [], []
+    tot = {"K": 0, "V": 0}
+    for h in range(Hkv):
+        rk = o.encode(kc, K[h].double().numpy())
+        rv = o.encode(vc, V[h].double().numpy())
+        sk = check_encoded(kc, rk, o.unpack(kc, kb[h * per_k:(h + 1) * per_k], T))
+        sv = check_encoded(vc, rv, o.unpack(vc, vb[h * per_v:(h + 1) * per_v], T))
+        tot["K"] += sk["band_code_flips"] + sk["band_sign_flips"]
+        tot["V"] += sv["band_code_flips"]
+        ke.append(rk)
+        ve.append(rv)
+        kp.append(o.pack(kc, rk))
+        vp.append(o.pack(vc, rv))
+    say("band flips", tot)
+    say("full GQA layer: decode parity")
+    scale = 1 / math.sqrt(128)
+    ref = o.decode_attention(kc, vc, q[0].double().numpy(), ke, ve, scale)
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), up(np.concatenate(kp)), up(np.concatenate(vp)),
+                           T, Hkv, scale).cpu().numpy()[0]
+    nvmax = max(float(np.max(e.nx.astype(np.float64))) for e in ve)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"full layer decode: max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3

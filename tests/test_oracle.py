@@ -268,10 +268,9 @@ def test_layout_worked_example(layout):
         assert list(buf[:4]) == rows[("row", "code0")]
         assert list(buf[128:132]) == rows[("row", "nx")]
     else:
-        words = buf[:128].reshape(16, 8)
-        assert list(words[:8, 0]) == rows[("col", "plane0")]
-        assert list(words[8:, 0]) == rows[("col", "plane1")]
-        assert not words[:, 1:].any()
+        fields = buf[:128].reshape(8, 16)
+        assert list(fields[:, 0]) == rows[("col", "dim_byte0")]
+        assert not fields[:, 1:].any()
         assert list(buf[128:132]) == rows[("col", "nx")]
     back = o.unpack(codec, buf, 2)
     assert np.array_equal(back.idx, idx)
