@@ -241,7 +241,7 @@ tq_status map_hip(hipError_t e) {
 
 int64_t decode_nsplit(int64_t max_tokens) {
   const int64_t ntiles = (max_tokens + kTile - 1) / kTile;
-  return std::max<int64_t>(1, (ntiles + 7) / 8);
+  return std::max<int64_t>(1, (ntiles + 7) / 8);  // <= 1024 for max_tokens <= 512K
 }
 constexpr int kDecodeChunkTiles = 8;
 
@@ -463,7 +463,7 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
       kv->k_stride_head % 16 || kv->v_stride_seq % 16 || kv->v_stride_head % 16 || !aligned16(q))
     return TQ_EALIGN;
   if (B == 0) return TQ_OK;
-  if (B > 65535) return TQ_EUNSUPPORTED;
+  if (B > 65535 || decode_nsplit(kv->max_tokens) > 1024) return TQ_EUNSUPPORTED;
   const int64_t nqt = int64_t(B) * Hq;
   if (!workspace || workspace_bytes < tq_workspace_size(kcb, TQ_OP_DECODE, nqt, kv->max_tokens, Hkv))
     return TQ_EWORKSPACE;

@@ -95,21 +95,86 @@ __device__ __forceinline__ uint16_t f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-// Stage a [128][128] bf16 matrix into LDS rows of LDS_ROW elements; with
+// Stage a [128][128] 16-bit matrix into LDS rows of LDS_ROW elements; with
 // `perm` the column index has bits 2 and 3 swapped (sketch operand order).
+// Each thread keeps its 16-byte loads in flight before storing them.
 __device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool perm) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < D * D / 4; e += blockDim.x) {
-    const int row = e / (D / 4), grp = e % (D / 4);
-    const int col = grp * 4;
-    const int dst = perm ? ((col & ~15) | (((col >> 2) & 1) << 3) | (((col >> 3) & 1) << 2)) : col;
-    const u32x2 v = *reinterpret_cast<const u32x2*>(g + row * D + col);
-    *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + dst) = v;
+  constexpr int CHUNKS = D * D / 8;  // 16-byte chunks
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int base = 0; base < CHUNKS; base += 8 * nt) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * nt + tid;
+      if (e < CHUNKS) v[u] = *reinterpret_cast<const u32x4*>(g + e * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * nt + tid;
+      if (e >= CHUNKS) continue;
+      const int row = e / (D / 8), col = (e % (D / 8)) * 8;
+      if (!perm) {
+        *reinterpret_cast<u32x4*>(lds + row * LDS_ROW + col) = v[u];
+      } else {
+        const int d0 = (col & ~15) | (((col >> 2) & 1) << 3) | (((col >> 3) & 1) << 2);
+        const int d1 = ((col + 4) & ~15) | ((((col + 4) >> 2) & 1) << 3) | ((((col + 4) >> 3) & 1) << 2);
+        *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + d0) = u32x2{v[u][0], v[u][1]};
+        *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + d1) = u32x2{v[u][2], v[u][3]};
+      }
+    }
   }
 }
 
+
+// Index of v among 2^UB Lloyd-Max cells: number of boundaries T[k] <= v, by
+// a binary search of UB compares whose thresholds are picked with selects
+// (ties go to the upper cell).  T holds 2^UB - 1 scaled boundaries.
+typedef float f32x16v __attribute__((ext_vector_type(16)));
+
+// Index of v among 2^UB Lloyd-Max cells: number of boundaries T[k] <= v, by
+// a binary search of UB compares whose thresholds are picked with selects
+// (ties go to the upper cell).  T holds the 2^UB - 1 scaled boundaries in a
+// register vector (a plain array would be indexed through scratch memory).
+template <int UB>
+__device__ __forceinline__ int quant_tree(float v, f32x16v T) {
+  if constexpr (UB == 1) {
+    return v >= T[0] ? 1 : 0;
+  } else if constexpr (UB == 2) {
+    const bool b1 = v >= T[1];
+    const bool b0 = v >= (b1 ? T[2] : T[0]);
+    return (b1 ? 2 : 0) | (b0 ? 1 : 0);
+  } else if constexpr (UB == 3) {
+    const bool b2 = v >= T[3];
+    const bool b1 = v >= (b2 ? T[5] : T[1]);
+    const float t0 = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
+    const bool b0 = v >= t0;
+    return (b2 ? 4 : 0) | (b1 ? 2 : 0) | (b0 ? 1 : 0);
+  } else {
+    static_assert(UB == 4, "1..4 index bits");
+    const bool b3 = v >= T[7];
+    const bool b2 = v >= (b3 ? T[11] : T[3]);
+    const float t1 = b3 ? (b2 ? T[13] : T[9]) : (b2 ? T[5] : T[1]);
+    const bool b1 = v >= t1;
+    const float u0 = b2 ? (b1 ? T[14] : T[12]) : (b1 ? T[10] : T[8]);
+    const float u1 = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
+    const bool b0 = v >= (b3 ? u0 : u1);
+    return (b3 ? 8 : 0) | (b2 ? 4 : 0) | (b1 ? 2 : 0) | (b0 ? 1 : 0);
+  }
+}
+
+// OR across groups of `VPD` consecutive lanes (8 or 16) with DPP moves:
+// quad xor-1, quad xor-2, then half-row / row mirrors.
+template <int VPD>
+__device__ __forceinline__ uint32_t group_or(uint32_t w) {
+  w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  if constexpr (VPD >= 8) w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (VPD >= 16) w |= uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x140, 0xF, 0xF, true)); // row_mirror
+  return w;
+}
+
 template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
-__global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
+__global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
   // MODE: 0 mse, 1 prod with a full 128-dim MFMA sketch, 2 prod with a small
   // (m <= 4) sketch on rotated dims 0..m-1 (SpectralQuant selective QJL).
   extern __shared__ __align__(16) uint8_t smem[];
@@ -151,7 +216,9 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
   constexpr int NPL = UNIFORM ? UB : 1;   // planes held in the word arrays
   constexpr int LV = 1 << (UNIFORM ? UB : 1);
 
-  for (int64_t tile = int64_t(blockIdx.x) * 4 + wave; tile < ntiles; tile += int64_t(gridDim.x) * 4) {
+  const int nwaves = blockDim.x >> 6;
+  for (int64_t tile = int64_t(blockIdx.x) * nwaves + wave; tile < ntiles;
+       tile += int64_t(gridDim.x) * nwaves) {
     uint8_t* trec = rbase + tile * cv.tile_bytes;
     for (int sub = 0; sub < NSUB; ++sub) {
       // ---------------------------------------------------------- load X
@@ -167,20 +234,38 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
         const int64_t t = tile * kTile + slot;
         valid[nb] = t < a.tokens;
         float ss = 0.f, mx = 0.f;
-        float v[8][8];
         if (BF16IN) {
+          // raw bf16 pairs stay packed until the scale is known
           const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
+          u32x4 r[8];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const u32x4 r = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+          for (int c = 0; c < 8; ++c)
+            r[c] = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              v[c][2 * i] = __uint_as_float(r[i] << 16);
-              v[c][2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+              const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
+              ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+              mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
             }
-          }
+          ss += xor32f(ss);
+          mx = fmaxf(mx, xor32f(mx));
+          const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+          const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+          // x * 2^e is exact in fp16 (8 significant bits, exponent in range)
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float lo = __uint_as_float(r[c][i] << 16) * p2;
+              const float hi = __uint_as_float(r[c][i] & 0xffff0000u) * p2;
+              xh[nb][c][i] = f16b(lo) | (f16b(hi) << 16);
+            }
+          wsc[nb] = 16.f * p2;
         } else {
           const float* row = reinterpret_cast<const float*>(xbase) + t * a.xs_t + 64 * hh;
+          float v[8][8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             if (valid[nb]) {
@@ -193,34 +278,36 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
               for (int i = 0; i < 8; ++i) v[c][i] = 0.f;
             }
           }
-        }
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+          for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ss = fmaf(v[c][i], v[c][i], ss);
-            mx = fmaxf(mx, fabsf(v[c][i]));
+            for (int i = 0; i < 8; ++i) {
+              ss = fmaf(v[c][i], v[c][i], ss);
+              mx = fmaxf(mx, fabsf(v[c][i]));
+            }
+          ss += xor32f(ss);
+          mx = fmaxf(mx, xor32f(mx));
+          // 2^(14 - floor(log2 mx)) from the exponent field of mx
+          const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+          const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float sc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sc[i] = v[c][i] * p2;
+            split8h(sc, xh[nb][c], xl[nb][c]);
           }
-        ss += xor32f(ss);
-        mx = fmaxf(mx, xor32f(mx));
-        // 2^(14 - floor(log2 mx)) from the exponent field of mx
-        const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
-        const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float sc[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sc[i] = v[c][i] * p2;
-          split8h(sc, xh[nb][c], xl[nb][c]);
+          wsc[nb] = 16.f * p2;
         }
         nxv[nb] = sqrtf(ss);
         // A zero vector encodes y = 0: thresholds and residual in unit scale.
         sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
-        wsc[nb] = 16.f * p2 * sx[nb];
+        wsc[nb] *= sx[nb];
       }
 
       // scaled boundaries / centroids (uniform codec)
-      float T[NB][LV > 1 ? LV - 1 : 1], C[NB][LV];
+      f32x16v T[NB];
+      float C[NB][LV];
       if (UNIFORM) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -282,12 +369,11 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
             int idx = 0;
             float chat = 0.f;
             if (UNIFORM) {
-              chat = C[nb][0];
+              idx = quant_tree<UB>(v, T[nb]);
+              if (MODE != 0) {
+                chat = C[nb][0];
 #pragma unroll
-              for (int k = 0; k < LV - 1; ++k) {
-                const bool ge = v >= T[nb][k];
-                idx += ge ? 1 : 0;
-                chat = ge ? C[nb][k + 1] : chat;
+                for (int k = 1; k < LV; ++k) chat = idx == k ? C[nb][k] : chat;
               }
             } else {
               const int L = 1 << cv.dim_bits[dim];
@@ -322,9 +408,7 @@ __global__ __launch_bounds__(256, 1) void encode_d128_kernel(CodecView cv, Encod
               // together across their lanes (butterfly); the group's first lane
               // stores the dword of dim `dim`.
               constexpr int VPD = 32 / UB;
-              uint32_t w = uint32_t(idx) << (UB * (j & (VPD - 1)));
-#pragma unroll
-              for (int o = 1; o < VPD; o <<= 1) w |= uint32_t(__shfl_xor(int(w), o, 64));
+              const uint32_t w = group_or<VPD>(uint32_t(idx) << (UB * (j & (VPD - 1))));
               if ((j & (VPD - 1)) == 0) {
                 const int word = (sub * NB * 32 + nb * 32 + j) / VPD;
                 *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = w;
@@ -475,11 +559,12 @@ hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  int64_t gx = (ntiles + 3) / 4;
-  const int64_t want = std::max<int64_t>(1, (2 * int64_t(cus) + sets - 1) / sets);
+  // one 8-wave workgroup per CU (the LDS copy of Pi/S), each looping over tiles
+  int64_t gx = (ntiles + 7) / 8;
+  const int64_t want = std::max<int64_t>(1, (int64_t(cus) + sets - 1) / sets);
   gx = std::max<int64_t>(1, std::min(gx, want));
   const dim3 grid{unsigned(gx), unsigned(sets), 1u};
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, cv, a);
+  hipLaunchKernelGGL(kern, grid, dim3(512), lds, s, cv, a);
   return hipGetLastError();
 }
 
@@ -490,7 +575,7 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
   if (!cv.uniform) {
     // SpectralQuant keys: row layout, small sketch
     if (col || cv.mode != TQ_PROD || cv.m > 4 || !a.x_bf16) return hipErrorNotSupported;
-    return launch_one<2, true, 2, false, false, 1>(cv, a, s);
+    return launch_one<1, true, 2, false, false, 1>(cv, a, s);
   }
   const int mode = cv.mode == TQ_MSE ? 0 : (cv.m == D ? 1 : 2);
   if (mode == 2) return hipErrorNotSupported;

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrep
     float acc[8];
 #pragma unroll
     for (int qq = 0; qq < 8; ++qq) acc[qq] = 0.f;
+#pragma unroll 8
     for (int k = 0; k < d; k += 4) {
       const float4 r = *reinterpret_cast<const float4*>(row + k);
 #pragma unroll
@@ -338,30 +339,65 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
 }
 
 // Merge of the splits and inverse value rotation: block (query head, b).
+// The split weights exp(m_s - M) are formed once in LDS; the accumulator
+// reads are independent loads, unrolled.
 template <int G>
 __global__ __launch_bounds__(128) void decode_combine_kernel(CodecView vc, DecodeArgs a) {
   constexpr int D = 128;
   __shared__ float sy[D];
+  __shared__ float sf[1024];
+  __shared__ float sred[2];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int g = hq / G, gg = hq % G;
-  const float* part = a.part + (int64_t(b) * a.Hkv + g) * a.nsplit * (G * (2 + D));
+  const int stride = G * (2 + D);
+  const float* part = a.part + (int64_t(b) * a.Hkv + g) * a.nsplit * stride;
   const int i = threadIdx.x;
+  const int ns = min(a.nsplit, 1024);
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, part[s * G * (2 + D) + gg]);
-  float accv = 0.f, l = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* ps = part + s * G * (2 + D);
-    const float f = ps[gg] == -INFINITY ? 0.f : __expf(ps[gg] - M);
-    accv += f * ps[2 * G + gg * D + i];
-    l += f * ps[G + gg];
+  for (int s2 = i; s2 < ns; s2 += D) {
+    const float m = part[s2 * stride + gg];
+    sf[s2] = m;
+    M = fmaxf(M, m);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((i & 63) == 0) sred[i >> 6] = M;
+  __syncthreads();
+  M = fmaxf(sred[0], sred[1]);
+  float lpart = 0.f;
+  for (int s2 = i; s2 < ns; s2 += D) {
+    const float f = sf[s2] == -INFINITY ? 0.f : __expf(sf[s2] - M);
+    sf[s2] = f;
+    lpart += f * part[s2 * stride + G + gg];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o, 64);
+  __syncthreads();
+  if ((i & 63) == 0) sred[i >> 6] = lpart;
+  __syncthreads();
+  const float l = sred[0] + sred[1];
+  float accv = 0.f;
+  const float* pa = part + 2 * G + gg * D + i;
+  int s2 = 0;
+  for (; s2 + 8 <= ns; s2 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pa[(s2 + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) accv = fmaf(sf[s2 + u], v[u], accv);
+  }
+  for (; s2 < ns; ++s2) accv = fmaf(sf[s2], pa[s2 * stride], accv);
   sy[i] = l > 0.f ? accv / l : 0.f;
   __syncthreads();
   const int hv = vc.heads > 1 ? g : 0;
   const float* rot = vc.rot + size_t(hv) * D * D;
-  float o = 0.f;
-  for (int k = 0; k < D; ++k) o = fmaf(rot[k * D + i], sy[k], o);
-  a.out[(int64_t(b) * a.Hq + hq) * D + i] = o;
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < D; k += 2) {
+    o0 = fmaf(rot[k * D + i], sy[k], o0);
+    o1 = fmaf(rot[(k + 1) * D + i], sy[k + 1], o1);
+  }
+  a.out[(int64_t(b) * a.Hq + hq) * D + i] = o0 + o1;
 }
 
 // ------------------------------------------------------------------ top-k
