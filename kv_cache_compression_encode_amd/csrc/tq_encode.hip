@@ -217,10 +217,34 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   constexpr int LV = 1 << (UNIFORM ? UB : 1);
 
   const int nwaves = blockDim.x >> 6;
-  for (int64_t tile = int64_t(blockIdx.x) * nwaves + wave; tile < ntiles;
-       tile += int64_t(gridDim.x) * nwaves) {
+  const int64_t tstep = int64_t(gridDim.x) * nwaves;
+  // bf16 input: the raw rows of the next sub-tile are loaded while the
+  // current one is processed (register double buffer).
+  u32x4 pre[NB][8];
+  auto load_raw = [&](int64_t tl, int sb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t t = tl * kTile + sb * 32 * NB + nb * 32 + j;
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
+      const bool ok = tl < ntiles && t < a.tokens;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        pre[nb][c] = ok ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+    }
+  };
+  if (BF16IN) load_raw(int64_t(blockIdx.x) * nwaves + wave, 0);
+  for (int64_t tile = int64_t(blockIdx.x) * nwaves + wave; tile < ntiles; tile += tstep) {
     uint8_t* trec = rbase + tile * cv.tile_bytes;
     for (int sub = 0; sub < NSUB; ++sub) {
+      u32x4 cur[NB][8];
+      if (BF16IN) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) cur[nb][c] = pre[nb][c];
+        if (sub + 1 < NSUB) load_raw(tile, sub + 1);
+        else load_raw(tile + tstep, 0);
+      }
       // ---------------------------------------------------------- load X
       // xh/xl: fp16 hi/lo fragments of x * 2^e, e chosen per vector so that
       // max|x| * 2^e lies in [2^14, 2^15); w = 16 * 2^e * s_x is the factor
@@ -235,12 +259,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         valid[nb] = t < a.tokens;
         float ss = 0.f, mx = 0.f;
         if (BF16IN) {
-          // raw bf16 pairs stay packed until the scale is known
-          const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
-          u32x4 r[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c)
-            r[c] = valid[nb] ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+          // raw bf16 pairs (prefetched) stay packed until the scale is known
+          const u32x4* r = cur[nb];
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -343,9 +363,11 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
           for (int p = 0; p < NPL; ++p) cw[nb][p] = 0;
         // ------------------------------------------------ rotation block
-        f32x16 acc[NB];
+        // with one 32-vector block the Pi hi and Pi lo products go to two
+        // independent accumulator chains
+        f32x16 acc[NB], acc2[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = acc2[nb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
@@ -354,11 +376,17 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
-            acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
-            if (!BF16IN) acc[nb] = mfma32h(ah, xl[nb][c], acc[nb]);
+            if (NB == 1) acc2[nb] = mfma32h(al, xh[nb][c], acc2[nb]);
+            else acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
+            if (!BF16IN) acc2[nb] = mfma32h(ah, xl[nb][c], acc2[nb]);
           }
         }
+        if (NB == 1 || !BF16IN) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) acc[nb] += acc2[nb];
+        }
         // ------------------------------------------------ quantize block
+        uint32_t colkeep[NB][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -371,9 +399,17 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             if (UNIFORM) {
               idx = quant_tree<UB>(v, T[nb]);
               if (MODE != 0) {
-                chat = C[nb][0];
+                // select tree over the centroids driven by the index bits
+                float lvl[LV];
 #pragma unroll
-                for (int k = 1; k < LV; ++k) chat = idx == k ? C[nb][k] : chat;
+                for (int k = 0; k < LV; ++k) lvl[k] = C[nb][k];
+#pragma unroll
+                for (int bt = 0; bt < UB; ++bt) {
+                  const bool on = (idx >> bt) & 1;
+#pragma unroll
+                  for (int k = 0; k < (LV >> (bt + 1)); ++k) lvl[k] = on ? lvl[2 * k + 1] : lvl[2 * k];
+                }
+                chat = lvl[0];
               }
             } else {
               const int L = 1 << cv.dim_bits[dim];
@@ -405,14 +441,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               cw[nb][0] = (lane == k0 + 4 ? uint32_t(m >> 32) : cw[nb][0]);
             } else {
               // col layout, UB bits: the 32/UB vectors of a dword are OR-ed
-              // together across their lanes (butterfly); the group's first lane
-              // stores the dword of dim `dim`.
+              // together across their lanes (DPP butterfly); lane j of the
+              // group keeps the dword of register r with r % VPD == j % VPD,
+              // stored after the block.
               constexpr int VPD = 32 / UB;
               const uint32_t w = group_or<VPD>(uint32_t(idx) << (UB * (j & (VPD - 1))));
-              if ((j & (VPD - 1)) == 0) {
-                const int word = (sub * NB * 32 + nb * 32 + j) / VPD;
-                *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = w;
-              }
+              if ((r % VPD) == (j & (VPD - 1))) colkeep[nb][r / VPD] = w;
             }
             const float res = v - chat;
             if (MODE == 1) {
@@ -432,6 +466,18 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             for (int p = 0; p < NPL; ++p) {
               const uint32_t w = cw[nb][p] | xor32(cw[nb][p]);
               if (hh == 0) *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
+            }
+          }
+          if (COL && UB > 1) {
+            // lane j holds, for r = k*VPD + (j % VPD), the dword of dim
+            // 32mb + 8(r/4) + 4hh + r%4 covering vectors (j / VPD)*VPD ..
+            constexpr int VPD = 32 / UB;
+#pragma unroll
+            for (int k = 0; k < 16 / VPD; ++k) {
+              const int r = k * VPD + (j & (VPD - 1));
+              const int dim = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const int word = (sub * NB * 32 + nb * 32 + j) / VPD;
+              *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = colkeep[nb][k];
             }
           }
           if (COL && UB == 1) {
