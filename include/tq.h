@@ -169,11 +169,14 @@ int64_t tq_records_bytes(const tq_codebook* cb, int64_t n);
  *   records  device; the tiles of set (b, h) start at
  *            records + b*rs_b + h*rs_h bytes (16-byte aligned) and hold
  *            ceil(tokens/64) tiles.
- * Supported: d = 128 (any codec) and d multiple of 128 up to 4096 with a
- * uniform ROW codec. */
+ *   workspace device scratch of tq_workspace_size(cb, TQ_OP_ENCODE, 0, 0, 0)
+ *            bytes (0 for d = 128: may be NULL).
+ * Supported: d = 128 (fused kernel, any codec) and d a multiple of 128 up to
+ * 4096 with a uniform ROW codec (GEMM-based path, rows in chunks). */
 tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
                     int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
-                    void* records, int64_t rs_b, int64_t rs_h, void* stream);
+                    void* records, int64_t rs_b, int64_t rs_h, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Inner-product scores of nq queries against n ROW records of head `head`:
  *   scores[i][t] = n_x (sum_j q'_j c[idx_j] + n_r sqrt(pi/2)/m sum_j qs_j (2 bit_j - 1)),
@@ -213,16 +216,19 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
 /* Top-k inner-product search over n ROW records ([TQ] "Validation": vector
  * search with TurboQuant codes).  For each query the k largest scores
  * (as tq_score), descending; equal scores go to the smaller id.
- *   top_scores device fp32 [nq][k]; top_ids device int64 [nq][k]; 1 <= k <= 64.
+ *   top_scores device fp32 [nq][k]; top_ids device int64 [nq][k]; 1 <= k <= 16.
  *   workspace >= tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k). */
 tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
                          const void* records, int64_t n, int32_t k, float* top_scores,
                          int64_t* top_ids, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-enum { TQ_OP_SCORE = 0, TQ_OP_DECODE = 1, TQ_OP_TOPK = 2 };
+enum { TQ_OP_SCORE = 0, TQ_OP_DECODE = 1, TQ_OP_TOPK = 2, TQ_OP_ENCODE = 3 };
 
-/* Device workspace bytes an operation needs (0 on bad arguments). */
+/* Device workspace bytes an operation needs (0 on bad arguments or when none
+ * is needed):  TQ_OP_SCORE (a = nq, b = n), TQ_OP_DECODE (a = B*Hq,
+ * b = max_tokens, c = Hkv), TQ_OP_TOPK (a = nq, b = n, c = k),
+ * TQ_OP_ENCODE (no size arguments). */
 size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b, int64_t c);
 
 const char* tq_status_string(tq_status s);

@@ -133,8 +133,12 @@ def encode(cb: Codebook, x: torch.Tensor, records: Optional[torch.Tensor] = None
     if records is None:
         records = torch.empty(B * H * per, dtype=torch.uint8, device=x.device)
     s = x4.stride()
+    ws_bytes = cb.workspace(L.TQ_OP_ENCODE, 0, 0)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device) if ws_bytes else None
     L.check(L.lib().tq_encode(cb.handle, x4.data_ptr(), _dtype_code(x4), B, H, T, s[0], s[1], s[2],
-                              records.data_ptr(), H * per, per, _stream(x.device)), "tq_encode")
+                              records.data_ptr(), H * per, per,
+                              ws.data_ptr() if ws is not None else None, ws_bytes,
+                              _stream(x.device)), "tq_encode")
     return records
 
 

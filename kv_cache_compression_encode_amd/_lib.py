@@ -11,7 +11,7 @@ TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16 = 0, 1
 TQ_ROT_HAAR, TQ_ROT_GIVEN, TQ_ROT_CALIBRATE = 0, 1, 2
 TQ_LAYOUT_ROW, TQ_LAYOUT_COL = 0, 1
-TQ_OP_SCORE, TQ_OP_DECODE, TQ_OP_TOPK = 0, 1, 2
+TQ_OP_SCORE, TQ_OP_DECODE, TQ_OP_TOPK, TQ_OP_ENCODE = 0, 1, 2, 3
 TQ_TILE = 64
 TQ_MAX_LEVELS = 32
 
@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
     L.tq_codebook_export.restype = i32
     L.tq_records_bytes.argtypes = [p, i64]
     L.tq_records_bytes.restype = i64
-    L.tq_encode.argtypes = [p, p, i32, i64, i64, i64, i64, i64, i64, p, i64, i64, p]
+    L.tq_encode.argtypes = [p, p, i32, i64, i64, i64, i64, i64, i64, p, i64, i64, p, sz, p]
     L.tq_encode.restype = i32
     L.tq_score.argtypes = [p, p, i64, i32, p, i64, p, p, sz, p]
     L.tq_score.restype = i32

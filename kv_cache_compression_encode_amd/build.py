@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_encode.hip", "tq_ops.hip", "tq_decode.hip"]
+SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_encode.hip", "tq_ops.hip", "tq_decode.hip", "tq_large.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # no packed-fp32 instructions in device code
@@ -38,7 +38,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for p in procs:
         _wait(p)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

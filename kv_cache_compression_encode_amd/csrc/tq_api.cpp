@@ -246,7 +246,10 @@ int64_t decode_nsplit(int64_t max_tokens) {
 constexpr int kDecodeChunkTiles = 8;
 
 int64_t topk_nseg(int64_t n) {
-  return std::max<int64_t>(1, std::min<int64_t>(1024, (n + 4095) / 4096));
+  // one partial list per 4096 keys (whole key chunks of the wide-vector path)
+  const int64_t per_chunk = (large_score_chunk() + 4095) / 4096;
+  const int64_t chunks = (n + large_score_chunk() - 1) / large_score_chunk();
+  return std::max<int64_t>(1, std::min<int64_t>(1024, std::max((n + 4095) / 4096, chunks * per_chunk)));
 }
 
 bool supported_query_d(int d) { return d % 64 == 0 && d >= 64 && d <= 4096; }
@@ -374,7 +377,8 @@ int64_t tq_records_bytes(const tq_codebook* cb, int64_t n) {
 
 tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
                     int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
-                    void* records, int64_t rs_b, int64_t rs_h, void* stream) {
+                    void* records, int64_t rs_b, int64_t rs_h, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if (!cb) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
   if (batch < 0 || heads < 0 || tokens < 0) return TQ_EINVAL;
@@ -384,24 +388,37 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
   if (batch * heads > 65535) return TQ_EUNSUPPORTED;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->info.num_heads > 1 && heads != cb->info.num_heads) return TQ_EINVAL;
-  if (cb->desc.d != 128) return TQ_EUNSUPPORTED;
+  const int d = cb->desc.d;
+  const bool large = d != 128;
+  if (large && (d % 128 || d > 4096 || !cb->uniform || cb->desc.layout != TQ_LAYOUT_ROW ||
+                (cb->desc.mode == TQ_PROD && cb->m != d)))
+    return TQ_EUNSUPPORTED;
   const int64_t esz = x_dtype == TQ_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(records) || (xs_t * esz) % 16 || (xs_h * esz) % 16 ||
       (xs_b * esz) % 16 || rs_b % 16 || rs_h % 16)
     return TQ_EALIGN;
+  const size_t need = tq_workspace_size(cb, TQ_OP_ENCODE, 0, 0, 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_EWORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return TQ_EALIGN;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   EncodeArgs a{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
                static_cast<uint8_t*>(records), rs_b, rs_h};
-  return map_hip(launch_encode_d128(make_view(cb), a, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (large) return map_hip(launch_encode_large(cb->device, make_view(cb), a, workspace, s));
+  return map_hip(launch_encode_d128(make_view(cb), a, s));
 }
 
 size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b, int64_t c) {
   if (!cb || a < 0 || b < 0) return 0;
   const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
   const size_t qprep = size_t(a) * (d + m) * 4;
+  const bool large = cb->desc.d != 128;
   auto round = [](size_t v) { return (v + 255) & ~size_t(255); };
   switch (op) {
-    case TQ_OP_SCORE: return round(qprep);
+    case TQ_OP_ENCODE:
+      return large ? large_encode_workspace(make_view(cb)) : 0;
+    case TQ_OP_SCORE:
+      return round(qprep) + (large ? large_score_workspace(make_view(cb), a) : 0);
     case TQ_OP_DECODE: {
       if (c <= 0) return 0;
       const size_t part = size_t(a) * size_t(decode_nsplit(b)) * (2 + d) * 4;
@@ -409,8 +426,8 @@ size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b
     }
     case TQ_OP_TOPK: {
       if (c <= 0 || c > 16) return 0;
-      const size_t sc = size_t(a) * size_t(b) * 4;
       const size_t ps = size_t(a) * size_t(topk_nseg(b)) * size_t(c);
+      const size_t sc = large ? large_score_workspace(make_view(cb), a) : size_t(a) * size_t(b) * 4;
       return round(qprep) + round(sc) + round(ps * 4) + round(ps * 8);
     }
   }
@@ -426,6 +443,8 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   if (!q || !records || !scores) return TQ_EINVAL;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d)) return TQ_EUNSUPPORTED;
+  if (cb->desc.d != 128 && (cb->desc.d % 128 || !cb->uniform || (cb->desc.mode == TQ_PROD && cb->m != cb->desc.d)))
+    return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
   if (nq > int64_t(65535) * 16) return TQ_EUNSUPPORTED;
   if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0)) return TQ_EWORKSPACE;
@@ -438,6 +457,11 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
   tq_status st = map_hip(launch_query_prep(cv, qa, s));
   if (st != TQ_OK) return st;
+  if (cb->desc.d != 128) {
+    void* lw = static_cast<uint8_t*>(workspace) + ((size_t(nq) * (cb->desc.d + std::max(cb->m, 1)) * 4 + 255) & ~size_t(255));
+    return map_hip(launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
+                                      scores, lw, s, nullptr, nullptr));
+  }
   return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s));
 }
 
@@ -527,7 +551,7 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   float* qs = qr + nq * d;
   w += round(size_t(nq) * (d + m) * 4);
   float* sc = reinterpret_cast<float*>(w);
-  w += round(size_t(nq) * size_t(n) * 4);
+  w += round(cb->desc.d != 128 ? large_score_workspace(cv, nq) : size_t(nq) * size_t(n) * 4);
   const int nseg = int(topk_nseg(n));
   const size_t ps = size_t(nq) * nseg * k;
   float* pss = reinterpret_cast<float*>(w);
@@ -536,6 +560,27 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
   tq_status st = map_hip(launch_query_prep(cv, qa, s));
   if (st != TQ_OK) return st;
+  if (cb->desc.d != 128) {
+    // key chunks of large_score_chunk() rows, each cut into segments of up
+    // to 4096 keys; the partial lists of all chunks are merged at the end
+    struct Ctx { int64_t nq; int k; int per_chunk; int total; float* ps; int64_t* pi; };
+    const int per_chunk = int((large_score_chunk() + 4095) / 4096);
+    const int64_t nchunks = (n + large_score_chunk() - 1) / large_score_chunk();
+    Ctx ctx{nq, k, per_chunk, int(nchunks * per_chunk), pss, psi};
+    if (ctx.total > nseg) return TQ_EUNSUPPORTED;
+    ChunkFn fn = [](void* c, const float* scores, int64_t ld, int64_t r0, int64_t rows,
+                    hipStream_t st2) -> hipError_t {
+      // segments of a short last chunk that get no columns emit -inf entries
+      Ctx* x = static_cast<Ctx*>(c);
+      const int seg_base = int(r0 / large_score_chunk()) * x->per_chunk;
+      return launch_topk_segments(scores, ld, rows, r0, x->nq, x->k, x->per_chunk, seg_base, x->total,
+                                  x->ps, x->pi, st2);
+    };
+    hipError_t e = launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
+                                      nullptr, sc, s, fn, &ctx);
+    if (e != hipSuccess) return map_hip(e);
+    return map_hip(launch_topk_merge(pss, psi, nq, ctx.total, k, top_scores, top_ids, s));
+  }
   return map_hip(launch_topk(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, k, top_scores,
                              top_ids, sc, pss, psi, nseg, s));
 }

@@ -1,0 +1,387 @@
+// TurboQuant encode and scoring for wide vectors (d a multiple of 128, e.g.
+// the 1536-dim vector-search workload).  At this width the rotation
+// Y = X Pi^T, the QJL sketch Z = R S^T and the scoring Q' K_hat^T are plain
+// dense GEMMs over whole rows, so they run as rocBLAS GEMMs on fp16 hi/lo
+// operand splits with fp32 accumulation (fp32-accurate results); the
+// per-element steps in between are the kernels below:
+//   rowprep   : n_x, per-row power-of-two scale, fp16 hi/lo split of x;
+//   quantize  : Lloyd-Max index per coordinate (TurboQuant paper review,
+//               "Method"), row-layout bit planes, residual r = y - c[idx]
+//               split into fp16 hi/lo for the sketch GEMM, ||r||^2;
+//   signpack  : sign bits [z >= 0] and the fp16 norms;
+//   dequant   : c[idx] (fp16) and +-1 signs of stored records, for scoring;
+//   combine   : s = n_x (code + n_r sqrt(pi/2)/m sign) from the GEMM parts.
+// Rows are processed in chunks so the workspace stays bounded.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "tq_kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
+
+__device__ __forceinline__ uint16_t f16b(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16v(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
+
+// One wave per row: n_x, scale 2^e putting max|x| in [2^14, 2^15), and the
+// fp16 hi/lo parts of x * 2^e.  w[row] = 16 * 2^e * s_x relates the GEMM
+// output (with 16 Pi) to the rotated unit vector; nx[row] = ||x||.
+__global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16, int64_t ld,
+                                                      int64_t rows, int d, uint16_t* xh,
+                                                      uint16_t* xl, float* w, float* nx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  auto at = [&](int i) -> float {
+    if (x_bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[row * ld + i]) << 16);
+    return static_cast<const float*>(x)[row * ld + i];
+  };
+  float ss = 0.f, mx = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    const float v = at(i);
+    ss = fmaf(v, v, ss);
+    mx = fmaxf(mx, fabsf(v));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ss += __shfl_xor(ss, o, 64);
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
+  const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+  const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+  for (int i = lane; i < d; i += 64) {
+    const float v = at(i) * p2;
+    const uint16_t h = f16b(v);
+    xh[row * d + i] = h;
+    xl[row * d + i] = f16b(v - f16v(h));
+  }
+  if (lane == 0) {
+    const float n = sqrtf(ss);
+    nx[row] = n;
+    w[row] = 16.f * p2 * (n > 0.f ? n : 1.f);
+  }
+}
+
+// Thread per (row, 32-coordinate word).  Rows >= rows_valid (padding of the
+// last tile) get zero records.
+__global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float* y, const float* w,
+                                                       const float* nx, int64_t row0, int64_t rows,
+                                                       int64_t rows_valid, uint8_t* rec, uint16_t* rh,
+                                                       uint16_t* rl, float* rr) {
+  const int d = cv.d, words = d / 32;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / words;
+  const int wd = int(gid % words);
+  if (row >= rows) return;
+  const int64_t grow = row0 + row;  // row within the whole call
+  const int64_t tile = grow / kTile;
+  const int slot = int(grow % kTile);
+  uint8_t* trec = rec + tile * cv.tile_bytes;
+  const bool valid = row < rows_valid;
+  const int ub = cv.ubits;
+  uint32_t planes[kMaxBits] = {0, 0, 0, 0, 0};
+  float rsum = 0.f;
+  if (valid) {
+    const float wr = w[row];
+    const float inv = 1.f / wr;
+    const float* yr = y + row * d + 32 * wd;
+    for (int k = 0; k < 32; ++k) {
+      const float v = yr[k];
+      int idx = 0;
+      for (int t = 0; t < (1 << ub) - 1; ++t) idx += v >= cv.uthr[t] * wr ? 1 : 0;
+      for (int p = 0; p < ub; ++p) planes[p] |= uint32_t((idx >> p) & 1) << k;
+      if (cv.mode == TQ_PROD) {
+        const int dim = 32 * wd + k;
+        const float r = v * inv - cv.ucen[idx];
+        if (dim < cv.m) {
+          rsum = fmaf(r, r, rsum);
+          const float rs = 32.f * r;
+          const uint16_t h = f16b(rs);
+          rh[row * cv.m + dim] = h;
+          rl[row * cv.m + dim] = f16b(rs - f16v(h));
+        }
+      }
+    }
+  }
+  for (int p = 0; p < ub; ++p) {
+    const int byte = p * (d / 8) + 4 * wd;  // position in the row bit string
+    const int chunk = byte / 16, within = byte % 16;
+    *reinterpret_cast<uint32_t*>(trec + size_t(chunk) * kTile * 16 + size_t(slot) * 16 + within) = planes[p];
+  }
+  if (cv.mode == TQ_PROD && valid && rsum != 0.f) atomicAdd(&rr[row], rsum);
+  if (wd == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = valid ? f16b(nx[row]) : uint16_t(0);
+}
+
+// Thread per (row, 32-sign word); word 0 also writes n_r.
+__global__ __launch_bounds__(256) void signpack_kernel(CodecView cv, const float* z, const float* rr,
+                                                       int64_t row0, int64_t rows, int64_t rows_valid,
+                                                       uint8_t* rec) {
+  const int m = cv.m, words = (m + 31) / 32;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / words;
+  const int wd = int(gid % words);
+  if (row >= rows) return;
+  const int64_t grow = row0 + row;
+  uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
+  const int slot = int(grow % kTile);
+  const bool valid = row < rows_valid;
+  uint32_t bits = 0;
+  if (valid)
+    for (int k = 0; k < 32 && 32 * wd + k < m; ++k)
+      bits |= uint32_t(z[row * m + 32 * wd + k] >= 0.f) << k;
+  const int byte = 4 * wd;
+  const int chunk = byte / 16, within = byte % 16;
+  const int width = min(16, cv.sign_bytes - chunk * 16);
+  uint8_t* dst = trec + cv.off_signs + size_t(chunk) * kTile * 16 + size_t(slot) * width + within;
+  for (int b = 0; b < 4 && within + b < width; ++b) dst[b] = uint8_t(bits >> (8 * b));
+  if (wd == 0)
+    *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = valid ? f16b(sqrtf(rr[row])) : uint16_t(0);
+}
+
+// Thread per (row, 32-coordinate word): c[idx] as fp16 and signs as +-1 fp16.
+__global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_t* rec, int64_t row0,
+                                                      int64_t rows, uint16_t* khat, uint16_t* sg) {
+  const int d = cv.d, words = d / 32, swords = cv.mode == TQ_PROD ? (cv.m + 31) / 32 : 0;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = gid / (words + swords);
+  const int wd = int(gid % (words + swords));
+  if (row >= rows) return;
+  const int64_t grow = row0 + row;
+  const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
+  const int slot = int(grow % kTile);
+  if (wd < words) {
+    uint32_t planes[kMaxBits];
+    for (int p = 0; p < cv.ubits; ++p) {
+      const int byte = p * (d / 8) + 4 * wd;
+      planes[p] = *reinterpret_cast<const uint32_t*>(trec + size_t(byte / 16) * kTile * 16 + size_t(slot) * 16 + byte % 16);
+    }
+    for (int k = 0; k < 32; ++k) {
+      int idx = 0;
+      for (int p = 0; p < cv.ubits; ++p) idx |= int((planes[p] >> k) & 1) << p;
+      khat[row * d + 32 * wd + k] = f16b(cv.ucen[idx]);
+    }
+  } else {
+    const int sw = wd - words;
+    const int byte = 4 * sw;
+    const int chunk = byte / 16, within = byte % 16;
+    const int width = min(16, cv.sign_bytes - chunk * 16);
+    const uint8_t* src = trec + cv.off_signs + size_t(chunk) * kTile * 16 + size_t(slot) * width + within;
+    uint32_t bits = 0;
+    for (int b = 0; b < 4 && within + b < width; ++b) bits |= uint32_t(src[b]) << (8 * b);
+    for (int k = 0; k < 32 && 32 * sw + k < cv.m; ++k)
+      sg[row * cv.m + 32 * sw + k] = (bits >> k) & 1 ? 0x3C00u : 0xBC00u;
+  }
+}
+
+// One wave per row of a [rows][cols] fp32 matrix: scale 2^e putting the
+// row's max |v| in [2^14, 2^15), fp16 hi/lo parts of v 2^e stacked as out
+// rows 0..rows-1 (hi) and rows..2rows-1 (lo), and inv[row] = 2^-e.
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* src, int64_t rows, int cols,
+                                                         uint16_t* out, float* inv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* r = src + row * cols;
+  float mx = 0.f;
+  for (int i = lane; i < cols; i += 64) mx = fmaxf(mx, fabsf(r[i]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+  const int e = mx > 0.f ? min(253, max(1, 268 - ebits)) : 127;
+  const float p2 = __uint_as_float(uint32_t(e) << 23);
+  for (int i = lane; i < cols; i += 64) {
+    const float v = r[i] * p2;
+    const uint16_t h = f16b(v);
+    out[row * cols + i] = h;
+    out[(rows + row) * cols + i] = f16b(v - f16v(h));
+  }
+  if (lane == 0) inv[row] = __uint_as_float(uint32_t(254 - e) << 23);
+}
+
+// s[q][t] = n_x (qinv[q] (code[q] + code[q + nq]) + n_r k qsinv[q] (sign[q] + sign[q + nq]))
+__global__ void combine_kernel(CodecView cv, const float* code, const float* sign, const float* qinv,
+                               const float* qsinv, int64_t nq, int64_t nc, int64_t ld_parts,
+                               const uint8_t* rec, int64_t row0, float* out, int64_t ld_out) {
+  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= nq * nc) return;
+  const int64_t q = e / nc, t = e % nc;
+  const int64_t grow = row0 + t;
+  const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
+  const int slot = int(grow % kTile);
+  const float nx = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nx + 2 * slot));
+  float s = qinv[q] * (code[q * ld_parts + t] + code[(q + nq) * ld_parts + t]);
+  if (cv.mode == TQ_PROD) {
+    const float nr = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * slot));
+    s += nr * kQjl / float(cv.m) * qsinv[q] * (sign[q * ld_parts + t] + sign[(q + nq) * ld_parts + t]);
+  }
+  out[q * ld_out + t] = nx * s;
+}
+
+// ------------------------------------------------------------- rocBLAS
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64] = {};
+
+rocblas_handle blas(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) g_blas[dev] = nullptr;
+  return g_blas[dev];
+}
+
+// Row-major C[M][N] (+)= A[M][K] * B[N][K]^T with fp16 A, B and fp32 C.
+hipError_t gemm_abt(rocblas_handle h, const uint16_t* a, const uint16_t* b, float* c, int64_t M,
+                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, bool accumulate) {
+  const float one = 1.f, beta = accumulate ? 1.f : 0.f;
+  // column-major: C^T (N x M) = B (N x K) * A^T, i.e. op(B_cm) = T, op(A_cm) = N
+  rocblas_status st = rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none,
+                                      rocblas_int(N), rocblas_int(M), rocblas_int(K), &one,
+                                      b, rocblas_datatype_f16_r, rocblas_int(ldb), a,
+                                      rocblas_datatype_f16_r, rocblas_int(lda), &beta, c,
+                                      rocblas_datatype_f32_r, rocblas_int(ldc), c,
+                                      rocblas_datatype_f32_r, rocblas_int(ldc),
+                                      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
+}
+
+unsigned blocks_for(int64_t threads, int bs = 256) { return unsigned((threads + bs - 1) / bs); }
+
+}  // namespace
+
+int64_t large_encode_chunk() { return 16384; }
+
+size_t large_encode_workspace(const CodecView& cv) {
+  const size_t C = size_t(large_encode_chunk()), d = size_t(cv.d), m = size_t(std::max(cv.m, 1));
+  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
+  // xh, xl | y (reused for z) | rh, rl | w, nx, rr
+  return 2 * r(C * d * 2) + r(C * std::max(d, m) * 4) + 2 * r(C * m * 2) + 3 * r(C * 4);
+}
+
+hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs& a, void* ws,
+                               hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  rocblas_handle h = blas(device);
+  if (!h) return hipErrorLaunchFailure;
+  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorLaunchFailure;
+  const int64_t C = large_encode_chunk();
+  const int d = cv.d, m = std::max(cv.m, 1);
+  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * d * 2);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * d * 2);
+  float* y = reinterpret_cast<float*>(p); p += r(size_t(C) * std::max(d, m) * 4);
+  uint16_t* rh = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * m * 2);
+  uint16_t* rl = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * m * 2);
+  float* w = reinterpret_cast<float*>(p); p += r(size_t(C) * 4);
+  float* nx = reinterpret_cast<float*>(p); p += r(size_t(C) * 4);
+  float* rr = reinterpret_cast<float*>(p);
+  const int esz = a.x_bf16 ? 2 : 4;
+  for (int64_t b = 0; b < a.batch; ++b)
+    for (int64_t hh = 0; hh < a.heads; ++hh) {
+      const int hc = cv.heads > 1 ? int(hh) : 0;
+      const uint16_t* rot_hi = cv.rot_hi + size_t(hc) * d * d;
+      const uint16_t* rot_lo = cv.rot_lo + size_t(hc) * d * d;
+      const uint8_t* xs = static_cast<const uint8_t*>(a.x) + (b * a.xs_b + hh * a.xs_h) * esz;
+      uint8_t* rec = a.rec + b * a.rs_b + hh * a.rs_h;
+      const int64_t padded = (a.tokens + kTile - 1) / kTile * kTile;
+      for (int64_t r0 = 0; r0 < padded; r0 += C) {
+        const int64_t rows = std::min(C, padded - r0);
+        const int64_t valid = std::max<int64_t>(0, std::min(rows, a.tokens - r0));
+        if (valid > 0) {
+          hipLaunchKernelGGL(rowprep_kernel, dim3(blocks_for(valid * 64)), dim3(256), 0, s,
+                             xs + r0 * a.xs_t * esz, a.x_bf16, a.xs_t, valid, d, xh, xl, w, nx);
+          hipError_t e = hipGetLastError();
+          if (e != hipSuccess) return e;
+          // y = xh (16Pi_hi)^T + xh (16Pi_lo)^T + xl (16Pi_hi)^T
+          if ((e = gemm_abt(h, xh, rot_hi, y, valid, d, d, d, d, d, false)) != hipSuccess) return e;
+          if ((e = gemm_abt(h, xh, rot_lo, y, valid, d, d, d, d, d, true)) != hipSuccess) return e;
+          if ((e = gemm_abt(h, xl, rot_hi, y, valid, d, d, d, d, d, true)) != hipSuccess) return e;
+          if (cv.mode == TQ_PROD) {
+            if ((e = launch_fill_zero(rr, valid, s)) != hipSuccess) return e;
+          }
+        }
+        hipLaunchKernelGGL(quantize_kernel, dim3(blocks_for(rows * (d / 32))), dim3(256), 0, s, cv, y,
+                           w, nx, r0, rows, valid, rec, rh, rl, rr);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (cv.mode == TQ_PROD) {
+          if (valid > 0) {
+            // z = rh S_hi^T + rh S_lo^T + rl S_hi^T  (z reuses the y buffer)
+            if ((e = gemm_abt(h, rh, cv.sk_hi, y, valid, m, m, m, m, m, false)) != hipSuccess) return e;
+            if ((e = gemm_abt(h, rh, cv.sk_lo, y, valid, m, m, m, m, m, true)) != hipSuccess) return e;
+            if ((e = gemm_abt(h, rl, cv.sk_hi, y, valid, m, m, m, m, m, true)) != hipSuccess) return e;
+          }
+          hipLaunchKernelGGL(signpack_kernel, dim3(blocks_for(rows * ((m + 31) / 32))), dim3(256), 0, s,
+                             cv, y, rr, r0, rows, valid, rec);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+      }
+    }
+  return hipSuccess;
+}
+
+int64_t large_score_chunk() { return 65536; }
+
+size_t large_score_workspace(const CodecView& cv, int64_t nq) {
+  const size_t NC = size_t(large_score_chunk()), d = size_t(cv.d), m = size_t(std::max(cv.m, 1));
+  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
+  // qr hi/lo | qs hi/lo | scales | khat | sg | code parts | sign parts | chunk scores
+  return r(2 * size_t(nq) * d * 2) + r(2 * size_t(nq) * m * 2) + r(2 * size_t(nq) * 4) + r(NC * d * 2) +
+         r(NC * m * 2) + 2 * r(2 * size_t(nq) * NC * 4) + r(size_t(nq) * NC * 4);
+}
+
+// Scores of nq prepared queries (qr [nq][d], qs [nq][m] fp32) against n
+// records.  With out != nullptr the scores are written to out[nq][n];
+// otherwise each key chunk's scores are handed to `chunk_cb(scores, ld, r0,
+// rows)` (used by the top-k search).
+hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, const float* qs,
+                              int64_t nq, const uint8_t* rec, int64_t n, float* out, void* ws,
+                              hipStream_t s, ChunkFn chunk_cb, void* cb_ctx) {
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  rocblas_handle h = blas(device);
+  if (!h) return hipErrorLaunchFailure;
+  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorLaunchFailure;
+  const int64_t NC = large_score_chunk();
+  const int d = cv.d, m = std::max(cv.m, 1);
+  const bool prod = cv.mode == TQ_PROD;
+  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  uint16_t* qrs = reinterpret_cast<uint16_t*>(p); p += r(2 * size_t(nq) * d * 2);
+  uint16_t* qss = reinterpret_cast<uint16_t*>(p); p += r(2 * size_t(nq) * m * 2);
+  float* qinv = reinterpret_cast<float*>(p);
+  float* qsinv = qinv + nq; p += r(2 * size_t(nq) * 4);
+  uint16_t* khat = reinterpret_cast<uint16_t*>(p); p += r(size_t(NC) * d * 2);
+  uint16_t* sg = reinterpret_cast<uint16_t*>(p); p += r(size_t(NC) * m * 2);
+  float* code = reinterpret_cast<float*>(p); p += r(2 * size_t(nq) * NC * 4);
+  float* sign = reinterpret_cast<float*>(p); p += r(2 * size_t(nq) * NC * 4);
+  float* chunk = reinterpret_cast<float*>(p);
+  hipLaunchKernelGGL(split_rows_kernel, dim3(blocks_for(nq * 64)), dim3(256), 0, s, qr, nq, d, qrs, qinv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (prod) {
+    hipLaunchKernelGGL(split_rows_kernel, dim3(blocks_for(nq * 64)), dim3(256), 0, s, qs, nq, m, qss, qsinv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  for (int64_t r0 = 0; r0 < n; r0 += NC) {
+    const int64_t rows = std::min(NC, n - r0);
+    const int words = d / 32 + (prod ? (m + 31) / 32 : 0);
+    hipLaunchKernelGGL(dequant_kernel, dim3(blocks_for(rows * words)), dim3(256), 0, s, cv, rec, r0,
+                       rows, khat, sg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // [q_hi; q_lo] khat^T and [qs_hi; qs_lo] sg^T
+    if ((e = gemm_abt(h, qrs, khat, code, 2 * nq, rows, d, d, d, NC, false)) != hipSuccess) return e;
+    if (prod && (e = gemm_abt(h, qss, sg, sign, 2 * nq, rows, m, m, m, NC, false)) != hipSuccess) return e;
+    float* dst = out ? out + r0 : chunk;
+    const int64_t ld = out ? n : NC;
+    hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(nq * rows)), dim3(256), 0, s, cv, code, sign, qinv,
+                       qsinv, nq, rows, NC, rec, r0, dst, ld);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!out && chunk_cb && (e = chunk_cb(cb_ctx, chunk, NC, r0, rows, s)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tq

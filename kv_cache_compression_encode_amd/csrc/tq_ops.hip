@@ -409,23 +409,25 @@ __device__ __forceinline__ bool better(float s1, int64_t i1, float s2, int64_t i
 
 // Block (segment, query): per-thread top-16 of a strided subset, then k rounds
 // of a block-wide arg-max over the thread heads.
-__global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, int64_t n, int k,
-                                                           int nseg, float* ps, int64_t* pi) {
+__global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, int64_t ld,
+                                                           int64_t cols, int64_t id_base, int k,
+                                                           int nseg, int seg_base, int total_seg,
+                                                           float* ps, int64_t* pi) {
   __shared__ float rs[256];
   __shared__ int64_t ri[256];
   __shared__ int rt[256];
   const int seg = blockIdx.x;
   const int64_t qi = blockIdx.y;
-  const int64_t per = (n + nseg - 1) / nseg;
-  const int64_t lo = seg * per, hi = min(n, lo + per);
+  const int64_t per = (cols + nseg - 1) / nseg;
+  const int64_t lo = seg * per, hi = min(cols, lo + per);
   float ls[kTopMax];
   int64_t li[kTopMax];
 #pragma unroll
   for (int r = 0; r < kTopMax; ++r) { ls[r] = -INFINITY; li[r] = INT64_MAX; }
-  const float* row = scores + qi * n;
+  const float* row = scores + qi * ld;
   for (int64_t t = lo + threadIdx.x; t < hi; t += blockDim.x) {
     float s = row[t];
-    int64_t id = t;
+    int64_t id = id_base + t;
     if (!better(s, id, ls[kTopMax - 1], li[kTopMax - 1])) continue;
 #pragma unroll
     for (int r = 0; r < kTopMax; ++r) {
@@ -456,8 +458,9 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, 
       __syncthreads();
     }
     if (threadIdx.x == 0) {
-      ps[(qi * nseg + seg) * k + round] = rs[0];
-      pi[(qi * nseg + seg) * k + round] = ri[0];
+      const int64_t o = (qi * total_seg + seg_base + seg) * k + round;
+      ps[o] = rs[0];
+      pi[o] = ri[0];
     }
     if (threadIdx.x == rt[0]) ++head;
     __syncthreads();
@@ -543,18 +546,40 @@ hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeA
   return hipGetLastError();
 }
 
+hipError_t launch_topk_segments(const float* scores, int64_t ld, int64_t cols, int64_t id_base,
+                                int64_t nq, int k, int nseg, int seg_base, int total_seg,
+                                float* ps, int64_t* pi, hipStream_t s) {
+  hipLaunchKernelGGL(topk_segment_kernel, dim3(unsigned(nseg), unsigned(nq)), dim3(256), 0, s, scores,
+                     ld, cols, id_base, k, nseg, seg_base, total_seg, ps, pi);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_merge(const float* ps, const int64_t* pi, int64_t nq, int total_seg, int k,
+                             float* out_s, int64_t* out_i, hipStream_t s) {
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(nq)), dim3(64), 0, s, ps, pi, total_seg, k, out_s,
+                     out_i);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
                        const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,
                        float* ws_scores, float* ws_part_s, int64_t* ws_part_i, int nsplit,
                        hipStream_t s) {
   hipError_t e = launch_score(cv, qr, qs, nq, rec, n, ws_scores, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_segment_kernel, dim3(unsigned(nsplit), unsigned(nq)), dim3(256), 0, s,
-                     ws_scores, n, k, nsplit, ws_part_s, ws_part_i);
-  e = hipGetLastError();
+  e = launch_topk_segments(ws_scores, n, n, 0, nq, k, nsplit, 0, nsplit, ws_part_s, ws_part_i, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(nq)), dim3(64), 0, s, ws_part_s, ws_part_i,
-                     nsplit, k, top_s, top_i);
+  return launch_topk_merge(ws_part_s, ws_part_i, nq, nsplit, k, top_s, top_i, s);
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ from __future__ import annotations
 import math
 from typing import Optional
 
+import numpy as np
 import torch
 
 KV_TOP_FRACTIONS = (0.50, 0.16, 0.10, 0.04)
@@ -156,3 +157,15 @@ WORKLOADS = {
 def seed(workload: int, role: str) -> int:
     return 100 * workload + {"data": 1, "queries": 2, "rotation": 3, "sketch": 4,
                              "calibration": 5, "values": 6, "vrotation": 7}[role]
+
+
+def random_codes(n: int, d: int, levels: int, m: int, seed: int):
+    """Arbitrary stored codes for scoring tests: indices uniform in [0, levels),
+    sign bits fair coins, n_x uniform in [0.5, 1.5) and n_r in [0.05, 0.7),
+    both as fp16.  Returns (idx [n][d] int64, signs [n][m] bool or None, nx, nr)."""
+    g = np.random.Generator(np.random.Philox(seed))
+    idx = g.integers(0, levels, size=(n, d), dtype=np.int64)
+    signs = g.integers(0, 2, size=(n, m), dtype=np.uint8).astype(bool) if m > 0 else None
+    nx = g.uniform(0.5, 1.5, size=n).astype(np.float16)
+    nr = g.uniform(0.05, 0.7, size=n).astype(np.float16) if m > 0 else None
+    return idx, signs, nx, nr

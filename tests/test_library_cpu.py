@@ -131,13 +131,17 @@ def test_argument_errors_before_launch():
     buf = ctypes.create_string_buffer(1024)
     # host-only codebook: no device tables -> EINVAL, nothing launched
     st = lib.tq_encode(cb.handle, ctypes.addressof(buf), L.TQ_F32, 1, 1, 4, 0, 0, 128,
-                       ctypes.addressof(buf), 0, 0, None)
+                       ctypes.addressof(buf), 0, 0, None, 0, None)
     assert st == L.TQ_EINVAL
-    st = lib.tq_encode(cb.handle, None, L.TQ_F32, 1, 1, 4, 0, 0, 128, ctypes.addressof(buf), 0, 0, None)
+    st = lib.tq_encode(cb.handle, None, L.TQ_F32, 1, 1, 4, 0, 0, 128, ctypes.addressof(buf), 0, 0,
+                       None, 0, None)
     assert st == L.TQ_EINVAL
     st = lib.tq_encode(cb.handle, ctypes.addressof(buf), 5, 1, 1, 4, 0, 0, 128,
-                       ctypes.addressof(buf), 0, 0, None)
+                       ctypes.addressof(buf), 0, 0, None, 0, None)
     assert st == L.TQ_EINVAL
+    assert lib.tq_workspace_size(cb.handle, L.TQ_OP_ENCODE, 0, 0, 0) == 0
+    wide = tq.Codebook(1536, tq.TQ_PROD, 2, device=-1)
+    assert lib.tq_workspace_size(wide.handle, L.TQ_OP_ENCODE, 0, 0, 0) > 0
     assert lib.tq_workspace_size(cb.handle, L.TQ_OP_TOPK, 4, 100, 17) == 0
     assert lib.tq_workspace_size(cb.handle, L.TQ_OP_SCORE, 4, 100, 0) >= 4 * 256 * 4
     assert lib.tq_codebook_free(None) == L.TQ_EINVAL
