@@ -1,16 +1,19 @@
 // TurboQuant encode and scoring for wide vectors (d a multiple of 128, e.g.
 // the 1536-dim vector-search workload).  At this width the rotation
 // Y = X Pi^T, the QJL sketch Z = R S^T and the scoring Q' K_hat^T are plain
-// dense GEMMs over whole rows, so they run as rocBLAS GEMMs on fp16 hi/lo
-// operand splits with fp32 accumulation (fp32-accurate results); the
-// per-element steps in between are the kernels below:
-//   rowprep   : n_x, per-row power-of-two scale, fp16 hi/lo split of x;
+// dense GEMMs over whole rows, so they run as rocBLAS fp16 GEMMs with fp32
+// accumulation.  fp32 accuracy comes from hi/lo fp16 splits laid side by side
+// along the reduction axis: [a_hi | a_hi | a_lo] . [b_hi | b_lo | b_hi]^T =
+// a_hi b_hi + a_hi b_lo + a_lo b_hi, one GEMM per product.  The per-element
+// steps in between are the kernels below:
+//   rowprep   : n_x, per-row power-of-two scale, split of x;
 //   quantize  : Lloyd-Max index per coordinate (TurboQuant paper review,
 //               "Method"), row-layout bit planes, residual r = y - c[idx]
-//               split into fp16 hi/lo for the sketch GEMM, ||r||^2;
+//               split for the sketch GEMM, ||r||^2;
 //   signpack  : sign bits [z >= 0] and the fp16 norms;
-//   dequant   : c[idx] (fp16) and +-1 signs of stored records, for scoring;
-//   combine   : s = n_x (code + n_r sqrt(pi/2)/m sign) from the GEMM parts.
+//   dequant   : key rows [c[idx] | +-n_r] (fp16) of stored records;
+//   qsplit    : query rows [q' | sqrt(pi/2)/m q_s], scaled, split hi/lo;
+//   combine   : s = n_x (hi part + lo part) / query scale.
 // Rows are processed in chunks so the workspace stays bounded.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
@@ -29,11 +32,11 @@ __device__ __forceinline__ uint16_t f16b(float x) { return __builtin_bit_cast(ui
 __device__ __forceinline__ float f16v(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
 
 // One wave per row: n_x, scale 2^e putting max|x| in [2^14, 2^15), and the
-// fp16 hi/lo parts of x * 2^e.  w[row] = 16 * 2^e * s_x relates the GEMM
-// output (with 16 Pi) to the rotated unit vector; nx[row] = ||x||.
+// row [hi | hi | lo] of x 2^e in fp16 (xcat, [rows][3d]).  w[row] = 16 2^e n_x
+// relates the GEMM output (with 16 Pi) to the rotated unit vector.
 __global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16, int64_t ld,
-                                                      int64_t rows, int d, uint16_t* xh,
-                                                      uint16_t* xl, float* w, float* nx) {
+                                                      int64_t rows, int d, uint16_t* xcat, float* w,
+                                                      float* nx) {
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -53,12 +56,14 @@ __global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16,
     mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   }
   const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
-  const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+  const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(253, max(1, 268 - ebits))) << 23) : 1.f;
+  uint16_t* out = xcat + row * 3 * d;
   for (int i = lane; i < d; i += 64) {
     const float v = at(i) * p2;
     const uint16_t h = f16b(v);
-    xh[row * d + i] = h;
-    xl[row * d + i] = f16b(v - f16v(h));
+    out[i] = h;
+    out[d + i] = h;
+    out[2 * d + i] = f16b(v - f16v(h));
   }
   if (lane == 0) {
     const float n = sqrtf(ss);
@@ -67,12 +72,25 @@ __global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16,
   }
 }
 
+// [rows][3 cols] = [hi | lo | hi] of a pair of fp16 matrices [rows][cols].
+__global__ void cat3_kernel(const uint16_t* hi, const uint16_t* lo, int64_t rows, int cols,
+                            uint16_t* out) {
+  const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= rows * cols) return;
+  const int64_t r = e / cols;
+  const int c = int(e % cols);
+  uint16_t* o = out + r * 3 * cols;
+  o[c] = hi[e];
+  o[cols + c] = lo[e];
+  o[2 * cols + c] = hi[e];
+}
+
 // Thread per (row, 32-coordinate word).  Rows >= rows_valid (padding of the
 // last tile) get zero records.
 __global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float* y, const float* w,
                                                        const float* nx, int64_t row0, int64_t rows,
-                                                       int64_t rows_valid, uint8_t* rec, uint16_t* rh,
-                                                       uint16_t* rl, float* rr) {
+                                                       int64_t rows_valid, uint8_t* rec, uint16_t* rcat,
+                                                       float* rr) {
   const int d = cv.d, words = d / 32;
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t row = gid / words;
@@ -102,8 +120,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float
           rsum = fmaf(r, r, rsum);
           const float rs = 32.f * r;
           const uint16_t h = f16b(rs);
-          rh[row * cv.m + dim] = h;
-          rl[row * cv.m + dim] = f16b(rs - f16v(h));
+          uint16_t* o = rcat + row * 3 * cv.m;
+          o[dim] = h;
+          o[cv.m + dim] = h;
+          o[2 * cv.m + dim] = f16b(rs - f16v(h));
         }
       }
     }
@@ -143,10 +163,12 @@ __global__ __launch_bounds__(256) void signpack_kernel(CodecView cv, const float
     *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = valid ? f16b(sqrtf(rr[row])) : uint16_t(0);
 }
 
-// Thread per (row, 32-coordinate word): c[idx] as fp16 and signs as +-1 fp16.
+// Thread per (row, 32-coordinate word): key row [c[idx] | +-n_r] in fp16
+// (kcat, [rows][d + m]); +-n_r is exact since n_r is stored as fp16.
 __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_t* rec, int64_t row0,
-                                                      int64_t rows, uint16_t* khat, uint16_t* sg) {
+                                                      int64_t rows, uint16_t* kcat) {
   const int d = cv.d, words = d / 32, swords = cv.mode == TQ_PROD ? (cv.m + 31) / 32 : 0;
+  const int kw = d + (cv.mode == TQ_PROD ? cv.m : 0);
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t row = gid / (words + swords);
   const int wd = int(gid % (words + swords));
@@ -154,6 +176,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_
   const int64_t grow = row0 + row;
   const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
   const int slot = int(grow % kTile);
+  uint16_t* out = kcat + row * kw;
   if (wd < words) {
     uint32_t planes[kMaxBits];
     for (int p = 0; p < cv.ubits; ++p) {
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_
     for (int k = 0; k < 32; ++k) {
       int idx = 0;
       for (int p = 0; p < cv.ubits; ++p) idx |= int((planes[p] >> k) & 1) << p;
-      khat[row * d + 32 * wd + k] = f16b(cv.ucen[idx]);
+      out[32 * wd + k] = f16b(cv.ucen[idx]);
     }
   } else {
     const int sw = wd - words;
@@ -173,40 +196,44 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_
     const uint8_t* src = trec + cv.off_signs + size_t(chunk) * kTile * 16 + size_t(slot) * width + within;
     uint32_t bits = 0;
     for (int b = 0; b < 4 && within + b < width; ++b) bits |= uint32_t(src[b]) << (8 * b);
+    const uint16_t nr = *reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * slot);
     for (int k = 0; k < 32 && 32 * sw + k < cv.m; ++k)
-      sg[row * cv.m + 32 * sw + k] = (bits >> k) & 1 ? 0x3C00u : 0xBC00u;
+      out[d + 32 * sw + k] = (bits >> k) & 1 ? nr : uint16_t(nr ^ 0x8000u);
   }
 }
 
-// One wave per row of a [rows][cols] fp32 matrix: scale 2^e putting the
-// row's max |v| in [2^14, 2^15), fp16 hi/lo parts of v 2^e stacked as out
-// rows 0..rows-1 (hi) and rows..2rows-1 (lo), and inv[row] = 2^-e.
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* src, int64_t rows, int cols,
-                                                         uint16_t* out, float* inv) {
+// One wave per query: row v = [q' | sqrt(pi/2)/m q_s] (d + m values), scale
+// 2^e putting max |v| in [2^14, 2^15), fp16 hi/lo parts of v 2^e as rows
+// q (hi) and nq + q (lo) of out [2 nq][d + m], and inv[q] = 2^-e.
+__global__ __launch_bounds__(256) void qsplit_kernel(const float* qr, const float* qs, int64_t nq,
+                                                     int d, int m, float kq, uint16_t* out,
+                                                     float* inv) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float* r = src + row * cols;
+  const int64_t q = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (q >= nq) return;
+  const int w = d + m;
+  auto at = [&](int i) -> float { return i < d ? qr[q * d + i] : kq * qs[q * m + (i - d)]; };
   float mx = 0.f;
-  for (int i = lane; i < cols; i += 64) mx = fmaxf(mx, fabsf(r[i]));
+  for (int i = lane; i < w; i += 64) mx = fmaxf(mx, fabsf(at(i)));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
   const int e = mx > 0.f ? min(253, max(1, 268 - ebits)) : 127;
   const float p2 = __uint_as_float(uint32_t(e) << 23);
-  for (int i = lane; i < cols; i += 64) {
-    const float v = r[i] * p2;
+  for (int i = lane; i < w; i += 64) {
+    const float v = at(i) * p2;
     const uint16_t h = f16b(v);
-    out[row * cols + i] = h;
-    out[(rows + row) * cols + i] = f16b(v - f16v(h));
+    out[q * w + i] = h;
+    out[(nq + q) * w + i] = f16b(v - f16v(h));
   }
-  if (lane == 0) inv[row] = __uint_as_float(uint32_t(254 - e) << 23);
+  if (lane == 0) inv[q] = __uint_as_float(uint32_t(254 - e) << 23);
 }
 
-// s[q][t] = n_x (qinv[q] (code[q] + code[q + nq]) + n_r k qsinv[q] (sign[q] + sign[q + nq]))
-__global__ void combine_kernel(CodecView cv, const float* code, const float* sign, const float* qinv,
-                               const float* qsinv, int64_t nq, int64_t nc, int64_t ld_parts,
-                               const uint8_t* rec, int64_t row0, float* out, int64_t ld_out) {
+// s[q][t] = n_x[t] inv[q] (part[q][t] + part[nq + q][t]); may run in place
+// (out == part, ld_out == ld_parts).
+__global__ void combine_kernel(CodecView cv, const float* part, const float* inv, int64_t nq,
+                               int64_t nc, int64_t ld_parts, const uint8_t* rec, int64_t row0,
+                               float* out, int64_t ld_out) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= nq * nc) return;
   const int64_t q = e / nc, t = e % nc;
@@ -214,12 +241,8 @@ __global__ void combine_kernel(CodecView cv, const float* code, const float* sig
   const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
   const int slot = int(grow % kTile);
   const float nx = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nx + 2 * slot));
-  float s = qinv[q] * (code[q * ld_parts + t] + code[(q + nq) * ld_parts + t]);
-  if (cv.mode == TQ_PROD) {
-    const float nr = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * slot));
-    s += nr * kQjl / float(cv.m) * qsinv[q] * (sign[q * ld_parts + t] + sign[(q + nq) * ld_parts + t]);
-  }
-  out[q * ld_out + t] = nx * s;
+  const float s = part[q * ld_parts + t] + part[(q + nq) * ld_parts + t];
+  out[q * ld_out + t] = nx * (inv[q] * s);
 }
 
 // ------------------------------------------------------------- rocBLAS
@@ -253,12 +276,35 @@ unsigned blocks_for(int64_t threads, int bs = 256) { return unsigned((threads + 
 
 int64_t large_encode_chunk() { return 16384; }
 
-size_t large_encode_workspace(const CodecView& cv) {
+namespace {
+struct EncodeWs {
+  uint16_t *xcat, *rcat, *bpi, *bs;
+  float *y, *w, *nx, *rr;
+};
+
+size_t encode_ws_layout(const CodecView& cv, void* base, EncodeWs* out) {
   const size_t C = size_t(large_encode_chunk()), d = size_t(cv.d), m = size_t(std::max(cv.m, 1));
   auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  // xh, xl | y (reused for z) | rh, rl | w, nx, rr
-  return 2 * r(C * d * 2) + r(C * std::max(d, m) * 4) + 2 * r(C * m * 2) + 3 * r(C * 4);
+  const size_t sizes[] = {r(C * 3 * d * 2), r(C * 3 * m * 2), r(d * 3 * d * 2), r(m * 3 * m * 2),
+                          r(C * std::max(d, m) * 4), r(C * 4), r(C * 4), r(C * 4)};
+  size_t off[8], tot = 0;
+  for (int i = 0; i < 8; ++i) { off[i] = tot; tot += sizes[i]; }
+  if (out) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    out->xcat = reinterpret_cast<uint16_t*>(p + off[0]);
+    out->rcat = reinterpret_cast<uint16_t*>(p + off[1]);
+    out->bpi = reinterpret_cast<uint16_t*>(p + off[2]);
+    out->bs = reinterpret_cast<uint16_t*>(p + off[3]);
+    out->y = reinterpret_cast<float*>(p + off[4]);
+    out->w = reinterpret_cast<float*>(p + off[5]);
+    out->nx = reinterpret_cast<float*>(p + off[6]);
+    out->rr = reinterpret_cast<float*>(p + off[7]);
+  }
+  return tot;
 }
+}  // namespace
+
+size_t large_encode_workspace(const CodecView& cv) { return encode_ws_layout(cv, nullptr, nullptr); }
 
 hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs& a, void* ws,
                                hipStream_t s) {
@@ -268,22 +314,27 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
   if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorLaunchFailure;
   const int64_t C = large_encode_chunk();
   const int d = cv.d, m = std::max(cv.m, 1);
-  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  uint16_t* xh = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * d * 2);
-  uint16_t* xl = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * d * 2);
-  float* y = reinterpret_cast<float*>(p); p += r(size_t(C) * std::max(d, m) * 4);
-  uint16_t* rh = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * m * 2);
-  uint16_t* rl = reinterpret_cast<uint16_t*>(p); p += r(size_t(C) * m * 2);
-  float* w = reinterpret_cast<float*>(p); p += r(size_t(C) * 4);
-  float* nx = reinterpret_cast<float*>(p); p += r(size_t(C) * 4);
-  float* rr = reinterpret_cast<float*>(p);
+  const bool prod = cv.mode == TQ_PROD;
+  EncodeWs W;
+  encode_ws_layout(cv, ws, &W);
   const int esz = a.x_bf16 ? 2 : 4;
+  hipError_t e;
+  if (prod) {
+    hipLaunchKernelGGL(cat3_kernel, dim3(blocks_for(int64_t(m) * m)), dim3(256), 0, s, cv.sk_hi, cv.sk_lo,
+                       int64_t(m), m, W.bs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  int cur_head = -1;
   for (int64_t b = 0; b < a.batch; ++b)
     for (int64_t hh = 0; hh < a.heads; ++hh) {
       const int hc = cv.heads > 1 ? int(hh) : 0;
-      const uint16_t* rot_hi = cv.rot_hi + size_t(hc) * d * d;
-      const uint16_t* rot_lo = cv.rot_lo + size_t(hc) * d * d;
+      if (hc != cur_head) {  // [16 Pi_hi | 16 Pi_lo | 16 Pi_hi] of this head
+        hipLaunchKernelGGL(cat3_kernel, dim3(blocks_for(int64_t(d) * d)), dim3(256), 0, s,
+                           cv.rot_hi + size_t(hc) * d * d, cv.rot_lo + size_t(hc) * d * d, int64_t(d), d,
+                           W.bpi);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        cur_head = hc;
+      }
       const uint8_t* xs = static_cast<const uint8_t*>(a.x) + (b * a.xs_b + hh * a.xs_h) * esz;
       uint8_t* rec = a.rec + b * a.rs_b + hh * a.rs_h;
       const int64_t padded = (a.tokens + kTile - 1) / kTile * kTile;
@@ -292,30 +343,22 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
         const int64_t valid = std::max<int64_t>(0, std::min(rows, a.tokens - r0));
         if (valid > 0) {
           hipLaunchKernelGGL(rowprep_kernel, dim3(blocks_for(valid * 64)), dim3(256), 0, s,
-                             xs + r0 * a.xs_t * esz, a.x_bf16, a.xs_t, valid, d, xh, xl, w, nx);
-          hipError_t e = hipGetLastError();
-          if (e != hipSuccess) return e;
-          // y = xh (16Pi_hi)^T + xh (16Pi_lo)^T + xl (16Pi_hi)^T
-          if ((e = gemm_abt(h, xh, rot_hi, y, valid, d, d, d, d, d, false)) != hipSuccess) return e;
-          if ((e = gemm_abt(h, xh, rot_lo, y, valid, d, d, d, d, d, true)) != hipSuccess) return e;
-          if ((e = gemm_abt(h, xl, rot_hi, y, valid, d, d, d, d, d, true)) != hipSuccess) return e;
-          if (cv.mode == TQ_PROD) {
-            if ((e = launch_fill_zero(rr, valid, s)) != hipSuccess) return e;
-          }
+                             xs + r0 * a.xs_t * esz, a.x_bf16, a.xs_t, valid, d, W.xcat, W.w, W.nx);
+          if ((e = hipGetLastError()) != hipSuccess) return e;
+          if ((e = gemm_abt(h, W.xcat, W.bpi, W.y, valid, d, 3 * d, 3 * d, 3 * d, d, false)) != hipSuccess)
+            return e;
+          if (prod && (e = launch_fill_zero(W.rr, valid, s)) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(quantize_kernel, dim3(blocks_for(rows * (d / 32))), dim3(256), 0, s, cv, y,
-                           w, nx, r0, rows, valid, rec, rh, rl, rr);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if (cv.mode == TQ_PROD) {
-          if (valid > 0) {
-            // z = rh S_hi^T + rh S_lo^T + rl S_hi^T  (z reuses the y buffer)
-            if ((e = gemm_abt(h, rh, cv.sk_hi, y, valid, m, m, m, m, m, false)) != hipSuccess) return e;
-            if ((e = gemm_abt(h, rh, cv.sk_lo, y, valid, m, m, m, m, m, true)) != hipSuccess) return e;
-            if ((e = gemm_abt(h, rl, cv.sk_hi, y, valid, m, m, m, m, m, true)) != hipSuccess) return e;
-          }
+        hipLaunchKernelGGL(quantize_kernel, dim3(blocks_for(rows * (d / 32))), dim3(256), 0, s, cv, W.y,
+                           W.w, W.nx, r0, rows, valid, rec, W.rcat, W.rr);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (prod) {
+          // z = [rh | rh | rl] [S_hi | S_lo | S_hi]^T  (z reuses the y buffer)
+          if (valid > 0 &&
+              (e = gemm_abt(h, W.rcat, W.bs, W.y, valid, m, 3 * m, 3 * m, 3 * m, m, false)) != hipSuccess)
+            return e;
           hipLaunchKernelGGL(signpack_kernel, dim3(blocks_for(rows * ((m + 31) / 32))), dim3(256), 0, s,
-                             cv, y, rr, r0, rows, valid, rec);
+                             cv, W.y, W.rr, r0, rows, valid, rec);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
       }
@@ -325,18 +368,40 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
 
 int64_t large_score_chunk() { return 65536; }
 
-size_t large_score_workspace(const CodecView& cv, int64_t nq) {
-  const size_t NC = size_t(large_score_chunk()), d = size_t(cv.d), m = size_t(std::max(cv.m, 1));
+namespace {
+struct ScoreWs {
+  uint16_t *qcat, *kcat;
+  float *inv, *part;
+};
+
+size_t score_ws_layout(const CodecView& cv, int64_t nq, void* base, ScoreWs* out) {
+  const size_t NC = size_t(large_score_chunk()), d = size_t(cv.d);
+  const size_t kw = d + (cv.mode == TQ_PROD ? size_t(cv.m) : 0);
   auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  // qr hi/lo | qs hi/lo | scales | khat | sg | code parts | sign parts | chunk scores
-  return r(2 * size_t(nq) * d * 2) + r(2 * size_t(nq) * m * 2) + r(2 * size_t(nq) * 4) + r(NC * d * 2) +
-         r(NC * m * 2) + 2 * r(2 * size_t(nq) * NC * 4) + r(size_t(nq) * NC * 4);
+  const size_t sizes[] = {r(2 * size_t(nq) * kw * 2), r(NC * kw * 2), r(size_t(nq) * 4),
+                          r(2 * size_t(nq) * NC * 4)};
+  size_t off[4], tot = 0;
+  for (int i = 0; i < 4; ++i) { off[i] = tot; tot += sizes[i]; }
+  if (out) {
+    uint8_t* p = static_cast<uint8_t*>(base);
+    out->qcat = reinterpret_cast<uint16_t*>(p + off[0]);
+    out->kcat = reinterpret_cast<uint16_t*>(p + off[1]);
+    out->inv = reinterpret_cast<float*>(p + off[2]);
+    out->part = reinterpret_cast<float*>(p + off[3]);
+  }
+  return tot;
+}
+}  // namespace
+
+size_t large_score_workspace(const CodecView& cv, int64_t nq) {
+  return score_ws_layout(cv, nq, nullptr, nullptr);
 }
 
 // Scores of nq prepared queries (qr [nq][d], qs [nq][m] fp32) against n
-// records.  With out != nullptr the scores are written to out[nq][n];
-// otherwise each key chunk's scores are handed to `chunk_cb(scores, ld, r0,
-// rows)` (used by the top-k search).
+// records: s = n_x <[q' | sqrt(pi/2)/m q_s], [c[idx] | n_r sign]>, one GEMM
+// per key chunk.  With out != nullptr the scores go to out[nq][n]; otherwise
+// each chunk's scores (in the workspace, row stride large_score_chunk()) are
+// handed to chunk_cb(scores, ld, r0, rows) (the top-k search).
 hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, const float* qs,
                               int64_t nq, const uint8_t* rec, int64_t n, float* out, void* ws,
                               hipStream_t s, ChunkFn chunk_cb, void* cb_ctx) {
@@ -345,41 +410,29 @@ hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, 
   if (!h) return hipErrorLaunchFailure;
   if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorLaunchFailure;
   const int64_t NC = large_score_chunk();
-  const int d = cv.d, m = std::max(cv.m, 1);
   const bool prod = cv.mode == TQ_PROD;
-  auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  uint16_t* qrs = reinterpret_cast<uint16_t*>(p); p += r(2 * size_t(nq) * d * 2);
-  uint16_t* qss = reinterpret_cast<uint16_t*>(p); p += r(2 * size_t(nq) * m * 2);
-  float* qinv = reinterpret_cast<float*>(p);
-  float* qsinv = qinv + nq; p += r(2 * size_t(nq) * 4);
-  uint16_t* khat = reinterpret_cast<uint16_t*>(p); p += r(size_t(NC) * d * 2);
-  uint16_t* sg = reinterpret_cast<uint16_t*>(p); p += r(size_t(NC) * m * 2);
-  float* code = reinterpret_cast<float*>(p); p += r(2 * size_t(nq) * NC * 4);
-  float* sign = reinterpret_cast<float*>(p); p += r(2 * size_t(nq) * NC * 4);
-  float* chunk = reinterpret_cast<float*>(p);
-  hipLaunchKernelGGL(split_rows_kernel, dim3(blocks_for(nq * 64)), dim3(256), 0, s, qr, nq, d, qrs, qinv);
+  const int d = cv.d, m = prod ? cv.m : 0, kw = d + m;
+  ScoreWs W;
+  score_ws_layout(cv, nq, ws, &W);
+  hipLaunchKernelGGL(qsplit_kernel, dim3(blocks_for(nq * 64)), dim3(256), 0, s, qr, qs, nq, d, m,
+                     prod ? kQjl / float(cv.m) : 0.f, W.qcat, W.inv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (prod) {
-    hipLaunchKernelGGL(split_rows_kernel, dim3(blocks_for(nq * 64)), dim3(256), 0, s, qs, nq, m, qss, qsinv);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   for (int64_t r0 = 0; r0 < n; r0 += NC) {
     const int64_t rows = std::min(NC, n - r0);
     const int words = d / 32 + (prod ? (m + 31) / 32 : 0);
-    hipLaunchKernelGGL(dequant_kernel, dim3(blocks_for(rows * words)), dim3(256), 0, s, cv, rec, r0,
-                       rows, khat, sg);
+    hipLaunchKernelGGL(dequant_kernel, dim3(blocks_for(rows * words)), dim3(256), 0, s, cv, rec, r0, rows,
+                       W.kcat);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // [q_hi; q_lo] khat^T and [qs_hi; qs_lo] sg^T
-    if ((e = gemm_abt(h, qrs, khat, code, 2 * nq, rows, d, d, d, NC, false)) != hipSuccess) return e;
-    if (prod && (e = gemm_abt(h, qss, sg, sign, 2 * nq, rows, m, m, m, NC, false)) != hipSuccess) return e;
-    float* dst = out ? out + r0 : chunk;
+    // [q_hi; q_lo] kcat^T  ->  part [2 nq][NC]
+    if ((e = gemm_abt(h, W.qcat, W.kcat, W.part, 2 * nq, rows, kw, kw, kw, NC, false)) != hipSuccess)
+      return e;
+    float* dst = out ? out + r0 : W.part;
     const int64_t ld = out ? n : NC;
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(nq * rows)), dim3(256), 0, s, cv, code, sign, qinv,
-                       qsinv, nq, rows, NC, rec, r0, dst, ld);
+    hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(nq * rows)), dim3(256), 0, s, cv, W.part, W.inv, nq,
+                       rows, NC, rec, r0, dst, ld);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (!out && chunk_cb && (e = chunk_cb(cb_ctx, chunk, NC, r0, rows, s)) != hipSuccess) return e;
+    if (!out && chunk_cb && (e = chunk_cb(cb_ctx, W.part, NC, r0, rows, s)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
