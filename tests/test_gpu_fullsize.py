@@ -1,0 +1,148 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on sampled outputs the oracle computes one by one (MI355X)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_encode_amd as tq
+import synth
+from oracle import tq_oracle as o
+from tests.parity import check_encoded, check_scores
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tile_slice(codec, buf, set_bytes, set_index, t0, t1):
+    tb = o.tile_bytes(codec)
+    base = set_index * set_bytes
+    return buf[base + t0 * tb: base + t1 * tb]
+
+
+def test_bulk_prefill_full_size_sampled():
+    """32 layers x 8 heads x 131072 tokens of bf16 K and V encoded in one call
+    each; tiles at the start, middle and end of sampled (layer, head) sets
+    against the oracle."""
+    L, H, T, D = 32, 8, 131072, 128
+    say("bulk prefill: generate 2 x 8.6 GB")
+    law = synth.KVLaw(H, D, 305)
+    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=303, seed_sketch=304)
+    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=303, layout=tq.TQ_LAYOUT_COL)
+    kc = o.turboquant_codec(D, 3, "prod", rot_seed=303, sketch_seed=304)
+    vc = o.turboquant_codec(D, 4, "mse", rot_seed=303, layout="col")
+    for name, cb, codec, seed in [("K", kcb, kc, 301), ("V", vcb, vc, 306)]:
+        X = synth.kv_cache(L, H, T, D, seed, law, device=DEV)
+        say(f"bulk prefill: encode {name}")
+        rec = tq.encode(cb, X)
+        torch.cuda.synchronize()
+        per = cb.records_bytes(T)
+        assert rec.numel() == L * H * per
+        for (l, h) in [(0, 0), (13, 5), (31, 7)]:
+            for t0 in (0, 1024, T // 64 - 2):
+                rows = X[l, h, t0 * 64:(t0 + 2) * 64].cpu().double().numpy()
+                ref = o.encode(codec, rows)
+                got_buf = rec[(l * H + h) * per + t0 * cb.tile_bytes:
+                              (l * H + h) * per + (t0 + 2) * cb.tile_bytes].cpu().numpy()
+                st = check_encoded(codec, ref, o.unpack(codec, got_buf, 128))
+                say(name, l, h, t0, st)
+        del X, rec
+        torch.cuda.empty_cache()
+
+
+def test_sq_decode_full_size_sampled():
+    """64 sequences x 8192 tokens, 8 KV / 32 query heads, SpectralQuant keys:
+    encode parity on sampled heads, decode parity on sampled sequences (their
+    records replaced by the oracle's so both sides read the same records)."""
+    B, H, T, QH, D = 64, 8, 8192, 32, 128
+    law = synth.KVLaw(H, D, 405)
+    calib = torch.stack([law.sample(h, 2048, torch.Generator().manual_seed(405 + h), "cpu")
+                         for h in range(H)])
+    bitmap = [5, 3, 2, 2] + [1] * 124
+    kcb = tq.Codebook(D, tq.TQ_PROD, 0, bitmap=bitmap, qjl_dims=4, rotation=tq.TQ_ROT_CALIBRATE,
+                      num_heads=H, seed_sketch=404, calib=calib)
+    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=407, layout=tq.TQ_LAYOUT_COL)
+    kc = o.spectralquant_codec(calib.float().numpy().astype(np.float64), bitmap, 4, sketch_seed=404)
+    vc = o.turboquant_codec(D, 4, "mse", rot_seed=407, layout="col")
+    say("sq decode: generate and encode")
+    K = synth.kv_cache(B, H, T, D, 401, law, device=DEV)
+    V = synth.kv_cache(B, H, T, D, 406, law, device=DEV)
+    q = synth.kv_queries(B, QH, H, D, 402, law, device=DEV)
+    krec, vrec = tq.encode(kcb, K), tq.encode(vcb, V)
+    torch.cuda.synchronize()
+    kper, vper = kcb.records_bytes(T), vcb.records_bytes(T)
+    seqs = [0, 37, 63]
+    ke, ve = {}, {}
+    for b in seqs:
+        for g in range(H):
+            kx = K[b, g].cpu().double().numpy()
+            vx = V[b, g].cpu().double().numpy()
+            ke[b, g] = o.encode(kc, kx, head=g)
+            ve[b, g] = o.encode(vc, vx)
+            if g in (0, 7):
+                sk = check_encoded(kc, ke[b, g], o.unpack(kc, krec[(b * H + g) * kper:(b * H + g + 1) * kper]
+                                                          .cpu().numpy(), T))
+                sv = check_encoded(vc, ve[b, g], o.unpack(vc, vrec[(b * H + g) * vper:(b * H + g + 1) * vper]
+                                                          .cpu().numpy(), T))
+                say("sq encode", b, g, sk, sv)
+            krec[(b * H + g) * kper:(b * H + g + 1) * kper] = torch.from_numpy(o.pack(kc, ke[b, g])).to(DEV)
+            vrec[(b * H + g) * vper:(b * H + g + 1) * vper] = torch.from_numpy(o.pack(vc, ve[b, g])).to(DEV)
+    del K, V
+    say("sq decode: full-batch decode")
+    scale = 1 / math.sqrt(D)
+    out = tq.decode_attend(kcb, vcb, q, krec, vrec, T, H, scale).cpu().numpy()
+    qc = q.cpu().double().numpy()
+    for b in seqs:
+        ref = o.decode_attention(kc, vc, qc[b], [ke[b, g] for g in range(H)],
+                                 [ve[b, g] for g in range(H)], scale)
+        nvmax = max(float(np.max(ve[b, g].nx.astype(np.float64))) for g in range(H))
+        err = float(np.max(np.abs(out[b] - ref))) / nvmax
+        say(f"sq decode seq {b}: max |out - ref| / max n_v = {err:.3g}")
+        assert err <= 1e-3
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_vector_search_full_size_sampled(bits):
+    """1e6 x 1536 database, 1024 queries, top-10.  Encode parity on sampled
+    tiles; for sampled queries each returned (id, score) is checked against
+    the oracle's encoding and score of that vector, and recall@10 against the
+    exact fp64 top-10 is reported."""
+    n, nq, d, k = 1_000_000, 1024, 1536, 10
+    say(f"vector search b={bits}: generate")
+    law = synth.LowRankLaw(d, 64, 505, device=DEV)
+    x = synth.lowrank_vectors(n, law, 501, device=DEV)
+    q = synth.lowrank_vectors(nq, law, 502, device=DEV)
+    cb = tq.Codebook(d, tq.TQ_PROD, bits, seed_rotation=503, seed_sketch=504)
+    codec = o.turboquant_codec(d, bits, "prod", rot_seed=503, sketch_seed=504)
+    say("vector search: encode + search")
+    rec = tq.encode(cb, x)
+    s, ids = tq.search_topk(cb, q, rec, n, k)
+    torch.cuda.synchronize()
+    s, ids = s.cpu().numpy(), ids.cpu().numpy()
+    tb = cb.tile_bytes
+    for t0 in (0, 255, 256, n // 64 - 1, (n + 63) // 64 - 1):
+        rows = np.arange(t0 * 64, min(n, t0 * 64 + 64))
+        ref = o.encode(codec, x[rows[0]:rows[-1] + 1].cpu().double().numpy())
+        got = o.unpack(codec, rec[t0 * tb:(t0 + 1) * tb].cpu().numpy(), len(rows))
+        say("encode tile", t0, check_encoded(codec, ref, got))
+    sample = [0, 1, 511, 1023]
+    qs = q[sample].cpu().double().numpy()
+    recalls = []
+    exact = np.concatenate([(x[i:i + 65536].cpu().double().numpy() @ qs.T)
+                            for i in range(0, n, 65536)], axis=0).T        # [len(sample)][n]
+    for j, r in enumerate(sample):
+        assert np.all(np.diff(s[r]) <= 0)
+        assert len(set(ids[r].tolist())) == k and ids[r].min() >= 0 and ids[r].max() < n
+        enc = o.encode(codec, x[torch.from_numpy(ids[r]).to(DEV)].cpu().double().numpy())
+        ref_s = o.score(codec, qs[j:j + 1], enc)[0]
+        check_scores(s[r][None, :], ref_s[None, :], qs[j:j + 1], enc.nx)
+        true = set(np.argsort(-exact[j], kind="stable")[:k].tolist())
+        recalls.append(len(true & set(ids[r].tolist())) / k)
+    say(f"vector search b={bits}: recall@10 vs exact top-10 on {len(sample)} queries = {np.mean(recalls):.3f}")
