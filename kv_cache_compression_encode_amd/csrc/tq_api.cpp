@@ -245,9 +245,11 @@ int64_t decode_nsplit(int64_t max_tokens) {
 }
 constexpr int kDecodeChunkTiles = 8;
 
+constexpr int kLargeTopkSegments = 4;  // partial lists per key chunk of the wide-vector path
+
 int64_t topk_nseg(int64_t n) {
-  // one partial list per 4096 keys (whole key chunks of the wide-vector path)
-  const int64_t per_chunk = (large_score_chunk() + 4095) / 4096;
+  // one partial list per 4096 keys (at least those of the wide-vector path)
+  const int64_t per_chunk = kLargeTopkSegments;
   const int64_t chunks = (n + large_score_chunk() - 1) / large_score_chunk();
   return std::max<int64_t>(1, std::min<int64_t>(1024, std::max((n + 4095) / 4096, chunks * per_chunk)));
 }
@@ -272,6 +274,13 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.off_nx = int(cb->info.off_nx);
   v.off_nr = int(cb->info.off_nr);
   v.tail_bits = cb->info.index_bits_total - cb->desc.d;
+  v.sq_ok = 0;
+  if (!cb->uniform && int(cb->bits.size()) == cb->desc.d && cb->desc.d > 4) {
+    bool ok = true;
+    for (int i = 0; i < cb->desc.d; ++i)
+      ok = ok && (i < 4 ? cb->bits[i] >= 1 && cb->bits[i] <= 5 : cb->bits[i] == 1);
+    v.sq_ok = ok;
+  }
   v.rot = cb->dev.rot;
   v.rot_hi = cb->dev.rot_hi;
   v.rot_lo = cb->dev.rot_lo;
@@ -454,14 +463,16 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   const CodecView cv = make_view(cb);
   float* qr = static_cast<float*>(workspace);
   float* qs = qr + nq * cb->desc.d;
-  QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
-  tq_status st = map_hip(launch_query_prep(cv, qa, s));
-  if (st != TQ_OK) return st;
   if (cb->desc.d != 128) {
+    tq_status st = map_hip(launch_query_prep_large(cb->device, cv, q, nq, head, qr, qs, s));
+    if (st != TQ_OK) return st;
     void* lw = static_cast<uint8_t*>(workspace) + ((size_t(nq) * (cb->desc.d + std::max(cb->m, 1)) * 4 + 255) & ~size_t(255));
     return map_hip(launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
                                       scores, lw, s, nullptr, nullptr));
   }
+  QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
+  tq_status st = map_hip(launch_query_prep(cv, qa, s));
+  if (st != TQ_OK) return st;
   return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s));
 }
 
@@ -557,14 +568,13 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   float* pss = reinterpret_cast<float*>(w);
   w += round(ps * 4);
   int64_t* psi = reinterpret_cast<int64_t*>(w);
-  QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
-  tq_status st = map_hip(launch_query_prep(cv, qa, s));
-  if (st != TQ_OK) return st;
   if (cb->desc.d != 128) {
-    // key chunks of large_score_chunk() rows, each cut into segments of up
-    // to 4096 keys; the partial lists of all chunks are merged at the end
+    tq_status st = map_hip(launch_query_prep_large(cb->device, cv, q, nq, 0, qr, qs, s));
+    if (st != TQ_OK) return st;
+    // key chunks of large_score_chunk() rows, each cut into 4 segments; the
+    // partial lists of all chunks are merged at the end
     struct Ctx { int64_t nq; int k; int per_chunk; int total; float* ps; int64_t* pi; };
-    const int per_chunk = int((large_score_chunk() + 4095) / 4096);
+    const int per_chunk = kLargeTopkSegments;
     const int64_t nchunks = (n + large_score_chunk() - 1) / large_score_chunk();
     Ctx ctx{nq, k, per_chunk, int(nchunks * per_chunk), pss, psi};
     if (ctx.total > nseg) return TQ_EUNSUPPORTED;
@@ -581,6 +591,9 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
     if (e != hipSuccess) return map_hip(e);
     return map_hip(launch_topk_merge(pss, psi, nq, ctx.total, k, top_scores, top_ids, s));
   }
+  QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
+  tq_status st = map_hip(launch_query_prep(cv, qa, s));
+  if (st != TQ_OK) return st;
   return map_hip(launch_topk(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, k, top_scores,
                              top_ids, sc, pss, psi, nseg, s));
 }

@@ -12,6 +12,12 @@
 // w_p q'), rows 8..15 the sign part (hi and lo of qs); the +-1 operands are
 // built from the key bits with one shift and one and-or per fp16 pair.
 //
+// SpectralQuant keys (UB = 0): dims 4..127 carry one bit each, so their part
+// of <q', c(idx)> is linear in plane 0 (c_i(b) = mu_i + gamma_i s) and runs
+// on the same MFMA chain (rows 0..7 only); the multi-bit dims 0..3 (index bits
+// in plane 0 plus the tail byte) read a per-query LDS table of q'_i c_i(idx),
+// and the 4 QJL signs are a 4-term dot product on the VALU.
+//
 // Values: TurboQuant-mse col records with 4 index bits: 8 consecutive tokens
 // of one coordinate are one dword; a 256-entry LDS table maps each byte (two
 // tokens) to the fp16 pair of their centroids, giving the B operand of
@@ -75,8 +81,12 @@ __device__ __forceinline__ float grp_sum(float v) {
 template <int G, int UB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
+  constexpr bool SQ = UB == 0;
   __shared__ float sqr[4][D];
   __shared__ float sqs[4][D];
+  __shared__ float slow[SQ ? 4 : 1][4][kMaxLevels];  // SQ: q'_i c_i(idx), dims 0..3
+  __shared__ float smu[4];
+  __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
   __shared__ uint32_t slut[256];
   __shared__ __align__(16) uint16_t sP[4][16][64];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
@@ -87,28 +97,61 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
     const int gg = e / D, i = e % D;
     const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
     sqr[gg][i] = gg < G ? a.qr[qi * D + i] : 0.f;
-    sqs[gg][i] = gg < G ? a.qs[qi * kc.m + i] : 0.f;
+    sqs[gg][i] = gg < G && i < kc.m ? a.qs[qi * kc.m + i] : 0.f;
   }
+  const int hk = kc.heads > 1 ? g : 0;
+  const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   {
     const int t = threadIdx.x;  // 256 threads: one table entry each
     slut[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
   }
   for (int e = threadIdx.x; e < 4 * 16 * 64; e += blockDim.x) (&sP[0][0][0])[e] = 0;
   __syncthreads();
+  if (SQ) {
+    for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
+      const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
+      slow[gg][i][l] = sqr[gg][i] * kcen[i * kMaxLevels + l];
+    }
+    {
+      const uint32_t t = threadIdx.x;  // 256 threads: one tail-byte pattern each
+      uint32_t packed = 0;
+      for (int i = 0; i < 4; ++i) {
+        const int bi = kc.dim_bits[i];
+        uint32_t v = 0;
+        for (int pl = 1; pl < bi; ++pl) v |= ((t >> (kc.bitpos[pl * D + i] - D)) & 1u) << pl;
+        packed |= v << (5 * i);
+      }
+      stail[t] = packed;
+    }
+    if (threadIdx.x < 64) {  // sum_{i >= 4} mu_i q'_i per query
+      const int lane = threadIdx.x;
+      for (int gg = 0; gg < 4; ++gg) {
+        float v = 0.f;
+        for (int i = 4 + lane; i < D; i += 64)
+          v += 0.5f * (kcen[i * kMaxLevels] + kcen[i * kMaxLevels + 1]) * sqr[gg][i];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) smu[gg] = v;
+      }
+    }
+    __syncthreads();
+  }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g16 = lane >> 4;
 
   // ---- score A fragments: chunk (p, c): lane row r = n, dims 32 g16 + 8c + s
   float wp[2];
-  if (UB == 2) {
+  if (SQ) {
+    wp[0] = wp[1] = 0.f;
+  } else if (UB == 2) {
     wp[0] = 0.5f * (kc.ucen[3] - kc.ucen[2]);
     wp[1] = 0.5f * (kc.ucen[3] + kc.ucen[2]);
   } else {
     wp[0] = kc.ucen[1];
     wp[1] = 0.f;
   }
-  constexpr int NP = UB + 1;  // planes incl. signs
+  constexpr int NP = SQ ? 1 : UB + 1;  // +-1 planes in the MFMA chain (incl. signs)
   u32x4 A[NP][4];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -124,8 +167,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
         const int dim = 32 * g16 + 8 * c + s;
         float x = 0.f;
         if (gq < G) {
-          if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
-          if (rowsig && sign_part) x = sqs[gq][dim];
+          if (SQ) {
+            if (!rowsig && dim >= 4) x = 0.5f * (kcen[dim * kMaxLevels + 1] - kcen[dim * kMaxLevels]) * sqr[gq][dim];
+          } else {
+            if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
+            if (rowsig && sign_part) x = sqs[gq][dim];
+          }
         }
         const float hi = f16v(f16b(x));
         v[s] = lo ? x - hi : x;
@@ -158,7 +205,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
       const int tok = 16 * nb + n;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int off = p < UB ? p * kTile * 16 : kc.off_signs;
+        const int off = SQ ? 0 : (p < UB ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
         kw[nb][p] = *reinterpret_cast<const uint32_t*>(kt + off + tok * 16 + 4 * g16);
       }
     }
@@ -169,12 +216,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
       for (int kc2 = 0; kc2 < 2; ++kc2)
         vw[vb][kc2] = *reinterpret_cast<const uint32_t*>(vt + (16 * vb + n) * 32 + 16 * kc2 + 4 * g16);
     float nx[4], nr[4], nv[4];
+    uint32_t sqb[4];  // SQ: plane-0 byte 0 | tail byte << 8 | sign byte << 16
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int tok = 16 * nb + n;
       nx[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * tok));
       nr[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * tok));
       nv[nb] = h2f(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok));
+      if (SQ)
+        sqb[nb] = uint32_t(kt[tok * 16]) | (uint32_t(kt[kTile * 16 + tok]) << 8) |
+                  (uint32_t(kt[kc.off_signs + tok]) << 16);
     }
     // ---- scores
     float lg[4][2];
@@ -185,8 +236,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc = mfma16(A[p][c], expand_pm1((kw[nb][p] >> (8 * c)) & 0xffu), acc);
-      const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
-      const float sa = __shfl_xor(xa, 32, 64), sb = __shfl_xor(xb, 32, 64);
+      float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
+      float sa, sb;
+      if (SQ) {
+        // dims 0..3 from the table, the mu part, and the 4 signs
+        const uint32_t w = sqb[nb];
+        const uint32_t tl = stail[(w >> 8) & 0xffu];
+        int idx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) idx[i] = int(((w >> i) & 1u) | ((tl >> (5 * i)) & 31u));
+        const int q0 = (2 * g16) & 3, q1 = q0 + 1;
+        float ea = smu[q0], eb = smu[q1];
+        sa = 0.f;
+        sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ea += slow[q0][i][idx[i]];
+          eb += slow[q1][i][idx[i]];
+          const float sg = (w >> (16 + i)) & 1u ? 1.f : -1.f;
+          sa = fmaf(sg, sqs[q0][i], sa);
+          sb = fmaf(sg, sqs[q1][i], sb);
+        }
+        xa += ea;
+        xb += eb;
+      } else {
+        sa = __shfl_xor(xa, 32, 64);
+        sb = __shfl_xor(xb, 32, 64);
+      }
       const int tok = tile * kTile + 16 * nb + n;
       const bool valid = tok < len;
       const float coef = nr[nb] * coef_scale;
@@ -273,11 +349,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
 
 }  // namespace
 
+// SpectralQuant key codec the MFMA kernel handles: one bit on dims 4..127,
+// 1..5 bits on dims 0..3 whose extra bits fit one tail byte, 4 QJL signs.
+static bool sq_keys(const CodecView& kv) {
+  if (kv.uniform || kv.mode != TQ_PROD || kv.m != 4 || kv.layout != TQ_LAYOUT_ROW) return false;
+  if (kv.tail_bits > 8 || kv.code_bytes != 17 - (kv.tail_bits == 0) || kv.sign_bytes != 1) return false;
+  return kv.sq_ok != 0;
+}
+
 bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G) {
-  return kv.d == D && vv.d == D && kv.uniform && kv.mode == TQ_PROD && kv.m == D &&
-         kv.layout == TQ_LAYOUT_ROW && (kv.ubits == 1 || kv.ubits == 2) && vv.uniform &&
-         vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL && vv.ubits == 4 &&
-         (G == 1 || G == 2 || G == 4);
+  const bool keys = kv.d == D && kv.layout == TQ_LAYOUT_ROW &&
+                    ((kv.uniform && kv.mode == TQ_PROD && kv.m == D && (kv.ubits == 1 || kv.ubits == 2)) ||
+                     sq_keys(kv));
+  return keys && vv.d == D && vv.uniform && vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL &&
+         vv.ubits == 4 && (G == 1 || G == 2 || G == 4);
 }
 
 hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
@@ -285,7 +370,9 @@ hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const De
   const int G = a.Hq / a.Hkv;
   dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
 #define TQ_LAUNCH(GG, UU) hipLaunchKernelGGL((decode_mfma_kernel<GG, UU>), grid, dim3(256), 0, s, kv, vv, a)
-  if (kv.ubits == 2) {
+  if (!kv.uniform) {
+    if (G == 4) TQ_LAUNCH(4, 0); else if (G == 2) TQ_LAUNCH(2, 0); else TQ_LAUNCH(1, 0);
+  } else if (kv.ubits == 2) {
     if (G == 4) TQ_LAUNCH(4, 2); else if (G == 2) TQ_LAUNCH(2, 2); else TQ_LAUNCH(1, 2);
   } else {
     if (G == 4) TQ_LAUNCH(4, 1); else if (G == 2) TQ_LAUNCH(2, 1); else TQ_LAUNCH(1, 1);

@@ -15,6 +15,7 @@ struct CodecView {
   int code_bytes, sign_bytes, tile_bytes;
   int off_signs, off_nx, off_nr;
   int tail_bits;  // ROW, non-uniform: index bits beyond plane 0 (<= 32)
+  int sq_ok;      // non-uniform with 1 bit on dims 4.. and 1..5 bits on dims 0..3
   const float* rot;
   const uint16_t* rot_hi;
   const uint16_t* rot_lo;
@@ -107,6 +108,8 @@ size_t large_score_workspace(const CodecView& cv, int64_t nq);
 hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, const float* qs,
                               int64_t nq, const uint8_t* rec, int64_t n, float* out, void* ws,
                               hipStream_t s, ChunkFn chunk_cb, void* cb_ctx);
+hipError_t launch_query_prep_large(int device, const CodecView& cv, const float* q, int64_t nq, int head,
+                                   float* qr, float* qs, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 }  // namespace tq

@@ -85,120 +85,146 @@ __global__ void cat3_kernel(const uint16_t* hi, const uint16_t* lo, int64_t rows
   o[2 * cols + c] = hi[e];
 }
 
-// Thread per (row, 32-coordinate word).  Rows >= rows_valid (padding of the
-// last tile) get zero records.
+// One wave per row, 64 coordinates per step (lane = coordinate): index by the
+// thresholds (scaled by w[row] instead of dividing y), bit planes by ballot,
+// residual r = y - c[idx] split into rcat [rows][3m] = [hi | hi | lo] of 32 r,
+// and ||r||^2 by a wave reduction.  Rows >= rows_valid (padding of the last
+// tile) get zero records.
 __global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float* y, const float* w,
                                                        const float* nx, int64_t row0, int64_t rows,
                                                        int64_t rows_valid, uint8_t* rec, uint16_t* rcat,
                                                        float* rr) {
-  const int d = cv.d, words = d / 32;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = gid / words;
-  const int wd = int(gid % words);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int64_t grow = row0 + row;  // row within the whole call
-  const int64_t tile = grow / kTile;
-  const int slot = int(grow % kTile);
-  uint8_t* trec = rec + tile * cv.tile_bytes;
-  const bool valid = row < rows_valid;
-  const int ub = cv.ubits;
-  uint32_t planes[kMaxBits] = {0, 0, 0, 0, 0};
-  float rsum = 0.f;
-  if (valid) {
-    const float wr = w[row];
-    const float inv = 1.f / wr;
-    const float* yr = y + row * d + 32 * wd;
-    for (int k = 0; k < 32; ++k) {
-      const float v = yr[k];
-      int idx = 0;
-      for (int t = 0; t < (1 << ub) - 1; ++t) idx += v >= cv.uthr[t] * wr ? 1 : 0;
-      for (int p = 0; p < ub; ++p) planes[p] |= uint32_t((idx >> p) & 1) << k;
-      if (cv.mode == TQ_PROD) {
-        const int dim = 32 * wd + k;
-        const float r = v * inv - cv.ucen[idx];
-        if (dim < cv.m) {
-          rsum = fmaf(r, r, rsum);
-          const float rs = 32.f * r;
-          const uint16_t h = f16b(rs);
-          uint16_t* o = rcat + row * 3 * cv.m;
-          o[dim] = h;
-          o[cv.m + dim] = h;
-          o[2 * cv.m + dim] = f16b(rs - f16v(h));
-        }
-      }
-    }
-  }
-  for (int p = 0; p < ub; ++p) {
-    const int byte = p * (d / 8) + 4 * wd;  // position in the row bit string
-    const int chunk = byte / 16, within = byte % 16;
-    *reinterpret_cast<uint32_t*>(trec + size_t(chunk) * kTile * 16 + size_t(slot) * 16 + within) = planes[p];
-  }
-  if (cv.mode == TQ_PROD && valid && rsum != 0.f) atomicAdd(&rr[row], rsum);
-  if (wd == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = valid ? f16b(nx[row]) : uint16_t(0);
-}
-
-// Thread per (row, 32-sign word); word 0 also writes n_r.
-__global__ __launch_bounds__(256) void signpack_kernel(CodecView cv, const float* z, const float* rr,
-                                                       int64_t row0, int64_t rows, int64_t rows_valid,
-                                                       uint8_t* rec) {
-  const int m = cv.m, words = (m + 31) / 32;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = gid / words;
-  const int wd = int(gid % words);
-  if (row >= rows) return;
+  const int d = cv.d, ub = cv.ubits, nthr = (1 << ub) - 1;
+  const bool prod = cv.mode == TQ_PROD;
   const int64_t grow = row0 + row;
   uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
   const int slot = int(grow % kTile);
   const bool valid = row < rows_valid;
-  uint32_t bits = 0;
-  if (valid)
-    for (int k = 0; k < 32 && 32 * wd + k < m; ++k)
-      bits |= uint32_t(z[row * m + 32 * wd + k] >= 0.f) << k;
-  const int byte = 4 * wd;
-  const int chunk = byte / 16, within = byte % 16;
-  const int width = min(16, cv.sign_bytes - chunk * 16);
-  uint8_t* dst = trec + cv.off_signs + size_t(chunk) * kTile * 16 + size_t(slot) * width + within;
-  for (int b = 0; b < 4 && within + b < width; ++b) dst[b] = uint8_t(bits >> (8 * b));
-  if (wd == 0)
+  const float wr = valid ? w[row] : 1.f;
+  const float inv = 1.f / wr;
+  float thr[kMaxLevels - 1];
+#pragma unroll
+  for (int t = 0; t < kMaxLevels - 1; ++t) thr[t] = cv.uthr[t] * wr;
+  float rsum = 0.f;
+  for (int j = 0; j < d / 64; ++j) {
+    const int dim = 64 * j + lane;
+    int idx = 0;
+    float c = cv.ucen[0];
+    float v = 0.f;
+    if (valid) {
+      v = y[row * d + dim];
+#pragma unroll
+      for (int t = 0; t < kMaxLevels - 1; ++t)
+        if (t < nthr && v >= thr[t]) { idx = t + 1; c = cv.ucen[t + 1]; }
+    }
+    if (prod && valid && dim < cv.m) {
+      const float r = v * inv - c;
+      rsum = fmaf(r, r, rsum);
+      const float rs = 32.f * r;
+      const uint16_t h = f16b(rs);
+      uint16_t* o = rcat + row * 3 * cv.m;
+      o[dim] = h;
+      o[cv.m + dim] = h;
+      o[2 * cv.m + dim] = f16b(rs - f16v(h));
+    }
+    for (int p = 0; p < ub; ++p) {
+      const uint64_t mask = __ballot((idx >> p) & 1);
+      if (lane < 2) {
+        const int byte = p * (d / 8) + 8 * j + 4 * lane;  // position in the row bit string
+        *reinterpret_cast<uint32_t*>(trec + size_t(byte / 16) * kTile * 16 + size_t(slot) * 16 + byte % 16) =
+            uint32_t(mask >> (32 * lane));
+      }
+    }
+  }
+  if (prod) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rsum += __shfl_xor(rsum, o, 64);
+    if (lane == 0) rr[row] = rsum;
+  }
+  if (lane == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = valid ? f16b(nx[row]) : uint16_t(0);
+}
+
+// One wave per row: sign bits [z >= 0] by ballot (64 per step) and n_r.
+__global__ __launch_bounds__(256) void signpack_kernel(CodecView cv, const float* z, const float* rr,
+                                                       int64_t row0, int64_t rows, int64_t rows_valid,
+                                                       uint8_t* rec) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int m = cv.m;
+  const int64_t grow = row0 + row;
+  uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
+  const int slot = int(grow % kTile);
+  const bool valid = row < rows_valid;
+  for (int j = 0; j < m / 64; ++j) {
+    const bool bit = valid && z[row * m + 64 * j + lane] >= 0.f;
+    const uint64_t mask = __ballot(bit);
+    if (lane < 2) {
+      const int byte = 8 * j + 4 * lane;  // all sign chunks are 16 bytes wide (m % 128 == 0)
+      *reinterpret_cast<uint32_t*>(trec + cv.off_signs + size_t(byte / 16) * kTile * 16 + size_t(slot) * 16 +
+                                   byte % 16) = uint32_t(mask >> (32 * lane));
+    }
+  }
+  if (lane == 0)
     *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = valid ? f16b(sqrtf(rr[row])) : uint16_t(0);
 }
 
-// Thread per (row, 32-coordinate word): key row [c[idx] | +-n_r] in fp16
-// (kcat, [rows][d + m]); +-n_r is exact since n_r is stored as fp16.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// One wave per key row: kcat row [c[idx] | +-n_r] in fp16 ([rows][d + m]),
+// 8 coordinates (one byte of each bit plane) and one 16-byte store per lane
+// and step; +-n_r is exact since n_r is stored as fp16.
 __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_t* rec, int64_t row0,
                                                       int64_t rows, uint16_t* kcat) {
-  const int d = cv.d, words = d / 32, swords = cv.mode == TQ_PROD ? (cv.m + 31) / 32 : 0;
-  const int kw = d + (cv.mode == TQ_PROD ? cv.m : 0);
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t row = gid / (words + swords);
-  const int wd = int(gid % (words + swords));
+  __shared__ uint16_t scen[kMaxLevels];
+  if (threadIdx.x < kMaxLevels) scen[threadIdx.x] = f16b(cv.ucen[threadIdx.x]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  const bool prod = cv.mode == TQ_PROD;
+  const int d = cv.d, m = prod ? cv.m : 0, kw = d + m, ub = cv.ubits;
   const int64_t grow = row0 + row;
   const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
   const int slot = int(grow % kTile);
   uint16_t* out = kcat + row * kw;
-  if (wd < words) {
-    uint32_t planes[kMaxBits];
-    for (int p = 0; p < cv.ubits; ++p) {
-      const int byte = p * (d / 8) + 4 * wd;
-      planes[p] = *reinterpret_cast<const uint32_t*>(trec + size_t(byte / 16) * kTile * 16 + size_t(slot) * 16 + byte % 16);
+  for (int c8 = lane; c8 < d / 8; c8 += 64) {
+    uint32_t pb[kMaxBits];
+#pragma unroll
+    for (int p = 0; p < kMaxBits; ++p) {
+      const int byte = p * (d / 8) + c8;
+      pb[p] = p < ub ? trec[size_t(byte / 16) * kTile * 16 + size_t(slot) * 16 + byte % 16] : 0u;
     }
-    for (int k = 0; k < 32; ++k) {
-      int idx = 0;
-      for (int p = 0; p < cv.ubits; ++p) idx |= int((planes[p] >> k) & 1) << p;
-      out[32 * wd + k] = f16b(cv.ucen[idx]);
+    u32x4v o;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2 * k2 + h;
+        int idx = 0;
+#pragma unroll
+        for (int p = 0; p < kMaxBits; ++p) idx |= int((pb[p] >> k) & 1u) << p;
+        pair |= uint32_t(scen[idx]) << (16 * h);
+      }
+      o[k2] = pair;
     }
-  } else {
-    const int sw = wd - words;
-    const int byte = 4 * sw;
-    const int chunk = byte / 16, within = byte % 16;
-    const int width = min(16, cv.sign_bytes - chunk * 16);
-    const uint8_t* src = trec + cv.off_signs + size_t(chunk) * kTile * 16 + size_t(slot) * width + within;
-    uint32_t bits = 0;
-    for (int b = 0; b < 4 && within + b < width; ++b) bits |= uint32_t(src[b]) << (8 * b);
-    const uint16_t nr = *reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * slot);
-    for (int k = 0; k < 32 && 32 * sw + k < cv.m; ++k)
-      out[d + 32 * sw + k] = (bits >> k) & 1 ? nr : uint16_t(nr ^ 0x8000u);
+    *reinterpret_cast<u32x4v*>(out + 8 * c8) = o;
+  }
+  if (prod) {
+    const uint32_t nr = *reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * slot);
+    const uint32_t nn = nr ^ 0x8000u;
+    for (int c8 = lane; c8 < m / 8; c8 += 64) {
+      const uint32_t sb = trec[cv.off_signs + size_t(c8 / 16) * kTile * 16 + size_t(slot) * 16 + c8 % 16];
+      u32x4v o;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        o[k2] = ((sb >> (2 * k2)) & 1u ? nr : nn) | (((sb >> (2 * k2 + 1)) & 1u ? nr : nn) << 16);
+      *reinterpret_cast<u32x4v*>(out + d + 8 * c8) = o;
+    }
   }
 }
 
@@ -271,6 +297,16 @@ hipError_t gemm_abt(rocblas_handle h, const uint16_t* a, const uint16_t* b, floa
 }
 
 unsigned blocks_for(int64_t threads, int bs = 256) { return unsigned((threads + bs - 1) / bs); }
+
+// Row-major C[M][N] = A[M][K] * B[N][K]^T in fp32.
+hipError_t sgemm_abt(rocblas_handle h, const float* a, const float* b, float* c, int64_t M, int64_t N,
+                     int64_t K) {
+  const float one = 1.f, zero = 0.f;
+  rocblas_status st = rocblas_sgemm(h, rocblas_operation_transpose, rocblas_operation_none, rocblas_int(N),
+                                    rocblas_int(M), rocblas_int(K), &one, b, rocblas_int(K), a,
+                                    rocblas_int(K), &zero, c, rocblas_int(N));
+  return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
+}
 
 }  // namespace
 
@@ -347,23 +383,37 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
           if ((e = hipGetLastError()) != hipSuccess) return e;
           if ((e = gemm_abt(h, W.xcat, W.bpi, W.y, valid, d, 3 * d, 3 * d, 3 * d, d, false)) != hipSuccess)
             return e;
-          if (prod && (e = launch_fill_zero(W.rr, valid, s)) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(quantize_kernel, dim3(blocks_for(rows * (d / 32))), dim3(256), 0, s, cv, W.y,
-                           W.w, W.nx, r0, rows, valid, rec, W.rcat, W.rr);
+        hipLaunchKernelGGL(quantize_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, cv, W.y, W.w,
+                           W.nx, r0, rows, valid, rec, W.rcat, W.rr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (prod) {
           // z = [rh | rh | rl] [S_hi | S_lo | S_hi]^T  (z reuses the y buffer)
           if (valid > 0 &&
               (e = gemm_abt(h, W.rcat, W.bs, W.y, valid, m, 3 * m, 3 * m, 3 * m, m, false)) != hipSuccess)
             return e;
-          hipLaunchKernelGGL(signpack_kernel, dim3(blocks_for(rows * ((m + 31) / 32))), dim3(256), 0, s,
-                             cv, W.y, W.rr, r0, rows, valid, rec);
+          hipLaunchKernelGGL(signpack_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, cv, W.y, W.rr,
+                             r0, rows, valid, rec);
           if ((e = hipGetLastError()) != hipSuccess) return e;
         }
       }
     }
   return hipSuccess;
+}
+
+// q' = Pi_head q and (prod) q_s = S q' for nq fp32 queries, as fp32 GEMMs.
+hipError_t launch_query_prep_large(int device, const CodecView& cv, const float* q, int64_t nq, int head,
+                                   float* qr, float* qs, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  rocblas_handle h = blas(device);
+  if (!h) return hipErrorLaunchFailure;
+  if (rocblas_set_stream(h, s) != rocblas_status_success) return hipErrorLaunchFailure;
+  const int d = cv.d;
+  const int hc = cv.heads > 1 ? head : 0;
+  hipError_t e = sgemm_abt(h, q, cv.rot + size_t(hc) * d * d, qr, nq, d, d);
+  if (e != hipSuccess || cv.mode != TQ_PROD) return e;
+  // q_s = S q'[0:m]: rows of qr have stride d, so m must equal d here
+  return sgemm_abt(h, qr, cv.sketch, qs, nq, cv.m, cv.m);
 }
 
 int64_t large_score_chunk() { return 65536; }
@@ -420,8 +470,7 @@ hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, 
   if (e != hipSuccess) return e;
   for (int64_t r0 = 0; r0 < n; r0 += NC) {
     const int64_t rows = std::min(NC, n - r0);
-    const int words = d / 32 + (prod ? (m + 31) / 32 : 0);
-    hipLaunchKernelGGL(dequant_kernel, dim3(blocks_for(rows * words)), dim3(256), 0, s, cv, rec, r0, rows,
+    hipLaunchKernelGGL(dequant_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, cv, rec, r0, rows,
                        W.kcat);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // [q_hi; q_lo] kcat^T  ->  part [2 nq][NC]

@@ -467,27 +467,42 @@ __global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, 
   }
 }
 
+// One wave per query: k rounds of a wave-wide argmax over the heads of the
+// sorted partial lists (lane j owns lists j, j + 64, ...).
 __global__ __launch_bounds__(64) void topk_merge_kernel(const float* ps, const int64_t* pi,
                                                         int nseg, int k, float* out_s,
                                                         int64_t* out_i) {
+  __shared__ int heads[1024];
   const int64_t qi = blockIdx.x;
-  if (threadIdx.x != 0) return;
-  // segments hold sorted lists; k-way merge by repeated selection
-  int heads[1024];
-  for (int s = 0; s < nseg; ++s) heads[s] = 0;
+  const int lane = threadIdx.x;
+  for (int sg = lane; sg < nseg; sg += 64) heads[sg] = 0;
+  __syncthreads();
+  const float* qps = ps + qi * nseg * k;
+  const int64_t* qpi = pi + qi * nseg * k;
   for (int r = 0; r < k; ++r) {
-    int bs = -1;
-    float best_s = -INFINITY;
-    int64_t best_i = INT64_MAX;
-    for (int s = 0; s < nseg; ++s) {
-      if (heads[s] >= k) continue;
-      const float v = ps[(qi * nseg + s) * k + heads[s]];
-      const int64_t id = pi[(qi * nseg + s) * k + heads[s]];
-      if (bs < 0 || better(v, id, best_s, best_i)) { bs = s; best_s = v; best_i = id; }
+    float bs = -INFINITY;
+    int64_t bi = INT64_MAX;
+    int bseg = -1;
+    for (int sg = lane; sg < nseg; sg += 64) {
+      const int h = heads[sg];
+      if (h >= k) continue;
+      const float v = qps[sg * k + h];
+      const int64_t id = qpi[sg * k + h];
+      if (bseg < 0 || better(v, id, bs, bi)) { bs = v; bi = id; bseg = sg; }
     }
-    out_s[qi * k + r] = best_s;
-    out_i[qi * k + r] = best_i;
-    if (bs >= 0) ++heads[bs];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float os = __shfl_xor(bs, o, 64);
+      const int64_t oi = __shfl_xor(bi, o, 64);
+      const int oseg = __shfl_xor(bseg, o, 64);
+      if (oseg >= 0 && (bseg < 0 || better(os, oi, bs, bi))) { bs = os; bi = oi; bseg = oseg; }
+    }
+    if (lane == 0) {
+      out_s[qi * k + r] = bs;
+      out_i[qi * k + r] = bi;
+      if (bseg >= 0) ++heads[bseg];
+    }
+    __syncthreads();
   }
 }
 
