@@ -26,8 +26,8 @@ tq_status upload(T** dst, const T* src, size_t count) {
 
 void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
-  void* ptrs[] = {t.rot, t.rot_hi, t.rot_lo, t.sketch, t.sketch_hi, t.sketch_lo,
-                  t.thr, t.cen, t.bitpos, t.dim_bits};
+  void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
+                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -209,8 +209,15 @@ tq_status build_device(tq_codebook* cb) {
     hi[e] = f32_to_f16_rne(v);
     lo[e] = f32_to_f16_rne(v - f16_to_f32(hi[e]));
   }
+  // transposed copies: query rotation reads them column-coalesced
+  std::vector<float> rt(nr);
+  for (size_t hh = 0; hh < nr / (size_t(d) * d); ++hh)
+    for (int i = 0; i < d; ++i)
+      for (int k = 0; k < d; ++k)
+        rt[(hh * d + k) * d + i] = cb->rot32[(hh * d + i) * d + k];
   tq_status st;
   if ((st = upload(&cb->dev.rot, cb->rot32.data(), nr)) != TQ_OK) return st;
+  if ((st = upload(&cb->dev.rot_t, rt.data(), nr)) != TQ_OK) return st;
   if ((st = upload(&cb->dev.rot_hi, hi.data(), nr)) != TQ_OK) return st;
   if ((st = upload(&cb->dev.rot_lo, lo.data(), nr)) != TQ_OK) return st;
   if (!cb->sketch32.empty()) {
@@ -220,7 +227,12 @@ tq_status build_device(tq_codebook* cb) {
       shi[e] = f32_to_f16_rne(cb->sketch32[e]);
       slo[e] = f32_to_f16_rne(cb->sketch32[e] - f16_to_f32(shi[e]));
     }
+    const int m = cb->m;
+    std::vector<float> st_(ns);
+    for (int j = 0; j < m; ++j)
+      for (int k = 0; k < m; ++k) st_[size_t(k) * m + j] = cb->sketch32[size_t(j) * m + k];
     if ((st = upload(&cb->dev.sketch, cb->sketch32.data(), ns)) != TQ_OK) return st;
+    if ((st = upload(&cb->dev.sketch_t, st_.data(), ns)) != TQ_OK) return st;
     if ((st = upload(&cb->dev.sketch_hi, shi.data(), ns)) != TQ_OK) return st;
     if ((st = upload(&cb->dev.sketch_lo, slo.data(), ns)) != TQ_OK) return st;
   }
@@ -282,9 +294,11 @@ CodecView tq::make_view(const tq_codebook* cb) {
     v.sq_ok = ok;
   }
   v.rot = cb->dev.rot;
+  v.rot_t = cb->dev.rot_t;
   v.rot_hi = cb->dev.rot_hi;
   v.rot_lo = cb->dev.rot_lo;
   v.sketch = cb->dev.sketch;
+  v.sketch_t = cb->dev.sketch_t;
   v.sk_hi = cb->dev.sketch_hi;
   v.sk_lo = cb->dev.sketch_lo;
   v.thr = cb->dev.thr;
@@ -529,8 +543,16 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   da.max_tokens = kv->max_tokens;
   da.seq_lens = kv->seq_lens;
   da.scale = softmax_scale;
-  da.chunk_tiles = kDecodeChunkTiles;
-  da.nsplit = int(decode_nsplit(kv->max_tokens));
+  // splits of 8 tiles, widened while the grid keeps >= 2048 blocks (fewer
+  // partials and a longer tile loop per block for large batches); never more
+  // splits than the workspace holds
+  {
+    const int64_t ntiles = (int64_t(kv->max_tokens) + kTile - 1) / kTile;
+    int chunk = kDecodeChunkTiles;
+    while (chunk < 64 && int64_t(B) * Hkv * ((ntiles + 2 * chunk - 1) / (2 * chunk)) >= 2048) chunk *= 2;
+    da.chunk_tiles = chunk;
+    da.nsplit = int(std::max<int64_t>(1, (ntiles + chunk - 1) / chunk));
+  }
   da.part = part;
   da.out = out;
   return map_hip(launch_decode(kc, vc, da, s));

@@ -53,42 +53,83 @@ __device__ __forceinline__ float f16v(uint32_t h) {
 }
 __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
 
-// 8 bits -> 8 fp16 values +1 (bit set) / -1 (bit clear), element k from bit k.
-__device__ __forceinline__ u32x4 expand_pm1(uint32_t byte) {
-  const uint32_t nb = (~byte) & 0xffu;       // sign bit = NOT bit
-  const uint32_t x2 = nb | (nb << 15);       // bit k at k and k + 15
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Byte c of w -> 8 fp16 values +1 (bit set) / -1 (bit clear), element k from
+// bit k: the byte is copied into both 16-bit halves (one byte permute), each
+// pair of elements takes one packed 16-bit shift (bit 2j to bit 15 of the low
+// half, bit 2j+1 to bit 15 of the high half) and one and-xor with the fp16
+// pattern of -1.
+template <int C>
+__device__ __forceinline__ u32x4 expand_pm1(uint32_t w) {
+  // selector: bytes 0 and 2 <- byte C of w, bytes 1 and 3 <- 0
+  const uint32_t pair = __builtin_amdgcn_perm(0u, w, 0x0C000C00u | (C << 16) | C);
+  const u16x2 pv = __builtin_bit_cast(u16x2, pair);
   u32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t sp = x2 << (15 - 2 * j);  // bit 2j -> 15, bit 2j+1 -> 31
-    r[j] = (sp & 0x80008000u) | 0x3C003C00u;
+    const u16x2 sh = pv << u16x2{(unsigned short)(15 - 2 * j), (unsigned short)(14 - 2 * j)};
+    r[j] = (__builtin_bit_cast(uint32_t, sh) & 0x80008000u) ^ 0xBC00BC00u;
   }
   return r;
 }
 
+// Reductions over the 16 lanes of a row with DPP row rotations (no LDS
+// round trips), and exchanges with the lane 32 (or 16) positions away with
+// the gfx950 permlane swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 template <int G>
 __device__ __forceinline__ float grp_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+  v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp<0x122>(v));  // row_ror:2
+  return fmaxf(v, dpp<0x121>(v));  // row_ror:1
 }
 __device__ __forceinline__ float grp_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp<0x128>(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x122>(v);
+  return v + dpp<0x121>(v);
+}
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+// 4 x 4 transpose of (16-lane row, register): on return register k of row r
+// holds register r of row k (two permlane16 swaps, then two permlane32 swaps).
+__device__ __forceinline__ u32x4 transpose4(u32x4 m, int lane) {
+  (void)lane;
+  auto a = __builtin_amdgcn_permlane16_swap(m[0], m[1], false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(m[2], m[3], false, false);
+  auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+  return u32x4{c[0], d[0], c[1], d[1]};
+}
+
+__device__ __forceinline__ float xor16(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
 }
 
 template <int G, int UB>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
   constexpr bool SQ = UB == 0;
   __shared__ float sqr[4][D];
   __shared__ float sqs[4][D];
   __shared__ float slow[SQ ? 4 : 1][4][kMaxLevels];  // SQ: q'_i c_i(idx), dims 0..3
   __shared__ float smu[4];
+  __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
-  __shared__ uint32_t slut[256];
-  __shared__ __align__(16) uint16_t sP[4][16][64];  // per wave: [query row][token] fp16 weights
+  // value byte (two 4-bit codes) -> fp16 pair, one copy per LDS bank: entry e
+  // of lane l sits at slut[e * 32 + l % 32], so the random lookups of a wave
+  // never conflict
+  __shared__ uint32_t slut[256 * 32];
+  constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
+  __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
   __shared__ float sacc[4][4][D];
 
@@ -103,9 +144,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   {
     const int t = threadIdx.x;  // 256 threads: one table entry each
-    slut[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+    const uint32_t e = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) slut[t * 32 + ((c + t) & 31)] = e;
   }
-  for (int e = threadIdx.x; e < 4 * 16 * 64; e += blockDim.x) (&sP[0][0][0])[e] = 0;
+  for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
+  if (SQ && threadIdx.x < D) {
+    const float c0 = kcen[threadIdx.x * kMaxLevels], c1 = kcen[threadIdx.x * kMaxLevels + 1];
+    sgam[threadIdx.x] = 0.5f * (c1 - c0);
+    smuv[threadIdx.x] = 0.5f * (c1 + c0);
+  }
   __syncthreads();
   if (SQ) {
     for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
@@ -127,8 +175,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
       const int lane = threadIdx.x;
       for (int gg = 0; gg < 4; ++gg) {
         float v = 0.f;
-        for (int i = 4 + lane; i < D; i += 64)
-          v += 0.5f * (kcen[i * kMaxLevels] + kcen[i * kMaxLevels + 1]) * sqr[gg][i];
+        for (int i = 4 + lane; i < D; i += 64) v += smuv[i] * sqr[gg][i];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
         if (lane == 0) smu[gg] = v;
@@ -152,7 +199,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
     wp[1] = 0.f;
   }
   constexpr int NP = SQ ? 1 : UB + 1;  // +-1 planes in the MFMA chain (incl. signs)
-  u32x4 A[NP][4];
+  // the A fragments depend on the lane only: wave 0 builds them once into LDS
+  // and every wave reads them back per tile (keeping them live across the
+  // tile loop would exceed the register budget)
+  __shared__ u32x4 sA[NP * 4][64];
+  if (wave == 0) {
 #pragma unroll
   for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -168,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
         float x = 0.f;
         if (gq < G) {
           if (SQ) {
-            if (!rowsig && dim >= 4) x = 0.5f * (kcen[dim * kMaxLevels + 1] - kcen[dim * kMaxLevels]) * sqr[gq][dim];
+            if (!rowsig && dim >= 4) x = sgam[dim] * sqr[gq][dim];
           } else {
             if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
             if (rowsig && sign_part) x = sqs[gq][dim];
@@ -177,9 +228,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
         const float hi = f16v(f16b(x));
         v[s] = lo ? x - hi : x;
       }
+      u32x4 f;
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) A[p][c][s2] = f16b(v[2 * s2]) | (f16b(v[2 * s2 + 1]) << 16);
+      for (int s2 = 0; s2 < 4; ++s2) f[s2] = f16b(v[2 * s2]) | (f16b(v[2 * s2 + 1]) << 16);
+      sA[p * 4 + c][lane] = f;
     }
+  }
+  __syncthreads();
 
   const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
   const int ntiles = (len + kTile - 1) / kTile;
@@ -195,47 +250,91 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
 
   const int t_begin = split * a.chunk_tiles;
   const int t_end = min(ntiles, t_begin + a.chunk_tiles);
-  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
+  // ---- loads of one tile: key planes/signs (dword g16 of token 16nb+n),
+  // value fields, fp16 norms (raw), SQ low/tail/sign bytes; the next tile's
+  // loads are issued before the current tile is processed
+  // (raw values only: no ALU on loaded registers here, so the loads of the
+  // next tile stay in flight while the current one is processed)
+  // per-token words (norms, SQ bytes) are loaded once per token, by lane
+  // (n, g16) for token 16 g16 + n, and shuffled to the lanes that use them
+  // 16-byte loads: lane (n, g16) loads the whole 16-byte row of token
+  // 16 g16 + n of each key plane, and 16 bytes of the value fields; a 4 x 4
+  // transpose across the four 16-lane rows (permlane swaps) then gives every
+  // lane the dwords its MFMA operands need.  One 16-byte load per lane moves
+  // four times the data of a dword load through the address unit.
+  struct TileRegs {
+    u32x4 kw4[NP], vw4[4];
+    uint32_t nx, nr, nv, tl, sg;
+  };
+  TileRegs cur, nxt;
+  auto load_tile = [&](int tile, TileRegs& R) {
     const uint8_t* kt = kbase + int64_t(tile) * kc.tile_bytes;
     const uint8_t* vt = vbase + int64_t(tile) * vc.tile_bytes;
-    // ---- loads: key planes/signs (dword g16 of token 16nb+n), value fields
-    uint32_t kw[4][NP];
+    const int tok = 16 * g16 + n;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int tok = 16 * nb + n;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int off = SQ ? 0 : (p < UB ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
-        kw[nb][p] = *reinterpret_cast<const uint32_t*>(kt + off + tok * 16 + 4 * g16);
-      }
+    for (int p = 0; p < NP; ++p) {
+      const int off = SQ ? 0 : (p < UB ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
+      R.kw4[p] = *reinterpret_cast<const u32x4*>(kt + off + tok * 16);
     }
-    uint32_t vw[8][2];
+    // load j: dim 16 (2j + g16/2) + n, bytes 16 (g16 % 2) .. + 15 of its field
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
+    for (int j = 0; j < 4; ++j)
+      R.vw4[j] = *reinterpret_cast<const u32x4*>(vt + (16 * (2 * j + (g16 >> 1)) + n) * 32 + 16 * (g16 & 1));
+    R.nx = *reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * tok);
+    R.nr = *reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * tok);
+    R.nv = *reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok);
+    if (SQ) {
+      R.tl = kt[kTile * 16 + tok];
+      R.sg = kt[kc.off_signs + tok];
+    }
+  };
+  // tiles tile, tile + 4, ... alternate between two register sets (no copies
+  // between them, so nothing waits for the next tile's loads early)
+  auto process = [&](const TileRegs& R, int tile) {
+    uint32_t kw[4][NP], vw[8][2];
 #pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2)
-        vw[vb][kc2] = *reinterpret_cast<const uint32_t*>(vt + (16 * vb + n) * 32 + 16 * kc2 + 4 * g16);
+    for (int p = 0; p < NP; ++p) {
+      const u32x4 t = transpose4(R.kw4[p], lane);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) kw[nb][p] = t[nb];  // dword g16 of token 16 nb + n
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 t = transpose4(R.vw4[j], lane);
+      vw[2 * j][0] = t[0];
+      vw[2 * j][1] = t[1];
+      vw[2 * j + 1][0] = t[2];
+      vw[2 * j + 1][1] = t[3];
+    }
     float nx[4], nr[4], nv[4];
     uint32_t sqb[4];  // SQ: plane-0 byte 0 | tail byte << 8 | sign byte << 16
+    const uint32_t kpack = R.nx | (R.nr << 16);
+    const uint32_t spack = SQ ? ((R.kw4[0][0] & 0xffu) | (R.tl << 8) | (R.sg << 16)) : 0u;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int tok = 16 * nb + n;
-      nx[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * tok));
-      nr[nb] = h2f(*reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * tok));
-      nv[nb] = h2f(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok));
-      if (SQ)
-        sqb[nb] = uint32_t(kt[tok * 16]) | (uint32_t(kt[kTile * 16 + tok]) << 8) |
-                  (uint32_t(kt[kc.off_signs + tok]) << 16);
+      const uint32_t kk = uint32_t(__shfl(int(kpack), 16 * nb + n, 64));
+      nx[nb] = h2f(uint16_t(kk & 0xffffu));
+      nr[nb] = h2f(uint16_t(kk >> 16));
+      nv[nb] = h2f(uint16_t(__shfl(int(R.nv), 16 * nb + n, 64)));
+      sqb[nb] = SQ ? uint32_t(__shfl(int(spack), 16 * nb + n, 64)) : 0u;
     }
     // ---- scores
     float lg[4][2];
+    u32x4 A[NP][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) A[p][c] = sA[p * 4 + c][lane];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc = mfma16(A[p][c], expand_pm1((kw[nb][p] >> (8 * c)) & 0xffu), acc);
+      for (int p = 0; p < NP; ++p) {
+        acc = mfma16(A[p][0], expand_pm1<0>(kw[nb][p]), acc);
+        acc = mfma16(A[p][1], expand_pm1<1>(kw[nb][p]), acc);
+        acc = mfma16(A[p][2], expand_pm1<2>(kw[nb][p]), acc);
+        acc = mfma16(A[p][3], expand_pm1<3>(kw[nb][p]), acc);
+      }
       float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
       float sa, sb;
       if (SQ) {
@@ -260,8 +359,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
         xa += ea;
         xb += eb;
       } else {
-        sa = __shfl_xor(xa, 32, 64);
-        sb = __shfl_xor(xb, 32, 64);
+        sa = xor32(xa, lane);
+        sb = xor32(xb, lane);
       }
       const int tok = tile * kTile + 16 * nb + n;
       const bool valid = tok < len;
@@ -290,7 +389,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
     }
     // rescale: accumulator rows = queries 0..3 in lane group 0
     const float al01 = alpha[0], al11 = alpha[1];
-    const float al2 = __shfl_xor(al01, 16, 64), al3 = __shfl_xor(al11, 16, 64);
+    const float al2 = xor16(al01, lane), al3 = xor16(al11, lane);
     __builtin_amdgcn_wave_barrier();
     // ---- P V_hat
     u32x4 Ap[2];
@@ -307,14 +406,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(CodecView kc, CodecVie
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const uint32_t w = vw[vb][kc2];
         u32x4 B;
-        B[0] = slut[w & 0xffu];
-        B[1] = slut[(w >> 8) & 0xffu];
-        B[2] = slut[(w >> 16) & 0xffu];
-        B[3] = slut[w >> 24];
+        const uint32_t* lut = slut + (lane & 31);
+        B[0] = lut[(w & 0xffu) * 32];
+        B[1] = lut[((w >> 8) & 0xffu) * 32];
+        B[2] = lut[((w >> 16) & 0xffu) * 32];
+        B[3] = lut[(w >> 24) * 32];
         accv[vb] = mfma16(Ap[kc2], B, accv[vb]);
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  TileRegs& ra = cur;
+  TileRegs& rb = nxt;
+  if (t_begin + wave < t_end) load_tile(t_begin + wave, ra);
+  // the prefetches are unconditional (clamped to the last tile, a harmless
+  // re-read) so that the wait counters stay exact across the loop
+  for (int tile = t_begin + wave; tile < t_end; tile += 8) {
+    load_tile(min(tile + 4, t_end - 1), rb);
+    process(ra, tile);
+    if (tile + 4 >= t_end) break;
+    load_tile(min(tile + 8, t_end - 1), ra);
+    process(rb, tile + 4);
   }
   // ---- merge the 4 waves: group-0 lanes hold rows (queries) 0..3 of coord 16vb+n
   if (g16 < 2 && n == 0) {

@@ -47,9 +47,11 @@ float f16_to_f32(uint16_t h);
 // Device tables of a codebook.
 struct DeviceTables {
   float* rot = nullptr;          // [H][d][d] fp32, row i = basis vector i
+  float* rot_t = nullptr;        // [H][d][d] fp32 transpose (column-coalesced reads)
   uint16_t* rot_hi = nullptr;    // [H][d][d] fp16 high part of 16 Pi
   uint16_t* rot_lo = nullptr;    // [H][d][d] fp16 residual part of 16 Pi
   float* sketch = nullptr;       // [m][m] fp32
+  float* sketch_t = nullptr;     // [m][m] fp32 transpose
   uint16_t* sketch_hi = nullptr; // [m][m] fp16 high part
   uint16_t* sketch_lo = nullptr; // [m][m] fp16 residual part
   float* thr = nullptr;          // [H][d][kMaxLevels] boundaries (unused = +inf)

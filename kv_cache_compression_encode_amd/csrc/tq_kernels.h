@@ -17,9 +17,11 @@ struct CodecView {
   int tail_bits;  // ROW, non-uniform: index bits beyond plane 0 (<= 32)
   int sq_ok;      // non-uniform with 1 bit on dims 4.. and 1..5 bits on dims 0..3
   const float* rot;
+  const float* rot_t;    // transpose of rot
   const uint16_t* rot_hi;
   const uint16_t* rot_lo;
   const float* sketch;
+  const float* sketch_t; // transpose of sketch
   const uint16_t* sk_hi;
   const uint16_t* sk_lo;
   const float* thr;

@@ -37,64 +37,75 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ----------------------------------------------------------- query prep
-// Block: qb consecutive queries (same rotation head); q in LDS, thread i
-// computes rotated coordinates i, i + 256, ... for all qb queries, so each
-// Pi element read from L2 serves qb queries; then qs = S q'[0:m] from LDS.
+// Block: qb (<= 8) consecutive queries of one rotation head, staged in LDS.
+// Thread t computes output coordinate t % 128 over the half t / 128 of the
+// reduction range, reading the transposed matrices column-coalesced.  All
+// matrix loads (Pi and, for the full sketch, S) are issued before anything
+// waits, so the kernel costs about one memory round trip; the two halves'
+// partial sums meet in LDS.  d = 128.
 __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrepArgs a, int qb) {
-  extern __shared__ float sq[];  // [qb][d] input, then [qb][d] rotated
-  const int d = cv.d;
-  float* sr = sq + qb * d;
+  constexpr int D = 128, KH = 64;
+  extern __shared__ float sq[];  // [qb][D] input | [qb][D] rotated | [2][qb][D] partials
+  float* sr = sq + qb * D;
+  float* sp = sr + qb * D;
   const int64_t q0 = int64_t(blockIdx.x) * qb;
   const int nqb = int(min<int64_t>(qb, a.nq - q0));
-  for (int e = threadIdx.x; e < nqb * d; e += blockDim.x) {
-    const int64_t qi = q0 + e / d;
-    const int i = e % d;
-    float v;
-    if (a.q_bf16)
-      v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * d + i]) << 16);
-    else
-      v = static_cast<const float*>(a.q)[qi * d + i];
-    sq[e] = v;
-  }
-  __syncthreads();
   int head = a.fixed_head;
   if (a.q_per_head > 0) head = int((q0 / a.q_per_head) % a.hkv);
   if (cv.heads == 1) head = 0;
-  const float* rot = cv.rot + size_t(head) * d * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    const float* row = rot + size_t(i) * d;
-    float acc[8];
+  const int i = threadIdx.x & (D - 1), kh = threadIdx.x >> 7;
+  const bool full_sketch = cv.mode == TQ_PROD && cv.m == D;
+  const float* rt = cv.rot_t + size_t(head) * D * D + size_t(KH * kh) * D + i;
+  const float* st = cv.sketch_t + size_t(KH * kh) * D + i;
+  float r[KH], sk[KH];
 #pragma unroll
-    for (int qq = 0; qq < 8; ++qq) acc[qq] = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < d; k += 4) {
-      const float4 r = *reinterpret_cast<const float4*>(row + k);
+  for (int u = 0; u < KH; ++u) r[u] = rt[size_t(u) * D];
+  if (full_sketch) {
 #pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        if (qq < nqb) {
-          const float* x = sq + qq * d + k;
-          acc[qq] = fmaf(r.x, x[0], acc[qq]);
-          acc[qq] = fmaf(r.y, x[1], acc[qq]);
-          acc[qq] = fmaf(r.z, x[2], acc[qq]);
-          acc[qq] = fmaf(r.w, x[3], acc[qq]);
-        }
-      }
-    }
-#pragma unroll
-    for (int qq = 0; qq < 8; ++qq)
-      if (qq < nqb) {
-        sr[qq * d + i] = acc[qq];
-        a.qr[(q0 + qq) * d + i] = acc[qq];
-      }
+    for (int u = 0; u < KH; ++u) sk[u] = st[size_t(u) * D];
   }
-  if (cv.mode != TQ_PROD) return;
+  for (int e = threadIdx.x; e < nqb * D; e += blockDim.x) {
+    const int64_t qi = q0 + e / D;
+    const int c = e % D;
+    float v;
+    if (a.q_bf16)
+      v = __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * D + c]) << 16);
+    else
+      v = static_cast<const float*>(a.q)[qi * D + c];
+    sq[e] = v;
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < nqb * cv.m; e += blockDim.x) {
-    const int qq = e / cv.m, jrow = e % cv.m;
-    const float* srow = cv.sketch + size_t(jrow) * cv.m;
-    float acc = 0.f;
-    for (int k = 0; k < cv.m; ++k) acc = fmaf(srow[k], sr[qq * d + k], acc);
-    a.qs[(q0 + qq) * cv.m + jrow] = acc;
+  auto matvec = [&](const float (&m)[KH], const float* src, float* dst, float* gdst, int gld) {
+    for (int qq = 0; qq < nqb; ++qq) {
+      const float* x = src + qq * D + KH * kh;
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < KH; u += 2) {
+        acc0 = fmaf(m[u], x[u], acc0);
+        acc1 = fmaf(m[u + 1], x[u + 1], acc1);
+      }
+      sp[(kh * qb + qq) * D + i] = acc0 + acc1;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nqb * D; e += blockDim.x) {
+      const int qq = e / D, c = e % D;
+      const float v = sp[qq * D + c] + sp[(qb + qq) * D + c];
+      if (dst) dst[qq * D + c] = v;
+      gdst[(q0 + qq) * gld + c] = v;
+    }
+    __syncthreads();
+  };
+  matvec(r, sq, sr, a.qr, D);
+  if (cv.mode != TQ_PROD) return;
+  if (full_sketch) {
+    matvec(sk, sr, nullptr, a.qs, D);
+  } else {
+    for (int e = threadIdx.x; e < nqb * cv.m; e += blockDim.x) {
+      const int qq = e / cv.m, j = e % cv.m;
+      float acc = 0.f;
+      for (int k = 0; k < cv.m; ++k) acc = fmaf(cv.sketch[size_t(j) * cv.m + k], sr[qq * D + k], acc);
+      a.qs[(q0 + qq) * cv.m + j] = acc;
+    }
   }
 }
 
@@ -342,30 +353,34 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
 // The split weights exp(m_s - M) are formed once in LDS; the accumulator
 // reads are independent loads, unrolled.
 template <int G>
-__global__ __launch_bounds__(128) void decode_combine_kernel(CodecView vc, DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_combine_kernel(CodecView vc, DecodeArgs a) {
+  // One block per (sequence, query head): merge the split-K partials
+  // (log-sum-exp), then rotate back, out = Pi_v^T acc / l.  The 256 threads
+  // split the partials and the rotation's k range in two halves so that many
+  // loads are in flight (the grid is small for a single long sequence).
   constexpr int D = 128;
-  __shared__ float sy[D];
+  __shared__ float sy[2][D];
   __shared__ float sf[1024];
-  __shared__ float sred[2];
+  __shared__ float sred[4];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int g = hq / G, gg = hq % G;
   const int stride = G * (2 + D);
   const float* part = a.part + (int64_t(b) * a.Hkv + g) * a.nsplit * stride;
-  const int i = threadIdx.x;
+  const int t = threadIdx.x, i = t & (D - 1), half = t >> 7;
   const int ns = min(a.nsplit, 1024);
   float M = -INFINITY;
-  for (int s2 = i; s2 < ns; s2 += D) {
+  for (int s2 = t; s2 < ns; s2 += 256) {
     const float m = part[s2 * stride + gg];
     sf[s2] = m;
     M = fmaxf(M, m);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((i & 63) == 0) sred[i >> 6] = M;
+  if ((t & 63) == 0) sred[t >> 6] = M;
   __syncthreads();
-  M = fmaxf(sred[0], sred[1]);
+  M = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
   float lpart = 0.f;
-  for (int s2 = i; s2 < ns; s2 += D) {
+  for (int s2 = t; s2 < ns; s2 += 256) {
     const float f = sf[s2] == -INFINITY ? 0.f : __expf(sf[s2] - M);
     sf[s2] = f;
     lpart += f * part[s2 * stride + G + gg];
@@ -373,31 +388,44 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(CodecView vc, Decod
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o, 64);
   __syncthreads();
-  if ((i & 63) == 0) sred[i >> 6] = lpart;
+  if ((t & 63) == 0) sred[t >> 6] = lpart;
   __syncthreads();
-  const float l = sred[0] + sred[1];
+  const float l = sred[0] + sred[1] + sred[2] + sred[3];
+  // weighted sum of the partial accumulators: half h takes splits h, h + 2, ...
   float accv = 0.f;
   const float* pa = part + 2 * G + gg * D + i;
-  int s2 = 0;
-  for (; s2 + 8 <= ns; s2 += 8) {
-    float v[8];
+  int s2 = half;
+  for (; s2 + 30 < ns; s2 += 32) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = pa[(s2 + u) * stride];
+    for (int u = 0; u < 16; ++u) v[u] = pa[(s2 + 2 * u) * stride];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) accv = fmaf(sf[s2 + u], v[u], accv);
+    for (int u = 0; u < 16; ++u) accv = fmaf(sf[s2 + 2 * u], v[u], accv);
   }
-  for (; s2 < ns; ++s2) accv = fmaf(sf[s2], pa[s2 * stride], accv);
-  sy[i] = l > 0.f ? accv / l : 0.f;
+  for (; s2 < ns; s2 += 2) accv = fmaf(sf[s2], pa[s2 * stride], accv);
+  sy[half][i] = accv;
   __syncthreads();
+  if (half == 0) sy[0][i] = l > 0.f ? (sy[0][i] + sy[1][i]) / l : 0.f;
+  __syncthreads();
+  // out_i = sum_k Pi[k][i] y_k, k range split between the halves
   const int hv = vc.heads > 1 ? g : 0;
-  const float* rot = vc.rot + size_t(hv) * D * D;
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-  for (int k = 0; k < D; k += 2) {
-    o0 = fmaf(rot[k * D + i], sy[k], o0);
-    o1 = fmaf(rot[(k + 1) * D + i], sy[k + 1], o1);
+  const float* rot = vc.rot + size_t(hv) * D * D + size_t(64 * half) * D + i;
+  const float* yk = sy[0] + 64 * half;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k0 = 0; k0 < 64; k0 += 32) {
+    float r[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) r[u] = rot[size_t(k0 + u) * D];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) o[u & 3] = fmaf(r[u], yk[k0 + u], o[u & 3]);
   }
-  a.out[(int64_t(b) * a.Hq + hq) * D + i] = o0 + o1;
+  __syncthreads();
+  sy[1][i] = 0.f;
+  __syncthreads();
+  if (half == 1) sy[1][i] = (o[0] + o[1]) + (o[2] + o[3]);
+  __syncthreads();
+  if (half == 0) a.out[(int64_t(b) * a.Hq + hq) * D + i] = (o[0] + o[1]) + (o[2] + o[3]) + sy[1][i];
 }
 
 // ------------------------------------------------------------------ top-k
@@ -510,11 +538,13 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* ps, const i
 
 hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStream_t s) {
   // enough blocks to spread over the chip, up to 8 queries per Pi read
-  int qb = int(std::max<int64_t>(1, std::min<int64_t>(8, a.nq / 512)));
-  if (a.q_per_head > 0) qb = std::min(qb, a.q_per_head);  // one rotation head per block
-  while (qb > 1 && size_t(2) * qb * cv.d * 4 > 64 * 1024) --qb;
+  int qb = 1;  // a power of two, so that a block never straddles two heads' query groups
+  while (qb < 8 && int64_t(qb) * 2 * 512 <= a.nq) qb *= 2;
+  if (a.q_per_head > 0) qb = std::min(qb, a.q_per_head & -a.q_per_head);
+  if (cv.d != 128) return hipErrorNotSupported;
+  const size_t lds = size_t(4) * qb * cv.d * 4;
   const unsigned blocks = unsigned((a.nq + qb - 1) / qb);
-  hipLaunchKernelGGL(query_prep_kernel, dim3(blocks), dim3(256), size_t(2) * qb * cv.d * 4, s, cv, a, qb);
+  hipLaunchKernelGGL(query_prep_kernel, dim3(blocks), dim3(256), lds, s, cv, a, qb);
   return hipGetLastError();
 }
 
@@ -553,10 +583,10 @@ hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeA
   if (e != hipSuccess) return e;
   dim3 g2(unsigned(a.Hq), unsigned(a.B));
   switch (G) {
-    case 1: hipLaunchKernelGGL(decode_combine_kernel<1>, g2, dim3(128), 0, s, vv, a); break;
-    case 2: hipLaunchKernelGGL(decode_combine_kernel<2>, g2, dim3(128), 0, s, vv, a); break;
-    case 4: hipLaunchKernelGGL(decode_combine_kernel<4>, g2, dim3(128), 0, s, vv, a); break;
-    case 8: hipLaunchKernelGGL(decode_combine_kernel<8>, g2, dim3(128), 0, s, vv, a); break;
+    case 1: hipLaunchKernelGGL(decode_combine_kernel<1>, g2, dim3(256), 0, s, vv, a); break;
+    case 2: hipLaunchKernelGGL(decode_combine_kernel<2>, g2, dim3(256), 0, s, vv, a); break;
+    case 4: hipLaunchKernelGGL(decode_combine_kernel<4>, g2, dim3(256), 0, s, vv, a); break;
+    case 8: hipLaunchKernelGGL(decode_combine_kernel<8>, g2, dim3(256), 0, s, vv, a); break;
   }
   return hipGetLastError();
 }
