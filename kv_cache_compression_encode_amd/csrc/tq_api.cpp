@@ -130,7 +130,9 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
     std::vector<double> s(size_t(cb->m) * cb->m);
     philox_normals(ds.seed_sketch, 2, int64_t(cb->m) * cb->m, s.data());
     cb->sketch32.resize(s.size());
-    for (size_t e = 0; e < s.size(); ++e) cb->sketch32[e] = float(s[e]);
+    // S is stored in fp16 (the draws rounded to fp32, then to fp16): its
+    // products on fp16 MFMA are then exact and need no low part
+    for (size_t e = 0; e < s.size(); ++e) cb->sketch32[e] = f16_to_f32(f32_to_f16_rne(float(s[e])));
   }
 
   // ----------------------------------------------------------- codebooks

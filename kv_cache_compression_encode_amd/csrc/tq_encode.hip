@@ -16,8 +16,9 @@
 //   4. prod: residual r = y - c[idx] kept in the MFMA accumulator layout, which
 //      is exactly the B-operand layout of the next product, so the QJL sketch
 //      Z^T = S R^T runs on MFMA without any transpose (S columns are permuted
-//      once when staged); S and 32 r are split into fp16 hi + lo parts (three
-//      32x32x16 f16 MFMAs, ~2^-22 relative); sign bits = [z >= 0];
+//      once when staged); S is stored in fp16 and 32 r is split into fp16
+//      hi + lo parts (two 32x32x16 f16 MFMAs, ~2^-22 relative); sign bits =
+//      [z >= 0];
 //   5. fp16 norms n_x and n_r = ||r||.
 // The 32x32 accumulator of v_mfma_f32_32x32x16 holds, in lane l and register
 // r, row 8*(r/4) + 4*(l/32) + r%4 and column l%32.
@@ -180,10 +181,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* sPiHi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* sPiLo = sPiHi + D * LDS_ROW;
-  uint16_t* sSkHi = sPiLo + D * LDS_ROW;
-  uint16_t* sSkLo = sSkHi + D * LDS_ROW;
-  float* sThr = reinterpret_cast<float*>(MODE == 1 ? (uint8_t*)(sSkLo + D * LDS_ROW)
-                                                   : (uint8_t*)sSkHi);
+  uint16_t* sSk = sPiLo + D * LDS_ROW;  // S is stored in fp16 (exact, no low part)
+  float* sThr = reinterpret_cast<float*>(MODE == 1 ? (uint8_t*)(sSk + D * LDS_ROW)
+                                                   : (uint8_t*)sSk);
   float* sCen = sThr + D * kMaxLevels;
 
   const int64_t bh = blockIdx.y;
@@ -192,10 +192,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 
   stage_matrix(sPiHi, cv.rot_hi + size_t(hc) * D * D, false);
   stage_matrix(sPiLo, cv.rot_lo + size_t(hc) * D * D, false);
-  if (MODE == 1) {
-    stage_matrix(sSkHi, cv.sk_hi, true);
-    stage_matrix(sSkLo, cv.sk_lo, true);
-  }
+  if (MODE == 1) stage_matrix(sSk, cv.sk_hi, true);
   if (!UNIFORM) {
     for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
       sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
@@ -507,12 +504,10 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
             for (int ms = 0; ms < 4; ++ms) {
               const int off = (32 * ms + j) * LDS_ROW + 16 * chunk + 8 * hh;
-              const u32x4 sh = *reinterpret_cast<const u32x4*>(sSkHi + off);
-              const u32x4 sl = *reinterpret_cast<const u32x4*>(sSkLo + off);
+              const u32x4 sh = *reinterpret_cast<const u32x4*>(sSk + off);
 #pragma unroll
               for (int nb = 0; nb < NB; ++nb) {
                 z[nb][ms] = mfma32h(sh, rh[nb], z[nb][ms]);
-                z[nb][ms] = mfma32h(sl, rh[nb], z[nb][ms]);
                 z[nb][ms] = mfma32h(sh, rl[nb], z[nb][ms]);
               }
             }
@@ -594,7 +589,7 @@ template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
 hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB>;
   size_t lds = size_t(2) * D * LDS_ROW * 2;
-  if (MODE == 1) lds += size_t(2) * D * LDS_ROW * 2;
+  if (MODE == 1) lds += size_t(D) * LDS_ROW * 2;
   if (!UNIFORM) lds += size_t(2) * D * kMaxLevels * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));

@@ -4,7 +4,8 @@
 // dense GEMMs over whole rows, so they run as rocBLAS fp16 GEMMs with fp32
 // accumulation.  fp32 accuracy comes from hi/lo fp16 splits laid side by side
 // along the reduction axis: [a_hi | a_hi | a_lo] . [b_hi | b_lo | b_hi]^T =
-// a_hi b_hi + a_hi b_lo + a_lo b_hi, one GEMM per product.  The per-element
+// a_hi b_hi + a_hi b_lo + a_lo b_hi, one GEMM per product (the sketch S is
+// stored in fp16, so there [r_hi | r_lo] . [S | S]^T suffices).  The per-element
 // steps in between are the kernels below:
 //   rowprep   : n_x, per-row power-of-two scale, split of x;
 //   quantize  : Lloyd-Max index per coordinate (TurboQuant paper review,
@@ -72,13 +73,20 @@ __global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16,
   }
 }
 
-// [rows][3 cols] = [hi | lo | hi] of a pair of fp16 matrices [rows][cols].
+// [rows][3 cols] = [hi | lo | hi] of a pair of fp16 matrices [rows][cols]
+// (lo == nullptr: [rows][2 cols] = [hi | hi]).
 __global__ void cat3_kernel(const uint16_t* hi, const uint16_t* lo, int64_t rows, int cols,
                             uint16_t* out) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= rows * cols) return;
   const int64_t r = e / cols;
   const int c = int(e % cols);
+  if (!lo) {
+    uint16_t* o = out + r * 2 * cols;
+    o[c] = hi[e];
+    o[cols + c] = hi[e];
+    return;
+  }
   uint16_t* o = out + r * 3 * cols;
   o[c] = hi[e];
   o[cols + c] = lo[e];
@@ -87,7 +95,7 @@ __global__ void cat3_kernel(const uint16_t* hi, const uint16_t* lo, int64_t rows
 
 // One wave per row, 64 coordinates per step (lane = coordinate): index by the
 // thresholds (scaled by w[row] instead of dividing y), bit planes by ballot,
-// residual r = y - c[idx] split into rcat [rows][3m] = [hi | hi | lo] of 32 r,
+// residual r = y - c[idx] split into rcat [rows][2m] = [hi | lo] of 32 r,
 // and ||r||^2 by a wave reduction.  Rows >= rows_valid (padding of the last
 // tile) get zero records.
 __global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float* y, const float* w,
@@ -125,10 +133,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(CodecView cv, const float
       rsum = fmaf(r, r, rsum);
       const float rs = 32.f * r;
       const uint16_t h = f16b(rs);
-      uint16_t* o = rcat + row * 3 * cv.m;
+      uint16_t* o = rcat + row * 2 * cv.m;
       o[dim] = h;
-      o[cv.m + dim] = h;
-      o[2 * cv.m + dim] = f16b(rs - f16v(h));
+      o[cv.m + dim] = f16b(rs - f16v(h));
     }
     for (int p = 0; p < ub; ++p) {
       const uint64_t mask = __ballot((idx >> p) & 1);
@@ -321,7 +328,7 @@ struct EncodeWs {
 size_t encode_ws_layout(const CodecView& cv, void* base, EncodeWs* out) {
   const size_t C = size_t(large_encode_chunk()), d = size_t(cv.d), m = size_t(std::max(cv.m, 1));
   auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  const size_t sizes[] = {r(C * 3 * d * 2), r(C * 3 * m * 2), r(d * 3 * d * 2), r(m * 3 * m * 2),
+  const size_t sizes[] = {r(C * 3 * d * 2), r(C * 2 * m * 2), r(d * 3 * d * 2), r(m * 2 * m * 2),
                           r(C * std::max(d, m) * 4), r(C * 4), r(C * 4), r(C * 4)};
   size_t off[8], tot = 0;
   for (int i = 0; i < 8; ++i) { off[i] = tot; tot += sizes[i]; }
@@ -356,8 +363,8 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
   const int esz = a.x_bf16 ? 2 : 4;
   hipError_t e;
   if (prod) {
-    hipLaunchKernelGGL(cat3_kernel, dim3(blocks_for(int64_t(m) * m)), dim3(256), 0, s, cv.sk_hi, cv.sk_lo,
-                       int64_t(m), m, W.bs);
+    hipLaunchKernelGGL(cat3_kernel, dim3(blocks_for(int64_t(m) * m)), dim3(256), 0, s, cv.sk_hi,
+                       static_cast<const uint16_t*>(nullptr), int64_t(m), m, W.bs);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   int cur_head = -1;
@@ -388,9 +395,9 @@ hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs
                            W.nx, r0, rows, valid, rec, W.rcat, W.rr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (prod) {
-          // z = [rh | rh | rl] [S_hi | S_lo | S_hi]^T  (z reuses the y buffer)
+          // z = [rh | rl] [S | S]^T  (z reuses the y buffer)
           if (valid > 0 &&
-              (e = gemm_abt(h, W.rcat, W.bs, W.y, valid, m, 3 * m, 3 * m, 3 * m, m, false)) != hipSuccess)
+              (e = gemm_abt(h, W.rcat, W.bs, W.y, valid, m, 2 * m, 2 * m, 2 * m, m, false)) != hipSuccess)
             return e;
           hipLaunchKernelGGL(signpack_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, cv, W.y, W.rr,
                              r0, rows, valid, rec);

@@ -30,7 +30,8 @@ What it computes, step by step, and where the pages define it:
   "Sparks" list (rotation and codebook lookup fused into attention).
 
 Readings where the pages are silent (each also listed in the design doc):
-the generator of Pi and S (Philox4x32-10 + Box-Muller, below); fp16 norms;
+the generator of Pi and S (Philox4x32-10 + Box-Muller, below); S stored in
+fp16 (the draws rounded to fp32, then fp16); fp16 norms;
 ties go to the upper cell; sign(0) = +1; the sketch acts on the rotated
 residual, so the query sketch is S (Pi q); the record layout of the library.
 
@@ -124,6 +125,16 @@ def haar_rotation(d: int, seed: int) -> np.ndarray:
 def gaussian_sketch(m: int, seed: int) -> np.ndarray:
     """Seeded m x m matrix with i.i.d. N(0, 1) entries (fp64), row-major from the sketch stream."""
     return philox_normals(seed, STREAM_SKETCH, m * m).reshape(m, m)
+
+
+def stored_sketch(m: int, seed: int) -> np.ndarray:
+    """The sketch S as the codec stores it: the Gaussian draws rounded to fp32
+    and then to fp16 (round to nearest even each time), held in fp64.  The
+    QJL estimator is exactly unbiased for Gaussian rows; the fp16 rounding
+    (relative 2^-11 per entry) perturbs that by far less than the estimator's
+    own spread, which the Monte-Carlo test over sketches checks."""
+    g = gaussian_sketch(m, seed)
+    return g.astype(np.float32).astype(np.float16).astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -289,7 +300,7 @@ def turboquant_codec(d: int, bits: int, mode: str, rot_seed: int, sketch_seed: i
     lm = beta_codebook(d, mse_bits)
     rot = _f32(haar_rotation(d, rot_seed))[None]
     m = d if mode == "prod" else 0
-    sk = _f32(gaussian_sketch(m, sketch_seed)) if mode == "prod" else None
+    sk = stored_sketch(m, sketch_seed) if mode == "prod" else None
     c, t = _f32(lm.centroids), _f32(lm.boundaries)
     return Codec(d, mode, np.full(d, mse_bits), m, layout, rot, sk,
                  [[c] * d], [[t] * d], True, {"lloyd_max": lm})
@@ -322,7 +333,7 @@ def spectralquant_codec(calib: np.ndarray, bitmap, m: int, sketch_seed: int,
         sig.append(sigma)
         cents.append([_f32(books[int(bits[i])].centroids * sigma[i]) for i in range(d)])
         bnds.append([_f32(books[int(bits[i])].boundaries * sigma[i]) for i in range(d)])
-    sk = _f32(gaussian_sketch(m, sketch_seed))
+    sk = stored_sketch(m, sketch_seed)
     return Codec(d, "prod", bits, m, layout, np.stack(rots), sk, cents, bnds, False,
                  {"sigma": np.stack(sig)})
 

@@ -40,7 +40,7 @@ def test_rotation_and_sketch_match_oracle(d):
     ref_rot = o.haar_rotation(d, 303).astype(np.float32)
     n, mx = _ulp_mismatch(rot, ref_rot)
     assert mx <= 1 and n <= 2
-    ref_sk = o.gaussian_sketch(d, 304).astype(np.float32)
+    ref_sk = o.stored_sketch(d, 304).astype(np.float32)
     n, mx = _ulp_mismatch(sk, ref_sk)
     assert mx <= 1 and n <= 2
 

@@ -203,7 +203,7 @@ def test_prod_estimator_unbiased_over_sketch():
 
     def mk(s):
         c = o.Codec(**{**codec0.__dict__})
-        c.sketch = o._f32(o.gaussian_sketch(d, 5000 + s))
+        c.sketch = o.stored_sketch(d, 5000 + s)
         return c
 
     v, codec, enc = _prod_mc(d, mk, x, q, range(3000))
@@ -367,7 +367,7 @@ def test_selective_qjl_unbiased_on_signal_dims():
     vals = []
     for s in range(4000):
         c = o.Codec(**{**base.__dict__})
-        c.sketch = o._f32(o.gaussian_sketch(m, 777 + s))
+        c.sketch = o.stored_sketch(m, 777 + s)
         enc = o.encode(c, x[None], round_norms=False)
         qr, qs = o.prepare_query(c, q[None])
         vals.append(float(enc.nr[0]) * o.QJL_CONST / m * (qs[0] @ np.where(enc.signs[0], 1, -1)))
