@@ -56,15 +56,18 @@ __device__ __forceinline__ float f16v(uint32_t h) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h)));
 }
 
-// Pack 8 floats into fp16 hi and lo fragments (x ~= hi + lo to ~2^-22).
+// Pack 8 floats into fp16 hi and lo fragments, x = hi + lo to ~2^-21
+// relative: hi by a packed round-toward-zero conversion, the exact remainder
+// x - hi (fp32) converted the same way.
 __device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = f16b(v[2 * i]), h1 = f16b(v[2 * i + 1]);
-    const uint32_t l0 = f16b(v[2 * i] - f16v(h0));
-    const uint32_t l1 = f16b(v[2 * i + 1] - f16v(h1));
-    hi[i] = h0 | (h1 << 16);
-    lo[i] = l0 | (l1 << 16);
+    const auto h = __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]);
+    const float r0 = __builtin_fmaf(float(h[0]), -1.f, v[2 * i]);
+    const float r1 = __builtin_fmaf(float(h[1]), -1.f, v[2 * i + 1]);
+    const auto l = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    hi[i] = __builtin_bit_cast(uint32_t, h);
+    lo[i] = __builtin_bit_cast(uint32_t, l);
   }
 }
 
@@ -96,10 +99,20 @@ __device__ __forceinline__ uint16_t f16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-// Stage a [128][128] 16-bit matrix into LDS rows of LDS_ROW elements; with
-// `perm` the column index has bits 2 and 3 swapped (sketch operand order).
+// Output-row order of the rotation and sketch products.  LDS row
+// 32b + 8a + 4h + c (a, c in 0..3, h in 0..1) holds matrix row 32b + 16h + 4a + c,
+// so that accumulator register r of the lanes in half h of a 32x32 block holds
+// coordinate 32b + 16h + r: each half-wave owns 16 consecutive coordinates and
+// packs their bits with constant shifts.
+__host__ __device__ constexpr int lds_row_of(int g) {
+  return (g & ~31) | (((g >> 2) & 3) << 3) | (((g >> 4) & 1) << 2) | (g & 3);
+}
+
+// Stage a [128][128] 16-bit matrix into LDS rows of LDS_ROW elements, rows
+// placed by lds_row_of; with `colperm` bits 3 and 4 of the column index are
+// swapped, matching the residual's register order in the sketch operand.
 // Each thread keeps its 16-byte loads in flight before storing them.
-__device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool perm) {
+__device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool colperm) {
   constexpr int CHUNKS = D * D / 8;  // 16-byte chunks
   const int tid = threadIdx.x, nt = blockDim.x;
   for (int base = 0; base < CHUNKS; base += 8 * nt) {
@@ -114,14 +127,8 @@ __device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool perm) {
       const int e = base + u * nt + tid;
       if (e >= CHUNKS) continue;
       const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-      if (!perm) {
-        *reinterpret_cast<u32x4*>(lds + row * LDS_ROW + col) = v[u];
-      } else {
-        const int d0 = (col & ~15) | (((col >> 2) & 1) << 3) | (((col >> 3) & 1) << 2);
-        const int d1 = ((col + 4) & ~15) | ((((col + 4) >> 2) & 1) << 3) | ((((col + 4) >> 3) & 1) << 2);
-        *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + d0) = u32x2{v[u][0], v[u][1]};
-        *reinterpret_cast<u32x2*>(lds + row * LDS_ROW + d1) = u32x2{v[u][2], v[u][3]};
-      }
+      const int c2 = colperm ? ((col & ~24) | (((col >> 3) & 1) << 4) | (((col >> 4) & 1) << 3)) : col;
+      *reinterpret_cast<u32x4*>(lds + lds_row_of(row) * LDS_ROW + c2) = v[u];
     }
   }
 }
@@ -160,6 +167,47 @@ __device__ __forceinline__ int quant_tree(float v, f32x16v T) {
     const float u1 = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
     const bool b0 = v >= (b3 ? u0 : u1);
     return (b3 ? 8 : 0) | (b2 ? 4 : 0) | (b1 ? 2 : 0) | (b0 ? 1 : 0);
+  }
+}
+
+// Same search, returning the index bits b[p] (bit p of the index) and the
+// selected level of `L` (2^UB values) without building the index as an
+// integer: the level is picked by selects on the bits, most significant first.
+template <int UB>
+__device__ __forceinline__ float quant_bits(float v, f32x16v T, const float* L, bool (&b)[4]) {
+  if constexpr (UB == 1) {
+    b[0] = v >= T[0];
+    return b[0] ? L[1] : L[0];
+  } else if constexpr (UB == 2) {
+    b[1] = v >= T[1];
+    b[0] = v >= (b[1] ? T[2] : T[0]);
+    const float hi = b[1] ? L[3] : L[1], lo = b[1] ? L[2] : L[0];
+    return b[0] ? hi : lo;
+  } else if constexpr (UB == 3) {
+    b[2] = v >= T[3];
+    b[1] = v >= (b[2] ? T[5] : T[1]);
+    b[0] = v >= (b[2] ? (b[1] ? T[6] : T[4]) : (b[1] ? T[2] : T[0]));
+    const float l3 = b[2] ? (b[1] ? L[7] : L[5]) : (b[1] ? L[3] : L[1]);
+    const float l2 = b[2] ? (b[1] ? L[6] : L[4]) : (b[1] ? L[2] : L[0]);
+    return b[0] ? l3 : l2;
+  } else {
+    static_assert(UB == 4, "1..4 index bits");
+    b[3] = v >= T[7];
+    b[2] = v >= (b[3] ? T[11] : T[3]);
+    b[1] = v >= (b[3] ? (b[2] ? T[13] : T[9]) : (b[2] ? T[5] : T[1]));
+    const float u0 = b[2] ? (b[1] ? T[14] : T[12]) : (b[1] ? T[10] : T[8]);
+    const float u1 = b[2] ? (b[1] ? T[6] : T[4]) : (b[1] ? T[2] : T[0]);
+    b[0] = v >= (b[3] ? u0 : u1);
+    float l[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) l[k] = L[k];
+#pragma unroll
+    for (int bt = 3; bt >= 0; --bt) {
+      const int half = 1 << bt;
+#pragma unroll
+      for (int k = 0; k < half; ++k) l[k] = b[bt] ? l[k + half] : l[k];
+    }
+    return l[0];
   }
 }
 
@@ -217,16 +265,18 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   const int64_t tstep = int64_t(gridDim.x) * nwaves;
   // bf16 input: the raw rows of the next sub-tile are loaded while the
   // current one is processed (register double buffer).
+  // Loads are unconditional (rows past the end read the last row instead and
+  // their results are discarded), so no load sits behind a branch and the
+  // wait counters stay exact across the prefetch.
   u32x4 pre[NB][8];
   auto load_raw = [&](int64_t tl, int sb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t t = tl * kTile + sb * 32 * NB + nb * 32 + j;
-      const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + t * a.xs_t + 64 * hh;
-      const bool ok = tl < ntiles && t < a.tokens;
+      const int64_t tc = (tl < ntiles && t < a.tokens) ? t : a.tokens - 1;
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + tc * a.xs_t + 64 * hh;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        pre[nb][c] = ok ? *reinterpret_cast<const u32x4*>(row + 8 * c) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < 8; ++c) pre[nb][c] = *reinterpret_cast<const u32x4*>(row + 8 * c);
     }
   };
   if (BF16IN) load_raw(int64_t(blockIdx.x) * nwaves + wave, 0);
@@ -281,19 +331,15 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
           wsc[nb] = 16.f * p2;
         } else {
-          const float* row = reinterpret_cast<const float*>(xbase) + t * a.xs_t + 64 * hh;
+          const int64_t tc = valid[nb] ? t : a.tokens - 1;  // unconditional load, see load_raw
+          const float* row = reinterpret_cast<const float*>(xbase) + tc * a.xs_t + 64 * hh;
           float v[8][8];
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            if (valid[nb]) {
-              const float4 p0 = *reinterpret_cast<const float4*>(row + 8 * c);
-              const float4 p1 = *reinterpret_cast<const float4*>(row + 8 * c + 4);
-              v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
-              v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
-            } else {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) v[c][i] = 0.f;
-            }
+            const float4 p0 = *reinterpret_cast<const float4*>(row + 8 * c);
+            const float4 p1 = *reinterpret_cast<const float4*>(row + 8 * c + 4);
+            v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
+            v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
           }
 #pragma unroll
           for (int c = 0; c < 8; ++c)
@@ -322,22 +368,25 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         wsc[nb] *= sx[nb];
       }
 
-      // scaled boundaries / centroids (uniform codec)
+      // boundaries scaled to the accumulator (uniform codec); prod: the
+      // residual is formed directly in unit scale times 32, rsd = v rs - 32 c
       f32x16v T[NB];
-      float C[NB][LV];
+      float rs[NB];
+      float C32[LV];
       if (UNIFORM) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * wsc[nb];
-#pragma unroll
-          for (int k = 0; k < LV; ++k) C[nb][k] = cv.ucen[k] * wsc[nb];
+          rs[nb] = 32.f / wsc[nb];
         }
+#pragma unroll
+        for (int k = 0; k < LV; ++k) C32[k] = 32.f * cv.ucen[k];
       }
 
-      uint32_t cw[NB][NPL];      // code words of the current 32-dim block, plane p
+      uint32_t cw[NB][NPL];      // code bits of the current 32-dim block (this half's 16), plane p
       uint32_t tailw[NB];        // non-uniform row layout: bits beyond plane 0
-      uint32_t sw[NB][4];        // sign words (row layout)
+      uint32_t sw[NB][4];        // sign bits (row layout), this half's 16 per word
       float rr[NB];
       f32x16 z[NB][4];
 #pragma unroll
@@ -360,11 +409,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
           for (int p = 0; p < NPL; ++p) cw[nb][p] = 0;
         // ------------------------------------------------ rotation block
-        // with one 32-vector block the Pi hi and Pi lo products go to two
-        // independent accumulator chains
-        f32x16 acc[NB], acc2[NB];
+        // one accumulation chain per 32-vector block: Pi_hi x_hi, Pi_lo x_hi
+        // (and Pi_hi x_lo for fp32 input); register r of half hh holds
+        // coordinate 32 mb + 16 hh + r
+        f32x16 acc[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = acc2[nb] = f32x16{};
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
@@ -373,14 +423,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
-            if (NB == 1) acc2[nb] = mfma32h(al, xh[nb][c], acc2[nb]);
-            else acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
-            if (!BF16IN) acc2[nb] = mfma32h(ah, xl[nb][c], acc2[nb]);
+            acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
+            if (!BF16IN) acc[nb] = mfma32h(ah, xl[nb][c], acc[nb]);
           }
-        }
-        if (NB == 1 || !BF16IN) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[nb] += acc2[nb];
         }
         // ------------------------------------------------ quantize block
         uint32_t colkeep[NB][2];
@@ -388,18 +433,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int bit = 8 * (r >> 2) + 4 * hh + (r & 3);  // dim within block
-            const int dim = 32 * mb + bit;
+            const int dim = 32 * mb + 16 * hh + r;
             const float v = acc[nb][r];
             int idx = 0;
             float chat = 0.f;
-            if (UNIFORM) {
+            if (UNIFORM && !COL) {
+              // row layout: the index bits go straight into the plane words
+              bool bits[4] = {false, false, false, false};
+              chat = quant_bits<UB>(v, T[nb], C32, bits);
+#pragma unroll
+              for (int p = 0; p < NPL; ++p) cw[nb][p] |= uint32_t(bits[p]) << r;
+            } else if (UNIFORM) {
               idx = quant_tree<UB>(v, T[nb]);
               if (MODE != 0) {
-                // select tree over the centroids driven by the index bits
+                // select tree over the (32x) centroids driven by the index bits
                 float lvl[LV];
 #pragma unroll
-                for (int k = 0; k < LV; ++k) lvl[k] = C[nb][k];
+                for (int k = 0; k < LV; ++k) lvl[k] = C32[k];
 #pragma unroll
                 for (int bt = 0; bt < UB; ++bt) {
                   const bool on = (idx >> bt) & 1;
@@ -419,11 +469,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
             if (!valid[nb]) idx = 0;
             if (!COL) {
-              if (UNIFORM) {
-#pragma unroll
-                for (int p = 0; p < NPL; ++p) cw[nb][p] |= uint32_t((idx >> p) & 1) << bit;
-              } else {
-                cw[nb][0] |= uint32_t(idx & 1) << bit;
+              if (!UNIFORM) {
+                cw[nb][0] |= uint32_t(idx & 1) << r;
                 for (int p = 1; p < kMaxBits; ++p) {
                   const int pos = cv.bitpos[p * D + dim];
                   if (pos >= 0) tailw[nb] |= uint32_t((idx >> p) & 1) << (pos - D);
@@ -431,11 +478,10 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               }
             } else if (UB == 1) {
               // col layout, 1 bit: ballot over lanes = vectors; lanes 0..31
-              // carry dim (32mb + 8(r/4) + r%4), lanes 32..63 the dim 4 higher.
+              // carry dim 32mb + r, lanes 32..63 dim 32mb + 16 + r
               const uint64_t m = __ballot((idx & 1) != 0);
-              const int k0 = 8 * (r >> 2) + (r & 3);
-              cw[nb][0] = (lane == k0 ? uint32_t(m) : cw[nb][0]);
-              cw[nb][0] = (lane == k0 + 4 ? uint32_t(m >> 32) : cw[nb][0]);
+              cw[nb][0] = (lane == r ? uint32_t(m) : cw[nb][0]);
+              cw[nb][0] = (lane == 16 + r ? uint32_t(m >> 32) : cw[nb][0]);
             } else {
               // col layout, UB bits: the 32/UB vectors of a dword are OR-ed
               // together across their lanes (DPP butterfly); lane j of the
@@ -445,11 +491,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               const uint32_t w = group_or<VPD>(uint32_t(idx) << (UB * (j & (VPD - 1))));
               if ((r % VPD) == (j & (VPD - 1))) colkeep[nb][r / VPD] = w;
             }
-            const float res = v - chat;
             if (MODE == 1) {
-              rr[nb] = fmaf(res, res, rr[nb]);
-              acc[nb][r] = res;
+              const float rsd = fmaf(v, rs[nb], -chat);  // 32 (y - c) in unit scale
+              rr[nb] = fmaf(rsd, rsd, rr[nb]);
+              acc[nb][r] = rsd;
             } else if (MODE == 2) {
+              const float res = v - chat;
               if (mb == 0 && hh == 0 && r < 4) {
                 rsmall[nb][r] = dim < cv.m ? res : 0.f;
                 if (dim < cv.m) rr[nb] = fmaf(res, res, rr[nb]);
@@ -457,22 +504,24 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
           }
           if (!COL) {
-            // row layout: the two half-waves hold complementary bits of each word
+            // row layout: half hh holds bits 16 hh .. 16 hh + 15 of each word;
+            // slots past the end of the input are zero
             const int slot = sub * 32 * NB + nb * 32 + j;
 #pragma unroll
             for (int p = 0; p < NPL; ++p) {
-              const uint32_t w = cw[nb][p] | xor32(cw[nb][p]);
+              const uint32_t mine = valid[nb] ? cw[nb][p] << (16 * hh) : 0u;
+              const uint32_t w = mine | xor32(mine);
               if (hh == 0) *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
             }
           }
           if (COL && UB > 1) {
             // lane j holds, for r = k*VPD + (j % VPD), the dword of dim
-            // 32mb + 8(r/4) + 4hh + r%4 covering vectors (j / VPD)*VPD ..
+            // 32mb + 16hh + r covering vectors (j / VPD)*VPD ..
             constexpr int VPD = 32 / UB;
 #pragma unroll
             for (int k = 0; k < 16 / VPD; ++k) {
               const int r = k * VPD + (j & (VPD - 1));
-              const int dim = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+              const int dim = 32 * mb + 16 * hh + r;
               const int word = (sub * NB * 32 + nb * 32 + j) / VPD;
               *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = colkeep[nb][k];
             }
@@ -493,11 +542,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             u32x4 rh[NB], rl[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              // residual in unit-vector scale times 32 keeps both fp16 parts normal
-              const float rs = 32.f / wsc[nb];
               float v[8];
 #pragma unroll
-              for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i] * rs;
+              for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i];
               split8h(v, rh[nb], rl[nb]);
             }
             const int chunk = 2 * mb + q;
@@ -521,20 +568,13 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         const int slot = sub * 32 * NB + nb * 32 + j;
         if (MODE == 1) {
           rr[nb] += xor32f(rr[nb]);
+          // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
 #pragma unroll
           for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int bit = 8 * (r >> 2) + 4 * hh + (r & 3);
-              const bool s = z[nb][ms][r] >= 0.f && valid[nb];
-              if (!COL) {
-                sw[nb][ms] |= uint32_t(s) << bit;
-              } else {
-                const uint64_t m = __ballot(s);
-                const int k0 = 8 * (r >> 2) + (r & 3);
-                sw[nb][0] = (lane == k0 ? uint32_t(m) : sw[nb][0]);
-                sw[nb][0] = (lane == k0 + 4 ? uint32_t(m >> 32) : sw[nb][0]);
-              }
+              const bool sgn = z[nb][ms][r] >= 0.f && valid[nb];
+              if (!COL) sw[nb][ms] |= uint32_t(sgn) << r;
             }
         } else if (MODE == 2) {
           if (hh == 0) {
@@ -554,8 +594,13 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         // combine the two half-waves' bits (row layout)
         if (!COL) {
           if (!UNIFORM) tailw[nb] |= xor32(tailw[nb]);
+          if (MODE == 1) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) sw[nb][q] |= xor32(sw[nb][q]);
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t mine = sw[nb][q] << (16 * hh);
+              sw[nb][q] = mine | xor32(mine);
+            }
+          }
           if (!UNIFORM) {
             const int tb = cv.code_bytes - 16;  // tail bytes per vector (1..4)
             if (hh == 0)
@@ -576,7 +621,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           const float nx = valid[nb] ? nxv[nb] : 0.f;
           *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nx);
           if (MODE != 0) {
-            const float nr = valid[nb] ? sqrtf(rr[nb]) / wsc[nb] : 0.f;
+            // prod: rr sums (32 r)^2 in unit scale; SQ: r^2 in accumulator scale
+            const float nr = !valid[nb] ? 0.f : (MODE == 1 ? sqrtf(rr[nb]) * (1.f / 32.f) : sqrtf(rr[nb]) / wsc[nb]);
             *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = f16_bits(nr);
           }
         }
