@@ -182,7 +182,9 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
  *   scores[i][t] = n_x (sum_j q'_j c[idx_j] + n_r sqrt(pi/2)/m sum_j qs_j (2 bit_j - 1)),
  *   q' = Pi q, qs = S q'[0:m] ([TQ] "Method"; estimator of <q, x>).
  *   q        device fp32 [nq][d];  scores device fp32 [nq][n].
- *   workspace >= tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0) bytes (device). */
+ *   workspace >= tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0) bytes (device).
+ * Supported: d = 128 (any ROW codec; nq <= 262140) and d a multiple of 128 up
+ * to 4096 with a uniform codec (full sketch for prod); else TQ_EUNSUPPORTED. */
 tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t head,
                    const void* records, int64_t n, float* scores, void* workspace,
                    size_t workspace_bytes, void* stream);

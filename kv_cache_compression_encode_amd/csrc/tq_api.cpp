@@ -471,7 +471,7 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   if (cb->desc.d != 128 && (cb->desc.d % 128 || !cb->uniform || (cb->desc.mode == TQ_PROD && cb->m != cb->desc.d)))
     return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
-  if (nq > int64_t(65535) * 16) return TQ_EUNSUPPORTED;
+  if (nq > int64_t(65535) * 4) return TQ_EUNSUPPORTED;
   if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0)) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;

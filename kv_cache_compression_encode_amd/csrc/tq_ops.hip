@@ -19,6 +19,8 @@
 namespace tq {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
@@ -124,68 +126,104 @@ __device__ __forceinline__ int row_index_uniform(const uint8_t* tile, int slot, 
 }
 
 // ------------------------------------------------------------------ score
-// Block = 4 waves, each wave one record tile (lane = vector); a block of QB
-// queries (q' and qs) in LDS, read as broadcasts.
+// d = 128.  Block = 4 waves, each wave one record tile (lane = vector); QB
+// queries per block.  A lane loads its vector's record rows with 16-byte
+// loads (the bit planes, the sign row) and walks the coordinates on
+// registers; the queries sit in LDS as [coordinate][QB] so one 16-byte LDS
+// read serves the QB products of a coordinate.
 template <int QB>
 __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* qr, const float* qs,
                                                     int64_t nq, const uint8_t* rec, int64_t n,
                                                     float* scores) {
-  extern __shared__ float sm[];
-  const int d = cv.d, m = cv.m;
-  float* sqr = sm;                 // [QB][d]
-  float* sqs = sqr + QB * d;       // [QB][m]
-  float* scen = sqs + QB * m;      // [d][kMaxLevels] (non-uniform) or [kMaxLevels]
+  static_assert(QB == 4, "four queries per block");
+  constexpr int D = 128;
+  __shared__ float4 sqr[D];        // [coordinate] -> QB queries
+  __shared__ float4 sqs[D];        // [sketch row] -> QB queries
+  __shared__ float scen[D * kMaxLevels];
+  const int m = cv.m;
   const int64_t q0 = int64_t(blockIdx.y) * QB;
   const int nqb = int(min<int64_t>(QB, nq - q0));
-  for (int e = threadIdx.x; e < QB * d; e += blockDim.x)
-    sqr[e] = e / d < nqb ? qr[(q0 + e / d) * d + e % d] : 0.f;
-  for (int e = threadIdx.x; e < QB * m; e += blockDim.x)
-    sqs[e] = e / m < nqb ? qs[(q0 + e / m) * m + e % m] : 0.f;
-  const int ncen = cv.uniform ? kMaxLevels : d * kMaxLevels;
+  for (int e = threadIdx.x; e < D * QB; e += blockDim.x) {
+    const int i = e / QB, qq = e % QB;
+    reinterpret_cast<float*>(sqr)[e] = qq < nqb ? qr[(q0 + qq) * D + i] : 0.f;
+    reinterpret_cast<float*>(sqs)[e] = (qq < nqb && i < m) ? qs[(q0 + qq) * m + i] : 0.f;
+  }
+  const int ncen = cv.uniform ? kMaxLevels : D * kMaxLevels;
   for (int e = threadIdx.x; e < ncen; e += blockDim.x) scen[e] = cv.uniform ? cv.ucen[e] : cv.cen[e];
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tile = int64_t(blockIdx.x) * 4 + wave;
-  const int64_t v = tile * kTile + lane;
   if (tile * kTile >= n) return;
+  const int64_t v = tile * kTile + lane;
   const uint8_t* trec = rec + tile * cv.tile_bytes;
-  float acc[QB], sacc[QB];
+  // record rows of this lane's vector
+  const int np = cv.uniform ? cv.ubits : 1;
+  u32x4 pl[kMaxBits];
 #pragma unroll
-  for (int qq = 0; qq < QB; ++qq) acc[qq] = sacc[qq] = 0.f;
-  for (int dim = 0; dim < d; ++dim) {
-    int idx;
-    float c;
-    if (cv.uniform) {
-      idx = row_index_uniform(trec, lane, dim, d, cv.ubits);
-      c = scen[idx];
-    } else {
-      idx = (trec[size_t(lane) * 16 + (dim >> 3)] >> (dim & 7)) & 1;
-      for (int p = 1; p < kMaxBits; ++p) {
-        const int pos = cv.bitpos[p * d + dim];
-        if (pos >= 0) {
-          const int tb = cv.code_bytes - 16, t = pos - d;
-          idx |= ((trec[size_t(kTile) * 16 + size_t(lane) * tb + (t >> 3)] >> (t & 7)) & 1) << p;
+  for (int p = 0; p < kMaxBits; ++p)
+    pl[p] = p < np ? *reinterpret_cast<const u32x4*>(trec + size_t(p) * kTile * 16 + size_t(lane) * 16)
+                   : u32x4{0, 0, 0, 0};
+  uint32_t tail = 0;
+  if (!cv.uniform) {
+    const int tb = cv.code_bytes - 16;  // 1..4 tail bytes
+    for (int k = 0; k < tb; ++k) tail |= uint32_t(trec[size_t(kTile) * 16 + size_t(lane) * tb + k]) << (8 * k);
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const int dim = 32 * w + k;
+      int idx = 0;
+#pragma unroll
+      for (int p = 0; p < kMaxBits; ++p)
+        if (p < np) idx |= int((pl[p][w] >> k) & 1u) << p;
+      float c;
+      if (cv.uniform) {
+        c = scen[idx];
+      } else {
+        for (int p = 1; p < kMaxBits; ++p) {
+          const int pos = cv.bitpos[p * D + dim];
+          if (pos >= 0) idx |= int((tail >> (pos - D)) & 1u) << p;
+        }
+        c = scen[dim * kMaxLevels + idx];
+      }
+      const float4 q = sqr[dim];
+      acc.x = fmaf(q.x, c, acc.x);
+      acc.y = fmaf(q.y, c, acc.y);
+      acc.z = fmaf(q.z, c, acc.z);
+      acc.w = fmaf(q.w, c, acc.w);
+    }
+  }
+  float4 sacc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (cv.mode == TQ_PROD) {
+    if (m == D) {
+      const u32x4 sg = *reinterpret_cast<const u32x4*>(trec + cv.off_signs + size_t(lane) * 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+#pragma unroll 8
+        for (int k = 0; k < 32; ++k) {
+          const float sgn = (sg[w] >> k) & 1u ? 1.f : -1.f;
+          const float4 q = sqs[32 * w + k];
+          sacc.x = fmaf(q.x, sgn, sacc.x);
+          sacc.y = fmaf(q.y, sgn, sacc.y);
+          sacc.z = fmaf(q.z, sgn, sacc.z);
+          sacc.w = fmaf(q.w, sgn, sacc.w);
         }
       }
-      c = scen[dim * kMaxLevels + idx];
-    }
-#pragma unroll
-    for (int qq = 0; qq < QB; ++qq) acc[qq] = fmaf(sqr[qq * d + dim], c, acc[qq]);
-  }
-  if (cv.mode == TQ_PROD) {
-    for (int jrow = 0; jrow < m; ++jrow) {
-      int bit;
-      if (m == d || m > 8) {
-        const int chunk = jrow >> 7, in = jrow & 127;
-        const int w = min(16, cv.sign_bytes - chunk * 16);
-        bit = (trec[cv.off_signs + size_t(chunk) * kTile * 16 + size_t(lane) * w + (in >> 3)] >> (in & 7)) & 1;
-      } else {
-        bit = (trec[cv.off_signs + size_t(lane) * cv.sign_bytes + (jrow >> 3)] >> (jrow & 7)) & 1;
+    } else {
+      uint32_t sg = 0;
+      for (int k = 0; k < cv.sign_bytes; ++k)
+        sg |= uint32_t(trec[cv.off_signs + size_t(lane) * cv.sign_bytes + k]) << (8 * k);
+      for (int jrow = 0; jrow < m; ++jrow) {
+        const float sgn = (sg >> jrow) & 1u ? 1.f : -1.f;
+        const float4 q = sqs[jrow];
+        sacc.x = fmaf(q.x, sgn, sacc.x);
+        sacc.y = fmaf(q.y, sgn, sacc.y);
+        sacc.z = fmaf(q.z, sgn, sacc.z);
+        sacc.w = fmaf(q.w, sgn, sacc.w);
       }
-      const float sgn = bit ? 1.f : -1.f;
-#pragma unroll
-      for (int qq = 0; qq < QB; ++qq) sacc[qq] = fmaf(sqs[qq * m + jrow], sgn, sacc[qq]);
     }
   }
   if (v >= n) return;
@@ -194,9 +232,11 @@ __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* q
                        ? f16_to_f32(*reinterpret_cast<const uint16_t*>(trec + cv.off_nr + 2 * lane))
                        : 0.f;
   const float coef = cv.mode == TQ_PROD ? nr * kQjl / float(m) : 0.f;
+  const float out[4] = {acc.x + coef * sacc.x, acc.y + coef * sacc.y, acc.z + coef * sacc.z,
+                        acc.w + coef * sacc.w};
 #pragma unroll
   for (int qq = 0; qq < QB; ++qq)
-    if (qq < nqb) scores[(q0 + qq) * n + v] = nx * (acc[qq] + coef * sacc[qq]);
+    if (qq < nqb) scores[(q0 + qq) * n + v] = nx * out[qq];
 }
 
 // ------------------------------------------------------------ decode
@@ -550,16 +590,11 @@ hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStr
 
 hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
                         const uint8_t* rec, int64_t n, float* scores, hipStream_t s) {
-  constexpr int QB = 16;
+  constexpr int QB = 4;
+  if (cv.d != 128 || cv.layout != TQ_LAYOUT_ROW || (cv.uniform && cv.ubits > kMaxBits)) return hipErrorNotSupported;
   const int64_t ntiles = (n + kTile - 1) / kTile;
   dim3 grid(unsigned((ntiles + 3) / 4), unsigned((nq + QB - 1) / QB));
-  const size_t lds = (size_t(QB) * cv.d + size_t(QB) * std::max(cv.m, 1) +
-                      (cv.uniform ? kMaxLevels : size_t(cv.d) * kMaxLevels)) * 4;
-  auto kern = score_kernel<QB>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, cv, qr, qs, nq, rec, n, scores);
+  hipLaunchKernelGGL(score_kernel<QB>, grid, dim3(256), 0, s, cv, qr, qs, nq, rec, n, scores);
   return hipGetLastError();
 }
 
