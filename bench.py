@@ -37,10 +37,12 @@ K_REC, V_REC = 52, 66
 K_ENC_BYTES = 2 * D + K_REC          # 308 B per key
 V_ENC_BYTES = 2 * D + V_REC          # 322 B per value
 DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decode
-# fp32 copy-kernel calibration of FETCH_SIZE / WRITE_SIZE (KiB per dispatch)
-# lives in profiles/; traffic is left null until counters are taken for the
-# kernel as built.
-TRAFFIC = None  # per call name: HBM bytes per launch from FETCH_SIZE + WRITE_SIZE
+# HBM bytes per launch of a call's kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a
+# plain 1 GiB device copy (factors 2.0 and 1.0); the summary and the commands
+# are in profiles/.  Valid for the kernels as built when the counters were
+# taken; a call missing here reports null.
+TRAFFIC = {"encode_keys": 82040198}
 
 
 def parse():
@@ -180,39 +182,37 @@ def cpu_baseline_search(bits):
 
 
 # ------------------------------------------------------------ timing helpers
-class Timer:
-    """HIP events around library calls on torch's current stream (the stream
-    the library launches on)."""
+def time_calls(torch, calls, steps, warmup):
+    """Whole-step time, then each call's average launch time.
 
-    def __init__(self, torch, names, steps):
-        self.torch = torch
-        self.names = names
-        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-                   for _ in range(steps)]
-
-    def mark(self, step, i):
-        self.ev[step][i].record()
-
-    def ms(self):
-        self.torch.cuda.synchronize()
-        out = {}
-        for j, n in enumerate(self.names):
-            out[n] = sum(e[j].elapsed_time(e[j + 1]) for e in self.ev) / len(self.ev)
-        return out
-
-
-def whole_steps(torch, step, steps, warmup):
+    calls: list of (name, fn(i)) run in order as one step.  Per call, `steps`
+    launches (cycling over the workload's inputs) run back to back between one
+    pair of HIP events on torch's current stream, the stream the library
+    launches on, so the figure is the kernels' own time plus launch gaps."""
+    def step(i):
+        for _, fn in calls:
+            fn(i)
     for i in range(warmup):
-        step(i, None, 0)
+        step(i)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for i in range(steps):
-        step(i, None, 0)
+        step(i)
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    ms_step = t0.elapsed_time(t1) / steps
+    per = {}
+    for name, fn in calls:
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            fn(i)
+        t1.record()
+        torch.cuda.synchronize()
+        per[name] = t0.elapsed_time(t1) / steps
+    return ms_step, per
 
 
 def result(args, metric, value, unit, ms_step, workload, dtype, roof, breakdown, extra=None):
@@ -251,21 +251,11 @@ def run_gqa_layer(args, torch, tq, synth):
     ws = tq.DecodeWorkspace(kcb, HQ, T, HKV, dev)
     scale = 1 / math.sqrt(D)
 
-    def step(i, tm, si):
-        l = i % NLAYERS
-        tm and tm.mark(si, 0)
-        tq.encode(kcb, K[l], records=krec[l])
-        tm and tm.mark(si, 1)
-        tq.encode(vcb, V[l], records=vrec[l])
-        tm and tm.mark(si, 2)
-        tq.decode_attend(kcb, vcb, q, krec[l], vrec[l], T, HKV, scale, out=out, workspace=ws)
-        tm and tm.mark(si, 3)
-
-    ms_step = whole_steps(torch, step, args.steps, args.warmup)
-    tm = Timer(torch, ["encode_keys", "encode_values", "decode_attend"], args.steps)
-    for i in range(args.steps):
-        step(i, tm, i)
-    t = tm.ms()
+    calls = [("encode_keys", lambda i: tq.encode(kcb, K[i % NLAYERS], records=krec[i % NLAYERS])),
+             ("encode_values", lambda i: tq.encode(vcb, V[i % NLAYERS], records=vrec[i % NLAYERS])),
+             ("decode_attend", lambda i: tq.decode_attend(kcb, vcb, q, krec[i % NLAYERS], vrec[i % NLAYERS], T,
+                                                          HKV, scale, out=out, workspace=ws))]
+    ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
     nk = HKV * T
     nbytes = {"encode_keys": nk * K_ENC_BYTES, "encode_values": nk * V_ENC_BYTES,
               "decode_attend": nk * DEC_BYTES}
@@ -293,18 +283,9 @@ def run_small(args, torch, tq, synth):
     cb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=103, seed_sketch=104)
     rec = torch.empty(cb.records_bytes(n), dtype=torch.uint8, device=dev)
 
-    def step(i, tm, si):
-        tm and tm.mark(si, 0)
-        tq.encode(cb, x, records=rec)
-        tm and tm.mark(si, 1)
-        tq.score(cb, q, rec, n)
-        tm and tm.mark(si, 2)
-
-    ms_step = whole_steps(torch, step, args.steps, args.warmup)
-    tm = Timer(torch, ["encode", "score"], args.steps)
-    for i in range(args.steps):
-        step(i, tm, i)
-    t = tm.ms()
+    calls = [("encode", lambda i: tq.encode(cb, x, records=rec)),
+             ("score", lambda i: tq.score(cb, q, rec, n))]
+    ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
     nbytes = {"encode": n * (4 * D + 52), "score": n * 52 + nq * n * 4}
     bd = {k: {"ms": t[k], "GBps": nbytes[k] / (t[k] * 1e-3) / 1e9} for k in t}
     res = result(args, "TurboQuant-prod encode + score vectors/s (d=128, 4096 vectors, 16 queries)",
@@ -329,18 +310,9 @@ def run_bulk(args, torch, tq, synth):
     krec = torch.empty(L * H * kcb.records_bytes(TT), dtype=torch.uint8, device=dev)
     vrec = torch.empty(L * H * vcb.records_bytes(TT), dtype=torch.uint8, device=dev)
 
-    def step(i, tm, si):
-        tm and tm.mark(si, 0)
-        tq.encode(kcb, K, records=krec)
-        tm and tm.mark(si, 1)
-        tq.encode(vcb, V, records=vrec)
-        tm and tm.mark(si, 2)
-
-    ms_step = whole_steps(torch, step, args.steps, args.warmup)
-    tm = Timer(torch, ["encode_keys", "encode_values"], args.steps)
-    for i in range(args.steps):
-        step(i, tm, i)
-    t = tm.ms()
+    calls = [("encode_keys", lambda i: tq.encode(kcb, K, records=krec)),
+             ("encode_values", lambda i: tq.encode(vcb, V, records=vrec))]
+    ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
     nk = L * H * TT
     nbytes = {"encode_keys": nk * K_ENC_BYTES, "encode_values": nk * V_ENC_BYTES}
     dom = max(t, key=lambda k: t[k])
@@ -381,17 +353,9 @@ def run_sq(args, torch, tq, synth):
     ws = tq.DecodeWorkspace(kcb, B * QH, TT, H, dev)
     scale = 1 / math.sqrt(D)
 
-    def step(i, tm, si):
-        c = i % ncache
-        tm and tm.mark(si, 0)
-        tq.decode_attend(kcb, vcb, qs[c], krec[c], vrec[c], TT, H, scale, out=out, workspace=ws)
-        tm and tm.mark(si, 1)
-
-    ms_step = whole_steps(torch, step, args.steps, args.warmup)
-    tm = Timer(torch, ["decode_attend"], args.steps)
-    for i in range(args.steps):
-        step(i, tm, i)
-    t = tm.ms()
+    calls = [("decode_attend", lambda i: tq.decode_attend(kcb, vcb, qs[i % ncache], krec[i % ncache],
+                                                          vrec[i % ncache], TT, H, scale, out=out, workspace=ws))]
+    ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
     nk = B * H * TT
     nbytes = nk * (kper + vper) // TT
     res = result(args, "SpectralQuant batched decode token-heads/s, % of HBM roofline",
@@ -416,18 +380,9 @@ def run_search(args, torch, tq, synth):
     cb = tq.Codebook(d, tq.TQ_PROD, args.bits, seed_rotation=503, seed_sketch=504)
     rec = torch.empty(cb.records_bytes(n), dtype=torch.uint8, device=dev)
 
-    def step(i, tm, si):
-        tm and tm.mark(si, 0)
-        tq.encode(cb, x, records=rec)
-        tm and tm.mark(si, 1)
-        tq.search_topk(cb, q, rec, n, k)
-        tm and tm.mark(si, 2)
-
-    ms_step = whole_steps(torch, step, args.steps, args.warmup)
-    tm = Timer(torch, ["encode", "search_topk"], args.steps)
-    for i in range(args.steps):
-        step(i, tm, i)
-    t = tm.ms()
+    calls = [("encode", lambda i: tq.encode(cb, x, records=rec)),
+             ("search_topk", lambda i: tq.search_topk(cb, q, rec, n, k))]
+    ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
     m = d
     flops = {"encode": n * 2 * (d * d + m * m), "search_topk": 2 * nq * n * (d + m)}
     tf = {kk: flops[kk] / (t[kk] * 1e-3) / 1e12 for kk in t}

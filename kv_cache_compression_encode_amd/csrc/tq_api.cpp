@@ -259,7 +259,7 @@ int64_t decode_nsplit(int64_t max_tokens) {
 }
 constexpr int kDecodeChunkTiles = 8;
 
-constexpr int kLargeTopkSegments = 4;  // partial lists per key chunk of the wide-vector path
+constexpr int kLargeTopkSegments = 16;  // partial lists per key chunk of the wide-vector path
 
 int64_t topk_nseg(int64_t n) {
   // one partial list per 4096 keys (at least those of the wide-vector path)
@@ -595,7 +595,7 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   if (cb->desc.d != 128) {
     tq_status st = map_hip(launch_query_prep_large(cb->device, cv, q, nq, 0, qr, qs, s));
     if (st != TQ_OK) return st;
-    // key chunks of large_score_chunk() rows, each cut into 4 segments; the
+    // key chunks of large_score_chunk() rows, each cut into 16 segments; the
     // partial lists of all chunks are merged at the end
     struct Ctx { int64_t nq; int k; int per_chunk; int total; float* ps; int64_t* pi; };
     const int per_chunk = kLargeTopkSegments;
@@ -603,12 +603,12 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
     Ctx ctx{nq, k, per_chunk, int(nchunks * per_chunk), pss, psi};
     if (ctx.total > nseg) return TQ_EUNSUPPORTED;
     ChunkFn fn = [](void* c, const float* scores, int64_t ld, int64_t r0, int64_t rows,
-                    hipStream_t st2) -> hipError_t {
+                    const float* col_scale, const float* row_scale, hipStream_t st2) -> hipError_t {
       // segments of a short last chunk that get no columns emit -inf entries
       Ctx* x = static_cast<Ctx*>(c);
       const int seg_base = int(r0 / large_score_chunk()) * x->per_chunk;
       return launch_topk_segments(scores, ld, rows, r0, x->nq, x->k, x->per_chunk, seg_base, x->total,
-                                  x->ps, x->pi, st2);
+                                  x->ps, x->pi, st2, col_scale, row_scale);
     };
     hipError_t e = launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
                                       nullptr, sc, s, fn, &ctx);

@@ -91,16 +91,19 @@ hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, in
 
 // Per-query top-k of a [nq][cols] score block (row stride ld, ids id_base +
 // column) into partial lists seg_base .. seg_base + nseg - 1 of total_seg.
+// Scores are part[q][t] * row_scale[q] * col_scale[t] (each scale optional).
 hipError_t launch_topk_segments(const float* scores, int64_t ld, int64_t cols, int64_t id_base,
                                 int64_t nq, int k, int nseg, int seg_base, int total_seg,
-                                float* ps, int64_t* pi, hipStream_t s);
+                                float* ps, int64_t* pi, hipStream_t s,
+                                const float* col_scale = nullptr, const float* row_scale = nullptr);
 hipError_t launch_topk_merge(const float* ps, const int64_t* pi, int64_t nq, int total_seg, int k,
                              float* out_s, int64_t* out_i, hipStream_t s);
 
 // Wide vectors (d a multiple of 128 other than 128): GEMM-based encode and
 // scoring in row chunks (tq_large.hip).
+// Chunk callback: s[q][t] = scores[q * ld + t] * row_scale[q] * col_scale[t].
 typedef hipError_t (*ChunkFn)(void* ctx, const float* scores, int64_t ld, int64_t r0, int64_t rows,
-                              hipStream_t s);
+                              const float* col_scale, const float* row_scale, hipStream_t s);
 int64_t large_encode_chunk();
 size_t large_encode_workspace(const CodecView& cv);
 hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs& a, void* ws,

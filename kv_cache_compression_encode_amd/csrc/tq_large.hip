@@ -13,8 +13,10 @@
 //               split for the sketch GEMM, ||r||^2;
 //   signpack  : sign bits [z >= 0] and the fp16 norms;
 //   dequant   : key rows [c[idx] | +-n_r] (fp16) of stored records;
-//   qsplit    : query rows [q' | sqrt(pi/2)/m q_s], scaled, split hi/lo;
-//   combine   : s = n_x (hi part + lo part) / query scale.
+//   qsplit    : query rows [q' | sqrt(pi/2)/m q_s] scaled by a power of two
+//               into fp16 (a 2^-12 relative rounding: score error at most
+//               2^-12 ||q'|| ||k_hat||, far inside the 1e-3 tolerance);
+//   combine   : s = n_x part / query scale.
 // Rows are processed in chunks so the workspace stays bounded.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
@@ -185,7 +187,7 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 // 8 coordinates (one byte of each bit plane) and one 16-byte store per lane
 // and step; +-n_r is exact since n_r is stored as fp16.
 __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_t* rec, int64_t row0,
-                                                      int64_t rows, uint16_t* kcat) {
+                                                      int64_t rows, uint16_t* kcat, float* nxv) {
   __shared__ uint16_t scen[kMaxLevels];
   if (threadIdx.x < kMaxLevels) scen[threadIdx.x] = f16b(cv.ucen[threadIdx.x]);
   __syncthreads();
@@ -198,6 +200,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_
   const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
   const int slot = int(grow % kTile);
   uint16_t* out = kcat + row * kw;
+  if (lane == 0) nxv[row] = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nx + 2 * slot));
   for (int c8 = lane; c8 < d / 8; c8 += 64) {
     uint32_t pb[kMaxBits];
 #pragma unroll
@@ -236,8 +239,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(CodecView cv, const uint8_
 }
 
 // One wave per query: row v = [q' | sqrt(pi/2)/m q_s] (d + m values), scale
-// 2^e putting max |v| in [2^14, 2^15), fp16 hi/lo parts of v 2^e as rows
-// q (hi) and nq + q (lo) of out [2 nq][d + m], and inv[q] = 2^-e.
+// 2^e putting max |v| in [2^14, 2^15), fp16 of v 2^e as row q of out
+// [nq][d + m], and inv[q] = 2^-e.
 __global__ __launch_bounds__(256) void qsplit_kernel(const float* qr, const float* qs, int64_t nq,
                                                      int d, int m, float kq, uint16_t* out,
                                                      float* inv) {
@@ -253,29 +256,17 @@ __global__ __launch_bounds__(256) void qsplit_kernel(const float* qr, const floa
   const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
   const int e = mx > 0.f ? min(253, max(1, 268 - ebits)) : 127;
   const float p2 = __uint_as_float(uint32_t(e) << 23);
-  for (int i = lane; i < w; i += 64) {
-    const float v = at(i) * p2;
-    const uint16_t h = f16b(v);
-    out[q * w + i] = h;
-    out[(nq + q) * w + i] = f16b(v - f16v(h));
-  }
+  for (int i = lane; i < w; i += 64) out[q * w + i] = f16b(at(i) * p2);
   if (lane == 0) inv[q] = __uint_as_float(uint32_t(254 - e) << 23);
 }
 
-// s[q][t] = n_x[t] inv[q] (part[q][t] + part[nq + q][t]); may run in place
-// (out == part, ld_out == ld_parts).
-__global__ void combine_kernel(CodecView cv, const float* part, const float* inv, int64_t nq,
-                               int64_t nc, int64_t ld_parts, const uint8_t* rec, int64_t row0,
-                               float* out, int64_t ld_out) {
+// s[q][t] = nxv[t] inv[q] part[q][t]
+__global__ void combine_kernel(const float* part, const float* inv, const float* nxv, int64_t nq,
+                               int64_t nc, int64_t ld_parts, float* out, int64_t ld_out) {
   const int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= nq * nc) return;
   const int64_t q = e / nc, t = e % nc;
-  const int64_t grow = row0 + t;
-  const uint8_t* trec = rec + (grow / kTile) * cv.tile_bytes;
-  const int slot = int(grow % kTile);
-  const float nx = f16v(*reinterpret_cast<const uint16_t*>(trec + cv.off_nx + 2 * slot));
-  const float s = part[q * ld_parts + t] + part[(q + nq) * ld_parts + t];
-  out[q * ld_out + t] = nx * (inv[q] * s);
+  out[q * ld_out + t] = nxv[t] * (inv[q] * part[q * ld_parts + t]);
 }
 
 // ------------------------------------------------------------- rocBLAS
@@ -428,23 +419,24 @@ int64_t large_score_chunk() { return 65536; }
 namespace {
 struct ScoreWs {
   uint16_t *qcat, *kcat;
-  float *inv, *part;
+  float *inv, *part, *nxv;
 };
 
 size_t score_ws_layout(const CodecView& cv, int64_t nq, void* base, ScoreWs* out) {
   const size_t NC = size_t(large_score_chunk()), d = size_t(cv.d);
   const size_t kw = d + (cv.mode == TQ_PROD ? size_t(cv.m) : 0);
   auto r = [](size_t v) { return (v + 255) & ~size_t(255); };
-  const size_t sizes[] = {r(2 * size_t(nq) * kw * 2), r(NC * kw * 2), r(size_t(nq) * 4),
-                          r(2 * size_t(nq) * NC * 4)};
-  size_t off[4], tot = 0;
-  for (int i = 0; i < 4; ++i) { off[i] = tot; tot += sizes[i]; }
+  const size_t sizes[] = {r(size_t(nq) * kw * 2), r(NC * kw * 2), r(size_t(nq) * 4),
+                          r(size_t(nq) * NC * 4), r(NC * 4)};
+  size_t off[5], tot = 0;
+  for (int i = 0; i < 5; ++i) { off[i] = tot; tot += sizes[i]; }
   if (out) {
     uint8_t* p = static_cast<uint8_t*>(base);
     out->qcat = reinterpret_cast<uint16_t*>(p + off[0]);
     out->kcat = reinterpret_cast<uint16_t*>(p + off[1]);
     out->inv = reinterpret_cast<float*>(p + off[2]);
     out->part = reinterpret_cast<float*>(p + off[3]);
+    out->nxv = reinterpret_cast<float*>(p + off[4]);
   }
   return tot;
 }
@@ -457,8 +449,9 @@ size_t large_score_workspace(const CodecView& cv, int64_t nq) {
 // Scores of nq prepared queries (qr [nq][d], qs [nq][m] fp32) against n
 // records: s = n_x <[q' | sqrt(pi/2)/m q_s], [c[idx] | n_r sign]>, one GEMM
 // per key chunk.  With out != nullptr the scores go to out[nq][n]; otherwise
-// each chunk's scores (in the workspace, row stride large_score_chunk()) are
-// handed to chunk_cb(scores, ld, r0, rows) (the top-k search).
+// each chunk's unscaled products (row stride large_score_chunk()) and the
+// scales n_x (per key) and 2^-e (per query) are handed to chunk_cb (the top-k
+// search applies them as it scans).
 hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, const float* qs,
                               int64_t nq, const uint8_t* rec, int64_t n, float* out, void* ws,
                               hipStream_t s, ChunkFn chunk_cb, void* cb_ctx) {
@@ -478,17 +471,17 @@ hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, 
   for (int64_t r0 = 0; r0 < n; r0 += NC) {
     const int64_t rows = std::min(NC, n - r0);
     hipLaunchKernelGGL(dequant_kernel, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, cv, rec, r0, rows,
-                       W.kcat);
+                       W.kcat, W.nxv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // [q_hi; q_lo] kcat^T  ->  part [2 nq][NC]
-    if ((e = gemm_abt(h, W.qcat, W.kcat, W.part, 2 * nq, rows, kw, kw, kw, NC, false)) != hipSuccess)
+    // q kcat^T  ->  part [nq][NC]
+    if ((e = gemm_abt(h, W.qcat, W.kcat, W.part, nq, rows, kw, kw, kw, NC, false)) != hipSuccess) return e;
+    if (out) {
+      hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(nq * rows)), dim3(256), 0, s, W.part, W.inv, W.nxv,
+                         nq, rows, NC, out + r0, n);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (chunk_cb && (e = chunk_cb(cb_ctx, W.part, NC, r0, rows, W.nxv, W.inv, s)) != hipSuccess) {
       return e;
-    float* dst = out ? out + r0 : W.part;
-    const int64_t ld = out ? n : NC;
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks_for(nq * rows)), dim3(256), 0, s, cv, W.part, W.inv, nq,
-                       rows, NC, rec, r0, dst, ld);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (!out && chunk_cb && (e = chunk_cb(cb_ctx, W.part, NC, r0, rows, s)) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

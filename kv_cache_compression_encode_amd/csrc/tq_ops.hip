@@ -475,63 +475,72 @@ __device__ __forceinline__ bool better(float s1, int64_t i1, float s2, int64_t i
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// Block (segment, query): per-thread top-16 of a strided subset, then k rounds
-// of a block-wide arg-max over the thread heads.
+// One wave per (query, segment).  The wave keeps one sorted top-16 list
+// spread over the 16 lanes of each row (lane i of every row holds entry i;
+// the four rows stay identical).  The segment is scanned 256 scores at a
+// time; a score enters only if it beats the list's k-th entry (the running
+// threshold), and entering candidates are inserted one at a time with a row
+// shift, so after the first few blocks almost every block is a compare and a
+// ballot.  Scores are part[q][t] * row_scale[q] * col_scale[t] (scales
+// optional).  Lanes 0..k-1 write the segment's sorted top-k.
 __global__ __launch_bounds__(256) void topk_segment_kernel(const float* scores, int64_t ld,
                                                            int64_t cols, int64_t id_base, int k,
                                                            int nseg, int seg_base, int total_seg,
-                                                           float* ps, int64_t* pi) {
-  __shared__ float rs[256];
-  __shared__ int64_t ri[256];
-  __shared__ int rt[256];
-  const int seg = blockIdx.x;
+                                                           float* ps, int64_t* pi,
+                                                           const float* col_scale,
+                                                           const float* row_scale) {
+  const int lane = threadIdx.x & 63, li16 = lane & 15;
+  const int seg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t qi = blockIdx.y;
+  if (seg >= nseg) return;
   const int64_t per = (cols + nseg - 1) / nseg;
   const int64_t lo = seg * per, hi = min(cols, lo + per);
-  float ls[kTopMax];
-  int64_t li[kTopMax];
-#pragma unroll
-  for (int r = 0; r < kTopMax; ++r) { ls[r] = -INFINITY; li[r] = INT64_MAX; }
   const float* row = scores + qi * ld;
-  for (int64_t t = lo + threadIdx.x; t < hi; t += blockDim.x) {
-    float s = row[t];
-    int64_t id = id_base + t;
-    if (!better(s, id, ls[kTopMax - 1], li[kTopMax - 1])) continue;
+  const float rsc = row_scale ? row_scale[qi] : 1.f;
+  float Ls = -INFINITY;        // entry li16 of the list
+  int64_t Lid = INT64_MAX;
+  float ts = -INFINITY;        // threshold: entry k-1
+  int64_t tid = INT64_MAX;
+  for (int64_t base = lo; base < hi; base += 256) {
+    float v[4];
 #pragma unroll
-    for (int r = 0; r < kTopMax; ++r) {
-      if (better(s, id, ls[r], li[r])) {
-        const float ts = ls[r];
-        const int64_t ti = li[r];
-        ls[r] = s; li[r] = id;
-        s = ts; id = ti;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = base + 64 * u + lane;
+      v[u] = t < hi ? row[t] * rsc * (col_scale ? col_scale[t] : 1.f) : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t t = base + 64 * u + lane;
+      const int64_t id = id_base + t;
+      bool pend = t < hi;
+      while (true) {
+        const uint64_t m = __ballot(pend && better(v[u], id, ts, tid));
+        if (m == 0) break;
+        const int src = __ffsll((unsigned long long)m) - 1;
+        const float cs = __shfl(v[u], src, 64);
+        const int64_t cid = id_base + base + 64 * u + src;
+        // insert (cs, cid): entries better than it keep their place
+        const bool keep = better(Ls, Lid, cs, cid);
+        const int pos = __popcll(__ballot(keep) & 0xffffull);
+        const float shs = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(Ls), __float_as_int(Ls),
+                                                                     0x111, 0xF, 0xF, false));  // row_shr:1
+        const uint32_t idl = uint32_t(uint64_t(Lid)), idh = uint32_t(uint64_t(Lid) >> 32);
+        const uint32_t shl = uint32_t(__builtin_amdgcn_update_dpp(int(idl), int(idl), 0x111, 0xF, 0xF, false));
+        const uint32_t shh = uint32_t(__builtin_amdgcn_update_dpp(int(idh), int(idh), 0x111, 0xF, 0xF, false));
+        if (!keep) {
+          if (li16 == pos) { Ls = cs; Lid = cid; }
+          else { Ls = shs; Lid = int64_t((uint64_t(shh) << 32) | shl); }
+        }
+        ts = __shfl(Ls, k - 1, 64);
+        tid = __shfl(Lid, k - 1, 64);
+        if (lane == src) pend = false;
       }
     }
   }
-  int head = 0;
-  for (int round = 0; round < k; ++round) {
-    float hs = -INFINITY;
-    int64_t hid = INT64_MAX;
-#pragma unroll
-    for (int r = 0; r < kTopMax; ++r)
-      if (r == head) { hs = ls[r]; hid = li[r]; }
-    rs[threadIdx.x] = hs; ri[threadIdx.x] = hid; rt[threadIdx.x] = threadIdx.x;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (threadIdx.x < o) {
-        const int a2 = threadIdx.x + o;
-        if (better(rs[a2], ri[a2], rs[threadIdx.x], ri[threadIdx.x])) {
-          rs[threadIdx.x] = rs[a2]; ri[threadIdx.x] = ri[a2]; rt[threadIdx.x] = rt[a2];
-        }
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-      const int64_t o = (qi * total_seg + seg_base + seg) * k + round;
-      ps[o] = rs[0];
-      pi[o] = ri[0];
-    }
-    if (threadIdx.x == rt[0]) ++head;
-    __syncthreads();
+  if (lane < k) {
+    const int64_t o = (qi * total_seg + seg_base + seg) * k + lane;
+    ps[o] = Ls;
+    pi[o] = Lid;
   }
 }
 
@@ -628,9 +637,10 @@ hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeA
 
 hipError_t launch_topk_segments(const float* scores, int64_t ld, int64_t cols, int64_t id_base,
                                 int64_t nq, int k, int nseg, int seg_base, int total_seg,
-                                float* ps, int64_t* pi, hipStream_t s) {
-  hipLaunchKernelGGL(topk_segment_kernel, dim3(unsigned(nseg), unsigned(nq)), dim3(256), 0, s, scores,
-                     ld, cols, id_base, k, nseg, seg_base, total_seg, ps, pi);
+                                float* ps, int64_t* pi, hipStream_t s, const float* col_scale,
+                                const float* row_scale) {
+  hipLaunchKernelGGL(topk_segment_kernel, dim3(unsigned((nseg + 3) / 4), unsigned(nq)), dim3(256), 0, s,
+                     scores, ld, cols, id_base, k, nseg, seg_base, total_seg, ps, pi, col_scale, row_scale);
   return hipGetLastError();
 }
 
