@@ -211,6 +211,18 @@ __device__ __forceinline__ float quant_bits(float v, f32x16v T, const float* L, 
   }
 }
 
+// w = 2 w + [b]: one v_addc with the comparison's lane mask as the carry in
+// (the mask is the same SGPR pair the selects of the quantizer use).  Bits
+// pushed for registers r = 15 .. 0 land at bit r.
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, bool b) {
+  const uint64_t m = __ballot(b);
+  uint32_t r;
+  uint64_t cout;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(cout) : "v"(w), "s"(m));
+  (void)cout;
+  return r;
+}
+
 // OR across groups of `VPD` consecutive lanes (8 or 16) with DPP moves:
 // quad xor-1, quad xor-2, then half-row / row mirrors.
 template <int VPD>
@@ -268,30 +280,22 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   // Loads are unconditional (rows past the end read the last row instead and
   // their results are discarded), so no load sits behind a branch and the
   // wait counters stay exact across the prefetch.
-  u32x4 pre[NB][8];
-  auto load_raw = [&](int64_t tl, int sb) {
+  // The raw rows alternate between two register sets (the next sub-tile's
+  // loads go to one set while the other is processed; no copies between them).
+  u32x4 bufA[NB][8], bufB[NB][8];
+  auto load_raw = [&](int64_t tl, int sb, u32x4 (&dst)[NB][8]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t t = tl * kTile + sb * 32 * NB + nb * 32 + j;
       const int64_t tc = (tl < ntiles && t < a.tokens) ? t : a.tokens - 1;
       const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + tc * a.xs_t + 64 * hh;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) pre[nb][c] = *reinterpret_cast<const u32x4*>(row + 8 * c);
+      for (int c = 0; c < 8; ++c) dst[nb][c] = *reinterpret_cast<const u32x4*>(row + 8 * c);
     }
   };
-  if (BF16IN) load_raw(int64_t(blockIdx.x) * nwaves + wave, 0);
-  for (int64_t tile = int64_t(blockIdx.x) * nwaves + wave; tile < ntiles; tile += tstep) {
+  auto process = [&](const u32x4 (&cur)[NB][8], int64_t tile, int sub) {
     uint8_t* trec = rbase + tile * cv.tile_bytes;
-    for (int sub = 0; sub < NSUB; ++sub) {
-      u32x4 cur[NB][8];
-      if (BF16IN) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) cur[nb][c] = pre[nb][c];
-        if (sub + 1 < NSUB) load_raw(tile, sub + 1);
-        else load_raw(tile + tstep, 0);
-      }
+    {
       // ---------------------------------------------------------- load X
       // xh/xl: fp16 hi/lo fragments of x * 2^e, e chosen per vector so that
       // max|x| * 2^e lies in [2^14, 2^15); w = 16 * 2^e * s_x is the factor
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int r = 15; r >= 0; --r) {  // descending: row-code bits are pushed MSB first
             const int dim = 32 * mb + 16 * hh + r;
             const float v = acc[nb][r];
             int idx = 0;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               bool bits[4] = {false, false, false, false};
               chat = quant_bits<UB>(v, T[nb], C32, bits);
 #pragma unroll
-              for (int p = 0; p < NPL; ++p) cw[nb][p] |= uint32_t(bits[p]) << r;
+              for (int p = 0; p < NPL; ++p) cw[nb][p] = push_bit(cw[nb][p], bits[p]);
             } else if (UNIFORM) {
               idx = quant_tree<UB>(v, T[nb]);
               if (MODE != 0) {
@@ -511,7 +515,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             for (int p = 0; p < NPL; ++p) {
               const uint32_t mine = valid[nb] ? cw[nb][p] << (16 * hh) : 0u;
               const uint32_t w = mine | xor32(mine);
-              if (hh == 0) *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
+              // both halves hold the same word: an unconditional store keeps
+              // the number of memory operations the same on every path
+              *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
             }
           }
           if (COL && UB > 1) {
@@ -570,12 +576,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           rr[nb] += xor32f(rr[nb]);
           // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
 #pragma unroll
-          for (int ms = 0; ms < 4; ++ms)
+          for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const bool sgn = z[nb][ms][r] >= 0.f && valid[nb];
-              if (!COL) sw[nb][ms] |= uint32_t(sgn) << r;
-            }
+            for (int r = 15; r >= 0; --r)
+              if (!COL) sw[nb][ms] = push_bit(sw[nb][ms], z[nb][ms][r] >= 0.f);
+            if (!valid[nb]) sw[nb][ms] = 0;
+          }
         } else if (MODE == 2) {
           if (hh == 0) {
 #pragma unroll
@@ -603,21 +609,22 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           }
           if (!UNIFORM) {
             const int tb = cv.code_bytes - 16;  // tail bytes per vector (1..4)
-            if (hh == 0)
-              for (int k = 0; k < tb; ++k)
-                trec[size_t(kTile) * 16 + size_t(slot) * tb + k] = uint8_t(tailw[nb] >> (8 * k));
+            for (int k = 0; k < tb; ++k)
+              trec[size_t(kTile) * 16 + size_t(slot) * tb + k] = uint8_t(tailw[nb] >> (8 * k));
           }
           if (MODE == 1) {
             uint8_t* dst = trec + cv.off_signs + slot * 16 + 8 * hh;
             *reinterpret_cast<u32x2*>(dst) = hh ? u32x2{sw[nb][2], sw[nb][3]}
                                                 : u32x2{sw[nb][0], sw[nb][1]};
           } else if (MODE == 2) {
-            if (hh == 0)
-              for (int k = 0; k < cv.sign_bytes; ++k)
-                trec[cv.off_signs + size_t(slot) * cv.sign_bytes + k] = uint8_t(sw[nb][0] >> (8 * k));
+            sw[nb][0] |= xor32(sw[nb][0]);  // only half 0 formed the small sketch
+            for (int k = 0; k < cv.sign_bytes; ++k)
+              trec[cv.off_signs + size_t(slot) * cv.sign_bytes + k] = uint8_t(sw[nb][0] >> (8 * k));
           }
         }
-        if (hh == 0) {
+        // both halves store the same norms (no divergent branch around stores)
+        if (MODE == 2) rr[nb] += xor32f(rr[nb]);  // only half 0 summed the small residual
+        {
           const float nx = valid[nb] ? nxv[nb] : 0.f;
           *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nx);
           if (MODE != 0) {
@@ -627,6 +634,48 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           }
         }
       }
+    }
+  };
+  // (tile, sub-tile) positions of this wave, in order
+  auto next_pos = [&](int64_t& tl, int& sb) {
+    if (sb + 1 < NSUB) { ++sb; } else { sb = 0; tl += tstep; }
+  };
+  int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
+  int sub = 0;
+  if (BF16IN) load_raw(tile, 0, bufA);
+  if constexpr (NB == 1) {
+    while (tile < ntiles) {
+      int64_t t1 = tile;
+      int s1 = sub;
+      next_pos(t1, s1);
+      if (BF16IN) load_raw(t1, s1, bufB);
+      process(bufA, tile, sub);
+      tile = t1;
+      sub = s1;
+      if (tile >= ntiles) break;
+      next_pos(t1, s1);
+      if (BF16IN) load_raw(t1, s1, bufA);
+      process(bufB, tile, sub);
+      tile = t1;
+      sub = s1;
+    }
+  } else {
+    // two 32-vector blocks per sub-tile: one code path, the prefetched set
+    // is copied (two alternating instances would not fit the registers)
+    while (tile < ntiles) {
+      int64_t t1 = tile;
+      int s1 = sub;
+      next_pos(t1, s1);
+      if (BF16IN) load_raw(t1, s1, bufB);
+      process(bufA, tile, sub);
+      if (BF16IN) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) bufA[nb][c] = bufB[nb][c];
+      }
+      tile = t1;
+      sub = s1;
     }
   }
 }
