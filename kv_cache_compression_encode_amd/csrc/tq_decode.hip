@@ -124,10 +124,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __shared__ float smu[4];
   __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
-  // value byte (two 4-bit codes) -> fp16 pair, one copy per LDS bank: entry e
-  // of lane l sits at slut[e * 32 + l % 32], so the random lookups of a wave
-  // never conflict
-  __shared__ uint32_t slut[256 * 32];
+  // value byte (two 4-bit codes) -> fp16 pair; kLutCopies copies, entry e of
+  // lane l at slut[e * kLutCopies + l % kLutCopies] (more copies spread the
+  // random lookups of a wave over more banks; one copy keeps the block's
+  // set-up short)
+  constexpr int kLutCopies = 1;
+  __shared__ uint32_t slut[256 * kLutCopies];
   constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
   __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   {
     const int t = threadIdx.x;  // 256 threads: one table entry each
     const uint32_t e = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
-#pragma unroll 8
-    for (int c = 0; c < 32; ++c) slut[t * 32 + ((c + t) & 31)] = e;
+#pragma unroll
+    for (int c = 0; c < kLutCopies; ++c) slut[t * kLutCopies + ((c + t) & (kLutCopies - 1))] = e;
   }
   for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
   if (SQ && threadIdx.x < D) {
@@ -406,11 +408,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const uint32_t w = vw[vb][kc2];
         u32x4 B;
-        const uint32_t* lut = slut + (lane & 31);
-        B[0] = lut[(w & 0xffu) * 32];
-        B[1] = lut[((w >> 8) & 0xffu) * 32];
-        B[2] = lut[((w >> 16) & 0xffu) * 32];
-        B[3] = lut[(w >> 24) * 32];
+        const uint32_t* lut = slut + (lane & (kLutCopies - 1));
+        B[0] = lut[(w & 0xffu) * kLutCopies];
+        B[1] = lut[((w >> 8) & 0xffu) * kLutCopies];
+        B[2] = lut[((w >> 16) & 0xffu) * kLutCopies];
+        B[3] = lut[(w >> 24) * kLutCopies];
         accv[vb] = mfma16(Ap[kc2], B, accv[vb]);
       }
     }
