@@ -27,7 +27,7 @@ tq_status upload(T** dst, const T* src, size_t count) {
 void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
   void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
-                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits};
+                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -242,6 +242,34 @@ tq_status build_device(tq_codebook* cb) {
   if ((st = upload(&cb->dev.cen, cb->cen32.data(), cb->cen32.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.bitpos, cb->bitpos.data(), cb->bitpos.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.dim_bits, cb->bits.data(), size_t(d))) != TQ_OK) return st;
+  if (!cb->uniform && d == 128) {
+    // tail byte t -> bits 1.. of the indices of dims 0..3 (dim i at bits 5i..5i+4),
+    // for the bit positions D..D+7 of the row bit string
+    std::vector<uint32_t> tail(256, 0u);
+    for (uint32_t t = 0; t < 256; ++t) {
+      uint32_t packed = 0;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t v = 0;
+        for (int pl = 1; pl < cb->bits[i] && pl < kMaxBits; ++pl) {
+          const int pos = cb->bitpos[size_t(pl) * d + i] - d;
+          if (pos >= 0 && pos < 8) v |= ((t >> pos) & 1u) << pl;
+        }
+        packed |= (v & 31u) << (5 * i);
+      }
+      tail[t] = packed;
+    }
+    const int heads = cb->info.num_heads;
+    std::vector<float> gm(size_t(heads) * 2 * d);
+    for (int hh = 0; hh < heads; ++hh)
+      for (int i = 0; i < d; ++i) {
+        const float c0 = cb->cen32[(size_t(hh) * d + i) * kMaxLevels];
+        const float c1 = cb->cen32[(size_t(hh) * d + i) * kMaxLevels + 1];
+        gm[(size_t(hh) * 2 + 0) * d + i] = 0.5f * (c1 - c0);
+        gm[(size_t(hh) * 2 + 1) * d + i] = 0.5f * (c1 + c0);
+      }
+    if ((st = upload(&cb->dev.sq_tail, tail.data(), tail.size())) != TQ_OK) return st;
+    if ((st = upload(&cb->dev.sq_gm, gm.data(), gm.size())) != TQ_OK) return st;
+  }
   return TQ_OK;
 }
 
@@ -293,7 +321,7 @@ CodecView tq::make_view(const tq_codebook* cb) {
     bool ok = true;
     for (int i = 0; i < cb->desc.d; ++i)
       ok = ok && (i < 4 ? cb->bits[i] >= 1 && cb->bits[i] <= 5 : cb->bits[i] == 1);
-    v.sq_ok = ok;
+    v.sq_ok = ok && cb->dev.sq_tail != nullptr;
   }
   v.rot = cb->dev.rot;
   v.rot_t = cb->dev.rot_t;
@@ -307,6 +335,8 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.cen = cb->dev.cen;
   v.bitpos = cb->dev.bitpos;
   v.dim_bits = cb->dev.dim_bits;
+  v.sq_tail = cb->dev.sq_tail;
+  v.sq_gm = cb->dev.sq_gm;
   for (int k = 0; k < kMaxLevels; ++k) {
     v.uthr[k] = cb->thr32[k];
     v.ucen[k] = cb->cen32[k];
@@ -545,13 +575,19 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   da.max_tokens = kv->max_tokens;
   da.seq_lens = kv->seq_lens;
   da.scale = softmax_scale;
-  // splits of 8 tiles, widened while the grid keeps >= 2048 blocks (fewer
-  // partials and a longer tile loop per block for large batches); never more
-  // splits than the workspace holds
+  // splits of 8 tiles, widened while the grid still fills every resident
+  // workgroup slot (two per CU): fewer block set-ups and partials for large
+  // batches, down to one split per sequence (then no merge pass at all);
+  // never more splits than the workspace holds
   {
     const int64_t ntiles = (int64_t(kv->max_tokens) + kTile - 1) / kTile;
+    int cus = 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, kcb->device) != hipSuccess) cus = 256;
+    const int64_t slots = 2 * int64_t(cus);
     int chunk = kDecodeChunkTiles;
-    while (chunk < 64 && int64_t(B) * Hkv * ((ntiles + 2 * chunk - 1) / (2 * chunk)) >= 2048) chunk *= 2;
+    while (chunk < 1024 && chunk < ntiles &&
+           int64_t(B) * Hkv * ((ntiles + 2 * chunk - 1) / (2 * chunk)) >= slots)
+      chunk *= 2;
     da.chunk_tiles = chunk;
     da.nsplit = int(std::max<int64_t>(1, (ntiles + chunk - 1) / chunk));
   }

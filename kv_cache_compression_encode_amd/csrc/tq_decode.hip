@@ -124,134 +124,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __shared__ float smu[4];
   __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
-  // value byte (two 4-bit codes) -> fp16 pair; kLutCopies copies, entry e of
-  // lane l at slut[e * kLutCopies + l % kLutCopies] (more copies spread the
-  // random lookups of a wave over more banks; one copy keeps the block's
-  // set-up short)
-  constexpr int kLutCopies = 1;
-  __shared__ uint32_t slut[256 * kLutCopies];
+  __shared__ float skc[SQ ? 4 : 1][kMaxLevels];  // SQ: levels of dims 0..3
+  // value byte (two 4-bit codes) -> fp16 pair of their levels
+  __shared__ uint32_t slut[256];
   constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
   __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
   __shared__ float sacc[4][4][D];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
-    const int gg = e / D, i = e % D;
-    const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
-    sqr[gg][i] = gg < G ? a.qr[qi * D + i] : 0.f;
-    sqs[gg][i] = gg < G && i < kc.m ? a.qs[qi * kc.m + i] : 0.f;
-  }
-  const int hk = kc.heads > 1 ? g : 0;
-  const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
-  {
-    const int t = threadIdx.x;  // 256 threads: one table entry each
-    const uint32_t e = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
-#pragma unroll
-    for (int c = 0; c < kLutCopies; ++c) slut[t * kLutCopies + ((c + t) & (kLutCopies - 1))] = e;
-  }
-  for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
-  if (SQ && threadIdx.x < D) {
-    const float c0 = kcen[threadIdx.x * kMaxLevels], c1 = kcen[threadIdx.x * kMaxLevels + 1];
-    sgam[threadIdx.x] = 0.5f * (c1 - c0);
-    smuv[threadIdx.x] = 0.5f * (c1 + c0);
-  }
-  __syncthreads();
-  if (SQ) {
-    for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
-      const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
-      slow[gg][i][l] = sqr[gg][i] * kcen[i * kMaxLevels + l];
-    }
-    {
-      const uint32_t t = threadIdx.x;  // 256 threads: one tail-byte pattern each
-      uint32_t packed = 0;
-      for (int i = 0; i < 4; ++i) {
-        const int bi = kc.dim_bits[i];
-        uint32_t v = 0;
-        for (int pl = 1; pl < bi; ++pl) v |= ((t >> (kc.bitpos[pl * D + i] - D)) & 1u) << pl;
-        packed |= v << (5 * i);
-      }
-      stail[t] = packed;
-    }
-    if (threadIdx.x < 64) {  // sum_{i >= 4} mu_i q'_i per query
-      const int lane = threadIdx.x;
-      for (int gg = 0; gg < 4; ++gg) {
-        float v = 0.f;
-        for (int i = 4 + lane; i < D; i += 64) v += smuv[i] * sqr[gg][i];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0) smu[gg] = v;
-      }
-    }
-    __syncthreads();
-  }
-
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g16 = lane >> 4;
-
-  // ---- score A fragments: chunk (p, c): lane row r = n, dims 32 g16 + 8c + s
-  float wp[2];
-  if (SQ) {
-    wp[0] = wp[1] = 0.f;
-  } else if (UB == 2) {
-    wp[0] = 0.5f * (kc.ucen[3] - kc.ucen[2]);
-    wp[1] = 0.5f * (kc.ucen[3] + kc.ucen[2]);
-  } else {
-    wp[0] = kc.ucen[1];
-    wp[1] = 0.f;
-  }
-  constexpr int NP = SQ ? 1 : UB + 1;  // +-1 planes in the MFMA chain (incl. signs)
-  // the A fragments depend on the lane only: wave 0 builds them once into LDS
-  // and every wave reads them back per tile (keeping them live across the
-  // tile loop would exceed the register budget)
-  __shared__ u32x4 sA[NP * 4][64];
-  if (wave == 0) {
-#pragma unroll
-  for (int p = 0; p < NP; ++p)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool sign_part = p == NP - 1;
-      const int r = n;
-      const bool rowsig = r >= 8;
-      const int gq = (r & 7) >> 1, lo = r & 1;
-      float v[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int dim = 32 * g16 + 8 * c + s;
-        float x = 0.f;
-        if (gq < G) {
-          if (SQ) {
-            if (!rowsig && dim >= 4) x = sgam[dim] * sqr[gq][dim];
-          } else {
-            if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
-            if (rowsig && sign_part) x = sqs[gq][dim];
-          }
-        }
-        const float hi = f16v(f16b(x));
-        v[s] = lo ? x - hi : x;
-      }
-      u32x4 f;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) f[s2] = f16b(v[2 * s2]) | (f16b(v[2 * s2 + 1]) << 16);
-      sA[p * 4 + c][lane] = f;
-    }
-  }
-  __syncthreads();
-
   const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
   const int ntiles = (len + kTile - 1) / kTile;
   const uint8_t* kbase = a.krec + int64_t(b) * a.ks_seq + int64_t(g) * a.ks_head;
   const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
-  const float coef_scale = kQjl / float(kc.m);
-
-  // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
-  f32x4 accv[8];
-#pragma unroll
-  for (int vb = 0; vb < 8; ++vb) accv[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   const int t_begin = split * a.chunk_tiles;
   const int t_end = min(ntiles, t_begin + a.chunk_tiles);
+  constexpr int NP = SQ ? 1 : UB + 1;  // +-1 planes in the MFMA chain (incl. signs)
   // ---- loads of one tile: key planes/signs (dword g16 of token 16nb+n),
   // value fields, fp16 norms (raw), SQ low/tail/sign bytes; the next tile's
   // loads are issued before the current tile is processed
@@ -290,6 +180,102 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       R.sg = kt[kc.off_signs + tok];
     }
   };
+  TileRegs& ra = cur;
+  TileRegs& rb = nxt;
+  // the first tile's loads go out before the set-up below and overlap it
+  if (t_begin + wave < t_end) load_tile(t_begin + wave, ra);
+
+  // ---- set-up: one round of independent loads, then LDS-only arithmetic
+  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+    const int gg = e / D, i = e % D;
+    const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
+    sqr[gg][i] = gg < G ? a.qr[qi * D + i] : 0.f;
+    sqs[gg][i] = gg < G && i < kc.m ? a.qs[qi * kc.m + i] : 0.f;
+  }
+  const int hk = kc.heads > 1 ? g : 0;
+  const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
+  {
+    const int t = threadIdx.x;  // 256 threads: one value-table entry each
+    slut[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+  }
+  for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
+  if (SQ) {
+    stail[threadIdx.x] = kc.sq_tail[threadIdx.x];
+    if (threadIdx.x < D) {
+      sgam[threadIdx.x] = kc.sq_gm[(size_t(hk) * 2 + 0) * D + threadIdx.x];
+      smuv[threadIdx.x] = kc.sq_gm[(size_t(hk) * 2 + 1) * D + threadIdx.x];
+    } else {
+      const int e = threadIdx.x - D;  // 128 threads: levels of dims 0..3
+      skc[e / kMaxLevels][e % kMaxLevels] = kcen[(e / kMaxLevels) * kMaxLevels + e % kMaxLevels];
+    }
+  }
+  __syncthreads();
+  if (SQ) {
+    for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
+      const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
+      slow[gg][i][l] = sqr[gg][i] * skc[i][l];
+    }
+    {  // wave w: sum_{i >= 4} mu_i q'_i of query w
+      float v = 0.f;
+      for (int i = 4 + lane; i < D; i += 64) v += smuv[i] * sqr[wave][i];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) smu[wave] = v;
+    }
+  }
+
+  // ---- score A fragments: chunk (p, c): lane row r = n, dims 32 g16 + 8c + s
+  float wp[2];
+  if (SQ) {
+    wp[0] = wp[1] = 0.f;
+  } else if (UB == 2) {
+    wp[0] = 0.5f * (kc.ucen[3] - kc.ucen[2]);
+    wp[1] = 0.5f * (kc.ucen[3] + kc.ucen[2]);
+  } else {
+    wp[0] = kc.ucen[1];
+    wp[1] = 0.f;
+  }
+  // the A fragments depend on the lane only: the waves build them once into
+  // LDS (fragment f by wave f % 4) and read them back per tile (keeping them
+  // live across the tile loop would exceed the register budget)
+  __shared__ u32x4 sA[NP * 4][64];
+  for (int f = wave; f < NP * 4; f += 4) {
+    const int p = f / 4, c = f % 4;
+    const bool sign_part = p == NP - 1;
+    const int r = n;
+    const bool rowsig = r >= 8;
+    const int gq = (r & 7) >> 1, lo = r & 1;
+    float v[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int dim = 32 * g16 + 8 * c + s;
+      float x = 0.f;
+      if (gq < G) {
+        if (SQ) {
+          if (!rowsig && dim >= 4) x = sgam[dim] * sqr[gq][dim];
+        } else {
+          if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
+          if (rowsig && sign_part) x = sqs[gq][dim];
+        }
+      }
+      const float hi = f16v(f16b(x));
+      v[s] = lo ? x - hi : x;
+    }
+    u32x4 fr;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) fr[s2] = f16b(v[2 * s2]) | (f16b(v[2 * s2 + 1]) << 16);
+    sA[f][lane] = fr;
+  }
+  __syncthreads();
+
+  const float coef_scale = kQjl / float(kc.m);
+
+  // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  f32x4 accv[8];
+#pragma unroll
+  for (int vb = 0; vb < 8; ++vb) accv[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   // tiles tile, tile + 4, ... alternate between two register sets (no copies
   // between them, so nothing waits for the next tile's loads early)
   auto process = [&](const TileRegs& R, int tile) {
@@ -408,19 +394,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int kc2 = 0; kc2 < 2; ++kc2) {
         const uint32_t w = vw[vb][kc2];
         u32x4 B;
-        const uint32_t* lut = slut + (lane & (kLutCopies - 1));
-        B[0] = lut[(w & 0xffu) * kLutCopies];
-        B[1] = lut[((w >> 8) & 0xffu) * kLutCopies];
-        B[2] = lut[((w >> 16) & 0xffu) * kLutCopies];
-        B[3] = lut[(w >> 24) * kLutCopies];
+        B[0] = slut[w & 0xffu];
+        B[1] = slut[(w >> 8) & 0xffu];
+        B[2] = slut[(w >> 16) & 0xffu];
+        B[3] = slut[w >> 24];
         accv[vb] = mfma16(Ap[kc2], B, accv[vb]);
       }
     }
     __builtin_amdgcn_wave_barrier();
   };
-  TileRegs& ra = cur;
-  TileRegs& rb = nxt;
-  if (t_begin + wave < t_end) load_tile(t_begin + wave, ra);
   // the prefetches are unconditional (clamped to the last tile, a harmless
   // re-read) so that the wait counters stay exact across the loop
   for (int tile = t_begin + wave; tile < t_end; tile += 8) {
@@ -445,7 +427,26 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int q = 0; q < 4; ++q) sacc[wave][q][16 * vb + n] = accv[vb][q];
   }
   __syncthreads();
-  float* out = a.part + ((int64_t(b) * a.Hkv + g) * a.nsplit + split) * (G * (2 + D));
+  if (a.nsplit > 1) {
+    float* out = a.part + ((int64_t(b) * a.Hkv + g) * a.nsplit + split) * (G * (2 + D));
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+      const int gg = e / D, i = e % D;
+      float M = -INFINITY;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
+      float accs = 0.f, l = 0.f;
+      for (int w = 0; w < 4; ++w) {
+        const float f = sm_m[w][gg] == -INFINITY ? 0.f : __expf(sm_m[w][gg] - M);
+        accs += f * sacc[w][gg][i];
+        l += f * sm_l[w][gg];
+      }
+      out[2 * G + gg * D + i] = accs;
+      if (i == 0) { out[gg] = M; out[G + gg] = l; }
+    }
+    return;
+  }
+  // one split per sequence: normalise and rotate back here,
+  // out_i = sum_k Pi_v[k][i] y_k with y = acc / l (the query set-up arrays
+  // are free again and hold y and the second half's sums)
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int gg = e / D, i = e % D;
     float M = -INFINITY;
@@ -456,8 +457,36 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       accs += f * sacc[w][gg][i];
       l += f * sm_l[w][gg];
     }
-    out[2 * G + gg * D + i] = accs;
-    if (i == 0) { out[gg] = M; out[G + gg] = l; }
+    sqr[gg][i] = l > 0.f ? accs / l : 0.f;
+  }
+  __syncthreads();
+  {
+    const int i = threadIdx.x & (D - 1), half = threadIdx.x >> 7;
+    const int hv = vc.heads > 1 ? g : 0;
+    const float* rot = vc.rot + size_t(hv) * D * D + size_t(64 * half) * D + i;
+    float o[G];
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) o[gg] = 0.f;
+#pragma unroll
+    for (int k0 = 0; k0 < 64; k0 += 16) {
+      float r[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) r[u] = rot[size_t(k0 + u) * D];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) o[gg] = fmaf(r[u], sqr[gg][64 * half + k0 + u], o[gg]);
+    }
+    if (half == 1) {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) sqs[gg][i] = o[gg];
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg)
+        a.out[(int64_t(b) * a.Hq + g * G + gg) * D + i] = o[gg] + sqs[gg][i];
+    }
   }
 }
 

@@ -58,6 +58,10 @@ struct DeviceTables {
   float* cen = nullptr;          // [H][d][kMaxLevels] centroids
   int16_t* bitpos = nullptr;     // [kMaxBits][d] bit position in the ROW bit string, -1 if absent
   uint8_t* dim_bits = nullptr;   // [d]
+  // non-uniform d = 128 codecs: decode tables of the one-bit dims and the
+  // tail byte (built once here instead of in every decode workgroup)
+  uint32_t* sq_tail = nullptr;   // [256] tail byte -> index bits 1.. of dims 0..3, 5 bits per dim
+  float* sq_gm = nullptr;        // [H][2][d] (c1 - c0) / 2 and (c1 + c0) / 2 per dim
 };
 
 }  // namespace tq

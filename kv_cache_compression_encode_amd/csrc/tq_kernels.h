@@ -28,6 +28,8 @@ struct CodecView {
   const float* cen;
   const int16_t* bitpos;
   const uint8_t* dim_bits;
+  const uint32_t* sq_tail;  // non-uniform d = 128: tail byte -> packed index bits of dims 0..3
+  const float* sq_gm;       // non-uniform d = 128: [H][2][d] half-difference and mean of levels 0, 1
   float uthr[kMaxLevels];
   float ucen[kMaxLevels];
 };

@@ -614,6 +614,8 @@ hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeA
   hipError_t e;
   if (decode_mfma_supported(kv, vv, G)) {
     e = launch_decode_mfma(kv, vv, a, s);
+    // a single split is normalised and rotated back inside the MFMA kernel
+    if (e != hipSuccess || a.nsplit == 1) return e;
   } else {
     switch (G) {
       case 1: hipLaunchKernelGGL(decode_partial_kernel<1>, grid, dim3(256), 0, s, kv, vv, a); break;
