@@ -125,8 +125,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
   __shared__ float skc[SQ ? 4 : 1][kMaxLevels];  // SQ: levels of dims 0..3
-  // value byte (two 4-bit codes) -> fp16 pair of their levels
-  __shared__ uint32_t slut[256];
+  // value byte (two 4-bit codes) -> fp16 pair of their levels, 32 copies:
+  // entry e for lane l at slut[e * 32 + l % 32], so that the random lookups
+  // of a wave hit 32 distinct banks
+  __shared__ uint32_t slut1[256];
+  __shared__ uint32_t slut[256 * 32];
   constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
   __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   {
     const int t = threadIdx.x;  // 256 threads: one value-table entry each
-    slut[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+    slut1[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
   }
   for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
   if (SQ) {
@@ -210,6 +213,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     }
   }
   __syncthreads();
+#pragma unroll 8
+  for (int k = 0; k < 32; ++k) {  // consecutive threads write consecutive words
+    const int e = k * 256 + threadIdx.x;
+    slut[e] = slut1[e >> 5];
+  }
   if (SQ) {
     for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
       const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
@@ -269,6 +277,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __syncthreads();
 
   const float coef_scale = kQjl / float(kc.m);
+  // SQ: the query whose table part this lane forms (see the score step)
+  const int q_own = ((g16 & 1) << 1) | (g16 >> 1);
+  const float* slow_own = &slow[SQ ? q_own : 0][0][0];
+  const float smu_own = SQ ? smu[q_own] : 0.f;
+  float sqs_own[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sqs_own[i] = SQ ? sqs[q_own][i] : 0.f;
 
   // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
@@ -306,6 +321,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       nv[nb] = h2f(uint16_t(__shfl(int(R.nv), 16 * nb + n, 64)));
       sqb[nb] = SQ ? uint32_t(__shfl(int(spack), 16 * nb + n, 64)) : 0u;
     }
+    // value B fragments: table lookups issued before the score step
+    u32x4 Bv[8][2];
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const uint32_t w = vw[vb][kc2];
+        const uint32_t* lut = slut + (lane & 31);
+        Bv[vb][kc2][0] = lut[(w & 0xffu) << 5];
+        Bv[vb][kc2][1] = lut[((w >> 8) & 0xffu) << 5];
+        Bv[vb][kc2][2] = lut[((w >> 16) & 0xffu) << 5];
+        Bv[vb][kc2][3] = lut[(w >> 24) << 5];
+      }
     // ---- scores
     float lg[4][2];
     u32x4 A[NP][4];
@@ -323,38 +351,34 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         acc = mfma16(A[p][2], expand_pm1<2>(kw[nb][p]), acc);
         acc = mfma16(A[p][3], expand_pm1<3>(kw[nb][p]), acc);
       }
-      float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
-      float sa, sb;
-      if (SQ) {
-        // dims 0..3 from the table, the mu part, and the 4 signs
-        const uint32_t w = sqb[nb];
-        const uint32_t tl = stail[(w >> 8) & 0xffu];
-        int idx[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) idx[i] = int(((w >> i) & 1u) | ((tl >> (5 * i)) & 31u));
-        const int q0 = (2 * g16) & 3, q1 = q0 + 1;
-        float ea = smu[q0], eb = smu[q1];
-        sa = 0.f;
-        sb = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ea += slow[q0][i][idx[i]];
-          eb += slow[q1][i][idx[i]];
-          const float sg = (w >> (16 + i)) & 1u ? 1.f : -1.f;
-          sa = fmaf(sg, sqs[q0][i], sa);
-          sb = fmaf(sg, sqs[q1][i], sb);
-        }
-        xa += ea;
-        xb += eb;
-      } else {
-        sa = xor32(xa, lane);
-        sb = xor32(xb, lane);
-      }
+      const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
       const int tok = tile * kTile + 16 * nb + n;
       const bool valid = tok < len;
       const float coef = nr[nb] * coef_scale;
-      lg[nb][0] = valid ? a.scale * nx[nb] * (xa + coef * sa) : -INFINITY;
-      lg[nb][1] = valid ? a.scale * nx[nb] * (xb + coef * sb) : -INFINITY;
+      float ta, tb;  // score parts beyond the MFMA rows of queries qa = 2 (g16 & 1), qb = qa + 1
+      if (SQ) {
+        // dims 0..3 from the table, the mu part and the 4 signs, for one query
+        // per lane (q_own), the partner query's part from the lane 32 away:
+        // lanes (n, 0) / (n, 2) take queries 0 / 1, lanes (n, 1) / (n, 3) 2 / 3
+        const uint32_t w = sqb[nb];
+        const uint32_t tl = stail[(w >> 8) & 0xffu];
+        float e = smu_own;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t idx = ((w >> i) & 1u) | ((tl >> (5 * i)) & 31u);
+          e += slow_own[i * kMaxLevels + idx];
+          const float sg = (w >> (16 + i)) & 1u ? sqs_own[i] : -sqs_own[i];
+          e = fmaf(coef, sg, e);
+        }
+        ta = e;
+        tb = xor32(e, lane);
+        if (g16 >= 2) { const float t = ta; ta = tb; tb = t; }
+      } else {
+        ta = coef * xor32(xa, lane);
+        tb = coef * xor32(xb, lane);
+      }
+      lg[nb][0] = valid ? a.scale * nx[nb] * (xa + ta) : -INFINITY;
+      lg[nb][1] = valid ? a.scale * nx[nb] * (xb + tb) : -INFINITY;
     }
     // ---- online softmax (lanes of group 0: queries 0,1; group 1: queries 2,3)
     float alpha[2];
@@ -392,13 +416,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       accv[vb][3] *= al3;
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const uint32_t w = vw[vb][kc2];
-        u32x4 B;
-        B[0] = slut[w & 0xffu];
-        B[1] = slut[(w >> 8) & 0xffu];
-        B[2] = slut[(w >> 16) & 0xffu];
-        B[3] = slut[w >> 24];
-        accv[vb] = mfma16(Ap[kc2], B, accv[vb]);
+        accv[vb] = mfma16(Ap[kc2], Bv[vb][kc2], accv[vb]);
       }
     }
     __builtin_amdgcn_wave_barrier();

@@ -211,6 +211,39 @@ __device__ __forceinline__ float quant_bits(float v, f32x16v T, const float* L, 
   }
 }
 
+// The uniform codebooks are Lloyd-Max solutions for a symmetric law, so
+// their boundaries are symmetric about 0 (T[L/2 - 1] = 0, T[L/2 - 1 + k] =
+// -T[L/2 - 1 - k]) and so are their levels.  The quantizers below use this:
+// the sign of v picks the half and |v| is searched among the L/2 - 1 positive
+// boundaries only.  Decisions equal those of the full search except when
+// v < 0 lies exactly on a boundary (a tie, which then goes to the lower cell).
+
+// Transpose of an 8 x 8 matrix of nibbles held by 8 consecutive lanes (lane
+// t of the group holds row t, element c at bits 4c..4c+3): on return lane t
+// holds column t.  Three exchange stages with the lanes 4, 2 and 1 away swap
+// blocks of 4, 2 and 1 nibbles; the per-lane selectors come from
+// nib_transpose_consts.
+struct NibT {
+  uint32_t selA, selB, rotC, mskC;
+};
+__device__ __forceinline__ NibT nib_transpose_consts(int t) {
+  NibT c;
+  c.selA = (t & 4) ? 0x03020706u : 0x05040100u;  // own bytes 0,1 + partner's 0,1 / partner's 2,3 + own 2,3
+  c.selB = (t & 2) ? 0x03070105u : 0x06020400u;  // interleave bytes with the partner's
+  c.rotC = (t & 1) ? 4u : 28u;                    // partner's nibbles to the other half of each byte
+  c.mskC = (t & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;   // nibbles kept from the own word
+  return c;
+}
+__device__ __forceinline__ uint32_t nib_transpose8(uint32_t w, const NibT& c) {
+  uint32_t x = uint32_t(__builtin_amdgcn_ds_swizzle(int(w), 0x101F));  // lane ^ 4 (bitmask mode, xor 4)
+  w = __builtin_amdgcn_perm(x, w, c.selA);
+  x = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]: lane ^ 2
+  w = __builtin_amdgcn_perm(x, w, c.selB);
+  x = uint32_t(__builtin_amdgcn_mov_dpp(int(w), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]: lane ^ 1
+  x = __builtin_amdgcn_alignbit(x, x, c.rotC);
+  return (w & c.mskC) | (x & ~c.mskC);
+}
+
 // w = 2 w + [b]: one v_addc with the comparison's lane mask as the carry in
 // (the mask is the same SGPR pair the selects of the quantizer use).  Bits
 // pushed for registers r = 15 .. 0 land at bit r.
@@ -221,6 +254,49 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t w, bool b) {
   asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(cout) : "v"(w), "s"(m));
   (void)cout;
   return r;
+}
+
+// w = 2 w + (bit of this lane in the lane mask m), one v_addc.
+__device__ __forceinline__ uint32_t push_mask(uint32_t w, uint64_t m) {
+  uint32_t r;
+  uint64_t cout;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(cout) : "v"(w), "s"(m));
+  (void)cout;
+  return r;
+}
+
+// 16 levels: P[k] = T[8 + k] (k < 7) scaled like v.  Appends the 4-bit
+// index of v to w (w = 16 w + idx): for v >= 0 the index is 8 + m and for
+// v < 0 it is 7 - m, m = number of P[k] <= |v|, so bit 3 is [v >= 0] and
+// bits 2..0 are those of m, inverted when v < 0 (lane masks combined on the
+// scalar unit).
+__device__ __forceinline__ uint32_t quant4_sym_push(uint32_t w, float v, const float (&P)[7]) {
+  const float a = fabsf(v);
+  const uint64_t pos = __ballot(v >= 0.f);
+  const bool b2 = a >= P[3];
+  const uint64_t m2 = __ballot(b2);
+  const bool b1 = a >= (b2 ? P[5] : P[1]);
+  const uint64_t m1 = __ballot(b1);
+  const float tu = b1 ? P[6] : P[4], tl = b1 ? P[2] : P[0];
+  const uint64_t m0 = __ballot(a >= (b2 ? tu : tl));
+  w = push_mask(w, pos);
+  w = push_mask(w, ~(pos ^ m2));
+  w = push_mask(w, ~(pos ^ m1));
+  return push_mask(w, ~(pos ^ m0));
+}
+
+// 4 levels: P = T[2] scaled like v, L2 / L3 levels 2 / 3 (levels 0 / 1 are
+// their negatives).  Appends index bit 1 ([v >= 0]) to w1 and index bit 0
+// ([v >= 0] == [|v| >= P]) to w0; returns the selected level.
+__device__ __forceinline__ float quant2_sym_push(float v, float P, float L2, float L3, uint32_t& w0,
+                                                 uint32_t& w1) {
+  const bool pos = v >= 0.f;
+  const bool m = fabsf(v) >= P;
+  const uint64_t mp = __ballot(pos), mm = __ballot(m);
+  w1 = push_mask(w1, mp);
+  w0 = push_mask(w0, ~(mp ^ mm));
+  const float c = m ? L3 : L2;
+  return pos ? c : -c;
 }
 
 // OR across groups of `VPD` consecutive lanes (8 or 16) with DPP moves:
@@ -272,6 +348,10 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   constexpr int NSUB = 2 / NB;            // sub-tiles of 32*NB vectors per tile
   constexpr int NPL = UNIFORM ? UB : 1;   // planes held in the word arrays
   constexpr int LV = 1 << (UNIFORM ? UB : 1);
+  // symmetric search paths: 16-level col codes (values), 4-level row codes
+  constexpr bool SYM4 = UNIFORM && COL && UB == 4 && MODE == 0;
+  constexpr bool SYM2 = UNIFORM && !COL && UB == 2;
+  const NibT nibc = nib_transpose_consts(int(threadIdx.x & 7));
 
   const int nwaves = blockDim.x >> 6;
   const int64_t tstep = int64_t(gridDim.x) * nwaves;
@@ -375,6 +455,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // boundaries scaled to the accumulator (uniform codec); prod: the
       // residual is formed directly in unit scale times 32, rsd = v rs - 32 c
       f32x16v T[NB];
+      float P4[NB][7];
       float rs[NB];
       float C32[LV];
       if (UNIFORM) {
@@ -382,6 +463,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * wsc[nb];
+          if (SYM4)
+#pragma unroll
+            for (int k = 0; k < 7; ++k) P4[nb][k] = cv.uthr[8 + k] * wsc[nb];
           rs[nb] = 32.f / wsc[nb];
         }
 #pragma unroll
@@ -419,11 +503,20 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         f32x16 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+        // the Pi fragments are read from LDS two steps ahead of the MFMAs
+        // that take them, so that the LDS latency overlaps the chain
+        u32x4 fh[3], fl[3];
+        auto read_pi = [&](int c) {
+          const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
+          fh[c % 3] = *reinterpret_cast<const u32x4*>(sPiHi + off);
+          fl[c % 3] = *reinterpret_cast<const u32x4*>(sPiLo + off);
+        };
+        read_pi(0);
+        read_pi(1);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
-          const u32x4 ah = *reinterpret_cast<const u32x4*>(sPiHi + off);
-          const u32x4 al = *reinterpret_cast<const u32x4*>(sPiLo + off);
+          if (c + 2 < 8) read_pi(c + 2);
+          const u32x4 ah = fh[c % 3], al = fl[c % 3];
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
@@ -433,6 +526,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         }
         // ------------------------------------------------ quantize block
         uint32_t colkeep[NB][2];
+        uint32_t pk[NB][2];  // SYM4: nibbles of registers 8k .. 8k + 7 (register 8k + c at bits 4c)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -443,10 +537,16 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             float chat = 0.f;
             if (UNIFORM && !COL) {
               // row layout: the index bits go straight into the plane words
-              bool bits[4] = {false, false, false, false};
-              chat = quant_bits<UB>(v, T[nb], C32, bits);
+              if constexpr (SYM2) {
+                chat = quant2_sym_push(v, T[nb][2], C32[2], C32[3], cw[nb][0], cw[nb][NPL - 1]);
+              } else {
+                bool bits[4] = {false, false, false, false};
+                chat = quant_bits<UB>(v, T[nb], C32, bits);
 #pragma unroll
-              for (int p = 0; p < NPL; ++p) cw[nb][p] = push_bit(cw[nb][p], bits[p]);
+                for (int p = 0; p < NPL; ++p) cw[nb][p] = push_bit(cw[nb][p], bits[p]);
+              }
+            } else if (SYM4) {
+              pk[nb][r >> 3] = quant4_sym_push((r & 7) == 7 ? 0u : pk[nb][r >> 3], v, P4[nb]);
             } else if (UNIFORM) {
               idx = quant_tree<UB>(v, T[nb]);
               if (MODE != 0) {
@@ -480,6 +580,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                   if (pos >= 0) tailw[nb] |= uint32_t((idx >> p) & 1) << (pos - D);
                 }
               }
+            } else if (SYM4) {
+              // packed and transposed after the block
             } else if (UB == 1) {
               // col layout, 1 bit: ballot over lanes = vectors; lanes 0..31
               // carry dim 32mb + r, lanes 32..63 dim 32mb + 16 + r
@@ -520,7 +622,21 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
             }
           }
-          if (COL && UB > 1) {
+          if (SYM4) {
+            // lane j holds the nibbles of registers 8k .. 8k + 7 of vector j;
+            // after the 8-lane transposes lane j holds register
+            // r = 8k + (j % 8) of vectors 8 (j / 8) .. 8 (j / 8) + 7, which is
+            // the col dword of dim 32mb + 16hh + r for those vectors
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const uint32_t w = nib_transpose8(valid[nb] ? pk[nb][k] : 0u, nibc);
+              const int r = 8 * k + (j & 7);
+              const int dim = 32 * mb + 16 * hh + r;
+              const int word = (sub * NB * 32 + nb * 32 + j) / 8;
+              *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 32 + 4 * word) = w;
+            }
+          }
+          if (COL && UB > 1 && !SYM4) {
             // lane j holds, for r = k*VPD + (j % VPD), the dword of dim
             // 32mb + 16hh + r covering vectors (j / VPD)*VPD ..
             constexpr int VPD = 32 / UB;
