@@ -33,6 +33,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int LDS_ROW = D + 8;  // bf16 elements per staged row (16-byte pad)
@@ -392,28 +393,67 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         if (BF16IN) {
           // raw bf16 pairs (prefetched) stay packed until the scale is known
           const u32x4* r = cur[nb];
+          {
+            float s0 = 0.f, s1 = 0.f;  // two chains; fp32 FMAs (exact squares)
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
-              ss = fmaf(lo, lo, fmaf(hi, hi, ss));
-              mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
-            }
+              for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
+                s0 = fmaf(lo, lo, s0);
+                s1 = fmaf(hi, hi, s1);
+              }
+            ss = s0 + s1;
+          }
           ss += xor32f(ss);
-          mx = fmaxf(mx, xor32f(mx));
-          const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
-          const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
-          // x * 2^e is exact in fp16 (8 significant bits, exponent in range)
+          // scale 2^s, s = 14 - floor(log2 ||x||): every |x_i| 2^s < 2^15.
+          // x_i 2^s in fp16 is then formed from the bf16 bits directly: the
+          // exponent field drops by D = 112 - s (saturating at 0, which
+          // flushes elements below 2^-14 of the scaled range, i.e. under
+          // 2^-28 ||x||), the 7 mantissa bits move up by 3, the sign stays.
+          // Norms whose floor(log2) is below -98, and non-finite ones, take
+          // the general path below (float scaling by the largest element).
+          const int es = int((__float_as_uint(ss) >> 23) & 0xff);  // biased exponent of ||x||^2
+          const int en = (es - 127) >> 1;                            // floor(log2 ||x||) (normal ss)
+          const bool fast = ss == 0.f || (es > 0 && es < 255 && en >= -98);
+          if (__builtin_expect(__ballot(!fast) == 0, 1)) {
+            const int dsh = ss == 0.f ? 98 : 98 + en;  // D
+            const uint32_t dd = uint32_t(dsh) << 7;
+            const u16x2 sub2 = {uint16_t(dd), uint16_t(dd)};
 #pragma unroll
-          for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float lo = __uint_as_float(r[c][i] << 16) * p2;
-              const float hi = __uint_as_float(r[c][i] & 0xffff0000u) * p2;
-              xh[nb][c][i] = f16b(lo) | (f16b(hi) << 16);
-            }
-          wsc[nb] = 16.f * p2;
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t w = r[c][i];
+                u16x2 e = __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+                e = __builtin_elementwise_sub_sat(e, sub2);
+                e = e << u16x2{3, 3};
+                xh[nb][c][i] = (w & 0x80008000u) | __builtin_bit_cast(uint32_t, e);
+              }
+            const float p2 = ss == 0.f ? 1.f : __uint_as_float(uint32_t(141 - en) << 23);
+            wsc[nb] = 16.f * p2;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
+                mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+              }
+            mx = fmaxf(mx, xor32f(mx));
+            const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+            const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+            // x * 2^e is exact in fp16 (8 significant bits, exponent in range)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(r[c][i] << 16) * p2;
+                const float hi = __uint_as_float(r[c][i] & 0xffff0000u) * p2;
+                xh[nb][c][i] = f16b(lo) | (f16b(hi) << 16);
+              }
+            wsc[nb] = 16.f * p2;
+          }
         } else {
           const int64_t tc = valid[nb] ? t : a.tokens - 1;  // unconditional load, see load_raw
           const float* row = reinterpret_cast<const float*>(xbase) + tc * a.xs_t + 64 * hh;
