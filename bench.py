@@ -42,7 +42,7 @@ DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decod
 # plain 1 GiB device copy (factors 2.0 and 1.0); the summary and the commands
 # are in profiles/.  Valid for the kernels as built when the counters were
 # taken; a call missing here reports null.
-TRAFFIC = {"encode_keys": 82040198}
+TRAFFIC = {"encode_keys": 82135912}
 
 
 def parse():
@@ -365,7 +365,7 @@ def run_sq(args, torch, tq, synth):
                               "values mse b=4 col; step = one fused decode token per sequence",
                   "caches_cycled": ncache},
                  "f32", hbm_roof("decode_attend", t["decode_attend"], nbytes,
-                                 "one library call: query prep + split-K attention + combine"),
+                                 "one library call: query prep, then the fused score + softmax + P V kernel (one split per sequence at this batch: the merge and the inverse value rotation run inside it)"),
                  {"decode_attend": {"ms": t["decode_attend"], "bytes": nbytes}},
                  {"record_bytes_per_token_head": (kper + vper) / TT})
     return res, cpu_baseline_sq
