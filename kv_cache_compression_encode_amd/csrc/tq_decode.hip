@@ -9,8 +9,9 @@
 // is one contraction over K = [plane 0 | plane 1 | signs] (3 x 128) of +-1
 // values with the weighted query: a single chain of 16x16x32 f16 MFMAs per 16
 // keys.  Rows 0..7 carry the code part of 4 queries (fp16 hi and lo parts of
-// w_p q'), rows 8..15 the sign part (hi and lo of qs); the +-1 operands are
-// built from the key bits with one shift and one and-or per fp16 pair.
+// w_p q'), rows 8..15 the sign part (hi and lo of qs); each +-1 operand (8
+// fp16 values for 8 key bits) is one 16-byte read of a 256-entry LDS table
+// indexed by the key byte.
 //
 // SpectralQuant keys (UB = 0): dims 4..127 carry one bit each, so their part
 // of <q', c(idx)> is linear in plane 0 (c_i(b) = mu_i + gamma_i s) and runs
@@ -52,27 +53,6 @@ __device__ __forceinline__ float f16v(uint32_t h) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h)));
 }
 __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_cast(_Float16, h)); }
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Byte c of w -> 8 fp16 values +1 (bit set) / -1 (bit clear), element k from
-// bit k: the byte is copied into both 16-bit halves (one byte permute), each
-// pair of elements takes one packed 16-bit shift (bit 2j to bit 15 of the low
-// half, bit 2j+1 to bit 15 of the high half) and one and-xor with the fp16
-// pattern of -1.
-template <int C>
-__device__ __forceinline__ u32x4 expand_pm1(uint32_t w) {
-  // selector: bytes 0 and 2 <- byte C of w, bytes 1 and 3 <- 0
-  const uint32_t pair = __builtin_amdgcn_perm(0u, w, 0x0C000C00u | (C << 16) | C);
-  const u16x2 pv = __builtin_bit_cast(u16x2, pair);
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u16x2 sh = pv << u16x2{(unsigned short)(15 - 2 * j), (unsigned short)(14 - 2 * j)};
-    r[j] = (__builtin_bit_cast(uint32_t, sh) & 0x80008000u) ^ 0xBC00BC00u;
-  }
-  return r;
-}
 
 // Reductions over the 16 lanes of a row with DPP row rotations (no LDS
 // round trips), and exchanges with the lane 32 (or 16) positions away with
@@ -247,6 +227,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // LDS (fragment f by wave f % 4) and read them back per tile (keeping them
   // live across the tile loop would exceed the register budget)
   __shared__ u32x4 sA[NP * 4][64];
+  // byte -> 8 fp16 +-1 values (element k from bit k): the B operands of the
+  // score chain are read from this table instead of being expanded on the VALU
+  __shared__ u32x4 spm[256];
+  {
+    const uint32_t e = threadIdx.x;
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r[j] = (((e >> (2 * j)) & 1u) ? 0x3C00u : 0xBC00u) | ((((e >> (2 * j + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+    spm[e] = r;
+  }
   for (int f = wave; f < NP * 4; f += 4) {
     const int p = f / 4, c = f % 4;
     const bool sign_part = p == NP - 1;
@@ -346,10 +337,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        acc = mfma16(A[p][0], expand_pm1<0>(kw[nb][p]), acc);
-        acc = mfma16(A[p][1], expand_pm1<1>(kw[nb][p]), acc);
-        acc = mfma16(A[p][2], expand_pm1<2>(kw[nb][p]), acc);
-        acc = mfma16(A[p][3], expand_pm1<3>(kw[nb][p]), acc);
+        acc = mfma16(A[p][0], spm[kw[nb][p] & 0xffu], acc);
+        acc = mfma16(A[p][1], spm[(kw[nb][p] >> 8) & 0xffu], acc);
+        acc = mfma16(A[p][2], spm[(kw[nb][p] >> 16) & 0xffu], acc);
+        acc = mfma16(A[p][3], spm[kw[nb][p] >> 24], acc);
       }
       const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
       const int tok = tile * kTile + 16 * nb + n;
