@@ -557,12 +557,18 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   float* qs = qr + nqt * d;
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                          ((size_t(nqt) * (d + m) * 4 + 255) & ~size_t(255)));
-  QueryPrepArgs qa{q, q_dtype == TQ_BF16, nqt, G, Hkv, 0, qr, qs};
-  tq_status st = map_hip(launch_query_prep(kc, qa, s));
-  if (st != TQ_OK) return st;
+  // the MFMA decode rotates its queries itself; the general path reads them
+  // prepared
+  if (!decode_mfma_supported(kc, vc, G)) {
+    QueryPrepArgs qa{q, q_dtype == TQ_BF16, nqt, G, Hkv, 0, qr, qs};
+    const tq_status st = map_hip(launch_query_prep(kc, qa, s));
+    if (st != TQ_OK) return st;
+  }
   DecodeArgs da{};
   da.qr = qr;
   da.qs = qs;
+  da.q = q;
+  da.q_bf16 = q_dtype == TQ_BF16;
   da.B = B;
   da.Hq = Hq;
   da.Hkv = Hkv;

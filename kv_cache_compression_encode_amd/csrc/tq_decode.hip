@@ -168,14 +168,32 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // the first tile's loads go out before the set-up below and overlap it
   if (t_begin + wave < t_end) load_tile(t_begin + wave, ra);
 
-  // ---- set-up: one round of independent loads, then LDS-only arithmetic
-  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+  // ---- set-up: one round of independent loads, then arithmetic on LDS.
+  // The G queries are rotated here, q' = Pi_h q and qs = S q'[0:m]: thread t
+  // forms coordinate t % 128 over half t / 128 of each sum, reading the
+  // transposed matrices column-coalesced (all their loads go out first).
+  const int hk = kc.heads > 1 ? g : 0;
+  const int ci = threadIdx.x & (D - 1), kh = threadIdx.x >> 7;
+  float rcol[D / 2], scol[SQ ? 1 : D / 2];
+  {
+    const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(kh * (D / 2)) * D + ci;
+#pragma unroll
+    for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+    if (!SQ) {
+      const float* st = kc.sketch_t + size_t(kh * (D / 2)) * D + ci;
+#pragma unroll
+      for (int u = 0; u < D / 2; ++u) scol[u] = st[size_t(u) * D];
+    }
+  }
+  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {  // raw queries, staged in sqs
     const int gg = e / D, i = e % D;
     const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
-    sqr[gg][i] = gg < G ? a.qr[qi * D + i] : 0.f;
-    sqs[gg][i] = gg < G && i < kc.m ? a.qs[qi * kc.m + i] : 0.f;
+    float v = 0.f;
+    if (gg < G)
+      v = a.q_bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * D + i]) << 16)
+                   : static_cast<const float*>(a.q)[qi * D + i];
+    sqs[gg][i] = v;
   }
-  const int hk = kc.heads > 1 ? g : 0;
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   {
     const int t = threadIdx.x;  // 256 threads: one value-table entry each
@@ -193,6 +211,48 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     }
   }
   __syncthreads();
+  {
+    // q' = Pi q: half sums into the (still unused) merge buffer, then added
+    float* part = &sacc[0][0][0];  // [2][4][D]
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int u = 0; u < D / 2; u += 2) {
+        s0 = fmaf(rcol[u], sqs[gg][kh * (D / 2) + u], s0);
+        s1 = fmaf(rcol[u + 1], sqs[gg][kh * (D / 2) + u + 1], s1);
+      }
+      part[(kh * 4 + gg) * D + ci] = s0 + s1;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqr[e / D][e % D] = part[e] + part[4 * D + e];
+    __syncthreads();
+    if (!SQ) {
+      // qs = S q' (m = d)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < D / 2; u += 2) {
+          s0 = fmaf(scol[u], sqr[gg][kh * (D / 2) + u], s0);
+          s1 = fmaf(scol[u + 1], sqr[gg][kh * (D / 2) + u + 1], s1);
+        }
+        part[(kh * 4 + gg) * D + ci] = s0 + s1;
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqs[e / D][e % D] = part[e] + part[4 * D + e];
+    } else {
+      // qs = S q'[0:m], m <= 4 (entries past m are zero)
+      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+        const int gg = e / D, j = e % D;
+        float acc = 0.f;
+        if (j < kc.m)
+          for (int k = 0; k < kc.m; ++k) acc = fmaf(kc.sketch[j * kc.m + k], sqr[gg][k], acc);
+        sqs[gg][j] = acc;
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll 8
   for (int k = 0; k < 32; ++k) {  // consecutive threads write consecutive words
     const int e = k * 256 + threadIdx.x;

@@ -64,8 +64,10 @@ hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, i
                         const uint8_t* rec, int64_t n, float* scores, hipStream_t s);
 
 struct DecodeArgs {
-  const float* qr;     // [B][Hq][d]
+  const float* qr;     // [B][Hq][d]   (prepared queries; the MFMA kernel forms its own)
   const float* qs;     // [B][Hq][mk]
+  const void* q;       // [B][Hq][d] raw queries (fp32 or bf16), read by the MFMA kernel
+  int q_bf16;
   int B, Hq, Hkv;
   const uint8_t* krec;
   const uint8_t* vrec;
