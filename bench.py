@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--workload", default="gqa_layer",
                    choices=["gqa_layer", "small", "bulk_prefill", "sq_decode", "vector_search"])
     p.add_argument("--bits", type=int, default=2, help="vector_search: TurboQuant-prod bits (2 or 4)")
+    p.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
+                   help="gqa_layer / bulk_prefill: dense seeded Haar Pi (default) or the randomized "
+                        "Hadamard rotation mode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device copy (counter calibration)")
@@ -98,8 +101,8 @@ def cpu_baseline_gqa():
     k = synth.kv_cache(1, 1, n, D, 201, law)[0, 0].double().numpy()
     v = synth.kv_cache(1, 1, n, D, 251, law)[0, 0].double().numpy()
     q = synth.kv_queries(1, 4, 1, D, 202, law)[0].double().numpy()
-    kc = o.turboquant_codec(D, 3, "prod", rot_seed=203, sketch_seed=204)
-    vc = o.turboquant_codec(D, 4, "mse", rot_seed=203, layout="col")
+    kc = o.turboquant_codec(D, 3, "prod", rot_seed=203, sketch_seed=204, rotation=ROTATION)
+    vc = o.turboquant_codec(D, 4, "mse", rot_seed=203, layout="col", rotation=ROTATION)
 
     def run():
         ke, ve = o.encode(kc, k), o.encode(vc, v)
@@ -130,8 +133,8 @@ def cpu_baseline_bulk():
     law = synth.KVLaw(1, D, 305)
     k = synth.kv_cache(1, 1, n, D, 301, law)[0, 0].double().numpy()
     v = synth.kv_cache(1, 1, n, D, 306, law)[0, 0].double().numpy()
-    kc = o.turboquant_codec(D, 3, "prod", rot_seed=303, sketch_seed=304)
-    vc = o.turboquant_codec(D, 4, "mse", rot_seed=303, layout="col")
+    kc = o.turboquant_codec(D, 3, "prod", rot_seed=303, sketch_seed=304, rotation=ROTATION)
+    vc = o.turboquant_codec(D, 4, "mse", rot_seed=303, layout="col", rotation=ROTATION)
 
     def run():
         o.pack(kc, o.encode(kc, k))
@@ -225,10 +228,24 @@ def result(args, metric, value, unit, ms_step, workload, dtype, roof, breakdown,
     return res
 
 
+ROTATION = "haar"  # set from --rotation
+
+
+def rot_kw(tq):
+    return {"rotation": tq.TQ_ROT_HADAMARD} if ROTATION == "hadamard" else {}
+
+
+def rot_note(s):
+    return s + ("; randomized Hadamard rotation (register Walsh-Hadamard transform in the encode)"
+                if ROTATION == "hadamard" else "")
+
+
 def hbm_roof(name, ms, nbytes, note=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # the counters were taken for the dense-Pi kernels
+    traffic = TRAFFIC.get(name) if isinstance(TRAFFIC, dict) and ROTATION == "haar" else None
     r = {"bound": "hbm", "kernel": name, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-         "frac": gbs / HBM_PEAK_GBS, "traffic": TRAFFIC.get(name) if isinstance(TRAFFIC, dict) else None,
+         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
          "bytes_per_launch": nbytes, "avg_launch_ms": ms}
     if note:
         r["note"] = note
@@ -242,8 +259,8 @@ def run_gqa_layer(args, torch, tq, synth):
     K = [synth.kv_cache(1, HKV, T, D, 201 + 1000 * l, law, device=dev)[0] for l in range(NLAYERS)]
     V = [synth.kv_cache(1, HKV, T, D, 251 + 1000 * l, law, device=dev)[0] for l in range(NLAYERS)]
     q = synth.kv_queries(1, HQ, HKV, D, 202, law, device=dev)
-    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204)
-    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL)
+    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204, **rot_kw(tq))
+    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
     assert kcb.tile_bytes == 64 * K_REC and vcb.tile_bytes == 64 * V_REC
     krec = [torch.empty(HKV * kcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
     vrec = [torch.empty(HKV * vcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
@@ -264,9 +281,9 @@ def run_gqa_layer(args, torch, tq, synth):
               "hbm_frac": nbytes[k] / (t[k] * 1e-3) / 1e9 / HBM_PEAK_GBS} for k in t}
     res = result(args, "compressed-key scoring keys/s & KV encode GB/s at d=128, % of HBM roofline",
                  nk / (ms_step * 1e-3), "keys/s", ms_step,
-                 {"workload": "gqa_decode_layer: 32 q / 8 kv heads, d=128, 32768 tokens, batch 1, "
-                              "bf16 K/V; K TurboQuant-prod b=3 (row records), V TurboQuant-mse b=4 "
-                              "(col records); step = encode K + encode V + decode attention",
+                 {"workload": rot_note("gqa_decode_layer: 32 q / 8 kv heads, d=128, 32768 tokens, batch 1, "
+                                       "bf16 K/V; K TurboQuant-prod b=3 (row records), V TurboQuant-mse b=4 "
+                                       "(col records); step = encode K + encode V + decode attention"),
                   "layers_cycled": NLAYERS},
                  "f32 (split-f16 MFMA)", hbm_roof(dom, t[dom], nbytes[dom]), bd,
                  {"decode_keys_per_s": nk / (t["decode_attend"] * 1e-3),
@@ -305,8 +322,8 @@ def run_bulk(args, torch, tq, synth):
     law = synth.KVLaw(H, D, 305)
     K = synth.kv_cache(L, H, TT, D, 301, law, device=dev)
     V = synth.kv_cache(L, H, TT, D, 306, law, device=dev)
-    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=303, seed_sketch=304)
-    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=303, layout=tq.TQ_LAYOUT_COL)
+    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=303, seed_sketch=304, **rot_kw(tq))
+    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=303, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
     krec = torch.empty(L * H * kcb.records_bytes(TT), dtype=torch.uint8, device=dev)
     vrec = torch.empty(L * H * vcb.records_bytes(TT), dtype=torch.uint8, device=dev)
 
@@ -320,8 +337,8 @@ def run_bulk(args, torch, tq, synth):
               "hbm_frac": nbytes[k] / (t[k] * 1e-3) / 1e9 / HBM_PEAK_GBS} for k in t}
     gbs = (nbytes["encode_keys"] + nbytes["encode_values"]) / (ms_step * 1e-3) / 1e9
     res = result(args, "KV encode GB/s at d=128 (bulk prefill), % of HBM roofline", gbs, "GB/s", ms_step,
-                 {"workload": "bulk_prefill: 32 layers x 8 kv heads x 131072 tokens x d=128 bf16 K and V; "
-                              "K prod b=3 row, V mse b=4 col; step = encode all K and V"},
+                 {"workload": rot_note("bulk_prefill: 32 layers x 8 kv heads x 131072 tokens x d=128 bf16 K "
+                                       "and V; K prod b=3 row, V mse b=4 col; step = encode all K and V")},
                  "f32 (split-f16 MFMA)", hbm_roof(dom, t[dom], nbytes[dom]), bd,
                  {"token_heads_per_s": nk / (ms_step * 1e-3),
                   "compression_ratio": (2 * D * 2) / (K_REC + V_REC)})
@@ -411,12 +428,17 @@ DEFAULT_STEPS = {"gqa_layer": (50, 5), "small": (200, 10), "bulk_prefill": (10, 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding of this path is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
+              "no multi-GPU figure", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
         return
+    global ROTATION
+    ROTATION = args.rotation
+    if ROTATION != "haar" and args.workload not in ("gqa_layer", "bulk_prefill"):
+        print("--rotation applies to the gqa_layer and bulk_prefill workloads", file=sys.stderr)
+        sys.exit(2)
     st, wu = DEFAULT_STEPS[args.workload]
     args.steps = st if args.steps is None else args.steps
     args.warmup = wu if args.warmup is None else args.warmup

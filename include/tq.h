@@ -70,7 +70,7 @@ typedef enum {
 
 enum { TQ_MSE = 0, TQ_PROD = 1 };                 /* [TQ] "Method"                  */
 enum { TQ_F32 = 0, TQ_BF16 = 1 };                 /* element types of x and q       */
-enum { TQ_ROT_HAAR = 0, TQ_ROT_GIVEN = 1, TQ_ROT_CALIBRATE = 2 };
+enum { TQ_ROT_HAAR = 0, TQ_ROT_GIVEN = 1, TQ_ROT_CALIBRATE = 2, TQ_ROT_HADAMARD = 3 };
 enum { TQ_LAYOUT_ROW = 0, TQ_LAYOUT_COL = 1 };
 
 #define TQ_TILE 64          /* vectors per record tile                         */
@@ -103,12 +103,20 @@ typedef struct tq_codebook tq_codebook;
  *              codebook = Gaussian Lloyd-Max with b_i levels scaled by sigma_i,
  *              the RMS of rotated coordinate i of the normalised calibration
  *              vectors.
+ *              TQ_ROT_HADAMARD: randomized Hadamard rotation ([LK]: the
+ *              reference cache's O(d log d) mode; the launch post's summary
+ *              "random Hadamard rotation"): Pi = H diag(s) / sqrt(d) with H the
+ *              Sylvester Walsh-Hadamard matrix (H[i][j] = (-1)^popcount(i & j))
+ *              and s_j = +1 / -1 from bit 0 of word j of the Philox stream 3
+ *              of seed_rotation; d must be a power of two; Beta-law codebooks
+ *              as for TQ_ROT_HAAR.  The d = 128 encode applies it as a fast
+ *              Walsh-Hadamard transform; every other call uses Pi itself.
  *   num_heads  rotations held by the codebook (one per KV head for
  *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN); TQ_ROT_HAAR uses 1.
  *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map;
  *              the GPU encode writes COL records for 1, 2 or 4 index bits).
- *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1) and S
- *              (stream 2).
+ *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1; the
+ *              Hadamard signs use stream 3) and S (stream 2).
  *   device     HIP device ordinal that holds the codebook's tables.
  */
 typedef struct {

@@ -15,11 +15,11 @@ import torch
 
 from . import _lib as L
 from ._lib import (TQ_BF16, TQ_F32, TQ_LAYOUT_COL, TQ_LAYOUT_ROW, TQ_MSE, TQ_PROD,
-                   TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_TILE, TQError)
+                   TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_TILE, TQError)
 
 __all__ = ["Codebook", "encode", "score", "decode_attend", "search_topk", "TQError",
            "TQ_MSE", "TQ_PROD", "TQ_LAYOUT_ROW", "TQ_LAYOUT_COL", "TQ_ROT_HAAR",
-           "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_TILE"]
+           "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_ROT_HADAMARD", "TQ_TILE"]
 
 
 def _stream(device) -> ctypes.c_void_p:

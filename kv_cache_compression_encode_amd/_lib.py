@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libt
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_ENOMEM, TQ_EWORKSPACE, TQ_EDEVICE = range(7)
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16 = 0, 1
-TQ_ROT_HAAR, TQ_ROT_GIVEN, TQ_ROT_CALIBRATE = 0, 1, 2
+TQ_ROT_HAAR, TQ_ROT_GIVEN, TQ_ROT_CALIBRATE, TQ_ROT_HADAMARD = 0, 1, 2, 3
 TQ_LAYOUT_ROW, TQ_LAYOUT_COL = 0, 1
 TQ_OP_SCORE, TQ_OP_DECODE, TQ_OP_TOPK, TQ_OP_ENCODE = 0, 1, 2, 3
 TQ_TILE = 64

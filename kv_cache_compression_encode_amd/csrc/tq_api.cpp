@@ -27,7 +27,7 @@ tq_status upload(T** dst, const T* src, size_t count) {
 void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
   void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
-                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm};
+                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm, t.had_mask};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -86,6 +86,23 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
     philox_normals(ds.seed_rotation, 1, int64_t(d) * d, g.data());
     cb->rot64.resize(size_t(d) * d);
     haar_from_gaussian(d, g.data(), cb->rot64.data());
+  } else if (ds.rotation == TQ_ROT_HADAMARD) {
+    // Pi = H diag(s) / sqrt(d): H Sylvester Walsh-Hadamard, s_j from bit 0 of
+    // word j of the Philox stream 3 (block j / 4, word j % 4)
+    if (d & (d - 1)) return TQ_EUNSUPPORTED;
+    cb->hsign.assign(d, 1);
+    const uint32_t key[2] = {uint32_t(ds.seed_rotation), uint32_t(ds.seed_rotation >> 32)};
+    for (int blk = 0; blk * 4 < d; ++blk) {
+      const uint32_t ctr[4] = {uint32_t(blk), 0u, 3u, 0u};
+      uint32_t w[4];
+      philox4x32_10(ctr, key, w);
+      for (int k = 0; k < 4 && blk * 4 + k < d; ++k) cb->hsign[blk * 4 + k] = (w[k] & 1u) ? -1 : 1;
+    }
+    cb->rot64.resize(size_t(d) * d);
+    const double inv = 1.0 / std::sqrt(double(d));
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        cb->rot64[size_t(i) * d + j] = ((__builtin_popcount(unsigned(i & j)) & 1) ? -inv : inv) * cb->hsign[j];
   } else if (ds.rotation == TQ_ROT_GIVEN) {
     if (!ds.given) return TQ_EINVAL;
     heads = std::max(1, ds.num_heads);
@@ -242,6 +259,15 @@ tq_status build_device(tq_codebook* cb) {
   if ((st = upload(&cb->dev.cen, cb->cen32.data(), cb->cen32.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.bitpos, cb->bitpos.data(), cb->bitpos.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.dim_bits, cb->bits.data(), size_t(d))) != TQ_OK) return st;
+  if (!cb->hsign.empty() && d == 128) {
+    std::vector<uint32_t> mask(64, 0u);
+    for (int hh = 0; hh < 2; ++hh)
+      for (int k = 0; k < 32; ++k) {
+        const int i0 = 64 * hh + 2 * k;
+        mask[hh * 32 + k] = (cb->hsign[i0] < 0 ? 0x8000u : 0u) | (cb->hsign[i0 + 1] < 0 ? 0x80000000u : 0u);
+      }
+    if ((st = upload(&cb->dev.had_mask, mask.data(), mask.size())) != TQ_OK) return st;
+  }
   if (!cb->uniform && d == 128) {
     // tail byte t -> bits 1.. of the indices of dims 0..3 (dim i at bits 5i..5i+4),
     // for the bit positions D..D+7 of the row bit string
@@ -337,6 +363,7 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.dim_bits = cb->dev.dim_bits;
   v.sq_tail = cb->dev.sq_tail;
   v.sq_gm = cb->dev.sq_gm;
+  v.had_mask = cb->dev.had_mask;
   for (int k = 0; k < kMaxLevels; ++k) {
     v.uthr[k] = cb->thr32[k];
     v.ucen[k] = cb->cen32[k];
@@ -368,7 +395,7 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
   if (ds.mode == TQ_PROD && !ds.bitmap && ds.bits < 2) return TQ_EINVAL;
   if (ds.layout != TQ_LAYOUT_ROW && ds.layout != TQ_LAYOUT_COL) return TQ_EINVAL;
   if (ds.qjl_dims < 0 || ds.num_heads < 0) return TQ_EINVAL;
-  if (ds.rotation == TQ_ROT_HAAR && ds.num_heads > 1) return TQ_EINVAL;
+  if ((ds.rotation == TQ_ROT_HAAR || ds.rotation == TQ_ROT_HADAMARD) && ds.num_heads > 1) return TQ_EINVAL;
   tq_codebook* cb = new (std::nothrow) tq_codebook();
   if (!cb) return TQ_ENOMEM;
   cb->desc = ds;

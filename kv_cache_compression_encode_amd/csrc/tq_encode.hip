@@ -836,6 +836,260 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   }
 }
 
+// ---------------------------------------------------------------------------
+// Randomized Hadamard rotation (Pi = H diag(s) / sqrt(d)), bf16 input, uniform
+// codebooks.  The rotation is a fast Walsh-Hadamard transform in registers
+// instead of the two MFMA passes of a dense Pi; the QJL sketch stays on MFMA.
+//
+// Lane (j, hh) holds input dims 64 hh .. 64 hh + 63 of vector j.  After the
+// sign flips (XOR of the bf16 sign bits) and six in-lane butterfly stages,
+// element t holds u_t of its half; the last stage pairs the two halves: a
+// permlane32 swap of registers t and t + 32 leaves, in lane half hh,
+// P_t = y_{32 hh + t} and M_t = y_{64 + 32 hh + t} (t < 32, y = H s x
+// unnormalised).  So each lane owns two whole 32-dim blocks (mb = hh and
+// mb = 2 + hh): its ROW words need no cross-half merge, and for the sketch
+// the K order (chunk c, half hh, element i) -> dim of register 8c + i is
+// matched by permuting the columns of S when it is staged.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int had_dim(int hh, int k) {  // dim held in register k (0..63) of half hh
+  return k < 32 ? 32 * hh + k : 64 + 32 * hh + (k - 32);
+}
+
+// Stage S (fp16 [128][128]) with rows placed by lds_row_of and LDS column
+// 16c + 8h + i holding S column had_dim(h, 8c + i).
+__device__ void stage_sketch_had(uint16_t* lds, const uint16_t* g) {
+  constexpr int CHUNKS = D * D / 8;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int base = 0; base < CHUNKS; base += 8 * nt) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * nt + tid;
+      if (e < CHUNKS) v[u] = *reinterpret_cast<const u32x4*>(g + e * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = base + u * nt + tid;
+      if (e >= CHUNKS) continue;
+      const int row = e / (D / 8), col = (e % (D / 8)) * 8;  // 8 consecutive S columns
+      // col = had_dim(h, 8c): dims 0..31 -> h 0, c 0..3; 32..63 -> h 1, c 0..3;
+      // 64..95 -> h 0, c 4..7; 96..127 -> h 1, c 4..7
+      const int h = (col >> 5) & 1, c = (col & 31) / 8 + 4 * (col >> 6);
+      *reinterpret_cast<u32x4*>(lds + lds_row_of(row) * LDS_ROW + 16 * c + 8 * h) = v[u];
+    }
+  }
+}
+
+template <int MODE, bool COL, int UB>
+__global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, EncodeArgs a) {
+  // MODE 0: mse (COL with 4 index bits, or ROW); MODE 1: prod with the full
+  // 128-dim sketch (ROW)
+  static_assert(MODE == 0 || !COL, "prod records are ROW");
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* sMask = reinterpret_cast<uint32_t*>(smem);           // [2][32] sign-bit masks
+  uint16_t* sSk = reinterpret_cast<uint16_t*>(smem + 256);        // MODE 1: staged S
+  const int64_t bh = blockIdx.y;
+  const int64_t b = bh / a.heads, h = bh % a.heads;
+  if (threadIdx.x < 64) sMask[threadIdx.x] = cv.had_mask[threadIdx.x];
+  if (MODE == 1) stage_sketch_had(sSk, cv.sk_hi);
+  __syncthreads();
+
+  const int lane = lane_id();
+  const int j = lane & 31, hh = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int64_t ntiles = (a.tokens + kTile - 1) / kTile;
+  const uint8_t* xbase = static_cast<const uint8_t*>(a.x) + (b * a.xs_b + h * a.xs_h) * 2;
+  uint8_t* rbase = a.rec + b * a.rs_b + h * a.rs_h;
+  constexpr int LV = 1 << UB;
+  constexpr bool SYM4 = COL && UB == 4;
+  constexpr bool SYM2 = !COL && UB == 2;
+  static_assert(!COL || SYM4, "col records: 4 index bits");
+  const NibT nibc = nib_transpose_consts(int(threadIdx.x & 7));
+  const float kSqrtD = 11.313708498984761f;  // sqrt(128): y = FWHT / sqrt(d)
+
+  const int nwaves = blockDim.x >> 6;
+  const int64_t tstep = int64_t(gridDim.x) * nwaves;
+  u32x4 bufA[8], bufB[8];
+  auto load_raw = [&](int64_t tl, int sb, u32x4 (&dst)[8]) {
+    const int64_t t = tl * kTile + sb * 32 + j;
+    const int64_t tc = (tl < ntiles && t < a.tokens) ? t : a.tokens - 1;
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(xbase) + tc * a.xs_t + 64 * hh;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dst[c] = *reinterpret_cast<const u32x4*>(row + 8 * c);
+  };
+  auto process = [&](const u32x4 (&cur)[8], int64_t tile, int sub) {
+    uint8_t* trec = rbase + tile * cv.tile_bytes;
+    const int slot = sub * 32 + j;
+    const bool valid = tile * kTile + slot < a.tokens;
+    // ------------------------------------------------ signs, norm, unpack
+    float v[64];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 m = *reinterpret_cast<const u32x4*>(sMask + 32 * hh + 4 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = cur[c][i] ^ m[i];
+        const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+        v[8 * c + 2 * i] = lo;
+        v[8 * c + 2 * i + 1] = hi;
+        s0 = fmaf(lo, lo, s0);
+        s1 = fmaf(hi, hi, s1);
+      }
+    }
+    float ss = s0 + s1;
+    ss += xor32f(ss);
+    const float nxv = sqrtf(ss);
+    const float sx = nxv > 0.f ? nxv : 1.f;  // a zero vector encodes y = 0
+    const float wsc = kSqrtD * sx;           // accumulator = wsc * (unit-vector coordinate)
+    // ------------------------------------------------ Walsh-Hadamard
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1)
+#pragma unroll
+      for (int t = 0; t < 64; ++t)
+        if (!(t & st)) {
+          const float p = v[t], q = v[t + st];
+          v[t] = p + q;
+          v[t + st] = p - q;
+        }
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[t]), __float_as_uint(v[t + 32]), false, false);
+      const float A = __uint_as_float(sw[0]), B = __uint_as_float(sw[1]);
+      v[t] = A + B;       // P_t: dim 32 hh + t
+      v[t + 32] = A - B;  // M_t: dim 64 + 32 hh + t
+    }
+    // ------------------------------------------------ quantize
+    f32x16v T = {};
+#pragma unroll
+    for (int k = 0; k < LV - 1; ++k) T[k] = cv.uthr[k] * wsc;
+    float P4[7];
+    if (SYM4)
+#pragma unroll
+      for (int k = 0; k < 7; ++k) P4[k] = cv.uthr[8 + k] * wsc;
+    float C32[LV];
+#pragma unroll
+    for (int k = 0; k < LV; ++k) C32[k] = 32.f * cv.ucen[k];
+    const float rs = 32.f / wsc;
+    float rr = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {  // dims 32 mb .. 32 mb + 31, mb = hh + 2 blk
+      const int mb = hh + 2 * blk;
+      if constexpr (COL) {
+        // nibbles of 8 consecutive dims per word, then the 8-lane transpose
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int i = 7; i >= 0; --i) w = quant4_sym_push(w, v[32 * blk + 8 * g + i], P4);
+          w = nib_transpose8(valid ? w : 0u, nibc);
+          const int dim = 32 * mb + 8 * g + (j & 7);
+          *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 32 + 4 * (slot / 8)) = w;
+        }
+      } else {
+        uint32_t cw[UB];
+#pragma unroll
+        for (int p = 0; p < UB; ++p) cw[p] = 0;
+#pragma unroll
+        for (int r = 31; r >= 0; --r) {  // descending: dim 32 mb + r lands at bit r
+          const float val = v[32 * blk + r];
+          float chat;
+          if constexpr (SYM2) {
+            chat = quant2_sym_push(val, T[2], C32[2], C32[3], cw[0], cw[1]);
+          } else {
+            bool bits[4] = {false, false, false, false};
+            chat = quant_bits<UB>(val, T, C32, bits);
+#pragma unroll
+            for (int p = 0; p < UB; ++p) cw[p] = push_bit(cw[p], bits[p]);
+          }
+          if (MODE == 1) {
+            const float rsd = fmaf(val, rs, -chat);  // 32 (y - c) in unit scale
+            rr = fmaf(rsd, rsd, rr);
+            v[32 * blk + r] = rsd;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < UB; ++p)
+          *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = valid ? cw[p] : 0u;
+      }
+    }
+    // ------------------------------------------------ sketch and signs
+    if constexpr (MODE == 1) {
+      f32x16 z[4];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4 rh, rl;
+        split8h(&v[8 * c], rh, rl);
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) {
+          const u32x4 sh = *reinterpret_cast<const u32x4*>(sSk + (32 * ms + j) * LDS_ROW + 16 * c + 8 * hh);
+          z[ms] = mfma32h(sh, rh, c == 0 ? f32x16{} : z[ms]);
+          z[ms] = mfma32h(sh, rl, z[ms]);
+        }
+      }
+      rr += xor32f(rr);
+      uint32_t sw[4];
+      // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        sw[ms] = 0;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) sw[ms] = push_bit(sw[ms], z[ms][r] >= 0.f);
+        const uint32_t mine = valid ? sw[ms] << (16 * hh) : 0u;
+        sw[ms] = mine | xor32(mine);
+      }
+      uint8_t* dst = trec + cv.off_signs + slot * 16 + 8 * hh;
+      *reinterpret_cast<u32x2*>(dst) = hh ? u32x2{sw[2], sw[3]} : u32x2{sw[0], sw[1]};
+    }
+    // ------------------------------------------------ norms (both halves store the same)
+    *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(valid ? nxv : 0.f);
+    if (MODE == 1)
+      *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) =
+          f16_bits(valid ? sqrtf(rr) * (1.f / 32.f) : 0.f);
+  };
+  int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
+  int sub = 0;
+  auto next_pos = [&](int64_t& tl, int& sb) {
+    if (sb + 1 < 2) { ++sb; } else { sb = 0; tl += tstep; }
+  };
+  load_raw(tile, 0, bufA);
+  while (tile < ntiles) {
+    int64_t t1 = tile;
+    int s1 = sub;
+    next_pos(t1, s1);
+    load_raw(t1, s1, bufB);
+    process(bufA, tile, sub);
+    tile = t1;
+    sub = s1;
+    if (tile >= ntiles) break;
+    next_pos(t1, s1);
+    load_raw(t1, s1, bufA);
+    process(bufB, tile, sub);
+    tile = t1;
+    sub = s1;
+  }
+}
+
+template <int MODE, bool COL, int UB>
+hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
+  auto kern = encode_had_kernel<MODE, COL, UB>;
+  const size_t lds = 256 + (MODE == 1 ? size_t(D) * LDS_ROW * 2 : 0);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (a.tokens + kTile - 1) / kTile;
+  const int64_t sets = a.batch * a.heads;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  int64_t gx = (ntiles + 7) / 8;
+  const int64_t want = std::max<int64_t>(1, (int64_t(cus) + sets - 1) / sets);
+  gx = std::max<int64_t>(1, std::min(gx, want));
+  hipLaunchKernelGGL(kern, dim3(unsigned(gx), unsigned(sets), 1u), dim3(512), lds, s, cv, a);
+  return hipGetLastError();
+}
+
 template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
 hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB>;
@@ -864,6 +1118,12 @@ hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
 
 hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   const bool col = cv.layout == TQ_LAYOUT_COL;
+  if (cv.had_mask && cv.uniform && a.x_bf16) {
+    // randomized Hadamard rotation: the register transform for the GQA K/V
+    // codecs; any other combination uses the dense Pi below
+    if (cv.mode == TQ_MSE && col && cv.ubits == 4) return launch_had<0, true, 4>(cv, a, s);
+    if (cv.mode == TQ_PROD && !col && cv.m == D && cv.ubits == 2) return launch_had<1, false, 2>(cv, a, s);
+  }
   if (!cv.uniform) {
     // SpectralQuant keys: row layout, small sketch
     if (col || cv.mode != TQ_PROD || cv.m > 4 || !a.x_bf16) return hipErrorNotSupported;

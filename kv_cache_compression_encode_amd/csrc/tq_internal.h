@@ -62,6 +62,9 @@ struct DeviceTables {
   // tail byte (built once here instead of in every decode workgroup)
   uint32_t* sq_tail = nullptr;   // [256] tail byte -> index bits 1.. of dims 0..3, 5 bits per dim
   float* sq_gm = nullptr;        // [H][2][d] (c1 - c0) / 2 and (c1 + c0) / 2 per dim
+  // randomized Hadamard rotation at d = 128: per half h of the input (dims
+  // 64h .. 64h + 63) and packed bf16 pair k, the sign bits (15 and 31) to flip
+  uint32_t* had_mask = nullptr;  // [2][32]
 };
 
 }  // namespace tq
@@ -80,5 +83,6 @@ struct tq_codebook {
   std::vector<double> cen64, thr64;          // [H][d][kMaxLevels], [H][d][kMaxLevels-1]
   std::vector<float> cen32, thr32;           // [H][d][kMaxLevels]
   std::vector<int16_t> bitpos;               // [kMaxBits][d]
+  std::vector<int8_t> hsign;                 // TQ_ROT_HADAMARD: the signs s [d]
   tq::DeviceTables dev;
 };

@@ -30,6 +30,7 @@ struct CodecView {
   const uint8_t* dim_bits;
   const uint32_t* sq_tail;  // non-uniform d = 128: tail byte -> packed index bits of dims 0..3
   const float* sq_gm;       // non-uniform d = 128: [H][2][d] half-difference and mean of levels 0, 1
+  const uint32_t* had_mask; // randomized Hadamard, d = 128: [2][32] XOR masks of the bf16 sign bits
   float uthr[kMaxLevels];
   float ucen[kMaxLevels];
 };

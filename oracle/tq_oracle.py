@@ -12,6 +12,8 @@ What it computes, step by step, and where the pages define it:
 * Random rotation Pi (seeded Haar orthogonal, QR of a Gaussian matrix) and the
   Gaussian sketch S -- TurboQuant paper review, "Method"; the launch kit names
   the dense-QR rotation mode (OnlyTerp/turboquant LAUNCH.md, Show HN post).
+  Its other mode, a randomized Hadamard rotation H diag(s) / sqrt(d) (same
+  launch post: the O(d log d) mode, "random Hadamard rotation").
 * Lloyd-Max scalar codebook for the post-rotation coordinate law (a Beta law,
   about N(0, 1/d)) -- paper review, "Method" and the summary under the title.
 * TurboQuant-mse: store ||x||, rotate x/||x||, quantize every coordinate to the
@@ -29,8 +31,10 @@ What it computes, step by step, and where the pages define it:
   cache) and top-k search -- paper review, "Background", "Validation" and the
   "Sparks" list (rotation and codebook lookup fused into attention).
 
-Readings where the pages are silent (each also listed in the design doc):
-the generator of Pi and S (Philox4x32-10 + Box-Muller, below); S stored in
+Readings where the pages are silent (each listed with the design notes):
+the generator of Pi and S (Philox4x32-10 + Box-Muller, below); the Hadamard
+mode's construction (one sign layer s, then Sylvester H, scaled by 1/sqrt(d);
+s from bit 0 of the sign stream's words); S stored in
 fp16 (the draws rounded to fp32, then fp16); fp16 norms;
 ties go to the upper cell; sign(0) = +1; the sketch acts on the rotated
 residual, so the query sketch is S (Pi q); the record layout of the library.
@@ -83,6 +87,7 @@ def philox4x32_10(counter, key):
 
 STREAM_ROTATION = 1
 STREAM_SKETCH = 2
+STREAM_SIGNS = 3
 
 
 def philox_normals(seed: int, stream: int, count: int) -> np.ndarray:
@@ -120,6 +125,38 @@ def haar_rotation(d: int, seed: int) -> np.ndarray:
     g = philox_normals(seed, STREAM_ROTATION, d * d).reshape(d, d)
     q, r = np.linalg.qr(g)
     return q * np.sign(np.diag(r))[None, :]
+
+
+def rademacher_signs(d: int, seed: int) -> np.ndarray:
+    """d signs +1 / -1 from the sign stream: sign j is +1 when bit 0 of word j
+    (block j div 4, word j mod 4) is 0 and -1 when it is 1."""
+    nblk = (d + 3) // 4
+    i = np.arange(nblk, dtype=np.uint64)
+    ctr = np.stack([i & _MASK32, i >> np.uint64(32),
+                    np.full(nblk, STREAM_SIGNS, np.uint64), np.zeros(nblk, np.uint64)], axis=-1)
+    key = np.array([seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF], dtype=np.uint64)
+    w = philox4x32_10(ctr, key).reshape(-1)[:d]
+    return np.where((w & np.uint64(1)) == 0, 1.0, -1.0)
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """Walsh-Hadamard matrix of order d (a power of two) by Sylvester's
+    doubling, H_2n = [[H_n, H_n], [H_n, -H_n]] from H_1 = [1]; entry (i, j)
+    is (-1)^popcount(i & j)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("the Walsh-Hadamard order must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_rotation(d: int, seed: int) -> np.ndarray:
+    """Randomized Hadamard rotation Pi = H diag(s) / sqrt(d) (fp64): the
+    reference cache's O(d log d) rotation mode (OnlyTerp/turboquant launch
+    post, repository layout; the summary's "random Hadamard rotation"), with
+    seeded Rademacher signs s.  Orthogonal because H H^T = d I."""
+    return sylvester_hadamard(d) * rademacher_signs(d, seed)[None, :] / math.sqrt(d)
 
 
 def gaussian_sketch(m: int, seed: int) -> np.ndarray:
@@ -291,14 +328,20 @@ def _f32(a):
 
 
 def turboquant_codec(d: int, bits: int, mode: str, rot_seed: int, sketch_seed: int = 0,
-                     layout: str = "row") -> Codec:
+                     layout: str = "row", rotation: str = "haar") -> Codec:
     """TurboQuant-mse (bits per coordinate) or TurboQuant-prod (bits-1 mse bits +
-    1 QJL bit, sketch over all d rotated dims); paper review, "Method"."""
+    1 QJL bit, sketch over all d rotated dims); paper review, "Method".
+    rotation: "haar" (dense seeded Haar) or "hadamard" (randomized Hadamard)."""
     mse_bits = bits - 1 if mode == "prod" else bits
     if mse_bits < 1:
         raise ValueError("prod needs bits >= 2 here (at least one mse bit)")
     lm = beta_codebook(d, mse_bits)
-    rot = _f32(haar_rotation(d, rot_seed))[None]
+    if rotation == "haar":
+        rot = _f32(haar_rotation(d, rot_seed))[None]
+    elif rotation == "hadamard":
+        rot = _f32(hadamard_rotation(d, rot_seed))[None]
+    else:
+        raise ValueError(rotation)
     m = d if mode == "prod" else 0
     sk = stored_sketch(m, sketch_seed) if mode == "prod" else None
     c, t = _f32(lm.centroids), _f32(lm.boundaries)

@@ -45,6 +45,16 @@ def test_rotation_and_sketch_match_oracle(d):
     assert mx <= 1 and n <= 2
 
 
+@pytest.mark.parametrize("d,seed", [(8, 5), (128, 203), (1024, 9)])
+def test_hadamard_rotation_matches_oracle(d, seed):
+    cb = tq.Codebook(d, tq.TQ_PROD, 3, rotation=tq.TQ_ROT_HADAMARD, seed_rotation=seed, seed_sketch=4,
+                     device=-1)
+    rot = cb.export()[0]
+    assert np.array_equal(rot, o.hadamard_rotation(d, seed).astype(np.float32))
+    with pytest.raises(tq.TQError):
+        tq.Codebook(96, tq.TQ_MSE, 2, rotation=tq.TQ_ROT_HADAMARD, device=-1)
+
+
 def test_rotation_matches_oracle_d1536():
     cb = tq.Codebook(1536, tq.TQ_MSE, 2, seed_rotation=503, device=-1)
     rot = cb.export()[0]

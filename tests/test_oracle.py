@@ -62,6 +62,51 @@ def test_haar_entries_and_rotated_coordinate_law():
     assert stats.kstest(np.concatenate(coords), cdf).pvalue > 1e-3
 
 
+def test_sylvester_hadamard_closed_form():
+    # order 4 written out (Sylvester's construction), and H H^T = d I with
+    # entry (i, j) = (-1)^popcount(i & j) at every order up to 256
+    h4 = np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], float)
+    assert np.array_equal(o.sylvester_hadamard(4), h4)
+    for d in (1, 2, 8, 64, 256):
+        h = o.sylvester_hadamard(d)
+        assert np.array_equal(h @ h.T, d * np.eye(d))
+        i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+        par = np.vectorize(lambda v: bin(v).count("1") & 1)(i & j)
+        assert np.array_equal(h, np.where(par == 1, -1.0, 1.0))
+    with pytest.raises(ValueError):
+        o.sylvester_hadamard(96)
+
+
+def test_hadamard_rotation_orthogonal_and_sign_averaged_law():
+    d = 128
+    p = o.hadamard_rotation(d, 7)
+    assert np.max(np.abs(p @ p.T - np.eye(d))) < 1e-13
+    assert np.allclose(np.abs(p), 1 / math.sqrt(d))
+    # the signs act on the input: for a fixed x, averaging over the signs
+    # gives E[y_i^2] = ||x||^2 / d for every i (a sign layer on the output
+    # instead would leave y_i^2 = (H x)_i^2 / d, far from flat for this x)
+    x = np.zeros(d)
+    x[0], x[1], x[9] = 0.6, 0.48, 0.64
+    ys = np.stack([o.hadamard_rotation(d, 500 + s) @ x for s in range(400)])
+    m2 = (ys ** 2).mean(axis=0)
+    assert np.max(np.abs(m2 * d - 1)) < 0.35 and abs(m2.mean() * d - 1) < 1e-12
+    s = o.rademacher_signs(4096, 3)
+    assert set(np.unique(s)) == {-1.0, 1.0} and abs(s.mean()) < 4 / math.sqrt(4096)
+
+
+def test_hadamard_codec_mse_near_codebook():
+    # a randomized Hadamard rotation spreads a generic vector like the Haar
+    # rotation: the empirical distortion stays near the Beta codebook's D
+    d, b = 128, 2
+    codec = o.turboquant_codec(d, b, "mse", rot_seed=11, rotation="hadamard")
+    x = np.random.default_rng(2).normal(size=(20000, d))
+    enc = o.encode(codec, x, round_norms=False)
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    err = np.sum((u - o.reconstruct(codec, enc) / enc.nx[:, None]) ** 2, axis=1)
+    D = codec.extra["lloyd_max"].mse * d
+    assert abs(err.mean() - D) < 0.03 * D
+
+
 # --------------------------------------------------------------- codebooks
 def _density(d):
     z = math.exp(special.betaln(0.5, (d - 1) / 2))
