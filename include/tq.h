@@ -118,6 +118,11 @@ typedef struct tq_codebook tq_codebook;
  *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1; the
  *              Hadamard signs use stream 3) and S (stream 2).
  *   device     HIP device ordinal that holds the codebook's tables.
+ *   waterfill_bits  TQ_ROT_CALIBRATE with bitmap NULL only (0 = off): the
+ *              per-dim index bits are allocated from the calibration spectrum
+ *              by discrete reverse water-filling ([SQ] tweet 6) with
+ *              tq_water_fill: waterfill_bits index bits in total, 1..5 per dim,
+ *              lambda_i = sigma_i^2 averaged over the heads.
  */
 typedef struct {
   int32_t d;
@@ -135,6 +140,7 @@ typedef struct {
   int64_t calib_n;
   int32_t calib_dtype;
   int32_t device;
+  int32_t waterfill_bits;
 } tq_codebook_desc;
 
 /* Sizes of a codec's records. */
@@ -152,6 +158,23 @@ typedef struct {
  * Synchronous.  [TQ] "Method": codebooks are solved once, offline. */
 tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out);
 tq_status tq_codebook_free(tq_codebook* cb);
+
+/* Discrete reverse water-filling of index bits over dimensions with variances
+ * lambda ([SQ] tweet 6: water-filling of the bits over the dominant dims,
+ * after Shannon and Berger).  Host only; no device work.
+ *   lambda      host [d] variances (>= 0) of the rotated coordinates.
+ *   total_bits  index bits to hand out, d*min_bits <= total_bits <= d*max_bits.
+ *   min_bits, max_bits  per-dim range, 1 <= min_bits <= max_bits <= 5.
+ *   bits_out    host [d], written.
+ * Every dim starts at min_bits; then, one bit at a time, the dim with the
+ * largest drop lambda_i (D(b_i) - D(b_i + 1)) of its distortion gets the bit,
+ * D(b) being the mean squared error of the b-bit Lloyd-Max quantizer of the
+ * standard normal law (ties to the lower dim).  D is convex in b, so this
+ * greedy allocation minimises sum_i lambda_i D(b_i) under the budget.
+ * TQ_EINVAL on a null pointer, d < 1, a negative lambda or a budget or range
+ * outside the bounds above. */
+tq_status tq_water_fill(const double* lambda, int32_t d, int32_t total_bits, int32_t min_bits,
+                        int32_t max_bits, uint8_t* bits_out);
 tq_status tq_codebook_get_info(const tq_codebook* cb, tq_codebook_info* info);
 
 /* Copy a codebook's parameters to host memory (any pointer may be NULL):

@@ -17,7 +17,7 @@ from . import _lib as L
 from ._lib import (TQ_BF16, TQ_F32, TQ_LAYOUT_COL, TQ_LAYOUT_ROW, TQ_MSE, TQ_PROD,
                    TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_TILE, TQError)
 
-__all__ = ["Codebook", "encode", "score", "decode_attend", "search_topk", "TQError",
+__all__ = ["Codebook", "encode", "score", "decode_attend", "search_topk", "water_fill", "TQError",
            "TQ_MSE", "TQ_PROD", "TQ_LAYOUT_ROW", "TQ_LAYOUT_COL", "TQ_ROT_HAAR",
            "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_ROT_HADAMARD", "TQ_TILE"]
 
@@ -43,7 +43,7 @@ class Codebook:
                  qjl_dims: int = 0, rotation: int = TQ_ROT_HAAR, num_heads: int = 1,
                  layout: int = TQ_LAYOUT_ROW, seed_rotation: int = 0, seed_sketch: int = 0,
                  given: Optional[np.ndarray] = None, calib: Optional[np.ndarray] = None,
-                 device: int = 0):
+                 device: int = 0, waterfill_bits: int = 0):
         desc = L.CodebookDesc()
         desc.d, desc.mode, desc.bits = d, mode, bits
         keep = []
@@ -72,6 +72,7 @@ class Codebook:
             desc.calib = c.ctypes.data
             desc.calib_n = c.shape[-2]
         desc.device = device
+        desc.waterfill_bits = waterfill_bits
         h = ctypes.c_void_p()
         L.check(L.lib().tq_codebook_build(ctypes.byref(desc), ctypes.byref(h)), "tq_codebook_build")
         self._h = h
@@ -117,6 +118,16 @@ class Codebook:
 
     def alloc_records(self, n: int, sets: int = 1) -> torch.Tensor:
         return torch.zeros(sets * self.records_bytes(n), dtype=torch.uint8, device=f"cuda:{self.device}")
+
+
+def water_fill(lam, total_bits: int, min_bits: int = 1, max_bits: int = 5) -> np.ndarray:
+    """Per-dim index bits by discrete reverse water-filling over variances lam
+    (host call of the library's tq_water_fill)."""
+    lam = np.ascontiguousarray(np.asarray(lam, dtype=np.float64))
+    out = np.zeros(len(lam), dtype=np.uint8)
+    L.check(L.lib().tq_water_fill(lam.ctypes.data, len(lam), total_bits, min_bits, max_bits, out.ctypes.data),
+            "tq_water_fill")
+    return out
 
 
 def encode(cb: Codebook, x: torch.Tensor, records: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -64,7 +64,13 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
   // ---------------------------------------------------------------- bits
   cb->bits.assign(d, 0);
   const int ub = ds.mode == TQ_PROD ? ds.bits - 1 : ds.bits;
-  if (ds.bitmap) {
+  const bool waterfill = ds.waterfill_bits > 0;
+  if (waterfill) {
+    // allocated from the calibration spectrum once the rotation is known
+    if (ds.bitmap || ds.rotation != TQ_ROT_CALIBRATE) return TQ_EINVAL;
+    if (ds.waterfill_bits < d || ds.waterfill_bits > d * kMaxBits) return TQ_EINVAL;
+    std::fill(cb->bits.begin(), cb->bits.end(), uint8_t(1));
+  } else if (ds.bitmap) {
     for (int i = 0; i < d; ++i) {
       if (ds.bitmap[i] < 1 || ds.bitmap[i] > kMaxBits) return TQ_EINVAL;
       cb->bits[i] = ds.bitmap[i];
@@ -152,25 +158,14 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
     for (size_t e = 0; e < s.size(); ++e) cb->sketch32[e] = f16_to_f32(f32_to_f16_rne(float(s[e])));
   }
 
-  // ----------------------------------------------------------- codebooks
-  cb->cen64.assign(size_t(heads) * d * kMaxLevels, 0.0);
-  cb->thr64.assign(size_t(heads) * d * (kMaxLevels - 1), 0.0);
-  cb->cen32.assign(size_t(heads) * d * kMaxLevels, 0.f);
-  cb->thr32.assign(size_t(heads) * d * kMaxLevels, INFINITY);
-  LloydMaxResult books[kMaxBits + 1];
-  bool have[kMaxBits + 1] = {};
-  for (int i = 0; i < d; ++i) {
-    const int b = cb->bits[i];
-    if (!have[b]) {
-      books[b] = ds.rotation == TQ_ROT_CALIBRATE ? lloyd_max_gaussian(b) : lloyd_max_sphere(d, b);
-      have[b] = true;
-    }
-  }
-  for (int h = 0; h < heads; ++h) {
-    std::vector<double> sigma(d, 1.0);
-    if (ds.rotation == TQ_ROT_CALIBRATE) {
-      // sigma_i: RMS of rotated coordinate i of the normalised calibration vectors
-      std::vector<double> acc(d, 0.0), u(d);
+  // ------------------------------------------------ calibration spectrum
+  // sigma_i (per head): RMS of rotated coordinate i of the normalised
+  // calibration vectors
+  std::vector<double> sig(size_t(heads) * d, 1.0);
+  if (ds.rotation == TQ_ROT_CALIBRATE) {
+    std::vector<double> acc(d), u(d);
+    for (int h = 0; h < heads; ++h) {
+      std::fill(acc.begin(), acc.end(), 0.0);
       const float* p = &cb->rot32[size_t(h) * d * d];
       for (int64_t t = 0; t < ds.calib_n; ++t) {
         double nn = 0;
@@ -188,8 +183,36 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
           acc[i] += y * y;
         }
       }
-      for (int i = 0; i < d; ++i) sigma[i] = std::sqrt(acc[i] / double(ds.calib_n));
+      for (int i = 0; i < d; ++i) sig[size_t(h) * d + i] = std::sqrt(acc[i] / double(ds.calib_n));
     }
+  }
+  if (waterfill) {
+    std::vector<double> lam(d, 0.0);
+    for (int h = 0; h < heads; ++h)
+      for (int i = 0; i < d; ++i) lam[i] += sig[size_t(h) * d + i] * sig[size_t(h) * d + i] / heads;
+    if (tq_water_fill(lam.data(), d, ds.waterfill_bits, 1, kMaxBits, cb->bits.data()) != TQ_OK)
+      return TQ_EINVAL;
+    cb->uniform = std::all_of(cb->bits.begin(), cb->bits.end(), [&](uint8_t b) { return b == cb->bits[0]; });
+    cb->ubits = cb->uniform ? cb->bits[0] : 0;
+    if (ds.layout == TQ_LAYOUT_COL && !cb->uniform) return TQ_EUNSUPPORTED;
+  }
+
+  // ----------------------------------------------------------- codebooks
+  cb->cen64.assign(size_t(heads) * d * kMaxLevels, 0.0);
+  cb->thr64.assign(size_t(heads) * d * (kMaxLevels - 1), 0.0);
+  cb->cen32.assign(size_t(heads) * d * kMaxLevels, 0.f);
+  cb->thr32.assign(size_t(heads) * d * kMaxLevels, INFINITY);
+  LloydMaxResult books[kMaxBits + 1];
+  bool have[kMaxBits + 1] = {};
+  for (int i = 0; i < d; ++i) {
+    const int b = cb->bits[i];
+    if (!have[b]) {
+      books[b] = ds.rotation == TQ_ROT_CALIBRATE ? lloyd_max_gaussian(b) : lloyd_max_sphere(d, b);
+      have[b] = true;
+    }
+  }
+  for (int h = 0; h < heads; ++h) {
+    const double* sigma = &sig[size_t(h) * d];
     for (int i = 0; i < d; ++i) {
       const LloydMaxResult& lm = books[cb->bits[i]];
       const int L = 1 << cb->bits[i];
@@ -392,7 +415,7 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
   const tq_codebook_desc& ds = *desc;
   if (ds.d < 2 || ds.d > 4096) return TQ_EINVAL;
   if (ds.mode != TQ_MSE && ds.mode != TQ_PROD) return TQ_EINVAL;
-  if (ds.mode == TQ_PROD && !ds.bitmap && ds.bits < 2) return TQ_EINVAL;
+  if (ds.mode == TQ_PROD && !ds.bitmap && ds.waterfill_bits <= 0 && ds.bits < 2) return TQ_EINVAL;
   if (ds.layout != TQ_LAYOUT_ROW && ds.layout != TQ_LAYOUT_COL) return TQ_EINVAL;
   if (ds.qjl_dims < 0 || ds.num_heads < 0) return TQ_EINVAL;
   if ((ds.rotation == TQ_ROT_HAAR || ds.rotation == TQ_ROT_HADAMARD) && ds.num_heads > 1) return TQ_EINVAL;
@@ -417,6 +440,32 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
     return st;
   }
   *out = cb;
+  return TQ_OK;
+}
+
+tq_status tq_water_fill(const double* lambda, int32_t d, int32_t total_bits, int32_t min_bits,
+                        int32_t max_bits, uint8_t* bits_out) {
+  if (!lambda || !bits_out || d < 1) return TQ_EINVAL;
+  if (min_bits < 1 || max_bits > kMaxBits || min_bits > max_bits) return TQ_EINVAL;
+  if (int64_t(total_bits) < int64_t(d) * min_bits || int64_t(total_bits) > int64_t(d) * max_bits)
+    return TQ_EINVAL;
+  for (int i = 0; i < d; ++i)
+    if (!(lambda[i] >= 0.0)) return TQ_EINVAL;
+  // distortion of the b-bit Gaussian Lloyd-Max quantizer, b = min..max
+  double D[kMaxBits + 1];
+  for (int b = min_bits; b <= max_bits; ++b) D[b] = lloyd_max_gaussian(b).mse;
+  std::vector<int> bits(d, min_bits);
+  for (int64_t left = int64_t(total_bits) - int64_t(d) * min_bits; left > 0; --left) {
+    int best = -1;
+    double gain = -1.0;
+    for (int i = 0; i < d; ++i) {
+      if (bits[i] >= max_bits) continue;
+      const double g = lambda[i] * (D[bits[i]] - D[bits[i] + 1]);
+      if (g > gain) { gain = g; best = i; }  // strict: ties stay with the lower dim
+    }
+    ++bits[best];
+  }
+  for (int i = 0; i < d; ++i) bits_out[i] = uint8_t(bits[i]);
   return TQ_OK;
 }
 

@@ -349,8 +349,32 @@ def turboquant_codec(d: int, bits: int, mode: str, rot_seed: int, sketch_seed: i
                  [[c] * d], [[t] * d], True, {"lloyd_max": lm})
 
 
+def water_fill(lam, total_bits: int, min_bits: int = 1, max_bits: int = 5) -> np.ndarray:
+    """Discrete reverse water-filling of index bits over dims of variance lam
+    (SpectralQuant thread, tweet 6: water-filling, after Shannon and Berger,
+    puts more bits on the dominant dims).  Reading: the distortion of dim i
+    at b bits is lam_i D(b), D the b-bit Gaussian Lloyd-Max error; every dim
+    starts at min_bits and each further bit goes to the dim whose distortion
+    drops the most (ties to the lower dim) until total_bits are spent."""
+    lam = np.asarray(lam, dtype=np.float64)
+    d = len(lam)
+    if not (d * min_bits <= total_bits <= d * max_bits):
+        raise ValueError("budget outside [d min_bits, d max_bits]")
+    D = {b: gaussian_codebook(b).mse for b in range(min_bits, max_bits + 1)}
+    bits = np.full(d, min_bits, dtype=np.int64)
+    for _ in range(total_bits - d * min_bits):
+        best, gain = -1, -1.0
+        for i in range(d):
+            if bits[i] < max_bits:
+                g = lam[i] * (D[bits[i]] - D[bits[i] + 1])
+                if g > gain:
+                    best, gain = i, g
+        bits[best] += 1
+    return bits
+
+
 def spectralquant_codec(calib: np.ndarray, bitmap, m: int, sketch_seed: int,
-                        layout: str = "row") -> Codec:
+                        layout: str = "row", waterfill_bits: int = 0) -> Codec:
     """SpectralQuant keys: per-head eigenbasis rotation, water-filled bit map
     (e.g. [5,3,2,2] on the top-4 dims, 1 bit elsewhere) and QJL on the first m
     rotated dims (SpectralQuant thread, tweets 4, 5, 6).
@@ -358,22 +382,29 @@ def spectralquant_codec(calib: np.ndarray, bitmap, m: int, sketch_seed: int,
     Per-dim codebook: Gaussian Lloyd-Max with b_i bits scaled by sigma_i, the RMS
     of the i-th rotated coordinate of the normalised calibration vectors.
 
-    calib: [H][n][d] calibration keys.
+    calib: [H][n][d] calibration keys.  With bitmap None and waterfill_bits > 0
+    the bit map is water_fill(lambda, waterfill_bits) with lambda_i = sigma_i^2
+    averaged over the heads.
     """
     calib = np.asarray(calib, dtype=np.float64)
     heads, _, d = calib.shape
-    bits = np.asarray(bitmap, dtype=np.int64)
-    books = {b: gaussian_codebook(int(b)) for b in set(bits.tolist())}
-    rots, cents, bnds, sig = [], [], [], []
+    rots, sig = [], []
     for h in range(heads):
         _, rows = eigenbasis(calib[h])
         p = _f32(rows)
         x = calib[h]
         u = x / np.linalg.norm(x, axis=1, keepdims=True)
         y = u @ p.T
-        sigma = np.sqrt(np.mean(y * y, axis=0))
         rots.append(p)
-        sig.append(sigma)
+        sig.append(np.sqrt(np.mean(y * y, axis=0)))
+    if bitmap is None:
+        bits = water_fill(np.mean(np.stack(sig) ** 2, axis=0), waterfill_bits)
+    else:
+        bits = np.asarray(bitmap, dtype=np.int64)
+    books = {b: gaussian_codebook(int(b)) for b in set(bits.tolist())}
+    cents, bnds = [], []
+    for h in range(heads):
+        sigma = sig[h]
         cents.append([_f32(books[int(bits[i])].centroids * sigma[i]) for i in range(d)])
         bnds.append([_f32(books[int(bits[i])].boundaries * sigma[i]) for i in range(d)])
     sk = stored_sketch(m, sketch_seed)

@@ -22,9 +22,10 @@ def fp16_ulps(a, b):
     return np.abs(a - b)
 
 
-def check_encoded(codec, ref, got, band=BAND):
-    """Assert the comparison rules; return counts for reporting."""
-    near = o.boundary_distance(codec, ref.y) < band
+def check_encoded(codec, ref, got, band=BAND, head=0):
+    """Assert the comparison rules; return counts for reporting.  `head`
+    selects the codebook head whose boundaries define the band."""
+    near = o.boundary_distance(codec, ref.y, head) < band
     flips = got.idx != ref.idx
     bad = flips & ~near
     assert not bad.any(), f"{int(bad.sum())} code(s) differ away from any boundary, first at " \

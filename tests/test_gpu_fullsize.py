@@ -88,7 +88,7 @@ def test_sq_decode_full_size_sampled():
             ve[b, g] = o.encode(vc, vx)
             if g in (0, 7):
                 sk = check_encoded(kc, ke[b, g], o.unpack(kc, krec[(b * H + g) * kper:(b * H + g + 1) * kper]
-                                                          .cpu().numpy(), T))
+                                                          .cpu().numpy(), T), head=g)
                 sv = check_encoded(vc, ve[b, g], o.unpack(vc, vrec[(b * H + g) * vper:(b * H + g + 1) * vper]
                                                           .cpu().numpy(), T))
                 say("sq encode", b, g, sk, sv)

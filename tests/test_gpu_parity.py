@@ -188,7 +188,7 @@ def test_encode_spectralquant():
     per = kcb.records_bytes(T)
     for h in range(Hkv):
         ref = o.encode(kc, K[h].double().numpy(), head=h)
-        say("SQ K", check_encoded(kc, ref, o.unpack(kc, buf[h * per:(h + 1) * per], T)))
+        say("SQ K", check_encoded(kc, ref, o.unpack(kc, buf[h * per:(h + 1) * per], T), head=h))
 
 
 # ------------------------------------------------------------------- top-k

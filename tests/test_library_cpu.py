@@ -55,6 +55,33 @@ def test_hadamard_rotation_matches_oracle(d, seed):
         tq.Codebook(96, tq.TQ_MSE, 2, rotation=tq.TQ_ROT_HADAMARD, device=-1)
 
 
+def test_water_fill_matches_oracle():
+    rng = np.random.default_rng(9)
+    for d, total in ((4, 12), (128, 136), (128, 200), (64, 300)):
+        lam = rng.gamma(0.4, size=d)
+        assert np.array_equal(tq.water_fill(lam, total), o.water_fill(lam, total))
+    with pytest.raises(tq.TQError):
+        tq.water_fill([1.0, 2.0], 1)
+    with pytest.raises(tq.TQError):
+        tq.water_fill([1.0, -2.0], 4)
+
+
+def test_water_filled_codebook_matches_oracle():
+    import synth, torch
+    law = synth.KVLaw(2, 128, 405)
+    calib = torch.stack([law.sample(h, 512, torch.Generator().manual_seed(405 + h), "cpu") for h in range(2)])
+    cb = tq.Codebook(128, tq.TQ_PROD, 0, qjl_dims=4, rotation=tq.TQ_ROT_CALIBRATE, num_heads=2,
+                     seed_sketch=404, calib=calib, waterfill_bits=136, device=-1)
+    ref = o.spectralquant_codec(calib.float().numpy().astype(np.float64), None, 4, sketch_seed=404,
+                                waterfill_bits=136)
+    for h in range(2):
+        _, _, cen, thr, lv = cb.export(h)
+        assert np.array_equal(lv, 1 << ref.bits)
+        for i in range(128):
+            L = lv[i]
+            assert np.allclose(cen[i, :L], ref.centroids[h][i], rtol=1e-6, atol=1e-9)
+
+
 def test_rotation_matches_oracle_d1536():
     cb = tq.Codebook(1536, tq.TQ_MSE, 2, seed_rotation=503, device=-1)
     rot = cb.export()[0]

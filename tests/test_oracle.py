@@ -400,6 +400,37 @@ def test_eigenbasis_and_spectrum():
         assert 0.75 < frac < 0.95
 
 
+def test_water_fill_is_optimal_by_brute_force():
+    # the greedy allocation minimises sum lambda_i D(b_i) exactly (D convex):
+    # check against every allocation of small cases
+    import itertools
+    D = {b: o.gaussian_codebook(b).mse for b in range(1, 6)}
+    rng = np.random.default_rng(5)
+    for d, total in ((3, 7), (4, 12), (4, 9), (5, 11)):
+        for _ in range(6):
+            lam = np.sort(rng.gamma(0.7, size=d))[::-1]
+            got = o.water_fill(lam, total)
+            assert got.sum() == total and got.min() >= 1 and got.max() <= 5
+            best = min(sum(lam[i] * D[b[i]] for i in range(d))
+                       for b in itertools.product(range(1, 6), repeat=d) if sum(b) == total)
+            assert sum(lam[i] * D[got[i]] for i in range(d)) <= best * (1 + 1e-12)
+
+
+def test_water_fill_special_cases():
+    # equal variances share the bits evenly (the surplus to the lower dims);
+    # a larger variance never gets fewer bits; the budget bounds are enforced
+    assert np.array_equal(o.water_fill([1.0] * 8, 20), [3, 3, 3, 3, 2, 2, 2, 2])
+    lam = np.array([0.5, 0.1, 0.04, 0.04] + [0.2 / 124] * 124)
+    bits = o.water_fill(lam, 136)
+    assert list(bits[:4]) == [5, 3, 2, 2] and np.all(bits[4:] == 1)  # the [SQ] tweet-6 map
+    r = np.random.default_rng(6).gamma(0.5, size=64)
+    b = o.water_fill(r, 150)
+    order = np.argsort(-r, kind="stable")
+    assert np.all(np.diff(b[order]) <= 0)
+    with pytest.raises(ValueError):
+        o.water_fill([1.0] * 4, 3)
+
+
 def test_selective_qjl_unbiased_on_signal_dims():
     # QJL on the first m=4 rotated dims only (SpectralQuant thread, tweet 5): the
     # sign term estimates <q'_{0..3}, r_{0..3}> without bias over random S.
