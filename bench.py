@@ -185,6 +185,21 @@ def cpu_baseline_search(bits):
 
 
 # ------------------------------------------------------------ timing helpers
+def time_one(torch, fn, steps, warmup):
+    """Average time of `steps` back-to-back calls of fn between one pair of HIP events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def time_calls(torch, calls, steps, warmup):
     """Whole-step time, then each call's average launch time.
 
@@ -273,6 +288,12 @@ def run_gqa_layer(args, torch, tq, synth):
              ("decode_attend", lambda i: tq.decode_attend(kcb, vcb, q, krec[i % NLAYERS], vrec[i % NLAYERS], T,
                                                           HKV, scale, out=out, workspace=ws))]
     ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
+    # append-on-decode, outside the step: the new token of every KV head
+    # encoded into slot T - 1 of the layer's K and V records
+    pos = torch.tensor([T - 1], dtype=torch.int32, device=dev)
+    kn, vn = K[0][:, T - 1].unsqueeze(0), V[0][:, T - 1].unsqueeze(0)
+    append_ms = time_one(torch, lambda: (tq.append(kcb, kn, krec[0], pos, T), tq.append(vcb, vn, vrec[0], pos, T)),
+                         args.steps, args.warmup)
     nk = HKV * T
     nbytes = {"encode_keys": nk * K_ENC_BYTES, "encode_values": nk * V_ENC_BYTES,
               "decode_attend": nk * DEC_BYTES}
@@ -287,6 +308,7 @@ def run_gqa_layer(args, torch, tq, synth):
                   "layers_cycled": NLAYERS},
                  "f32 (split-f16 MFMA)", hbm_roof(dom, t[dom], nbytes[dom]), bd,
                  {"decode_keys_per_s": nk / (t["decode_attend"] * 1e-3),
+                  "append_kv_ms": append_ms,
                   "encode_GBps": (nbytes["encode_keys"] + nbytes["encode_values"]) /
                   ((t["encode_keys"] + t["encode_values"]) * 1e-3) / 1e9})
     return res, cpu_baseline_gqa
@@ -381,6 +403,14 @@ def run_sq(args, torch, tq, synth):
     calls = [("decode_attend", lambda i: tq.decode_attend(kcb, vcb, qs[i % ncache], krec[i % ncache],
                                                           vrec[i % ncache], TT, H, scale, out=out, workspace=ws))]
     ms_step, t = time_calls(torch, calls, args.steps, args.warmup)
+    # append-on-decode, outside the step: one new K and V token per sequence
+    # and KV head into slot TT - 1
+    pos = torch.full((B,), TT - 1, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(409)
+    kn = torch.randn(B, H, D, generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn(B, H, D, generator=gen, device=dev).to(torch.bfloat16)
+    append_ms = time_one(torch, lambda: (tq.append(kcb, kn, krec[0], pos, TT), tq.append(vcb, vn, vrec[0], pos, TT)),
+                         args.steps, args.warmup)
     nk = B * H * TT
     nbytes = nk * (kper + vper) // TT
     res = result(args, "SpectralQuant batched decode token-heads/s, % of HBM roofline",
@@ -395,6 +425,7 @@ def run_sq(args, torch, tq, synth):
                                  "and the inverse value rotation run inside it"),
                  {"decode_attend": {"ms": t["decode_attend"], "bytes": nbytes}},
                  {"record_bytes_per_token_head": (kper + vper) / TT,
+                  "append_kv_ms": append_ms,
                   "calibration_s": calib_s,
                   "calibration": "8 heads x 2048 tokens on the host: covariance, Jacobi eigenbasis, per-dim "
                                  "scales, Lloyd-Max codebooks, device upload",

@@ -173,6 +173,28 @@ tq_status tq_codebook_free(tq_codebook* cb);
  * greedy allocation minimises sum_i lambda_i D(b_i) under the budget.
  * TQ_EINVAL on a null pointer, d < 1, a negative lambda or a budget or range
  * outside the bounds above. */
+/* Append-on-decode (d = 128): encode one new vector per (sequence, head) into
+ * its existing records, at token index positions[b] of sequence b.
+ * TurboQuant also quantizes the tokens generated during decoding (TurboQuant
+ * paper review, "Comparison"); this call writes them in place, so the next
+ * tq_decode_attend (with seq_lens advanced past them) reads them like any
+ * other token.
+ *   x          device [B][H][d] new vectors (fp32 or bf16), last dim
+ *              contiguous, strides xs_b, xs_h in elements; head h is encoded
+ *              with rotation head h of a multi-head codebook.
+ *   records    device; the records of (b, h) start at records + b * rs_b +
+ *              h * rs_h bytes and hold `capacity` tokens (their tile count).
+ *   positions  device int32 [B]; entries outside [0, capacity) are skipped.
+ * Supported: ROW records of any bit map (mse, or prod with m <= d), COL
+ * records of uniform mse codecs with 1, 2 or 4 index bits; TQ_EUNSUPPORTED
+ * otherwise.  Only the new slot's bytes (COL: the new vector's bits in each
+ * dim's field) change.  Calls for the same records must not overlap.
+ * Errors: TQ_EINVAL (null pointer, negative size, bad dtype), TQ_EALIGN
+ * (records or record strides not 4-byte aligned), TQ_EDEVICE (launch). */
+tq_status tq_append(const tq_codebook* cb, const void* x, int32_t x_dtype, int32_t B, int32_t H,
+                    int64_t xs_b, int64_t xs_h, void* records, int64_t rs_b, int64_t rs_h,
+                    const int32_t* positions, int32_t capacity, void* stream);
+
 tq_status tq_water_fill(const double* lambda, int32_t d, int32_t total_bits, int32_t min_bits,
                         int32_t max_bits, uint8_t* bits_out);
 tq_status tq_codebook_get_info(const tq_codebook* cb, tq_codebook_info* info);

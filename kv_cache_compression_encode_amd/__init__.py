@@ -17,7 +17,7 @@ from . import _lib as L
 from ._lib import (TQ_BF16, TQ_F32, TQ_LAYOUT_COL, TQ_LAYOUT_ROW, TQ_MSE, TQ_PROD,
                    TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_TILE, TQError)
 
-__all__ = ["Codebook", "encode", "score", "decode_attend", "search_topk", "water_fill", "TQError",
+__all__ = ["Codebook", "encode", "append", "score", "decode_attend", "search_topk", "water_fill", "TQError",
            "TQ_MSE", "TQ_PROD", "TQ_LAYOUT_ROW", "TQ_LAYOUT_COL", "TQ_ROT_HAAR",
            "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_ROT_HADAMARD", "TQ_TILE"]
 
@@ -118,6 +118,21 @@ class Codebook:
 
     def alloc_records(self, n: int, sets: int = 1) -> torch.Tensor:
         return torch.zeros(sets * self.records_bytes(n), dtype=torch.uint8, device=f"cuda:{self.device}")
+
+
+def append(cb: Codebook, x: torch.Tensor, records: torch.Tensor, positions: torch.Tensor,
+           capacity: int) -> None:
+    """Encode x [B][H][d] (one new vector per sequence and head) into slot
+    positions[b] of the records of (b, h), which hold `capacity` tokens per
+    (b, h) set laid out like encode()'s output of shape [B][H][capacity]."""
+    if x.stride(-1) != 1:
+        x = x.contiguous()
+    B, H, d = x.shape
+    s = x.stride()
+    per = cb.records_bytes(capacity)
+    pos = positions.to(device=x.device, dtype=torch.int32).contiguous()
+    L.check(L.lib().tq_append(cb.handle, x.data_ptr(), _dtype_code(x), B, H, s[0], s[1], records.data_ptr(),
+                              H * per, per, pos.data_ptr(), capacity, _stream(x.device)), "tq_append")
 
 
 def water_fill(lam, total_bits: int, min_bits: int = 1, max_bits: int = 5) -> np.ndarray:

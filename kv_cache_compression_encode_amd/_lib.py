@@ -15,7 +15,7 @@ TQ_OP_SCORE, TQ_OP_DECODE, TQ_OP_TOPK, TQ_OP_ENCODE = 0, 1, 2, 3
 TQ_TILE = 64
 TQ_MAX_LEVELS = 32
 
-EXPORTED = ["tq_codebook_build", "tq_codebook_free", "tq_water_fill", "tq_codebook_get_info", "tq_codebook_export",
+EXPORTED = ["tq_codebook_build", "tq_codebook_free", "tq_water_fill", "tq_append", "tq_codebook_get_info", "tq_codebook_export",
             "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_search_topk",
             "tq_workspace_size", "tq_status_string"]
 
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.tq_search_topk.restype = i32
     L.tq_workspace_size.argtypes = [p, i32, i64, i64, i64]
     L.tq_workspace_size.restype = sz
+    L.tq_append.argtypes = [p, p, i32, i32, i32, i64, i64, p, i64, i64, p, i32, p]
+    L.tq_append.restype = i32
     L.tq_water_fill.argtypes = [p, i32, i32, i32, i32, p]
     L.tq_water_fill.restype = i32
     L.tq_status_string.argtypes = [i32]

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_encode.hip", "tq_ops.hip", "tq_decode.hip", "tq_large.hip"]
+SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_encode.hip", "tq_ops.hip", "tq_decode.hip", "tq_large.hip",
+           "tq_append.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # no packed-fp32 instructions in device code

@@ -443,6 +443,25 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
   return TQ_OK;
 }
 
+tq_status tq_append(const tq_codebook* cb, const void* x, int32_t x_dtype, int32_t B, int32_t H,
+                    int64_t xs_b, int64_t xs_h, void* records, int64_t rs_b, int64_t rs_h,
+                    const int32_t* positions, int32_t capacity, void* stream) {
+  if (!cb || !x || !records || !positions) return TQ_EINVAL;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+  if (B < 0 || H < 0 || capacity < 0 || xs_b < 0 || xs_h < 0 || rs_b < 0 || rs_h < 0) return TQ_EINVAL;
+  if (!on_device(cb)) return TQ_EINVAL;
+  if (cb->info.num_heads > 1 && cb->info.num_heads != H) return TQ_EINVAL;
+  const CodecView cv = make_view(cb);
+  if (!append_supported(cv)) return TQ_EUNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(records) & 3) || (rs_b & 3) || (rs_h & 3)) return TQ_EALIGN;
+  if (B == 0 || H == 0 || capacity == 0) return TQ_OK;
+  if (B > 65535 || H > 65535) return TQ_EUNSUPPORTED;
+  if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
+  AppendArgs a{x, x_dtype == TQ_BF16, B, H, xs_b, xs_h, static_cast<uint8_t*>(records), rs_b, rs_h,
+               positions, capacity};
+  return map_hip(launch_append(cv, a, static_cast<hipStream_t>(stream)));
+}
+
 tq_status tq_water_fill(const double* lambda, int32_t d, int32_t total_bits, int32_t min_bits,
                         int32_t max_bits, uint8_t* bits_out) {
   if (!lambda || !bits_out || d < 1) return TQ_EINVAL;

@@ -47,6 +47,21 @@ struct EncodeArgs {
 
 hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s);
 
+// One new vector per (sequence, head) written into slot positions[b] of the
+// existing records (d = 128).
+struct AppendArgs {
+  const void* x;        // [B][H][d] rows with strides xs_b, xs_h (elements)
+  int x_bf16;
+  int B, H;
+  int64_t xs_b, xs_h;
+  uint8_t* rec;         // set (b, h) at rec + b * rs_b + h * rs_h
+  int64_t rs_b, rs_h;
+  const int32_t* positions;  // [B]
+  int capacity;         // tokens the records hold
+};
+bool append_supported(const CodecView& cv);
+hipError_t launch_append(const CodecView& cv, const AppendArgs& a, hipStream_t s);
+
 // q' = Pi_h q and qs = S q'[0:m] for nq queries; head_of_query maps query ->
 // rotation head (NULL: all head 0; else head = (query / group) % hkv ...).
 struct QueryPrepArgs {
