@@ -731,3 +731,245 @@ def unpack(codec: Codec, buf: np.ndarray, n: int) -> Encoded:
             nr[rows] = buf[base + fo: base + fo + 2 * TILE].view(np.float16)
     return Encoded(idx[:n], None if sg is None else sg[:n], nx[:n],
                    None if nr is None else nr[:n], None, None)
+
+
+# ---------------------------------------------------------------------------
+# Outlier-channel split (TurboQuant paper review, "Method": for the KV-cache
+# experiments the channels are divided into an outlier group and a regular
+# group, each quantized by its own, independent TurboQuant instance; the
+# 2.5-bit setting gives 32 outlier channels 3 bits and the other 96 channels
+# 2 bits).
+#
+# Readings (the pages name the split and one bit budget, nothing more):
+# * the outlier channels are given by the caller, per KV head (the launch kit
+#   speaks of outlier channels found online and of per-model channel lists);
+# * the regular instance takes the remaining channels in ascending order and
+#   the seeds (rot_seed, sketch_seed); the outlier instance takes the listed
+#   channels in list order and the seeds (rot_seed + 1, sketch_seed + 1);
+# * both instances use the same mode; each stores its own norms.
+#
+# Library record layout of a split codec (d a multiple of 32): the two
+# instances' rotated coordinates are interleaved.  Stored coordinate i, with
+# blk = i // 32 and r = i % 32 and p = o / (d / 32) outlier coordinates per
+# 32-block, is outlier coordinate blk * p + r when r < p, else regular
+# coordinate blk * (32 - p) + r - p.  Codes and sign bits follow the row
+# layout over the stored coordinates (per-dim bits: the outlier instance's on
+# outlier coordinates); the tile's fields are codes, signs (prod), n_x and
+# n_r (prod) of the regular instance, then n_x and n_r (prod) of the outlier
+# instance, fp16 x 64 each.
+# ---------------------------------------------------------------------------
+@dataclass
+class SplitCodec:
+    d: int
+    mode: str
+    outlier: np.ndarray      # [H][o] outlier channels per head, in instance order
+    regular: np.ndarray      # [H][d - o] the other channels, ascending
+    inst_o: Codec            # TurboQuant instance of dimension o
+    inst_r: Codec            # TurboQuant instance of dimension d - o
+
+    @property
+    def o(self) -> int:
+        return self.outlier.shape[1]
+
+    @property
+    def heads(self) -> int:
+        return self.outlier.shape[0]
+
+
+@dataclass
+class SplitEncoded:
+    o: Encoded               # outlier instance
+    r: Encoded               # regular instance
+
+
+def outlier_split_codec(d: int, outlier_channels, bits_outlier: int, bits_regular: int, mode: str,
+                        rot_seed: int, sketch_seed: int = 0) -> SplitCodec:
+    """Two independent TurboQuant instances over a channel split (paper
+    review, "Method", KV-cache setting).  outlier_channels: [o] or [H][o]."""
+    ch = np.atleast_2d(np.asarray(outlier_channels, dtype=np.int64))
+    o = ch.shape[1]
+    if not 0 < o < d:
+        raise ValueError("need 0 < o < d outlier channels")
+    regular = []
+    for h in range(ch.shape[0]):
+        s = set(ch[h].tolist())
+        if len(s) != o or min(s) < 0 or max(s) >= d:
+            raise ValueError("outlier channels must be distinct and in [0, d)")
+        regular.append([c for c in range(d) if c not in s])
+    inst_o = turboquant_codec(o, bits_outlier, mode, rot_seed + 1, sketch_seed + 1)
+    inst_r = turboquant_codec(d - o, bits_regular, mode, rot_seed, sketch_seed)
+    return SplitCodec(d, mode, ch, np.asarray(regular, dtype=np.int64), inst_o, inst_r)
+
+
+def split_encode(sc: SplitCodec, x: np.ndarray, head: int = 0, round_norms: bool = True) -> SplitEncoded:
+    """Each channel group encoded by its own instance."""
+    x = np.asarray(x, dtype=np.float64)
+    return SplitEncoded(encode(sc.inst_o, x[:, sc.outlier[head]], 0, round_norms),
+                        encode(sc.inst_r, x[:, sc.regular[head]], 0, round_norms))
+
+
+def split_score(sc: SplitCodec, q: np.ndarray, enc: SplitEncoded, head: int = 0) -> np.ndarray:
+    """<q, x> estimated as the sum of the two instances' estimates over their channels."""
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    return (score(sc.inst_o, q[:, sc.outlier[head]], enc.o)
+            + score(sc.inst_r, q[:, sc.regular[head]], enc.r))
+
+
+def split_reconstruct(sc: SplitCodec, enc: SplitEncoded, head: int = 0) -> np.ndarray:
+    """x_hat with each channel group reconstructed by its instance."""
+    n = enc.o.idx.shape[0]
+    out = np.zeros((n, sc.d))
+    out[:, sc.outlier[head]] = reconstruct(sc.inst_o, enc.o)
+    out[:, sc.regular[head]] = reconstruct(sc.inst_r, enc.r)
+    return out
+
+
+def split_decode_attention(kcodec, vcodec, q: np.ndarray, kenc: list, venc: list,
+                           scale: float) -> np.ndarray:
+    """decode_attention with keys and/or values of a split codec (either may
+    also be a plain Codec).  Query head h reads KV head h // (Hq / Hkv); a
+    codec with one head serves every KV head."""
+    def sc_(codec, qq, enc, g):
+        if isinstance(codec, SplitCodec):
+            return split_score(codec, qq, enc, g if codec.heads > 1 else 0)
+        return score(codec, qq, enc, g if codec.heads > 1 else 0)
+
+    def rec_(codec, enc, g):
+        if isinstance(codec, SplitCodec):
+            return split_reconstruct(codec, enc, g if codec.heads > 1 else 0)
+        return reconstruct(codec, enc, g if codec.heads > 1 else 0)
+
+    hq = q.shape[0]
+    group = hq // len(kenc)
+    out = np.zeros((hq, q.shape[1]))
+    for h in range(hq):
+        g = h // group
+        s = sc_(kcodec, q[h:h + 1], kenc[g], g)[0] * scale
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[h] = p @ rec_(vcodec, venc[g], g)
+    return out
+
+
+def split_stored_order(d: int, o: int):
+    """(group [d], coord [d]): stored coordinate i holds coordinate coord[i] of
+    the outlier instance (group 1) or of the regular instance (group 0)."""
+    if d % 32 or (o * 32) % d:
+        raise ValueError("the interleaved layout needs d % 32 == 0 and o a multiple of d / 32")
+    p = o * 32 // d
+    group = np.zeros(d, dtype=np.int64)
+    coord = np.zeros(d, dtype=np.int64)
+    for i in range(d):
+        blk, r = divmod(i, 32)
+        if r < p:
+            group[i], coord[i] = 1, blk * p + r
+        else:
+            group[i], coord[i] = 0, blk * (32 - p) + r - p
+    return group, coord
+
+
+def split_stored_codec(sc: SplitCodec) -> Codec:
+    """The split codec seen as one d-dim codec in stored order: rotation rows
+    of head h = the instances' rotation rows placed on their channels, the
+    block-diagonal sketch, per-dim bits and codebooks.  (The library holds a
+    split codec in this form; the oracle itself encodes and scores with the
+    two instances.)"""
+    d = sc.d
+    group, coord = split_stored_order(d, sc.o)
+    rot = np.zeros((sc.heads, d, d))
+    for h in range(sc.heads):
+        for i in range(d):
+            if group[i]:
+                rot[h, i, sc.outlier[h]] = sc.inst_o.rot[0][coord[i]]
+            else:
+                rot[h, i, sc.regular[h]] = sc.inst_r.rot[0][coord[i]]
+    inst = [sc.inst_r, sc.inst_o]
+    bits = np.array([int(inst[group[i]].bits[coord[i]]) for i in range(d)], dtype=np.int64)
+    sk = None
+    if sc.mode == "prod":
+        sk = np.zeros((d, d))
+        for i in range(d):
+            for j in range(d):
+                if group[i] == group[j]:
+                    sk[i, j] = inst[group[i]].sketch[coord[i], coord[j]]
+    cents = [[inst[group[i]].centroids[0][0] for i in range(d)]] * sc.heads
+    bnds = [[inst[group[i]].boundaries[0][0] for i in range(d)]] * sc.heads
+    return Codec(d, sc.mode, bits, d if sc.mode == "prod" else 0, "row", rot, sk, cents, bnds, False,
+                 {"group": group, "coord": coord})
+
+
+def _split_stored_encoded(sc: SplitCodec, enc: SplitEncoded) -> Encoded:
+    group, coord = split_stored_order(sc.d, sc.o)
+    parts = [enc.r, enc.o]
+    n = enc.o.idx.shape[0]
+    idx = np.zeros((n, sc.d), dtype=np.int64)
+    signs = np.zeros((n, sc.d), dtype=bool) if sc.mode == "prod" else None
+    for i in range(sc.d):
+        idx[:, i] = parts[group[i]].idx[:, coord[i]]
+        if signs is not None:
+            signs[:, i] = parts[group[i]].signs[:, coord[i]]
+    return Encoded(idx, signs, enc.r.nx, enc.r.nr, None, None)
+
+
+def split_tile_fields(sc: SplitCodec):
+    """tile_fields of the stored-order codec, then the outlier instance's norms."""
+    fields = tile_fields(split_stored_codec(sc))
+    off = fields[-1][1] + fields[-1][2]
+    fields.append(("nx_o", off, 2 * TILE))
+    if sc.mode == "prod":
+        fields.append(("nr_o", off + 2 * TILE, 2 * TILE))
+    return fields
+
+
+def split_tile_bytes(sc: SplitCodec) -> int:
+    f = split_tile_fields(sc)
+    return f[-1][1] + f[-1][2]
+
+
+def split_pack(sc: SplitCodec, enc: SplitEncoded) -> np.ndarray:
+    """Bytes of the record tiles of a split codec (layout above)."""
+    stored = split_stored_codec(sc)
+    inner = pack(stored, _split_stored_encoded(sc, enc))
+    tb_in, tb = tile_bytes(stored), split_tile_bytes(sc)
+    n = enc.o.idx.shape[0]
+    ntile = (n + TILE - 1) // TILE
+    fields = dict((f[0], f[1]) for f in split_tile_fields(sc))
+    pad = ntile * TILE - n
+    nxo = np.concatenate([enc.o.nx, np.zeros(pad, np.float16)])
+    nro = np.concatenate([enc.o.nr, np.zeros(pad, np.float16)]) if sc.mode == "prod" else None
+    buf = np.zeros(ntile * tb, dtype=np.uint8)
+    for t in range(ntile):
+        rows = slice(t * TILE, (t + 1) * TILE)
+        buf[t * tb: t * tb + tb_in] = inner[t * tb_in: (t + 1) * tb_in]
+        buf[t * tb + fields["nx_o"]: t * tb + fields["nx_o"] + 2 * TILE] = nxo[rows].view(np.uint8)
+        if nro is not None:
+            buf[t * tb + fields["nr_o"]: t * tb + fields["nr_o"] + 2 * TILE] = nro[rows].view(np.uint8)
+    return buf
+
+
+def split_unpack(sc: SplitCodec, buf: np.ndarray, n: int) -> SplitEncoded:
+    """Inverse of split_pack (y and z come back as None)."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    stored = split_stored_codec(sc)
+    tb_in, tb = tile_bytes(stored), split_tile_bytes(sc)
+    ntile = (n + TILE - 1) // TILE
+    fields = dict((f[0], f[1]) for f in split_tile_fields(sc))
+    inner = np.concatenate([buf[t * tb: t * tb + tb_in] for t in range(ntile)])
+    st = unpack(stored, inner, n)
+    nxo = np.concatenate([buf[t * tb + fields["nx_o"]: t * tb + fields["nx_o"] + 2 * TILE]
+                          for t in range(ntile)]).view(np.float16)[:n]
+    nro = None
+    if sc.mode == "prod":
+        nro = np.concatenate([buf[t * tb + fields["nr_o"]: t * tb + fields["nr_o"] + 2 * TILE]
+                              for t in range(ntile)]).view(np.float16)[:n]
+    group, coord = split_stored_order(sc.d, sc.o)
+    out = []
+    for gsel, inst in ((1, sc.inst_o), (0, sc.inst_r)):
+        cols = np.nonzero(group == gsel)[0]
+        order = cols[np.argsort(coord[cols])]
+        idx = st.idx[:, order]
+        sg = st.signs[:, order] if st.signs is not None else None
+        out.append((idx, sg))
+    enc_o = Encoded(out[0][0], out[0][1], nxo, nro, None, None)
+    enc_r = Encoded(out[1][0], out[1][1], st.nx, st.nr, None, None)
+    return SplitEncoded(enc_o, enc_r)

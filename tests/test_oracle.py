@@ -451,3 +451,126 @@ def test_selective_qjl_unbiased_on_signal_dims():
     target = qr[0, :m] @ r
     vals = np.array(vals)
     assert abs(vals.mean() - target) < 4 * vals.std(ddof=1) / math.sqrt(len(vals))
+
+
+# --------------------------------------------------- outlier-channel split
+def _split(mode="prod", bits=(3, 2), heads=1, seed=11):
+    rng = np.random.default_rng(seed)
+    ch = np.stack([rng.permutation(128)[:32] for _ in range(heads)])
+    return o.outlier_split_codec(128, ch, bits[0], bits[1], mode, rot_seed=40 + seed, sketch_seed=50 + seed)
+
+
+def test_split_layout_worked_example():
+    sc = _split()
+    group, coord = o.split_stored_order(128, 32)
+    rows = _rows("split_layout_example.txt")
+    for r in rows:
+        if r[0] == "order":
+            i, g, c = int(r[1]), int(r[2]), int(r[3])
+            assert (group[i], coord[i]) == (g, c)
+    enc_o = o.Encoded(np.full((1, 32), 3), np.ones((1, 32), bool), np.array([2.0], np.float16),
+                      np.array([0.25], np.float16), None, None)
+    enc_r = o.Encoded(np.zeros((1, 96), np.int64), np.zeros((1, 96), bool), np.array([1.0], np.float16),
+                      np.array([0.5], np.float16), None, None)
+    buf = o.split_pack(sc, o.SplitEncoded(enc_o, enc_r))
+    for r in rows:
+        if r[0] == "bytes":
+            off, want = int(r[1]), [int(v, 16) for v in r[2:]]
+            assert list(buf[off:off + len(want)]) == want, off
+        if r[0] == "tile":
+            assert len(buf) == int(r[1]) == o.split_tile_bytes(sc)
+    back = o.split_unpack(sc, buf, 1)
+    assert np.array_equal(back.o.idx, enc_o.idx) and np.array_equal(back.r.signs, enc_r.signs)
+
+
+@pytest.mark.parametrize("n", [1, 64, 130])
+def test_split_pack_roundtrip(n):
+    sc = _split()
+    x = np.random.default_rng(n).normal(size=(n, 128))
+    enc = o.split_encode(sc, x)
+    back = o.split_unpack(sc, o.split_pack(sc, enc), n)
+    for a, b in ((enc.o, back.o), (enc.r, back.r)):
+        assert np.array_equal(a.idx, b.idx) and np.array_equal(a.signs, b.signs)
+        assert np.array_equal(a.nx, b.nx) and np.array_equal(a.nr, b.nr)
+
+
+def test_split_estimator_unbiased_over_sketches():
+    # Each instance's prod estimate is unbiased over its sketch (paper review,
+    # "Results"), so the sum over the two channel groups is unbiased for
+    # <q, x>, and with independent sketches its variance is the sum of the two
+    # QJL variances (n_r^2 / m_g)((pi/2)|q'_g|^2 - <q'_g, r_g/|r_g|>^2) n_x,g^2,
+    # each with its own sketch size m_g.
+    rng = np.random.default_rng(7)
+    x, q = rng.normal(size=128), rng.normal(size=128)
+    x[[3, 77]] *= 10.0
+    sc0 = _split(seed=3)
+    vals = []
+    for s in range(2000):
+        sc = o.SplitCodec(**{**sc0.__dict__})
+        sc.inst_o = o.Codec(**{**sc0.inst_o.__dict__})
+        sc.inst_r = o.Codec(**{**sc0.inst_r.__dict__})
+        sc.inst_o.sketch = o.stored_sketch(32, 7000 + s)
+        sc.inst_r.sketch = o.stored_sketch(96, 9000 + s)
+        enc = o.split_encode(sc, x[None], round_norms=False)
+        vals.append(o.split_score(sc, q[None], enc)[0, 0])
+    vals = np.array(vals)
+    se = vals.std(ddof=1) / math.sqrt(len(vals))
+    assert abs(vals.mean() - q @ x) < 4 * se
+    var = 0.0
+    enc = o.split_encode(sc0, x[None], round_norms=False)
+    for inst, part, chans in ((sc0.inst_o, enc.o, sc0.outlier[0]), (sc0.inst_r, enc.r, sc0.regular[0])):
+        qr = inst.rot[0] @ q[chans]
+        r = part.y[0] - o.dequantize(inst, part.idx, 0)[0]
+        nr = np.linalg.norm(r)
+        var += (nr ** 2 / inst.m) * ((math.pi / 2) * qr @ qr - (qr @ (r / nr)) ** 2) * float(part.nx[0]) ** 2
+    assert abs(vals.var(ddof=1) / var - 1) < 0.12
+
+
+def test_split_distortion_is_per_group():
+    # Each group is normalised by its own norm, so its relative distortion is
+    # the Lloyd-Max error of its own instance, d_g * D_g(b_g) (paper review,
+    # "Method"), whatever the scale of the other group.
+    sc = _split(mode="mse", bits=(4, 2), seed=5)
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=(3000, 128))
+    x[:, sc.outlier[0]] *= 30.0
+    xh = o.split_reconstruct(sc, o.split_encode(sc, x, round_norms=False))
+    for chans, inst in ((sc.outlier[0], sc.inst_o), (sc.regular[0], sc.inst_r)):
+        err = np.sum((x[:, chans] - xh[:, chans]) ** 2, axis=1) / np.sum(x[:, chans] ** 2, axis=1)
+        want = inst.d * inst.extra["lloyd_max"].mse
+        assert abs(err.mean() / want - 1) < 0.05
+
+
+def test_split_stored_form_gives_same_scores():
+    # The library holds a split codec as one codec in stored order (rotation
+    # rows placed on the channels, block-diagonal sketch, per-dim codebooks,
+    # per-group norms and QJL factors sqrt(pi/2)/m_g).  Scoring through that
+    # form, written out here from the layout rule, must give the two-instance
+    # scores.
+    for heads in (1, 2):
+        sc = _split(heads=heads, seed=20 + heads)
+        st = o.split_stored_codec(sc)
+        group = st.extra["group"]
+        rng = np.random.default_rng(heads)
+        x, q = rng.normal(size=(40, 128)), rng.normal(size=(3, 128))
+        for h in range(heads):
+            enc = o.split_encode(sc, x, head=h)
+            ref = o.split_score(sc, q, enc, head=h)
+            flat = o._split_stored_encoded(sc, enc)
+            qr = q @ st.rot[h].T
+            qs = qr @ st.sketch.T
+            chat = np.stack([np.array([st.centroids[h][i][flat.idx[t, i]] for i in range(128)])
+                             for t in range(40)])
+            pm = np.where(flat.signs, 1.0, -1.0)
+            got = np.zeros_like(ref)
+            for gsel, part in ((1, enc.o), (0, enc.r)):
+                cols = group == gsel
+                kap = math.sqrt(math.pi / 2) / cols.sum()
+                code = qr[:, cols] @ chat[:, cols].T
+                qjl = (qs[:, cols] @ pm[:, cols].T) * (part.nr.astype(np.float64) * kap)[None]
+                got += (code + qjl) * part.nx.astype(np.float64)[None]
+            assert np.allclose(got, ref, rtol=1e-10, atol=1e-10)
+            # the stored rotation is orthogonal and the stored sketch block-diagonal
+            assert np.max(np.abs(st.rot[h] @ st.rot[h].T - np.eye(128))) < 1e-5
+            assert not st.sketch[np.ix_(group == 1, group == 0)].any()
+
