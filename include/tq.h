@@ -32,7 +32,9 @@
  * Records are grouped in TILES of 64 consecutive vectors; a buffer holding n
  * records is ceil(n/64) tiles of tq_codebook_info.tile_bytes bytes.  Fields of
  * a tile, in order: codes, signs (prod only), n_x (64 x fp16), n_r (64 x fp16,
- * prod only).  Norms are fp16, round to nearest even.
+ * prod only); an outlier-split codec then adds the outlier instance's n_x and
+ * (prod) n_r, and its n_x / n_r fields are the regular instance's.  Norms are
+ * fp16, round to nearest even.
  *   ROW layout (for keys and database vectors, read one vector per lane):
  *     a vector's index bits form one bit string, plane by plane (plane p holds
  *     bit p of the index of every dim with more than p bits, dims ascending);
@@ -112,7 +114,8 @@ typedef struct tq_codebook tq_codebook;
  *              as for TQ_ROT_HAAR.  The d = 128 encode applies it as a fast
  *              Walsh-Hadamard transform; every other call uses Pi itself.
  *   num_heads  rotations held by the codebook (one per KV head for
- *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN); TQ_ROT_HAAR uses 1.
+ *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN, or per outlier channel list of
+ *              a split codec); TQ_ROT_HAAR otherwise uses 1.
  *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map;
  *              the GPU encode writes COL records for 1, 2 or 4 index bits).
  *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1; the
@@ -123,6 +126,32 @@ typedef struct tq_codebook tq_codebook;
  *              by discrete reverse water-filling ([SQ] tweet 6) with
  *              tq_water_fill: waterfill_bits index bits in total, 1..5 per dim,
  *              lambda_i = sigma_i^2 averaged over the heads.
+ *   outlier_dims  o, 0 = off.  Outlier-channel split ([TQ] "Method": for the
+ *              KV-cache experiments the channels are divided into an outlier
+ *              and a regular group, each quantized by its own TurboQuant
+ *              instance; 32 channels at 3 bits + 96 at 2 bits is the 2.5-bit
+ *              setting).  The regular instance covers the other d - o channels
+ *              (ascending) with `bits`, Pi from seed_rotation and S from
+ *              seed_sketch; the outlier instance covers outlier_channels (in
+ *              list order) with outlier_bits, seeds seed_rotation + 1 and
+ *              seed_sketch + 1; both are Haar TurboQuant codecs of `mode` at
+ *              their own dimension (Beta-law codebooks at o and d - o, prod
+ *              with a full sketch of each instance).  Needs d = 128,
+ *              o in {32, 64, 96}, rotation TQ_ROT_HAAR, bitmap NULL,
+ *              qjl_dims 0, layout ROW; num_heads >= 1 channel lists.
+ *              The codec is held in "stored order": stored coordinate i
+ *              (blk = i / 32, r = i % 32, p = o / 4 per block) is outlier
+ *              coordinate p blk + r when r < p, else regular coordinate
+ *              (32 - p) blk + r - p; the rotation rows, the (block-diagonal)
+ *              sketch, the per-dim codebooks, the index bits and the sign bits
+ *              all follow that order, and tq_codebook_export returns them so.
+ *              Scores: s = sum over the two groups g of
+ *              n_x,g (sum_{i in g} q'_i c_i[idx_i]
+ *                     + n_r,g sqrt(pi/2)/m_g sum_{j in g} qs_j (2 bit_j - 1)),
+ *              m_g the group's size; each group stores its own norms.
+ *   outlier_bits   total bits per coordinate of the outlier instance.
+ *   outlier_channels  host int32 [num_heads][o]: distinct channels in [0, d)
+ *              per head (head h of a multi-head codec uses row h).
  */
 typedef struct {
   int32_t d;
@@ -141,6 +170,9 @@ typedef struct {
   int32_t calib_dtype;
   int32_t device;
   int32_t waterfill_bits;
+  int32_t outlier_dims;
+  int32_t outlier_bits;
+  const int32_t* outlier_channels;
 } tq_codebook_desc;
 
 /* Sizes of a codec's records. */
@@ -149,9 +181,12 @@ typedef struct {
   int32_t index_bits_total;   /* B = sum of per-dim index bits                 */
   int32_t code_bytes;         /* per vector, ceil(B/8)                          */
   int32_t sign_bytes;         /* per vector, ceil(m/8) (0 for mse)              */
-  int32_t norms;              /* fp16 norms per vector: 1 (mse) or 2 (prod)     */
+  int32_t norms;              /* fp16 norms per vector: 1 (mse) or 2 (prod), x2 split */
   int64_t tile_bytes;         /* bytes of one 64-vector tile                    */
   int64_t off_signs, off_nx, off_nr;  /* byte offsets of the fields in a tile  */
+  int32_t outlier_dims;       /* o of a split codec, else 0                    */
+  int32_t outlier_per_block;  /* o / 4: outlier coordinates per 32 stored ones */
+  int64_t off_nx_o, off_nr_o; /* split: outlier instance's norms, else -1      */
 } tq_codebook_info;
 
 /* Build a codebook (host math once, then device tables on desc->device).

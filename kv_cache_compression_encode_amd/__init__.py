@@ -37,13 +37,16 @@ def _dtype_code(t: torch.Tensor) -> int:
 class Codebook:
     """A built codec (rotation(s), sketch, Lloyd-Max tables) on one device.
 
-    device=-1 builds a host-only codebook, usable for export and layout queries."""
+    device=-1 builds a host-only codebook, usable for export and layout queries.
+    outlier_channels ([o] or [H][o]) with outlier_bits builds an outlier-channel
+    split codec (two TurboQuant instances, `bits` on the other channels)."""
 
     def __init__(self, d: int, mode: int, bits: int, *, bitmap: Optional[Sequence[int]] = None,
                  qjl_dims: int = 0, rotation: int = TQ_ROT_HAAR, num_heads: int = 1,
                  layout: int = TQ_LAYOUT_ROW, seed_rotation: int = 0, seed_sketch: int = 0,
                  given: Optional[np.ndarray] = None, calib: Optional[np.ndarray] = None,
-                 device: int = 0, waterfill_bits: int = 0):
+                 device: int = 0, waterfill_bits: int = 0,
+                 outlier_channels: Optional[np.ndarray] = None, outlier_bits: int = 0):
         desc = L.CodebookDesc()
         desc.d, desc.mode, desc.bits = d, mode, bits
         keep = []
@@ -73,6 +76,13 @@ class Codebook:
             desc.calib_n = c.shape[-2]
         desc.device = device
         desc.waterfill_bits = waterfill_bits
+        if outlier_channels is not None:
+            oc = np.ascontiguousarray(np.atleast_2d(np.asarray(outlier_channels, dtype=np.int32)))
+            keep.append(oc)
+            desc.outlier_dims, desc.outlier_bits = oc.shape[1], outlier_bits
+            desc.outlier_channels = oc.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+            if num_heads == 1:
+                desc.num_heads = oc.shape[0]
         h = ctypes.c_void_p()
         L.check(L.lib().tq_codebook_build(ctypes.byref(desc), ctypes.byref(h)), "tq_codebook_build")
         self._h = h

@@ -28,7 +28,9 @@ class CodebookDesc(ctypes.Structure):
                 ("seed_sketch", ctypes.c_uint64), ("given", ctypes.POINTER(ctypes.c_float)),
                 ("calib", ctypes.c_void_p), ("calib_n", ctypes.c_int64),
                 ("calib_dtype", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("waterfill_bits", ctypes.c_int32)]
+                ("waterfill_bits", ctypes.c_int32), ("outlier_dims", ctypes.c_int32),
+                ("outlier_bits", ctypes.c_int32),
+                ("outlier_channels", ctypes.POINTER(ctypes.c_int32))]
 
 
 class CodebookInfo(ctypes.Structure):
@@ -38,7 +40,9 @@ class CodebookInfo(ctypes.Structure):
                 ("code_bytes", ctypes.c_int32), ("sign_bytes", ctypes.c_int32),
                 ("norms", ctypes.c_int32), ("tile_bytes", ctypes.c_int64),
                 ("off_signs", ctypes.c_int64), ("off_nx", ctypes.c_int64),
-                ("off_nr", ctypes.c_int64)]
+                ("off_nr", ctypes.c_int64), ("outlier_dims", ctypes.c_int32),
+                ("outlier_per_block", ctypes.c_int32), ("off_nx_o", ctypes.c_int64),
+                ("off_nr_o", ctypes.c_int64)]
 
 
 class KVView(ctypes.Structure):

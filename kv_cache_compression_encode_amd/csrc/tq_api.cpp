@@ -27,7 +27,8 @@ tq_status upload(T** dst, const T* src, size_t count) {
 void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
   void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
-                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm, t.had_mask};
+                  t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm, t.had_mask,
+                  t.omask};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -56,10 +57,137 @@ void fill_info(tq_codebook* cb) {
   off += 2 * kTile;
   in.off_nr = cb->desc.mode == TQ_PROD ? off : -1;
   if (cb->desc.mode == TQ_PROD) off += 2 * kTile;
+  in.outlier_dims = cb->outlier;
+  in.outlier_per_block = cb->outlier ? cb->outlier * 32 / d : 0;
+  in.off_nx_o = in.off_nr_o = -1;
+  if (cb->outlier) {
+    in.norms *= 2;
+    in.off_nx_o = off;
+    off += 2 * kTile;
+    if (cb->desc.mode == TQ_PROD) {
+      in.off_nr_o = off;
+      off += 2 * kTile;
+    }
+  }
   in.tile_bytes = off;
 }
 
+// Outlier-channel split: two Haar TurboQuant instances (outlier channels with
+// outlier_bits, the others with bits) held as one codec in stored order.
+// Stored coordinate i = 32 blk + r is outlier coordinate p blk + r for r < p
+// (p = o / 4), else regular coordinate (32 - p) blk + r - p.  Rotation row i
+// is that instance's Pi row placed on its channels; the sketch is
+// block-diagonal (S_o on outlier pairs, S_r on regular pairs, zero across).
+tq_status build_split(tq_codebook* cb, const tq_codebook_desc& ds) {
+  const int d = ds.d, o = ds.outlier_dims;
+  if (d != 128) return TQ_EUNSUPPORTED;
+  if (o != 32 && o != 64 && o != 96) return TQ_EUNSUPPORTED;
+  if (!ds.outlier_channels || ds.bitmap || ds.waterfill_bits > 0 || ds.rotation != TQ_ROT_HAAR)
+    return TQ_EINVAL;
+  if (ds.layout != TQ_LAYOUT_ROW || (ds.qjl_dims != 0 && ds.qjl_dims != d)) return TQ_EUNSUPPORTED;
+  const int heads = std::max(1, ds.num_heads);
+  const int ub_r = ds.mode == TQ_PROD ? ds.bits - 1 : ds.bits;
+  const int ub_o = ds.mode == TQ_PROD ? ds.outlier_bits - 1 : ds.outlier_bits;
+  if (ub_r < 1 || ub_r > kMaxBits || ub_o < 1 || ub_o > kMaxBits) return TQ_EINVAL;
+  // channel lists: outlier channels in list order, the others ascending
+  std::vector<int> och(size_t(heads) * o), rch(size_t(heads) * (d - o));
+  for (int h = 0; h < heads; ++h) {
+    std::vector<char> seen(d, 0);
+    for (int k = 0; k < o; ++k) {
+      const int c = ds.outlier_channels[size_t(h) * o + k];
+      if (c < 0 || c >= d || seen[c]) return TQ_EINVAL;
+      seen[c] = 1;
+      och[size_t(h) * o + k] = c;
+    }
+    int k = 0;
+    for (int c = 0; c < d; ++c)
+      if (!seen[c]) rch[size_t(h) * (d - o) + k++] = c;
+  }
+  const int p = o * 32 / d;
+  std::vector<int> grp(d), crd(d);
+  for (int i = 0; i < d; ++i) {
+    const int blk = i / 32, r = i % 32;
+    grp[i] = r < p ? 1 : 0;
+    crd[i] = r < p ? p * blk + r : (32 - p) * blk + r - p;
+  }
+  cb->outlier = o;
+  cb->omask.assign(size_t(heads) * (d / 32), 0u);
+  for (int h = 0; h < heads; ++h)
+    for (int k = 0; k < o; ++k) {
+      const int c = och[size_t(h) * o + k];
+      cb->omask[size_t(h) * (d / 32) + c / 32] |= 1u << (c % 32);
+    }
+  cb->uniform = false;
+  cb->ubits = 0;
+  cb->m = ds.mode == TQ_PROD ? d : 0;
+  cb->bits.assign(d, 0);
+  for (int i = 0; i < d; ++i) cb->bits[i] = uint8_t(grp[i] ? ub_o : ub_r);
+  // rotations: Pi_o (seed_rotation + 1) and Pi_r (seed_rotation), stream 1
+  const int dims[2] = {d - o, o};
+  std::vector<double> pi[2];
+  for (int gsel = 0; gsel < 2; ++gsel) {
+    const int n = dims[gsel];
+    std::vector<double> g(size_t(n) * n);
+    philox_normals(ds.seed_rotation + uint64_t(gsel), 1, int64_t(n) * n, g.data());
+    pi[gsel].resize(size_t(n) * n);
+    haar_from_gaussian(n, g.data(), pi[gsel].data());
+  }
+  cb->rot64.assign(size_t(heads) * d * d, 0.0);
+  for (int h = 0; h < heads; ++h)
+    for (int i = 0; i < d; ++i) {
+      const int gsel = grp[i], n = dims[gsel];
+      const int* ch = gsel ? &och[size_t(h) * o] : &rch[size_t(h) * (d - o)];
+      for (int k = 0; k < n; ++k) cb->rot64[(size_t(h) * d + i) * d + ch[k]] = pi[gsel][size_t(crd[i]) * n + k];
+    }
+  cb->rot32.resize(cb->rot64.size());
+  for (size_t e = 0; e < cb->rot64.size(); ++e) cb->rot32[e] = float(cb->rot64[e]);
+  // sketches: S_o (seed_sketch + 1) and S_r (seed_sketch), stream 2, fp16 values
+  if (ds.mode == TQ_PROD) {
+    std::vector<float> sk[2];
+    for (int gsel = 0; gsel < 2; ++gsel) {
+      const int n = dims[gsel];
+      std::vector<double> s(size_t(n) * n);
+      philox_normals(ds.seed_sketch + uint64_t(gsel), 2, int64_t(n) * n, s.data());
+      sk[gsel].resize(s.size());
+      for (size_t e = 0; e < s.size(); ++e) sk[gsel][e] = f16_to_f32(f32_to_f16_rne(float(s[e])));
+    }
+    cb->sketch32.assign(size_t(d) * d, 0.f);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        if (grp[i] == grp[j])
+          cb->sketch32[size_t(i) * d + j] = sk[grp[i]][size_t(crd[i]) * dims[grp[i]] + crd[j]];
+  }
+  // per-dim Beta-law codebooks of each instance's dimension
+  const LloydMaxResult books[2] = {lloyd_max_sphere(d - o, ub_r), lloyd_max_sphere(o, ub_o)};
+  cb->cen64.assign(size_t(heads) * d * kMaxLevels, 0.0);
+  cb->thr64.assign(size_t(heads) * d * (kMaxLevels - 1), 0.0);
+  cb->cen32.assign(size_t(heads) * d * kMaxLevels, 0.f);
+  cb->thr32.assign(size_t(heads) * d * kMaxLevels, INFINITY);
+  for (int h = 0; h < heads; ++h)
+    for (int i = 0; i < d; ++i) {
+      const LloydMaxResult& lm = books[grp[i]];
+      const int L = 1 << cb->bits[i];
+      for (int k = 0; k < L; ++k) {
+        cb->cen64[(size_t(h) * d + i) * kMaxLevels + k] = lm.centroids[k];
+        cb->cen32[(size_t(h) * d + i) * kMaxLevels + k] = float(lm.centroids[k]);
+      }
+      for (int k = 0; k + 1 < L; ++k) {
+        cb->thr64[(size_t(h) * d + i) * (kMaxLevels - 1) + k] = lm.boundaries[k];
+        cb->thr32[(size_t(h) * d + i) * kMaxLevels + k] = float(lm.boundaries[k]);
+      }
+    }
+  cb->bitpos.assign(size_t(kMaxBits) * d, -1);
+  int pos = 0;
+  for (int pl = 0; pl < kMaxBits; ++pl)
+    for (int i = 0; i < d; ++i)
+      if (cb->bits[i] > pl) cb->bitpos[size_t(pl) * d + i] = int16_t(pos++);
+  fill_info(cb);
+  cb->info.num_heads = heads;
+  return TQ_OK;
+}
+
 tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
+  if (ds.outlier_dims != 0) return ds.outlier_dims < 0 ? TQ_EINVAL : build_split(cb, ds);
   const int d = ds.d;
   // ---------------------------------------------------------------- bits
   cb->bits.assign(d, 0);
@@ -291,7 +419,9 @@ tq_status build_device(tq_codebook* cb) {
       }
     if ((st = upload(&cb->dev.had_mask, mask.data(), mask.size())) != TQ_OK) return st;
   }
-  if (!cb->uniform && d == 128) {
+  if (!cb->omask.empty())
+    if ((st = upload(&cb->dev.omask, cb->omask.data(), cb->omask.size())) != TQ_OK) return st;
+  if (!cb->uniform && !cb->outlier && d == 128) {
     // tail byte t -> bits 1.. of the indices of dims 0..3 (dim i at bits 5i..5i+4),
     // for the bit positions D..D+7 of the row bit string
     std::vector<uint32_t> tail(256, 0u);
@@ -365,8 +495,15 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.off_nx = int(cb->info.off_nx);
   v.off_nr = int(cb->info.off_nr);
   v.tail_bits = cb->info.index_bits_total - cb->desc.d;
+  v.outl = cb->outlier;
+  v.o4 = cb->info.outlier_per_block;
+  v.off_nxo = int(cb->info.off_nx_o);
+  v.off_nro = int(cb->info.off_nr_o);
+  v.split_ub_o = cb->outlier ? cb->bits[0] : 0;                // stored dim 0: outlier
+  v.split_ub_r = cb->outlier ? cb->bits[cb->desc.d - 1] : 0;   // last stored dim: regular
+  v.omask = cb->dev.omask;
   v.sq_ok = 0;
-  if (!cb->uniform && int(cb->bits.size()) == cb->desc.d && cb->desc.d > 4) {
+  if (!cb->uniform && !cb->outlier && int(cb->bits.size()) == cb->desc.d && cb->desc.d > 4) {
     bool ok = true;
     for (int i = 0; i < cb->desc.d; ++i)
       ok = ok && (i < 4 ? cb->bits[i] >= 1 && cb->bits[i] <= 5 : cb->bits[i] == 1);
@@ -418,7 +555,8 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
   if (ds.mode == TQ_PROD && !ds.bitmap && ds.waterfill_bits <= 0 && ds.bits < 2) return TQ_EINVAL;
   if (ds.layout != TQ_LAYOUT_ROW && ds.layout != TQ_LAYOUT_COL) return TQ_EINVAL;
   if (ds.qjl_dims < 0 || ds.num_heads < 0) return TQ_EINVAL;
-  if ((ds.rotation == TQ_ROT_HAAR || ds.rotation == TQ_ROT_HADAMARD) && ds.num_heads > 1) return TQ_EINVAL;
+  if ((ds.rotation == TQ_ROT_HAAR || ds.rotation == TQ_ROT_HADAMARD) && ds.num_heads > 1 && ds.outlier_dims == 0)
+    return TQ_EINVAL;
   tq_codebook* cb = new (std::nothrow) tq_codebook();
   if (!cb) return TQ_ENOMEM;
   cb->desc = ds;
@@ -433,6 +571,7 @@ tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out) {
   cb->desc.bitmap = nullptr;
   cb->desc.given = nullptr;
   cb->desc.calib = nullptr;
+  cb->desc.outlier_channels = nullptr;
   if (st == TQ_OK && cb->device >= 0) st = build_device(cb);
   if (st != TQ_OK) {
     free_device(cb);
@@ -614,7 +753,7 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
   tq_status st = map_hip(launch_query_prep(cv, qa, s));
   if (st != TQ_OK) return st;
-  return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s));
+  return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s, head));
 }
 
 tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,

@@ -12,7 +12,11 @@
 // records: the vector's bit string is assembled in LDS from the bit positions
 // table and written byte by byte into its 16-byte chunks.  COL records: each
 // lane rewrites the bits of its two dims in the dims' fields (read, mask,
-// write; no other wave touches these words).
+// write; no other wave touches these words).  Outlier-channel split codecs:
+// each group (stored coordinates i with i % 32 < o4, and the rest) is
+// normalised by its own norm, taken from its rotated coordinates (the
+// rotation is orthogonal on each group's channels), and keeps its own n_x and
+// n_r.
 #include <hip/hip_runtime.h>
 
 #include "tq_kernels.h"
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(64) void append_kernel(CodecView cv, AppendArgs a) 
     x1 = xp[l + 64];
   }
   const float nx = sqrtf(wave_sum(fmaf(x0, x0, x1 * x1)));
-  const float inv = nx > 0.f ? 1.f / nx : 0.f;  // a zero vector encodes y = 0
+  float inv = nx > 0.f ? 1.f / nx : 0.f;  // a zero vector encodes y = 0
   sx[l] = x0;
   sx[l + 64] = x1;
   if (l < int(sizeof(sbits) / 4)) sbits[l] = 0u;
@@ -69,7 +73,18 @@ __global__ __launch_bounds__(64) void append_kernel(CodecView cv, AppendArgs a) 
     c0 = fmaf(rt[size_t(k + 1) * D + l], sx[k + 1], c0);
     c1 = fmaf(rt[size_t(k + 1) * D + l + 64], sx[k + 1], c1);
   }
-  const float y[2] = {(a0 + c0) * inv, (a1 + c1) * inv};
+  const float z0 = a0 + c0, z1 = a1 + c1;
+  // split: lane l's dims l and l + 64 share l % 32, so one group per lane
+  const bool og = cv.outl && (l & 31) < cv.o4;
+  float nxo = 0.f, nxr = nx;
+  if (cv.outl) {
+    const float q = fmaf(z0, z0, z1 * z1);
+    nxo = sqrtf(wave_sum(og ? q : 0.f));
+    nxr = sqrtf(wave_sum(og ? 0.f : q));
+    const float ng = og ? nxo : nxr;
+    inv = ng > 0.f ? 1.f / ng : 0.f;
+  }
+  const float y[2] = {z0 * inv, z1 * inv};
 
   // ---- quantize: idx = number of boundaries <= y
   int idx[2];
@@ -118,7 +133,9 @@ __global__ __launch_bounds__(64) void append_kernel(CodecView cv, AppendArgs a) 
 
   // ---- prod: residual norm and the QJL sketch signs
   if (cv.mode == TQ_PROD) {
-    const float nr = sqrtf(wave_sum(fmaf(res[0], res[0], res[1] * res[1])));
+    const float rq = fmaf(res[0], res[0], res[1] * res[1]);
+    const float nr = sqrtf(wave_sum(og ? 0.f : rq));
+    const float nro = cv.outl ? sqrtf(wave_sum(og ? rq : 0.f)) : 0.f;
     sr[l] = res[0];
     sr[l + 64] = res[1];
     __syncthreads();
@@ -144,8 +161,10 @@ __global__ __launch_bounds__(64) void append_kernel(CodecView cv, AppendArgs a) 
           uint8_t(ssign[B >> 2] >> (8 * (B & 3)));
     }
     if (l == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = f16_bits(nr);
+    if (l == 0 && cv.outl) *reinterpret_cast<uint16_t*>(trec + cv.off_nro + 2 * slot) = f16_bits(nro);
   }
-  if (l == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nx);
+  if (l == 0) *reinterpret_cast<uint16_t*>(trec + cv.off_nx + 2 * slot) = f16_bits(nxr);
+  if (l == 0 && cv.outl) *reinterpret_cast<uint16_t*>(trec + cv.off_nxo + 2 * slot) = f16_bits(nxo);
 }
 
 }  // namespace

@@ -311,10 +311,15 @@ __device__ __forceinline__ uint32_t group_or(uint32_t w) {
   return w;
 }
 
-template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
   // MODE: 0 mse, 1 prod with a full 128-dim MFMA sketch, 2 prod with a small
   // (m <= 4) sketch on rotated dims 0..m-1 (SpectralQuant selective QJL).
+  // SPLIT: outlier-channel split codec in stored order with 32 outlier
+  // coordinates (half 0, registers 0..7 of every 32-dim block) at 2 index
+  // bits and 96 regular ones at 1 bit; each group is normalised by its own
+  // norm, summed over its channels (the head's channel mask) as the rows
+  // are loaded.
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* sPiHi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* sPiLo = sPiHi + D * LDS_ROW;
@@ -330,13 +335,28 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   stage_matrix(sPiHi, cv.rot_hi + size_t(hc) * D * D, false);
   stage_matrix(sPiLo, cv.rot_lo + size_t(hc) * D * D, false);
   if (MODE == 1) stage_matrix(sSk, cv.sk_hi, true);
-  if (!UNIFORM) {
+  if (!UNIFORM && !SPLIT) {
     for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
       sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
       sCen[e] = cv.cen[size_t(hc) * D * kMaxLevels + e];
     }
   }
   __syncthreads();
+  // SPLIT: outlier boundary t_2 and levels c_2, c_3 (dim 0), regular level
+  // c_1 (dim 8), and this half's outlier-channel mask (channels 64 hh ..)
+  float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f;
+  uint32_t om[2] = {0u, 0u};
+  if constexpr (SPLIT) {
+    const float* th = cv.thr + size_t(hc) * D * kMaxLevels;
+    const float* ce = cv.cen + size_t(hc) * D * kMaxLevels;
+    spl_t2 = th[2];
+    spl_c2 = 32.f * ce[2];
+    spl_c3 = 32.f * ce[3];
+    spl_c1 = 32.f * ce[8 * kMaxLevels + 1];
+    const int hf = int(threadIdx.x & 63) >> 5;
+    om[0] = cv.omask[hc * 4 + 2 * hf];
+    om[1] = cv.omask[hc * 4 + 2 * hf + 1];
+  }
 
   const int lane = lane_id();
   const int j = lane & 31, hh = lane >> 5;
@@ -383,6 +403,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // between the accumulator and the rotated unit vector y.
       u32x4 xh[NB][8], xl[NB][8];
       float sx[NB], nxv[NB], wsc[NB];
+      float so2[NB];  // SPLIT: sum of squares over this vector's outlier channels
       bool valid[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -395,17 +416,40 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           const u32x4* r = cur[nb];
           {
             float s0 = 0.f, s1 = 0.f;  // two chains; fp32 FMAs (exact squares)
+            float o0 = 0.f, o1 = 0.f;  // SPLIT: outlier channels only
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
-                s0 = fmaf(lo, lo, s0);
-                s1 = fmaf(hi, hi, s1);
+                if constexpr (SPLIT) {
+                  // channel 64 hh + 8c + 2i (+1): bit (8c + 2i) % 32 of mask word c / 4
+                  const int k = (8 * c + 2 * i) & 31;
+                  const uint32_t lw = r[c][i] << 16, hw = r[c][i] & 0xffff0000u;
+                  const float lo_o = __uint_as_float(lw & uint32_t(-int((om[c >> 2] >> k) & 1u)));
+                  const float hi_o = __uint_as_float(hw & uint32_t(-int((om[c >> 2] >> (k + 1)) & 1u)));
+                  o0 = fmaf(lo_o, lo_o, o0);
+                  o1 = fmaf(hi_o, hi_o, o1);
+                  const float lo_r = lo - lo_o, hi_r = hi - hi_o;  // exact: x or 0
+                  s0 = fmaf(lo_r, lo_r, s0);
+                  s1 = fmaf(hi_r, hi_r, s1);
+                } else {
+                  s0 = fmaf(lo, lo, s0);
+                  s1 = fmaf(hi, hi, s1);
+                }
               }
             ss = s0 + s1;
+            so2[nb] = o0 + o1;
           }
-          ss += xor32f(ss);
+          if constexpr (SPLIT) {
+            // ss holds the regular channels here; the scale below needs ||x||
+            ss += xor32f(ss);
+            so2[nb] += xor32f(so2[nb]);
+            nxv[nb] = sqrtf(ss);        // regular instance's norm
+            ss += so2[nb];
+          } else {
+            ss += xor32f(ss);
+          }
           // scale 2^s, s = 14 - floor(log2 ||x||): every |x_i| 2^s < 2^15.
           // x_i 2^s in fp16 is then formed from the bf16 bits directly: the
           // exponent field drops by D = 112 - s (saturating at 0, which
@@ -465,14 +509,29 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
             v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
           }
+          float so = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              ss = fmaf(v[c][i], v[c][i], ss);
+              if constexpr (SPLIT) {
+                const bool ob = (om[c >> 2] >> ((8 * c + i) & 31)) & 1u;
+                if (ob) so = fmaf(v[c][i], v[c][i], so);
+                else ss = fmaf(v[c][i], v[c][i], ss);
+              } else {
+                ss = fmaf(v[c][i], v[c][i], ss);
+              }
               mx = fmaxf(mx, fabsf(v[c][i]));
             }
-          ss += xor32f(ss);
+          if constexpr (SPLIT) {
+            ss += xor32f(ss);
+            so += xor32f(so);
+            so2[nb] = so;
+            nxv[nb] = sqrtf(ss);        // regular instance's norm
+            ss += so;
+          } else {
+            ss += xor32f(ss);
+          }
           mx = fmaxf(mx, xor32f(mx));
           // 2^(14 - floor(log2 mx)) from the exponent field of mx
           const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
@@ -486,10 +545,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           }
           wsc[nb] = 16.f * p2;
         }
-        nxv[nb] = sqrtf(ss);
-        // A zero vector encodes y = 0: thresholds and residual in unit scale.
-        sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
-        wsc[nb] *= sx[nb];
+        if constexpr (!SPLIT) {
+          nxv[nb] = sqrtf(ss);
+          // A zero vector encodes y = 0: thresholds and residual in unit scale.
+          sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
+          wsc[nb] *= sx[nb];
+        }
       }
 
       // boundaries scaled to the accumulator (uniform codec); prod: the
@@ -529,6 +590,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       }
       float zsmall[NB][4];
       float rsmall[NB][4];
+      // SPLIT: per group the factor between the accumulator and the unit
+      // vector (16 2^e times the group's norm; a zero group encodes y = 0)
+      float nxo[NB], rso[NB], rsr[NB], rro[NB], P2o[NB];
+      uint32_t p1w[NB];
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          nxo[nb] = sqrtf(so2[nb]);
+          const float wso = wsc[nb] * (nxo[nb] > 0.f ? nxo[nb] : 1.f);
+          const float wsr = wsc[nb] * (nxv[nb] > 0.f ? nxv[nb] : 1.f);
+          rso[nb] = 32.f / wso;
+          rsr[nb] = 32.f / wsr;
+          P2o[nb] = spl_t2 * wso;
+          rro[nb] = 0.f;
+          p1w[nb] = 0u;
+        }
+      }
 
 #pragma unroll 1
       for (int mb = 0; mb < 4; ++mb) {
@@ -575,7 +653,25 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             const float v = acc[nb][r];
             int idx = 0;
             float chat = 0.f;
-            if (UNIFORM && !COL) {
+            if constexpr (SPLIT) {
+              // registers 0..7 of half 0: outlier, 2 index bits (symmetric
+              // 4-level search: bit 1 = [v >= 0], bit 0 = [v >= 0] == [|v| >= t_2]);
+              // all others: regular, 1 bit = [v >= 0] (2 symmetric levels)
+              const bool pos = v >= 0.f;
+              const uint64_t mp = __ballot(pos);
+              if (r < 8) {
+                const bool big = fabsf(v) >= P2o[nb];
+                const uint64_t mm = __ballot(big);
+                constexpr uint64_t kHalf0 = 0x00000000ffffffffull;
+                cw[nb][0] = push_mask(cw[nb][0], (~(mp ^ mm) & kHalf0) | (mp & ~kHalf0));
+                p1w[nb] = push_mask(p1w[nb], mp);  // plane 1 (kept from half 0)
+                const float c = hh ? spl_c1 : (big ? spl_c3 : spl_c2);
+                chat = pos ? c : -c;
+              } else {
+                cw[nb][0] = push_mask(cw[nb][0], mp);
+                chat = pos ? spl_c1 : -spl_c1;
+              }
+            } else if (UNIFORM && !COL) {
               // row layout: the index bits go straight into the plane words
               if constexpr (SYM2) {
                 chat = quant2_sym_push(v, T[nb][2], C32[2], C32[3], cw[nb][0], cw[nb][NPL - 1]);
@@ -613,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
             if (!valid[nb]) idx = 0;
             if (!COL) {
-              if (!UNIFORM) {
+              if (!UNIFORM && !SPLIT) {
                 cw[nb][0] |= uint32_t(idx & 1) << r;
                 for (int p = 1; p < kMaxBits; ++p) {
                   const int pos = cv.bitpos[p * D + dim];
@@ -637,7 +733,17 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               const uint32_t w = group_or<VPD>(uint32_t(idx) << (UB * (j & (VPD - 1))));
               if ((r % VPD) == (j & (VPD - 1))) colkeep[nb][r / VPD] = w;
             }
-            if (MODE == 1) {
+            if (MODE == 1 && SPLIT) {
+              const bool og = r < 8 && !hh;
+              const float rsd = fmaf(v, og ? rso[nb] : rsr[nb], -chat);  // 32 (y - c), own group's unit
+              if (r < 8) {
+                rro[nb] = fmaf(rsd, og ? rsd : 0.f, rro[nb]);
+                rr[nb] = fmaf(rsd, og ? 0.f : rsd, rr[nb]);
+              } else {
+                rr[nb] = fmaf(rsd, rsd, rr[nb]);
+              }
+              acc[nb][r] = rsd;
+            } else if (MODE == 1) {
               const float rsd = fmaf(v, rs[nb], -chat);  // 32 (y - c) in unit scale
               rr[nb] = fmaf(rsd, rsd, rr[nb]);
               acc[nb][r] = rsd;
@@ -730,6 +836,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         const int slot = sub * 32 * NB + nb * 32 + j;
         if (MODE == 1) {
           rr[nb] += xor32f(rr[nb]);
+          if (SPLIT) rro[nb] += xor32f(rro[nb]);
           // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
 #pragma unroll
           for (int ms = 0; ms < 4; ++ms) {
@@ -755,7 +862,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         }
         // combine the two half-waves' bits (row layout)
         if (!COL) {
-          if (!UNIFORM) tailw[nb] |= xor32(tailw[nb]);
+          if (!UNIFORM && !SPLIT) tailw[nb] |= xor32(tailw[nb]);
           if (MODE == 1) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -763,7 +870,14 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               sw[nb][q] = mine | xor32(mine);
             }
           }
-          if (!UNIFORM) {
+          if constexpr (SPLIT) {
+            // plane 1 (4 bytes per vector, [64][4] at 64 * 16): bit 8 mb + r =
+            // bit 1 of outlier coordinate 8 mb + r; block mb's pushes sit in
+            // byte 3 - mb, hence the byte swap
+            const uint32_t mine = hh ? 0u : __builtin_bswap32(p1w[nb]);
+            const uint32_t w = valid[nb] ? (mine | xor32(mine)) : 0u;
+            *reinterpret_cast<uint32_t*>(trec + size_t(kTile) * 16 + size_t(slot) * 4) = w;
+          } else if (!UNIFORM) {
             const int tb = cv.code_bytes - 16;  // tail bytes per vector (1..4)
             for (int k = 0; k < tb; ++k)
               trec[size_t(kTile) * 16 + size_t(slot) * tb + k] = uint8_t(tailw[nb] >> (8 * k));
@@ -787,6 +901,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             // prod: rr sums (32 r)^2 in unit scale; SQ: r^2 in accumulator scale
             const float nr = !valid[nb] ? 0.f : (MODE == 1 ? sqrtf(rr[nb]) * (1.f / 32.f) : sqrtf(rr[nb]) / wsc[nb]);
             *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) = f16_bits(nr);
+          }
+          if constexpr (SPLIT) {  // the outlier instance's norms
+            *reinterpret_cast<uint16_t*>(trec + cv.off_nxo + 2 * slot) = f16_bits(valid[nb] ? nxo[nb] : 0.f);
+            if (MODE == 1)
+              *reinterpret_cast<uint16_t*>(trec + cv.off_nro + 2 * slot) =
+                  f16_bits(valid[nb] ? sqrtf(rro[nb]) * (1.f / 32.f) : 0.f);
           }
         }
       }
@@ -1090,12 +1210,12 @@ hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB>
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, bool SPLIT = false>
 hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
-  auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB>;
+  auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB, SPLIT>;
   size_t lds = size_t(2) * D * LDS_ROW * 2;
   if (MODE == 1) lds += size_t(D) * LDS_ROW * 2;
-  if (!UNIFORM) lds += size_t(2) * D * kMaxLevels * 4;
+  if (!UNIFORM && !SPLIT) lds += size_t(2) * D * kMaxLevels * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
@@ -1123,6 +1243,19 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
     // codecs; any other combination uses the dense Pi below
     if (cv.mode == TQ_MSE && col && cv.ubits == 4) return launch_had<0, true, 4>(cv, a, s);
     if (cv.mode == TQ_PROD && !col && cv.m == D && cv.ubits == 2) return launch_had<1, false, 2>(cv, a, s);
+  }
+  if (cv.outl) {
+    // outlier-channel split: 32 outlier coordinates at 2 index bits, the
+    // others at 1 (the 2.5-bit KV setting), row layout, full block sketch
+    if (col || cv.o4 != 8 || cv.split_ub_o != 2 || cv.split_ub_r != 1 || !cv.omask)
+      return hipErrorNotSupported;
+    if (cv.mode == TQ_PROD) {
+      if (cv.m != D) return hipErrorNotSupported;
+      return a.x_bf16 ? launch_one<1, true, 1, false, false, 1, true>(cv, a, s)
+                      : launch_one<1, false, 1, false, false, 1, true>(cv, a, s);
+    }
+    return a.x_bf16 ? launch_one<1, true, 0, false, false, 1, true>(cv, a, s)
+                    : launch_one<1, false, 0, false, false, 1, true>(cv, a, s);
   }
   if (!cv.uniform) {
     // SpectralQuant keys: row layout, small sketch

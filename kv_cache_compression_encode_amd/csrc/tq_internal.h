@@ -65,6 +65,8 @@ struct DeviceTables {
   // randomized Hadamard rotation at d = 128: per half h of the input (dims
   // 64h .. 64h + 63) and packed bf16 pair k, the sign bits (15 and 31) to flip
   uint32_t* had_mask = nullptr;  // [2][32]
+  // outlier-channel split: per head, bit c of the 128-bit mask = channel c is an outlier
+  uint32_t* omask = nullptr;     // [H][4]
 };
 
 }  // namespace tq
@@ -76,6 +78,8 @@ struct tq_codebook {
   int m = 0;
   bool uniform = true;
   int ubits = 0;  // index bits when uniform
+  int outlier = 0;  // o of an outlier-channel split codec (stored order), else 0
+  std::vector<uint32_t> omask;  // split: [H][d / 32] outlier-channel bit masks
   std::vector<uint8_t> bits;                 // [d]
   std::vector<double> rot64;                 // [H][d][d] (fp64 before rounding)
   std::vector<float> rot32;                  // [H][d][d]

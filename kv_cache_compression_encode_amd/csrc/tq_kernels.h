@@ -15,6 +15,11 @@ struct CodecView {
   int code_bytes, sign_bytes, tile_bytes;
   int off_signs, off_nx, off_nr;
   int tail_bits;  // ROW, non-uniform: index bits beyond plane 0 (<= 32)
+  // outlier-channel split (stored order): stored coordinate i belongs to the
+  // outlier instance when i % 32 < o4; its norms sit at off_nxo / off_nro
+  int outl, o4, off_nxo, off_nro;
+  const uint32_t* omask;       // split: [H][4] outlier-channel bit masks (bit c = channel c)
+  int split_ub_o, split_ub_r;  // index bits of the outlier / regular instance
   int sq_ok;      // non-uniform with 1 bit on dims 4.. and 1..5 bits on dims 0..3
   const float* rot;
   const float* rot_t;    // transpose of rot
@@ -77,7 +82,7 @@ struct QueryPrepArgs {
 hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStream_t s);
 
 hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
-                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s);
+                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s, int head = 0);
 
 struct DecodeArgs {
   const float* qr;     // [B][Hq][d]   (prepared queries; the MFMA kernel forms its own)

@@ -125,6 +125,13 @@ __device__ __forceinline__ int row_index_uniform(const uint8_t* tile, int slot, 
   return idx;
 }
 
+// Bit P of a vector's ROW bit string: chunk P / 128 of the tile is stored
+// [64 vectors][w] with w = 16 except for a shorter last chunk.
+__device__ __forceinline__ int row_bit(const uint8_t* tile, int slot, int P, int code_bytes) {
+  const int c = P >> 7, w = min(16, code_bytes - 16 * c);
+  return (tile[size_t(c) * kTile * 16 + size_t(slot) * w + ((P & 127) >> 3)] >> (P & 7)) & 1;
+}
+
 // ------------------------------------------------------------------ score
 // d = 128.  Block = 4 waves, each wave one record tile (lane = vector); QB
 // queries per block.  A lane loads its vector's record rows with 16-byte
@@ -134,12 +141,13 @@ __device__ __forceinline__ int row_index_uniform(const uint8_t* tile, int slot, 
 template <int QB>
 __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* qr, const float* qs,
                                                     int64_t nq, const uint8_t* rec, int64_t n,
-                                                    float* scores) {
+                                                    float* scores, int head) {
   static_assert(QB == 4, "four queries per block");
   constexpr int D = 128;
   __shared__ float4 sqr[D];        // [coordinate] -> QB queries
   __shared__ float4 sqs[D];        // [sketch row] -> QB queries
   __shared__ float scen[D * kMaxLevels];
+  __shared__ int16_t sbp[kMaxBits * D];  // split codecs: bit positions of the index bits
   const int m = cv.m;
   const int64_t q0 = int64_t(blockIdx.y) * QB;
   const int nqb = int(min<int64_t>(QB, nq - q0));
@@ -149,7 +157,10 @@ __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* q
     reinterpret_cast<float*>(sqs)[e] = (qq < nqb && i < m) ? qs[(q0 + qq) * m + i] : 0.f;
   }
   const int ncen = cv.uniform ? kMaxLevels : D * kMaxLevels;
-  for (int e = threadIdx.x; e < ncen; e += blockDim.x) scen[e] = cv.uniform ? cv.ucen[e] : cv.cen[e];
+  const float* hcen = cv.cen + size_t(head) * D * kMaxLevels;  // the head's per-dim levels
+  for (int e = threadIdx.x; e < ncen; e += blockDim.x) scen[e] = cv.uniform ? cv.ucen[e] : hcen[e];
+  if (cv.outl)
+    for (int e = threadIdx.x; e < kMaxBits * D; e += blockDim.x) sbp[e] = cv.bitpos[e];
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -168,6 +179,49 @@ __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* q
   if (!cv.uniform) {
     const int tb = cv.code_bytes - 16;  // 1..4 tail bytes
     for (int k = 0; k < tb; ++k) tail |= uint32_t(trec[size_t(kTile) * 16 + size_t(lane) * tb + k]) << (8 * k);
+  }
+  if (cv.outl) {
+    // outlier-channel split: stored coordinate 32 w + k belongs to the
+    // outlier instance for k < o4; each group has its own norms and QJL
+    // factor sqrt(pi/2) / m_g, m_g = the group's size
+    float4 ao = make_float4(0.f, 0.f, 0.f, 0.f), ar = ao, so = ao, sr = ao;
+    const u32x4 sg = cv.mode == TQ_PROD ? *reinterpret_cast<const u32x4*>(trec + cv.off_signs + size_t(lane) * 16)
+                                        : u32x4{0, 0, 0, 0};
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        const int dim = 32 * w + k;
+        int idx = int((pl[0][w] >> k) & 1u);
+        for (int p = 1; p < kMaxBits; ++p) {
+          const int pos = sbp[p * D + dim];
+          if (pos >= 0) idx |= row_bit(trec, lane, pos, cv.code_bytes) << p;
+        }
+        const float c = scen[dim * kMaxLevels + idx];
+        const bool og = k < cv.o4;
+        const float co = og ? c : 0.f, cr = c - co;
+        const float sgn = (sg[w] >> k) & 1u ? 1.f : -1.f;
+        const float go = og ? sgn : 0.f, gr = sgn - go;
+        const float4 q = sqr[dim], t = sqs[dim];
+        ao.x = fmaf(q.x, co, ao.x); ao.y = fmaf(q.y, co, ao.y); ao.z = fmaf(q.z, co, ao.z); ao.w = fmaf(q.w, co, ao.w);
+        ar.x = fmaf(q.x, cr, ar.x); ar.y = fmaf(q.y, cr, ar.y); ar.z = fmaf(q.z, cr, ar.z); ar.w = fmaf(q.w, cr, ar.w);
+        so.x = fmaf(t.x, go, so.x); so.y = fmaf(t.y, go, so.y); so.z = fmaf(t.z, go, so.z); so.w = fmaf(t.w, go, so.w);
+        sr.x = fmaf(t.x, gr, sr.x); sr.y = fmaf(t.y, gr, sr.y); sr.z = fmaf(t.z, gr, sr.z); sr.w = fmaf(t.w, gr, sr.w);
+      }
+    }
+    if (v >= n) return;
+    const auto h16 = [&](int off) { return f16_to_f32(*reinterpret_cast<const uint16_t*>(trec + off + 2 * lane)); };
+    const float nxr = h16(cv.off_nx), nxo = h16(cv.off_nxo);
+    const bool prod = cv.mode == TQ_PROD;
+    const float kr = prod ? h16(cv.off_nr) * kQjl / float(D - 4 * cv.o4) : 0.f;
+    const float ko = prod ? h16(cv.off_nro) * kQjl / float(4 * cv.o4) : 0.f;
+    const float out[4] = {nxo * (ao.x + ko * so.x) + nxr * (ar.x + kr * sr.x),
+                          nxo * (ao.y + ko * so.y) + nxr * (ar.y + kr * sr.y),
+                          nxo * (ao.z + ko * so.z) + nxr * (ar.z + kr * sr.z),
+                          nxo * (ao.w + ko * so.w) + nxr * (ar.w + kr * sr.w)};
+#pragma unroll
+    for (int qq = 0; qq < QB; ++qq)
+      if (qq < nqb) scores[(q0 + qq) * n + v] = out[qq];
+    return;
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -255,9 +309,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
   __shared__ float spw[4][G][kTile];
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sacc[4][G][D];
+  __shared__ int16_t sbp[kMaxBits * D];  // split keys: bit positions of the index bits
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int mk = kc.mode == TQ_PROD ? kc.m : 0;
+  if (kc.outl)
+    for (int e = threadIdx.x; e < kMaxBits * D; e += blockDim.x) sbp[e] = kc.bitpos[e];
   const int hk = kc.heads > 1 ? g : 0, hv = vc.heads > 1 ? g : 0;
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int gg = e / D, i = e % D;
@@ -293,6 +350,37 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
     const int tok = tile * kTile + lane;
     const bool valid = tok < len;
     // ---- scores (lane = token)
+    float sc[G];  // estimated <q, k> per query
+    if (kc.outl) {
+      // outlier-channel split: stored coordinate i is an outlier one when
+      // i % 32 < o4; each group has its own norms and QJL factor
+      float so[G], sr[G], go[G], gr[G];
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) so[gg] = sr[gg] = go[gg] = gr[gg] = 0.f;
+      for (int dim = 0; dim < D; ++dim) {
+        int idx = (kt[size_t(lane) * 16 + (dim >> 3)] >> (dim & 7)) & 1;
+        for (int p = 1; p < kMaxBits; ++p) {
+          const int pos = sbp[p * D + dim];
+          if (pos >= 0) idx |= row_bit(kt, lane, pos, kc.code_bytes) << p;
+        }
+        const float c = skcen[dim * kMaxLevels + idx];
+        const bool og = (dim & 31) < kc.o4;
+        float sgn = 0.f;
+        if (kc.mode == TQ_PROD) sgn = (kt[kc.off_signs + size_t(lane) * 16 + (dim >> 3)] >> (dim & 7)) & 1 ? 1.f : -1.f;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float qc = sqr[gg][dim] * c, qg = sqs[gg][dim] * sgn;
+          if (og) { so[gg] += qc; go[gg] += qg; } else { sr[gg] += qc; gr[gg] += qg; }
+        }
+      }
+      const auto h16 = [&](int off) { return f16_to_f32(*reinterpret_cast<const uint16_t*>(kt + off + 2 * lane)); };
+      const bool prod = kc.mode == TQ_PROD;
+      const float nxr = h16(kc.off_nx), nxo = h16(kc.off_nxo);
+      const float kr = prod ? h16(kc.off_nr) * kQjl / float(D - 4 * kc.o4) : 0.f;
+      const float ko = prod ? h16(kc.off_nro) * kQjl / float(4 * kc.o4) : 0.f;
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) sc[gg] = nxo * (so[gg] + ko * go[gg]) + nxr * (sr[gg] + kr * gr[gg]);
+    } else {
     float s[G], sg[G];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) s[gg] = sg[gg] = 0.f;
@@ -331,11 +419,14 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
       coef = f16_to_f32(*reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * lane)) * kQjl / float(mk);
     }
     const float nx = f16_to_f32(*reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * lane));
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) sc[gg] = nx * (s[gg] + coef * sg[gg]);
+    }
     const float nv = f16_to_f32(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * lane));
     // ---- online softmax
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      const float logit = valid ? a.scale * nx * (s[gg] + coef * sg[gg]) : -INFINITY;
+      const float logit = valid ? a.scale * sc[gg] : -INFINITY;
       const float mt = wave_max(logit);
       const float mnew = fmaxf(mrun[gg], mt);
       const float alpha = mrun[gg] == -INFINITY ? 0.f : __expf(mrun[gg] - mnew);
@@ -598,12 +689,13 @@ hipError_t launch_query_prep(const CodecView& cv, const QueryPrepArgs& a, hipStr
 }
 
 hipError_t launch_score(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
-                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s) {
+                        const uint8_t* rec, int64_t n, float* scores, hipStream_t s, int head) {
   constexpr int QB = 4;
   if (cv.d != 128 || cv.layout != TQ_LAYOUT_ROW || (cv.uniform && cv.ubits > kMaxBits)) return hipErrorNotSupported;
+  if (cv.outl && cv.mode == TQ_PROD && cv.m != 128) return hipErrorNotSupported;
   const int64_t ntiles = (n + kTile - 1) / kTile;
   dim3 grid(unsigned((ntiles + 3) / 4), unsigned((nq + QB - 1) / QB));
-  hipLaunchKernelGGL(score_kernel<QB>, grid, dim3(256), 0, s, cv, qr, qs, nq, rec, n, scores);
+  hipLaunchKernelGGL(score_kernel<QB>, grid, dim3(256), 0, s, cv, qr, qs, nq, rec, n, scores, head);
   return hipGetLastError();
 }
 

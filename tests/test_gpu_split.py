@@ -1,0 +1,204 @@
+"""Outlier-channel split codecs on the GPU against the CPU oracle (TurboQuant
+paper review, "Method": for the KV-cache experiments each channel group,
+outlier and regular, is quantized by its own TurboQuant instance; 32 channels
+at 3 bits + 96 at 2 bits is the 2.5-bit setting).  The outlier channels of
+each KV head are the 32 with the largest RMS over a seeded calibration
+sample of the synthetic KV law.  Every call goes through the C ABI."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_encode_amd as tq
+import synth
+from oracle import tq_oracle as o
+from tests.parity import check_encoded, check_scores
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def up(arr):
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(DEV)
+
+
+def outlier_channels(law, heads, o_=32, n=2048, seed=900):
+    """Per head the o_ channels of largest RMS over a calibration sample."""
+    out = []
+    for h in range(heads):
+        x = law.sample(h, n, torch.Generator().manual_seed(seed + h), "cpu").double()
+        rms = x.pow(2).mean(dim=0).sqrt().numpy()
+        out.append(np.argsort(-rms, kind="stable")[:o_])
+    return np.stack(out).astype(np.int32)
+
+
+def codecs(ch, bits=(3, 2), mode="prod", seeds=(211, 212)):
+    m = tq.TQ_PROD if mode == "prod" else tq.TQ_MSE
+    cb = tq.Codebook(128, m, bits[1], seed_rotation=seeds[0], seed_sketch=seeds[1], outlier_channels=ch,
+                     outlier_bits=bits[0])
+    sc = o.outlier_split_codec(128, ch, bits[0], bits[1], mode, rot_seed=seeds[0], sketch_seed=seeds[1])
+    return cb, sc
+
+
+def take(e, n):
+    return o.Encoded(e.idx[:n], None if e.signs is None else e.signs[:n], e.nx[:n],
+                     None if e.nr is None else e.nr[:n], None if e.y is None else e.y[:n],
+                     None if e.z is None else e.z[:n])
+
+
+def check_split(sc, ref, got):
+    return {"outlier": check_encoded(sc.inst_o, ref.o, got.o), "regular": check_encoded(sc.inst_r, ref.r, got.r)}
+
+
+@pytest.mark.parametrize("mode,dtype", [("prod", torch.bfloat16), ("prod", torch.float32),
+                                        ("mse", torch.bfloat16)])
+def test_split_encode(mode, dtype):
+    H, T = 2, 1000  # 16 tiles, a ragged last tile
+    say(f"split encode {mode} {dtype} H={H} T={T}")
+    law = synth.KVLaw(H, 128, 905)
+    X = synth.kv_cache(1, H, T, 128, 901, law)[0].to(dtype)
+    ch = outlier_channels(law, H)
+    cb, sc = codecs(ch, bits=(3, 2) if mode == "prod" else (2, 1), mode=mode)
+    buf = tq.encode(cb, X.to(DEV)).cpu().numpy()
+    per = cb.records_bytes(T)
+    assert per == ((T + 63) // 64) * o.split_tile_bytes(sc)
+    for h in range(H):
+        ref = o.split_encode(sc, X[h].double().numpy(), head=h)
+        got = o.split_unpack(sc, buf[h * per:(h + 1) * per], T)
+        say(h, check_split(sc, ref, got))
+        # the slots past T are zero: repacking what was read gives the same bytes
+        assert np.array_equal(o.split_pack(sc, got), buf[h * per:(h + 1) * per])
+
+
+def test_split_encode_zero_groups():
+    # a vector zero on one group: that group encodes y = 0 and stores n_x = 0
+    ch = np.arange(0, 128, 4, dtype=np.int32)[None]
+    cb, sc = codecs(ch)
+    x = torch.randn(70, 128, generator=torch.Generator().manual_seed(3))
+    x[3, ch[0]] = 0.0
+    reg = np.setdiff1d(np.arange(128), ch[0])
+    x[5, reg] = 0.0
+    x[7] = 0.0
+    got = o.split_unpack(sc, tq.encode(cb, x.to(DEV)).cpu().numpy(), 70)
+    assert float(got.o.nx[3]) == 0 and float(got.r.nx[5]) == 0
+    assert float(got.o.nx[7]) == 0 and float(got.r.nx[7]) == 0
+    s = tq.score(cb, torch.ones(1, 128, device=DEV), up(o.split_pack(sc, got)), 70).cpu().numpy()
+    assert s[0, 7] == 0.0
+
+
+def test_split_encode_unsupported_bits():
+    ch = np.arange(32, dtype=np.int32)[None]
+    cb, _ = codecs(ch, bits=(4, 3))
+    with pytest.raises(tq.TQError):
+        tq.encode(cb, torch.zeros(64, 128, device=DEV))
+
+
+@pytest.mark.parametrize("bits", [(3, 2), (4, 3), (2, 3)])
+def test_split_score(bits):
+    H, n, nq = 2, 777, 5
+    law = synth.KVLaw(H, 128, 915)
+    X = synth.kv_cache(1, H, n, 128, 911, law)[0].float()
+    q = synth.kv_queries(1, nq, 1, 128, 912, law)[0].float()
+    ch = outlier_channels(law, H)
+    cb, sc = codecs(ch, bits=bits)
+    for h in range(H):
+        ref = o.split_encode(sc, X[h].double().numpy(), head=h)
+        s = tq.score(cb, q.to(DEV), up(o.split_pack(sc, ref)), n, head=h).cpu().numpy()
+        want = o.split_score(sc, q.double().numpy(), ref, head=h)
+        nx = np.sqrt(ref.o.nx.astype(np.float64) ** 2 + ref.r.nx.astype(np.float64) ** 2)
+        say(bits, h, "max scaled error", check_scores(s, want, q.numpy(), nx))
+
+
+def test_split_topk():
+    n, nq, k = 5000, 6, 10
+    law = synth.KVLaw(1, 128, 925)
+    X = synth.kv_cache(1, 1, n, 128, 921, law)[0, 0].float()
+    q = synth.kv_queries(1, nq, 1, 128, 922, law)[0].float()
+    cb, sc = codecs(outlier_channels(law, 1))
+    ref = o.split_encode(sc, X.double().numpy())
+    s, i = tq.search_topk(cb, q.to(DEV), up(o.split_pack(sc, ref)), n, k)
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    full = o.split_score(sc, q.double().numpy(), ref)
+    rs, ri = o.topk(full, k)
+    for r in range(nq):
+        near = np.abs(full[r] - rs[r, -1]) <= 1e-3 * np.linalg.norm(q[r].numpy()) * np.max(np.abs(X.numpy()))
+        diff = set(i[r].tolist()) ^ set(ri[r].tolist())
+        assert all(near[j] for j in diff)
+        assert np.all(np.diff(s[r]) <= 0)
+
+
+def _decode(B, Hq, Hkv, T, seq_lens, kbits=(3, 2)):
+    law = synth.KVLaw(Hkv, 128, 935)
+    K = synth.kv_cache(B, Hkv, T, 128, 931, law)
+    V = synth.kv_cache(B, Hkv, T, 128, 932, law)
+    q = synth.kv_queries(B, Hq, Hkv, 128, 933, law)
+    kcb, sc = codecs(outlier_channels(law, Hkv), bits=kbits)
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=937, layout=tq.TQ_LAYOUT_COL)
+    vc = o.turboquant_codec(128, 4, "mse", rot_seed=937, layout="col")
+    ke = [[o.split_encode(sc, K[b, g].double().numpy(), head=g) for g in range(Hkv)] for b in range(B)]
+    ve = [[o.encode(vc, V[b, g].double().numpy()) for g in range(Hkv)] for b in range(B)]
+    kbuf = np.concatenate([o.split_pack(sc, e) for row in ke for e in row])
+    vbuf = np.concatenate([o.pack(vc, e) for row in ve for e in row])
+    scale = 1 / math.sqrt(128)
+    ref = np.zeros((B, Hq, 128))
+    for b in range(B):
+        L_ = seq_lens[b]
+        if L_ == 0:
+            continue
+        kk = [o.SplitEncoded(take(e.o, L_), take(e.r, L_)) for e in ke[b]]
+        vv = [take(e, L_) for e in ve[b]]
+        ref[b] = o.split_decode_attention(sc, vc, q[b].double().numpy(), kk, vv, scale)
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), up(kbuf), up(vbuf), T, Hkv, scale,
+                           seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=DEV)).cpu().numpy()
+    nvmax = max(float(np.max(e.nx.astype(np.float64))) for row in ve for e in row)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"split decode B={B} Hq={Hq} Hkv={Hkv} T={T} bits={kbits}: max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3
+
+
+def test_split_decode_gqa():
+    _decode(2, 8, 2, 700, [700, 129])
+
+
+def test_split_decode_other_bits():
+    _decode(1, 4, 1, 300, [300], kbits=(4, 3))
+
+
+@pytest.mark.parametrize("bits", [(3, 2), (4, 3)])
+def test_split_append(bits):
+    B, H, cap, steps = 3, 2, 200, 5
+    L0 = [0, 62, 128]
+    law = synth.KVLaw(H, 128, 945)
+    X = synth.kv_cache(B, H, cap, 128, 941, law)
+    cb, sc = codecs(outlier_channels(law, H), bits=bits)
+    full = {(b, h): o.split_encode(sc, X[b, h].double().numpy(), head=h) for b in range(B) for h in range(H)}
+    per = cb.records_bytes(cap)
+    rec = np.zeros(B * H * per, np.uint8)
+    for b in range(B):
+        for h in range(H):
+            if L0[b]:
+                p = o.split_pack(sc, o.SplitEncoded(take(full[b, h].o, L0[b]), take(full[b, h].r, L0[b])))
+                rec[(b * H + h) * per:(b * H + h) * per + len(p)] = p
+    rec = up(rec)
+    for s in range(steps):
+        pos = torch.tensor([L0[b] + s for b in range(B)], dtype=torch.int32, device=DEV)
+        tq.append(cb, torch.stack([X[b, :, L0[b] + s] for b in range(B)]).to(DEV), rec, pos, cap)
+    got_all = rec.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            n = L0[b] + steps
+            buf = got_all[(b * H + h) * per:(b * H + h + 1) * per]
+            got = o.split_unpack(sc, buf, n)
+            ref = o.SplitEncoded(take(full[b, h].o, n), take(full[b, h].r, n))
+            say(bits, b, h, check_split(sc, ref, got))
+            want = np.zeros(per, np.uint8)
+            p = o.split_pack(sc, got)
+            want[:len(p)] = p
+            assert np.array_equal(buf, want)

@@ -183,3 +183,51 @@ def test_argument_errors_before_launch():
     assert lib.tq_workspace_size(cb.handle, L.TQ_OP_SCORE, 4, 100, 0) >= 4 * 256 * 4
     assert lib.tq_codebook_free(None) == L.TQ_EINVAL
     assert lib.tq_status_string(L.TQ_EWORKSPACE) == b"workspace too small"
+
+
+@pytest.mark.parametrize("mode,bits,heads", [("prod", (3, 2), 1), ("prod", (3, 2), 2), ("mse", (3, 2), 1),
+                                             ("prod", (4, 3), 1)])
+def test_outlier_split_codebook_matches_oracle(mode, bits, heads):
+    # the library's stored-order codec (rotation rows on the channels,
+    # block-diagonal sketch, per-dim codebooks) against the oracle's two
+    # instances written out in the same order
+    rng = np.random.default_rng(heads + bits[0])
+    ch = np.stack([rng.permutation(128)[:32] for _ in range(heads)]).astype(np.int32)
+    m = tq.TQ_PROD if mode == "prod" else tq.TQ_MSE
+    cb = tq.Codebook(128, m, bits[1], seed_rotation=61, seed_sketch=62, outlier_channels=ch,
+                     outlier_bits=bits[0], device=-1)
+    sc = o.outlier_split_codec(128, ch, bits[0], bits[1], mode, rot_seed=61, sketch_seed=62)
+    st = o.split_stored_codec(sc)
+    assert cb.num_heads == heads and cb.info.outlier_dims == 32 and cb.info.outlier_per_block == 8
+    assert cb.tile_bytes == o.split_tile_bytes(sc)
+    fields = dict((f[0], f[1]) for f in o.split_tile_fields(sc))
+    assert cb.info.off_nx == fields["nx"] and cb.info.off_nx_o == fields["nx_o"]
+    if mode == "prod":
+        assert cb.info.off_nr == fields["nr"] and cb.info.off_nr_o == fields["nr_o"]
+        assert cb.info.off_signs == fields["sign0"]
+    for h in range(heads):
+        rot, sk, cen, thr, lv = cb.export(h)
+        n, mx = _ulp_mismatch(rot, st.rot[h].astype(np.float32))
+        assert mx <= 1 and n <= 4
+        assert np.array_equal(lv, 1 << st.bits)
+        for i in (0, 7, 8, 31, 32, 127):
+            L_ = 1 << int(st.bits[i])
+            assert np.allclose(cen[i, :L_], st.centroids[h][i], rtol=0, atol=1e-7)
+            assert np.allclose(thr[i, :L_ - 1], st.boundaries[h][i], rtol=0, atol=1e-7)
+        if mode == "prod":
+            n, mx = _ulp_mismatch(sk, st.sketch.astype(np.float32))
+            assert mx <= 1 and n <= 4
+
+
+def test_outlier_split_argument_errors():
+    ch = np.arange(32, dtype=np.int32)
+    with pytest.raises(tq.TQError):      # repeated channel
+        tq.Codebook(128, tq.TQ_PROD, 2, outlier_channels=np.r_[ch[:31], 0], outlier_bits=3, device=-1)
+    with pytest.raises(tq.TQError):      # channel out of range
+        tq.Codebook(128, tq.TQ_PROD, 2, outlier_channels=np.r_[ch[:31], 128], outlier_bits=3, device=-1)
+    with pytest.raises(tq.TQError):      # o must be 32, 64 or 96
+        tq.Codebook(128, tq.TQ_PROD, 2, outlier_channels=ch[:16], outlier_bits=3, device=-1)
+    with pytest.raises(tq.TQError):      # col layout
+        tq.Codebook(128, tq.TQ_MSE, 2, outlier_channels=ch, outlier_bits=3, layout=tq.TQ_LAYOUT_COL, device=-1)
+    with pytest.raises(tq.TQError):      # d = 128 only
+        tq.Codebook(256, tq.TQ_PROD, 2, outlier_channels=ch, outlier_bits=3, device=-1)
