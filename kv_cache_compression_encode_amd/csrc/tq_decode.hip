@@ -19,6 +19,14 @@
 // in plane 0 plus the tail byte) read a per-query LDS table of q'_i c_i(idx),
 // and the 4 QJL signs are a 4-term dot product on the VALU.
 //
+// Outlier-channel split keys (UB = 3): stored coordinates 32 g + s, s < 8,
+// are the outlier instance's (2 index bits, levels alpha s1 + beta s0); the
+// rest are regular (1 bit, c_1 s0).  In every MFMA of the chain chunk c = 0
+// holds exactly the outlier coordinates, so the outlier and regular parts
+// accumulate in two chains: plane 0 (4 chunks), plane 1 (its 32 bits: chunk 0
+// only) and the signs (4 chunks), 9 MFMAs per 16 keys; each part is then
+// scaled by its own group's norms and QJL factor.
+//
 // Values: TurboQuant-mse col records with 4 index bits: 8 consecutive tokens
 // of one coordinate are one dword; a 256-entry LDS table maps each byte (two
 // tokens) to the fp16 pair of their centroids, giving the B operand of
@@ -98,6 +106,7 @@ template <int G, int UB>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
   constexpr bool SQ = UB == 0;
+  constexpr bool SPL = UB == 3;  // outlier-channel split keys, 32 outlier coordinates
   __shared__ float sqr[4][D];
   __shared__ float sqs[4][D];
   __shared__ float slow[SQ ? 4 : 1][4][kMaxLevels];  // SQ: q'_i c_i(idx), dims 0..3
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
   const int t_begin = split * a.chunk_tiles;
   const int t_end = min(ntiles, t_begin + a.chunk_tiles);
-  constexpr int NP = SQ ? 1 : UB + 1;  // +-1 planes in the MFMA chain (incl. signs)
+  constexpr int NP = SQ ? 1 : (SPL ? 3 : UB + 1);  // +-1 planes in the MFMA chain (incl. signs)
   // ---- loads of one tile: key planes/signs (dword g16 of token 16nb+n),
   // value fields, fp16 norms (raw), SQ low/tail/sign bytes; the next tile's
   // loads are issued before the current tile is processed
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // four times the data of a dword load through the address unit.
   struct TileRegs {
     u32x4 kw4[NP], vw4[4];
-    uint32_t nx, nr, nv, tl, sg;
+    uint32_t nx, nr, nv, tl, sg, xo, ro;
   };
   TileRegs cur, nxt;
   auto load_tile = [&](int tile, TileRegs& R) {
@@ -148,7 +157,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     const int tok = 16 * g16 + n;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int off = SQ ? 0 : (p < UB ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
+      if (SPL && p == 1) {
+        // plane 1 of the split keys: one dword per token ([64][4] after plane 0)
+        R.kw4[1][0] = *reinterpret_cast<const uint32_t*>(kt + kTile * 16 + tok * 4);
+        continue;
+      }
+      const int off = SQ ? 0 : (p < (SPL ? 2 : UB) ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
       R.kw4[p] = *reinterpret_cast<const u32x4*>(kt + off + tok * 16);
     }
     // load j: dim 16 (2j + g16/2) + n, bytes 16 (g16 % 2) .. + 15 of its field
@@ -161,6 +175,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     if (SQ) {
       R.tl = kt[kTile * 16 + tok];
       R.sg = kt[kc.off_signs + tok];
+    }
+    if (SPL) {
+      R.xo = *reinterpret_cast<const uint16_t*>(kt + kc.off_nxo + 2 * tok);
+      R.ro = *reinterpret_cast<const uint16_t*>(kt + kc.off_nro + 2 * tok);
     }
   };
   TileRegs& ra = cur;
@@ -274,7 +292,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
 
   // ---- score A fragments: chunk (p, c): lane row r = n, dims 32 g16 + 8c + s
   float wp[2];
-  if (SQ) {
+  // split keys: outlier alpha, beta (dim 0's 4 levels), regular c_1 (dim 8)
+  float spl_a = 0.f, spl_b = 0.f, spl_c1 = 0.f;
+  if (SPL) {
+    const float* ce = kc.cen + size_t(hk) * D * kMaxLevels;
+    spl_a = 0.5f * (ce[3] + ce[2]);
+    spl_b = 0.5f * (ce[3] - ce[2]);
+    spl_c1 = ce[8 * kMaxLevels + 1];
+  }
+  if (SQ || SPL) {
     wp[0] = wp[1] = 0.f;
   } else if (UB == 2) {
     wp[0] = 0.5f * (kc.ucen[3] - kc.ucen[2]);
@@ -312,6 +338,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       if (gq < G) {
         if (SQ) {
           if (!rowsig && dim >= 4) x = sgam[dim] * sqr[gq][dim];
+        } else if (SPL) {
+          // plane 0: outlier beta / regular c_1; plane 1: outlier alpha (chunk 0)
+          if (!rowsig && p == 0) x = (c == 0 ? spl_b : spl_c1) * sqr[gq][dim];
+          if (!rowsig && p == 1 && c == 0) x = spl_a * sqr[gq][dim];
+          if (rowsig && sign_part) x = sqs[gq][dim];
         } else {
           if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
           if (rowsig && sign_part) x = sqs[gq][dim];
@@ -327,7 +358,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   }
   __syncthreads();
 
-  const float coef_scale = kQjl / float(kc.m);
+  // QJL factor sqrt(pi/2)/m; split keys: per group, m_g = 96 (regular) and 32
+  const float coef_scale = kQjl / float(SPL ? D - 32 : kc.m);
+  const float coef_scale_o = kQjl / 32.f;
   // SQ: the query whose table part this lane forms (see the score step)
   const int q_own = ((g16 & 1) << 1) | (g16 >> 1);
   const float* slow_own = &slow[SQ ? q_own : 0][0][0];
@@ -348,6 +381,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     uint32_t kw[4][NP], vw[8][2];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
+      if (SPL && p == 1) {
+        // replicated dword of token 16 g16 + n -> lane (n, g16) gets token
+        // 16 nb + n's dword; byte g16 of it holds block g16's 8 outlier bits
+        const uint32_t w1 = R.kw4[1][0];
+        const u32x4 t = transpose4(u32x4{w1, w1, w1, w1}, lane);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) kw[nb][1] = (t[nb] >> (8 * g16)) & 0xffu;
+        continue;
+      }
       const u32x4 t = transpose4(R.kw4[p], lane);
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) kw[nb][p] = t[nb];  // dword g16 of token 16 nb + n
@@ -360,15 +402,21 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       vw[2 * j + 1][0] = t[2];
       vw[2 * j + 1][1] = t[3];
     }
-    float nx[4], nr[4], nv[4];
+    float nx[4], nr[4], nv[4], nxo[4], nro[4];
     uint32_t sqb[4];  // SQ: plane-0 byte 0 | tail byte << 8 | sign byte << 16
     const uint32_t kpack = R.nx | (R.nr << 16);
+    const uint32_t opack = SPL ? (R.xo | (R.ro << 16)) : 0u;
     const uint32_t spack = SQ ? ((R.kw4[0][0] & 0xffu) | (R.tl << 8) | (R.sg << 16)) : 0u;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const uint32_t kk = uint32_t(__shfl(int(kpack), 16 * nb + n, 64));
       nx[nb] = h2f(uint16_t(kk & 0xffffu));
       nr[nb] = h2f(uint16_t(kk >> 16));
+      if (SPL) {
+        const uint32_t ko = uint32_t(__shfl(int(opack), 16 * nb + n, 64));
+        nxo[nb] = h2f(uint16_t(ko & 0xffffu));
+        nro[nb] = h2f(uint16_t(ko >> 16));
+      }
       nv[nb] = h2f(uint16_t(__shfl(int(R.nv), 16 * nb + n, 64)));
       sqb[nb] = SQ ? uint32_t(__shfl(int(spack), 16 * nb + n, 64)) : 0u;
     }
@@ -395,18 +443,41 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acco = f32x4{0.f, 0.f, 0.f, 0.f};  // split keys: outlier chain
+      if (SPL) {
+        acco = mfma16(A[0][0], spm[kw[nb][0] & 0xffu], acco);
+        acc = mfma16(A[0][1], spm[(kw[nb][0] >> 8) & 0xffu], acc);
+        acco = mfma16(A[1][0], spm[kw[nb][1]], acco);
+        acc = mfma16(A[0][2], spm[(kw[nb][0] >> 16) & 0xffu], acc);
+        acco = mfma16(A[2][0], spm[kw[nb][2] & 0xffu], acco);
+        acc = mfma16(A[0][3], spm[kw[nb][0] >> 24], acc);
+        acc = mfma16(A[2][1], spm[(kw[nb][2] >> 8) & 0xffu], acc);
+        acc = mfma16(A[2][2], spm[(kw[nb][2] >> 16) & 0xffu], acc);
+        acc = mfma16(A[2][3], spm[kw[nb][2] >> 24], acc);
+      } else {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        acc = mfma16(A[p][0], spm[kw[nb][p] & 0xffu], acc);
-        acc = mfma16(A[p][1], spm[(kw[nb][p] >> 8) & 0xffu], acc);
-        acc = mfma16(A[p][2], spm[(kw[nb][p] >> 16) & 0xffu], acc);
-        acc = mfma16(A[p][3], spm[kw[nb][p] >> 24], acc);
+        for (int p = 0; p < NP; ++p) {
+          acc = mfma16(A[p][0], spm[kw[nb][p] & 0xffu], acc);
+          acc = mfma16(A[p][1], spm[(kw[nb][p] >> 8) & 0xffu], acc);
+          acc = mfma16(A[p][2], spm[(kw[nb][p] >> 16) & 0xffu], acc);
+          acc = mfma16(A[p][3], spm[kw[nb][p] >> 24], acc);
+        }
       }
       const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
       const int tok = tile * kTile + 16 * nb + n;
       const bool valid = tok < len;
       const float coef = nr[nb] * coef_scale;
       float ta, tb;  // score parts beyond the MFMA rows of queries qa = 2 (g16 & 1), qb = qa + 1
+      if (SPL) {
+        // regular part n_x (code + coef sign) plus the outlier part with its own norms
+        const float oa = acco[0] + acco[1], ob = acco[2] + acco[3];
+        const float co = nro[nb] * coef_scale_o;
+        const float sa = nx[nb] * (xa + coef * xor32(xa, lane)) + nxo[nb] * (oa + co * xor32(oa, lane));
+        const float sb = nx[nb] * (xb + coef * xor32(xb, lane)) + nxo[nb] * (ob + co * xor32(ob, lane));
+        lg[nb][0] = valid ? a.scale * sa : -INFINITY;
+        lg[nb][1] = valid ? a.scale * sb : -INFINITY;
+        continue;
+      }
       if (SQ) {
         // dims 0..3 from the table, the mu part and the 4 signs, for one query
         // per lane (q_own), the partner query's part from the lane 32 away:
@@ -569,10 +640,17 @@ static bool sq_keys(const CodecView& kv) {
   return kv.sq_ok != 0;
 }
 
+// Outlier-split key codec the MFMA kernel handles: 32 outlier coordinates
+// (o4 = 8) with 2 index bits, the rest 1, full block sketch.
+static bool split_keys(const CodecView& kv) {
+  return kv.outl && kv.o4 == 8 && kv.split_ub_o == 2 && kv.split_ub_r == 1 && kv.mode == TQ_PROD &&
+         kv.m == D && kv.code_bytes == 20 && kv.layout == TQ_LAYOUT_ROW;
+}
+
 bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G) {
   const bool keys = kv.d == D && kv.layout == TQ_LAYOUT_ROW &&
                     ((kv.uniform && kv.mode == TQ_PROD && kv.m == D && (kv.ubits == 1 || kv.ubits == 2)) ||
-                     sq_keys(kv));
+                     sq_keys(kv) || split_keys(kv));
   return keys && vv.d == D && vv.uniform && vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL &&
          vv.ubits == 4 && (G == 1 || G == 2 || G == 4);
 }
@@ -582,7 +660,9 @@ hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const De
   const int G = a.Hq / a.Hkv;
   dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
 #define TQ_LAUNCH(GG, UU) hipLaunchKernelGGL((decode_mfma_kernel<GG, UU>), grid, dim3(256), 0, s, kv, vv, a)
-  if (!kv.uniform) {
+  if (kv.outl) {
+    if (G == 4) TQ_LAUNCH(4, 3); else if (G == 2) TQ_LAUNCH(2, 3); else TQ_LAUNCH(1, 3);
+  } else if (!kv.uniform) {
     if (G == 4) TQ_LAUNCH(4, 0); else if (G == 2) TQ_LAUNCH(2, 0); else TQ_LAUNCH(1, 0);
   } else if (kv.ubits == 2) {
     if (G == 4) TQ_LAUNCH(4, 2); else if (G == 2) TQ_LAUNCH(2, 2); else TQ_LAUNCH(1, 2);

@@ -168,7 +168,16 @@ def test_split_decode_gqa():
 
 
 def test_split_decode_other_bits():
+    # 3 index bits on the outlier channels: the general decode kernel
     _decode(1, 4, 1, 300, [300], kbits=(4, 3))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens", [(1, 2, 1, 300, [300]), (2, 4, 4, 1500, [1500, 777]),
+                                             (3, 16, 4, 200, [200, 1, 65])])
+def test_split_decode_mfma_shapes(B, Hq, Hkv, T, lens):
+    # 2.5-bit keys on the MFMA decode: group sizes 2, 1, 4; one split per
+    # sequence (fused epilogue) and several
+    _decode(B, Hq, Hkv, T, lens)
 
 
 @pytest.mark.parametrize("bits", [(3, 2), (4, 3)])
