@@ -9,7 +9,9 @@ compressed keys, softmax, .V over the compressed values).  Steps cycle over 8
 distinct layers so that inputs are streamed from HBM rather than the 256 MB
 Infinity Cache.  Reported value: keys per second through the whole step.
 
-Other workloads (--workload): small (4096 fp32 vectors, 16 queries),
+Other workloads (--workload): gqa_outlier (the same layer with 2.5-bit
+outlier-split keys: per KV head the 32 largest-RMS channels at 3 bits, the
+other 96 at 2 bits, two TurboQuant instances), small (4096 fp32 vectors, 16 queries),
 bulk_prefill (32 layers x 8 heads x 131072 tokens), sq_decode (SpectralQuant
 keys, 64 sequences x 8192 tokens), vector_search (1e6 x 1536 database, 1024
 queries, top-10).  Each prints one JSON line of the same shape.
@@ -34,6 +36,7 @@ D, HQ, HKV, T = 128, 32, 8, 32768
 NLAYERS = 8
 # Algorithmic bytes per vector: input row + record bytes (codes, signs, fp16 norms).
 K_REC, V_REC = 52, 66
+K_REC_SPLIT = 44                     # split keys: 16 + 4 code bytes, 16 sign bytes, 4 fp16 norms
 K_ENC_BYTES = 2 * D + K_REC          # 308 B per key
 V_ENC_BYTES = 2 * D + V_REC          # 322 B per value
 DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decode
@@ -51,7 +54,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="gqa_layer",
-                   choices=["gqa_layer", "small", "bulk_prefill", "sq_decode", "vector_search"])
+                   choices=["gqa_layer", "gqa_outlier", "small", "bulk_prefill", "sq_decode", "vector_search"])
     p.add_argument("--bits", type=int, default=2, help="vector_search: TurboQuant-prod bits (2 or 4)")
     p.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
                    help="gqa_layer / bulk_prefill: dense seeded Haar Pi (default) or the randomized "
@@ -110,6 +113,39 @@ def cpu_baseline_gqa():
     reps, el = _time_loop(run)
     return {"value": reps * n / el, "unit": "keys/s", "cores": _cores(), "kind": "oracle",
             "sample": f"1 kv head x {n} tokens (encode K+V, 4-head decode), {reps} reps in {el:.1f} s"}
+
+
+def outlier_channels(torch, law, heads, o_=32, n=2048, seed=900):
+    """Per KV head the o_ channels of largest RMS over n calibration tokens
+    (the split's channel lists, found once before the cache is built)."""
+    import numpy as np
+    out = []
+    for h in range(heads):
+        x = law.sample(h, n, torch.Generator().manual_seed(seed + h), "cpu").double()
+        out.append(np.argsort(-x.pow(2).mean(dim=0).sqrt().numpy(), kind="stable")[:o_])
+    return np.stack(out).astype(np.int32)
+
+
+def cpu_baseline_gqa_outlier():
+    """The oracle on a bounded sample: one KV head, 4096 tokens, split encode
+    of K, encode of V, then the 4 query heads' decode step."""
+    import torch
+    import synth
+    from oracle import tq_oracle as o
+    n = 4096
+    law = synth.KVLaw(1, D, 205)
+    k = synth.kv_cache(1, 1, n, D, 201, law)[0, 0].double().numpy()
+    v = synth.kv_cache(1, 1, n, D, 251, law)[0, 0].double().numpy()
+    q = synth.kv_queries(1, 4, 1, D, 202, law)[0].double().numpy()
+    kc = o.outlier_split_codec(D, outlier_channels(torch, law, 1), 3, 2, "prod", rot_seed=203, sketch_seed=204)
+    vc = o.turboquant_codec(D, 4, "mse", rot_seed=203, layout="col")
+
+    def run():
+        ke, ve = o.split_encode(kc, k), o.encode(vc, v)
+        o.split_decode_attention(kc, vc, q, [ke], [ve], 1 / math.sqrt(D))
+    reps, el = _time_loop(run)
+    return {"value": reps * n / el, "unit": "keys/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"1 kv head x {n} tokens (split encode K, encode V, 4-head decode), {reps} reps in {el:.1f} s"}
 
 
 def cpu_baseline_small():
@@ -268,15 +304,21 @@ def hbm_roof(name, ms, nbytes, note=None):
 
 
 # ------------------------------------------------------------ workloads
-def run_gqa_layer(args, torch, tq, synth):
+def run_gqa_layer(args, torch, tq, synth, split=False):
     dev = torch.device("cuda:0")
     law = synth.KVLaw(HKV, D, 205)
     K = [synth.kv_cache(1, HKV, T, D, 201 + 1000 * l, law, device=dev)[0] for l in range(NLAYERS)]
     V = [synth.kv_cache(1, HKV, T, D, 251 + 1000 * l, law, device=dev)[0] for l in range(NLAYERS)]
     q = synth.kv_queries(1, HQ, HKV, D, 202, law, device=dev)
-    kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204, **rot_kw(tq))
+    if split:
+        # 2.5-bit keys: per KV head 32 outlier channels at 3 bits, 96 at 2 bits
+        kcb = tq.Codebook(D, tq.TQ_PROD, 2, seed_rotation=203, seed_sketch=204,
+                          outlier_channels=outlier_channels(torch, law, HKV), outlier_bits=3)
+    else:
+        kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204, **rot_kw(tq))
     vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
-    assert kcb.tile_bytes == 64 * K_REC and vcb.tile_bytes == 64 * V_REC
+    k_rec = K_REC_SPLIT if split else K_REC
+    assert kcb.tile_bytes == 64 * k_rec and vcb.tile_bytes == 64 * V_REC
     krec = [torch.empty(HKV * kcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
     vrec = [torch.empty(HKV * vcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
     out = torch.empty(1, HQ, D, dtype=torch.float32, device=dev)
@@ -295,23 +337,30 @@ def run_gqa_layer(args, torch, tq, synth):
     append_ms = time_one(torch, lambda: (tq.append(kcb, kn, krec[0], pos, T), tq.append(vcb, vn, vrec[0], pos, T)),
                          args.steps, args.warmup)
     nk = HKV * T
-    nbytes = {"encode_keys": nk * K_ENC_BYTES, "encode_values": nk * V_ENC_BYTES,
-              "decode_attend": nk * DEC_BYTES}
+    nbytes = {"encode_keys": nk * (2 * D + k_rec), "encode_values": nk * V_ENC_BYTES,
+              "decode_attend": nk * (k_rec + V_REC)}
     dom = max(t, key=lambda k: t[k])
     bd = {k: {"ms": t[k], "GBps": nbytes[k] / (t[k] * 1e-3) / 1e9,
               "hbm_frac": nbytes[k] / (t[k] * 1e-3) / 1e9 / HBM_PEAK_GBS} for k in t}
+    keys_desc = ("K outlier-channel split, 2.5 bits (per KV head the 32 largest-RMS channels of a 2048-token "
+                 "calibration sample: TurboQuant-prod b=3; the other 96: b=2; row records, 44 B/key)"
+                 if split else "K TurboQuant-prod b=3 (row records)")
+    roof = hbm_roof(dom, t[dom], nbytes[dom])
+    if split:
+        roof["traffic"] = None  # counters were taken for the b=3 key kernels
     res = result(args, "compressed-key scoring keys/s & KV encode GB/s at d=128, % of HBM roofline",
                  nk / (ms_step * 1e-3), "keys/s", ms_step,
-                 {"workload": rot_note("gqa_decode_layer: 32 q / 8 kv heads, d=128, 32768 tokens, batch 1, "
-                                       "bf16 K/V; K TurboQuant-prod b=3 (row records), V TurboQuant-mse b=4 "
+                 {"workload": rot_note(("gqa_outlier" if split else "gqa_decode_layer") +
+                                       ": 32 q / 8 kv heads, d=128, 32768 tokens, batch 1, "
+                                       f"bf16 K/V; {keys_desc}, V TurboQuant-mse b=4 "
                                        "(col records); step = encode K + encode V + decode attention"),
                   "layers_cycled": NLAYERS},
-                 "f32 (split-f16 MFMA)", hbm_roof(dom, t[dom], nbytes[dom]), bd,
+                 "f32 (split-f16 MFMA)", roof, bd,
                  {"decode_keys_per_s": nk / (t["decode_attend"] * 1e-3),
                   "append_kv_ms": append_ms,
                   "encode_GBps": (nbytes["encode_keys"] + nbytes["encode_values"]) /
                   ((t["encode_keys"] + t["encode_values"]) * 1e-3) / 1e9})
-    return res, cpu_baseline_gqa
+    return res, (cpu_baseline_gqa_outlier if split else cpu_baseline_gqa)
 
 
 def run_small(args, torch, tq, synth):
@@ -466,7 +515,7 @@ def run_search(args, torch, tq, synth):
     return res, lambda: cpu_baseline_search(args.bits)
 
 
-DEFAULT_STEPS = {"gqa_layer": (50, 5), "small": (200, 10), "bulk_prefill": (10, 2), "sq_decode": (50, 5),
+DEFAULT_STEPS = {"gqa_layer": (50, 5), "gqa_outlier": (50, 5), "small": (200, 10), "bulk_prefill": (10, 2), "sq_decode": (50, 5),
                  "vector_search": (3, 1)}
 
 
@@ -490,7 +539,8 @@ def main():
     import torch
     import kv_cache_compression_encode_amd as tq
     import synth
-    run = {"gqa_layer": run_gqa_layer, "small": run_small, "bulk_prefill": run_bulk,
+    run = {"gqa_layer": run_gqa_layer, "small": run_small,
+           "gqa_outlier": lambda *a: run_gqa_layer(*a, split=True), "bulk_prefill": run_bulk,
            "sq_decode": run_sq, "vector_search": run_search}[args.workload]
     res, baseline = run(args, torch, tq, synth)
     if not args.no_cpu_baseline:

@@ -342,21 +342,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
     }
   }
   __syncthreads();
-  // SPLIT: outlier boundary t_2 and levels c_2, c_3 (dim 0), regular level
-  // c_1 (dim 8), and this half's outlier-channel mask (channels 64 hh ..)
-  float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f;
-  uint32_t om[2] = {0u, 0u};
-  if constexpr (SPLIT) {
-    const float* th = cv.thr + size_t(hc) * D * kMaxLevels;
-    const float* ce = cv.cen + size_t(hc) * D * kMaxLevels;
-    spl_t2 = th[2];
-    spl_c2 = 32.f * ce[2];
-    spl_c3 = 32.f * ce[3];
-    spl_c1 = 32.f * ce[8 * kMaxLevels + 1];
-    const int hf = int(threadIdx.x & 63) >> 5;
-    om[0] = cv.omask[hc * 4 + 2 * hf];
-    om[1] = cv.omask[hc * 4 + 2 * hf + 1];
-  }
 
   const int lane = lane_id();
   const int j = lane & 31, hh = lane >> 5;
@@ -404,6 +389,21 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       u32x4 xh[NB][8], xl[NB][8];
       float sx[NB], nxv[NB], wsc[NB];
       float so2[NB];  // SPLIT: sum of squares over this vector's outlier channels
+      // SPLIT: outlier boundary t_2 and levels c_2, c_3 (dim 0), regular
+      // level c_1 (dim 8), and this half's outlier-channel mask (channels
+      // 64 hh ..); read here, per tile, so that they stay in registers
+      float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f;
+      uint32_t om[2] = {0u, 0u};
+      if constexpr (SPLIT) {
+        const float* th = cv.thr + size_t(hc) * D * kMaxLevels;
+        const float* ce = cv.cen + size_t(hc) * D * kMaxLevels;
+        spl_t2 = th[2];
+        spl_c2 = 32.f * ce[2];
+        spl_c3 = 32.f * ce[3];
+        spl_c1 = 32.f * ce[8 * kMaxLevels + 1];
+        om[0] = cv.omask[hc * 4 + 2 * hh];
+        om[1] = cv.omask[hc * 4 + 2 * hh + 1];
+      }
       bool valid[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
