@@ -211,3 +211,37 @@ def test_split_append(bits):
             p = o.split_pack(sc, got)
             want[:len(p)] = p
             assert np.array_equal(buf, want)
+
+
+def test_gqa_outlier_full_size():
+    """The 2.5-bit split layer at its full size (32 q / 8 kv heads, 32768
+    tokens): every key's records against the oracle, then the decode step."""
+    Hq, Hkv, T = 32, 8, 32768
+    say("split full layer: generate")
+    law = synth.KVLaw(Hkv, 128, 205)
+    K = synth.kv_cache(1, Hkv, T, 128, 201, law)[0]
+    V = synth.kv_cache(1, Hkv, T, 128, 251, law)[0]
+    q = synth.kv_queries(1, Hq, Hkv, 128, 202, law)
+    kcb, sc = codecs(outlier_channels(law, Hkv), seeds=(203, 204))
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL)
+    vc = o.turboquant_codec(128, 4, "mse", rot_seed=203, layout="col")
+    say("split full layer: encode parity")
+    kb = tq.encode(kcb, K.to(DEV)).cpu().numpy()
+    per = kcb.records_bytes(T)
+    ke, ve, tot = [], [], 0
+    for h in range(Hkv):
+        ref = o.split_encode(sc, K[h].double().numpy(), head=h)
+        st = check_split(sc, ref, o.split_unpack(sc, kb[h * per:(h + 1) * per], T))
+        tot += sum(v["band_code_flips"] + v["band_sign_flips"] for v in st.values())
+        ke.append(ref)
+        ve.append(o.encode(vc, V[h].double().numpy()))
+    say("band flips", tot)
+    say("split full layer: decode parity")
+    scale = 1 / math.sqrt(128)
+    ref = o.split_decode_attention(sc, vc, q[0].double().numpy(), ke, ve, scale)
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), torch.from_numpy(kb).to(DEV),
+                           up(np.concatenate([o.pack(vc, e) for e in ve])), T, Hkv, scale).cpu().numpy()[0]
+    nvmax = max(float(np.max(e.nx.astype(np.float64))) for e in ve)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"split full layer decode: max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3
