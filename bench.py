@@ -460,6 +460,10 @@ def run_sq(args, torch, tq, synth):
     vn = torch.randn(B, H, D, generator=gen, device=dev).to(torch.bfloat16)
     append_ms = time_one(torch, lambda: (tq.append(kcb, kn, krec[0], pos, TT), tq.append(vcb, vn, vrec[0], pos, TT)),
                          args.steps, args.warmup)
+    # the SpectralQuant key encode of one cache, outside the step
+    K = synth.kv_cache(B, H, TT, D, 401, law, device=dev)
+    enc_ms = time_one(torch, lambda: tq.encode(kcb, K, records=krec[0]), 5, 1)
+    del K
     nk = B * H * TT
     nbytes = nk * (kper + vper) // TT
     res = result(args, "SpectralQuant batched decode token-heads/s, % of HBM roofline",
@@ -475,6 +479,8 @@ def run_sq(args, torch, tq, synth):
                  {"decode_attend": {"ms": t["decode_attend"], "bytes": nbytes}},
                  {"record_bytes_per_token_head": (kper + vper) / TT,
                   "append_kv_ms": append_ms,
+                  "encode_keys_ms": enc_ms,
+                  "encode_keys_GBps": nk * (2 * D + kper / TT) / (enc_ms * 1e-3) / 1e9,
                   "calibration_s": calib_s,
                   "calibration": "8 heads x 2048 tokens on the host: covariance, Jacobi eigenbasis, per-dim "
                                  "scales, Lloyd-Max codebooks, device upload",

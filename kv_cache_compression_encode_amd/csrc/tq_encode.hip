@@ -357,6 +357,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   // symmetric search paths: 16-level col codes (values), 4-level row codes
   constexpr bool SYM4 = UNIFORM && COL && UB == 4 && MODE == 0;
   constexpr bool SYM2 = UNIFORM && !COL && UB == 2;
+  // SpectralQuant key structure (non-uniform, MODE 2, UB = 2): dims 0..3 carry
+  // 1..5 bits, every other dim one bit
+  constexpr bool SQK = !UNIFORM && !SPLIT && MODE == 2 && UB == 2;
   const NibT nibc = nib_transpose_consts(int(threadIdx.x & 7));
 
   const int nwaves = blockDim.x >> 6;
@@ -698,6 +701,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 }
                 chat = lvl[0];
               }
+            } else if constexpr (SQK) {
+              if (mb == 0 && r < 4) {
+                // dims 0..3 (half 0) and 16..19 (half 1): branch-free binary
+                // search over the dim's 31 boundaries (unused ones are +inf),
+                // idx = number of boundaries <= v
+                const float* Tt = sThr + dim * kMaxLevels;
+                int k = 0;
+#pragma unroll
+                for (int st = 16; st >= 1; st >>= 1) k += v >= Tt[k + st - 1] * wsc[nb] ? st : 0;
+                idx = k;
+                chat = sCen[dim * kMaxLevels + k] * wsc[nb];
+              } else {
+                // one bit on every other dim: the 2-level boundary is 0, so the
+                // code is the sign; no level is needed (the residual covers
+                // dims < 4 only)
+                idx = v >= 0.f ? 1 : 0;
+              }
             } else {
               const int L = 1 << cv.dim_bits[dim];
               chat = sCen[dim * kMaxLevels] * wsc[nb];
@@ -709,7 +729,18 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
             if (!valid[nb]) idx = 0;
             if (!COL) {
-              if (!UNIFORM && !SPLIT) {
+              if (SQK) {
+                cw[nb][0] |= uint32_t(idx & 1) << r;
+                if (mb == 0 && r < 4) {
+                  // bits 1.. of dims 0..3 into the tail (half 1's dims have none)
+#pragma unroll
+                  for (int p = 1; p < kMaxBits; ++p) {
+                    const int pos = cv.bitpos[p * D + dim];
+                    const uint32_t bit = pos >= 0 ? uint32_t((idx >> p) & 1) : 0u;
+                    tailw[nb] |= bit << (pos >= 0 ? pos - D : 0);
+                  }
+                }
+              } else if (!UNIFORM && !SPLIT) {
                 cw[nb][0] |= uint32_t(idx & 1) << r;
                 for (int p = 1; p < kMaxBits; ++p) {
                   const int pos = cv.bitpos[p * D + dim];
@@ -1260,6 +1291,8 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
   if (!cv.uniform) {
     // SpectralQuant keys: row layout, small sketch
     if (col || cv.mode != TQ_PROD || cv.m > 4 || !a.x_bf16) return hipErrorNotSupported;
+    // UB = 2: the SpectralQuant structure (multi-bit dims 0..3 only)
+    if (cv.sq_ok) return launch_one<1, true, 2, false, false, 2>(cv, a, s);
     return launch_one<1, true, 2, false, false, 1>(cv, a, s);
   }
   const int mode = cv.mode == TQ_MSE ? 0 : (cv.m == D ? 1 : 2);
