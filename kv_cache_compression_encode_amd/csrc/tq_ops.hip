@@ -481,78 +481,107 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
 }
 
 // Merge of the splits and inverse value rotation: block (query head, b).
-// The split weights exp(m_s - M) are formed once in LDS; the accumulator
-// reads are independent loads, unrolled.
+// Up to 64 splits (the usual case) every load -- the split maxima and sums,
+// the partial accumulators and the rotation columns -- is issued at once, so
+// the kernel costs one memory round trip plus LDS reductions; more splits
+// take a loop over them.
 template <int G>
 __global__ __launch_bounds__(256) void decode_combine_kernel(CodecView vc, DecodeArgs a) {
   // One block per (sequence, query head): merge the split-K partials
-  // (log-sum-exp), then rotate back, out = Pi_v^T acc / l.  The 256 threads
-  // split the partials and the rotation's k range in two halves so that many
-  // loads are in flight (the grid is small for a single long sequence).
+  // (log-sum-exp), then rotate back, out = Pi_v^T acc / l.  Thread t takes
+  // coordinate i = t % 128 over half h = t / 128 of the splits and of the
+  // rotation's k range.
   constexpr int D = 128;
+  constexpr int kFast = 64;
   __shared__ float sy[2][D];
   __shared__ float sf[1024];
-  __shared__ float sred[4];
+  __shared__ float sred[8];
   const int hq = blockIdx.x, b = blockIdx.y;
   const int g = hq / G, gg = hq % G;
   const int stride = G * (2 + D);
   const float* part = a.part + (int64_t(b) * a.Hkv + g) * a.nsplit * stride;
-  const int t = threadIdx.x, i = t & (D - 1), half = t >> 7;
+  const int t = threadIdx.x, i = t & (D - 1), half = t >> 7, lane = t & 63, wv = t >> 6;
   const int ns = min(a.nsplit, 1024);
-  float M = -INFINITY;
-  for (int s2 = t; s2 < ns; s2 += 256) {
-    const float m = part[s2 * stride + gg];
-    sf[s2] = m;
-    M = fmaxf(M, m);
-  }
+  // rotation columns: out_i = sum_k Pi[k][i] y_k, k in this half
+  const int hv = vc.heads > 1 ? g : 0;
+  const float* rot = vc.rot + size_t(hv) * D * D + size_t(64 * half) * D + i;
+  float r[64];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((t & 63) == 0) sred[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
-  float lpart = 0.f;
-  for (int s2 = t; s2 < ns; s2 += 256) {
-    const float f = sf[s2] == -INFINITY ? 0.f : __expf(sf[s2] - M);
-    sf[s2] = f;
-    lpart += f * part[s2 * stride + G + gg];
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o, 64);
-  __syncthreads();
-  if ((t & 63) == 0) sred[t >> 6] = lpart;
-  __syncthreads();
-  const float l = sred[0] + sred[1] + sred[2] + sred[3];
-  // weighted sum of the partial accumulators: half h takes splits h, h + 2, ...
-  float accv = 0.f;
+  for (int u = 0; u < 64; ++u) r[u] = rot[size_t(u) * D];
   const float* pa = part + 2 * G + gg * D + i;
-  int s2 = half;
-  for (; s2 + 30 < ns; s2 += 32) {
-    float v[16];
+  float accv = 0.f, M, l;
+  if (ns <= kFast) {
+    // wave 0: split maxima; wave 1: split sums; every thread: its half's
+    // accumulator entries (splits half, half + 2, ...)
+    const float mv = (wv == 0 && lane < ns) ? part[lane * stride + gg] : -INFINITY;
+    const float lv = (wv == 1 && lane < ns) ? part[lane * stride + G + gg] : 0.f;
+    float v[kFast / 2];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = pa[(s2 + 2 * u) * stride];
+    for (int u = 0; u < kFast / 2; ++u) v[u] = half + 2 * u < ns ? pa[(half + 2 * u) * stride] : 0.f;
+    float m = mv;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) accv = fmaf(sf[s2 + 2 * u], v[u], accv);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (t == 0) sred[0] = m;
+    __syncthreads();
+    M = sred[0];
+    // weights exp(m_s - M) of the splits (a split without tokens has m = -inf)
+    if (wv == 0) {
+      const float f = mv == -INFINITY ? 0.f : __expf(mv - M);
+      sf[lane] = f;
+    }
+    __syncthreads();
+    if (wv == 1) {
+      float lp = sf[lane] * lv;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) lp += __shfl_xor(lp, o, 64);
+      if (lane == 0) sred[1] = lp;
+    }
+#pragma unroll
+    for (int u = 0; u < kFast / 2; ++u) accv = fmaf(sf[(half + 2 * u) & (kFast - 1)], v[u], accv);
+    __syncthreads();
+    l = sred[1];
+  } else {
+    float mx = -INFINITY;
+    for (int s2 = t; s2 < ns; s2 += 256) {
+      const float m = part[s2 * stride + gg];
+      sf[s2] = m;
+      mx = fmaxf(mx, m);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) sred[wv] = mx;
+    __syncthreads();
+    M = fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]));
+    float lpart = 0.f;
+    for (int s2 = t; s2 < ns; s2 += 256) {
+      const float f = sf[s2] == -INFINITY ? 0.f : __expf(sf[s2] - M);
+      sf[s2] = f;
+      lpart += f * part[s2 * stride + G + gg];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) lpart += __shfl_xor(lpart, o, 64);
+    __syncthreads();
+    if (lane == 0) sred[4 + wv] = lpart;
+    __syncthreads();
+    l = sred[4] + sred[5] + sred[6] + sred[7];
+    int s2 = half;
+    for (; s2 + 30 < ns; s2 += 32) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = pa[(s2 + 2 * u) * stride];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) accv = fmaf(sf[s2 + 2 * u], v[u], accv);
+    }
+    for (; s2 < ns; s2 += 2) accv = fmaf(sf[s2], pa[s2 * stride], accv);
   }
-  for (; s2 < ns; s2 += 2) accv = fmaf(sf[s2], pa[s2 * stride], accv);
   sy[half][i] = accv;
   __syncthreads();
   if (half == 0) sy[0][i] = l > 0.f ? (sy[0][i] + sy[1][i]) / l : 0.f;
   __syncthreads();
-  // out_i = sum_k Pi[k][i] y_k, k range split between the halves
-  const int hv = vc.heads > 1 ? g : 0;
-  const float* rot = vc.rot + size_t(hv) * D * D + size_t(64 * half) * D + i;
   const float* yk = sy[0] + 64 * half;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k0 = 0; k0 < 64; k0 += 32) {
-    float r[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) r[u] = rot[size_t(k0 + u) * D];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) o[u & 3] = fmaf(r[u], yk[k0 + u], o[u & 3]);
-  }
-  __syncthreads();
-  sy[1][i] = 0.f;
+  for (int u = 0; u < 64; ++u) o[u & 3] = fmaf(r[u], yk[u], o[u & 3]);
   __syncthreads();
   if (half == 1) sy[1][i] = (o[0] + o[1]) + (o[2] + o[3]);
   __syncthreads();
