@@ -174,6 +174,12 @@ def test_decode_attend_spectralquant():
     _decode_case(2, 8, 2, 500, sq=True)
 
 
+def test_decode_attend_many_splits():
+    # one sequence and one KV head over 70000 tokens: 137 splits of 8 tiles,
+    # more than the merge kernel takes in one round of loads
+    _decode_case(1, 4, 1, 70000, seq_lens=[70000 - 37])
+
+
 def test_encode_spectralquant():
     Hkv, T = 2, 700
     law = synth.KVLaw(Hkv, 128, 405)
