@@ -277,9 +277,17 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
                    const void* records, int64_t n, float* scores, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Compressed KV cache of one layer, records as written by tq_encode.  Set
- * (b, h) of the keys starts at k_records + b*k_stride_seq + h*k_stride_head
- * bytes; likewise for values. */
+/* Compressed KV cache of one layer, records as written by tq_encode.
+ * Contiguous layout (block_table NULL): set (b, h) of the keys starts at
+ * k_records + b*k_stride_seq + h*k_stride_head bytes; likewise for values.
+ * Paged layout (block_table non-NULL): k_records and v_records are pools of
+ * pages, each page_tiles record tiles (64 tokens per tile) of the codec; tile
+ * t of set (b, h) is tile t % page_tiles of page
+ * block_table[(b*Hkv + h)*max_pages + t / page_tiles] (a page index into the
+ * pool; keys and values use the same index in their own pools) and the
+ * strides are not used.  A page holds whole tiles, so tq_encode can fill it
+ * directly (records = the page, tokens = a multiple of 64 * page_tiles, or
+ * the set's tail). */
 typedef struct {
   const void* k_records;
   const void* v_records;
@@ -287,6 +295,9 @@ typedef struct {
   int64_t v_stride_seq, v_stride_head;
   int32_t max_tokens;         /* tokens stored per (b, h)                       */
   const int32_t* seq_lens;    /* device [B] valid tokens per sequence, or NULL  */
+  const int32_t* block_table; /* device [B*Hkv][max_pages] page indices, or NULL */
+  int32_t page_tiles;         /* tiles per page (paged layout), >= 1            */
+  int32_t max_pages;          /* entries per (b, h) row of block_table          */
 } tq_kv_view;
 
 /* One decode step of grouped-query attention over a compressed cache ([TQ]
@@ -302,6 +313,26 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
                            int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
                            const tq_kv_view* kv, float softmax_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* One decode step with append-on-decode (TurboQuant paper review,
+ * "Comparison": the tokens generated during decoding are quantized too):
+ * the new key and value of every (sequence, KV head) are encoded into slot
+ * seq_lens[b] of its records (as tq_append), then the step attends over
+ * seq_lens[b] + 1 tokens (as tq_decode_attend).  seq_lens is required and is
+ * not changed (the caller advances it); a sequence whose slot seq_lens[b] is
+ * not below max_tokens gets no new token and attends over max_tokens.
+ *   k_new, v_new  device [B][Hkv][d] of new_dtype (TQ_F32 or TQ_BF16), rows
+ *            contiguous.
+ *   kv       contiguous or paged view; its records are written (the new
+ *            slots only), so they must be device memory the caller owns.
+ * The codecs, q, out and workspace are as for tq_decode_attend; the key and
+ * value codecs must also be ones tq_append supports.  Errors: those of
+ * tq_decode_attend and tq_append, and TQ_EINVAL when seq_lens is NULL. */
+tq_status tq_decode_step(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                         int32_t q_dtype, const void* k_new, const void* v_new, int32_t new_dtype,
+                         int32_t B, int32_t Hq, int32_t Hkv, const tq_kv_view* kv,
+                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Top-k inner-product search over n ROW records ([TQ] "Validation": vector
  * search with TurboQuant codes).  For each query the k largest scores

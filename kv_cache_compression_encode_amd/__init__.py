@@ -17,7 +17,8 @@ from . import _lib as L
 from ._lib import (TQ_BF16, TQ_F32, TQ_LAYOUT_COL, TQ_LAYOUT_ROW, TQ_MSE, TQ_PROD,
                    TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_TILE, TQError)
 
-__all__ = ["Codebook", "encode", "append", "score", "decode_attend", "search_topk", "water_fill", "TQError",
+__all__ = ["Codebook", "encode", "append", "score", "decode_attend", "decode_step", "search_topk", "water_fill",
+           "TQError",
            "TQ_MSE", "TQ_PROD", "TQ_LAYOUT_ROW", "TQ_LAYOUT_COL", "TQ_ROT_HAAR",
            "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_ROT_HADAMARD", "TQ_TILE"]
 
@@ -198,22 +199,36 @@ class DecodeWorkspace:
         self.buf = torch.empty(max(self.bytes, 16), dtype=torch.uint8, device=device)
 
 
+def _kv_view(kcb, vcb, k_records, v_records, max_tokens, hkv, seq_lens, k_strides, v_strides,
+             block_table, page_tiles):
+    kper, vper = kcb.records_bytes(max_tokens), vcb.records_bytes(max_tokens)
+    ks = k_strides or (hkv * kper, kper)
+    vs = v_strides or (hkv * vper, vper)
+    bt, mp = None, 0
+    if block_table is not None:
+        block_table = block_table.to(dtype=torch.int32).contiguous()
+        bt, mp = block_table.data_ptr(), block_table.shape[-1]
+    view = L.KVView(k_records.data_ptr(), v_records.data_ptr(), ks[0], ks[1], vs[0], vs[1],
+                    max_tokens, seq_lens.data_ptr() if seq_lens is not None else None, bt, page_tiles, mp)
+    return view, block_table
+
+
 def decode_attend(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_records: torch.Tensor,
                   v_records: torch.Tensor, max_tokens: int, hkv: int, scale: float,
                   seq_lens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                   workspace: Optional[DecodeWorkspace] = None,
-                  k_strides=None, v_strides=None) -> torch.Tensor:
+                  k_strides=None, v_strides=None, block_table: Optional[torch.Tensor] = None,
+                  page_tiles: int = 1) -> torch.Tensor:
     """One decode step of GQA attention over compressed K/V records.
 
     q: [B][Hq][d] (fp32 or bf16).  Records of (b, g) are at b*Hkv*per + g*per
-    unless strides (seq, head) in bytes are given."""
+    unless strides (seq, head) in bytes are given; with block_table
+    ([B*Hkv][max_pages] int32) the records are pools of pages of page_tiles
+    tiles."""
     B, Hq, d = q.shape
     q = q.contiguous()
-    kper, vper = kcb.records_bytes(max_tokens), vcb.records_bytes(max_tokens)
-    ks = k_strides or (hkv * kper, kper)
-    vs = v_strides or (hkv * vper, vper)
-    view = L.KVView(k_records.data_ptr(), v_records.data_ptr(), ks[0], ks[1], vs[0], vs[1],
-                    max_tokens, seq_lens.data_ptr() if seq_lens is not None else None)
+    view, _bt = _kv_view(kcb, vcb, k_records, v_records, max_tokens, hkv, seq_lens, k_strides, v_strides,
+                         block_table, page_tiles)
     if out is None:
         out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
     if workspace is None:
@@ -222,6 +237,32 @@ def decode_attend(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_records: torc
                                      hkv, ctypes.byref(view), scale, out.data_ptr(),
                                      workspace.buf.data_ptr(), workspace.bytes, _stream(q.device)),
             "tq_decode_attend")
+    return out
+
+
+def decode_step(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                k_records: torch.Tensor, v_records: torch.Tensor, max_tokens: int, hkv: int, scale: float,
+                seq_lens: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[DecodeWorkspace] = None, k_strides=None, v_strides=None,
+                block_table: Optional[torch.Tensor] = None, page_tiles: int = 1) -> torch.Tensor:
+    """Append k_new / v_new ([B][Hkv][d]) at slot seq_lens[b] of each
+    (sequence, KV head), then attend over seq_lens[b] + 1 tokens (seq_lens is
+    not changed).  Other arguments as for decode_attend."""
+    B, Hq, d = q.shape
+    q = q.contiguous()
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must have the same dtype")
+    k_new, v_new = k_new.contiguous(), v_new.contiguous()
+    view, _bt = _kv_view(kcb, vcb, k_records, v_records, max_tokens, hkv, seq_lens, k_strides, v_strides,
+                         block_table, page_tiles)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = DecodeWorkspace(kcb, B * Hq, max_tokens, hkv, q.device)
+    L.check(L.lib().tq_decode_step(kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), k_new.data_ptr(),
+                                   v_new.data_ptr(), _dtype_code(k_new), B, Hq, hkv, ctypes.byref(view), scale,
+                                   out.data_ptr(), workspace.buf.data_ptr(), workspace.bytes,
+                                   _stream(q.device)), "tq_decode_step")
     return out
 
 

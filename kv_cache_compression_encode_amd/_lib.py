@@ -16,7 +16,7 @@ TQ_TILE = 64
 TQ_MAX_LEVELS = 32
 
 EXPORTED = ["tq_codebook_build", "tq_codebook_free", "tq_water_fill", "tq_append", "tq_codebook_get_info", "tq_codebook_export",
-            "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_search_topk",
+            "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_decode_step", "tq_search_topk",
             "tq_workspace_size", "tq_status_string"]
 
 
@@ -49,7 +49,9 @@ class KVView(ctypes.Structure):
     _fields_ = [("k_records", ctypes.c_void_p), ("v_records", ctypes.c_void_p),
                 ("k_stride_seq", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
                 ("v_stride_seq", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
-                ("max_tokens", ctypes.c_int32), ("seq_lens", ctypes.c_void_p)]
+                ("max_tokens", ctypes.c_int32), ("seq_lens", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("page_tiles", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,6 +83,9 @@ def lib() -> ctypes.CDLL:
     L.tq_decode_attend.argtypes = [p, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),
                                    ctypes.c_float, p, p, sz, p]
     L.tq_decode_attend.restype = i32
+    L.tq_decode_step.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),
+                                 ctypes.c_float, p, p, sz, p]
+    L.tq_decode_step.restype = i32
     L.tq_search_topk.argtypes = [p, p, i64, p, i64, i32, p, p, p, sz, p]
     L.tq_search_topk.restype = i32
     L.tq_workspace_size.argtypes = [p, i32, i64, i64, i64]

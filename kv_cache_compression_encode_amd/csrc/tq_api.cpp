@@ -597,7 +597,7 @@ tq_status tq_append(const tq_codebook* cb, const void* x, int32_t x_dtype, int32
   if (B > 65535 || H > 65535) return TQ_EUNSUPPORTED;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   AppendArgs a{x, x_dtype == TQ_BF16, B, H, xs_b, xs_h, static_cast<uint8_t*>(records), rs_b, rs_h,
-               positions, capacity};
+               positions, capacity, nullptr, 0, 0};
   return map_hip(launch_append(cv, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -756,10 +756,29 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   return map_hip(launch_score(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, scores, s, head));
 }
 
-tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
-                           int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
-                           const tq_kv_view* kv, float softmax_scale, float* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a paged view (see tq_kv_view): power-of-two pages, a block table
+// row long enough for max_tokens, 4-byte aligned table.
+tq_status check_paging(const tq_kv_view* kv, int* page_shift) {
+  *page_shift = 0;
+  if (!kv->block_table) return TQ_OK;
+  const int pt = kv->page_tiles;
+  if (pt < 1 || (pt & (pt - 1)) || pt > (1 << 20)) return TQ_EINVAL;
+  while ((1 << *page_shift) < pt) ++*page_shift;
+  const int64_t ntiles = (int64_t(kv->max_tokens) + kTile - 1) / kTile;
+  if (int64_t(kv->max_pages) * pt < ntiles) return TQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(kv->block_table) & 3) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+// Decode attention over seq_lens[b] + len_add tokens (see tq_decode_attend).
+tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, int32_t q_dtype,
+                      int32_t B, int32_t Hq, int32_t Hkv, const tq_kv_view* kv, float softmax_scale,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream, int len_add,
+                      bool checks_only) {
   if (!kcb || !vcb || !q || !kv || !out || !kv->k_records || !kv->v_records) return TQ_EINVAL;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || kv->max_tokens < 0) return TQ_EINVAL;
@@ -777,12 +796,15 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   if (!aligned16(kv->k_records) || !aligned16(kv->v_records) || kv->k_stride_seq % 16 ||
       kv->k_stride_head % 16 || kv->v_stride_seq % 16 || kv->v_stride_head % 16 || !aligned16(q))
     return TQ_EALIGN;
+  int page_shift = 0;
+  if (const tq_status ps = check_paging(kv, &page_shift); ps != TQ_OK) return ps;
   if (B == 0) return TQ_OK;
   if (B > 65535 || decode_nsplit(kv->max_tokens) > 1024) return TQ_EUNSUPPORTED;
   const int64_t nqt = int64_t(B) * Hq;
   if (!workspace || workspace_bytes < tq_workspace_size(kcb, TQ_OP_DECODE, nqt, kv->max_tokens, Hkv))
     return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
+  if (checks_only) return TQ_OK;
   if (hipSetDevice(kcb->device) != hipSuccess) return TQ_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const CodecView kc = make_view(kcb), vc = make_view(vcb);
@@ -815,6 +837,10 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   da.max_tokens = kv->max_tokens;
   da.seq_lens = kv->seq_lens;
   da.scale = softmax_scale;
+  da.len_add = len_add;
+  da.block_table = kv->block_table;
+  da.page_shift = page_shift;
+  da.max_pages = kv->max_pages;
   // splits of 8 tiles, widened while the grid still fills every resident
   // workgroup slot (two per CU): fewer block set-ups and partials for large
   // batches, down to one split per sequence (then no merge pass at all);
@@ -834,6 +860,55 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
   da.part = part;
   da.out = out;
   return map_hip(launch_decode(kc, vc, da, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                           int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                           const tq_kv_view* kv, float softmax_scale, float* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace, workspace_bytes,
+                     stream, 0, false);
+}
+
+tq_status tq_decode_step(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                         int32_t q_dtype, const void* k_new, const void* v_new, int32_t new_dtype,
+                         int32_t B, int32_t Hq, int32_t Hkv, const tq_kv_view* kv,
+                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!kv || !kv->seq_lens || !k_new || !v_new) return TQ_EINVAL;
+  if (new_dtype != TQ_F32 && new_dtype != TQ_BF16) return TQ_EINVAL;
+  // every check of both parts runs before anything is launched
+  tq_status st = decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace,
+                             workspace_bytes, stream, 1, true);
+  if (st != TQ_OK || B == 0) return st;
+  if (kcb->info.num_heads > 1 && kcb->info.num_heads != Hkv) return TQ_EINVAL;
+  const CodecView kc = make_view(kcb), vc = make_view(vcb);
+  if (!append_supported(kc) || !append_supported(vc)) return TQ_EUNSUPPORTED;
+  if ((kv->k_stride_seq & 3) || (kv->k_stride_head & 3) || (kv->v_stride_seq & 3) || (kv->v_stride_head & 3))
+    return TQ_EALIGN;
+  if (B > 65535 || Hkv > 65535) return TQ_EUNSUPPORTED;
+  int page_shift = 0;
+  check_paging(kv, &page_shift);
+  if (hipSetDevice(kcb->device) != hipSuccess) return TQ_EDEVICE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t d = kcb->desc.d;
+  // the new tokens go to slot seq_lens[b]; slots at or past max_tokens are skipped
+  AppendArgs ka{k_new, new_dtype == TQ_BF16, B, Hkv, Hkv * d, d,
+                static_cast<uint8_t*>(const_cast<void*>(kv->k_records)), kv->k_stride_seq, kv->k_stride_head,
+                kv->seq_lens, kv->max_tokens, kv->block_table, page_shift, kv->max_pages};
+  AppendArgs va = ka;
+  va.x = v_new;
+  va.rec = static_cast<uint8_t*>(const_cast<void*>(kv->v_records));
+  va.rs_b = kv->v_stride_seq;
+  va.rs_h = kv->v_stride_head;
+  if ((st = map_hip(launch_append(kc, ka, s))) != TQ_OK) return st;
+  if ((st = map_hip(launch_append(vc, va, s))) != TQ_OK) return st;
+  return decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace, workspace_bytes,
+                     stream, 1, false);
 }
 
 tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,

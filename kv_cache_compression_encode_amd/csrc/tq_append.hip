@@ -99,8 +99,13 @@ __global__ __launch_bounds__(64) void append_kernel(CodecView cv, AppendArgs a) 
     idx[u] = k;
     res[u] = i < cv.m ? y[u] - cv.cen[(size_t(hc) * D + i) * kMaxLevels + k] : 0.f;
   }
-  const int slot = pos % kTile;
-  uint8_t* trec = a.rec + int64_t(b) * a.rs_b + int64_t(h) * a.rs_h + int64_t(pos / kTile) * cv.tile_bytes;
+  const int slot = pos % kTile, tile = pos / kTile;
+  uint8_t* trec;
+  if (a.block_table) {
+    trec = a.rec + paged_tile(a.block_table, a.page_shift, a.max_pages, int64_t(b) * a.H + h, tile) * cv.tile_bytes;
+  } else {
+    trec = a.rec + int64_t(b) * a.rs_b + int64_t(h) * a.rs_h + int64_t(tile) * cv.tile_bytes;
+  }
 
   // ---- codes
   if (cv.layout == TQ_LAYOUT_ROW) {

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g16 = lane >> 4;
-  const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
+  const int len = a.seq_lens ? min(a.seq_lens[b] + a.len_add, a.max_tokens) : a.max_tokens;
   const int ntiles = (len + kTile - 1) / kTile;
   const uint8_t* kbase = a.krec + int64_t(b) * a.ks_seq + int64_t(g) * a.ks_head;
   const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
@@ -154,6 +154,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   auto load_tile = [&](int tile, TileRegs& R) {
     const uint8_t* kt = kbase + int64_t(tile) * kc.tile_bytes;
     const uint8_t* vt = vbase + int64_t(tile) * vc.tile_bytes;
+    if (a.block_table) {
+      // the tile index is the wave's: one scalar read of the block table
+      const int64_t pt = paged_tile(a.block_table, a.page_shift, a.max_pages, int64_t(b) * a.Hkv + g,
+                                    __builtin_amdgcn_readfirstlane(tile));
+      kt = a.krec + pt * kc.tile_bytes;
+      vt = a.vrec + pt * vc.tile_bytes;
+    }
     const int tok = 16 * g16 + n;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {

@@ -63,6 +63,11 @@ struct AppendArgs {
   int64_t rs_b, rs_h;
   const int32_t* positions;  // [B]
   int capacity;         // tokens the records hold
+  // paged records (block_table non-NULL): tile t of set (b, h) is tile
+  // t % 2^page_shift of page block_table[(b * H + h) * max_pages + (t >> page_shift)]
+  // of the pool rec; rs_b and rs_h are then unused
+  const int32_t* block_table;
+  int page_shift, max_pages;
 };
 bool append_supported(const CodecView& cv);
 hipError_t launch_append(const CodecView& cv, const AppendArgs& a, hipStream_t s);
@@ -98,9 +103,23 @@ struct DecodeArgs {
   float scale;
   int chunk_tiles;     // tiles per split
   int nsplit;
+  int len_add;         // tokens attended = min(seq_lens[b] + len_add, max_tokens)
+  // paged records (block_table non-NULL): tile t of set (b, g) is tile
+  // t % 2^page_shift of page block_table[(b * Hkv + g) * max_pages + (t >> page_shift)]
+  // of the pools krec / vrec; the strides are then unused
+  const int32_t* block_table;
+  int page_shift, max_pages;
   float* part;         // workspace partials
   float* out;          // [B][Hq][d]
 };
+
+// Index, within its page pool, of tile t of set `row` (= b * H + h) of a
+// paged cache: the page's first tile plus the tile's place in the page.
+__device__ __forceinline__ int64_t paged_tile(const int32_t* block_table, int page_shift, int max_pages,
+                                              int64_t row, int t) {
+  const int pg = block_table[row * max_pages + (t >> page_shift)];
+  return (int64_t(pg) << page_shift) + (t & ((1 << page_shift) - 1));
+}
 hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
                          hipStream_t s);
 // MFMA decode partial kernel (d = 128, prod keys with 1-2 index bits and a

@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int len = a.seq_lens ? min(a.seq_lens[b], a.max_tokens) : a.max_tokens;
+  const int len = a.seq_lens ? min(a.seq_lens[b] + a.len_add, a.max_tokens) : a.max_tokens;
   const int ntiles = (len + kTile - 1) / kTile;
   const uint8_t* kbase = a.krec + int64_t(b) * a.ks_seq + int64_t(g) * a.ks_head;
   const uint8_t* vbase = a.vrec + int64_t(b) * a.vs_seq + int64_t(g) * a.vs_head;
@@ -347,6 +347,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
   for (int tile = t_begin + wave; tile < t_end; tile += 4) {
     const uint8_t* kt = kbase + int64_t(tile) * kc.tile_bytes;
     const uint8_t* vt = vbase + int64_t(tile) * vc.tile_bytes;
+    if (a.block_table) {
+      const int64_t pt = paged_tile(a.block_table, a.page_shift, a.max_pages, int64_t(b) * a.Hkv + g, tile);
+      kt = a.krec + pt * kc.tile_bytes;
+      vt = a.vrec + pt * vc.tile_bytes;
+    }
     const int tok = tile * kTile + lane;
     const bool valid = tok < len;
     // ---- scores (lane = token)
