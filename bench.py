@@ -336,6 +336,16 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
     kn, vn = K[0][:, T - 1].unsqueeze(0), V[0][:, T - 1].unsqueeze(0)
     append_ms = time_one(torch, lambda: (tq.append(kcb, kn, krec[0], pos, T), tq.append(vcb, vn, vrec[0], pos, T)),
                          args.steps, args.warmup)
+    # the whole decode step on a paged view of the same records (pages of 4
+    # tiles, the table mapping each KV head to its own pages in order): append
+    # the new token at slot T - 1, then attend over T tokens
+    page_tiles = 4
+    npg = (T // 64) // page_tiles
+    table = torch.arange(HKV * npg, dtype=torch.int32, device=dev).reshape(HKV, npg)
+    step_ms = time_one(torch, lambda: tq.decode_step(kcb, vcb, q, kn, vn, krec[0], vrec[0], T, HKV, scale, pos,
+                                                     out=out, workspace=ws, block_table=table,
+                                                     page_tiles=page_tiles),
+                       args.steps, args.warmup)
     nk = HKV * T
     nbytes = {"encode_keys": nk * (2 * D + k_rec), "encode_values": nk * V_ENC_BYTES,
               "decode_attend": nk * (k_rec + V_REC)}
@@ -358,6 +368,7 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
                  "f32 (split-f16 MFMA)", roof, bd,
                  {"decode_keys_per_s": nk / (t["decode_attend"] * 1e-3),
                   "append_kv_ms": append_ms,
+                  "decode_step_paged_ms": step_ms,
                   "encode_GBps": (nbytes["encode_keys"] + nbytes["encode_values"]) /
                   ((t["encode_keys"] + t["encode_values"]) * 1e-3) / 1e9})
     return res, (cpu_baseline_gqa_outlier if split else cpu_baseline_gqa)

@@ -285,7 +285,9 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
  * t of set (b, h) is tile t % page_tiles of page
  * block_table[(b*Hkv + h)*max_pages + t / page_tiles] (a page index into the
  * pool; keys and values use the same index in their own pools) and the
- * strides are not used.  A page holds whole tiles, so tq_encode can fill it
+ * strides are not used.  Only the entries of tiles below seq_lens[b] (below
+ * max_tokens without seq_lens; tq_decode_step: through slot seq_lens[b]) are
+ * read.  A page holds whole tiles, so tq_encode can fill it
  * directly (records = the page, tokens = a multiple of 64 * page_tiles, or
  * the set's tail). */
 typedef struct {

@@ -905,8 +905,7 @@ tq_status tq_decode_step(const tq_codebook* kcb, const tq_codebook* vcb, const v
   va.rec = static_cast<uint8_t*>(const_cast<void*>(kv->v_records));
   va.rs_b = kv->v_stride_seq;
   va.rs_h = kv->v_stride_head;
-  if ((st = map_hip(launch_append(kc, ka, s))) != TQ_OK) return st;
-  if ((st = map_hip(launch_append(vc, va, s))) != TQ_OK) return st;
+  if ((st = map_hip(launch_append_pair(kc, ka, vc, va, s))) != TQ_OK) return st;
   return decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace, workspace_bytes,
                      stream, 1, false);
 }

@@ -190,8 +190,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   };
   TileRegs& ra = cur;
   TileRegs& rb = nxt;
-  // the first tile's loads go out before the set-up below and overlap it
-  if (t_begin + wave < t_end) load_tile(t_begin + wave, ra);
+  // the first tile's loads go out before the set-up below and overlap it.
+  // Contiguous records: they do not wait for seq_lens, since any tile below
+  // max_tokens is in the records (a wave without a tile leaves them unused).
+  // Paged records: only tiles below seq_lens are looked up in the block table
+  // (the entries past them need not name pages).
+  if (!a.block_table) {
+    const int tmax = (a.max_tokens + kTile - 1) / kTile;
+    load_tile(min(t_begin + wave, tmax - 1), ra);
+  } else if (t_begin + wave < t_end) {
+    load_tile(t_begin + wave, ra);
+  }
 
   // ---- set-up: one round of independent loads, then arithmetic on LDS.
   // The G queries are rotated here, q' = Pi_h q and qs = S q'[0:m]: thread t

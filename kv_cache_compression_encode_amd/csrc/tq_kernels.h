@@ -71,6 +71,9 @@ struct AppendArgs {
 };
 bool append_supported(const CodecView& cv);
 hipError_t launch_append(const CodecView& cv, const AppendArgs& a, hipStream_t s);
+// The key and the value of a decode step in one launch (same B and H).
+hipError_t launch_append_pair(const CodecView& kc, const AppendArgs& ka, const CodecView& vc,
+                              const AppendArgs& va, hipStream_t s);
 
 // q' = Pi_h q and qs = S q'[0:m] for nq queries; head_of_query maps query ->
 // rotation head (NULL: all head 0; else head = (query / group) % hkv ...).
