@@ -43,9 +43,10 @@ DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decod
 # HBM bytes per launch of a call's kernel from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a
 # plain 1 GiB device copy (factors 2.0 and 1.0); the summary and the commands
-# are in profiles/.  Valid for the kernels as built when the counters were
-# taken; a call missing here reports null.
-TRAFFIC = {"encode_keys": 82135912}
+# are in profiles/.  Keyed by (workload, call): a reading holds for that
+# launch size only, and for the kernels as built when the counters were
+# taken; a pair missing here reports null.
+TRAFFIC = {("gqa_layer", "encode_keys"): 82135912}
 
 
 def parse():
@@ -291,10 +292,10 @@ def rot_note(s):
                 if ROTATION == "hadamard" else "")
 
 
-def hbm_roof(name, ms, nbytes, note=None):
+def hbm_roof(workload, name, ms, nbytes, note=None):
     gbs = nbytes / (ms * 1e-3) / 1e9
     # the counters were taken for the dense-Pi kernels
-    traffic = TRAFFIC.get(name) if isinstance(TRAFFIC, dict) and ROTATION == "haar" else None
+    traffic = TRAFFIC.get((workload, name)) if ROTATION == "haar" else None
     r = {"bound": "hbm", "kernel": name, "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
          "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
          "bytes_per_launch": nbytes, "avg_launch_ms": ms}
@@ -355,9 +356,7 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
     keys_desc = ("K outlier-channel split, 2.5 bits (per KV head the 32 largest-RMS channels of a 2048-token "
                  "calibration sample: TurboQuant-prod b=3; the other 96: b=2; row records, 44 B/key)"
                  if split else "K TurboQuant-prod b=3 (row records)")
-    roof = hbm_roof(dom, t[dom], nbytes[dom])
-    if split:
-        roof["traffic"] = None  # counters were taken for the b=3 key kernels
+    roof = hbm_roof("gqa_outlier" if split else "gqa_layer", dom, t[dom], nbytes[dom])
     res = result(args, "compressed-key scoring keys/s & KV encode GB/s at d=128, % of HBM roofline",
                  nk / (ms_step * 1e-3), "keys/s", ms_step,
                  {"workload": rot_note(("gqa_outlier" if split else "gqa_decode_layer") +
@@ -392,7 +391,7 @@ def run_small(args, torch, tq, synth):
                  {"workload": "small: 4096 iid N(0,I) fp32 vectors d=128, prod b=3, encode then "
                               "score 16 queries x 4096 keys"},
                  "f32 (split-f16 MFMA)",
-                 hbm_roof("encode", t["encode"], nbytes["encode"],
+                 hbm_roof("small", "encode", t["encode"], nbytes["encode"],
                           "2 MiB workload: launch-bound, cache-resident; fraction shown for completeness"),
                  bd, {"score_keys_per_s": n * nq / (t["score"] * 1e-3)})
     return res, cpu_baseline_small
@@ -421,7 +420,7 @@ def run_bulk(args, torch, tq, synth):
     res = result(args, "KV encode GB/s at d=128 (bulk prefill), % of HBM roofline", gbs, "GB/s", ms_step,
                  {"workload": rot_note("bulk_prefill: 32 layers x 8 kv heads x 131072 tokens x d=128 bf16 K "
                                        "and V; K prod b=3 row, V mse b=4 col; step = encode all K and V")},
-                 "f32 (split-f16 MFMA)", hbm_roof(dom, t[dom], nbytes[dom]), bd,
+                 "f32 (split-f16 MFMA)", hbm_roof("bulk_prefill", dom, t[dom], nbytes[dom]), bd,
                  {"token_heads_per_s": nk / (ms_step * 1e-3),
                   "compression_ratio": (2 * D * 2) / (K_REC + V_REC)})
     return res, cpu_baseline_bulk
@@ -483,7 +482,7 @@ def run_sq(args, torch, tq, synth):
                               "SpectralQuant (per-head eigenbasis, bits [5,3,2,2]+1, QJL on 4 dims), "
                               "values mse b=4 col; step = one fused decode token per sequence",
                   "caches_cycled": ncache},
-                 "f32", hbm_roof("decode_attend", t["decode_attend"], nbytes,
+                 "f32", hbm_roof("sq_decode", "decode_attend", t["decode_attend"], nbytes,
                                  "one library call: the fused score + softmax + P V kernel, which rotates its "
                                  "queries in its set-up; one split per sequence at this batch, so the merge "
                                  "and the inverse value rotation run inside it"),
