@@ -57,18 +57,28 @@ __device__ __forceinline__ float f16v(uint32_t h) {
   return float(__builtin_bit_cast(_Float16, uint16_t(h)));
 }
 
-// Pack 8 floats into fp16 hi and lo fragments, x = hi + lo to ~2^-21
+// -1.0f in a scalar register the compiler cannot see through: fma(h, m1, x)
+// with an fp16 h then stays one mixed-precision FMA (v_fma_mix_f32 reads the
+// fp16 half in place) instead of being folded into a conversion plus a
+// subtraction.
+__device__ __forceinline__ float opaque_minus_one() {
+  float m1;
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(m1));
+  return m1;
+}
+
+// Pack 8 floats into fp16 hi and lo fragments, x = hi + lo to ~2^-22
 // relative: hi by a packed round-toward-zero conversion, the exact remainder
-// x - hi (fp32) converted the same way.
-__device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo) {
+// x - hi (one mixed FMA per element) rounded to nearest.
+__device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo, float m1) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const auto h = __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]);
-    const float r0 = __builtin_fmaf(float(h[0]), -1.f, v[2 * i]);
-    const float r1 = __builtin_fmaf(float(h[1]), -1.f, v[2 * i + 1]);
-    const auto l = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    const float r0 = __builtin_fmaf(float(h[0]), m1, v[2 * i]);
+    const float r1 = __builtin_fmaf(float(h[1]), m1, v[2 * i + 1]);
     hi[i] = __builtin_bit_cast(uint32_t, h);
-    lo[i] = __builtin_bit_cast(uint32_t, l);
+    lo[i] = uint32_t(__builtin_bit_cast(uint16_t, _Float16(r0))) |
+            (uint32_t(__builtin_bit_cast(uint16_t, _Float16(r1))) << 16);
   }
 }
 
@@ -287,17 +297,37 @@ __device__ __forceinline__ uint32_t quant4_sym_push(uint32_t w, float v, const f
 }
 
 // 4 levels: P = T[2] scaled like v, L2 / L3 levels 2 / 3 (levels 0 / 1 are
-// their negatives).  Appends index bit 1 ([v >= 0]) to w1 and index bit 0
-// ([v >= 0] == [|v| >= P]) to w0; returns the selected level.
+// their negatives), L2, L3 > 0.  Index bit 1 is [v >= 0] and index bit 0 is
+// [v >= 0] == [|v| >= P].  Appends the sign bit of v ([v < 0]) to w1 and
+// [|v| >= P] to w0 (one v_alignbit and one v_addc); sym2_finish turns the
+// two words into the index planes once all bits are in.  Returns the
+// selected level.  v is never -0 here (accumulator values).
 __device__ __forceinline__ float quant2_sym_push(float v, float P, float L2, float L3, uint32_t& w0,
                                                  uint32_t& w1) {
-  const bool pos = v >= 0.f;
   const bool m = fabsf(v) >= P;
-  const uint64_t mp = __ballot(pos), mm = __ballot(m);
-  w1 = push_mask(w1, mp);
-  w0 = push_mask(w0, ~(mp ^ mm));
-  const float c = m ? L3 : L2;
-  return pos ? c : -c;
+  w0 = push_mask(w0, __ballot(m));
+  w1 = __builtin_amdgcn_alignbit(w1, __float_as_uint(v), 31);
+  // the level with the sign of v, formed on the bits (one v_and_or) so that
+  // the caller's -level stays a source modifier of its FMA
+  return __uint_as_float(__float_as_uint(m ? L3 : L2) | (__float_as_uint(v) & 0x80000000u));
+}
+// After quant2_sym_push over the bits in `mask`: w1 = [v < 0] bits and
+// w0 = [|v| >= P] bits become index bit 0 = [v < 0] xor [|v| >= P] and
+// index bit 1 = not [v < 0].
+__device__ __forceinline__ void sym2_finish(uint32_t& w0, uint32_t& w1, uint32_t mask) {
+  w0 ^= w1;
+  w1 ^= mask;
+}
+
+// Sign word of 16 accumulator values, pushed from register 15 down to 0:
+// bit r = [z_r >= 0].  The float sign bits are shifted in (one v_alignbit
+// each) and flipped at the end; z is never -0 (each MFMA chain starts at +0
+// and a sum with +0 never rounds to -0).
+__device__ __forceinline__ uint32_t sign_word16(const f32x16& z) {
+  uint32_t neg = 0u;
+#pragma unroll
+  for (int r = 15; r >= 0; --r) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(z[r]), 31);
+  return neg ^ 0xffffu;
 }
 
 // OR across groups of `VPD` consecutive lanes (8 or 16) with DPP moves:
@@ -384,6 +414,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   };
   auto process = [&](const u32x4 (&cur)[NB][8], int64_t tile, int sub) {
     uint8_t* trec = rbase + tile * cv.tile_bytes;
+    const float m1 = opaque_minus_one();
     {
       // ---------------------------------------------------------- load X
       // xh/xl: fp16 hi/lo fragments of x * 2^e, e chosen per vector so that
@@ -418,14 +449,18 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           // raw bf16 pairs (prefetched) stay packed until the scale is known
           const u32x4* r = cur[nb];
           {
-            float s0 = 0.f, s1 = 0.f;  // two chains; fp32 FMAs (exact squares)
+            // two chains; the squares of bf16 values are exact in fp32
+            float s0 = 0.f, s1 = 0.f;
             float o0 = 0.f, o1 = 0.f;  // SPLIT: outlier channels only
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
-                if constexpr (SPLIT) {
+                if constexpr (!SPLIT) {
+                  s0 = fmaf(lo, lo, s0);
+                  s1 = fmaf(hi, hi, s1);
+                } else {
                   // channel 64 hh + 8c + 2i (+1): bit (8c + 2i) % 32 of mask word c / 4
                   const int k = (8 * c + 2 * i) & 31;
                   const uint32_t lw = r[c][i] << 16, hw = r[c][i] & 0xffff0000u;
@@ -436,9 +471,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                   const float lo_r = lo - lo_o, hi_r = hi - hi_o;  // exact: x or 0
                   s0 = fmaf(lo_r, lo_r, s0);
                   s1 = fmaf(hi_r, hi_r, s1);
-                } else {
-                  s0 = fmaf(lo, lo, s0);
-                  s1 = fmaf(hi, hi, s1);
                 }
               }
             ss = s0 + s1;
@@ -544,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             float sc[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) sc[i] = v[c][i] * p2;
-            split8h(sc, xh[nb][c], xl[nb][c]);
+            split8h(sc, xh[nb][c], xl[nb][c], m1);
           }
           wsc[nb] = 16.f * p2;
         }
@@ -786,6 +818,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               }
             }
           }
+          if constexpr (SYM2) sym2_finish(cw[nb][0], cw[nb][NPL - 1], 0xffffu);
           if (!COL) {
             // row layout: half hh holds bits 16 hh .. 16 hh + 15 of each word;
             // slots past the end of the input are zero
@@ -844,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               float v[8];
 #pragma unroll
               for (int i = 0; i < 8; ++i) v[i] = acc[nb][8 * q + i];
-              split8h(v, rh[nb], rl[nb]);
+              split8h(v, rh[nb], rl[nb], m1);
             }
             const int chunk = 2 * mb + q;
 #pragma unroll
@@ -871,10 +904,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
 #pragma unroll
           for (int ms = 0; ms < 4; ++ms) {
-#pragma unroll
-            for (int r = 15; r >= 0; --r)
-              if (!COL) sw[nb][ms] = push_bit(sw[nb][ms], z[nb][ms][r] >= 0.f);
-            if (!valid[nb]) sw[nb][ms] = 0;
+            if (!COL) sw[nb][ms] = valid[nb] ? sign_word16(z[nb][ms]) : 0u;
           }
         } else if (MODE == 2) {
           if (hh == 0) {
@@ -1070,6 +1100,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
   };
   auto process = [&](const u32x4 (&cur)[8], int64_t tile, int sub) {
     uint8_t* trec = rbase + tile * cv.tile_bytes;
+    const float m1 = opaque_minus_one();
     const int slot = sub * 32 + j;
     const bool valid = tile * kTile + slot < a.tokens;
     // ------------------------------------------------ signs, norm, unpack
@@ -1159,6 +1190,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
             v[32 * blk + r] = rsd;
           }
         }
+        if constexpr (SYM2) sym2_finish(cw[0], cw[1], 0xffffffffu);
 #pragma unroll
         for (int p = 0; p < UB; ++p)
           *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = valid ? cw[p] : 0u;
@@ -1170,7 +1202,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         u32x4 rh, rl;
-        split8h(&v[8 * c], rh, rl);
+        split8h(&v[8 * c], rh, rl, m1);
 #pragma unroll
         for (int ms = 0; ms < 4; ++ms) {
           const u32x4 sh = *reinterpret_cast<const u32x4*>(sSk + (32 * ms + j) * LDS_ROW + 16 * c + 8 * hh);
@@ -1183,10 +1215,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
       // register r of half hh of block ms holds sketch row 32 ms + 16 hh + r
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms) {
-        sw[ms] = 0;
-#pragma unroll
-        for (int r = 15; r >= 0; --r) sw[ms] = push_bit(sw[ms], z[ms][r] >= 0.f);
-        const uint32_t mine = valid ? sw[ms] << (16 * hh) : 0u;
+        const uint32_t mine = valid ? sign_word16(z[ms]) << (16 * hh) : 0u;
         sw[ms] = mine | xor32(mine);
       }
       uint8_t* dst = trec + cv.off_signs + slot * 16 + 8 * hh;
