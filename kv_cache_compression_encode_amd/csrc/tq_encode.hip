@@ -276,24 +276,31 @@ __device__ __forceinline__ uint32_t push_mask(uint32_t w, uint64_t m) {
   return r;
 }
 
-// 16 levels: P[k] = T[8 + k] (k < 7) scaled like v.  Appends the 4-bit
-// index of v to w (w = 16 w + idx): for v >= 0 the index is 8 + m and for
-// v < 0 it is 7 - m, m = number of P[k] <= |v|, so bit 3 is [v >= 0] and
-// bits 2..0 are those of m, inverted when v < 0 (lane masks combined on the
-// scalar unit).
+// 16 levels: P[k] = T[8 + k] (k < 7) scaled like v.  The 4-bit index of v
+// is 8 + m for v >= 0 and 7 - m for v < 0, m = number of P[k] <= |v| (a
+// 3-step binary search), so bit 3 is [v >= 0] and bits 2..0 are those of m,
+// inverted when v < 0.  quant4_sym_push appends the raw nibble
+// [v < 0, m2, m1, m0] to w (w = 16 w + nibble: the float sign bit by one
+// v_alignbit, the search bits by v_addc from their compare masks);
+// quant4_finish turns a word of 8 raw nibbles into indices.  v is never -0
+// here (accumulator values).
 __device__ __forceinline__ uint32_t quant4_sym_push(uint32_t w, float v, const float (&P)[7]) {
   const float a = fabsf(v);
-  const uint64_t pos = __ballot(v >= 0.f);
   const bool b2 = a >= P[3];
   const uint64_t m2 = __ballot(b2);
   const bool b1 = a >= (b2 ? P[5] : P[1]);
   const uint64_t m1 = __ballot(b1);
   const float tu = b1 ? P[6] : P[4], tl = b1 ? P[2] : P[0];
   const uint64_t m0 = __ballot(a >= (b2 ? tu : tl));
-  w = push_mask(w, pos);
-  w = push_mask(w, ~(pos ^ m2));
-  w = push_mask(w, ~(pos ^ m1));
-  return push_mask(w, ~(pos ^ m0));
+  w = __builtin_amdgcn_alignbit(w, __float_as_uint(v), 31);
+  w = push_mask(w, m2);
+  w = push_mask(w, m1);
+  return push_mask(w, m0);
+}
+// Raw nibbles [n, m2, m1, m0] -> indices [not n, m2 ^ n, m1 ^ n, m0 ^ n].
+__device__ __forceinline__ uint32_t quant4_finish(uint32_t w) {
+  const uint32_t n = w & 0x88888888u;
+  return w ^ ((n >> 1) | (n >> 2) | (n >> 3)) ^ 0x88888888u;
 }
 
 // 4 levels: P = T[2] scaled like v, L2 / L3 levels 2 / 3 (levels 0 / 1 are
@@ -839,7 +846,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             // the col dword of dim 32mb + 16hh + r for those vectors
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-              const uint32_t w = nib_transpose8(valid[nb] ? pk[nb][k] : 0u, nibc);
+              const uint32_t w = nib_transpose8(valid[nb] ? quant4_finish(pk[nb][k]) : 0u, nibc);
               const int r = 8 * k + (j & 7);
               const int dim = 32 * mb + 16 * hh + r;
               const int word = (sub * NB * 32 + nb * 32 + j) / 8;
@@ -1164,7 +1171,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
           uint32_t w = 0;
 #pragma unroll
           for (int i = 7; i >= 0; --i) w = quant4_sym_push(w, v[32 * blk + 8 * g + i], P4);
-          w = nib_transpose8(valid ? w : 0u, nibc);
+          w = nib_transpose8(valid ? quant4_finish(w) : 0u, nibc);
           const int dim = 32 * mb + 8 * g + (j & 7);
           *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 32 + 4 * (slot / 8)) = w;
         }
