@@ -276,6 +276,15 @@ __device__ __forceinline__ uint32_t push_mask(uint32_t w, uint64_t m) {
   return r;
 }
 
+// push_mask for a mask that is dead afterwards: the carry-out goes back into
+// the mask's own SGPR pair, so that consecutive pushes do not all write one
+// shared pair (each such write-after-write costs a wait state).
+__device__ __forceinline__ uint32_t push_mask_last(uint32_t w, uint64_t m) {
+  uint32_t r;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %1" : "=v"(r), "+s"(m) : "v"(w));
+  return r;
+}
+
 // 16 levels: P[k] = T[8 + k] (k < 7) scaled like v.  The 4-bit index of v
 // is 8 + m for v >= 0 and 7 - m for v < 0, m = number of P[k] <= |v| (a
 // 3-step binary search), so bit 3 is [v >= 0] and bits 2..0 are those of m,
@@ -293,9 +302,9 @@ __device__ __forceinline__ uint32_t quant4_sym_push(uint32_t w, float v, const f
   const float tu = b1 ? P[6] : P[4], tl = b1 ? P[2] : P[0];
   const uint64_t m0 = __ballot(a >= (b2 ? tu : tl));
   w = __builtin_amdgcn_alignbit(w, __float_as_uint(v), 31);
-  w = push_mask(w, m2);
-  w = push_mask(w, m1);
-  return push_mask(w, m0);
+  w = push_mask_last(w, m2);
+  w = push_mask_last(w, m1);
+  return push_mask_last(w, m0);
 }
 // Raw nibbles [n, m2, m1, m0] -> indices [not n, m2 ^ n, m1 ^ n, m0 ^ n].
 __device__ __forceinline__ uint32_t quant4_finish(uint32_t w) {
