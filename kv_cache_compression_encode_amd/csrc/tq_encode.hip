@@ -119,29 +119,36 @@ __host__ __device__ constexpr int lds_row_of(int g) {
   return (g & ~31) | (((g >> 2) & 3) << 3) | (((g >> 4) & 1) << 2) | (g & 3);
 }
 
-// Stage a [128][128] 16-bit matrix into LDS rows of LDS_ROW elements, rows
-// placed by lds_row_of; with `colperm` bits 3 and 4 of the column index are
-// swapped, matching the residual's register order in the sketch operand.
-// Each thread keeps its 16-byte loads in flight before storing them.
-__device__ void stage_matrix(uint16_t* lds, const uint16_t* g, bool colperm) {
-  constexpr int CHUNKS = D * D / 8;  // 16-byte chunks
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int base = 0; base < CHUNKS; base += 8 * nt) {
-    u32x4 v[8];
+// Stage N [128][128] 16-bit matrices into LDS rows of LDS_ROW elements,
+// rows placed by lds_row_of; with colperm[m] bits 3 and 4 of the column
+// index are swapped, matching the residual's register order in the sketch
+// operand.  512 threads, 4 chunks of 16 bytes of each matrix per thread, in
+// two phases: stage_load issues every load (one memory round trip for all
+// N), stage_store writes LDS once they have arrived; loads issued between
+// the two stay in flight across the stores.
+constexpr int kStagePer = D * D / 8 / 512;
+static_assert(D * D / 8 % 512 == 0, "whole chunks per thread");
+template <int N>
+__device__ __forceinline__ void stage_load(const uint16_t* const (&g)[N], u32x4 (&v)[N][kStagePer]) {
+  const int tid = threadIdx.x;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = base + u * nt + tid;
-      if (e < CHUNKS) v[u] = *reinterpret_cast<const u32x4*>(g + e * 8);
-    }
+  for (int m = 0; m < N; ++m)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = base + u * nt + tid;
-      if (e >= CHUNKS) continue;
+    for (int u = 0; u < kStagePer; ++u) v[m][u] = *reinterpret_cast<const u32x4*>(g[m] + (u * 512 + tid) * 8);
+}
+template <int N>
+__device__ __forceinline__ void stage_store(uint16_t* const (&lds)[N], const bool (&colperm)[N],
+                                            const u32x4 (&v)[N][kStagePer]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < N; ++m)
+#pragma unroll
+    for (int u = 0; u < kStagePer; ++u) {
+      const int e = u * 512 + tid;
       const int row = e / (D / 8), col = (e % (D / 8)) * 8;
-      const int c2 = colperm ? ((col & ~24) | (((col >> 3) & 1) << 4) | (((col >> 4) & 1) << 3)) : col;
-      *reinterpret_cast<u32x4*>(lds + lds_row_of(row) * LDS_ROW + c2) = v[u];
+      const int c2 = colperm[m] ? ((col & ~24) | (((col >> 3) & 1) << 4) | (((col >> 4) & 1) << 3)) : col;
+      *reinterpret_cast<u32x4*>(lds[m] + lds_row_of(row) * LDS_ROW + c2) = v[m][u];
     }
-  }
 }
 
 
@@ -377,17 +384,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   const int64_t bh = blockIdx.y;
   const int64_t b = bh / a.heads, h = bh % a.heads;
   const int hc = cv.heads > 1 ? int(h) : 0;
-
-  stage_matrix(sPiHi, cv.rot_hi + size_t(hc) * D * D, false);
-  stage_matrix(sPiLo, cv.rot_lo + size_t(hc) * D * D, false);
-  if (MODE == 1) stage_matrix(sSk, cv.sk_hi, true);
-  if (!UNIFORM && !SPLIT) {
-    for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
-      sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
-      sCen[e] = cv.cen[size_t(hc) * D * kMaxLevels + e];
-    }
-  }
-  __syncthreads();
 
   const int lane = lane_id();
   const int j = lane & 31, hh = lane >> 5;
@@ -995,7 +991,30 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   };
   int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
   int sub = 0;
-  if (BF16IN) load_raw(tile, 0, bufA);
+  // the tables' loads go out first, then the first rows; the tables are
+  // stored to LDS as soon as they arrive, with the rows still in flight
+  {
+    constexpr int NM = MODE == 1 ? 3 : 2;  // Pi hi, Pi lo (, S)
+    const uint16_t* src[NM];
+    uint16_t* dst[NM];
+    bool perm[NM];
+    src[0] = cv.rot_hi + size_t(hc) * D * D, dst[0] = sPiHi, perm[0] = false;
+    src[1] = cv.rot_lo + size_t(hc) * D * D, dst[1] = sPiLo, perm[1] = false;
+    if constexpr (NM == 3) src[2] = cv.sk_hi, dst[2] = sSk, perm[2] = true;
+    u32x4 sv[NM][kStagePer];
+    stage_load<NM>(src, sv);
+    __builtin_amdgcn_sched_barrier(0);  // keep the two groups of loads in this order
+    if (BF16IN) load_raw(tile, 0, bufA);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_store<NM>(dst, perm, sv);
+  }
+  if (!UNIFORM && !SPLIT) {
+    for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
+      sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
+      sCen[e] = cv.cen[size_t(hc) * D * kMaxLevels + e];
+    }
+  }
+  __syncthreads();
   if constexpr (NB == 1) {
     while (tile < ntiles) {
       int64_t t1 = tile;
