@@ -46,7 +46,7 @@ DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decod
 # are in profiles/.  Keyed by (workload, call): a reading holds for that
 # launch size only, and for the kernels as built when the counters were
 # taken; a pair missing here reports null.
-TRAFFIC = {}
+TRAFFIC = {("gqa_layer", "encode_keys"): 82030994, ("gqa_layer", "encode_values"): 85160860}
 
 
 def parse():
@@ -84,7 +84,7 @@ def _cores():
         return os.cpu_count() or 1
 
 
-def _time_loop(fn, budget_s=10.0, max_reps=50):
+def _time_loop(fn, budget_s=10.0, max_reps=100000):
     reps, t0 = 0, time.perf_counter()
     while True:
         fn()
