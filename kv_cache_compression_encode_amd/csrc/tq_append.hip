@@ -122,8 +122,19 @@ __device__ __forceinline__ void append_one(const CodecView& cv, const AppendArgs
     const float xv = t < D ? sx[t] : 0.f;
     const float q = cv.outl ? z * z : xv * xv;
     coord_sums(og ? q : 0.f, og ? 0.f : q, red, nxo, nxr);
-    nxo = sqrtf(nxo);
-    nxr = sqrtf(nxr);
+    if ((cv.outl && nxo < 0x1p-100f) || nxr < 0x1p-100f) {
+      // a norm below 2^-50 (squares that may be denormal or flushed) or a
+      // zero group: the sums again over the values times 2^64 (exact
+      // scaling); the sums are the same on every thread, so is the branch
+      const float zs = z * 0x1p64f, xs = xv * 0x1p64f;
+      const float q2 = cv.outl ? zs * zs : xs * xs;
+      coord_sums(og ? q2 : 0.f, og ? 0.f : q2, red, nxo, nxr);
+      nxo = sqrtf(nxo) * 0x1p-64f;
+      nxr = sqrtf(nxr) * 0x1p-64f;
+    } else {
+      nxo = sqrtf(nxo);
+      nxr = sqrtf(nxr);
+    }
   }
   const float ng = og ? nxo : nxr;
   const float inv = ng > 0.f ? 1.f / ng : 0.f;  // a zero vector (group) encodes y = 0

@@ -434,6 +434,10 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // between the accumulator and the rotated unit vector y.
       u32x4 xh[NB][8], xl[NB][8];
       float sx[NB], nxv[NB], wsc[NB];
+      // norms are sqrt(sum of squares) / nd: nd = 1 when the squares were
+      // summed unscaled, 2^e when they were summed over x * 2^e (then no
+      // square underflows, whatever the vector's magnitude)
+      float nd[NB];
       float so2[NB];  // SPLIT: sum of squares over this vector's outlier channels
       // SPLIT: outlier boundary t_2 and levels c_2, c_3 (dim 0), regular
       // level c_1 (dim 8), and this half's outlier-channel mask (channels
@@ -456,6 +460,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         const int slot = sub * 32 * NB + nb * 32 + j;
         const int64_t t = tile * kTile + slot;
         valid[nb] = t < a.tokens;
+        nd[nb] = 1.f;
         float ss = 0.f, mx = 0.f;
         if (BF16IN) {
           // raw bf16 pairs (prefetched) stay packed until the scale is known
@@ -502,13 +507,15 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           // exponent field drops by D = 112 - s (saturating at 0, which
           // flushes elements below 2^-14 of the scaled range, i.e. under
           // 2^-28 ||x||), the 7 mantissa bits move up by 3, the sign stays.
-          // Norms whose floor(log2) is below -98, and non-finite ones, take
-          // the general path below (float scaling by the largest element).
+          // Norms whose floor(log2) is below -50 (their squares may be
+          // denormal or flushed: zero vectors too), and non-finite ones, take
+          // the general path below (float scaling by the largest element,
+          // squares summed over the scaled values).
           const int es = int((__float_as_uint(ss) >> 23) & 0xff);  // biased exponent of ||x||^2
           const int en = (es - 127) >> 1;                            // floor(log2 ||x||) (normal ss)
-          const bool fast = ss == 0.f || (es > 0 && es < 255 && en >= -98);
+          const bool fast = es > 0 && es < 255 && en >= -50;
           if (__builtin_expect(__ballot(!fast) == 0, 1)) {
-            const int dsh = ss == 0.f ? 98 : 98 + en;  // D
+            const int dsh = 98 + en;  // D
             const uint32_t dd = uint32_t(dsh) << 7;
             const u16x2 sub2 = {uint16_t(dd), uint16_t(dd)};
 #pragma unroll
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 e = e << u16x2{3, 3};
                 xh[nb][c][i] = (w & 0x80008000u) | __builtin_bit_cast(uint32_t, e);
               }
-            const float p2 = ss == 0.f ? 1.f : __uint_as_float(uint32_t(141 - en) << 23);
+            const float p2 = __uint_as_float(uint32_t(141 - en) << 23);
             wsc[nb] = 16.f * p2;
           } else {
 #pragma unroll
@@ -535,6 +542,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
             const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
             // x * 2^e is exact in fp16 (8 significant bits, exponent in range)
+            float t0 = 0.f, t1 = 0.f, u0 = 0.f, u1 = 0.f;  // scaled squares (SPLIT: u outliers)
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -542,7 +550,29 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 const float lo = __uint_as_float(r[c][i] << 16) * p2;
                 const float hi = __uint_as_float(r[c][i] & 0xffff0000u) * p2;
                 xh[nb][c][i] = f16b(lo) | (f16b(hi) << 16);
+                if constexpr (SPLIT) {
+                  const int k = (8 * c + 2 * i) & 31;
+                  const bool olo = (om[c >> 2] >> k) & 1u, ohi = (om[c >> 2] >> (k + 1)) & 1u;
+                  u0 = fmaf(olo ? lo : 0.f, lo, u0);
+                  u1 = fmaf(ohi ? hi : 0.f, hi, u1);
+                  t0 = fmaf(olo ? 0.f : lo, lo, t0);
+                  t1 = fmaf(ohi ? 0.f : hi, hi, t1);
+                } else {
+                  t0 = fmaf(lo, lo, t0);
+                  t1 = fmaf(hi, hi, t1);
+                }
               }
+            float tt = t0 + t1;
+            tt += xor32f(tt);
+            nd[nb] = p2;
+            if constexpr (SPLIT) {
+              float uu = u0 + u1;
+              uu += xor32f(uu);
+              nxv[nb] = sqrtf(tt) / p2;  // regular instance's norm
+              so2[nb] = uu;              // outliers, scaled
+            } else {
+              ss = tt;
+            }
             wsc[nb] = 16.f * p2;
           }
         } else {
@@ -556,44 +586,43 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             v[c][0] = p0.x; v[c][1] = p0.y; v[c][2] = p0.z; v[c][3] = p0.w;
             v[c][4] = p1.x; v[c][5] = p1.y; v[c][6] = p1.z; v[c][7] = p1.w;
           }
-          float so = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              if constexpr (SPLIT) {
-                const bool ob = (om[c >> 2] >> ((8 * c + i) & 31)) & 1u;
-                if (ob) so = fmaf(v[c][i], v[c][i], so);
-                else ss = fmaf(v[c][i], v[c][i], ss);
-              } else {
-                ss = fmaf(v[c][i], v[c][i], ss);
-              }
-              mx = fmaxf(mx, fabsf(v[c][i]));
-            }
-          if constexpr (SPLIT) {
-            ss += xor32f(ss);
-            so += xor32f(so);
-            so2[nb] = so;
-            nxv[nb] = sqrtf(ss);        // regular instance's norm
-            ss += so;
-          } else {
-            ss += xor32f(ss);
-          }
+            for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(v[c][i]));
           mx = fmaxf(mx, xor32f(mx));
           // 2^(14 - floor(log2 mx)) from the exponent field of mx
           const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
           const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+          // squares summed over the scaled values (none underflows)
+          float so = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             float sc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sc[i] = v[c][i] * p2;
+            for (int i = 0; i < 8; ++i) {
+              sc[i] = v[c][i] * p2;
+              if constexpr (SPLIT) {
+                const bool ob = (om[c >> 2] >> ((8 * c + i) & 31)) & 1u;
+                so = fmaf(ob ? sc[i] : 0.f, sc[i], so);
+                ss = fmaf(ob ? 0.f : sc[i], sc[i], ss);
+              } else {
+                ss = fmaf(sc[i], sc[i], ss);
+              }
+            }
             split8h(sc, xh[nb][c], xl[nb][c], m1);
+          }
+          ss += xor32f(ss);
+          nd[nb] = p2;
+          if constexpr (SPLIT) {
+            so += xor32f(so);
+            so2[nb] = so;                 // outliers, scaled
+            nxv[nb] = sqrtf(ss) / p2;     // regular instance's norm
           }
           wsc[nb] = 16.f * p2;
         }
         if constexpr (!SPLIT) {
-          nxv[nb] = sqrtf(ss);
+          nxv[nb] = sqrtf(ss) / nd[nb];
           // A zero vector encodes y = 0: thresholds and residual in unit scale.
           sx[nb] = nxv[nb] > 0.f ? nxv[nb] : 1.f;
           wsc[nb] *= sx[nb];
@@ -644,7 +673,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       if constexpr (SPLIT) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          nxo[nb] = sqrtf(so2[nb]);
+          nxo[nb] = sqrtf(so2[nb]) / nd[nb];
           const float wso = wsc[nb] * (nxo[nb] > 0.f ? nxo[nb] : 1.f);
           const float wsr = wsc[nb] * (nxv[nb] > 0.f ? nxv[nb] : 1.f);
           rso[nb] = 32.f / wso;
@@ -1156,9 +1185,35 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
     }
     float ss = s0 + s1;
     ss += xor32f(ss);
-    const float nxv = sqrtf(ss);
-    const float sx = nxv > 0.f ? nxv : 1.f;  // a zero vector encodes y = 0
-    const float wsc = kSqrtD * sx;           // accumulator = wsc * (unit-vector coordinate)
+    // Norms below 2^-50 (whose squares may be denormal or flushed) and zero
+    // vectors: the wave scales every vector by 2^e from its largest element
+    // and sums the squares again.  The scaling is exact, so vectors of
+    // ordinary size get the same values as without it.  Zeros become +0
+    // here: the sign flips make -0 inputs, and a butterfly of two -0 is -0,
+    // which only an all-zero vector could carry to the output, where the
+    // quantizer reads sign bits.
+    float nd = 1.f;  // stored norm = sqrt(ss) / nd
+    if (__ballot(!(ss >= 0x1p-100f)) != 0) {
+      float mx = 0.f;
+#pragma unroll
+      for (int t = 0; t < 64; ++t) mx = fmaxf(mx, fabsf(v[t]));
+      mx = fmaxf(mx, xor32f(mx));
+      const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
+      nd = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
+      float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 64; t += 2) {
+        v[t] = v[t] * nd + 0.f;  // -0 -> +0
+        v[t + 1] = v[t + 1] * nd + 0.f;
+        q0 = fmaf(v[t], v[t], q0);
+        q1 = fmaf(v[t + 1], v[t + 1], q1);
+      }
+      ss = q0 + q1;
+      ss += xor32f(ss);
+    }
+    const float nxv = sqrtf(ss) / nd;
+    const float sx = ss > 0.f ? sqrtf(ss) : 1.f;  // a zero vector encodes y = 0
+    const float wsc = kSqrtD * sx;                // accumulator = wsc * (unit-vector coordinate)
     // ------------------------------------------------ Walsh-Hadamard
 #pragma unroll
     for (int st = 1; st < 64; st <<= 1)

@@ -47,29 +47,28 @@ __global__ __launch_bounds__(256) void rowprep_kernel(const void* x, int x_bf16,
     if (x_bf16) return __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[row * ld + i]) << 16);
     return static_cast<const float*>(x)[row * ld + i];
   };
-  float ss = 0.f, mx = 0.f;
-  for (int i = lane; i < d; i += 64) {
-    const float v = at(i);
-    ss = fmaf(v, v, ss);
-    mx = fmaxf(mx, fabsf(v));
-  }
+  float mx = 0.f;
+  for (int i = lane; i < d; i += 64) mx = fmaxf(mx, fabsf(at(i)));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    ss += __shfl_xor(ss, o, 64);
-    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
   const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(253, max(1, 268 - ebits))) << 23) : 1.f;
+  // the squares are summed over x 2^e, so none underflows whatever the
+  // row's magnitude (the scaling is exact: n_x is the same for ordinary rows)
+  float ss = 0.f;
   uint16_t* out = xcat + row * 3 * d;
   for (int i = lane; i < d; i += 64) {
     const float v = at(i) * p2;
+    ss = fmaf(v, v, ss);
     const uint16_t h = f16b(v);
     out[i] = h;
     out[d + i] = h;
     out[2 * d + i] = f16b(v - f16v(h));
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if (lane == 0) {
-    const float n = sqrtf(ss);
+    const float n = sqrtf(ss) / p2;
     nx[row] = n;
     w[row] = 16.f * p2 * (n > 0.f ? n : 1.f);
   }

@@ -101,6 +101,43 @@ def test_append_fp32_input():
     _run("keys", dtype=torch.float32)
 
 
+@pytest.mark.parametrize("kind", ["keys", "values"])
+def test_append_special_rows(kind):
+    """One appended vector per head: zeros, -0, magnitudes near 1e-30 (whose
+    squares underflow fp32), one nonzero coordinate, near 1e3, and a Gaussian
+    row (bf16), into slot 0; against the oracle's encode of the same rows."""
+    H = 6
+    g = torch.Generator().manual_seed(47)
+    x = torch.randn(H, 128, generator=g)
+    x[0] = 0.0
+    x[1] = -torch.zeros(128)
+    x[2] *= 1e-30
+    x[3] = 0.0
+    x[3, 77] = -1.5
+    x[4] *= 1e3
+    xb = x.to(torch.bfloat16)
+    if kind == "keys":
+        cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=31, seed_sketch=32)
+        codec = o.turboquant_codec(128, 3, "prod", rot_seed=31, sketch_seed=32)
+    else:
+        cb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=31, layout=tq.TQ_LAYOUT_COL)
+        codec = o.turboquant_codec(128, 4, "mse", rot_seed=31, layout="col")
+    cap = 64
+    per = cb.records_bytes(cap)
+    rec = torch.zeros(H * per, dtype=torch.uint8, device=DEV)
+    tq.append(cb, xb.reshape(1, H, 128).to(DEV), rec, torch.zeros(1, dtype=torch.int32, device=DEV), cap)
+    torch.cuda.synchronize()
+    buf = rec.cpu().numpy()
+    ref = o.encode(codec, xb.double().numpy())
+    heads = [o.unpack(codec, buf[h * per:(h + 1) * per], cap) for h in range(H)]
+    got = o.Encoded(np.stack([e.idx[0] for e in heads]),
+                    None if ref.signs is None else np.stack([e.signs[0] for e in heads]),
+                    np.array([e.nx[0] for e in heads]),
+                    None if ref.nr is None else np.array([e.nr[0] for e in heads]), None, None)
+    say(kind, check_encoded(codec, ref, got))
+    assert float(got.nx[0]) == 0.0 and float(got.nx[1]) == 0.0
+
+
 def test_decode_after_append():
     kcb, kc, krec, kfull, L0, steps, K = _run("keys")
     vcb, vc, vrec, vfull, _, _, V = _run("values")

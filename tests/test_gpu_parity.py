@@ -92,6 +92,46 @@ def test_zero_vectors_and_empty():
     assert out.shape[0] == 16
 
 
+@pytest.mark.parametrize("kind", ["keys", "values", "keys_fp32", "keys_hadamard", "values_hadamard"])
+def test_bf16_special_rows(kind):
+    """Rows that are all +0, all -0, one nonzero coordinate, signed zeros
+    among nonzeros, and magnitudes near 1e-30 (whose squares underflow fp32:
+    the encoders' scaled norm path) and 1e3, among Gaussian rows, 100 rows
+    (one full tile and a ragged one), bf16 (fp32 for keys_fp32), dense or
+    Hadamard rotation: codes, signs and norms against the oracle under the
+    usual rules; the all-zero rows store n_x = 0 and, for keys, the signs of
+    S(0 - c)."""
+    n = 100
+    g = torch.Generator().manual_seed(41)
+    x = torch.randn(n, 128, generator=g)
+    x[3] = 0.0
+    x[4] = -torch.zeros(128)
+    x[5] = 0.0
+    x[5, 17] = -2.5
+    x[6, ::2] = -0.0
+    x[7, 1::3] = 0.0
+    x[8] *= 1e-30
+    x[9] *= 1e3
+    x[70] = -torch.zeros(128)
+    xb = x if kind == "keys_fp32" else x.to(torch.bfloat16)
+    rot = {"rotation": tq.TQ_ROT_HADAMARD} if kind.endswith("hadamard") else {}
+    orot = {"rotation": "hadamard"} if kind.endswith("hadamard") else {}
+    if kind.startswith("keys"):
+        cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=21, seed_sketch=22, **rot)
+        codec = o.turboquant_codec(128, 3, "prod", rot_seed=21, sketch_seed=22, **orot)
+    else:
+        cb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=21, layout=tq.TQ_LAYOUT_COL, **rot)
+        codec = o.turboquant_codec(128, 4, "mse", rot_seed=21, layout="col", **orot)
+    ref = o.encode(codec, xb.double().numpy())
+    got = o.unpack(codec, gpu_records(cb, xb), n)
+    say(kind, check_encoded(codec, ref, got))
+    for r in (3, 4, 70):
+        assert float(got.nx[r]) == 0.0
+        if kind.startswith("keys"):
+            assert np.array_equal(got.signs[r], ref.signs[r])
+    assert float(got.nx[8]) == float(ref.nx[8])
+
+
 # --------------------------------------------------------- bf16 KV workload
 def kv_inputs(heads, tokens, seed):
     law = synth.KVLaw(heads, 128, synth.seed(2, "calibration"))

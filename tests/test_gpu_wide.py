@@ -37,6 +37,27 @@ def encoded_rows(enc, rows):
                      None if enc.z is None else enc.z[rows])
 
 
+def test_encode_d1536_special_rows():
+    """Rows of zeros, of -0, one nonzero coordinate, and magnitudes near 1e-30
+    and 1e3 (70 rows, fp32), against the oracle; zero rows store n_x = 0."""
+    g = torch.Generator().manual_seed(43)
+    x = torch.randn(70, D, generator=g)
+    x[2] = 0.0
+    x[3] = -torch.zeros(D)
+    x[4] = 0.0
+    x[4, 700] = 3.0
+    x[5] *= 1e-30
+    x[6] *= 1e3
+    cb = tq.Codebook(D, tq.TQ_PROD, 2, seed_rotation=503, seed_sketch=504)
+    codec = o.turboquant_codec(D, 2, "prod", rot_seed=503, sketch_seed=504)
+    rec = tq.encode(cb, x.to(DEV))
+    torch.cuda.synchronize()
+    ref = o.encode(codec, x.double().numpy())
+    got = o.unpack(codec, rec.cpu().numpy(), 70)
+    say(check_encoded(codec, ref, got))
+    assert float(got.nx[2]) == 0.0 and float(got.nx[3]) == 0.0
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_encode_d1536(bits):
     """1000 vectors: 16 tiles with a ragged tail, against the oracle."""
