@@ -542,7 +542,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             const int ebits = int((__float_as_uint(mx) >> 23) & 0xff);
             const float p2 = mx > 0.f ? __uint_as_float(uint32_t(min(254, max(1, 268 - ebits))) << 23) : 1.f;
             // x * 2^e is exact in fp16 (8 significant bits, exponent in range)
-            float t0 = 0.f, t1 = 0.f, u0 = 0.f, u1 = 0.f;  // scaled squares (SPLIT: u outliers)
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -550,23 +549,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 const float lo = __uint_as_float(r[c][i] << 16) * p2;
                 const float hi = __uint_as_float(r[c][i] & 0xffff0000u) * p2;
                 xh[nb][c][i] = f16b(lo) | (f16b(hi) << 16);
-                if constexpr (SPLIT) {
-                  const int k = (8 * c + 2 * i) & 31;
-                  const bool olo = (om[c >> 2] >> k) & 1u, ohi = (om[c >> 2] >> (k + 1)) & 1u;
-                  u0 = fmaf(olo ? lo : 0.f, lo, u0);
-                  u1 = fmaf(ohi ? hi : 0.f, hi, u1);
-                  t0 = fmaf(olo ? 0.f : lo, lo, t0);
-                  t1 = fmaf(ohi ? 0.f : hi, hi, t1);
-                } else {
-                  t0 = fmaf(lo, lo, t0);
-                  t1 = fmaf(hi, hi, t1);
-                }
               }
-            float tt = t0 + t1;
+            // squares of the scaled values (none underflows), from the row in
+            // memory again: a rare path, kept as a short loop
+            const int64_t tr = valid[nb] ? t : a.tokens - 1;
+            const uint16_t* xrow = reinterpret_cast<const uint16_t*>(xbase) + tr * a.xs_t + 64 * hh;
+            float tt = 0.f, uu = 0.f;  // SPLIT: uu sums the outlier channels
+#pragma unroll 1
+            for (int e = 0; e < 64; ++e) {
+              const float xe = __uint_as_float(uint32_t(xrow[e]) << 16) * p2;
+              bool ob = false;
+              if constexpr (SPLIT) ob = ((e < 32 ? om[0] : om[1]) >> (e & 31)) & 1u;
+              uu = fmaf(ob ? xe : 0.f, xe, uu);
+              tt = fmaf(ob ? 0.f : xe, xe, tt);
+            }
             tt += xor32f(tt);
             nd[nb] = p2;
             if constexpr (SPLIT) {
-              float uu = u0 + u1;
               uu += xor32f(uu);
               nxv[nb] = sqrtf(tt) / p2;  // regular instance's norm
               so2[nb] = uu;              // outliers, scaled
@@ -1185,13 +1184,32 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
     }
     float ss = s0 + s1;
     ss += xor32f(ss);
+    // ------------------------------------------------ Walsh-Hadamard
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1)
+#pragma unroll
+      for (int t = 0; t < 64; ++t)
+        if (!(t & st)) {
+          const float p = v[t], q = v[t + st];
+          v[t] = p + q;
+          v[t + st] = p - q;
+        }
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[t]), __float_as_uint(v[t + 32]), false, false);
+      const float A = __uint_as_float(sw[0]), B = __uint_as_float(sw[1]);
+      v[t] = A + B;       // P_t: dim 32 hh + t
+      v[t + 32] = A - B;  // M_t: dim 64 + 32 hh + t
+    }
     // Norms below 2^-50 (whose squares may be denormal or flushed) and zero
-    // vectors: the wave scales every vector by 2^e from its largest element
-    // and sums the squares again.  The scaling is exact, so vectors of
-    // ordinary size get the same values as without it.  Zeros become +0
-    // here: the sign flips make -0 inputs, and a butterfly of two -0 is -0,
-    // which only an all-zero vector could carry to the output, where the
-    // quantizer reads sign bits.
+    // vectors: the wave scales every transformed vector by 2^e from its
+    // largest coordinate and sums the squares again (the transform has
+    // sum (Hx)_i^2 = 128 ||x||^2).  The scaling is exact and commutes with
+    // the butterflies, so vectors of ordinary size get the same values as
+    // without it.  Zeros become +0 here: the sign flips make -0 inputs and a
+    // butterfly of two -0 is -0, which only an all-zero vector can carry to
+    // the output, where the quantizer reads sign bits.  Placed after the
+    // transform, so that the butterflies overlap the norm's reduction.
     float nd = 1.f;  // stored norm = sqrt(ss) / nd
     if (__ballot(!(ss >= 0x1p-100f)) != 0) {
       float mx = 0.f;
@@ -1210,27 +1228,11 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
       }
       ss = q0 + q1;
       ss += xor32f(ss);
+      ss *= 1.f / 128.f;
     }
     const float nxv = sqrtf(ss) / nd;
     const float sx = ss > 0.f ? sqrtf(ss) : 1.f;  // a zero vector encodes y = 0
     const float wsc = kSqrtD * sx;                // accumulator = wsc * (unit-vector coordinate)
-    // ------------------------------------------------ Walsh-Hadamard
-#pragma unroll
-    for (int st = 1; st < 64; st <<= 1)
-#pragma unroll
-      for (int t = 0; t < 64; ++t)
-        if (!(t & st)) {
-          const float p = v[t], q = v[t + st];
-          v[t] = p + q;
-          v[t + st] = p - q;
-        }
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[t]), __float_as_uint(v[t + 32]), false, false);
-      const float A = __uint_as_float(sw[0]), B = __uint_as_float(sw[1]);
-      v[t] = A + B;       // P_t: dim 32 hh + t
-      v[t + 32] = A - B;  // M_t: dim 64 + 32 hh + t
-    }
     // ------------------------------------------------ quantize
     f32x16v T = {};
 #pragma unroll
