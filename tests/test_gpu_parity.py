@@ -59,6 +59,20 @@ def test_score_prod_d128():
     say("max scaled error", r)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encode_mse_row_bf16(bits):
+    """TurboQuant-mse with row records from bf16 KV rows (the row-layout value
+    encode), 777 vectors over two heads' worth of tiles, against the oracle."""
+    n = 777
+    law = synth.KVLaw(1, 128, 61)
+    x = synth.kv_cache(1, 1, n, 128, 62, law)[0, 0]
+    cb = tq.Codebook(128, tq.TQ_MSE, bits, seed_rotation=63)
+    codec = o.turboquant_codec(128, bits, "mse", rot_seed=63)
+    ref = o.encode(codec, x.double().numpy())
+    got = o.unpack(codec, gpu_records(cb, x), n)
+    say(bits, check_encoded(codec, ref, got))
+
+
 @pytest.mark.parametrize("bits,mode", [(2, tq.TQ_MSE), (4, tq.TQ_MSE), (2, tq.TQ_PROD), (5, tq.TQ_PROD)])
 def test_encode_and_score_other_bits(bits, mode):
     say(f"bits={bits} mode={mode}")
