@@ -442,7 +442,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // SPLIT: outlier boundary t_2 and levels c_2, c_3 (dim 0), regular
       // level c_1 (dim 8), and this half's outlier-channel mask (channels
       // 64 hh ..); read here, per tile, so that they stay in registers
-      float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f;
+      float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f, spl_lo = 0.f, spl_hi = 0.f;
       uint32_t om[2] = {0u, 0u};
       if constexpr (SPLIT) {
         const float* th = cv.thr + size_t(hc) * D * kMaxLevels;
@@ -451,6 +451,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         spl_c2 = 32.f * ce[2];
         spl_c3 = 32.f * ce[3];
         spl_c1 = 32.f * ce[8 * kMaxLevels + 1];
+        spl_lo = hh ? spl_c1 : spl_c2;  // level magnitude below / above t_2
+        spl_hi = hh ? spl_c1 : spl_c3;  // (half 1: the regular level)
         om[0] = cv.omask[hc * 4 + 2 * hh];
         om[1] = cv.omask[hc * 4 + 2 * hh + 1];
       }
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           const float wsr = wsc[nb] * (nxv[nb] > 0.f ? nxv[nb] : 1.f);
           rso[nb] = 32.f / wso;
           rsr[nb] = 32.f / wsr;
-          P2o[nb] = spl_t2 * wso;
+          P2o[nb] = hh ? -INFINITY : spl_t2 * wso;  // half 1 holds no outliers
           rro[nb] = 0.f;
           p1w[nb] = 0u;
         }
@@ -731,20 +733,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             if constexpr (SPLIT) {
               // registers 0..7 of half 0: outlier, 2 index bits (symmetric
               // 4-level search: bit 1 = [v >= 0], bit 0 = [v >= 0] == [|v| >= t_2]);
-              // all others: regular, 1 bit = [v >= 0] (2 symmetric levels)
-              const bool pos = v >= 0.f;
-              const uint64_t mp = __ballot(pos);
+              // all others: regular, 1 bit = [v >= 0] (2 symmetric levels).
+              // Each pushed bit is the complement of the index bit (flipped
+              // per word after the block): the sign bit of v (never -0), or for
+              // the outliers' bit 0 the sign bit of v xor (|v| - t_2), since
+              // [v < 0] xor [|v| < t_2] = not ([v >= 0] == [|v| >= t_2]).  On
+              // half 1, P2o = -inf makes |v| - P2o positive, so registers 0..7
+              // push the sign bit of v there too.
+              const uint32_t vb = __float_as_uint(v);
               if (r < 8) {
-                const bool big = fabsf(v) >= P2o[nb];
-                const uint64_t mm = __ballot(big);
-                constexpr uint64_t kHalf0 = 0x00000000ffffffffull;
-                cw[nb][0] = push_mask(cw[nb][0], (~(mp ^ mm) & kHalf0) | (mp & ~kHalf0));
-                p1w[nb] = push_mask(p1w[nb], mp);  // plane 1 (kept from half 0)
-                const float c = hh ? spl_c1 : (big ? spl_c3 : spl_c2);
-                chat = pos ? c : -c;
+                const float u = fabsf(v) - P2o[nb];
+                cw[nb][0] = __builtin_amdgcn_alignbit(cw[nb][0], vb ^ __float_as_uint(u), 31);
+                p1w[nb] = __builtin_amdgcn_alignbit(p1w[nb], vb, 31);  // plane 1 (kept from half 0)
+                const float c = u >= 0.f ? spl_hi : spl_lo;
+                chat = __uint_as_float(__float_as_uint(c) | (vb & 0x80000000u));
               } else {
-                cw[nb][0] = push_mask(cw[nb][0], mp);
-                chat = pos ? spl_c1 : -spl_c1;
+                cw[nb][0] = __builtin_amdgcn_alignbit(cw[nb][0], vb, 31);
+                chat = __uint_as_float(__float_as_uint(spl_c1) | (vb & 0x80000000u));
               }
             } else if (UNIFORM && !COL) {
               // row layout: the index bits go straight into the plane words
@@ -859,6 +864,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
           }
           if constexpr (SYM2) sym2_finish(cw[nb][0], cw[nb][NPL - 1], 0xffffu);
+          if constexpr (SPLIT) cw[nb][0] ^= 0xffffu;  // complemented pushes
           if (!COL) {
             // row layout: half hh holds bits 16 hh .. 16 hh + 15 of each word;
             // slots past the end of the input are zero
@@ -975,7 +981,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             // plane 1 (4 bytes per vector, [64][4] at 64 * 16): bit 8 mb + r =
             // bit 1 of outlier coordinate 8 mb + r; block mb's pushes sit in
             // byte 3 - mb, hence the byte swap
-            const uint32_t mine = hh ? 0u : __builtin_bswap32(p1w[nb]);
+            const uint32_t mine = hh ? 0u : __builtin_bswap32(~p1w[nb]);  // complemented pushes
             const uint32_t w = valid[nb] ? (mine | xor32(mine)) : 0u;
             *reinterpret_cast<uint32_t*>(trec + size_t(kTile) * 16 + size_t(slot) * 4) = w;
           } else if (!UNIFORM) {
