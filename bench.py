@@ -46,7 +46,7 @@ DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decod
 # are in profiles/.  Keyed by (workload, call): a reading holds for that
 # launch size only, and for the kernels as built when the counters were
 # taken; a pair missing here reports null.
-TRAFFIC = {("gqa_layer", "encode_keys"): 81995948, ("gqa_layer", "encode_values"): 94153294}
+TRAFFIC = {("gqa_layer", "encode_keys"): 82039249, ("gqa_layer", "encode_values"): 94172737}
 
 
 def parse():
