@@ -29,19 +29,13 @@
 namespace tq {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
-constexpr int LDS_ROW = D + 8;  // bf16 elements per staged row (16-byte pad)
-
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
+constexpr int LDS_ROW = D + 8;  // 16-bit elements per staged row (16-byte pad)
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 
@@ -52,9 +46,6 @@ __device__ __forceinline__ f32x16 mfma32h(u32x4 a, u32x4 b, f32x16 c) {
 
 __device__ __forceinline__ uint32_t f16b(float x) {
   return uint32_t(__builtin_bit_cast(uint16_t, (_Float16)x));
-}
-__device__ __forceinline__ float f16v(uint32_t h) {
-  return float(__builtin_bit_cast(_Float16, uint16_t(h)));
 }
 
 // -1.0f in a scalar register the compiler cannot see through: fma(h, m1, x)
@@ -79,23 +70,6 @@ __device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo, fl
     hi[i] = __builtin_bit_cast(uint32_t, h);
     lo[i] = uint32_t(__builtin_bit_cast(uint16_t, _Float16(r0))) |
             (uint32_t(__builtin_bit_cast(uint16_t, _Float16(r1))) << 16);
-  }
-}
-
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)x));
-}
-__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
-
-// Pack 8 floats into bf16 hi and lo fragments (x ~= hi + lo).
-__device__ __forceinline__ void split8(const float* v, u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = bf16_bits(v[2 * i]), h1 = bf16_bits(v[2 * i + 1]);
-    const uint32_t l0 = bf16_bits(v[2 * i] - bf16_val(h0));
-    const uint32_t l1 = bf16_bits(v[2 * i + 1] - bf16_val(h1));
-    hi[i] = h0 | (h1 << 16);
-    lo[i] = l0 | (l1 << 16);
   }
 }
 
