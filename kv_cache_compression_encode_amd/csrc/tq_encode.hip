@@ -1078,6 +1078,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
 __host__ __device__ constexpr int had_dim(int hh, int k) {  // dim held in register k (0..63) of half hh
   return k < 32 ? 32 * hh + k : 64 + 32 * hh + (k - 32);
 }
+static_assert(had_dim(0, 0) == 0 && had_dim(1, 0) == 32 && had_dim(0, 32) == 64 && had_dim(1, 63) == 127,
+              "the two halves' registers cover dims 0..127 in blocks of 32");
 
 // Stage S (fp16 [128][128]) with rows placed by lds_row_of and LDS column
 // 16c + 8h + i holding S column had_dim(h, 8c + i).

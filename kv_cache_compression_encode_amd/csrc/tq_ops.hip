@@ -294,8 +294,6 @@ __global__ __launch_bounds__(256) void score_kernel(CodecView cv, const float* q
 }
 
 // ------------------------------------------------------------ decode
-constexpr int kMaxG = 8;
-
 // Split-K partial: block (split, kv head g, sequence b), 4 waves each taking
 // tiles of the split in turn.  Partial record per (b, g, split):
 // [G] max, [G] sum, [G][128] accumulator.
@@ -594,8 +592,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CodecView vc, Decod
 }
 
 // ------------------------------------------------------------------ top-k
-constexpr int kTopMax = 16;
-
 __device__ __forceinline__ bool better(float s1, int64_t i1, float s2, int64_t i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
