@@ -538,8 +538,8 @@ DEFAULT_STEPS = {"gqa_layer": (50, 5), "gqa_outlier": (50, 5), "small": (200, 10
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures "
-              "no multi-GPU figure", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): there is no "
+              "multi-GPU figure", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe()

@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   TQ_OK = 0,
   TQ_EINVAL = 1,        /* bad argument: null pointer, non-positive size, bad enum  */
-  TQ_EUNSUPPORTED = 2,  /* valid request this build does not implement (e.g. d)    */
+  TQ_EUNSUPPORTED = 2,  /* valid request the library does not implement (e.g. d)  */
   TQ_EALIGN = 3,        /* a pointer or stride violates the stated alignment       */
   TQ_ENOMEM = 4,        /* device or host allocation failed (codebook build only)  */
   TQ_EWORKSPACE = 5,    /* workspace missing or smaller than tq_workspace_size     */

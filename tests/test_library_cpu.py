@@ -5,6 +5,7 @@ before anything is launched.  No kernel runs here."""
 import ctypes
 import os
 import re
+import sys
 
 import numpy as np
 import pytest
@@ -231,3 +232,14 @@ def test_outlier_split_argument_errors():
         tq.Codebook(128, tq.TQ_MSE, 2, outlier_channels=ch, outlier_bits=3, layout=tq.TQ_LAYOUT_COL, device=-1)
     with pytest.raises(tq.TQError):      # d = 128 only
         tq.Codebook(256, tq.TQ_PROD, 2, outlier_channels=ch, outlier_bits=3, device=-1)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and a message,
+    before touching any device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
