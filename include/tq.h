@@ -194,20 +194,6 @@ typedef struct {
 tq_status tq_codebook_build(const tq_codebook_desc* desc, tq_codebook** out);
 tq_status tq_codebook_free(tq_codebook* cb);
 
-/* Discrete reverse water-filling of index bits over dimensions with variances
- * lambda ([SQ] tweet 6: water-filling of the bits over the dominant dims,
- * after Shannon and Berger).  Host only; no device work.
- *   lambda      host [d] variances (>= 0) of the rotated coordinates.
- *   total_bits  index bits to hand out, d*min_bits <= total_bits <= d*max_bits.
- *   min_bits, max_bits  per-dim range, 1 <= min_bits <= max_bits <= 5.
- *   bits_out    host [d], written.
- * Every dim starts at min_bits; then, one bit at a time, the dim with the
- * largest drop lambda_i (D(b_i) - D(b_i + 1)) of its distortion gets the bit,
- * D(b) being the mean squared error of the b-bit Lloyd-Max quantizer of the
- * standard normal law (ties to the lower dim).  D is convex in b, so this
- * greedy allocation minimises sum_i lambda_i D(b_i) under the budget.
- * TQ_EINVAL on a null pointer, d < 1, a negative lambda or a budget or range
- * outside the bounds above. */
 /* Append-on-decode (d = 128): encode one new vector per (sequence, head) into
  * its existing records, at token index positions[b] of sequence b.
  * TurboQuant also quantizes the tokens generated during decoding (TurboQuant
@@ -230,6 +216,20 @@ tq_status tq_append(const tq_codebook* cb, const void* x, int32_t x_dtype, int32
                     int64_t xs_b, int64_t xs_h, void* records, int64_t rs_b, int64_t rs_h,
                     const int32_t* positions, int32_t capacity, void* stream);
 
+/* Discrete reverse water-filling of index bits over dimensions with variances
+ * lambda ([SQ] tweet 6: water-filling of the bits over the dominant dims,
+ * after Shannon and Berger).  Host only; no device work.
+ *   lambda      host [d] variances (>= 0) of the rotated coordinates.
+ *   total_bits  index bits to hand out, d*min_bits <= total_bits <= d*max_bits.
+ *   min_bits, max_bits  per-dim range, 1 <= min_bits <= max_bits <= 5.
+ *   bits_out    host [d], written.
+ * Every dim starts at min_bits; then, one bit at a time, the dim with the
+ * largest drop lambda_i (D(b_i) - D(b_i + 1)) of its distortion gets the bit,
+ * D(b) being the mean squared error of the b-bit Lloyd-Max quantizer of the
+ * standard normal law (ties to the lower dim).  D is convex in b, so this
+ * greedy allocation minimises sum_i lambda_i D(b_i) under the budget.
+ * TQ_EINVAL on a null pointer, d < 1, a negative lambda or a budget or range
+ * outside the bounds above. */
 tq_status tq_water_fill(const double* lambda, int32_t d, int32_t total_bits, int32_t min_bits,
                         int32_t max_bits, uint8_t* bits_out);
 tq_status tq_codebook_get_info(const tq_codebook* cb, tq_codebook_info* info);
@@ -247,7 +247,12 @@ tq_status tq_codebook_export(const tq_codebook* cb, int32_t head, float* rot, fl
 int64_t tq_records_bytes(const tq_codebook* cb, int64_t n);
 
 /* Encode a batch of vector sets.  [TQ] "Method": n_x = ||x||, y = Pi x/n_x,
- * idx_i = #{boundaries t of dim i with t <= y_i} (ties to the upper cell); prod:
+ * idx_i = #{boundaries t of dim i with t <= y_i}, so a y_i exactly on a
+ * boundary goes to the upper cell -- except in the d = 128 kernels of uniform
+ * codecs, which search |y_i| among the positive boundaries (the codebook is
+ * symmetric) and put a negative y_i exactly on a boundary into the lower cell,
+ * the one of larger magnitude (both readings agree everywhere off the
+ * boundaries); prod:
  * r = y - c[idx] on dims 0..m-1, n_r = ||r||, bit_j = [(S r)_j >= 0].  A zero
  * vector encodes y = 0 and stores n_x = 0.
  *   x        device, element (b, h, t, i) at x[b*xs_b + h*xs_h + t*xs_t + i] of
@@ -311,6 +316,9 @@ typedef struct {
  *   vcb      COL mse codec of the values (num_heads 1 or Hkv); same d = 128.
  *   q        device [B][Hq][d] of q_dtype;  out device fp32 [B][Hq][d].
  *   workspace >= tq_workspace_size(kcb, TQ_OP_DECODE, B*Hq, max_tokens, Hkv). */
+/* A sequence with no tokens (seq_lens[b] = 0, or max_tokens = 0) gets an
+ * all-zero output; with max_tokens = 0 no record, block-table entry or
+ * workspace byte is read. */
 tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
                            int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
                            const tq_kv_view* kv, float softmax_scale, float* out,

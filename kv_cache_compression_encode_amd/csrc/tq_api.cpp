@@ -800,6 +800,12 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   if (const tq_status ps = check_paging(kv, &page_shift); ps != TQ_OK) return ps;
   if (B == 0) return TQ_OK;
   if (B > 65535 || decode_nsplit(kv->max_tokens) > 1024) return TQ_EUNSUPPORTED;
+  if (kv->max_tokens == 0) {
+    // an empty cache: every output is zero, no record or workspace is touched
+    if (checks_only) return TQ_OK;
+    if (hipSetDevice(kcb->device) != hipSuccess) return TQ_EDEVICE;
+    return map_hip(launch_fill_zero(out, int64_t(B) * Hq * 128, static_cast<hipStream_t>(stream)));
+  }
   const int64_t nqt = int64_t(B) * Hq;
   if (!workspace || workspace_bytes < tq_workspace_size(kcb, TQ_OP_DECODE, nqt, kv->max_tokens, Hkv))
     return TQ_EWORKSPACE;
@@ -885,6 +891,9 @@ tq_status tq_decode_step(const tq_codebook* kcb, const tq_codebook* vcb, const v
   tq_status st = decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace,
                              workspace_bytes, stream, 1, true);
   if (st != TQ_OK || B == 0) return st;
+  if (kv->max_tokens == 0)  // no slot to append to: the attention over nothing is zero
+    return decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace, workspace_bytes,
+                       stream, 1, false);
   if (kcb->info.num_heads > 1 && kcb->info.num_heads != Hkv) return TQ_EINVAL;
   const CodecView kc = make_view(kcb), vc = make_view(vcb);
   if (!append_supported(kc) || !append_supported(vc)) return TQ_EUNSUPPORTED;

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // (the entries past them need not name pages).
   if (!a.block_table) {
     const int tmax = (a.max_tokens + kTile - 1) / kTile;
-    load_tile(min(t_begin + wave, tmax - 1), ra);
+    if (tmax > 0) load_tile(min(t_begin + wave, tmax - 1), ra);
   } else if (t_begin + wave < t_end) {
     load_tile(t_begin + wave, ra);
   }

@@ -461,12 +461,21 @@ def encode(codec: Codec, x: np.ndarray, head: int = 0, round_norms: bool = True)
     store = (lambda v: v.astype(np.float16)) if round_norms else (lambda v: v)
     if codec.mode == "mse":
         return Encoded(idx, None, store(nx), None, y, None)
+    nr, z = residual_sketch(codec, y, idx, head)
+    return Encoded(idx, z >= 0, store(nx), store(nr), y, z)
+
+
+def residual_sketch(codec: Codec, y: np.ndarray, idx: np.ndarray, head: int = 0):
+    """The QJL stage of TurboQuant-prod for given codes (paper review,
+    "Method"): the residual r = y - c[idx] on dims 0..m-1, its norm n_r (fp64)
+    and the sketch z = S r, whose signs are stored.  encode() calls it with its
+    own codes; the comparison rules call it with another quantizer's codes."""
     m = codec.m
     chat = dequantize(codec, idx, head)
     r = y[:, :m] - chat[:, :m]                   # residual of the mse stage
     nr = np.sqrt(np.sum(r * r, axis=1))
     z = r @ codec.sketch.T                       # S r
-    return Encoded(idx, z >= 0, store(nx), store(nr), y, z)
+    return nr, z
 
 
 def boundary_distance(codec: Codec, y: np.ndarray, head: int = 0) -> np.ndarray:
@@ -685,50 +694,50 @@ def unpack(codec: Codec, buf: np.ndarray, n: int) -> Encoded:
     tb = tile_bytes(codec)
     fields = dict((f[0], (f[1], f[2])) for f in tile_fields(codec))
     d = codec.d
+    tiles = buf[:ntile * tb].reshape(ntile, tb)
+
+    def field_rows(name, w):
+        # a [64 vectors][w bytes] field of every tile, as [ntile * 64][w]
+        fo, _ = fields[name]
+        return tiles[:, fo:fo + TILE * w].reshape(ntile * TILE, w)
+
     idx = np.zeros((ntile * TILE, d), dtype=np.int64)
-    sg = np.zeros((ntile * TILE, codec.m), dtype=bool) if codec.mode == "prod" else None
-    nx = np.zeros(ntile * TILE, np.float16)
-    nr = np.zeros(ntile * TILE, np.float16) if codec.mode == "prod" else None
-    pdims = plane_dims(codec.bits)
-    total_bits = int(codec.bits.sum())
-    for t in range(ntile):
-        base = t * tb
-        rows = slice(t * TILE, (t + 1) * TILE)
-        if codec.layout == "row":
-            nbytes = (total_bits + 7) // 8
-            cb = np.zeros((TILE, nbytes), np.uint8)
-            for j, (o, w) in enumerate(_chunks(nbytes)):
-                fo, _ = fields[f"code{j}"]
-                cb[:, o:o + w] = buf[base + fo: base + fo + TILE * w].reshape(TILE, w)
-            bitsarr = np.unpackbits(cb, axis=1, bitorder="little")[:, :total_bits].astype(np.int64)
-            k = 0
-            for p, dims in enumerate(pdims):
-                idx[rows, dims] |= bitsarr[:, k:k + len(dims)] << p
-                k += len(dims)
-            if sg is not None:
-                nb = (codec.m + 7) // 8
-                sb = np.zeros((TILE, nb), np.uint8)
-                for j, (o, w) in enumerate(_chunks(nb)):
-                    fo, _ = fields[f"sign{j}"]
-                    sb[:, o:o + w] = buf[base + fo: base + fo + TILE * w].reshape(TILE, w)
-                sg[rows] = np.unpackbits(sb, axis=1, bitorder="little")[:, :codec.m].astype(bool)
-        else:
-            b = int(codec.bits[0])
+    sg = None
+    if codec.layout == "row":
+        total_bits = int(codec.bits.sum())
+        nbytes = (total_bits + 7) // 8
+        cb = np.concatenate([field_rows(f"code{j}", w) for j, (_, w) in enumerate(_chunks(nbytes))], axis=1)
+        bitsarr = np.unpackbits(cb, axis=1, bitorder="little")[:, :total_bits]
+        small = np.zeros((ntile * TILE, d), dtype=np.uint8)
+        k = 0
+        for p, dims in enumerate(plane_dims(codec.bits)):
+            # a plane over a run of consecutive dims (every uniform codec) is a slice
+            cols = slice(dims[0], dims[-1] + 1) if dims[-1] - dims[0] + 1 == len(dims) else dims
+            small[:, cols] |= bitsarr[:, k:k + len(dims)] << np.uint8(p)
+            k += len(dims)
+        idx[:] = small
+        if codec.mode == "prod":
+            nb = (codec.m + 7) // 8
+            sb = np.concatenate([field_rows(f"sign{j}", w) for j, (_, w) in enumerate(_chunks(nb))], axis=1)
+            sg = np.unpackbits(sb, axis=1, bitorder="little")[:, :codec.m].astype(bool)
+    else:
+        b = int(codec.bits[0])
+        if codec.mode == "prod":
+            sg = np.zeros((ntile * TILE, codec.m), dtype=bool)
+        for t in range(ntile):
+            rows = slice(t * TILE, (t + 1) * TILE)
             fo, fl = fields["codes"]
-            per_dim = buf[base + fo: base + fo + fl].reshape(codec.d, 8 * b)
+            per_dim = tiles[t, fo:fo + fl].reshape(codec.d, 8 * b)
             for i in range(codec.d):
                 bits = np.unpackbits(per_dim[i], bitorder="little").reshape(TILE, b).astype(np.int64)
                 idx[rows, i] = (bits << np.arange(b)[None, :]).sum(axis=1)
             if sg is not None:
                 fo, fl = fields["signs"]
-                words = buf[base + fo: base + fo + fl].reshape(-1, 8)
+                words = tiles[t, fo:fo + fl].reshape(-1, 8)
                 for j in range(codec.m):
                     sg[rows, j] = np.unpackbits(words[j], bitorder="little").astype(bool)
-        fo, _ = fields["nx"]
-        nx[rows] = buf[base + fo: base + fo + 2 * TILE].view(np.float16)
-        if nr is not None:
-            fo, _ = fields["nr"]
-            nr[rows] = buf[base + fo: base + fo + 2 * TILE].view(np.float16)
+    nx = np.ascontiguousarray(field_rows("nx", 2)).view(np.float16).reshape(-1)
+    nr = np.ascontiguousarray(field_rows("nr", 2)).view(np.float16).reshape(-1) if codec.mode == "prod" else None
     return Encoded(idx[:n], None if sg is None else sg[:n], nx[:n],
                    None if nr is None else nr[:n], None, None)
 

@@ -108,12 +108,29 @@ def test_sq_decode_full_size_sampled():
         assert err <= 1e-3
 
 
+def _oracle_scores_of_records(codec, rec, n, qs, chunk_tiles=1024):
+    """The oracle's scores of sampled queries against all n GPU records,
+    unpacked and scored a chunk of tiles at a time, and the records' n_x."""
+    tb = o.tile_bytes(codec)
+    out, nx = [], []
+    for t0 in range(0, (n + 63) // 64, chunk_tiles):
+        t1 = min((n + 63) // 64, t0 + chunk_tiles)
+        rows = min(n, t1 * 64) - t0 * 64
+        enc = o.unpack(codec, rec[t0 * tb:t1 * tb].cpu().numpy(), rows)
+        out.append(o.score(codec, qs, enc))
+        nx.append(enc.nx.astype(np.float64))
+    return np.concatenate(out, axis=1), np.concatenate(nx)
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("bits", [2, 4])
 def test_vector_search_full_size_sampled(bits):
-    """1e6 x 1536 database, 1024 queries, top-10.  Encode parity on sampled
-    tiles; for sampled queries each returned (id, score) is checked against
-    the oracle's encoding and score of that vector, and recall@10 against the
-    exact fp64 top-10 is reported."""
+    """1e6 x 1536 database, 1024 queries, top-10, in the benchmark's launch
+    configuration.  Encode parity on sampled tiles; for sampled queries the
+    oracle scores all 1e6 GPU records, and the returned ids must be the
+    oracle's top-10 of those records except near-ties (within the score
+    tolerance of the 10th score), with every returned score within tolerance.
+    Recall@10 against the exact fp64 top-10 is reported."""
     n, nq, d, k = 1_000_000, 1024, 1536, 10
     say(f"vector search b={bits}: generate")
     law = synth.LowRankLaw(d, 64, 505, device=DEV)
@@ -134,15 +151,21 @@ def test_vector_search_full_size_sampled(bits):
         say("encode tile", t0, check_encoded(codec, ref, got))
     sample = [0, 1, 511, 1023]
     qs = q[sample].cpu().double().numpy()
-    recalls = []
+    say("vector search: oracle scores of all records for the sampled queries")
+    full, nx_all = _oracle_scores_of_records(codec, rec, n, qs)           # [len(sample)][n], [n]
     exact = np.concatenate([(x[i:i + 65536].cpu().double().numpy() @ qs.T)
                             for i in range(0, n, 65536)], axis=0).T        # [len(sample)][n]
+    recalls = []
     for j, r in enumerate(sample):
         assert np.all(np.diff(s[r]) <= 0)
         assert len(set(ids[r].tolist())) == k and ids[r].min() >= 0 and ids[r].max() < n
-        enc = o.encode(codec, x[torch.from_numpy(ids[r]).to(DEV)].cpu().double().numpy())
-        ref_s = o.score(codec, qs[j:j + 1], enc)[0]
-        check_scores(s[r][None, :], ref_s[None, :], qs[j:j + 1], enc.nx)
+        tol = 1e-3 * np.linalg.norm(qs[j]) * nx_all
+        assert np.all(np.abs(s[r] - full[j, ids[r]]) <= tol[ids[r]]), "returned scores off the oracle's"
+        rs, ri = o.topk(full[j:j + 1], k)
+        diff = set(ids[r].tolist()) ^ set(ri[0].tolist())
+        assert all(abs(full[j, i] - rs[0, -1]) <= 2 * tol[i] for i in diff), \
+            [(i, full[j, i] - rs[0, -1], tol[i]) for i in diff]
         true = set(np.argsort(-exact[j], kind="stable")[:k].tolist())
         recalls.append(len(true & set(ids[r].tolist())) / k)
+        say(f"query {r}: top-10 = oracle top-10 of the records up to {len(diff)} near-tie swaps")
     say(f"vector search b={bits}: recall@10 vs exact top-10 on {len(sample)} queries = {np.mean(recalls):.3f}")

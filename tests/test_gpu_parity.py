@@ -224,6 +224,27 @@ def test_decode_attend_gqa_batch_and_seq_lens():
     _decode_case(3, 16, 4, 300, seq_lens=[300, 1, 129])
 
 
+def test_decode_attend_empty_sequences():
+    # a sequence with no tokens attends to nothing: its output is zero (also
+    # when several splits see no tile); the others are unaffected
+    _decode_case(4, 8, 2, 700, seq_lens=[0, 700, 0, 65])
+
+
+def test_decode_attend_max_tokens_zero():
+    # an empty cache: all outputs zero, and no record is read (the record
+    # buffers here hold a single byte)
+    kcb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204)
+    vcb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=207, layout=tq.TQ_LAYOUT_COL)
+    q = torch.randn(2, 8, 128, device=DEV)
+    rec = torch.zeros(16, dtype=torch.uint8, device=DEV)
+    out = torch.full((2, 8, 128), 7.0, device=DEV)
+    tq.decode_attend(kcb, vcb, q, rec, rec, 0, 2, 0.1, out=out)
+    sl = torch.zeros(2, dtype=torch.int32, device=DEV)
+    tq.decode_attend(kcb, vcb, q, rec, rec, 0, 2, 0.1, seq_lens=sl)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
 def test_decode_attend_spectralquant():
     _decode_case(2, 8, 2, 500, sq=True)
 

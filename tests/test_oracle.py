@@ -206,6 +206,115 @@ def test_quantize_matches_brute_force_d8():
     assert np.array_equal(idx[ok], brute[ok])
 
 
+def _perdim_codec(d, bits_of_dim, seed):
+    """A codec whose dims carry different bit counts (and so different
+    boundaries): Beta-law Lloyd-Max books of each dim's width, scaled per dim."""
+    base = o.turboquant_codec(d, 2, "mse", rot_seed=seed)
+    rng = np.random.default_rng(seed)
+    scale = rng.uniform(0.5, 2.0, size=d)
+    cents = [o._f32(o.beta_codebook(d, int(b)).centroids * scale[i]) for i, b in enumerate(bits_of_dim)]
+    bnds = [o._f32(o.beta_codebook(d, int(b)).boundaries * scale[i]) for i, b in enumerate(bits_of_dim)]
+    return o.Codec(d, "mse", np.asarray(bits_of_dim), 0, "row", base.rot, None, [cents], [bnds], False)
+
+
+@pytest.mark.parametrize("uniform", [True, False])
+def test_boundary_distance_planted_points(uniform):
+    # Values fixed by construction: a point on a boundary is at distance 0,
+    # one nudged by delta from it at delta, a midpoint between neighbouring
+    # boundaries at half their gap, a point past the outermost boundary at its
+    # offset; each dim measured against its own boundaries.
+    d = 8
+    codec = o.turboquant_codec(d, 3, "mse", rot_seed=3) if uniform else \
+        _perdim_codec(d, [1, 2, 3, 4, 5, 3, 2, 1], 4)
+    rows, want = [], []
+    for i in range(d):
+        t = codec.boundaries[0][0 if uniform else i]
+        gaps = np.diff(t)
+        half = 0.5 * (gaps.min() if len(gaps) else 1.0)
+        delta = 1e-3 * half
+        cases = [(t[0], 0.0), (t[-1], 0.0), (t[0] - delta, delta), (t[-1] + 3 * delta, 3 * delta),
+                 (t[len(t) // 2] + delta, delta), (t[-1] + 0.25, 0.25)]
+        if len(t) > 1:
+            cases.append((0.5 * (t[0] + t[1]), 0.5 * (t[1] - t[0])))
+        for val, dist in cases:
+            y = np.full(d, 0.5 * (t[0] + t[-1]) if len(t) > 1 else t[0] + 0.5)
+            y[i] = val
+            rows.append(y)
+            want.append((i, dist))
+    got = o.boundary_distance(codec, np.array(rows))
+    for r, (i, dist) in enumerate(want):
+        assert abs(got[r, i] - dist) <= 1e-15 + 1e-12 * abs(dist), (r, i, got[r, i], dist)
+
+
+@pytest.mark.parametrize("uniform", [True, False])
+def test_boundary_distance_is_the_code_stability_radius(uniform):
+    # The comparison rules excuse a code flip only within the band around a
+    # boundary; that rests on boundary_distance being exactly how far a value
+    # can move before its code changes.  Moving by (1 - eps) of the distance
+    # either way keeps every code; moving by (1 + eps) of it changes the code
+    # in at least one of the two directions.
+    d = 128
+    codec = o.turboquant_codec(d, 4, "mse", rot_seed=7) if uniform else \
+        _perdim_codec(d, np.random.default_rng(9).integers(1, 6, size=d), 8)
+    rng = np.random.default_rng(5)
+    y = rng.normal(size=(400, d)) / math.sqrt(d)
+    idx = o.quantize(codec, y, 0)
+    dist = o.boundary_distance(codec, y)
+    ok = dist > 1e-9
+    for eps, changes in ((1e-6, False), (1e-6, True)):
+        f = 1 - eps if not changes else 1 + eps
+        up = o.quantize(codec, y + f * dist, 0) != idx
+        dn = o.quantize(codec, y - f * dist, 0) != idx
+        if changes:
+            assert np.all((up | dn)[ok])
+        else:
+            assert not np.any((up | dn)[ok])
+
+
+def test_mse_prod_crossover():
+    # Paper review, figure "Inner-product distortion vs bit-width": the
+    # unbiased prod variant has the lower inner-product error at low bit
+    # widths, the mse variant beyond about 3 bits.  Measured here on the
+    # self inner product <x, x_hat> of unit vectors (the case where the mse
+    # variant's bias is largest), averaged over 12 rotations and sketches:
+    # prod wins at b = 2 and 3, mse at b = 4 and 5.  A dropped or mis-scaled
+    # QJL term makes prod biased and loses at every b.
+    d, npairs = 128, 64
+    rng = np.random.default_rng(21)
+    err = {}
+    for mode in ("mse", "prod"):
+        for b in (2, 3, 4, 5):
+            e = []
+            for seed in range(12):
+                codec = o.turboquant_codec(d, b, mode, rot_seed=3000 + seed, sketch_seed=4000 + seed)
+                x = rng.normal(size=(npairs, d))
+                x /= np.linalg.norm(x, axis=1, keepdims=True)
+                enc = o.encode(codec, x, round_norms=False)
+                s = np.diag(o.score(codec, x, enc))
+                e.append(np.mean((s - 1.0) ** 2))
+            err[mode, b] = float(np.mean(e))
+    assert err["prod", 2] < err["mse", 2] and err["prod", 3] < err["mse", 3], err
+    assert err["mse", 4] < err["prod", 4] and err["mse", 5] < err["prod", 5], err
+
+
+def test_residual_sketch_of_own_codes_is_encode():
+    # The QJL stage recomputed from a vector's own codes gives its stored
+    # signs and n_r; from other codes it gives the residual of those codes.
+    d = 128
+    codec = o.turboquant_codec(d, 3, "prod", rot_seed=31, sketch_seed=32)
+    x = np.random.default_rng(6).normal(size=(50, d))
+    enc = o.encode(codec, x, round_norms=False)
+    nr, z = o.residual_sketch(codec, enc.y, enc.idx)
+    assert np.array_equal(z >= 0, enc.signs) and np.allclose(nr, enc.nr, rtol=0, atol=0)
+    other = enc.idx.copy()
+    other[:, 0] = 1 - other[:, 0] % 2 + 2 * (other[:, 0] // 2)   # flip the low bit of dim 0
+    nr2, z2 = o.residual_sketch(codec, enc.y, other)
+    c = codec.centroids[0][0]
+    r2 = enc.y - c[other]
+    assert np.allclose(nr2, np.linalg.norm(r2, axis=1), rtol=1e-14)
+    assert np.allclose(z2, r2 @ codec.sketch.T, rtol=1e-12, atol=1e-14)
+
+
 def test_empirical_mse_matches_codebook():
     d, b = 128, 2
     codec = o.turboquant_codec(d, b, "mse", rot_seed=11)
@@ -396,7 +505,7 @@ def test_eigenbasis_and_spectrum():
         assert np.max(np.abs(cov @ rows.T - rows.T * lam[None, :])) < 1e-9 * lam[0]
         assert np.all(np.diff(lam) <= 0)
         frac = lam[:4].sum() / lam.sum()
-        # "~80% of the variance lives in 4 of 128 dimensions" (SpectralQuant thread, tweet 2)
+        # about 80% of the variance in 4 of 128 eigendirections (SpectralQuant thread, tweet 2)
         assert 0.75 < frac < 0.95
 
 
