@@ -28,7 +28,7 @@ void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
   void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
                   t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm, t.had_mask,
-                  t.omask};
+                  t.omask, t.rot_tiles, t.sk_tiles};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -406,6 +406,37 @@ tq_status build_device(tq_codebook* cb) {
     if ((st = upload(&cb->dev.sketch_hi, shi.data(), ns)) != TQ_OK) return st;
     if ((st = upload(&cb->dev.sketch_lo, slo.data(), ns)) != TQ_OK) return st;
   }
+  if (d != 128 && d % 128 == 0 && cb->uniform && !cb->outlier) {
+    // operand tiles of the wide MFMA kernels: per 128-row block and 32-column
+    // tile, [hi, lo][128][32] of 16 Pi (and [128][32] of S), rows of every
+    // 32-row group in the order 8a + 4h + c <- 16h + 4a + c, so that the
+    // accumulator registers of a half-wave cover 16 consecutive rows
+    auto perm = [](int g) { return (g & ~31) | (((g >> 2) & 1) << 4) | (((g >> 3) & 3) << 2) | (g & 3); };
+    const int heads = int(nr / (size_t(d) * d)), nkt = d / 32;
+    std::vector<uint16_t> rt_(nr * 2);
+    for (int hh = 0; hh < heads; ++hh)
+      for (int b = 0; b < d / 128; ++b)
+        for (int kt = 0; kt < nkt; ++kt)
+          for (int pl = 0; pl < 2; ++pl)
+            for (int g = 0; g < 128; ++g)
+              for (int e = 0; e < 32; ++e) {
+                const size_t src = (size_t(hh) * d + size_t(b) * 128 + perm(g)) * d + size_t(kt) * 32 + e;
+                const size_t dst = ((((size_t(hh) * (d / 128) + b) * nkt + kt) * 2 + pl) * 128 + g) * 32 + e;
+                rt_[dst] = pl == 0 ? hi[src] : lo[src];
+              }
+    if ((st = upload(&cb->dev.rot_tiles, rt_.data(), rt_.size())) != TQ_OK) return st;
+    if (!cb->sketch32.empty() && cb->m % 128 == 0) {
+      const int m = cb->m, mkt = m / 32;
+      std::vector<uint16_t> sk(size_t(m) * m);
+      for (int b = 0; b < m / 128; ++b)
+        for (int kt = 0; kt < mkt; ++kt)
+          for (int g = 0; g < 128; ++g)
+            for (int e = 0; e < 32; ++e)
+              sk[((size_t(b) * mkt + kt) * 128 + g) * 32 + e] =
+                  f32_to_f16_rne(cb->sketch32[(size_t(b) * 128 + perm(g)) * m + size_t(kt) * 32 + e]);
+      if ((st = upload(&cb->dev.sk_tiles, sk.data(), sk.size())) != TQ_OK) return st;
+    }
+  }
   if ((st = upload(&cb->dev.thr, cb->thr32.data(), cb->thr32.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.cen, cb->cen32.data(), cb->cen32.size())) != TQ_OK) return st;
   if ((st = upload(&cb->dev.bitpos, cb->bitpos.data(), cb->bitpos.size())) != TQ_OK) return st;
@@ -466,13 +497,16 @@ int64_t decode_nsplit(int64_t max_tokens) {
 }
 constexpr int kDecodeChunkTiles = 8;
 
-constexpr int kLargeTopkSegments = 16;  // partial lists per key chunk of the wide-vector path
+constexpr int kTopkSegments = 16;  // partial lists per key chunk of the general top-k path
 
-int64_t topk_nseg(int64_t n) {
-  // one partial list per 4096 keys (at least those of the wide-vector path)
-  const int64_t per_chunk = kLargeTopkSegments;
-  const int64_t chunks = (n + large_score_chunk() - 1) / large_score_chunk();
-  return std::max<int64_t>(1, std::min<int64_t>(1024, std::max((n + 4095) / 4096, chunks * per_chunk)));
+// Keys per chunk of the general top-k path (scores of a chunk are written to
+// the workspace, then scanned): about 2^26 scores per chunk, at most 64 chunks,
+// whole record tiles.
+int64_t topk_chunk(int64_t nq, int64_t n) {
+  int64_t c = std::max<int64_t>(4096, (int64_t(1) << 26) / std::max<int64_t>(1, nq));
+  c = std::max(c, (n + 63) / 64);
+  c = (c + kTile - 1) / kTile * kTile;
+  return std::min(c, (n + kTile - 1) / kTile * kTile);
 }
 
 bool supported_query_d(int d) { return d % 64 == 0 && d >= 64 && d <= 4096; }
@@ -524,12 +558,67 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.sq_tail = cb->dev.sq_tail;
   v.sq_gm = cb->dev.sq_gm;
   v.had_mask = cb->dev.had_mask;
+  v.rot_tiles = cb->dev.rot_tiles;
+  v.sk_tiles = cb->dev.sk_tiles;
   for (int k = 0; k < kMaxLevels; ++k) {
     v.uthr[k] = cb->thr32[k];
     v.ucen[k] = cb->cen32[k];
   }
   return v;
 }
+
+namespace {
+
+// Workspace of the wide (d != 128) query preparation, the MFMA search /
+// dense scoring, and the general top-k path, laid out in this order after
+// the prepared queries ([nq][d] q' and [nq][m] qs, fp32).
+struct QueryWs {
+  size_t qprep, wide, tiles, inv, ps, pi, scores;
+  size_t total() const { return qprep + wide + tiles + inv + ps + pi + scores; }
+};
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int device_cus(int device) {
+  int cus = 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+// op TQ_OP_SCORE (k = 0) or TQ_OP_TOPK
+QueryWs query_ws(const tq_codebook* cb, int32_t op, int64_t nq, int64_t n, int k) {
+  QueryWs w{};
+  const CodecView cv = make_view(cb);
+  const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
+  w.qprep = round256(size_t(nq) * (d + m) * 4);
+  if (d != 128) w.wide = round256(wide_query_prep_workspace(cv, nq));
+  const bool mfma = search_mfma_supported(cv) && n < (int64_t(1) << 31);
+  if (op == TQ_OP_SCORE) {
+    if (d != 128) {
+      const SearchPlan p = search_plan(cv, nq, n, device_cus(cb->device));
+      w.tiles = p.tiles_bytes;
+      w.inv = p.inv_bytes;
+    }
+    return w;
+  }
+  if (mfma) {
+    const SearchPlan p = search_plan(cv, nq, n, device_cus(cb->device));
+    w.tiles = p.tiles_bytes;
+    w.inv = p.inv_bytes;
+    w.ps = round256(size_t(nq) * p.nparts * k * 4);
+    w.pi = round256(size_t(nq) * p.nparts * k * 8);
+  } else {
+    const int64_t chunk = topk_chunk(nq, n);
+    const int64_t nchunks = (n + chunk - 1) / chunk;
+    w.scores = round256(size_t(nq) * size_t(chunk) * 4);
+    w.ps = round256(size_t(nq) * nchunks * kTopkSegments * k * 4);
+    w.pi = round256(size_t(nq) * nchunks * kTopkSegments * k * 8);
+  }
+  return w;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -693,31 +782,28 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
   EncodeArgs a{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
                static_cast<uint8_t*>(records), rs_b, rs_h};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (large) return map_hip(launch_encode_large(cb->device, make_view(cb), a, workspace, s));
+  if (large) return map_hip(launch_encode_wide(make_view(cb), a, workspace, s));
   return map_hip(launch_encode_d128(make_view(cb), a, s));
 }
+
 
 size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b, int64_t c) {
   if (!cb || a < 0 || b < 0) return 0;
   const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
   const size_t qprep = size_t(a) * (d + m) * 4;
-  const bool large = cb->desc.d != 128;
-  auto round = [](size_t v) { return (v + 255) & ~size_t(255); };
   switch (op) {
     case TQ_OP_ENCODE:
-      return large ? large_encode_workspace(make_view(cb)) : 0;
+      return d != 128 ? wide_encode_workspace(make_view(cb)) : 0;
     case TQ_OP_SCORE:
-      return round(qprep) + (large ? large_score_workspace(make_view(cb), a) : 0);
+      return query_ws(cb, TQ_OP_SCORE, a, b, 0).total();
     case TQ_OP_DECODE: {
       if (c <= 0) return 0;
       const size_t part = size_t(a) * size_t(decode_nsplit(b)) * (2 + d) * 4;
-      return round(qprep) + round(part);
+      return round256(qprep) + round256(part);
     }
     case TQ_OP_TOPK: {
       if (c <= 0 || c > 16) return 0;
-      const size_t ps = size_t(a) * size_t(topk_nseg(b)) * size_t(c);
-      const size_t sc = large ? large_score_workspace(make_view(cb), a) : size_t(a) * size_t(b) * 4;
-      return round(qprep) + round(sc) + round(ps * 4) + round(ps * 8);
+      return query_ws(cb, TQ_OP_TOPK, a, b, int(c)).total();
     }
   }
   return 0;
@@ -732,23 +818,26 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   if (!q || !records || !scores) return TQ_EINVAL;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d)) return TQ_EUNSUPPORTED;
-  if (cb->desc.d != 128 && (cb->desc.d % 128 || !cb->uniform || (cb->desc.mode == TQ_PROD && cb->m != cb->desc.d)))
-    return TQ_EUNSUPPORTED;
+  const CodecView cv = make_view(cb);
+  if (cb->desc.d != 128 && (!search_mfma_supported(cv) || n >= (int64_t(1) << 31))) return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
   if (nq > int64_t(65535) * 4) return TQ_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0)) return TQ_EWORKSPACE;
+  const QueryWs W = query_ws(cb, TQ_OP_SCORE, nq, n, 0);
+  if (!workspace || workspace_bytes < W.total()) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const CodecView cv = make_view(cb);
-  float* qr = static_cast<float*>(workspace);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  float* qr = reinterpret_cast<float*>(w);
   float* qs = qr + nq * cb->desc.d;
   if (cb->desc.d != 128) {
-    tq_status st = map_hip(launch_query_prep_large(cb->device, cv, q, nq, head, qr, qs, s));
+    tq_status st = map_hip(launch_query_prep_wide(cv, q, nq, qr, qs, w + W.qprep, s));
     if (st != TQ_OK) return st;
-    void* lw = static_cast<uint8_t*>(workspace) + ((size_t(nq) * (cb->desc.d + std::max(cb->m, 1)) * 4 + 255) & ~size_t(255));
-    return map_hip(launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
-                                      scores, lw, s, nullptr, nullptr));
+    const SearchPlan p = search_plan(cv, nq, n, device_cus(cb->device));
+    uint8_t* t = w + W.qprep + W.wide;
+    return map_hip(launch_search(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, 0, p, t,
+                                 reinterpret_cast<float*>(t + W.tiles), nullptr, nullptr, nullptr, nullptr, scores,
+                                 s));
   }
   QueryPrepArgs qa{q, 0, nq, 0, 1, head, qr, qs};
   tq_status st = map_hip(launch_query_prep(cv, qa, s));
@@ -929,56 +1018,54 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->desc.layout != TQ_LAYOUT_ROW || !supported_query_d(cb->desc.d) || cb->info.num_heads != 1)
     return TQ_EUNSUPPORTED;
+  const CodecView cv = make_view(cb);
+  const bool mfma = search_mfma_supported(cv) && n < (int64_t(1) << 31);
+  if (cb->desc.d != 128 && !mfma) return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
   if (nq == 0) return TQ_OK;
   if (n < k) return TQ_EINVAL;
   if (nq > 65535) return TQ_EUNSUPPORTED;
-  if (!workspace || workspace_bytes < tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k)) return TQ_EWORKSPACE;
+  const QueryWs W = query_ws(cb, TQ_OP_TOPK, nq, n, k);
+  if (!workspace || workspace_bytes < W.total()) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const CodecView cv = make_view(cb);
-  const size_t d = size_t(cb->desc.d), m = size_t(std::max(cb->m, 1));
-  auto round = [](size_t v) { return (v + 255) & ~size_t(255); };
+  const size_t d = size_t(cb->desc.d);
   uint8_t* w = static_cast<uint8_t*>(workspace);
   float* qr = reinterpret_cast<float*>(w);
   float* qs = qr + nq * d;
-  w += round(size_t(nq) * (d + m) * 4);
-  float* sc = reinterpret_cast<float*>(w);
-  w += round(cb->desc.d != 128 ? large_score_workspace(cv, nq) : size_t(nq) * size_t(n) * 4);
-  const int nseg = int(topk_nseg(n));
-  const size_t ps = size_t(nq) * nseg * k;
-  float* pss = reinterpret_cast<float*>(w);
-  w += round(ps * 4);
-  int64_t* psi = reinterpret_cast<int64_t*>(w);
+  uint8_t* tiles = w + W.qprep + W.wide;
+  float* inv = reinterpret_cast<float*>(tiles + W.tiles);
+  float* pss = reinterpret_cast<float*>(tiles + W.tiles + W.inv);
+  int64_t* psi = reinterpret_cast<int64_t*>(tiles + W.tiles + W.inv + W.ps);
+  float* sc = reinterpret_cast<float*>(tiles + W.tiles + W.inv + W.ps + W.pi);
+  tq_status st;
   if (cb->desc.d != 128) {
-    tq_status st = map_hip(launch_query_prep_large(cb->device, cv, q, nq, 0, qr, qs, s));
-    if (st != TQ_OK) return st;
-    // key chunks of large_score_chunk() rows, each cut into 16 segments; the
-    // partial lists of all chunks are merged at the end
-    struct Ctx { int64_t nq; int k; int per_chunk; int total; float* ps; int64_t* pi; };
-    const int per_chunk = kLargeTopkSegments;
-    const int64_t nchunks = (n + large_score_chunk() - 1) / large_score_chunk();
-    Ctx ctx{nq, k, per_chunk, int(nchunks * per_chunk), pss, psi};
-    if (ctx.total > nseg) return TQ_EUNSUPPORTED;
-    ChunkFn fn = [](void* c, const float* scores, int64_t ld, int64_t r0, int64_t rows,
-                    const float* col_scale, const float* row_scale, hipStream_t st2) -> hipError_t {
-      // segments of a short last chunk that get no columns emit -inf entries
-      Ctx* x = static_cast<Ctx*>(c);
-      const int seg_base = int(r0 / large_score_chunk()) * x->per_chunk;
-      return launch_topk_segments(scores, ld, rows, r0, x->nq, x->k, x->per_chunk, seg_base, x->total,
-                                  x->ps, x->pi, st2, col_scale, row_scale);
-    };
-    hipError_t e = launch_score_large(cb->device, cv, qr, qs, nq, static_cast<const uint8_t*>(records), n,
-                                      nullptr, sc, s, fn, &ctx);
-    if (e != hipSuccess) return map_hip(e);
-    return map_hip(launch_topk_merge(pss, psi, nq, ctx.total, k, top_scores, top_ids, s));
+    st = map_hip(launch_query_prep_wide(cv, q, nq, qr, qs, w + W.qprep, s));
+  } else {
+    QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
+    st = map_hip(launch_query_prep(cv, qa, s));
   }
-  QueryPrepArgs qa{q, 0, nq, 0, 1, 0, qr, qs};
-  tq_status st = map_hip(launch_query_prep(cv, qa, s));
   if (st != TQ_OK) return st;
-  return map_hip(launch_topk(cv, qr, qs, nq, static_cast<const uint8_t*>(records), n, k, top_scores,
-                             top_ids, sc, pss, psi, nseg, s));
+  const uint8_t* rec = static_cast<const uint8_t*>(records);
+  if (mfma) {
+    const SearchPlan p = search_plan(cv, nq, n, device_cus(cb->device));
+    return map_hip(launch_search(cv, qr, qs, nq, rec, n, k, p, tiles, inv, pss, psi, top_scores, top_ids, nullptr,
+                                 s));
+  }
+  // general codecs (d = 128): scores of one key chunk at a time in the
+  // workspace, each chunk scanned into 16 partial lists, then one merge
+  const int64_t chunk = topk_chunk(nq, n);
+  const int64_t nchunks = (n + chunk - 1) / chunk;
+  const int total = int(nchunks * kTopkSegments);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t r0 = c * chunk, rows = std::min(chunk, n - r0);
+    hipError_t e = launch_score(cv, qr, qs, nq, rec + (r0 / kTile) * cv.tile_bytes, rows, sc, s);
+    if (e != hipSuccess) return map_hip(e);
+    e = launch_topk_segments(sc, rows, rows, r0, nq, k, kTopkSegments, int(c) * kTopkSegments, total, pss, psi, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
+  return map_hip(launch_topk_merge(pss, psi, nq, total, k, top_scores, top_ids, s));
 }
 
 }  // extern "C"

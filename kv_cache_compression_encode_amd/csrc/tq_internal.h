@@ -67,6 +67,11 @@ struct DeviceTables {
   uint32_t* had_mask = nullptr;  // [2][32]
   // outlier-channel split: per head, bit c of the 128-bit mask = channel c is an outlier
   uint32_t* omask = nullptr;     // [H][4]
+  // wide uniform codecs (d a multiple of 128 other than 128): the rotation and
+  // sketch in the tile order of the MFMA kernels, rows of each 32-row group
+  // permuted so that a half-wave's accumulators hold 16 consecutive rows
+  uint16_t* rot_tiles = nullptr; // [d/128][d/32][2][128][32] fp16 hi, lo of 16 Pi
+  uint16_t* sk_tiles = nullptr;  // [m/128][m/32][128][32] fp16 S
 };
 
 }  // namespace tq

@@ -36,6 +36,10 @@ struct CodecView {
   const uint32_t* sq_tail;  // non-uniform d = 128: tail byte -> packed index bits of dims 0..3
   const float* sq_gm;       // non-uniform d = 128: [H][2][d] half-difference and mean of levels 0, 1
   const uint32_t* had_mask; // randomized Hadamard, d = 128: [2][32] XOR masks of the bf16 sign bits
+  // d a multiple of 128 other than 128, uniform codecs: the MFMA operand tiles
+  // [d/128][d/32][hi, lo][128][32] of 16 Pi and [m/128][m/32][128][32] of S
+  const uint16_t* rot_tiles;
+  const uint16_t* sk_tiles;
   float uthr[kMaxLevels];
   float ucen[kMaxLevels];
 };
@@ -131,11 +135,6 @@ bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G);
 hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
                               hipStream_t s);
 
-hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
-                       const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,
-                       float* ws_scores, float* ws_part_s, int64_t* ws_part_i, int nsplit,
-                       hipStream_t s);
-
 // Per-query top-k of a [nq][cols] score block (row stride ld, ids id_base +
 // column) into partial lists seg_base .. seg_base + nseg - 1 of total_seg.
 // Scores are part[q][t] * row_scale[q] * col_scale[t] (each scale optional).
@@ -146,22 +145,28 @@ hipError_t launch_topk_segments(const float* scores, int64_t ld, int64_t cols, i
 hipError_t launch_topk_merge(const float* ps, const int64_t* pi, int64_t nq, int total_seg, int k,
                              float* out_s, int64_t* out_i, hipStream_t s);
 
-// Wide vectors (d a multiple of 128 other than 128): GEMM-based encode and
-// scoring in row chunks (tq_large.hip).
-// Chunk callback: s[q][t] = scores[q * ld + t] * row_scale[q] * col_scale[t].
-typedef hipError_t (*ChunkFn)(void* ctx, const float* scores, int64_t ld, int64_t r0, int64_t rows,
-                              const float* col_scale, const float* row_scale, hipStream_t s);
-int64_t large_encode_chunk();
-size_t large_encode_workspace(const CodecView& cv);
-hipError_t launch_encode_large(int device, const CodecView& cv, const EncodeArgs& a, void* ws,
-                               hipStream_t s);
-int64_t large_score_chunk();
-size_t large_score_workspace(const CodecView& cv, int64_t nq);
-hipError_t launch_score_large(int device, const CodecView& cv, const float* qr, const float* qs,
-                              int64_t nq, const uint8_t* rec, int64_t n, float* out, void* ws,
-                              hipStream_t s, ChunkFn chunk_cb, void* cb_ctx);
-hipError_t launch_query_prep_large(int device, const CodecView& cv, const float* q, int64_t nq, int head,
-                                   float* qr, float* qs, hipStream_t s);
+// Wide vectors (d a multiple of 128; encode and query preparation for d other
+// than 128) and the MFMA search / dense scoring (tq_wide.hip).
+int64_t wide_encode_chunk();
+size_t wide_encode_workspace(const CodecView& cv);
+hipError_t launch_encode_wide(const CodecView& cv, const EncodeArgs& a, void* ws, hipStream_t s);
+size_t wide_query_prep_workspace(const CodecView& cv, int64_t nq);
+hipError_t launch_query_prep_wide(const CodecView& cv, const float* q, int64_t nq, float* qr, float* qs,
+                                  void* ws, hipStream_t s);
+// Fused scoring + top-k (or dense scores) of uniform ROW codecs with 1..3
+// index bits: 128 queries per workgroup, keys split over nsplit workgroups
+// per query block, 4 partial lists (one per wave) per workgroup.
+struct SearchPlan {
+  int nqb, nsplit, nparts;
+  int64_t keys_per_split;
+  size_t tiles_bytes, inv_bytes;
+};
+bool search_mfma_supported(const CodecView& cv);
+SearchPlan search_plan(const CodecView& cv, int64_t nq, int64_t n, int cus);
+// dense != nullptr: scores [nq][n] are written instead of the top-k lists
+hipError_t launch_search(const CodecView& cv, const float* qr, const float* qs, int64_t nq, const uint8_t* rec,
+                         int64_t n, int k, const SearchPlan& p, void* tiles_ws, float* inv_ws, float* ps,
+                         int64_t* pi, float* out_s, int64_t* out_i, float* dense, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 }  // namespace tq

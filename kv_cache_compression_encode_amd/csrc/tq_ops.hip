@@ -775,17 +775,6 @@ hipError_t launch_topk_merge(const float* ps, const int64_t* pi, int64_t nq, int
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const CodecView& cv, const float* qr, const float* qs, int64_t nq,
-                       const uint8_t* rec, int64_t n, int k, float* top_s, int64_t* top_i,
-                       float* ws_scores, float* ws_part_s, int64_t* ws_part_i, int nsplit,
-                       hipStream_t s) {
-  hipError_t e = launch_score(cv, qr, qs, nq, rec, n, ws_scores, s);
-  if (e != hipSuccess) return e;
-  e = launch_topk_segments(ws_scores, n, n, 0, nq, k, nsplit, 0, nsplit, ws_part_s, ws_part_i, s);
-  if (e != hipSuccess) return e;
-  return launch_topk_merge(ws_part_s, ws_part_i, nq, nsplit, k, top_s, top_i, s);
-}
-
 __global__ void fill_zero_kernel(float* p, int64_t n) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.f;
