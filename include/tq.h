@@ -324,6 +324,21 @@ tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const
                            const tq_kv_view* kv, float softmax_scale, float* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* tq_decode_attend without any allocation, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid it).  The workspace is a device array inside the library, of
+ * TQ_NOALLOC_SCRATCH_BYTES on every GPU the library runs on (held until the
+ * process ends); its address is looked up on the first call for a device.
+ * Arguments, results and errors are those of tq_decode_attend, and
+ * TQ_EWORKSPACE when tq_workspace_size(kcb, TQ_OP_DECODE, B*Hq, max_tokens,
+ * Hkv) exceeds TQ_NOALLOC_SCRATCH_BYTES.  The call itself allocates nothing.
+ * All calls on one GPU share its array: calls that overlap on one GPU race
+ * (issue them on one stream, or order them). */
+#define TQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+tq_status tq_decode_attend_noalloc(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,
+                                   int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                   const tq_kv_view* kv, float softmax_scale, float* out, void* stream);
+
 /* One decode step with append-on-decode (TurboQuant paper review,
  * "Comparison": the tokens generated during decoding are quantized too):
  * the new key and value of every (sequence, KV head) are encoded into slot

@@ -240,6 +240,24 @@ def decode_attend(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_records: torc
     return out
 
 
+def decode_attend_noalloc(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_records: torch.Tensor,
+                          v_records: torch.Tensor, max_tokens: int, hkv: int, scale: float,
+                          out: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
+                          k_strides=None, v_strides=None, block_table: Optional[torch.Tensor] = None,
+                          page_tiles: int = 1) -> torch.Tensor:
+    """decode_attend through the entry point that allocates nothing (its
+    workspace is the library's own device array); `out` must be given."""
+    B, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous (this call allocates nothing)")
+    view, _bt = _kv_view(kcb, vcb, k_records, v_records, max_tokens, hkv, seq_lens, k_strides, v_strides,
+                         block_table, page_tiles)
+    L.check(L.lib().tq_decode_attend_noalloc(kcb.handle, vcb.handle, q.data_ptr(), _dtype_code(q), B, Hq, hkv,
+                                             ctypes.byref(view), scale, out.data_ptr(), _stream(q.device)),
+            "tq_decode_attend_noalloc")
+    return out
+
+
 def decode_step(kcb: Codebook, vcb: Codebook, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 k_records: torch.Tensor, v_records: torch.Tensor, max_tokens: int, hkv: int, scale: float,
                 seq_lens: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -13,10 +13,11 @@ TQ_ROT_HAAR, TQ_ROT_GIVEN, TQ_ROT_CALIBRATE, TQ_ROT_HADAMARD = 0, 1, 2, 3
 TQ_LAYOUT_ROW, TQ_LAYOUT_COL = 0, 1
 TQ_OP_SCORE, TQ_OP_DECODE, TQ_OP_TOPK, TQ_OP_ENCODE = 0, 1, 2, 3
 TQ_TILE = 64
+TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 TQ_MAX_LEVELS = 32
 
 EXPORTED = ["tq_codebook_build", "tq_codebook_free", "tq_water_fill", "tq_append", "tq_codebook_get_info", "tq_codebook_export",
-            "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_decode_step", "tq_search_topk",
+            "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_decode_attend_noalloc", "tq_decode_step", "tq_search_topk",
             "tq_workspace_size", "tq_status_string"]
 
 
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.tq_decode_attend.argtypes = [p, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),
                                    ctypes.c_float, p, p, sz, p]
     L.tq_decode_attend.restype = i32
+    L.tq_decode_attend_noalloc.argtypes = [p, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),
+                                           ctypes.c_float, p, p]
+    L.tq_decode_attend_noalloc.restype = i32
     L.tq_decode_step.argtypes = [p, p, p, i32, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),
                                  ctypes.c_float, p, p, sz, p]
     L.tq_decode_step.restype = i32

@@ -959,6 +959,13 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
 
 }  // namespace
 
+tq_status tq::decode_attend_ws(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, int32_t q_dtype,
+                               int32_t B, int32_t Hq, int32_t Hkv, const tq_kv_view* kv, float softmax_scale,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kcb, vcb, q, q_dtype, B, Hq, Hkv, kv, softmax_scale, out, workspace, workspace_bytes,
+                     stream, 0, false);
+}
+
 extern "C" {
 
 tq_status tq_decode_attend(const tq_codebook* kcb, const tq_codebook* vcb, const void* q,

@@ -38,6 +38,12 @@ LloydMaxResult lloyd_max_gaussian(int bits);
 // each row signed so that its largest-magnitude entry (first on ties) is > 0.
 void symmetric_eigen(int n, const double* a, double* lambda, double* rows);
 
+// tq_decode_attend with the caller's workspace (shared by the allocating and
+// the allocation-free entry points).
+tq_status decode_attend_ws(const tq_codebook* kcb, const tq_codebook* vcb, const void* q, int32_t q_dtype,
+                           int32_t B, int32_t Hq, int32_t Hkv, const tq_kv_view* kv, float softmax_scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
 uint16_t f32_to_bf16_rne(float x);
 float bf16_to_f32(uint16_t h);
 uint16_t f32_to_f16_rne(float x);
