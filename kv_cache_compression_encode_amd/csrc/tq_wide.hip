@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "tq_kernels.h"
 
@@ -593,8 +594,22 @@ struct SearchArgs {
   int nparts;               // partial lists per query = 4 * nsplit
   float* ps;                // [nq][nparts][k]
   int64_t* pi;
+  int* thr;                 // [nqb * 128] shared admission thresholds (order-preserving int of a float)
   float* scores;            // dense output [nq][n]
 };
+
+// Order-preserving map of floats (not NaN) to ints, so that thresholds can be
+// raised with an integer atomic max.
+__device__ __forceinline__ int ord_of(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7fffffff;
+}
+__device__ __forceinline__ float float_of_ord(int i) { return __int_as_float(i >= 0 ? i : i ^ 0x7fffffff); }
+
+__global__ void fill_ord_kernel(int* p, int64_t n, float v) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = ord_of(v);
+}
 
 __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
@@ -643,9 +658,8 @@ struct KeyTables {
   u32x2 cen[NC];
 };
 
-template <int UB, bool PROD, bool DENSE>
+template <int UB, bool PROD, bool DENSE, int KM>  // KM: list slots (k <= KM)
 __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
-  constexpr int KM = 16;
   constexpr int TP = 33;        // pitch of the transposition buffer (floats)
   constexpr int SP = SK + 8;    // LDS pitch of a query row (halves): 272 bytes, conflict-free 16-byte reads
   __shared__ __align__(16) uint16_t sA[2][AR * SP];
@@ -719,20 +733,19 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       kt0[v] = a.rec + (lk / kTile) * a.tile_bytes;
       kslot[v] = int(lk % kTile);
     }
-    // record chunks of tile kt: the sign chunk kt (kt < GS), else chunk kt - GS of every code plane
+    // record chunks of tile kt: the sign chunk kt (kt < GS), else chunk kt - GS
+    // of every code plane (branch-free: the sign tiles read the sign chunk
+    // into every plane register)
     auto load_chunks = [&](int kt, u32x4 (&dst)[2][UB]) {
+      const bool sg = PROD && kt < GS;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        if (PROD && kt < GS) {
-          dst[v][0] = *reinterpret_cast<const u32x4*>(kt0[v] + a.off_signs + size_t(kt) * kTile * 16 +
-                                                      size_t(kslot[v]) * 16);
-        } else {
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
-          for (int p = 0; p < UB; ++p)
-            dst[v][p] = *reinterpret_cast<const u32x4*>(kt0[v] + size_t(p * GC + kt - GS) * kTile * 16 +
-                                                        size_t(kslot[v]) * 16);
+        for (int p = 0; p < UB; ++p) {
+          const size_t off = sg ? size_t(a.off_signs) + size_t(kt) * kTile * 16
+                                : size_t(p * GC + kt - GS) * kTile * 16;
+          dst[v][p] = *reinterpret_cast<const u32x4*>(kt0[v] + off + size_t(kslot[v]) * 16);
         }
-      }
     };
     u32x4 cw[2][UB], ncw[2][UB];
     stage_load(0);
@@ -744,63 +757,78 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int v = 0; v < 2; ++v) acc[c][v] = f32x16{};
-    for (int kt = 0; kt < nkt; ++kt) {
-      const bool more = kt + 1 < nkt;
-      if (more) {
-        stage_load(kt + 1);
-        load_chunks(kt + 1, ncw);
-      }
-      if (PROD && kt == GS) {
-        // between the sign phase and the code phase: acc *= n_r of the key
+    // One tile of 128 reduction elements; the next tile's query rows and
+    // record chunks are loaded first (clamped to the last tile: the loads are
+    // unconditional, so the wait counters stay exact across the loop).
+    auto tile = [&](int kt, auto signs_c) {
+      constexpr bool SIGNS = decltype(signs_c)::value;
+      const int kn = min(kt + 1, nkt - 1);
+      stage_load(kn);
+      load_chunks(kn, ncw);
+      const uint16_t* LA = sA[kt & 1];
+      // 8 MFMA steps of 16: step t = (kq, s) takes elements 32 kq + 16 h + 8 s .. + 7.
+      // The LDS reads of step t + 1 (query fragments, key table rows) are
+      // issued before the MFMAs of step t, so their latency hides behind them.
+      auto read_step = [&](int t, u32x4 (&af)[4], u32x4 (&bf)[2]) {
+        const int kq = t >> 1, s = t & 1;
+        const int sh = 16 * h + 8 * s;
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-          const float nr = f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nr + 2 * kslot[v]));
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c][v] *= nr;
-        }
-      }
-      const bool signs = PROD && kt < GS;
-      const uint16_t* LA = sA[kt & 1];
-      // 8 MFMA steps of 16: step (kq, s) takes elements 32 kq + 16 h + 8 s .. + 7
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int sh = 16 * h + 8 * s;
-          u32x4 bf[2];
-#pragma unroll
-          for (int v = 0; v < 2; ++v) {
-            if (signs || UB == 1) {
-              bf[v] = tb.pm[(cw[v][0][kq] >> sh) & 0xffu];
-            } else {
-              const uint32_t b0 = (cw[v][0][kq] >> sh) & 0xffu, b1 = (cw[v][UB > 1 ? 1 : 0][kq] >> sh) & 0xffu;
-              uint32_t ilo = (b0 & 15u) | ((b1 & 15u) << 4), ihi = (b0 >> 4) | (b1 & 0xf0u);
-              if (UB == 3) {
-                const uint32_t b2 = (cw[v][UB == 3 ? 2 : 0][kq] >> sh) & 0xffu;
-                ilo |= (b2 & 15u) << 8;
-                ihi |= (b2 & 0xf0u) << 4;
-              }
-              const u32x2 lo = tb.cen[ilo], hi = tb.cen[ihi];
-              bf[v] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          if (SIGNS || UB == 1) {
+            bf[v] = tb.pm[(cw[v][0][kq] >> sh) & 0xffu];
+          } else {
+            const uint32_t b0 = (cw[v][0][kq] >> sh) & 0xffu, b1 = (cw[v][UB > 1 ? 1 : 0][kq] >> sh) & 0xffu;
+            uint32_t ilo = (b0 & 15u) | ((b1 & 15u) << 4), ihi = (b0 >> 4) | (b1 & 0xf0u);
+            if (UB == 3) {
+              const uint32_t b2 = (cw[v][UB == 3 ? 2 : 0][kq] >> sh) & 0xffu;
+              ilo |= (b2 & 15u) << 8;
+              ihi |= (b2 & 0xf0u) << 4;
             }
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4 af =
-                *reinterpret_cast<const u32x4*>(LA + (32 * c + j) * SP + 32 * kq + 16 * h + 8 * s);
-#pragma unroll
-            for (int v = 0; v < 2; ++v) acc[c][v] = mfma(af, bf[v], acc[c][v]);
+            const u32x2 lo = tb.cen[ilo], hi = tb.cen[ihi];
+            bf[v] = u32x4{lo[0], lo[1], hi[0], hi[1]};
           }
         }
-      if (more) {
-        stage_store(sA[(kt + 1) & 1]);
 #pragma unroll
-        for (int v = 0; v < 2; ++v)
+        for (int c = 0; c < 4; ++c)
+          af[c] = *reinterpret_cast<const u32x4*>(LA + (32 * c + j) * SP + 32 * kq + 16 * h + 8 * s);
+      };
+      auto mma_step = [&](const u32x4 (&af)[4], const u32x4 (&bf)[2]) {
 #pragma unroll
-          for (int p = 0; p < UB; ++p) cw[v][p] = ncw[v][p];
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int v = 0; v < 2; ++v) acc[c][v] = mfma(af[c], bf[v], acc[c][v]);
+      };
+      u32x4 afA[4], bfA[2], afB[4], bfB[2];
+      read_step(0, afA, bfA);
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        read_step(t + 1, afB, bfB);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(afA, bfA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 2 < 8) read_step(t + 2, afA, bfA);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(afB, bfB);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      stage_store(sA[(kt + 1) & 1]);
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int p = 0; p < UB; ++p) cw[v][p] = ncw[v][p];
       __syncthreads();
+    };
+    for (int kt = 0; kt < GS; ++kt) tile(kt, std::integral_constant<bool, true>{});
+    if (PROD) {
+      // between the sign phase and the code phase: acc *= n_r of the key
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const float nr = f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nr + 2 * kslot[v]));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c][v] *= nr;
+      }
     }
+    for (int kt = GS; kt < nkt; ++kt) tile(kt, std::integral_constant<bool, false>{});
     // ---- epilogue: s = acc n_x inv_q; acc[c][v][r] is query 32 c + 8 (r / 4) + 4 h + r % 4, key v
     float nxv[2];
 #pragma unroll
@@ -822,8 +850,18 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       continue;
     }
     float* T = sT[wave];
+    // A key can enter the final top-k of a query only if its score reaches
+    // the shared threshold: the k-th best score of some partial list, which
+    // never exceeds the final k-th best.  Every list raises the shared value
+    // (an integer atomic max) after each workgroup tile, so all workgroups of
+    // the query block filter against it.
 #pragma unroll
-    for (int hq = 0; hq < 2; ++hq)
+    for (int hq = 0; hq < 2; ++hq) {
+      TopList<KM>& Lq = hq == 0 ? L0 : L1;
+      const float iq = hq == 0 ? invA : invB;
+      int* tq = a.thr + int64_t(qb) * AR + 64 * hq + lane;
+      const float tg = float_of_ord(__hip_atomic_load(tq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const float ts0 = Lq.ts;
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
         // queries 64 hq .. 64 hq + 63 x keys 32 v .. 32 v + 31 of the wave, via LDS
@@ -835,31 +873,27 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float sc[32];
-#pragma unroll
-        for (int jj = 0; jj < 32; ++jj) sc[jj] = T[lane * TP + jj];
-        TopList<KM>& Lq = hq == 0 ? L0 : L1;
-        const float iq = hq == 0 ? invA : invB;
         const int kbase = int(kb) + 64 * wave + 32 * v;  // key id of column 0 (n < 2^31)
         const int kvalid = int(min<int64_t>(32, max<int64_t>(0, k1 - (kb + 64 * wave + 32 * v))));
+        const float* row = T + lane * TP;
         uint32_t cand = 0;
 #pragma unroll
         for (int jj = 0; jj < 32; ++jj) {
-          sc[jj] *= iq;
-          if (jj < kvalid && better(sc[jj], kbase + jj, Lq.ts, Lq.ti)) cand |= 1u << jj;
+          const float sc = row[jj] * iq;
+          if (jj < kvalid && sc >= tg && better(sc, kbase + jj, Lq.ts, Lq.ti)) cand |= 1u << jj;
         }
         while (cand) {
           const int jj = __builtin_ctz(cand);
           cand &= cand - 1;
-          float cs = sc[0];
-#pragma unroll
-          for (int t = 1; t < 32; ++t) cs = t == jj ? sc[t] : cs;
+          const float cs = row[jj] * iq;
           if (better(cs, kbase + jj, Lq.ts, Lq.ti)) Lq.insert(cs, kbase + jj, a.k);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
+      if (Lq.ts > ts0 && Lq.ts > tg) atomicMax(tq, ord_of(Lq.ts));
+    }
   }
   if (DENSE) return;
   // partial lists of this wave: part (split, wave) of each query
@@ -1089,7 +1123,7 @@ SearchPlan search_plan(const CodecView& cv, int64_t nq, int64_t n, int cus) {
   const int K = cv.d + (cv.mode == TQ_PROD ? cv.m : 0);
   auto rnd = [](size_t v) { return (v + 255) & ~size_t(255); };
   p.tiles_bytes = rnd(size_t(p.nqb) * AR * K * 2);
-  p.inv_bytes = rnd(size_t(p.nqb) * AR * 4);
+  p.inv_bytes = rnd(size_t(p.nqb) * AR * 4) * 2;  // query scales, then the shared thresholds
   return p;
 }
 
@@ -1130,19 +1164,28 @@ hipError_t launch_search(const CodecView& cv, const float* qr, const float* qs, 
   sa.ps = ps;
   sa.pi = pi;
   sa.scores = dense;
+  sa.thr = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(inv_ws) + p.inv_bytes / 2);
+  if (!dense) {
+    hipLaunchKernelGGL(fill_ord_kernel, dim3(blocks_of(nrows)), dim3(256), 0, s, sa.thr, nrows, -INFINITY);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const dim3 grid(unsigned(p.nqb * p.nsplit));
-#define TQ_S(U, P, D) hipLaunchKernelGGL((search_kernel<U, P, D>), grid, dim3(NT), 0, s, sa)
-#define TQ_S_UB(P, D)                 \
-  switch (cv.ubits) {                 \
-    case 1: TQ_S(1, P, D); break;     \
-    case 2: TQ_S(2, P, D); break;     \
-    default: TQ_S(3, P, D); break;    \
+#define TQ_S(U, P, D, KM) hipLaunchKernelGGL((search_kernel<U, P, D, KM>), grid, dim3(NT), 0, s, sa)
+#define TQ_S_UB(P, D, KM)                 \
+  switch (cv.ubits) {                     \
+    case 1: TQ_S(1, P, D, KM); break;     \
+    case 2: TQ_S(2, P, D, KM); break;     \
+    default: TQ_S(3, P, D, KM); break;    \
   }
   if (dense) {
-    if (prod) { TQ_S_UB(true, true) } else { TQ_S_UB(false, true) }
+    if (prod) { TQ_S_UB(true, true, 1) } else { TQ_S_UB(false, true, 1) }
     return hipGetLastError();
   }
-  if (prod) { TQ_S_UB(true, false) } else { TQ_S_UB(false, false) }
+  if (k <= 10) {
+    if (prod) { TQ_S_UB(true, false, 10) } else { TQ_S_UB(false, false, 10) }
+  } else {
+    if (prod) { TQ_S_UB(true, false, 16) } else { TQ_S_UB(false, false, 16) }
+  }
 #undef TQ_S_UB
 #undef TQ_S
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -273,13 +273,18 @@ def test_encode_spectralquant():
 
 
 # ------------------------------------------------------------------- top-k
-def test_search_topk_small():
-    n, d, nq, k = 20000, 128, 8, 10
+@pytest.mark.parametrize("mode,bits,k", [("prod", 2, 10), ("prod", 3, 16), ("prod", 4, 1), ("mse", 2, 7),
+                                         ("mse", 3, 12)])
+def test_search_topk_small(mode, bits, k):
+    # 1, 2 and 3 index bits (the MFMA search), both list sizes (k <= 10 and
+    # k <= 16), prod and mse; 20000 keys over several workgroup splits
+    n, d, nq = 20000, 128, 8
     x = synth.iid_gaussian(n, d, 501)
     x = x / x.norm(dim=1, keepdim=True)
     q = synth.iid_gaussian(nq, d, 502)
-    cb = tq.Codebook(d, tq.TQ_PROD, 2, seed_rotation=503, seed_sketch=504)
-    codec = o.turboquant_codec(d, 2, "prod", rot_seed=503, sketch_seed=504)
+    m = tq.TQ_PROD if mode == "prod" else tq.TQ_MSE
+    cb = tq.Codebook(d, m, bits, seed_rotation=503, seed_sketch=504)
+    codec = o.turboquant_codec(d, bits, mode, rot_seed=503, sketch_seed=504)
     ref = o.encode(codec, x.double().numpy())
     rec = up(o.pack(codec, ref))
     s, i = tq.search_topk(cb, q.to(DEV), rec, n, k)
@@ -287,12 +292,32 @@ def test_search_topk_small():
     full = o.score(codec, q.double().numpy(), ref)
     rs, ri = o.topk(full, k)
     for r in range(nq):
+        tol = 1e-3 * np.linalg.norm(q[r].numpy()) * ref.nx.astype(np.float64)
         kth = rs[r, -1]
-        near = np.abs(full[r] - kth) <= 1e-3 * np.linalg.norm(q[r].numpy())
         got_set, ref_set = set(i[r].tolist()), set(ri[r].tolist())
         diff = got_set ^ ref_set
-        assert all(near[j] for j in diff), f"query {r}: top-k differs beyond near-ties"
-        assert np.all(np.diff(s[r]) <= 0)
+        assert all(abs(full[r, j] - kth) <= 2 * tol[j] for j in diff), f"query {r}: top-k differs beyond near-ties"
+        assert np.all(np.diff(s[r]) <= 0) and len(got_set) == k
+        assert np.all(np.abs(s[r] - full[r, i[r]]) <= tol[i[r]])
+
+
+@pytest.mark.parametrize("k", [10, 16])
+def test_search_topk_equal_scores_take_smallest_ids(k):
+    # every key is the same record, so all scores tie: the top-k must be ids
+    # 0 .. k-1 (ties go to the smaller id) across all workgroups and lists
+    n, d, nq = 70000, 128, 3
+    x = synth.iid_gaussian(1, d, 511)
+    q = synth.iid_gaussian(nq, d, 512)
+    cb = tq.Codebook(d, tq.TQ_PROD, 2, seed_rotation=503, seed_sketch=504)
+    codec = o.turboquant_codec(d, 2, "prod", rot_seed=503, sketch_seed=504)
+    one = o.encode(codec, x.double().numpy())
+    rep = o.Encoded(np.repeat(one.idx, n, axis=0), np.repeat(one.signs, n, axis=0), np.repeat(one.nx, n),
+                    np.repeat(one.nr, n), None, None)
+    s, i = tq.search_topk(cb, q.to(DEV), up(o.pack(codec, rep)), n, k)
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    for r in range(nq):
+        assert i[r].tolist() == list(range(k)), i[r].tolist()
+        assert np.all(s[r] == s[r, 0])
 
 
 # -------------------------------------------- full-size decode layer (8B GQA)
