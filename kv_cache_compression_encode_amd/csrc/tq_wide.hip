@@ -240,10 +240,35 @@ __global__ __launch_bounds__(NT, 2) void rotate_kernel(RotArgs a) {
       for (int u = 0; u < NR; ++u) dst[v][u] = reinterpret_cast<const u32x4*>(xp[v] + int64_t(kt) * KT * esz)[u];
   };
   const uint16_t* tile0 = a.tiles + size_t(cb) * nkt * (2 * AR * KT);
+  // the tile's B operands: x 2^e as fp16 hi (+ lo for fp32 input)
+  u32x4 bh[2][2], bl[2][2];
+  auto convert = [&](const u32x4 (&src)[2][NR]) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        float f[8];
+        if (XBF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = src[v][s][e];
+            f[2 * e] = __uint_as_float(w << 16) * scv[v];
+            f[2 * e + 1] = __uint_as_float(w & 0xffff0000u) * scv[v];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bh[v][s][e] = h16(f[2 * e]) | (h16(f[2 * e + 1]) << 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = __uint_as_float(src[v][2 * s + e / 4][e % 4]) * scv[v];
+          split8(f, bh[v][s], bl[v][s]);
+        }
+      }
+  };
   AStage<2> st;
   st.load(tile0);
   load_b(0, raw);
   st.store(sA[0]);
+  convert(raw);
   __syncthreads();
 
   f32x16 acc[4][2];
@@ -253,53 +278,35 @@ __global__ __launch_bounds__(NT, 2) void rotate_kernel(RotArgs a) {
     for (int v = 0; v < 2; ++v) acc[c][v] = f32x16{};
 
   for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      st.load(tile0 + size_t(kt + 1) * (2 * AR * KT));
-      load_b(kt + 1, nraw);
-    }
-    // the tile's B operands: x 2^e as fp16 hi (+ lo for fp32 input)
-    u32x4 bh[2][2], bl[2][2];
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float f[8];
-        if (XBF16) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = raw[v][s][e];
-            f[2 * e] = __uint_as_float(w << 16) * scv[v];
-            f[2 * e + 1] = __uint_as_float(w & 0xffff0000u) * scv[v];
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) bh[v][s][e] = h16(f[2 * e]) | (h16(f[2 * e + 1]) << 16);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = __uint_as_float(raw[v][2 * s + e / 4][e % 4]) * scv[v];
-          split8(f, bh[v][s], bl[v][s]);
-        }
-      }
+    // the next tile's loads first (clamped to the last tile: unconditional,
+    // so the wait counters stay exact across the loop)
+    const int kn = min(kt + 1, nkt - 1);
+    st.load(tile0 + size_t(kn) * (2 * AR * KT));
+    load_b(kn, nraw);
     const uint16_t* L = sA[kt & 1];
+    // 8 steps (s, c): the Pi fragments of step i + 1 are read from LDS while
+    // the 6 MFMAs of step i run
+    u32x4 ah[2], al[2];
+    ah[0] = afrag(L, 0, 0, 0, lane);
+    al[0] = afrag(L, 1, 0, 0, lane);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 ah = afrag(L, 0, c, s, lane), al = afrag(L, 1, c, s, lane);
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          acc[c][v] = mfma(ah, bh[v][s], acc[c][v]);
-          acc[c][v] = mfma(al, bh[v][s], acc[c][v]);
-          if (!XBF16) acc[c][v] = mfma(ah, bl[v][s], acc[c][v]);
-        }
+    for (int i = 0; i < 8; ++i) {
+      const int s = i >> 2, c = i & 3;
+      if (i + 1 < 8) {
+        ah[(i + 1) & 1] = afrag(L, 0, (i + 1) & 3, (i + 1) >> 2, lane);
+        al[(i + 1) & 1] = afrag(L, 1, (i + 1) & 3, (i + 1) >> 2, lane);
       }
-    if (more) {
-      st.store(sA[(kt + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int u = 0; u < NR; ++u) raw[v][u] = nraw[v][u];
+      for (int v = 0; v < 2; ++v) {
+        acc[c][v] = mfma(ah[i & 1], bh[v][s], acc[c][v]);
+        acc[c][v] = mfma(al[i & 1], bh[v][s], acc[c][v]);
+        if (!XBF16) acc[c][v] = mfma(ah[i & 1], bl[v][s], acc[c][v]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    convert(nraw);
+    st.store(sA[(kt + 1) & 1]);
     __syncthreads();
   }
 
@@ -469,33 +476,35 @@ __global__ __launch_bounds__(NT, 2) void sketch_kernel(SketchArgs a) {
 #pragma unroll
     for (int v = 0; v < 2; ++v) acc[c][v] = f32x16{};
   for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      st.load(tile0 + size_t(kt + 1) * (AR * KT));
-      load_b(kt + 1, nbh, nbl);
-    }
+    // the next tile's loads first (clamped, unconditional: exact wait counters)
+    const int kn = min(kt + 1, nkt - 1);
+    st.load(tile0 + size_t(kn) * (AR * KT));
+    load_b(kn, nbh, nbl);
     const uint16_t* L = sA[kt & 1];
+    // 8 steps (s, c): the S fragment of step i + 1 is read while the 4
+    // MFMAs of step i run
+    u32x4 af[2];
+    af[0] = afrag(L, 0, 0, 0, lane);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < 8; ++i) {
+      const int s = i >> 2, c = i & 3;
+      if (i + 1 < 8) af[(i + 1) & 1] = afrag(L, 0, (i + 1) & 3, (i + 1) >> 2, lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 af = afrag(L, 0, c, s, lane);
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          acc[c][v] = mfma(af, bh[v][s], acc[c][v]);
-          acc[c][v] = mfma(af, bl[v][s], acc[c][v]);
-        }
+      for (int v = 0; v < 2; ++v) {
+        acc[c][v] = mfma(af[i & 1], bh[v][s], acc[c][v]);
+        acc[c][v] = mfma(af[i & 1], bl[v][s], acc[c][v]);
       }
-    if (more) {
-      st.store(sA[(kt + 1) & 1]);
-#pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          bh[v][s] = nbh[v][s];
-          bl[v][s] = nbl[v][s];
-        }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    st.store(sA[(kt + 1) & 1]);
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bh[v][s] = nbh[v][s];
+        bl[v][s] = nbl[v][s];
+      }
     __syncthreads();
   }
   const int coord0 = 128 * cb + 16 * h;
@@ -589,7 +598,7 @@ struct SearchArgs {
   int tile_bytes, off_signs, off_nx, off_nr;
   float cen[8];             // levels of the 2- and 3-bit codebooks
   int nsplit;
-  int64_t keys_per_split;   // a multiple of BW
+  int64_t keys_per_split;   // a multiple of the workgroup's keys per tile
   int k;                    // list length (top-k)
   int nparts;               // partial lists per query = 4 * nsplit
   float* ps;                // [nq][nparts][k]
@@ -658,7 +667,8 @@ struct KeyTables {
   u32x2 cen[NC];
 };
 
-template <int UB, bool PROD, bool DENSE, int KM>  // KM: list slots (k <= KM)
+// NV: 32-key blocks per wave (the workgroup takes 128 NV keys at a time)
+template <int UB, bool PROD, bool DENSE, int KM, int NV>  // KM: list slots (k <= KM)
 __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
   constexpr int TP = 33;        // pitch of the transposition buffer (floats)
   constexpr int SP = SK + 8;    // LDS pitch of a query row (halves): 272 bytes, conflict-free 16-byte reads
@@ -720,14 +730,15 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     }
   };
 
-  for (int64_t kb = k0; kb < k1; kb += BW) {
-    int64_t key[2];
-    bool kval[2];
-    const uint8_t* kt0[2];
-    int kslot[2];
+  constexpr int WK = 32 * NV;  // keys per wave
+  for (int64_t kb = k0; kb < k1; kb += 4 * WK) {
+    int64_t key[NV];
+    bool kval[NV];
+    const uint8_t* kt0[NV];
+    int kslot[NV];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      key[v] = kb + 64 * wave + 32 * v + j;
+    for (int v = 0; v < NV; ++v) {
+      key[v] = kb + WK * wave + 32 * v + j;
       kval[v] = key[v] < k1;
       const int64_t lk = kval[v] ? key[v] : k1 - 1;
       kt0[v] = a.rec + (lk / kTile) * a.tile_bytes;
@@ -736,10 +747,10 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     // record chunks of tile kt: the sign chunk kt (kt < GS), else chunk kt - GS
     // of every code plane (branch-free: the sign tiles read the sign chunk
     // into every plane register)
-    auto load_chunks = [&](int kt, u32x4 (&dst)[2][UB]) {
+    auto load_chunks = [&](int kt, u32x4 (&dst)[NV][UB]) {
       const bool sg = PROD && kt < GS;
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int p = 0; p < UB; ++p) {
           const size_t off = sg ? size_t(a.off_signs) + size_t(kt) * kTile * 16
@@ -747,16 +758,16 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
           dst[v][p] = *reinterpret_cast<const u32x4*>(kt0[v] + off + size_t(kslot[v]) * 16);
         }
     };
-    u32x4 cw[2][UB], ncw[2][UB];
+    u32x4 cw[NV][UB], ncw[NV][UB];
     stage_load(0);
     load_chunks(0, cw);
     stage_store(sA[0]);
     __syncthreads();
-    f32x16 acc[4][2];
+    f32x16 acc[4][NV];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int v = 0; v < 2; ++v) acc[c][v] = f32x16{};
+      for (int v = 0; v < NV; ++v) acc[c][v] = f32x16{};
     // One tile of 128 reduction elements; the next tile's query rows and
     // record chunks are loaded first (clamped to the last tile: the loads are
     // unconditional, so the wait counters stay exact across the loop).
@@ -769,11 +780,11 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       // 8 MFMA steps of 16: step t = (kq, s) takes elements 32 kq + 16 h + 8 s .. + 7.
       // The LDS reads of step t + 1 (query fragments, key table rows) are
       // issued before the MFMAs of step t, so their latency hides behind them.
-      auto read_step = [&](int t, u32x4 (&af)[4], u32x4 (&bf)[2]) {
+      auto read_step = [&](int t, u32x4 (&af)[4], u32x4 (&bf)[NV]) {
         const int kq = t >> 1, s = t & 1;
         const int sh = 16 * h + 8 * s;
 #pragma unroll
-        for (int v = 0; v < 2; ++v) {
+        for (int v = 0; v < NV; ++v) {
           if (SIGNS || UB == 1) {
             bf[v] = tb.pm[(cw[v][0][kq] >> sh) & 0xffu];
           } else {
@@ -792,28 +803,40 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
         for (int c = 0; c < 4; ++c)
           af[c] = *reinterpret_cast<const u32x4*>(LA + (32 * c + j) * SP + 32 * kq + 16 * h + 8 * s);
       };
-      auto mma_step = [&](const u32x4 (&af)[4], const u32x4 (&bf)[2]) {
+      auto mma_step = [&](const u32x4 (&af)[4], const u32x4 (&bf)[NV]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int v = 0; v < 2; ++v) acc[c][v] = mfma(af[c], bf[v], acc[c][v]);
+          for (int v = 0; v < NV; ++v) acc[c][v] = mfma(af[c], bf[v], acc[c][v]);
       };
-      u32x4 afA[4], bfA[2], afB[4], bfB[2];
+      // The reads of step t + 1 are interleaved with the 8 MFMAs of step t
+      // (one MFMA, then an LDS read and a few ALU instructions, eight times),
+      // so that they issue while the matrix core is busy.
+      auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4 * NV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three VALU
+        }
+      };
+      u32x4 afA[4], bfA[NV], afB[4], bfB[NV];
       read_step(0, afA, bfA);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
         read_step(t + 1, afB, bfB);
-        __builtin_amdgcn_sched_barrier(0);
         mma_step(afA, bfA);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
         if (t + 2 < 8) read_step(t + 2, afA, bfA);
-        __builtin_amdgcn_sched_barrier(0);
         mma_step(afB, bfB);
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
       }
       stage_store(sA[(kt + 1) & 1]);
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int p = 0; p < UB; ++p) cw[v][p] = ncw[v][p];
       __syncthreads();
@@ -822,7 +845,7 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     if (PROD) {
       // between the sign phase and the code phase: acc *= n_r of the key
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
+      for (int v = 0; v < NV; ++v) {
         const float nr = f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nr + 2 * kslot[v]));
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c][v] *= nr;
@@ -830,9 +853,9 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     }
     for (int kt = GS; kt < nkt; ++kt) tile(kt, std::integral_constant<bool, false>{});
     // ---- epilogue: s = acc n_x inv_q; acc[c][v][r] is query 32 c + 8 (r / 4) + 4 h + r % 4, key v
-    float nxv[2];
+    float nxv[NV];
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int v = 0; v < NV; ++v)
       nxv[v] = kval[v] ? f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nx + 2 * kslot[v])) : 0.f;
     if (DENSE) {
 #pragma unroll
@@ -844,7 +867,7 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
           if (q >= a.nq) continue;
           const float iq = sinv[qrow];
 #pragma unroll
-          for (int v = 0; v < 2; ++v)
+          for (int v = 0; v < NV; ++v)
             if (kval[v]) a.scores[q * a.n + key[v]] = acc[c][v][r] * nxv[v] * iq;
         }
       continue;
@@ -863,7 +886,7 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       const float tg = float_of_ord(__hip_atomic_load(tq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       const float ts0 = Lq.ts;
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
+      for (int v = 0; v < NV; ++v) {
         // queries 64 hq .. 64 hq + 63 x keys 32 v .. 32 v + 31 of the wave, via LDS
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
@@ -873,8 +896,8 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int kbase = int(kb) + 64 * wave + 32 * v;  // key id of column 0 (n < 2^31)
-        const int kvalid = int(min<int64_t>(32, max<int64_t>(0, k1 - (kb + 64 * wave + 32 * v))));
+        const int kbase = int(kb) + WK * wave + 32 * v;  // key id of column 0 (n < 2^31)
+        const int kvalid = int(min<int64_t>(32, max<int64_t>(0, k1 - (kb + WK * wave + 32 * v))));
         const float* row = T + lane * TP;
         uint32_t cand = 0;
 #pragma unroll
@@ -1110,15 +1133,21 @@ bool search_mfma_supported(const CodecView& cv) {
          cv.ubits <= 3 && (cv.mode != TQ_PROD || cv.m == cv.d);
 }
 
+// 32-key blocks per wave of the search kernel (four would let each query
+// fragment feed four MFMAs, but the accumulators then leave too few
+// registers for the lists and the record chunks)
+int search_nv(const CodecView&) { return 2; }
+
 SearchPlan search_plan(const CodecView& cv, int64_t nq, int64_t n, int cus) {
   SearchPlan p{};
   p.nqb = int((nq + AR - 1) / AR);
-  const int64_t wgt = (n + BW - 1) / BW;  // workgroup tiles of keys
+  const int wgk = 128 * search_nv(cv);          // keys per workgroup tile
+  const int64_t wgt = (n + wgk - 1) / wgk;      // workgroup tiles of keys
   int64_t ns = std::max<int64_t>(1, (int64_t(cus) + p.nqb - 1) / p.nqb);
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, wgt));
   ns = std::min<int64_t>(ns, 256);  // the merge takes at most 1024 lists per query
   p.nsplit = int(ns);
-  p.keys_per_split = (wgt + ns - 1) / ns * BW;
+  p.keys_per_split = (wgt + ns - 1) / ns * wgk;
   p.nparts = 4 * p.nsplit;
   const int K = cv.d + (cv.mode == TQ_PROD ? cv.m : 0);
   auto rnd = [](size_t v) { return (v + 255) & ~size_t(255); };
@@ -1170,12 +1199,12 @@ hipError_t launch_search(const CodecView& cv, const float* qr, const float* qs, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(unsigned(p.nqb * p.nsplit));
-#define TQ_S(U, P, D, KM) hipLaunchKernelGGL((search_kernel<U, P, D, KM>), grid, dim3(NT), 0, s, sa)
-#define TQ_S_UB(P, D, KM)                 \
-  switch (cv.ubits) {                     \
-    case 1: TQ_S(1, P, D, KM); break;     \
-    case 2: TQ_S(2, P, D, KM); break;     \
-    default: TQ_S(3, P, D, KM); break;    \
+#define TQ_S(U, P, D, KM, NV) hipLaunchKernelGGL((search_kernel<U, P, D, KM, NV>), grid, dim3(NT), 0, s, sa)
+#define TQ_S_UB(P, D, KM)                    \
+  switch (cv.ubits) {                        \
+    case 1: TQ_S(1, P, D, KM, 2); break;     \
+    case 2: TQ_S(2, P, D, KM, 2); break;     \
+    default: TQ_S(3, P, D, KM, 2); break;    \
   }
   if (dense) {
     if (prod) { TQ_S_UB(true, true, 1) } else { TQ_S_UB(false, true, 1) }
