@@ -99,8 +99,9 @@ typedef struct tq_codebook tq_codebook;
  *              TQ_ROT_GIVEN: Pi taken from `given` (host, [num_heads][d][d]
  *              fp32, row i = i-th basis vector), Beta-law codebooks.
  *              TQ_ROT_CALIBRATE: per head, Pi = eigenvectors of the centred
- *              covariance of `calib` (host, [num_heads][calib_n][d] of
- *              calib_dtype), eigenvalues descending, each row signed so its
+ *              covariance of `calib` ([num_heads][calib_n][d] of
+ *              calib_dtype; host, or device with calib_on_device), eigenvalues
+ *              descending, each row signed so its
  *              largest-magnitude entry is positive ([SQ] tweet 4); per-dim
  *              codebook = Gaussian Lloyd-Max with b_i levels scaled by sigma_i,
  *              the RMS of rotated coordinate i of the normalised calibration
@@ -111,8 +112,12 @@ typedef struct tq_codebook tq_codebook;
  *              Sylvester Walsh-Hadamard matrix (H[i][j] = (-1)^popcount(i & j))
  *              and s_j = +1 / -1 from bit 0 of word j of the Philox stream 3
  *              of seed_rotation; d must be a power of two; Beta-law codebooks
- *              as for TQ_ROT_HAAR.  The d = 128 encode applies it as a fast
- *              Walsh-Hadamard transform; every other call uses Pi itself.
+ *              as for TQ_ROT_HAAR.  At d = 128 it is applied as a fast
+ *              Walsh-Hadamard transform by the query rotation (tq_score,
+ *              tq_search_topk, tq_decode_attend, tq_decode_step), the inverse
+ *              value rotation of the decode output, tq_append, and tq_encode of
+ *              bf16 inputs into mse COL 4-bit or prod ROW 2-bit records; the
+ *              other encodes use Pi itself.
  *   num_heads  rotations held by the codebook (one per KV head for
  *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN, or per outlier channel list of
  *              a split codec); TQ_ROT_HAAR otherwise uses 1.
@@ -152,6 +157,14 @@ typedef struct tq_codebook tq_codebook;
  *   outlier_bits   total bits per coordinate of the outlier instance.
  *   outlier_channels  host int32 [num_heads][o]: distinct channels in [0, d)
  *              per head (head h of a multi-head codec uses row h).
+ *   calib_on_device  TQ_ROT_CALIBRATE: 0 = `calib` is a host array and the
+ *              calibration runs on the host; 1 = `calib` is a device array on
+ *              `device` (same shape and dtype) and the O(calib_n d^2) part of
+ *              the calibration runs there: per head the fp64 column sums,
+ *              second moment and second moment of the normalised vectors
+ *              ([SQ] tweet 4: the short calibration pass); the d x d
+ *              eigensolves and the codebooks stay on the host.  Needs d a
+ *              multiple of 32 and device >= 0.
  */
 typedef struct {
   int32_t d;
@@ -173,6 +186,7 @@ typedef struct {
   int32_t outlier_dims;
   int32_t outlier_bits;
   const int32_t* outlier_channels;
+  int32_t calib_on_device;
 } tq_codebook_desc;
 
 /* Sizes of a codec's records. */

@@ -62,7 +62,18 @@ class Codebook:
             keep.append(g)
             desc.given = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
         if calib is not None:
-            if isinstance(calib, torch.Tensor):
+            if isinstance(calib, torch.Tensor) and calib.is_cuda:
+                # calibration moments on the device that holds the vectors
+                c = calib.contiguous()
+                if c.dtype not in (torch.bfloat16, torch.float32) or c.device.index != device:
+                    raise ValueError("device calib: bf16 or fp32 on the codebook's device")
+                desc.calib_dtype = TQ_BF16 if c.dtype == torch.bfloat16 else TQ_F32
+                desc.calib_on_device = 1
+                torch.cuda.synchronize(c.device)  # the build reads it on the null stream
+                keep.append(c)
+                desc.calib = c.data_ptr()
+                desc.calib_n = c.shape[-2]
+            elif isinstance(calib, torch.Tensor):
                 if calib.dtype == torch.bfloat16:
                     c = np.ascontiguousarray(calib.cpu().view(torch.int16).numpy())
                     desc.calib_dtype = TQ_BF16
@@ -72,9 +83,10 @@ class Codebook:
             else:
                 c = np.ascontiguousarray(np.asarray(calib, dtype=np.float32))
                 desc.calib_dtype = TQ_F32
-            keep.append(c)
-            desc.calib = c.ctypes.data
-            desc.calib_n = c.shape[-2]
+            if not desc.calib_on_device:
+                keep.append(c)
+                desc.calib = c.ctypes.data
+                desc.calib_n = c.shape[-2]
         desc.device = device
         desc.waterfill_bits = waterfill_bits
         if outlier_channels is not None:

@@ -31,7 +31,8 @@ class CodebookDesc(ctypes.Structure):
                 ("calib_dtype", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("waterfill_bits", ctypes.c_int32), ("outlier_dims", ctypes.c_int32),
                 ("outlier_bits", ctypes.c_int32),
-                ("outlier_channels", ctypes.POINTER(ctypes.c_int32))]
+                ("outlier_channels", ctypes.POINTER(ctypes.c_int32)),
+                ("calib_on_device", ctypes.c_int32)]
 
 
 class CodebookInfo(ctypes.Structure):

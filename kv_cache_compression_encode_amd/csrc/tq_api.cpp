@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <thread>
 
 #include "tq_internal.h"
 #include "tq_kernels.h"
@@ -16,6 +18,60 @@ using namespace tq;
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// f(h) for h < heads, spread over host threads (one per head up to the
+// hardware's count).  False if any call ran out of memory.
+template <class F>
+bool for_each_head(int heads, F&& f) {
+  std::atomic<bool> ok{true};
+  auto run = [&](int h) {
+    try {
+      f(h);
+    } catch (const std::bad_alloc&) {
+      ok = false;
+    }
+  };
+  const int nth = std::max(1, std::min<int>(heads, int(std::thread::hardware_concurrency())));
+  if (nth == 1) {
+    for (int h = 0; h < heads; ++h) run(h);
+  } else {
+    std::vector<std::thread> pool;
+    for (int w = 0; w < nth; ++w)
+      pool.emplace_back([&, w] {
+        for (int h = w; h < heads; h += nth) run(h);
+      });
+    for (std::thread& t : pool) t.join();
+  }
+  return ok;
+}
+
+// The calibration moments on the device (calib_on_device): per head the
+// column sums, sum_t x x^T and sum_t x x^T / ||x||^2, fp64, copied back.
+tq_status device_moments(const tq_codebook_desc& ds, int heads, std::vector<double>& mom_x,
+                         std::vector<double>& mom_u, std::vector<double>& sum_x) {
+  const int d = ds.d;
+  const int64_t n = ds.calib_n;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  if (hipSetDevice(ds.device) != hipSuccess) return TQ_EDEVICE;
+  const size_t dd = size_t(heads) * d * d, hd = size_t(heads) * d;
+  double* buf = nullptr;
+  tq_status st = TQ_OK;
+  if (hipMalloc(reinterpret_cast<void**>(&buf), (2 * dd + hd + size_t(heads) * n) * sizeof(double)) != hipSuccess) {
+    st = TQ_ENOMEM;
+  } else {
+    double *mx = buf, *mu = mx + dd, *sx = mu + dd, *rinv2 = sx + hd;
+    if (launch_calib_moments(ds.calib, ds.calib_dtype == TQ_BF16, heads, n, d, rinv2, mx, mu, sx, nullptr) !=
+            hipSuccess ||
+        hipMemcpy(mom_x.data(), mx, dd * sizeof(double), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(mom_u.data(), mu, dd * sizeof(double), hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(sum_x.data(), sx, hd * sizeof(double), hipMemcpyDeviceToHost) != hipSuccess)
+      st = TQ_EDEVICE;
+    (void)hipFree(buf);
+  }
+  (void)hipSetDevice(prev);
+  return st;
+}
 
 template <class T>
 tq_status upload(T** dst, const T* src, size_t count) {
@@ -28,7 +84,7 @@ void free_device(tq_codebook* cb) {
   DeviceTables& t = cb->dev;
   void* ptrs[] = {t.rot, t.rot_t, t.rot_hi, t.rot_lo, t.sketch, t.sketch_t, t.sketch_hi,
                   t.sketch_lo, t.thr, t.cen, t.bitpos, t.dim_bits, t.sq_tail, t.sq_gm, t.had_mask,
-                  t.omask, t.rot_tiles, t.sk_tiles};
+                  t.had_sign, t.omask, t.rot_tiles, t.sk_tiles};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   t = DeviceTables{};
@@ -215,6 +271,7 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
 
   // ----------------------------------------------------------- rotations
   int heads = 1;
+  std::vector<double> mom_u;  // calibration on the device: sum_t u u^T per head
   if (ds.rotation == TQ_ROT_HAAR) {
     std::vector<double> g(size_t(d) * d);
     philox_normals(ds.seed_rotation, 1, int64_t(d) * d, g.data());
@@ -246,30 +303,52 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
     if (ds.calib_dtype != TQ_F32 && ds.calib_dtype != TQ_BF16) return TQ_EINVAL;
     heads = std::max(1, ds.num_heads);
     cb->rot64.resize(size_t(heads) * d * d);
-    std::vector<double> x(size_t(ds.calib_n) * d), cov(size_t(d) * d), lam(d);
-    for (int h = 0; h < heads; ++h) {
-      for (int64_t t = 0; t < ds.calib_n; ++t)
-        for (int i = 0; i < d; ++i) {
-          const size_t e = (size_t(h) * ds.calib_n + t) * d + i;
-          x[size_t(t) * d + i] = ds.calib_dtype == TQ_F32
-                                     ? double(static_cast<const float*>(ds.calib)[e])
-                                     : double(bf16_to_f32(static_cast<const uint16_t*>(ds.calib)[e]));
+    const double nn = double(ds.calib_n);
+    std::vector<double> cov(size_t(heads) * d * d);
+    if (ds.calib_on_device) {
+      if (d % 32 != 0 || ds.device < 0) return TQ_EINVAL;
+      std::vector<double> sum_x(size_t(heads) * d);
+      mom_u.resize(size_t(heads) * d * d);
+      const tq_status ms = device_moments(ds, heads, cov, mom_u, sum_x);
+      if (ms != TQ_OK) return ms;
+      // centred covariance: sum_t x x^T / n - mean mean^T
+      for (int h = 0; h < heads; ++h)
+        for (int i = 0; i < d; ++i)
+          for (int k = 0; k < d; ++k) {
+            double& c = cov[(size_t(h) * d + i) * d + k];
+            c = c / nn - (sum_x[size_t(h) * d + i] / nn) * (sum_x[size_t(h) * d + k] / nn);
+          }
+    } else {
+      const bool ok = for_each_head(heads, [&](int h) {
+        std::vector<double> x(size_t(ds.calib_n) * d), mean(d, 0.0);
+        for (int64_t t = 0; t < ds.calib_n; ++t)
+          for (int i = 0; i < d; ++i) {
+            const size_t e = (size_t(h) * ds.calib_n + t) * d + i;
+            x[size_t(t) * d + i] = ds.calib_dtype == TQ_F32
+                                       ? double(static_cast<const float*>(ds.calib)[e])
+                                       : double(bf16_to_f32(static_cast<const uint16_t*>(ds.calib)[e]));
+          }
+        for (int64_t t = 0; t < ds.calib_n; ++t)
+          for (int i = 0; i < d; ++i) mean[i] += x[size_t(t) * d + i];
+        for (int i = 0; i < d; ++i) mean[i] /= nn;
+        double* cv = &cov[size_t(h) * d * d];
+        for (int64_t t = 0; t < ds.calib_n; ++t) {
+          const double* r = &x[size_t(t) * d];
+          for (int i = 0; i < d; ++i) {
+            const double a = r[i] - mean[i];
+            for (int k = 0; k < d; ++k) cv[size_t(i) * d + k] += a * (r[k] - mean[k]);
+          }
         }
-      std::vector<double> mean(d, 0.0);
-      for (int64_t t = 0; t < ds.calib_n; ++t)
-        for (int i = 0; i < d; ++i) mean[i] += x[size_t(t) * d + i];
-      for (int i = 0; i < d; ++i) mean[i] /= double(ds.calib_n);
-      std::fill(cov.begin(), cov.end(), 0.0);
-      for (int64_t t = 0; t < ds.calib_n; ++t) {
-        const double* r = &x[size_t(t) * d];
-        for (int i = 0; i < d; ++i) {
-          const double a = r[i] - mean[i];
-          for (int k = 0; k < d; ++k) cov[size_t(i) * d + k] += a * (r[k] - mean[k]);
-        }
-      }
-      for (double& c : cov) c /= double(ds.calib_n);
-      symmetric_eigen(d, cov.data(), lam.data(), &cb->rot64[size_t(h) * d * d]);
+        for (size_t e = 0; e < size_t(d) * d; ++e) cv[e] /= nn;
+      });
+      if (!ok) return TQ_ENOMEM;
     }
+    // the d x d eigensolves, one host thread per head
+    const bool ok = for_each_head(heads, [&](int h) {
+      std::vector<double> lam(d);
+      symmetric_eigen(d, &cov[size_t(h) * d * d], lam.data(), &cb->rot64[size_t(h) * d * d]);
+    });
+    if (!ok) return TQ_ENOMEM;
   } else {
     return TQ_EINVAL;
   }
@@ -290,7 +369,25 @@ tq_status build_host(tq_codebook* cb, const tq_codebook_desc& ds) {
   // sigma_i (per head): RMS of rotated coordinate i of the normalised
   // calibration vectors
   std::vector<double> sig(size_t(heads) * d, 1.0);
-  if (ds.rotation == TQ_ROT_CALIBRATE) {
+  if (ds.rotation == TQ_ROT_CALIBRATE && !mom_u.empty()) {
+    // from the device moments: sigma_i^2 = p_i^T (sum_t u u^T) p_i / n
+    const bool ok = for_each_head(heads, [&](int h) {
+      const double* M = &mom_u[size_t(h) * d * d];
+      std::vector<double> p(d), w(d);
+      for (int i = 0; i < d; ++i) {
+        for (int k = 0; k < d; ++k) p[k] = double(cb->rot32[(size_t(h) * d + i) * d + k]);
+        for (int j = 0; j < d; ++j) {
+          double acc = 0;
+          for (int k = 0; k < d; ++k) acc += M[size_t(j) * d + k] * p[k];
+          w[j] = acc;
+        }
+        double v = 0;
+        for (int j = 0; j < d; ++j) v += p[j] * w[j];
+        sig[size_t(h) * d + i] = std::sqrt(std::max(v, 0.0) / double(ds.calib_n));
+      }
+    });
+    if (!ok) return TQ_ENOMEM;
+  } else if (ds.rotation == TQ_ROT_CALIBRATE) {
     std::vector<double> acc(d), u(d);
     for (int h = 0; h < heads; ++h) {
       std::fill(acc.begin(), acc.end(), 0.0);
@@ -449,6 +546,8 @@ tq_status build_device(tq_codebook* cb) {
         mask[hh * 32 + k] = (cb->hsign[i0] < 0 ? 0x8000u : 0u) | (cb->hsign[i0 + 1] < 0 ? 0x80000000u : 0u);
       }
     if ((st = upload(&cb->dev.had_mask, mask.data(), mask.size())) != TQ_OK) return st;
+    std::vector<float> sgn(cb->hsign.begin(), cb->hsign.end());
+    if ((st = upload(&cb->dev.had_sign, sgn.data(), sgn.size())) != TQ_OK) return st;
   }
   if (!cb->omask.empty())
     if ((st = upload(&cb->dev.omask, cb->omask.data(), cb->omask.size())) != TQ_OK) return st;
@@ -558,6 +657,7 @@ CodecView tq::make_view(const tq_codebook* cb) {
   v.sq_tail = cb->dev.sq_tail;
   v.sq_gm = cb->dev.sq_gm;
   v.had_mask = cb->dev.had_mask;
+  v.had_sign = cb->dev.had_sign;
   v.rot_tiles = cb->dev.rot_tiles;
   v.sk_tiles = cb->dev.sk_tiles;
   for (int k = 0; k < kMaxLevels; ++k) {

@@ -83,10 +83,15 @@ __device__ __forceinline__ void append_one(const CodecView& cv, const AppendArgs
 #pragma unroll
     for (int p = 0; p < kMaxBits; ++p) bpos[p] = cv.bitpos[p * D + i];
   }
+  // randomized Hadamard rotation: z = H (s x) / sqrt(d) by the wave
+  // transform instead of the columns of Pi
+  const bool had = cv.had_sign != nullptr;
   {
     const float* rt = cv.rot_t + size_t(hc) * D * D + size_t(64 * half) * D + i;
+    if (!had) {
 #pragma unroll
-    for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+      for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+    }
     if (full_sketch) {
       const float* st = cv.sketch_t + size_t(64 * half) * D + i;
 #pragma unroll
@@ -104,7 +109,19 @@ __device__ __forceinline__ void append_one(const CodecView& cv, const AppendArgs
   __syncthreads();
 
   // ---- z = Pi x (unnormalised): half sums, then coordinate i on threads < 128
-  {
+  if (had) {
+    // wave 0 transforms, wave 1 zeroes the second half's sums
+    const int lane = t & 63, wv = t >> 6;
+    if (wv == 0) {
+      float lo = sx[lane] * cv.had_sign[lane], hi = sx[lane + 64] * cv.had_sign[lane + 64];
+      fwht128_wave(lo, hi, lane);
+      part[0][lane] = lo * kInvSqrt128;
+      part[0][lane + 64] = hi * kInvSqrt128;
+    } else if (wv == 1) {
+      part[1][lane] = 0.f;
+      part[1][lane + 64] = 0.f;
+    }
+  } else {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int u = 0; u < D / 2; u += 2) {

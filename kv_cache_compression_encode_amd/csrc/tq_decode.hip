@@ -208,11 +208,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // transposed matrices column-coalesced (all their loads go out first).
   const int hk = kc.heads > 1 ? g : 0;
   const int ci = threadIdx.x & (D - 1), kh = threadIdx.x >> 7;
+  // randomized Hadamard keys: q' = H (s q) / sqrt(d) by the wave transform
+  // instead of the columns of Pi
+  const bool khad = kc.had_sign != nullptr;
   float rcol[D / 2], scol[SQ ? 1 : D / 2];
   {
     const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(kh * (D / 2)) * D + ci;
+    if (!khad) {
 #pragma unroll
-    for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+      for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+    }
     if (!SQ) {
       const float* st = kc.sketch_t + size_t(kh * (D / 2)) * D + ci;
 #pragma unroll
@@ -248,18 +253,26 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   {
     // q' = Pi q: half sums into the (still unused) merge buffer, then added
     float* part = &sacc[0][0][0];  // [2][4][D]
+    if (khad) {
+      // wave w transforms query w
+      float lo = sqs[wave][lane] * kc.had_sign[lane], hi = sqs[wave][lane + 64] * kc.had_sign[lane + 64];
+      fwht128_wave(lo, hi, lane);
+      sqr[wave][lane] = lo * kInvSqrt128;
+      sqr[wave][lane + 64] = hi * kInvSqrt128;
+    } else {
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      float s0 = 0.f, s1 = 0.f;
+      for (int gg = 0; gg < 4; ++gg) {
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int u = 0; u < D / 2; u += 2) {
-        s0 = fmaf(rcol[u], sqs[gg][kh * (D / 2) + u], s0);
-        s1 = fmaf(rcol[u + 1], sqs[gg][kh * (D / 2) + u + 1], s1);
+        for (int u = 0; u < D / 2; u += 2) {
+          s0 = fmaf(rcol[u], sqs[gg][kh * (D / 2) + u], s0);
+          s1 = fmaf(rcol[u + 1], sqs[gg][kh * (D / 2) + u + 1], s1);
+        }
+        part[(kh * 4 + gg) * D + ci] = s0 + s1;
       }
-      part[(kh * 4 + gg) * D + ci] = s0 + s1;
+      __syncthreads();
+      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqr[e / D][e % D] = part[e] + part[4 * D + e];
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqr[e / D][e % D] = part[e] + part[4 * D + e];
     __syncthreads();
     if (!SQ) {
       // qs = S q' (m = d)
@@ -616,6 +629,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     sqr[gg][i] = l > 0.f ? accs / l : 0.f;
   }
   __syncthreads();
+  if (vc.had_sign) {
+    // randomized Hadamard values: out = s (H y) / sqrt(d), wave w for query w
+    if (wave < G) {
+      float lo = sqr[wave][lane], hi = sqr[wave][lane + 64];
+      fwht128_wave(lo, hi, lane);
+      float* o = a.out + (int64_t(b) * a.Hq + g * G + wave) * D;
+      o[lane] = vc.had_sign[lane] * lo * kInvSqrt128;
+      o[lane + 64] = vc.had_sign[lane + 64] * hi * kInvSqrt128;
+    }
+    return;
+  }
   {
     const int i = threadIdx.x & (D - 1), half = threadIdx.x >> 7;
     const int hv = vc.heads > 1 ? g : 0;

@@ -71,6 +71,7 @@ struct DeviceTables {
   // randomized Hadamard rotation at d = 128: per half h of the input (dims
   // 64h .. 64h + 63) and packed bf16 pair k, the sign bits (15 and 31) to flip
   uint32_t* had_mask = nullptr;  // [2][32]
+  float* had_sign = nullptr;     // [d] the signs s as +-1.0f (query and value-output transforms)
   // outlier-channel split: per head, bit c of the 128-bit mask = channel c is an outlier
   uint32_t* omask = nullptr;     // [H][4]
   // wide uniform codecs (d a multiple of 128 other than 128): the rotation and

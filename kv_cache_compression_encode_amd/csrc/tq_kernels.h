@@ -36,6 +36,7 @@ struct CodecView {
   const uint32_t* sq_tail;  // non-uniform d = 128: tail byte -> packed index bits of dims 0..3
   const float* sq_gm;       // non-uniform d = 128: [H][2][d] half-difference and mean of levels 0, 1
   const uint32_t* had_mask; // randomized Hadamard, d = 128: [2][32] XOR masks of the bf16 sign bits
+  const float* had_sign;    // randomized Hadamard, d = 128: the signs s [d] as +-1.0f
   // d a multiple of 128 other than 128, uniform codecs: the MFMA operand tiles
   // [d/128][d/32][hi, lo][128][32] of 16 Pi and [m/128][m/32][128][32] of S
   const uint16_t* rot_tiles;
@@ -45,6 +46,13 @@ struct CodecView {
 };
 
 CodecView make_view(const tq_codebook* cb);
+
+// Calibration moments (SpectralQuant rotation) of heads x n vectors of d
+// coordinates (d a multiple of 32), fp64: per head the column sums [d], the
+// second moment [d][d] and the second moment of the normalised vectors
+// [d][d]; rinv2 is scratch of heads * n doubles.
+hipError_t launch_calib_moments(const void* x, int bf16, int heads, int64_t n, int d, double* rinv2,
+                                double* mom_x, double* mom_u, double* sum_x, hipStream_t s);
 
 struct EncodeArgs {
   const void* x;
@@ -127,6 +135,27 @@ __device__ __forceinline__ int64_t paged_tile(const int32_t* block_table, int pa
   const int pg = block_table[row * max_pages + (t >> page_shift)];
   return (int64_t(pg) << page_shift) + (t & ((1 << page_shift) - 1));
 }
+// Unnormalised Walsh-Hadamard transform in Sylvester order, y = H x with
+// H[i][j] = (-1)^popcount(i & j), of a 128-vector held by one wave: lane l
+// owns coordinates l (lo) and l + 64 (hi).  The stride-64 butterfly is within
+// the lane, strides 32 .. 1 pair lane l with lane l ^ stride (the lower one
+// keeps the sum, the upper one the difference).  The randomized Hadamard
+// rotation Pi = H diag(s) / sqrt(d) is then Pi x = H (s x) / sqrt(d) and
+// Pi^T y = s (H y) / sqrt(d), H being symmetric.
+__device__ __forceinline__ void fwht128_wave(float& lo, float& hi, int lane) {
+  const float a = lo + hi, b = lo - hi;
+  lo = a;
+  hi = b;
+#pragma unroll
+  for (int st = 32; st > 0; st >>= 1) {
+    const float pl = __shfl_xor(lo, st, 64), ph = __shfl_xor(hi, st, 64);
+    const bool up = (lane & st) != 0;
+    lo = up ? pl - lo : lo + pl;
+    hi = up ? ph - hi : hi + ph;
+  }
+}
+constexpr float kInvSqrt128 = 0.08838834764831845f;  // 1 / sqrt(128)
+
 hipError_t launch_decode(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
                          hipStream_t s);
 // MFMA decode partial kernel (d = 128, prod keys with 1-2 index bits and a

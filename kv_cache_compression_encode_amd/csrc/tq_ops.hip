@@ -59,9 +59,14 @@ __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrep
   const bool full_sketch = cv.mode == TQ_PROD && cv.m == D;
   const float* rt = cv.rot_t + size_t(head) * D * D + size_t(KH * kh) * D + i;
   const float* st = cv.sketch_t + size_t(KH * kh) * D + i;
+  // randomized Hadamard rotation: q' = H (s q) / sqrt(d) by the wave
+  // transform, so no columns of Pi are read
+  const bool had = cv.had_sign != nullptr;
   float r[KH], sk[KH];
+  if (!had) {
 #pragma unroll
-  for (int u = 0; u < KH; ++u) r[u] = rt[size_t(u) * D];
+    for (int u = 0; u < KH; ++u) r[u] = rt[size_t(u) * D];
+  }
   if (full_sketch) {
 #pragma unroll
     for (int u = 0; u < KH; ++u) sk[u] = st[size_t(u) * D];
@@ -97,7 +102,23 @@ __global__ __launch_bounds__(256) void query_prep_kernel(CodecView cv, QueryPrep
     }
     __syncthreads();
   };
-  matvec(r, sq, sr, a.qr, D);
+  if (had) {
+    const int lane = threadIdx.x & 63;
+    const float s_lo = cv.had_sign[lane], s_hi = cv.had_sign[lane + 64];
+    for (int qq = threadIdx.x >> 6; qq < nqb; qq += blockDim.x >> 6) {  // one query per wave
+      float lo = sq[qq * D + lane] * s_lo, hi = sq[qq * D + lane + 64] * s_hi;
+      fwht128_wave(lo, hi, lane);
+      lo *= kInvSqrt128;
+      hi *= kInvSqrt128;
+      sr[qq * D + lane] = lo;
+      sr[qq * D + lane + 64] = hi;
+      a.qr[(q0 + qq) * D + lane] = lo;
+      a.qr[(q0 + qq) * D + lane + 64] = hi;
+    }
+    __syncthreads();
+  } else {
+    matvec(r, sq, sr, a.qr, D);
+  }
   if (cv.mode != TQ_PROD) return;
   if (full_sketch) {
     matvec(sk, sr, nullptr, a.qs, D);
@@ -508,9 +529,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CodecView vc, Decod
   // rotation columns: out_i = sum_k Pi[k][i] y_k, k in this half
   const int hv = vc.heads > 1 ? g : 0;
   const float* rot = vc.rot + size_t(hv) * D * D + size_t(64 * half) * D + i;
+  const bool had = vc.had_sign != nullptr;  // randomized Hadamard: out = s (H y) / sqrt(d)
   float r[64];
+  if (!had) {
 #pragma unroll
-  for (int u = 0; u < 64; ++u) r[u] = rot[size_t(u) * D];
+    for (int u = 0; u < 64; ++u) r[u] = rot[size_t(u) * D];
+  }
   const float* pa = part + 2 * G + gg * D + i;
   float accv = 0.f, M, l;
   if (ns <= kFast) {
@@ -581,6 +605,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CodecView vc, Decod
   __syncthreads();
   if (half == 0) sy[0][i] = l > 0.f ? (sy[0][i] + sy[1][i]) / l : 0.f;
   __syncthreads();
+  if (had) {
+    if (wv == 0) {
+      float lo = sy[0][lane], hi = sy[0][lane + 64];
+      fwht128_wave(lo, hi, lane);
+      float* o = a.out + (int64_t(b) * a.Hq + hq) * D;
+      o[lane] = vc.had_sign[lane] * lo * kInvSqrt128;
+      o[lane + 64] = vc.had_sign[lane + 64] * hi * kInvSqrt128;
+    }
+    return;
+  }
   const float* yk = sy[0] + 64 * half;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

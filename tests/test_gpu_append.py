@@ -56,6 +56,9 @@ def _run(kind, dtype=torch.bfloat16):
     elif kind == "values":
         cb = tq.Codebook(128, tq.TQ_MSE, 4, seed_rotation=707, layout=tq.TQ_LAYOUT_COL)
         codec = o.turboquant_codec(128, 4, "mse", rot_seed=707, layout="col")
+    elif kind == "values_hadamard":
+        cb = tq.Codebook(128, tq.TQ_MSE, 4, rotation=tq.TQ_ROT_HADAMARD, seed_rotation=707, layout=tq.TQ_LAYOUT_COL)
+        codec = o.turboquant_codec(128, 4, "mse", rot_seed=707, layout="col", rotation="hadamard")
     elif kind == "values2":
         cb = tq.Codebook(128, tq.TQ_MSE, 2, seed_rotation=707, layout=tq.TQ_LAYOUT_COL)
         codec = o.turboquant_codec(128, 2, "mse", rot_seed=707, layout="col")
@@ -92,7 +95,7 @@ def _run(kind, dtype=torch.bfloat16):
     return cb, codec, rec, full, L0, steps, X
 
 
-@pytest.mark.parametrize("kind", ["keys", "values", "values2", "sq", "keys_hadamard"])
+@pytest.mark.parametrize("kind", ["keys", "values", "values2", "sq", "keys_hadamard", "values_hadamard"])
 def test_append_matches_whole_sequence_encode(kind):
     _run(kind)
 

@@ -1,7 +1,10 @@
 """Parity of the randomized Hadamard rotation mode on the GPU against the
 CPU oracle (launch post of the reference cache: its O(d log d) rotation
-mode).  The d = 128 bf16 encode of the GQA K/V codecs runs the register
-Walsh-Hadamard kernel; every other call uses the materialised Pi."""
+mode), whose Pi is the dense matrix H diag(s) / sqrt(d).  On the GPU the
+d = 128 bf16 encode of the GQA K/V codecs runs the register Walsh-Hadamard
+kernel, the query rotation of score / top-k / decode, the inverse value
+rotation of decode and the append run the wave transform; the other encodes
+use the materialised Pi."""
 import math
 import sys
 
@@ -12,7 +15,7 @@ import torch
 import kv_cache_compression_encode_amd as tq
 import synth
 from oracle import tq_oracle as o
-from tests.parity import check_encoded
+from tests.parity import check_encoded, check_scores
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -83,13 +86,59 @@ def test_encode_hadamard_dense_path(bits, mode, layout, dtype):
     say(check_encoded(codec, o.encode(codec, x.double().numpy()), o.unpack(codec, buf, n)))
 
 
-def test_decode_attend_hadamard():
-    B, Hq, Hkv, T = 2, 8, 2, 700
+@pytest.mark.parametrize("bits", [3, 4])
+def test_score_hadamard(bits):
+    # query rotation by the wave transform (prod: then the dense sketch)
+    say(f"hadamard score bits={bits}")
+    n = 3000
+    x = synth.iid_gaussian(n, 128, 41)
+    q = synth.iid_gaussian(16, 128, 42)
+    cb = tq.Codebook(128, tq.TQ_PROD, bits, rotation=HAD, seed_rotation=43, seed_sketch=44)
+    codec = o.turboquant_codec(128, bits, "prod", rot_seed=43, sketch_seed=44, rotation="hadamard")
+    ref = o.encode(codec, x.double().numpy())
+    s = tq.score(cb, q.to(DEV), up(o.pack(codec, ref)), n).cpu().numpy()
+    say("max scaled error", check_scores(s, o.score(codec, q.double().numpy(), ref), q.numpy(), ref.nx))
+    cbm = tq.Codebook(128, tq.TQ_MSE, bits, rotation=HAD, seed_rotation=43)
+    cm = o.turboquant_codec(128, bits, "mse", rot_seed=43, rotation="hadamard")
+    rm = o.encode(cm, x.double().numpy())
+    s = tq.score(cbm, q.to(DEV), up(o.pack(cm, rm)), n).cpu().numpy()
+    say("mse max scaled error", check_scores(s, o.score(cm, q.double().numpy(), rm), q.numpy(), rm.nx))
+
+
+def test_search_topk_hadamard():
+    n, d, nq, k = 20000, 128, 8, 10
+    x = synth.iid_gaussian(n, d, 45)
+    q = synth.iid_gaussian(nq, d, 46)
+    cb = tq.Codebook(d, tq.TQ_PROD, 2, rotation=HAD, seed_rotation=47, seed_sketch=48)
+    codec = o.turboquant_codec(d, 2, "prod", rot_seed=47, sketch_seed=48, rotation="hadamard")
+    ref = o.encode(codec, x.double().numpy())
+    s, i = tq.search_topk(cb, q.to(DEV), up(o.pack(codec, ref)), n, k)
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    full = o.score(codec, q.double().numpy(), ref)
+    rs, ri = o.topk(full, k)
+    for r in range(nq):
+        tol = 1e-3 * np.linalg.norm(q[r].numpy()) * ref.nx.astype(np.float64)
+        kth = rs[r, -1]
+        diff = set(i[r].tolist()) ^ set(ri[r].tolist())
+        assert all(abs(full[r, j] - kth) <= 2 * tol[j] for j in diff), f"query {r}: top-k differs beyond near-ties"
+        assert np.all(np.abs(s[r] - full[r, i[r]]) <= tol[i[r]])
+
+
+@pytest.mark.parametrize("T,key_bits", [(700, 3), (300, 3), (700, 4)])
+def test_decode_attend_hadamard(T, key_bits):
+    # T = 700: several splits, merged by the combine kernel (inverse value
+    # rotation there); T = 300: one split, rotated back inside the MFMA
+    # kernel; 4-bit keys: the generic kernel after the query-prep kernel
+    say(f"hadamard decode T={T} key bits={key_bits}")
+    B, Hq, Hkv = 2, 8, 2
     law = synth.KVLaw(Hkv, 128, 225)
     K = synth.kv_cache(B, Hkv, T, 128, 221, law)
     V = synth.kv_cache(B, Hkv, T, 128, 271, law)
     q = synth.kv_queries(B, Hq, Hkv, 128, 222, law)
     kcb, vcb, kc, vc = _codecs(223, 224)
+    if key_bits != 3:
+        kcb = tq.Codebook(128, tq.TQ_PROD, key_bits, rotation=HAD, seed_rotation=223, seed_sketch=224)
+        kc = o.turboquant_codec(128, key_bits, "prod", rot_seed=223, sketch_seed=224, rotation="hadamard")
     ke = [[o.encode(kc, K[b, g].double().numpy()) for g in range(Hkv)] for b in range(B)]
     ve = [[o.encode(vc, V[b, g].double().numpy()) for g in range(Hkv)] for b in range(B)]
     kbuf = np.concatenate([o.pack(kc, e) for row in ke for e in row])

@@ -184,6 +184,13 @@ def test_argument_errors_before_launch():
     assert lib.tq_workspace_size(cb.handle, L.TQ_OP_SCORE, 4, 100, 0) >= 4 * 256 * 4
     assert lib.tq_codebook_free(None) == L.TQ_EINVAL
     assert lib.tq_status_string(L.TQ_EWORKSPACE) == b"workspace too small"
+    # device calibration needs a device: refused before any device call
+    desc = L.CodebookDesc()
+    desc.d, desc.mode, desc.bits, desc.qjl_dims = 128, tq.TQ_PROD, 3, 4
+    desc.rotation, desc.num_heads, desc.calib_on_device = tq.TQ_ROT_CALIBRATE, 1, 1
+    desc.calib, desc.calib_n, desc.calib_dtype, desc.device = ctypes.addressof(buf), 8, L.TQ_F32, -1
+    h = ctypes.c_void_p()
+    assert lib.tq_codebook_build(ctypes.byref(desc), ctypes.byref(h)) == L.TQ_EINVAL and not h.value
 
 
 @pytest.mark.parametrize("mode,bits,heads", [("prod", (3, 2), 1), ("prod", (3, 2), 2), ("mse", (3, 2), 1),
