@@ -109,10 +109,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   constexpr bool SPL = UB == 3;  // outlier-channel split keys, 32 outlier coordinates
   __shared__ float sqr[4][D];
   __shared__ float sqs[4][D];
-  __shared__ float slow[SQ ? 4 : 1][4][kMaxLevels];  // SQ: q'_i c_i(idx), dims 0..3
+  // SQ, per query: [i][idx] = q'_i c_i(idx) for dims i = 0..3, and [4][s] =
+  // sum_i (+-qs_i) over the 4 QJL sign bits s (bit set: +)
+  __shared__ float sqtab[SQ ? 4 : 1][5][64];
   __shared__ float smu[4];
   __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
-  __shared__ uint32_t stail[SQ ? 256 : 1];  // SQ: tail byte -> index bits 1.. of dims 0..3 (5 bits each)
+  // SQ: tail byte -> byte i = 4 x (index bits 1.. of dim i), i = 0..3: with
+  // the low bits added, byte i is the byte offset of dim i's table entry
+  __shared__ uint32_t stail[SQ ? 256 : 1];
   __shared__ float skc[SQ ? 4 : 1][kMaxLevels];  // SQ: levels of dims 0..3
   // value byte (two 4-bit codes) -> fp16 pair of their levels, 32 copies:
   // entry e for lane l at slut[e * 32 + l % 32], so that the random lookups
@@ -240,7 +244,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   }
   for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
   if (SQ) {
-    stail[threadIdx.x] = kc.sq_tail[threadIdx.x];
+    {
+      const uint32_t tw = kc.sq_tail[threadIdx.x];  // dim i's bits 1.. at bits 5i .. 5i + 4
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b |= (((tw >> (5 * i)) & 31u) << 2) << (8 * i);
+      stail[threadIdx.x] = b;
+    }
     if (threadIdx.x < D) {
       sgam[threadIdx.x] = kc.sq_gm[(size_t(hk) * 2 + 0) * D + threadIdx.x];
       smuv[threadIdx.x] = kc.sq_gm[(size_t(hk) * 2 + 1) * D + threadIdx.x];
@@ -308,7 +318,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   if (SQ) {
     for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
       const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
-      slow[gg][i][l] = sqr[gg][i] * skc[i][l];
+      sqtab[gg][i][l] = sqr[gg][i] * skc[i][l];
+    }
+    if (threadIdx.x < 64) {
+      const int gg = threadIdx.x >> 4, sb = threadIdx.x & 15;
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v += ((sb >> i) & 1) ? sqs[gg][i] : -sqs[gg][i];
+      sqtab[gg][4][sb] = v;
     }
     {  // wave w: sum_{i >= 4} mu_i q'_i of query w
       float v = 0.f;
@@ -392,11 +409,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   const float coef_scale_o = kQjl / 32.f;
   // SQ: the query whose table part this lane forms (see the score step)
   const int q_own = ((g16 & 1) << 1) | (g16 >> 1);
-  const float* slow_own = &slow[SQ ? q_own : 0][0][0];
+  // byte offset of this query's tables in sqtab (a multiple of 256, so a
+  // table byte offset below 256 is ORed in)
+  const uint32_t qtab = SQ ? uint32_t(q_own) * (5 * 64 * 4) : 0u;
+  const char* sqtab_b = reinterpret_cast<const char*>(&sqtab[0][0][0]);
   const float smu_own = SQ ? smu[q_own] : 0.f;
-  float sqs_own[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) sqs_own[i] = SQ ? sqs[q_own][i] : 0.f;
 
   // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
@@ -432,10 +449,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       vw[2 * j + 1][1] = t[3];
     }
     float nx[4], nr[4], nv[4], nxo[4], nro[4];
-    uint32_t sqb[4];  // SQ: plane-0 byte 0 | tail byte << 8 | sign byte << 16
+    // SQ, per token before the exchange (once per token instead of once per
+    // token and query): the byte offsets 4 idx_i of dims 0..3 in their tables
+    // (low index bits = plane-0 bits 0..3, spread to bit 2 of each byte), and
+    // the sign-table offset 4 s in byte 2 of the n_v word
+    uint32_t sqb[4], nvb[4];
     const uint32_t kpack = R.nx | (R.nr << 16);
     const uint32_t opack = SPL ? (R.xo | (R.ro << 16)) : 0u;
-    const uint32_t spack = SQ ? ((R.kw4[0][0] & 0xffu) | (R.tl << 8) | (R.sg << 16)) : 0u;
+    const uint32_t spack = SQ ? ((((R.kw4[0][0] & 0xfu) * 0x810204u) & 0x04040404u) | stail[R.tl]) : 0u;
+    const uint32_t nvpack = SQ ? (R.nv | ((R.sg & 0xfu) << 18)) : R.nv;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const uint32_t kk = uint32_t(__shfl(int(kpack), 16 * nb + n, 64));
@@ -446,7 +468,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         nxo[nb] = h2f(uint16_t(ko & 0xffffu));
         nro[nb] = h2f(uint16_t(ko >> 16));
       }
-      nv[nb] = h2f(uint16_t(__shfl(int(R.nv), 16 * nb + n, 64)));
+      nvb[nb] = uint32_t(__shfl(int(nvpack), 16 * nb + n, 64));
+      nv[nb] = h2f(uint16_t(nvb[nb] & 0xffffu));
       sqb[nb] = SQ ? uint32_t(__shfl(int(spack), 16 * nb + n, 64)) : 0u;
     }
     // value B fragments: table lookups issued before the score step
@@ -512,15 +535,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         // per lane (q_own), the partner query's part from the lane 32 away:
         // lanes (n, 0) / (n, 2) take queries 0 / 1, lanes (n, 1) / (n, 3) 2 / 3
         const uint32_t w = sqb[nb];
-        const uint32_t tl = stail[(w >> 8) & 0xffu];
         float e = smu_own;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t idx = ((w >> i) & 1u) | ((tl >> (5 * i)) & 31u);
-          e += slow_own[i * kMaxLevels + idx];
-          const float sg = (w >> (16 + i)) & 1u ? sqs_own[i] : -sqs_own[i];
-          e = fmaf(coef, sg, e);
-        }
+        for (int i = 0; i < 4; ++i)
+          e += *reinterpret_cast<const float*>(sqtab_b + 256 * i + (qtab | ((w >> (8 * i)) & 0xffu)));
+        e = fmaf(coef, *reinterpret_cast<const float*>(sqtab_b + 1024 + (qtab | ((nvb[nb] >> 16) & 0xffu))), e);
         ta = e;
         tb = xor32(e, lane);
         if (g16 >= 2) { const float t = ta; ta = tb; tb = t; }
@@ -539,10 +558,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       mt = grp_max<G>(mt);
       const float mnew = fmaxf(mrun[k], mt);
       alpha[k] = mrun[k] == -INFINITY ? 0.f : __expf(mrun[k] - mnew);
+      // no token yet (mnew = -inf): every lg is -inf and exp(lg - 0) = 0
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
       float ps = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const float p = mnew == -INFINITY ? 0.f : __expf(lg[nb][k] - mnew);
+        const float p = __expf(lg[nb][k] - msafe);
         ps += p;
         const int q = 2 * g16 + k;
         if (g16 < 2 && q < G) sP[wave][q][16 * nb + n] = uint16_t(f16b(p * nv[nb]));
@@ -559,17 +580,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2)
       Ap[kc2] = *reinterpret_cast<const u32x4*>(&sP[wave][n][32 * kc2 + 8 * g16]);
+    // the accumulators are rescaled only when some query's running maximum
+    // moved (a factor of exactly 1 elsewhere), which after the first tiles
+    // is the exception
+    if (__ballot(al01 != 1.f || al11 != 1.f) != 0) {
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb) {
-      accv[vb][0] *= al01;
-      accv[vb][1] *= al11;
-      accv[vb][2] *= al2;
-      accv[vb][3] *= al3;
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        accv[vb] = mfma16(Ap[kc2], Bv[vb][kc2], accv[vb]);
+      for (int vb = 0; vb < 8; ++vb) {
+        accv[vb][0] *= al01;
+        accv[vb][1] *= al11;
+        accv[vb][2] *= al2;
+        accv[vb][3] *= al3;
       }
     }
+    // the two k-halves as two rounds over the 8 accumulators, so that
+    // consecutive MFMAs are independent
+#pragma unroll
+    for (int kc2 = 0; kc2 < 2; ++kc2)
+#pragma unroll
+      for (int vb = 0; vb < 8; ++vb) accv[vb] = mfma16(Ap[kc2], Bv[vb][kc2], accv[vb]);
     __builtin_amdgcn_wave_barrier();
   };
   // the prefetches are unconditional (clamped to the last tile, a harmless
