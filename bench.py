@@ -572,7 +572,8 @@ def run_search(args, torch, tq, synth):
     return res, lambda: cpu_baseline_search(args.bits)
 
 
-DEFAULT_STEPS = {"gqa_layer": (50, 5), "gqa_outlier": (50, 5), "small": (200, 10), "bulk_prefill": (10, 2), "sq_decode": (50, 5),
+DEFAULT_STEPS = {"gqa_layer": (200, 20), "gqa_outlier": (200, 20), "small": (200, 10), "bulk_prefill": (10, 2),
+                 "sq_decode": (200, 20),
                  "vector_search": (3, 1)}
 
 

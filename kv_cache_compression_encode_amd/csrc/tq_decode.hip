@@ -110,8 +110,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __shared__ float sqr[4][D];
   __shared__ float sqs[4][D];
   // SQ, per query: [i][idx] = q'_i c_i(idx) for dims i = 0..3, and [4][s] =
-  // sum_i (+-qs_i) over the 4 QJL sign bits s (bit set: +)
-  __shared__ float sqtab[SQ ? 4 : 1][5][64];
+  // sum_i (+-qs_i) over the 4 QJL sign bits s (bit set: +).  Query q's tables
+  // start at 336 q words: queries 0 and 2 (1 and 3), whose lanes read in the
+  // same LDS cycle, then sit 32 banks apart
+  constexpr int kSqtab = 336;
+  __shared__ float sqtab[SQ ? 4 * kSqtab : 1];
   __shared__ float smu[4];
   __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   // SQ: tail byte -> byte i = 4 x (index bits 1.. of dim i), i = 0..3: with
@@ -318,14 +321,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   if (SQ) {
     for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
       const int gg = e / (4 * kMaxLevels), i = (e / kMaxLevels) % 4, l = e % kMaxLevels;
-      sqtab[gg][i][l] = sqr[gg][i] * skc[i][l];
+      sqtab[gg * kSqtab + i * 64 + l] = sqr[gg][i] * skc[i][l];
     }
     if (threadIdx.x < 64) {
       const int gg = threadIdx.x >> 4, sb = threadIdx.x & 15;
       float v = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v += ((sb >> i) & 1) ? sqs[gg][i] : -sqs[gg][i];
-      sqtab[gg][4][sb] = v;
+      sqtab[gg * kSqtab + 4 * 64 + sb] = v;
     }
     {  // wave w: sum_{i >= 4} mu_i q'_i of query w
       float v = 0.f;
@@ -409,10 +412,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   const float coef_scale_o = kQjl / 32.f;
   // SQ: the query whose table part this lane forms (see the score step)
   const int q_own = ((g16 & 1) << 1) | (g16 >> 1);
-  // byte offset of this query's tables in sqtab (a multiple of 256, so a
-  // table byte offset below 256 is ORed in)
-  const uint32_t qtab = SQ ? uint32_t(q_own) * (5 * 64 * 4) : 0u;
-  const char* sqtab_b = reinterpret_cast<const char*>(&sqtab[0][0][0]);
+  // byte offset of this query's tables in sqtab
+  const uint32_t qtab = SQ ? uint32_t(q_own) * (kSqtab * 4) : 0u;
+  const char* sqtab_b = reinterpret_cast<const char*>(&sqtab[0]);
   const float smu_own = SQ ? smu[q_own] : 0.f;
 
   // running softmax state of the 2 queries handled by this lane's group (groups 0, 1)
@@ -538,8 +540,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         float e = smu_own;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          e += *reinterpret_cast<const float*>(sqtab_b + 256 * i + (qtab | ((w >> (8 * i)) & 0xffu)));
-        e = fmaf(coef, *reinterpret_cast<const float*>(sqtab_b + 1024 + (qtab | ((nvb[nb] >> 16) & 0xffu))), e);
+          e += *reinterpret_cast<const float*>(sqtab_b + 256 * i + (qtab + ((w >> (8 * i)) & 0xffu)));
+        e = fmaf(coef, *reinterpret_cast<const float*>(sqtab_b + 1024 + (qtab + ((nvb[nb] >> 16) & 0xffu))), e);
         ta = e;
         tb = xor32(e, lane);
         if (g16 >= 2) { const float t = ta; ta = tb; tb = t; }
