@@ -338,15 +338,18 @@ __device__ __forceinline__ uint32_t group_or(uint32_t w) {
   return w;
 }
 
-template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, bool SPLIT = false>
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
 __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
   // MODE: 0 mse, 1 prod with a full 128-dim MFMA sketch, 2 prod with a small
   // (m <= 4) sketch on rotated dims 0..m-1 (SpectralQuant selective QJL).
-  // SPLIT: outlier-channel split codec in stored order with 32 outlier
-  // coordinates (half 0, registers 0..7 of every 32-dim block) at 2 index
-  // bits and 96 regular ones at 1 bit; each group is normalised by its own
-  // norm, summed over its channels (the head's channel mask) as the rows
-  // are loaded.
+  // SPLIT: outlier-channel split codec in stored order, each group
+  // normalised by its own norm, summed over its channels (the head's channel
+  // mask) as the rows are loaded.  SPLIT 1: 32 outlier coordinates (half 0,
+  // registers 0..7 of every 32-dim block) at 2 index bits and 96 regular ones
+  // at 1 bit, with symmetric searches and plane words; SPLIT 2: any outlier
+  // count o (o / 4 = o4 leading coordinates of every 32-dim block) and index
+  // bits, per-dim binary searches against the group codebooks in LDS, the
+  // bits written plane by plane as byte runs of the row bit string.
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* sPiHi = reinterpret_cast<uint16_t*>(smem);
   uint16_t* sPiLo = sPiHi + D * LDS_ROW;
@@ -418,7 +421,11 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // 64 hh ..); read here, per tile, so that they stay in registers
       float spl_t2 = 0.f, spl_c2 = 0.f, spl_c3 = 0.f, spl_c1 = 0.f, spl_lo = 0.f, spl_hi = 0.f;
       uint32_t om[2] = {0u, 0u};
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT != 0) {
+        om[0] = cv.omask[hc * 4 + 2 * hh];
+        om[1] = cv.omask[hc * 4 + 2 * hh + 1];
+      }
+      if constexpr (SPLIT == 1) {
         const float* th = cv.thr + size_t(hc) * D * kMaxLevels;
         const float* ce = cv.cen + size_t(hc) * D * kMaxLevels;
         spl_t2 = th[2];
@@ -427,8 +434,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         spl_c1 = 32.f * ce[8 * kMaxLevels + 1];
         spl_lo = hh ? spl_c1 : spl_c2;  // level magnitude below / above t_2
         spl_hi = hh ? spl_c1 : spl_c3;  // (half 1: the regular level)
-        om[0] = cv.omask[hc * 4 + 2 * hh];
-        om[1] = cv.omask[hc * 4 + 2 * hh + 1];
       }
       bool valid[NB];
 #pragma unroll
@@ -625,6 +630,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       }
 
       uint32_t cw[NB][NPL];      // code bits of the current 32-dim block (this half's 16), plane p
+      uint32_t gw[NB][SPLIT == 2 ? kMaxBits : 1];  // SPLIT 2: plane p bits of this half's 16 coordinates
       uint32_t tailw[NB];        // non-uniform row layout: bits beyond plane 0
       uint32_t sw[NB][4];        // sign bits (row layout), this half's 16 per word
       float rr[NB];
@@ -643,14 +649,16 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       float rsmall[NB][4];
       // SPLIT: per group the factor between the accumulator and the unit
       // vector (16 2^e times the group's norm; a zero group encodes y = 0)
-      float nxo[NB], rso[NB], rsr[NB], rro[NB], P2o[NB];
+      float nxo[NB], rso[NB], rsr[NB], rro[NB], P2o[NB], wso_[NB], wsr_[NB];
       uint32_t p1w[NB];
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT != 0) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           nxo[nb] = sqrtf(so2[nb]) / nd[nb];
           const float wso = wsc[nb] * (nxo[nb] > 0.f ? nxo[nb] : 1.f);
           const float wsr = wsc[nb] * (nxv[nb] > 0.f ? nxv[nb] : 1.f);
+          wso_[nb] = wso;
+          wsr_[nb] = wsr;
           rso[nb] = 32.f / wso;
           rsr[nb] = 32.f / wsr;
           P2o[nb] = hh ? -INFINITY : spl_t2 * wso;  // half 1 holds no outliers
@@ -665,6 +673,11 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int p = 0; p < NPL; ++p) cw[nb][p] = 0;
+        if constexpr (SPLIT == 2)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int p = 0; p < kMaxBits; ++p) gw[nb][p] = 0;
         // ------------------------------------------------ rotation block
         // one accumulation chain per 32-vector block: Pi_hi x_hi, Pi_lo x_hi
         // (and Pi_hi x_lo for fp32 input); register r of half hh holds
@@ -704,7 +717,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             const float v = acc[nb][r];
             int idx = 0;
             float chat = 0.f;
-            if constexpr (SPLIT) {
+            if constexpr (SPLIT == 1) {
               // registers 0..7 of half 0: outlier, 2 index bits (symmetric
               // 4-level search: bit 1 = [v >= 0], bit 0 = [v >= 0] == [|v| >= t_2]);
               // all others: regular, 1 bit = [v >= 0] (2 symmetric levels).
@@ -725,6 +738,17 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 cw[nb][0] = __builtin_amdgcn_alignbit(cw[nb][0], vb, 31);
                 chat = __uint_as_float(__float_as_uint(spl_c1) | (vb & 0x80000000u));
               }
+            } else if constexpr (SPLIT == 2) {
+              // the coordinate's group codebook (boundaries +inf past its
+              // levels), against the group's scale: idx = #{t_k <= y}
+              const bool og = 16 * hh + r < cv.o4;
+              const float wg = og ? wso_[nb] : wsr_[nb];
+              const float* Tt = sThr + dim * kMaxLevels;
+              int k = 0;
+#pragma unroll
+              for (int st = 16; st >= 1; st >>= 1) k += v >= Tt[k + st - 1] * wg ? st : 0;
+              idx = k;
+              chat = 32.f * sCen[dim * kMaxLevels + k];
             } else if (UNIFORM && !COL) {
               // row layout: the index bits go straight into the plane words
               if constexpr (SYM2) {
@@ -791,6 +815,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                     tailw[nb] |= bit << (pos >= 0 ? pos - D : 0);
                   }
                 }
+              } else if constexpr (SPLIT == 2) {
+#pragma unroll
+                for (int p = 0; p < kMaxBits; ++p) gw[nb][p] |= uint32_t((idx >> p) & 1) << r;
               } else if (!UNIFORM && !SPLIT) {
                 cw[nb][0] |= uint32_t(idx & 1) << r;
                 for (int p = 1; p < kMaxBits; ++p) {
@@ -816,9 +843,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               if ((r % VPD) == (j & (VPD - 1))) colkeep[nb][r / VPD] = w;
             }
             if (MODE == 1 && SPLIT) {
-              const bool og = r < 8 && !hh;
+              const bool og = SPLIT == 1 ? (r < 8 && !hh) : (16 * hh + r < cv.o4);
               const float rsd = fmaf(v, og ? rso[nb] : rsr[nb], -chat);  // 32 (y - c), own group's unit
-              if (r < 8) {
+              if (SPLIT == 2 || r < 8) {
                 rro[nb] = fmaf(rsd, og ? rsd : 0.f, rro[nb]);
                 rr[nb] = fmaf(rsd, og ? 0.f : rsd, rr[nb]);
               } else {
@@ -838,7 +865,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             }
           }
           if constexpr (SYM2) sym2_finish(cw[nb][0], cw[nb][NPL - 1], 0xffffu);
-          if constexpr (SPLIT) cw[nb][0] ^= 0xffffu;  // complemented pushes
+          if constexpr (SPLIT == 1) cw[nb][0] ^= 0xffffu;  // complemented pushes
+          if constexpr (SPLIT == 2) cw[nb][0] = gw[nb][0];  // plane 0: every coordinate
           if (!COL) {
             // row layout: half hh holds bits 16 hh .. 16 hh + 15 of each word;
             // slots past the end of the input are zero
@@ -850,6 +878,33 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               // both halves hold the same word: an unconditional store keeps
               // the number of memory operations the same on every path
               *reinterpret_cast<uint32_t*>(trec + size_t(p) * kTile * 16 + slot * 16 + 4 * mb) = w;
+            }
+            if constexpr (SPLIT == 2) {
+              // planes 1..: plane p holds the coordinates with more than p
+              // index bits in stored order (both groups, or one), so block
+              // mb's bits are one run of n_p in {32, o4, 32 - o4} bits at
+              // base_p + n_p mb, byte-aligned; the bit string is stored in
+              // 16-byte chunks of 64 vectors (a shorter last chunk)
+              const int o4 = cv.o4;
+              int base = 4 * 32;
+              for (int p = 1; p < kMaxBits; ++p) {
+                const bool co = p < cv.split_ub_o, cr = p < cv.split_ub_r;
+                if (!co && !cr) break;
+                const int np = (co ? o4 : 0) + (cr ? 32 - o4 : 0);
+                const uint32_t mine = valid[nb] ? gw[nb][p] << (16 * hh) : 0u;
+                uint32_t w = mine | xor32(mine);
+                if (!co) w >>= o4;
+                else if (!cr) w &= (1u << o4) - 1u;
+                const int start = (base + np * mb) >> 3;  // first byte of the run
+                if (hh == 0) {
+                  for (int bt = 0; bt < np / 8; ++bt) {
+                    const int B = start + bt, c = B >> 4;
+                    const int wc = min(16, cv.code_bytes - 16 * c);
+                    trec[size_t(c) * kTile * 16 + size_t(slot) * wc + (B & 15)] = uint8_t(w >> (8 * bt));
+                  }
+                }
+                base += 4 * np;
+              }
             }
           }
           if (SYM4) {
@@ -951,14 +1006,14 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               sw[nb][q] = mine | xor32(mine);
             }
           }
-          if constexpr (SPLIT) {
+          if constexpr (SPLIT == 1) {
             // plane 1 (4 bytes per vector, [64][4] at 64 * 16): bit 8 mb + r =
             // bit 1 of outlier coordinate 8 mb + r; block mb's pushes sit in
             // byte 3 - mb, hence the byte swap
             const uint32_t mine = hh ? 0u : __builtin_bswap32(~p1w[nb]);  // complemented pushes
             const uint32_t w = valid[nb] ? (mine | xor32(mine)) : 0u;
             *reinterpret_cast<uint32_t*>(trec + size_t(kTile) * 16 + size_t(slot) * 4) = w;
-          } else if (!UNIFORM) {
+          } else if (!UNIFORM && !SPLIT) {
             const int tb = cv.code_bytes - 16;  // tail bytes per vector (1..4)
             for (int k = 0; k < tb; ++k)
               trec[size_t(kTile) * 16 + size_t(slot) * tb + k] = uint8_t(tailw[nb] >> (8 * k));
@@ -1016,7 +1071,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
     __builtin_amdgcn_sched_barrier(0);
     stage_store<NM>(dst, perm, sv);
   }
-  if (!UNIFORM && !SPLIT) {
+  if (!UNIFORM && SPLIT != 1) {
     for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
       sThr[e] = cv.thr[size_t(hc) * D * kMaxLevels + e];
       sCen[e] = cv.cen[size_t(hc) * D * kMaxLevels + e];
@@ -1344,12 +1399,12 @@ hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, bool SPLIT = false>
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
 hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB, SPLIT>;
   size_t lds = size_t(2) * D * LDS_ROW * 2;
   if (MODE == 1) lds += size_t(D) * LDS_ROW * 2;
-  if (!UNIFORM && !SPLIT) lds += size_t(2) * D * kMaxLevels * 4;
+  if (!UNIFORM && SPLIT != 1) lds += size_t(2) * D * kMaxLevels * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (e != hipSuccess) return e;
@@ -1379,17 +1434,25 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
     if (cv.mode == TQ_PROD && !col && cv.m == D && cv.ubits == 2) return launch_had<1, false, 2>(cv, a, s);
   }
   if (cv.outl) {
-    // outlier-channel split: 32 outlier coordinates at 2 index bits, the
-    // others at 1 (the 2.5-bit KV setting), row layout, full block sketch
-    if (col || cv.o4 != 8 || cv.split_ub_o != 2 || cv.split_ub_r != 1 || !cv.omask)
-      return hipErrorNotSupported;
+    // outlier-channel split, row layout, full block sketch: the 2.5-bit KV
+    // setting (32 outlier coordinates at 2 index bits, the others at 1) on
+    // its specialised path, any other outlier count and bits on the general
+    // one
+    if (col || !cv.omask) return hipErrorNotSupported;
+    const bool fast = cv.o4 == 8 && cv.split_ub_o == 2 && cv.split_ub_r == 1;
     if (cv.mode == TQ_PROD) {
       if (cv.m != D) return hipErrorNotSupported;
-      return a.x_bf16 ? launch_one<1, true, 1, false, false, 1, true>(cv, a, s)
-                      : launch_one<1, false, 1, false, false, 1, true>(cv, a, s);
+      if (fast)
+        return a.x_bf16 ? launch_one<1, true, 1, false, false, 1, 1>(cv, a, s)
+                        : launch_one<1, false, 1, false, false, 1, 1>(cv, a, s);
+      return a.x_bf16 ? launch_one<1, true, 1, false, false, 1, 2>(cv, a, s)
+                      : launch_one<1, false, 1, false, false, 1, 2>(cv, a, s);
     }
-    return a.x_bf16 ? launch_one<1, true, 0, false, false, 1, true>(cv, a, s)
-                    : launch_one<1, false, 0, false, false, 1, true>(cv, a, s);
+    if (fast)
+      return a.x_bf16 ? launch_one<1, true, 0, false, false, 1, 1>(cv, a, s)
+                      : launch_one<1, false, 0, false, false, 1, 1>(cv, a, s);
+    return a.x_bf16 ? launch_one<1, true, 0, false, false, 1, 2>(cv, a, s)
+                    : launch_one<1, false, 0, false, false, 1, 2>(cv, a, s);
   }
   if (!cv.uniform) {
     // SpectralQuant keys: row layout, small sketch

@@ -93,11 +93,28 @@ def test_split_encode_zero_groups():
     assert s[0, 7] == 0.0
 
 
-def test_split_encode_unsupported_bits():
-    ch = np.arange(32, dtype=np.int32)[None]
-    cb, _ = codecs(ch, bits=(4, 3))
-    with pytest.raises(tq.TQError):
-        tq.encode(cb, torch.zeros(64, 128, device=DEV))
+@pytest.mark.parametrize("o_,bits,mode,dtype", [(32, (4, 3), "prod", torch.bfloat16),
+                                                 (64, (3, 2), "prod", torch.float32),
+                                                 (96, (2, 3), "prod", torch.bfloat16),
+                                                 (32, (6, 2), "prod", torch.bfloat16),
+                                                 (64, (3, 2), "mse", torch.bfloat16),
+                                                 (96, (4, 1), "mse", torch.float32)])
+def test_split_encode_general(o_, bits, mode, dtype):
+    # outlier counts and bit widths off the 2.5-bit path (up to 5 index bits,
+    # bit strings over several 16-byte chunks, a short last chunk)
+    H, T = 2, 700
+    say(f"general split encode o={o_} bits={bits} {mode} {dtype}")
+    law = synth.KVLaw(H, 128, 925)
+    X = synth.kv_cache(1, H, T, 128, 921, law)[0].to(dtype)
+    ch = outlier_channels(law, H, o_=o_)
+    cb, sc = codecs(ch, bits=bits, mode=mode)
+    buf = tq.encode(cb, X.to(DEV)).cpu().numpy()
+    per = cb.records_bytes(T)
+    for h in range(H):
+        ref = o.split_encode(sc, X[h].double().numpy(), head=h)
+        got = o.split_unpack(sc, buf[h * per:(h + 1) * per], T)
+        say(h, check_split(sc, ref, got))
+        assert np.array_equal(o.split_pack(sc, got), buf[h * per:(h + 1) * per])
 
 
 @pytest.mark.parametrize("bits", [(3, 2), (4, 3), (2, 3)])
