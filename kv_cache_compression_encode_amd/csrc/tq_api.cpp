@@ -863,7 +863,7 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
   if (batch == 0 || heads == 0 || tokens == 0) return TQ_OK;  // nothing to encode
   if (!x || !records) return TQ_EINVAL;
   if (xs_b < 0 || xs_h < 0 || xs_t < cb->desc.d) return TQ_EINVAL;
-  if (batch * heads > 65535) return TQ_EUNSUPPORTED;
+  if (batch * heads > int64_t(65535) * 65535) return TQ_EUNSUPPORTED;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->info.num_heads > 1 && heads != cb->info.num_heads) return TQ_EINVAL;
   const int d = cb->desc.d;

@@ -358,7 +358,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                                                    : (uint8_t*)sSk);
   float* sCen = sThr + D * kMaxLevels;
 
-  const int64_t bh = blockIdx.y;
+  // (sequence, head) set: grid y, continued in grid z past 65535 sets
+  const int64_t bh = blockIdx.y + int64_t(blockIdx.z) * gridDim.y;
+  if (bh >= a.batch * a.heads) return;
   const int64_t b = bh / a.heads, h = bh % a.heads;
   const int hc = cv.heads > 1 ? int(h) : 0;
 
@@ -1169,7 +1171,8 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* sMask = reinterpret_cast<uint32_t*>(smem);           // [2][32] sign-bit masks
   uint16_t* sSk = reinterpret_cast<uint16_t*>(smem + 256);        // MODE 1: staged S
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = blockIdx.y + int64_t(blockIdx.z) * gridDim.y;
+  if (bh >= a.batch * a.heads) return;
   const int64_t b = bh / a.heads, h = bh % a.heads;
   if (threadIdx.x < 64) sMask[threadIdx.x] = cv.had_mask[threadIdx.x];
   if (MODE == 1) stage_sketch_had(sSk, cv.sk_hi);
@@ -1379,6 +1382,13 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
   }
 }
 
+// Grid of gx workgroups per (sequence, head) set: the sets run along y and,
+// past 65535, along z (the kernels skip the padding of the last z plane).
+dim3 set_grid(int64_t gx, int64_t sets) {
+  const int64_t sy = std::min<int64_t>(sets, 65535);
+  return dim3(unsigned(gx), unsigned(sy), unsigned((sets + sy - 1) / sy));
+}
+
 template <int MODE, bool COL, int UB>
 hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   auto kern = encode_had_kernel<MODE, COL, UB>;
@@ -1395,7 +1405,7 @@ hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   int64_t gx = (ntiles + 7) / 8;
   const int64_t want = std::max<int64_t>(1, (int64_t(cus) + sets - 1) / sets);
   gx = std::max<int64_t>(1, std::min(gx, want));
-  hipLaunchKernelGGL(kern, dim3(unsigned(gx), unsigned(sets), 1u), dim3(512), lds, s, cv, a);
+  hipLaunchKernelGGL(kern, set_grid(gx, sets), dim3(512), lds, s, cv, a);
   return hipGetLastError();
 }
 
@@ -1418,8 +1428,7 @@ hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   int64_t gx = (ntiles + 7) / 8;
   const int64_t want = std::max<int64_t>(1, (int64_t(cus) + sets - 1) / sets);
   gx = std::max<int64_t>(1, std::min(gx, want));
-  const dim3 grid{unsigned(gx), unsigned(sets), 1u};
-  hipLaunchKernelGGL(kern, grid, dim3(512), lds, s, cv, a);
+  hipLaunchKernelGGL(kern, set_grid(gx, sets), dim3(512), lds, s, cv, a);
   return hipGetLastError();
 }
 

@@ -31,6 +31,25 @@ def gpu_records(cb, x, **kw):
     return rec.cpu().numpy()
 
 
+def test_encode_many_sets():
+    # 2 x 32800 (sequence, head) sets of one token: more than 65535 sets, so
+    # the grid continues along z; sampled sets against the oracle
+    B, H = 2, 32800
+    say(f"encode {B} x {H} sets of one token")
+    x = synth.iid_gaussian(B * H, 128, 31).reshape(B, H, 1, 128).to(torch.bfloat16)
+    cb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=33, seed_sketch=34)
+    codec = o.turboquant_codec(128, 3, "prod", rot_seed=33, sketch_seed=34)
+    buf = gpu_records(cb, x)
+    per = cb.records_bytes(1)
+    assert buf.shape[0] == B * H * per
+    for bh in (0, 1, 65534, 65535, 65536, B * H - 1):
+        b, h = divmod(bh, H)
+        ref = o.encode(codec, x[b, h].double().numpy())
+        got = o.unpack(codec, buf[bh * per:(bh + 1) * per], 1)
+        check_encoded(codec, ref, got)
+        assert np.array_equal(o.pack(codec, got), buf[bh * per:(bh + 1) * per])
+
+
 # ------------------------------------------------ plain TurboQuant-prod, d=128
 @pytest.mark.parametrize("n", [4096, 1, 63, 65, 1000])
 def test_encode_prod_fp32_d128(n):
