@@ -227,7 +227,7 @@ def cpu_baseline_search(bits):
 
     def run():
         o.topk(o.score(c, q, o.encode(c, x)), 10)
-    reps, el = _time_loop(run, max_reps=20)
+    reps, el = _time_loop(run)
     return {"value": reps * n * nq / el, "unit": "query-key pairs/s (incl. encode)", "cores": _cores(),
             "kind": "oracle",
             "sample": f"{n} database vectors x {nq} queries: encode, score, top-10; {reps} reps in {el:.1f} s"}
