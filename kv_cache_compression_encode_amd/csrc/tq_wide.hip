@@ -667,28 +667,41 @@ struct KeyTables {
   u32x2 cen[NC];
 };
 
-// NV: 32-key blocks per wave (the workgroup takes 128 NV keys at a time)
-template <int UB, bool PROD, bool DENSE, int KM, int NV>  // KM: list slots (k <= KM)
-__global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
+// NV: 32-key blocks per wave (the workgroup takes 128 NV keys at a time).
+// QW: waves per key block.  QW = 1: 4 waves, each computing all 128 queries
+// of the block for its keys (one wave per SIMD: 4 x NV accumulator blocks and
+// two top-k lists per lane); QW = 2: 8 waves, wave w computing queries
+// 64 (w / 4) .. + 63 for the keys of sub-block w % 4, so that two waves share
+// each SIMD (2 x NV accumulator blocks, one list per lane) at the price of
+// reading each key operand twice.
+template <int UB, bool PROD, bool DENSE, int KM, int NV, int QW>  // KM: list slots (k <= KM)
+__global__ __launch_bounds__(NT * QW, 1) void search_kernel(SearchArgs a) {
+  constexpr int NTS = NT * QW;  // threads
+  constexpr int CQ = 4 / QW;    // 32-query row blocks per wave
+  constexpr int NL = CQ / 2;    // top-k lists per lane (64 queries each)
   constexpr int TP = 33;        // pitch of the transposition buffer (floats)
   constexpr int SP = SK + 8;    // LDS pitch of a query row (halves): 272 bytes, conflict-free 16-byte reads
   __shared__ __align__(16) uint16_t sA[2][AR * SP];
   __shared__ __align__(16) KeyTables<UB> tb;
   __shared__ float sinv[AR];
-  __shared__ float sT[DENSE ? 1 : 4][DENSE ? 1 : 64 * TP];
+  __shared__ float sT[DENSE ? 1 : 4 * QW][DENSE ? 1 : 64 * TP];
   const int qb = blockIdx.x % a.nqb, split = blockIdx.x / a.nqb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 31, h = lane >> 5;
+  const int kw = wave & 3;                        // key sub-block of the wave
+  const int qbase = QW == 2 ? 64 * (wave >> 2) : 0;  // first query row of the wave
   const int tid = threadIdx.x;
   // tables
   {
-    const uint32_t b = uint32_t(tid);
-    u32x4 e;
+    if (tid < 256) {
+      const uint32_t b = uint32_t(tid);
+      u32x4 e;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      e[i] = ((b >> (2 * i)) & 1u ? 0x3c00u : 0xbc00u) | (((b >> (2 * i + 1)) & 1u ? 0x3c00u : 0xbc00u) << 16);
-    tb.pm[b] = e;
+      for (int i = 0; i < 4; ++i)
+        e[i] = ((b >> (2 * i)) & 1u ? 0x3c00u : 0xbc00u) | (((b >> (2 * i + 1)) & 1u ? 0x3c00u : 0xbc00u) << 16);
+      tb.pm[b] = e;
+    }
     if (UB >= 2) {
-      for (int t = tid; t < KeyTables<UB>::NC; t += NT) {
+      for (int t = tid; t < KeyTables<UB>::NC; t += NTS) {
         uint32_t hv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -707,25 +720,28 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
   const uint16_t* qt = a.qtiles + size_t(qb) * nkt * (AR * SK);
   const int64_t k0 = int64_t(split) * a.keys_per_split;
   const int64_t k1 = min(a.n, k0 + a.keys_per_split);
-  TopList<KM> L0, L1;  // lists of queries 128 qb + lane and 128 qb + 64 + lane
-  L0.init();
-  L1.init();
-  const float invA = DENSE ? 0.f : a.inv[int64_t(qb) * AR + lane];
-  const float invB = DENSE ? 0.f : a.inv[int64_t(qb) * AR + 64 + lane];
+  // list hl of a lane holds query 128 qb + qbase + 64 hl + lane
+  TopList<KM> Ls[NL];
+  float invs[NL];
+#pragma unroll
+  for (int hl = 0; hl < NL; ++hl) {
+    Ls[hl].init();
+    invs[hl] = DENSE ? 0.f : a.inv[int64_t(qb) * AR + qbase + 64 * hl + lane];
+  }
   __syncthreads();
 
-  // query tile staging: 32 KB per tile, 8 chunks of 16 bytes per thread
-  constexpr int NS = AR * SK / 8 / NT;
+  // query tile staging: 32 KB per tile, 16 bytes per chunk, NS chunks per thread
+  constexpr int NS = AR * SK / 8 / NTS;
   u32x4 stg[NS];
   auto stage_load = [&](int kt) {
     const u32x4* g = reinterpret_cast<const u32x4*>(qt + size_t(kt) * (AR * SK));
 #pragma unroll
-    for (int u = 0; u < NS; ++u) stg[u] = g[u * NT + tid];
+    for (int u = 0; u < NS; ++u) stg[u] = g[u * NTS + tid];
   };
   auto stage_store = [&](uint16_t* lds) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int e = u * NT + tid, row = e / (SK / 8), c8 = e % (SK / 8);
+      const int e = u * NTS + tid, row = e / (SK / 8), c8 = e % (SK / 8);
       *reinterpret_cast<u32x4*>(lds + row * SP + c8 * 8) = stg[u];
     }
   };
@@ -738,7 +754,7 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     int kslot[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      key[v] = kb + WK * wave + 32 * v + j;
+      key[v] = kb + WK * kw + 32 * v + j;
       kval[v] = key[v] < k1;
       const int64_t lk = kval[v] ? key[v] : k1 - 1;
       kt0[v] = a.rec + (lk / kTile) * a.tile_bytes;
@@ -763,9 +779,9 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     load_chunks(0, cw);
     stage_store(sA[0]);
     __syncthreads();
-    f32x16 acc[4][NV];
+    f32x16 acc[CQ][NV];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < CQ; ++c)
 #pragma unroll
       for (int v = 0; v < NV; ++v) acc[c][v] = f32x16{};
     // One tile of 128 reduction elements; the next tile's query rows and
@@ -780,7 +796,7 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       // 8 MFMA steps of 16: step t = (kq, s) takes elements 32 kq + 16 h + 8 s .. + 7.
       // The LDS reads of step t + 1 (query fragments, key table rows) are
       // issued before the MFMAs of step t, so their latency hides behind them.
-      auto read_step = [&](int t, u32x4 (&af)[4], u32x4 (&bf)[NV]) {
+      auto read_step = [&](int t, u32x4 (&af)[CQ], u32x4 (&bf)[NV]) {
         const int kq = t >> 1, s = t & 1;
         const int sh = 16 * h + 8 * s;
 #pragma unroll
@@ -800,12 +816,12 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
           }
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          af[c] = *reinterpret_cast<const u32x4*>(LA + (32 * c + j) * SP + 32 * kq + 16 * h + 8 * s);
+        for (int c = 0; c < CQ; ++c)
+          af[c] = *reinterpret_cast<const u32x4*>(LA + (qbase + 32 * c + j) * SP + 32 * kq + 16 * h + 8 * s);
       };
-      auto mma_step = [&](const u32x4 (&af)[4], const u32x4 (&bf)[NV]) {
+      auto mma_step = [&](const u32x4 (&af)[CQ], const u32x4 (&bf)[NV]) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < CQ; ++c)
 #pragma unroll
           for (int v = 0; v < NV; ++v) acc[c][v] = mfma(af[c], bf[v], acc[c][v]);
       };
@@ -814,13 +830,13 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       // so that they issue while the matrix core is busy.
       auto interleave = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4 * NV; ++i) {
+        for (int i = 0; i < CQ * NV; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three VALU
         }
       };
-      u32x4 afA[4], bfA[NV], afB[4], bfB[NV];
+      u32x4 afA[CQ], bfA[NV], afB[CQ], bfB[NV];
       read_step(0, afA, bfA);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -848,21 +864,21 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
       for (int v = 0; v < NV; ++v) {
         const float nr = f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nr + 2 * kslot[v]));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c][v] *= nr;
+        for (int c = 0; c < CQ; ++c) acc[c][v] *= nr;
       }
     }
     for (int kt = GS; kt < nkt; ++kt) tile(kt, std::integral_constant<bool, false>{});
-    // ---- epilogue: s = acc n_x inv_q; acc[c][v][r] is query 32 c + 8 (r / 4) + 4 h + r % 4, key v
+    // ---- epilogue: s = acc n_x inv_q; acc[c][v][r] is query qbase + 32 c + 8 (r / 4) + 4 h + r % 4, key v
     float nxv[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       nxv[v] = kval[v] ? f16f(*reinterpret_cast<const uint16_t*>(kt0[v] + a.off_nx + 2 * kslot[v])) : 0.f;
     if (DENSE) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < CQ; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qrow = 32 * c + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int qrow = qbase + 32 * c + 8 * (r >> 2) + 4 * h + (r & 3);
           const int64_t q = int64_t(qb) * AR + qrow;
           if (q >= a.nq) continue;
           const float iq = sinv[qrow];
@@ -879,10 +895,10 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     // (an integer atomic max) after each workgroup tile, so all workgroups of
     // the query block filter against it.
 #pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      TopList<KM>& Lq = hq == 0 ? L0 : L1;
-      const float iq = hq == 0 ? invA : invB;
-      int* tq = a.thr + int64_t(qb) * AR + 64 * hq + lane;
+    for (int hq = 0; hq < NL; ++hq) {
+      TopList<KM>& Lq = Ls[hq];
+      const float iq = invs[hq];
+      int* tq = a.thr + int64_t(qb) * AR + qbase + 64 * hq + lane;
       const float tg = float_of_ord(__hip_atomic_load(tq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       const float ts0 = Lq.ts;
 #pragma unroll
@@ -896,8 +912,8 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int kbase = int(kb) + WK * wave + 32 * v;  // key id of column 0 (n < 2^31)
-        const int kvalid = int(min<int64_t>(32, max<int64_t>(0, k1 - (kb + WK * wave + 32 * v))));
+        const int kbase = int(kb) + WK * kw + 32 * v;  // key id of column 0 (n < 2^31)
+        const int kvalid = int(min<int64_t>(32, max<int64_t>(0, k1 - (kb + WK * kw + 32 * v))));
         const float* row = T + lane * TP;
         uint32_t cand = 0;
 #pragma unroll
@@ -919,13 +935,13 @@ __global__ __launch_bounds__(NT, 1) void search_kernel(SearchArgs a) {
     }
   }
   if (DENSE) return;
-  // partial lists of this wave: part (split, wave) of each query
-  const int part = split * 4 + wave;
+  // partial lists of this wave: part (split, key sub-block) of each query
+  const int part = split * 4 + kw;
 #pragma unroll
-  for (int hq = 0; hq < 2; ++hq) {
-    const int64_t q = int64_t(qb) * AR + 64 * hq + lane;
+  for (int hq = 0; hq < NL; ++hq) {
+    const int64_t q = int64_t(qb) * AR + qbase + 64 * hq + lane;
     if (q >= a.nq) continue;
-    const TopList<KM>& Lq = hq == 0 ? L0 : L1;
+    const TopList<KM>& Lq = Ls[hq];
     float* ps = a.ps + (q * a.nparts + part) * a.k;
     int64_t* pi = a.pi + (q * a.nparts + part) * a.k;
 #pragma unroll
@@ -1199,12 +1215,15 @@ hipError_t launch_search(const CodecView& cv, const float* qr, const float* qs, 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 grid(unsigned(p.nqb * p.nsplit));
-#define TQ_S(U, P, D, KM, NV) hipLaunchKernelGGL((search_kernel<U, P, D, KM, NV>), grid, dim3(NT), 0, s, sa)
-#define TQ_S_UB(P, D, KM)                    \
-  switch (cv.ubits) {                        \
-    case 1: TQ_S(1, P, D, KM, 2); break;     \
-    case 2: TQ_S(2, P, D, KM, 2); break;     \
-    default: TQ_S(3, P, D, KM, 2); break;    \
+  // two waves per key block for 1 and 2 index bits; at 3 the centroid table
+  // (32 KB) leaves no LDS for the second wave's transposition buffers
+#define TQ_S(U, P, D, KM, NV, QW) \
+  hipLaunchKernelGGL((search_kernel<U, P, D, KM, NV, QW>), grid, dim3(NT * QW), 0, s, sa)
+#define TQ_S_UB(P, D, KM)                       \
+  switch (cv.ubits) {                           \
+    case 1: TQ_S(1, P, D, KM, 2, 2); break;     \
+    case 2: TQ_S(2, P, D, KM, 2, 2); break;     \
+    default: TQ_S(3, P, D, KM, 2, 1); break;    \
   }
   if (dense) {
     if (prod) { TQ_S_UB(true, true, 1) } else { TQ_S_UB(false, true, 1) }
