@@ -60,16 +60,24 @@ __device__ __forceinline__ float opaque_minus_one() {
 
 // Pack 8 floats into fp16 hi and lo fragments, x = hi + lo to ~2^-22
 // relative: hi by a packed round-toward-zero conversion, the exact remainder
-// x - hi (one mixed FMA per element) rounded to nearest.
+// x - hi rounded to nearest, each half by one mixed-precision FMA that reads
+// its fp16 half of hi in place and writes its half of the lo word (mixlo,
+// then mixhi into the same register: no separate packing step).
+__device__ __forceinline__ uint32_t split_lo2(uint32_t hb, float v0, float v1) {
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(l)
+      : "v"(hb), "v"(v0), "v"(v1));
+  return l;
+}
 __device__ __forceinline__ void split8h(const float* v, u32x4& hi, u32x4& lo, float m1) {
+  (void)m1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]);
-    const float r0 = __builtin_fmaf(float(h[0]), m1, v[2 * i]);
-    const float r1 = __builtin_fmaf(float(h[1]), m1, v[2 * i + 1]);
-    hi[i] = __builtin_bit_cast(uint32_t, h);
-    lo[i] = uint32_t(__builtin_bit_cast(uint16_t, _Float16(r0))) |
-            (uint32_t(__builtin_bit_cast(uint16_t, _Float16(r1))) << 16);
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]));
+    hi[i] = h;
+    lo[i] = split_lo2(h, v[2 * i], v[2 * i + 1]);
   }
 }
 

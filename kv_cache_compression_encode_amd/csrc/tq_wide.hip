@@ -73,13 +73,20 @@ __device__ __forceinline__ uint32_t h16(float v) { return __builtin_bit_cast(uin
 __device__ __forceinline__ float f16f(uint32_t h) { return float(__builtin_bit_cast(_Float16, uint16_t(h))); }
 
 // 8 floats -> fp16 hi (round toward zero) and lo (the exact remainder,
-// rounded to nearest): v = hi + lo to about 2^-22 relative.
+// rounded to nearest): v = hi + lo to about 2^-22 relative.  Each half of a
+// lo word is one mixed-precision FMA, v - hi with the fp16 half of hi read in
+// place, written straight into its half of the word (mixlo, then mixhi).
 __device__ __forceinline__ void split8(const float (&v)[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const auto h = __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]);
-    hi[i] = __builtin_bit_cast(uint32_t, h);
-    lo[i] = h16(v[2 * i] - float(h[0])) | (h16(v[2 * i + 1] - float(h[1])) << 16);
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(v[2 * i], v[2 * i + 1]));
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %1, -1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(l)
+        : "v"(h), "v"(v[2 * i]), "v"(v[2 * i + 1]));
+    hi[i] = h;
+    lo[i] = l;
   }
 }
 
