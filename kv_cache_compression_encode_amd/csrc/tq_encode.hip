@@ -386,6 +386,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   // symmetric search paths: 16-level col codes (values), 4-level row codes
   constexpr bool SYM4 = UNIFORM && COL && UB == 4 && MODE == 0;
   constexpr bool SYM2 = UNIFORM && !COL && UB == 2;
+  // blocks software-pipelined (two rotation accumulators live at once)
+  constexpr bool PIPE = (SYM4 || (SYM2 && MODE == 1)) && NB == 1 && SPLIT == 0 && BF16IN;
   // SpectralQuant key structure (non-uniform, MODE 2, UB = 2): dims 0..3 carry
   // 1..5 bits, every other dim one bit
   constexpr bool SQK = !UNIFORM && !SPLIT && MODE == 2 && UB == 2;
@@ -677,8 +679,40 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         }
       }
 
-#pragma unroll 1
-      for (int mb = 0; mb < 4; ++mb) {
+      // ------------------------------------------------ rotation block
+      // one accumulation chain per 32-vector block: Pi_hi x_hi, Pi_lo x_hi
+      // (and Pi_hi x_lo for fp32 input); register r of half hh holds
+      // coordinate 32 mb + 16 hh + r
+      auto rotate = [&](int mb, f32x16 (&acc)[NB]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+        // the Pi fragments are read from LDS two steps ahead of the MFMAs
+        // that take them, so that the LDS latency overlaps the chain
+        // (one step ahead in the software pipeline, where the quantization
+        // of the previous block fills the wait)
+        constexpr int RD = PIPE ? 2 : 3;
+        u32x4 fh[RD], fl[RD];
+        auto read_pi = [&](int c) {
+          const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
+          fh[c % RD] = *reinterpret_cast<const u32x4*>(sPiHi + off);
+          fl[c % RD] = *reinterpret_cast<const u32x4*>(sPiLo + off);
+        };
+#pragma unroll
+        for (int c = 0; c < RD - 1; ++c) read_pi(c);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c + RD - 1 < 8) read_pi(c + RD - 1);
+          const u32x4 ah = fh[c % RD], al = fl[c % RD];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
+            acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
+            if (!BF16IN) acc[nb] = mfma32h(ah, xl[nb][c], acc[nb]);
+          }
+        }
+      };
+      // quantize, pack and sketch block mb from its rotated coordinates
+      auto block = [&](int mb, f32x16 (&acc)[NB]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -688,34 +722,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int p = 0; p < kMaxBits; ++p) gw[nb][p] = 0;
-        // ------------------------------------------------ rotation block
-        // one accumulation chain per 32-vector block: Pi_hi x_hi, Pi_lo x_hi
-        // (and Pi_hi x_lo for fp32 input); register r of half hh holds
-        // coordinate 32 mb + 16 hh + r
-        f32x16 acc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-        // the Pi fragments are read from LDS two steps ahead of the MFMAs
-        // that take them, so that the LDS latency overlaps the chain
-        u32x4 fh[3], fl[3];
-        auto read_pi = [&](int c) {
-          const int off = (32 * mb + j) * LDS_ROW + 64 * hh + 8 * c;
-          fh[c % 3] = *reinterpret_cast<const u32x4*>(sPiHi + off);
-          fl[c % 3] = *reinterpret_cast<const u32x4*>(sPiLo + off);
-        };
-        read_pi(0);
-        read_pi(1);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          if (c + 2 < 8) read_pi(c + 2);
-          const u32x4 ah = fh[c % 3], al = fl[c % 3];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            acc[nb] = mfma32h(ah, xh[nb][c], acc[nb]);
-            acc[nb] = mfma32h(al, xh[nb][c], acc[nb]);
-            if (!BF16IN) acc[nb] = mfma32h(ah, xl[nb][c], acc[nb]);
-          }
-        }
         // ------------------------------------------------ quantize block
         uint32_t colkeep[NB][2];
         uint32_t pk[NB][2];  // SYM4: nibbles of registers 8k .. 8k + 7 (register 8k + c at bits 4c)
@@ -976,6 +982,27 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
               }
             }
           }
+        }
+      };
+      if constexpr (PIPE) {
+        // software pipeline: the rotation MFMAs of block mb + 1 are issued
+        // ahead of the quantization of block mb, which does not depend on
+        // them, so the matrix cores and the vector ALU work at the same time
+        f32x16 a0[NB], a1[NB];
+        rotate(0, a0);
+        rotate(1, a1);
+        block(0, a0);
+        rotate(2, a0);
+        block(1, a1);
+        rotate(3, a1);
+        block(2, a0);
+        block(3, a1);
+      } else {
+#pragma unroll 1
+        for (int mb = 0; mb < 4; ++mb) {
+          f32x16 acc[NB];
+          rotate(mb, acc);
+          block(mb, acc);
         }
       }
 
