@@ -664,6 +664,35 @@ CodecView tq::make_view(const tq_codebook* cb) {
     v.uthr[k] = cb->thr32[k];
     v.ucen[k] = cb->cen32[k];
   }
+  v.qn = 0;
+  v.qinvw = v.qoff = 0.f;
+  if (cb->uniform && cb->ubits >= 1) {
+    // bucket width: the smallest gap between boundaries over s (at least 2.5),
+    // s stepped until no boundary lies within 2 % of a bucket edge; offset
+    // so that every coordinate of a unit vector (|y| <= 1, plus rounding)
+    // maps to a bucket >= 1, and half-integer, so that a boundary at 0 sits
+    // mid-bucket
+    const int nb = (1 << cb->ubits) - 1;
+    double gap = 2.0;
+    for (int k = 0; k + 1 < nb; ++k) gap = std::min(gap, double(cb->thr32[k + 1]) - double(cb->thr32[k]));
+    for (int step = 0; step < 200 && v.qn == 0; ++step) {
+      const double w = gap / (2.5 + 0.05 * step);
+      const double off = std::ceil(1.05 / w) + 1.5;
+      const int n = int(2.0 * off) + 2;
+      if (n > kQMax) break;
+      bool ok = true;
+      for (int k = 0; k < nb && ok; ++k) {
+        const double pos = double(cb->thr32[k]) / w + off;
+        const double fr = pos - std::floor(pos);
+        ok = fr >= 0.02 && fr <= 0.98;
+      }
+      if (ok) {
+        v.qn = n;
+        v.qinvw = float(1.0 / w);
+        v.qoff = float(off);
+      }
+    }
+  }
   return v;
 }
 

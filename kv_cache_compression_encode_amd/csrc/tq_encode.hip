@@ -365,6 +365,8 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   float* sThr = reinterpret_cast<float*>(MODE == 1 ? (uint8_t*)(sSk + D * LDS_ROW)
                                                    : (uint8_t*)sSk);
   float* sCen = sThr + D * kMaxLevels;
+  // 16-level COL codes: bucket table of the boundaries (one compare per coordinate)
+  __shared__ float2 sQ[UNIFORM && COL && UB == 4 && MODE == 0 ? kQMax : 1];
 
   // (sequence, head) set: grid y, continued in grid z past 65535 sets
   const int64_t bh = blockIdx.y + int64_t(blockIdx.z) * gridDim.y;
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       // boundaries scaled to the accumulator (uniform codec); prod: the
       // residual is formed directly in unit scale times 32, rsd = v rs - 32 c
       f32x16v T[NB];
-      float P4[NB][7];
+      float sK[NB];  // SYM4: bucket units per accumulator unit
       float rs[NB];
       float C32[LV];
       if (UNIFORM) {
@@ -632,9 +634,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int k = 0; k < LV - 1; ++k) T[nb][k] = cv.uthr[k] * wsc[nb];
-          if (SYM4)
-#pragma unroll
-            for (int k = 0; k < 7; ++k) P4[nb][k] = cv.uthr[8 + k] * wsc[nb];
+          if (SYM4) sK[nb] = cv.qinvw / wsc[nb];
           rs[nb] = 32.f / wsc[nb];
         }
 #pragma unroll
@@ -776,7 +776,14 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 for (int p = 0; p < NPL; ++p) cw[nb][p] = push_bit(cw[nb][p], bits[p]);
               }
             } else if (SYM4) {
-              pk[nb][r >> 3] = quant4_sym_push((r & 7) == 7 ? 0u : pk[nb][r >> 3], v, P4[nb]);
+              // bucket of y (clamped to the table; a NaN lands in bucket 0),
+              // then one compare against the bucket's boundary: the index
+              // is the count of boundaries below the bucket, plus one at or
+              // above its boundary
+              const float u = fminf(fmaxf(fmaf(v, sK[nb], cv.qoff), 0.f), float(cv.qn - 1));
+              const float2 e = sQ[uint32_t(u)];
+              const uint32_t w0 = (r & 7) == 7 ? 0u : pk[nb][r >> 3];
+              pk[nb][r >> 3] = (w0 << 4) + uint32_t(__float_as_int(e.y)) + (u >= e.x ? 1u : 0u);
             } else if (UNIFORM) {
               idx = quant_tree<UB>(v, T[nb]);
               if (MODE != 0) {
@@ -930,7 +937,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
             // the col dword of dim 32mb + 16hh + r for those vectors
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-              const uint32_t w = nib_transpose8(valid[nb] ? quant4_finish(pk[nb][k]) : 0u, nibc);
+              const uint32_t w = nib_transpose8(valid[nb] ? pk[nb][k] : 0u, nibc);
               const int r = 8 * k + (j & 7);
               const int dim = 32 * mb + 16 * hh + r;
               const int word = (sub * NB * 32 + nb * 32 + j) / 8;
@@ -1107,6 +1114,22 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
     if (BF16IN) load_raw(tile, 0, bufA);
     __builtin_amdgcn_sched_barrier(0);
     stage_store<NM>(dst, perm, sv);
+  }
+  if constexpr (SYM4) {
+    // bucket table of the 15 boundaries: entry e = (position of the
+    // boundary inside bucket e, or +inf; number of boundaries below it),
+    // positions y qinvw + qoff in bucket units
+    for (int e = threadIdx.x; e < cv.qn; e += blockDim.x) {
+      float thr = INFINITY;
+      int below = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) {
+        const float pos = fmaf(cv.uthr[k], cv.qinvw, cv.qoff);
+        if (pos < float(e)) ++below;
+        else if (pos < float(e + 1)) thr = pos;
+      }
+      sQ[e] = float2{thr, __int_as_float(below)};
+    }
   }
   if (!UNIFORM && SPLIT != 1) {
     for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x) {
@@ -1516,6 +1539,8 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
     default: return hipErrorNotSupported;                                   \
   }
   if (col && cv.ubits == 3) return hipErrorNotSupported;
+  // 16-level col codes take the bucket-table quantizer
+  if (col && cv.ubits == 4 && mode == 0 && (cv.qn < 2 || cv.qn > kQMax)) return hipErrorNotSupported;
   if (a.x_bf16) {
     // mse values take 32 vectors per wave step (about 190 VGPRs) rather than
     // 64 (256): twice the sub-tiles per wave for the row prefetch to overlap;

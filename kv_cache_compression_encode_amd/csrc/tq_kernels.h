@@ -43,7 +43,15 @@ struct CodecView {
   const uint16_t* sk_tiles;
   float uthr[kMaxLevels];
   float ucen[kMaxLevels];
+  // uniform codecs: bucket table of the boundaries for a one-compare
+  // quantizer.  A coordinate y of the unit vector falls in bucket
+  // floor(y qinvw + qoff) of qn buckets of width 1 / qinvw; every bucket
+  // holds at most one boundary, none within 2 % of a bucket edge (qn = 0:
+  // no table)
+  int qn;
+  float qinvw, qoff;
 };
+constexpr int kQMax = 512;  // largest bucket table
 
 CodecView make_view(const tq_codebook* cb);
 
