@@ -263,10 +263,13 @@ int64_t tq_records_bytes(const tq_codebook* cb, int64_t n);
 /* Encode a batch of vector sets.  [TQ] "Method": n_x = ||x||, y = Pi x/n_x,
  * idx_i = #{boundaries t of dim i with t <= y_i}, so a y_i exactly on a
  * boundary goes to the upper cell -- except in the d = 128 kernels of uniform
- * codecs, which search |y_i| among the positive boundaries (the codebook is
- * symmetric) and put a negative y_i exactly on a boundary into the lower cell,
- * the one of larger magnitude (both readings agree everywhere off the
- * boundaries); prod:
+ * codecs: with 2 index bits they compare |y_i| with the positive boundary
+ * (the codebook is symmetric) and put a negative y_i exactly on a boundary
+ * into the lower cell, the one of larger magnitude; with 4 index bits in the
+ * COL layout they compare y_i with the boundary of its bucket in bucket units
+ * (y_i / w + offset, rounded to fp32), which decides as the exact comparison
+ * except within about 1e-7 of a boundary (all readings agree everywhere off
+ * the boundaries); prod:
  * r = y - c[idx] on dims 0..m-1, n_r = ||r||, bit_j = [(S r)_j >= 0].  A zero
  * vector encodes y = 0 and stores n_x = 0.
  *   x        device, element (b, h, t, i) at x[b*xs_b + h*xs_h + t*xs_t + i] of

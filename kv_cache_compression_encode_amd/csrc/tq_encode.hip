@@ -213,10 +213,12 @@ __device__ __forceinline__ float quant_bits(float v, f32x16v T, const float* L, 
 
 // The uniform codebooks are Lloyd-Max solutions for a symmetric law, so
 // their boundaries are symmetric about 0 (T[L/2 - 1] = 0, T[L/2 - 1 + k] =
-// -T[L/2 - 1 - k]) and so are their levels.  The quantizers below use this:
-// the sign of v picks the half and |v| is searched among the L/2 - 1 positive
-// boundaries only.  Decisions equal those of the full search except when
+// -T[L/2 - 1 - k]) and so are their levels.  The 4-level quantizer below
+// uses this: the sign of v picks the half and |v| is compared with the one
+// positive boundary.  Decisions equal those of the full search except when
 // v < 0 lies exactly on a boundary (a tie, which then goes to the lower cell).
+// 16-level col codes instead look their coordinate's bucket up in a table of
+// the boundaries and make one compare in bucket units (see the kernels).
 
 // Transpose of an 8 x 8 matrix of nibbles held by 8 consecutive lanes (lane
 // t of the group holds row t, element c at bits 4c..4c+3): on return lane t
@@ -263,42 +265,6 @@ __device__ __forceinline__ uint32_t push_mask(uint32_t w, uint64_t m) {
   asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=s"(cout) : "v"(w), "s"(m));
   (void)cout;
   return r;
-}
-
-// push_mask for a mask that is dead afterwards: the carry-out goes back into
-// the mask's own SGPR pair, so that consecutive pushes do not all write one
-// shared pair (each such write-after-write costs a wait state).
-__device__ __forceinline__ uint32_t push_mask_last(uint32_t w, uint64_t m) {
-  uint32_t r;
-  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %1" : "=v"(r), "+s"(m) : "v"(w));
-  return r;
-}
-
-// 16 levels: P[k] = T[8 + k] (k < 7) scaled like v.  The 4-bit index of v
-// is 8 + m for v >= 0 and 7 - m for v < 0, m = number of P[k] <= |v| (a
-// 3-step binary search), so bit 3 is [v >= 0] and bits 2..0 are those of m,
-// inverted when v < 0.  quant4_sym_push appends the raw nibble
-// [v < 0, m2, m1, m0] to w (w = 16 w + nibble: the float sign bit by one
-// v_alignbit, the search bits by v_addc from their compare masks);
-// quant4_finish turns a word of 8 raw nibbles into indices.  v is never -0
-// here (accumulator values).
-__device__ __forceinline__ uint32_t quant4_sym_push(uint32_t w, float v, const float (&P)[7]) {
-  const float a = fabsf(v);
-  const bool b2 = a >= P[3];
-  const uint64_t m2 = __ballot(b2);
-  const bool b1 = a >= (b2 ? P[5] : P[1]);
-  const uint64_t m1 = __ballot(b1);
-  const float tu = b1 ? P[6] : P[4], tl = b1 ? P[2] : P[0];
-  const uint64_t m0 = __ballot(a >= (b2 ? tu : tl));
-  w = __builtin_amdgcn_alignbit(w, __float_as_uint(v), 31);
-  w = push_mask_last(w, m2);
-  w = push_mask_last(w, m1);
-  return push_mask_last(w, m0);
-}
-// Raw nibbles [n, m2, m1, m0] -> indices [not n, m2 ^ n, m1 ^ n, m0 ^ n].
-__device__ __forceinline__ uint32_t quant4_finish(uint32_t w) {
-  const uint32_t n = w & 0x88888888u;
-  return w ^ ((n >> 1) | (n >> 2) | (n >> 3)) ^ 0x88888888u;
 }
 
 // 4 levels: P = T[2] scaled like v, L2 / L3 levels 2 / 3 (levels 0 / 1 are
@@ -776,11 +742,12 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
                 for (int p = 0; p < NPL; ++p) cw[nb][p] = push_bit(cw[nb][p], bits[p]);
               }
             } else if (SYM4) {
-              // bucket of y (clamped to the table; a NaN lands in bucket 0),
-              // then one compare against the bucket's boundary: the index
-              // is the count of boundaries below the bucket, plus one at or
-              // above its boundary
-              const float u = fminf(fmaxf(fmaf(v, sK[nb], cv.qoff), 0.f), float(cv.qn - 1));
+              // bucket of y, clamped to the table by one median-of-three
+              // (a NaN that survives it converts to bucket 0), then one
+              // compare against the bucket's boundary: the index is the
+              // count of boundaries below the bucket, plus one at or above
+              // its boundary
+              const float u = __builtin_amdgcn_fmed3f(fmaf(v, sK[nb], cv.qoff), 0.f, float(cv.qn - 1));
               const float2 e = sQ[uint32_t(u)];
               const uint32_t w0 = (r & 7) == 7 ? 0u : pk[nb][r >> 3];
               pk[nb][r >> 3] = (w0 << 4) + uint32_t(__float_as_int(e.y)) + (u >= e.x ? 1u : 0u);
@@ -1232,8 +1199,24 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
   const int64_t bh = blockIdx.y + int64_t(blockIdx.z) * gridDim.y;
   if (bh >= a.batch * a.heads) return;
   const int64_t b = bh / a.heads, h = bh % a.heads;
+  // COL: bucket table of the 15 boundaries (one compare per coordinate, as
+  // in the dense-rotation kernel)
+  __shared__ float2 sQ[COL ? kQMax : 1];
   if (threadIdx.x < 64) sMask[threadIdx.x] = cv.had_mask[threadIdx.x];
   if (MODE == 1) stage_sketch_had(sSk, cv.sk_hi);
+  if constexpr (COL) {
+    for (int e = threadIdx.x; e < cv.qn; e += blockDim.x) {
+      float thr = INFINITY;
+      int below = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) {
+        const float pos = fmaf(cv.uthr[k], cv.qinvw, cv.qoff);
+        if (pos < float(e)) ++below;
+        else if (pos < float(e + 1)) thr = pos;
+      }
+      sQ[e] = float2{thr, __int_as_float(below)};
+    }
+  }
   __syncthreads();
 
   const int lane = lane_id();
@@ -1335,10 +1318,7 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
     f32x16v T = {};
 #pragma unroll
     for (int k = 0; k < LV - 1; ++k) T[k] = cv.uthr[k] * wsc;
-    float P4[7];
-    if (SYM4)
-#pragma unroll
-      for (int k = 0; k < 7; ++k) P4[k] = cv.uthr[8 + k] * wsc;
+    const float sK = SYM4 ? cv.qinvw / wsc : 0.f;  // bucket units per accumulator unit
     float C32[LV];
 #pragma unroll
     for (int k = 0; k < LV; ++k) C32[k] = 32.f * cv.ucen[k];
@@ -1353,8 +1333,13 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
         for (int g = 0; g < 4; ++g) {
           uint32_t w = 0;
 #pragma unroll
-          for (int i = 7; i >= 0; --i) w = quant4_sym_push(w, v[32 * blk + 8 * g + i], P4);
-          w = nib_transpose8(valid ? quant4_finish(w) : 0u, nibc);
+          for (int i = 7; i >= 0; --i) {
+            const float u = __builtin_amdgcn_fmed3f(fmaf(v[32 * blk + 8 * g + i], sK, cv.qoff), 0.f,
+                                                    float(cv.qn - 1));
+            const float2 e = sQ[uint32_t(u)];
+            w = (w << 4) + uint32_t(__float_as_int(e.y)) + (u >= e.x ? 1u : 0u);
+          }
+          w = nib_transpose8(valid ? w : 0u, nibc);
           const int dim = 32 * mb + 8 * g + (j & 7);
           *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 32 + 4 * (slot / 8)) = w;
         }
@@ -1497,7 +1482,8 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
   if (cv.had_mask && cv.uniform && a.x_bf16) {
     // randomized Hadamard rotation: the register transform for the GQA K/V
     // codecs; any other combination uses the dense Pi below
-    if (cv.mode == TQ_MSE && col && cv.ubits == 4) return launch_had<0, true, 4>(cv, a, s);
+    if (cv.mode == TQ_MSE && col && cv.ubits == 4 && cv.qn >= 2 && cv.qn <= kQMax)
+      return launch_had<0, true, 4>(cv, a, s);
     if (cv.mode == TQ_PROD && !col && cv.m == D && cv.ubits == 2) return launch_had<1, false, 2>(cv, a, s);
   }
   if (cv.outl) {
