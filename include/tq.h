@@ -293,8 +293,10 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
  *   q' = Pi q, qs = S q'[0:m] ([TQ] "Method"; estimator of <q, x>).
  *   q        device fp32 [nq][d];  scores device fp32 [nq][n].
  *   workspace >= tq_workspace_size(cb, TQ_OP_SCORE, nq, n, 0) bytes (device).
- * Supported: d = 128 (any ROW codec; nq <= 262140) and d a multiple of 128 up
- * to 4096 with a uniform codec (full sketch for prod); else TQ_EUNSUPPORTED. */
+ * Supported: d = 128 (any ROW codec) and d a multiple of 128 up to 4096 with a
+ * uniform codec (full sketch for prod); else TQ_EUNSUPPORTED.  More than
+ * 261632 queries run as consecutive passes of that many, sharing the
+ * workspace (whose size then covers one pass). */
 tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t head,
                    const void* records, int64_t n, float* scores, void* workspace,
                    size_t workspace_bytes, void* stream);
@@ -380,7 +382,8 @@ tq_status tq_decode_step(const tq_codebook* kcb, const tq_codebook* vcb, const v
  * search with TurboQuant codes).  For each query the k largest scores
  * (as tq_score), descending; equal scores go to the smaller id.
  *   top_scores device fp32 [nq][k]; top_ids device int64 [nq][k]; 1 <= k <= 16.
- *   workspace >= tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k). */
+ *   workspace >= tq_workspace_size(cb, TQ_OP_TOPK, nq, n, k); more than
+ *   65408 queries run as consecutive passes of that many, sharing it. */
 tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
                          const void* records, int64_t n, int32_t k, float* top_scores,
                          int64_t* top_ids, void* workspace, size_t workspace_bytes,

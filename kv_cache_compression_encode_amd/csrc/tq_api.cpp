@@ -597,6 +597,12 @@ int64_t decode_nsplit(int64_t max_tokens) {
 constexpr int kDecodeChunkTiles = 8;
 
 constexpr int kTopkSegments = 16;  // partial lists per key chunk of the general top-k path
+// Queries per internal pass of tq_score / tq_search_topk (the grid limits of
+// the d = 128 score and general top-k kernels; a multiple of the 128-query
+// blocks of the wide search).  Larger query sets run as consecutive passes
+// that share the workspace.
+constexpr int64_t kTopkQueries = 65408;
+constexpr int64_t kScoreQueries = 4 * kTopkQueries;
 
 // Keys per chunk of the general top-k path (scores of a chunk are written to
 // the workspace, then scanned): about 2^26 scores per chunk, at most 64 chunks,
@@ -924,7 +930,7 @@ size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b
     case TQ_OP_ENCODE:
       return d != 128 ? wide_encode_workspace(make_view(cb)) : 0;
     case TQ_OP_SCORE:
-      return query_ws(cb, TQ_OP_SCORE, a, b, 0).total();
+      return query_ws(cb, TQ_OP_SCORE, std::min(a, kScoreQueries), b, 0).total();
     case TQ_OP_DECODE: {
       if (c <= 0) return 0;
       const size_t part = size_t(a) * size_t(decode_nsplit(b)) * (2 + d) * 4;
@@ -932,7 +938,7 @@ size_t tq_workspace_size(const tq_codebook* cb, int32_t op, int64_t a, int64_t b
     }
     case TQ_OP_TOPK: {
       if (c <= 0 || c > 16) return 0;
-      return query_ws(cb, TQ_OP_TOPK, a, b, int(c)).total();
+      return query_ws(cb, TQ_OP_TOPK, std::min(a, kTopkQueries), b, int(c)).total();
     }
   }
   return 0;
@@ -950,7 +956,16 @@ tq_status tq_score(const tq_codebook* cb, const float* q, int64_t nq, int32_t he
   const CodecView cv = make_view(cb);
   if (cb->desc.d != 128 && (!search_mfma_supported(cv) || n >= (int64_t(1) << 31))) return TQ_EUNSUPPORTED;
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
-  if (nq > int64_t(65535) * 4) return TQ_EUNSUPPORTED;
+  if (nq > kScoreQueries) {
+    // consecutive passes over blocks of queries (rows of q and scores)
+    for (int64_t q0 = 0; q0 < nq; q0 += kScoreQueries) {
+      const int64_t c = std::min(kScoreQueries, nq - q0);
+      const tq_status st = tq_score(cb, q + q0 * cb->desc.d, c, head, records, n, scores + q0 * n, workspace,
+                                    workspace_bytes, stream);
+      if (st != TQ_OK) return st;
+    }
+    return TQ_OK;
+  }
   const QueryWs W = query_ws(cb, TQ_OP_SCORE, nq, n, 0);
   if (!workspace || workspace_bytes < W.total()) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
@@ -1160,7 +1175,16 @@ tq_status tq_search_topk(const tq_codebook* cb, const float* q, int64_t nq,
   if (!aligned16(records) || !aligned16(q)) return TQ_EALIGN;
   if (nq == 0) return TQ_OK;
   if (n < k) return TQ_EINVAL;
-  if (nq > 65535) return TQ_EUNSUPPORTED;
+  if (nq > kTopkQueries) {
+    // consecutive passes over blocks of queries (rows of q and of the lists)
+    for (int64_t q0 = 0; q0 < nq; q0 += kTopkQueries) {
+      const int64_t c = std::min(kTopkQueries, nq - q0);
+      const tq_status st = tq_search_topk(cb, q + q0 * cb->desc.d, c, records, n, k, top_scores + q0 * k,
+                                          top_ids + q0 * k, workspace, workspace_bytes, stream);
+      if (st != TQ_OK) return st;
+    }
+    return TQ_OK;
+  }
   const QueryWs W = query_ws(cb, TQ_OP_TOPK, nq, n, k);
   if (!workspace || workspace_bytes < W.total()) return TQ_EWORKSPACE;
   if (!aligned16(workspace)) return TQ_EALIGN;
