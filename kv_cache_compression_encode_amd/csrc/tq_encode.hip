@@ -33,6 +33,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int LDS_ROW = D + 8;  // 16-bit elements per staged row (16-byte pad)
@@ -426,19 +427,31 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
         if (BF16IN) {
           // raw bf16 pairs (prefetched) stay packed until the scale is known
           const u32x4* r = cur[nb];
-          {
+          if constexpr (!SPLIT) {
+            // ||x||^2 by bf16 dot products of each word with itself (the
+            // products are exact in fp32), four chains; the words go through
+            // scalars (a bit cast straight from a vector element has read
+            // element 0)
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const uint32_t w = r[c][i];
+                const bf2_t h = __builtin_bit_cast(bf2_t, w);
+                s4[i] = __builtin_amdgcn_fdot2_f32_bf16(h, h, s4[i], false);
+              }
+            ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+          } else {
             // two chains; the squares of bf16 values are exact in fp32
             float s0 = 0.f, s1 = 0.f;
-            float o0 = 0.f, o1 = 0.f;  // SPLIT: outlier channels only
+            float o0 = 0.f, o1 = 0.f;  // outlier channels only
 #pragma unroll
             for (int c = 0; c < 8; ++c)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const float lo = __uint_as_float(r[c][i] << 16), hi = __uint_as_float(r[c][i] & 0xffff0000u);
-                if constexpr (!SPLIT) {
-                  s0 = fmaf(lo, lo, s0);
-                  s1 = fmaf(hi, hi, s1);
-                } else {
+                {
                   // channel 64 hh + 8c + 2i (+1): bit (8c + 2i) % 32 of mask word c / 4
                   const int k = (8 * c + 2 * i) & 31;
                   const uint32_t lw = r[c][i] << 16, hw = r[c][i] & 0xffff0000u;
