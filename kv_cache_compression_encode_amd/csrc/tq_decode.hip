@@ -49,6 +49,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x for x <= 0 (or -inf): the hardware base-2 exponential
+__device__ __forceinline__ float exp2_le0(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
@@ -65,9 +70,11 @@ __device__ __forceinline__ float h2f(uint16_t h) { return float(__builtin_bit_ca
 // Reductions over the 16 lanes of a row with DPP row rotations (no LDS
 // round trips), and exchanges with the lane 32 (or 16) positions away with
 // the gfx950 permlane swaps.
+// (a row rotation reads a valid lane everywhere, so the move needs no old
+// value and the compiler folds it into the max or add as a DPP operand)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int G>
 __device__ __forceinline__ float grp_max(float v) {
@@ -407,6 +414,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   }
   __syncthreads();
 
+  // logits in base-2 units (softmax scale times log2 e), so that each
+  // exponential is one v_exp_f32; the running maxima are in the same units
+  // and go back to natural units only where partials leave the kernel
+  const float scale2 = a.scale * kLog2e;
   // QJL factor sqrt(pi/2)/m; split keys: per group, m_g = 96 (regular) and 32
   const float coef_scale = kQjl / float(SPL ? D - 32 : kc.m);
   const float coef_scale_o = kQjl / 32.f;
@@ -528,8 +539,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         const float co = nro[nb] * coef_scale_o;
         const float sa = nx[nb] * (xa + coef * xor32(xa, lane)) + nxo[nb] * (oa + co * xor32(oa, lane));
         const float sb = nx[nb] * (xb + coef * xor32(xb, lane)) + nxo[nb] * (ob + co * xor32(ob, lane));
-        lg[nb][0] = valid ? a.scale * sa : -INFINITY;
-        lg[nb][1] = valid ? a.scale * sb : -INFINITY;
+        lg[nb][0] = valid ? scale2 * sa : -INFINITY;
+        lg[nb][1] = valid ? scale2 * sb : -INFINITY;
         continue;
       }
       if (SQ) {
@@ -549,8 +560,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         ta = coef * xor32(xa, lane);
         tb = coef * xor32(xb, lane);
       }
-      lg[nb][0] = valid ? a.scale * nx[nb] * (xa + ta) : -INFINITY;
-      lg[nb][1] = valid ? a.scale * nx[nb] * (xb + tb) : -INFINITY;
+      lg[nb][0] = valid ? scale2 * nx[nb] * (xa + ta) : -INFINITY;
+      lg[nb][1] = valid ? scale2 * nx[nb] * (xb + tb) : -INFINITY;
     }
     // ---- online softmax (lanes of group 0: queries 0,1; group 1: queries 2,3)
     float alpha[2];
@@ -559,13 +570,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       float mt = fmaxf(fmaxf(lg[0][k], lg[1][k]), fmaxf(lg[2][k], lg[3][k]));
       mt = grp_max<G>(mt);
       const float mnew = fmaxf(mrun[k], mt);
-      alpha[k] = mrun[k] == -INFINITY ? 0.f : __expf(mrun[k] - mnew);
+      alpha[k] = mrun[k] == -INFINITY ? 0.f : exp2_le0(mrun[k] - mnew);
       // no token yet (mnew = -inf): every lg is -inf and exp(lg - 0) = 0
       const float msafe = mnew == -INFINITY ? 0.f : mnew;
       float ps = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const float p = __expf(lg[nb][k] - msafe);
+        const float p = exp2_le0(lg[nb][k] - msafe);
         ps += p;
         const int q = 2 * g16 + k;
         if (g16 < 2 && q < G) sP[wave][q][16 * nb + n] = uint16_t(f16b(p * nv[nb]));
@@ -634,12 +645,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
       float accs = 0.f, l = 0.f;
       for (int w = 0; w < 4; ++w) {
-        const float f = sm_m[w][gg] == -INFINITY ? 0.f : __expf(sm_m[w][gg] - M);
+        const float f = sm_m[w][gg] == -INFINITY ? 0.f : exp2_le0(sm_m[w][gg] - M);
         accs += f * sacc[w][gg][i];
         l += f * sm_l[w][gg];
       }
       out[2 * G + gg * D + i] = accs;
-      if (i == 0) { out[gg] = M; out[G + gg] = l; }
+      if (i == 0) { out[gg] = M * kLn2; out[G + gg] = l; }  // the maximum in natural units
     }
     return;
   }
@@ -652,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
     float accs = 0.f, l = 0.f;
     for (int w = 0; w < 4; ++w) {
-      const float f = sm_m[w][gg] == -INFINITY ? 0.f : __expf(sm_m[w][gg] - M);
+      const float f = sm_m[w][gg] == -INFINITY ? 0.f : exp2_le0(sm_m[w][gg] - M);
       accs += f * sacc[w][gg][i];
       l += f * sm_l[w][gg];
     }
