@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
   constexpr bool SQ = UB == 0;
   constexpr bool SPL = UB == 3;  // outlier-channel split keys, 32 outlier coordinates
-  __shared__ float sqr[4][D];
-  __shared__ float sqs[4][D];
+  __shared__ __align__(16) float sqr[4][D];
+  __shared__ __align__(16) float sqs[4][D];
   // SQ, per query: [i][idx] = q'_i c_i(idx) for dims i = 0..3, and [4][s] =
   // sum_i (+-qs_i) over the 4 QJL sign bits s (bit set: +).  Query q's tables
   // start at 336 q words: queries 0 and 2 (1 and 3), whose lanes read in the
@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   constexpr int kSqtab = 336;
   __shared__ float sqtab[SQ ? 4 * kSqtab : 1];
   __shared__ float smu[4];
-  __shared__ float sgam[SQ ? D : 1], smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
+  __shared__ __align__(16) float sgam[SQ ? D : 1];
+  __shared__ float smuv[SQ ? D : 1];  // SQ: one-bit dims' (c1 - c0)/2, (c1 + c0)/2
   // SQ: tail byte -> byte i = 4 x (index bits 1.. of dim i), i = 0..3: with
   // the low bits added, byte i is the byte offset of dim i's table entry
   __shared__ uint32_t stail[SQ ? 256 : 1];
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // entry e for lane l at slut[e * 32 + l % 32], so that the random lookups
   // of a wave hit 32 distinct banks
   __shared__ uint32_t slut1[256];
-  __shared__ uint32_t slut[256 * 32];
+  __shared__ __align__(16) uint32_t slut[256 * 32];
   constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
   __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
   __shared__ float sm_m[4][4], sm_l[4][4];
@@ -204,6 +205,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   };
   TileRegs& ra = cur;
   TileRegs& rb = nxt;
+  // the raw queries are loaded first (2 values per thread; their latency is
+  // the first the set-up waits for)
+  float qraw[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int gg = e / D, i = e % D;
+    const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
+    float v = 0.f;
+    if (gg < G)
+      v = a.q_bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * D + i]) << 16)
+                   : static_cast<const float*>(a.q)[qi * D + i];
+    qraw[u] = v;
+  }
   // the first tile's loads go out before the set-up below and overlap it.
   // Contiguous records: they do not wait for seq_lens, since any tile below
   // max_tokens is in the records (a wave without a tile leaves them unused).
@@ -221,38 +236,35 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // forms coordinate t % 128 over half t / 128 of each sum, reading the
   // transposed matrices column-coalesced (all their loads go out first).
   const int hk = kc.heads > 1 ? g : 0;
-  const int ci = threadIdx.x & (D - 1), kh = threadIdx.x >> 7;
   // randomized Hadamard keys: q' = H (s q) / sqrt(d) by the wave transform
   // instead of the columns of Pi
   const bool khad = kc.had_sign != nullptr;
-  float rcol[D / 2], scol[SQ ? 1 : D / 2];
+  // thread t takes columns 4 cg .. 4 cg + 3 (cg = t % 32) over rows
+  // 16 rg .. 16 rg + 15 (rg = t / 32) of the transposed matrices, as 16-byte
+  // loads; the 8 row groups' partial sums are added through LDS
+  const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
+  float4 rc4[16], sc4[16];  // sc4 unused (never loaded) for SpectralQuant keys
   {
-    const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(kh * (D / 2)) * D + ci;
+    const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(16 * rg) * D + 4 * cg;
     if (!khad) {
 #pragma unroll
-      for (int u = 0; u < D / 2; ++u) rcol[u] = rt[size_t(u) * D];
+      for (int u = 0; u < 16; ++u) rc4[u] = *reinterpret_cast<const float4*>(rt + size_t(u) * D);
     }
     if (!SQ) {
-      const float* st = kc.sketch_t + size_t(kh * (D / 2)) * D + ci;
+      const float* st = kc.sketch_t + size_t(16 * rg) * D + 4 * cg;
 #pragma unroll
-      for (int u = 0; u < D / 2; ++u) scol[u] = st[size_t(u) * D];
+      for (int u = 0; u < 16; ++u) sc4[u] = *reinterpret_cast<const float4*>(st + size_t(u) * D);
     }
   }
-  for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {  // raw queries, staged in sqs
-    const int gg = e / D, i = e % D;
-    const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
-    float v = 0.f;
-    if (gg < G)
-      v = a.q_bf16 ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.q)[qi * D + i]) << 16)
-                   : static_cast<const float*>(a.q)[qi * D + i];
-    sqs[gg][i] = v;
-  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) (&sqs[0][0])[threadIdx.x + 256 * u] = qraw[u];  // raw queries, staged in sqs
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   {
     const int t = threadIdx.x;  // 256 threads: one value-table entry each
     slut1[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
   }
-  for (int e = threadIdx.x; e < 4 * 16 * PROW; e += blockDim.x) (&sP[0][0][0])[e] = 0;
+  for (int e = threadIdx.x; e < 4 * 16 * PROW / 8; e += blockDim.x)
+    reinterpret_cast<u32x4*>(&sP[0][0][0])[e] = u32x4{0u, 0u, 0u, 0u};
   if (SQ) {
     {
       const uint32_t tw = kc.sq_tail[threadIdx.x];  // dim i's bits 1.. at bits 5i .. 5i + 4
@@ -271,8 +283,33 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   }
   __syncthreads();
   {
-    // q' = Pi q: half sums into the (still unused) merge buffer, then added
-    float* part = &sacc[0][0][0];  // [2][4][D]
+    // q' = Pi q: row-group partial sums into the (not yet filled) value
+    // table, then added
+    float* part = reinterpret_cast<float*>(slut);  // [8][4][D]
+    // partial sums of the 4 queries over this thread's rows, 4 columns each
+    auto rowgroup = [&](const float4 (&m4)[16], const float (&x)[4][D]) {
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float xv = x[gg][16 * rg + u];
+          acc.x = fmaf(m4[u].x, xv, acc.x);
+          acc.y = fmaf(m4[u].y, xv, acc.y);
+          acc.z = fmaf(m4[u].z, xv, acc.z);
+          acc.w = fmaf(m4[u].w, xv, acc.w);
+        }
+        *reinterpret_cast<float4*>(&part[(rg * 4 + gg) * D + 4 * cg]) = acc;
+      }
+    };
+    auto gather = [&](float (&y)[4][D]) {
+      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
+        float v = 0.f;
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) v += part[r8 * 4 * D + e];
+        y[e / D][e % D] = v;
+      }
+    };
     if (khad) {
       // wave w transforms query w
       float lo = sqs[wave][lane] * kc.had_sign[lane], hi = sqs[wave][lane + 64] * kc.had_sign[lane + 64];
@@ -280,34 +317,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       sqr[wave][lane] = lo * kInvSqrt128;
       sqr[wave][lane + 64] = hi * kInvSqrt128;
     } else {
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int u = 0; u < D / 2; u += 2) {
-          s0 = fmaf(rcol[u], sqs[gg][kh * (D / 2) + u], s0);
-          s1 = fmaf(rcol[u + 1], sqs[gg][kh * (D / 2) + u + 1], s1);
-        }
-        part[(kh * 4 + gg) * D + ci] = s0 + s1;
-      }
+      rowgroup(rc4, sqs);
       __syncthreads();
-      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqr[e / D][e % D] = part[e] + part[4 * D + e];
+      gather(sqr);
     }
     __syncthreads();
     if (!SQ) {
       // qs = S q' (m = d)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int u = 0; u < D / 2; u += 2) {
-          s0 = fmaf(scol[u], sqr[gg][kh * (D / 2) + u], s0);
-          s1 = fmaf(scol[u + 1], sqr[gg][kh * (D / 2) + u + 1], s1);
-        }
-        part[(kh * 4 + gg) * D + ci] = s0 + s1;
-      }
+      rowgroup(sc4, sqr);
       __syncthreads();
-      for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) sqs[e / D][e % D] = part[e] + part[4 * D + e];
+      gather(sqs);
     } else {
       // qs = S q'[0:m], m <= 4 (entries past m are zero)
       for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
@@ -320,10 +339,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     }
     __syncthreads();
   }
-#pragma unroll 8
-  for (int k = 0; k < 32; ++k) {  // consecutive threads write consecutive words
-    const int e = k * 256 + threadIdx.x;
-    slut[e] = slut1[e >> 5];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {  // consecutive threads write consecutive 16-byte groups
+    const int e4 = k * 256 + threadIdx.x;
+    const uint32_t v = slut1[e4 >> 3];
+    reinterpret_cast<u32x4*>(slut)[e4] = u32x4{v, v, v, v};
   }
   if (SQ) {
     for (int e = threadIdx.x; e < 4 * 4 * kMaxLevels; e += blockDim.x) {
@@ -386,22 +406,37 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     const int r = n;
     const bool rowsig = r >= 8;
     const int gq = (r & 7) >> 1, lo = r & 1;
+    const int dim0 = 32 * g16 + 8 * c;
+    // the 8 consecutive dims of this lane, two 16-byte reads each
+    float qv[8], gv[8];
+    {
+      const float* src = (rowsig ? &sqs[gq & 3][0] : &sqr[gq & 3][0]) + dim0;
+      const float4 u0 = *reinterpret_cast<const float4*>(src), u1 = *reinterpret_cast<const float4*>(src + 4);
+      qv[0] = u0.x; qv[1] = u0.y; qv[2] = u0.z; qv[3] = u0.w;
+      qv[4] = u1.x; qv[5] = u1.y; qv[6] = u1.z; qv[7] = u1.w;
+      if (SQ) {
+        const float4 w0 = *reinterpret_cast<const float4*>(&sgam[dim0]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sgam[dim0 + 4]);
+        gv[0] = w0.x; gv[1] = w0.y; gv[2] = w0.z; gv[3] = w0.w;
+        gv[4] = w1.x; gv[5] = w1.y; gv[6] = w1.z; gv[7] = w1.w;
+      }
+    }
     float v[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int dim = 32 * g16 + 8 * c + s;
+      const int dim = dim0 + s;
       float x = 0.f;
       if (gq < G) {
         if (SQ) {
-          if (!rowsig && dim >= 4) x = sgam[dim] * sqr[gq][dim];
+          if (!rowsig && dim >= 4) x = gv[s] * qv[s];
         } else if (SPL) {
           // plane 0: outlier beta / regular c_1; plane 1: outlier alpha (chunk 0)
-          if (!rowsig && p == 0) x = (c == 0 ? spl_b : spl_c1) * sqr[gq][dim];
-          if (!rowsig && p == 1 && c == 0) x = spl_a * sqr[gq][dim];
-          if (rowsig && sign_part) x = sqs[gq][dim];
+          if (!rowsig && p == 0) x = (c == 0 ? spl_b : spl_c1) * qv[s];
+          if (!rowsig && p == 1 && c == 0) x = spl_a * qv[s];
+          if (rowsig && sign_part) x = qv[s];
         } else {
-          if (!rowsig && !sign_part) x = wp[p] * sqr[gq][dim];
-          if (rowsig && sign_part) x = sqs[gq][dim];
+          if (!rowsig && !sign_part) x = wp[p] * qv[s];
+          if (rowsig && sign_part) x = qv[s];
         }
       }
       const float hi = f16v(f16b(x));
@@ -485,49 +520,47 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       nv[nb] = h2f(uint16_t(nvb[nb] & 0xffffu));
       sqb[nb] = SQ ? uint32_t(__shfl(int(spack), 16 * nb + n, 64)) : 0u;
     }
-    // value B fragments: table lookups issued before the score step
-    u32x4 Bv[8][2];
-#pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-      for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const uint32_t w = vw[vb][kc2];
-        const uint32_t* lut = slut + (lane & 31);
-        Bv[vb][kc2][0] = lut[(w & 0xffu) << 5];
-        Bv[vb][kc2][1] = lut[((w >> 8) & 0xffu) << 5];
-        Bv[vb][kc2][2] = lut[((w >> 16) & 0xffu) << 5];
-        Bv[vb][kc2][3] = lut[(w >> 24) << 5];
-      }
-    // ---- scores
+    // ---- scores: the four 16-key blocks accumulate in four independent
+    // MFMA chains, interleaved step by step (each chain's next MFMA is four
+    // MFMAs away, past its predecessor's latency); the operands of step k + 1
+    // (one query fragment, four key patterns) are read during step k
     float lg[4][2];
-    u32x4 A[NP][4];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) A[p][c] = sA[p * 4 + c][lane];
+    constexpr int KPN = SPL ? 9 : NP * 4;  // score MFMAs per 16 keys
+    // split keys: step k's (plane, byte) and whether it feeds the outlier chain
+    constexpr int spl_p[9] = {0, 0, 1, 0, 2, 0, 2, 2, 2};
+    constexpr int spl_c[9] = {0, 1, 0, 2, 0, 3, 1, 2, 3};
+    constexpr bool spl_o[9] = {true, false, true, false, true, false, false, false, false};
+    auto kbyte = [&](int nb, int k) -> uint32_t {
+      if (SPL) return spl_p[k] == 1 ? kw[nb][1] : (kw[nb][spl_p[k]] >> (8 * spl_c[k])) & 0xffu;
+      return (kw[nb][k >> 2] >> (8 * (k & 3))) & 0xffu;
+    };
+    auto afrag = [&](int k) -> u32x4 { return SPL ? sA[spl_p[k] * 4 + spl_c[k]][lane] : sA[k][lane]; };
+    f32x4 accs[4], accso[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 acco = f32x4{0.f, 0.f, 0.f, 0.f};  // split keys: outlier chain
-      if (SPL) {
-        acco = mfma16(A[0][0], spm[kw[nb][0] & 0xffu], acco);
-        acc = mfma16(A[0][1], spm[(kw[nb][0] >> 8) & 0xffu], acc);
-        acco = mfma16(A[1][0], spm[kw[nb][1]], acco);
-        acc = mfma16(A[0][2], spm[(kw[nb][0] >> 16) & 0xffu], acc);
-        acco = mfma16(A[2][0], spm[kw[nb][2] & 0xffu], acco);
-        acc = mfma16(A[0][3], spm[kw[nb][0] >> 24], acc);
-        acc = mfma16(A[2][1], spm[(kw[nb][2] >> 8) & 0xffu], acc);
-        acc = mfma16(A[2][2], spm[(kw[nb][2] >> 16) & 0xffu], acc);
-        acc = mfma16(A[2][3], spm[kw[nb][2] >> 24], acc);
-      } else {
+      accs[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accso[nb] = f32x4{0.f, 0.f, 0.f, 0.f};  // split keys: outlier chain
+    }
+    u32x4 Ak[2], Bk[2][4];
+    Ak[0] = afrag(0);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          acc = mfma16(A[p][0], spm[kw[nb][p] & 0xffu], acc);
-          acc = mfma16(A[p][1], spm[(kw[nb][p] >> 8) & 0xffu], acc);
-          acc = mfma16(A[p][2], spm[(kw[nb][p] >> 16) & 0xffu], acc);
-          acc = mfma16(A[p][3], spm[kw[nb][p] >> 24], acc);
-        }
+    for (int nb = 0; nb < 4; ++nb) Bk[0][nb] = spm[kbyte(nb, 0)];
+#pragma unroll
+    for (int k = 0; k < KPN; ++k) {
+      if (k + 1 < KPN) {
+        Ak[(k + 1) & 1] = afrag(k + 1);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) Bk[(k + 1) & 1][nb] = spm[kbyte(nb, k + 1)];
       }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (SPL && spl_o[k]) accso[nb] = mfma16(Ak[k & 1], Bk[k & 1][nb], accso[nb]);
+        else accs[nb] = mfma16(Ak[k & 1], Bk[k & 1][nb], accs[nb]);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const f32x4 acc = accs[nb], acco = accso[nb];
       const float xa = acc[0] + acc[1], xb = acc[2] + acc[3];
       const int tok = tile * kTile + 16 * nb + n;
       const bool valid = tok < len;
@@ -563,6 +596,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       lg[nb][0] = valid ? scale2 * nx[nb] * (xa + ta) : -INFINITY;
       lg[nb][1] = valid ? scale2 * nx[nb] * (xb + tb) : -INFINITY;
     }
+    // value B fragments: table lookups issued before the softmax, whose
+    // arithmetic covers their latency
+    u32x4 Bv[8][2];
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const uint32_t w = vw[vb][kc2];
+        const uint32_t* lut = slut + (lane & 31);
+        Bv[vb][kc2][0] = lut[(w & 0xffu) << 5];
+        Bv[vb][kc2][1] = lut[((w >> 8) & 0xffu) << 5];
+        Bv[vb][kc2][2] = lut[((w >> 16) & 0xffu) << 5];
+        Bv[vb][kc2][3] = lut[(w >> 24) << 5];
+      }
     // ---- online softmax (lanes of group 0: queries 0,1; group 1: queries 2,3)
     float alpha[2];
 #pragma unroll
