@@ -109,6 +109,19 @@ __host__ __device__ constexpr int lds_row_of(int g) {
 // two phases: stage_load issues every load (one memory round trip for all
 // N), stage_store writes LDS once they have arrived; loads issued between
 // the two stay in flight across the stores.
+// Next job of a workgroup's job counter in LDS: every lane of the wave adds
+// (lane 0 one, the others zero), so that lane 0's return value is the
+// counter before this wave's increment whatever order the lanes are served
+// in.  Written as one LDS atomic with its wait: the compiler's own lowering
+// of a wave-level atomic adds a loop over the active lanes and a branch.
+__device__ __forceinline__ int take_job(int* counter, int lane) {
+  const uint32_t addr = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) int*)counter));
+  const uint32_t one = lane == 0 ? 1u : 0u;
+  uint32_t old;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)" : "=v"(old) : "v"(addr), "v"(one));
+  return int(__builtin_amdgcn_readfirstlane(old));
+}
+
 constexpr int kStagePer = D * D / 8 / 512;
 static_assert(D * D / 8 % 512 == 0, "whole chunks per thread");
 template <int N>
@@ -1072,12 +1085,24 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       }
     }
   };
-  // (tile, sub-tile) positions of this wave, in order
-  auto next_pos = [&](int64_t& tl, int& sb) {
-    if (sb + 1 < NSUB) { ++sb; } else { sb = 0; tl += tstep; }
+  // Jobs of this workgroup: job j is tile (j / nwaves) tstep + blockIdx.x
+  // nwaves + j % nwaves (both of its sub-tiles when NSUB = 2, else one
+  // sub-tile).  Wave w starts with job w.  When the workgroup has at least
+  // 4 jobs per wave, each further job goes to the wave that asks first (a
+  // counter in LDS): the two waves sharing a SIMD are not issued at equal
+  // rates, and a fixed split leaves the slower one last.  With fewer, a
+  // late extra job costs more than the imbalance, and wave w keeps jobs
+  // w, w + nwaves, ...
+  __shared__ int sJob;
+  const bool dyn = ntiles >= 4 * tstep;
+  auto next_tile = [&](int64_t tl) {
+    if (!dyn) return tl + tstep;  // uniform over the workgroup
+    const int jb = take_job(&sJob, lane);
+    const int r = jb / nwaves;
+    return int64_t(r) * tstep + int64_t(blockIdx.x) * nwaves + (jb - r * nwaves);
   };
   int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
-  int sub = 0;
+  if (threadIdx.x == 0) sJob = nwaves;
   // the tables' loads go out first, then the first rows; the tables are
   // stored to LDS as soon as they arrive, with the rows still in flight
   {
@@ -1119,30 +1144,23 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   }
   __syncthreads();
   if constexpr (NB == 1) {
+    // one tile per job: its second half is loaded while the first is
+    // processed, the next job's first half while the second is
     while (tile < ntiles) {
-      int64_t t1 = tile;
-      int s1 = sub;
-      next_pos(t1, s1);
-      if (BF16IN) load_raw(t1, s1, bufB);
-      process(bufA, tile, sub);
+      if (BF16IN) load_raw(tile, 1, bufB);
+      process(bufA, tile, 0);
+      const int64_t t1 = next_tile(tile);
+      if (BF16IN) load_raw(t1, 0, bufA);
+      process(bufB, tile, 1);
       tile = t1;
-      sub = s1;
-      if (tile >= ntiles) break;
-      next_pos(t1, s1);
-      if (BF16IN) load_raw(t1, s1, bufA);
-      process(bufB, tile, sub);
-      tile = t1;
-      sub = s1;
     }
   } else {
     // two 32-vector blocks per sub-tile: one code path, the prefetched set
     // is copied (two alternating instances would not fit the registers)
     while (tile < ntiles) {
-      int64_t t1 = tile;
-      int s1 = sub;
-      next_pos(t1, s1);
-      if (BF16IN) load_raw(t1, s1, bufB);
-      process(bufA, tile, sub);
+      const int64_t t1 = next_tile(tile);
+      if (BF16IN) load_raw(t1, 0, bufB);
+      process(bufA, tile, 0);
       if (BF16IN) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -1150,7 +1168,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
           for (int c = 0; c < 8; ++c) bufA[nb][c] = bufB[nb][c];
       }
       tile = t1;
-      sub = s1;
     }
   }
 }
@@ -1415,26 +1432,28 @@ __global__ __launch_bounds__(512, 1) void encode_had_kernel(CodecView cv, Encode
       *reinterpret_cast<uint16_t*>(trec + cv.off_nr + 2 * slot) =
           f16_bits(valid ? sqrtf(rr) * (1.f / 32.f) : 0.f);
   };
-  int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
-  int sub = 0;
-  auto next_pos = [&](int64_t& tl, int& sb) {
-    if (sb + 1 < 2) { ++sb; } else { sb = 0; tl += tstep; }
+  // jobs handed out as in encode_d128_kernel (one tile, both sub-tiles, per
+  // job; from the counter with at least 4 jobs per wave); the counter
+  // starts once the barrier below has passed
+  __shared__ int sJob;
+  const bool dyn = ntiles >= 4 * tstep;
+  auto next_tile = [&](int64_t tl) {
+    if (!dyn) return tl + tstep;  // uniform over the workgroup
+    const int jb = take_job(&sJob, lane);
+    const int r = jb / nwaves;
+    return int64_t(r) * tstep + int64_t(blockIdx.x) * nwaves + (jb - r * nwaves);
   };
+  int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
+  if (threadIdx.x == 0) sJob = nwaves;
+  __syncthreads();
   load_raw(tile, 0, bufA);
   while (tile < ntiles) {
-    int64_t t1 = tile;
-    int s1 = sub;
-    next_pos(t1, s1);
-    load_raw(t1, s1, bufB);
-    process(bufA, tile, sub);
+    load_raw(tile, 1, bufB);
+    process(bufA, tile, 0);
+    const int64_t t1 = next_tile(tile);
+    load_raw(t1, 0, bufA);
+    process(bufB, tile, 1);
     tile = t1;
-    sub = s1;
-    if (tile >= ntiles) break;
-    next_pos(t1, s1);
-    load_raw(t1, s1, bufA);
-    process(bufB, tile, sub);
-    tile = t1;
-    sub = s1;
   }
 }
 
