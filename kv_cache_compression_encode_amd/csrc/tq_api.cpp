@@ -1083,18 +1083,23 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   // splits of 8 tiles, widened while the grid still fills every resident
   // workgroup slot (two per CU): fewer block set-ups and partials for large
   // batches, down to one split per sequence (then no merge pass at all);
-  // never more splits than the workspace holds
+  // never more splits than the workspace holds.  With fewer (sequence, KV
+  // head) pairs than CUs the MFMA kernel runs 8-wave workgroups, one per CU,
+  // on splits of 16 tiles (two per wave, as with 8 tiles over 4 waves), so
+  // that each CU sets up once
   {
     const int64_t ntiles = (int64_t(kv->max_tokens) + kTile - 1) / kTile;
     int cus = 256;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, kcb->device) != hipSuccess) cus = 256;
-    const int64_t slots = 2 * int64_t(cus);
-    int chunk = kDecodeChunkTiles;
+    const bool wide = int64_t(B) * Hkv < cus && decode_mfma_supported(kc, vc, Hq / Hkv);
+    const int64_t slots = (wide ? 1 : 2) * int64_t(cus);
+    int chunk = wide ? 2 * kDecodeChunkTiles : kDecodeChunkTiles;
     while (chunk < 1024 && chunk < ntiles &&
            int64_t(B) * Hkv * ((ntiles + 2 * chunk - 1) / (2 * chunk)) >= slots)
       chunk *= 2;
     da.chunk_tiles = chunk;
     da.nsplit = int(std::max<int64_t>(1, (ntiles + chunk - 1) / chunk));
+    da.waves = wide && da.nsplit > 1 ? 8 : 4;
   }
   da.part = part;
   da.out = out;

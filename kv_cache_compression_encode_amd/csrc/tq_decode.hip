@@ -109,9 +109,14 @@ __device__ __forceinline__ float xor16(float v, int lane) {
   return __uint_as_float((lane & 16) ? r[0] : r[1]);
 }
 
-template <int G, int UB>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
+// NW waves per workgroup: 4 (two workgroups per CU), or 8 (one per CU, for
+// small batches split into many workgroups: the set-up, which loads the
+// columns of Pi and S, then runs once per CU)
+template <int G, int UB, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NT = 64 * NW;  // threads
   constexpr bool SQ = UB == 0;
   constexpr bool SPL = UB == 3;  // outlier-channel split keys, 32 outlier coordinates
   __shared__ __align__(16) float sqr[4][D];
@@ -135,9 +140,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   __shared__ uint32_t slut1[256];
   __shared__ __align__(16) uint32_t slut[256 * 32];
   constexpr int PROW = 64 + 8;  // padded row of the P buffer (bank spread)
-  __shared__ __align__(16) uint16_t sP[4][16][PROW];  // per wave: [query row][token] fp16 weights
-  __shared__ float sm_m[4][4], sm_l[4][4];
-  __shared__ float sacc[4][4][D];
+  __shared__ __align__(16) uint16_t sP[NW][16][PROW];  // per wave: [query row][token] fp16 weights
+  __shared__ float sm_m[NW][4], sm_l[NW][4];
+  __shared__ float sacc[NW][4][D];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -205,12 +210,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   };
   TileRegs& ra = cur;
   TileRegs& rb = nxt;
-  // the raw queries are loaded first (2 values per thread; their latency is
-  // the first the set-up waits for)
-  float qraw[2];
+  // the raw queries are loaded first (512 values over the threads; their
+  // latency is the first the set-up waits for)
+  constexpr int QPT = 4 * D / NT;
+  float qraw[QPT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = threadIdx.x + 256 * u;
+  for (int u = 0; u < QPT; ++u) {
+    const int e = threadIdx.x + NT * u;
     const int gg = e / D, i = e % D;
     const int64_t qi = int64_t(b) * a.Hq + g * G + gg;
     float v = 0.f;
@@ -239,33 +245,34 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // randomized Hadamard keys: q' = H (s q) / sqrt(d) by the wave transform
   // instead of the columns of Pi
   const bool khad = kc.had_sign != nullptr;
-  // thread t takes columns 4 cg .. 4 cg + 3 (cg = t % 32) over rows
-  // 16 rg .. 16 rg + 15 (rg = t / 32) of the transposed matrices, as 16-byte
-  // loads; the 8 row groups' partial sums are added through LDS
+  // thread t takes columns 4 cg .. 4 cg + 3 (cg = t % 32) over the RPT rows
+  // RPT rg .. RPT rg + RPT - 1 (rg = t / 32) of the transposed matrices, as
+  // 16-byte loads; the NRG row groups' partial sums are added through LDS
+  constexpr int NRG = NT / 32, RPT = D / NRG;
   const int cg = threadIdx.x & 31, rg = threadIdx.x >> 5;
-  float4 rc4[16], sc4[16];  // sc4 unused (never loaded) for SpectralQuant keys
+  float4 rc4[RPT], sc4[RPT];  // sc4 unused (never loaded) for SpectralQuant keys
   {
-    const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(16 * rg) * D + 4 * cg;
+    const float* rt = kc.rot_t + size_t(hk) * D * D + size_t(RPT * rg) * D + 4 * cg;
     if (!khad) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) rc4[u] = *reinterpret_cast<const float4*>(rt + size_t(u) * D);
+      for (int u = 0; u < RPT; ++u) rc4[u] = *reinterpret_cast<const float4*>(rt + size_t(u) * D);
     }
     if (!SQ) {
-      const float* st = kc.sketch_t + size_t(16 * rg) * D + 4 * cg;
+      const float* st = kc.sketch_t + size_t(RPT * rg) * D + 4 * cg;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) sc4[u] = *reinterpret_cast<const float4*>(st + size_t(u) * D);
+      for (int u = 0; u < RPT; ++u) sc4[u] = *reinterpret_cast<const float4*>(st + size_t(u) * D);
     }
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) (&sqs[0][0])[threadIdx.x + 256 * u] = qraw[u];  // raw queries, staged in sqs
+  for (int u = 0; u < QPT; ++u) (&sqs[0][0])[threadIdx.x + NT * u] = qraw[u];  // raw queries, staged in sqs
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
-  {
-    const int t = threadIdx.x;  // 256 threads: one value-table entry each
+  if (threadIdx.x < 256) {
+    const int t = threadIdx.x;  // one value-table entry per thread
     slut1[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
   }
-  for (int e = threadIdx.x; e < 4 * 16 * PROW / 8; e += blockDim.x)
+  for (int e = threadIdx.x; e < NW * 16 * PROW / 8; e += blockDim.x)
     reinterpret_cast<u32x4*>(&sP[0][0][0])[e] = u32x4{0u, 0u, 0u, 0u};
-  if (SQ) {
+  if (SQ && threadIdx.x < 256) {
     {
       const uint32_t tw = kc.sq_tail[threadIdx.x];  // dim i's bits 1.. at bits 5i .. 5i + 4
       uint32_t b = 0;
@@ -285,15 +292,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   {
     // q' = Pi q: row-group partial sums into the (not yet filled) value
     // table, then added
-    float* part = reinterpret_cast<float*>(slut);  // [8][4][D]
+    float* part = reinterpret_cast<float*>(slut);  // [NRG][4][D]
+    static_assert(NRG * 4 * D <= 256 * 32, "partials fit the value table");
     // partial sums of the 4 queries over this thread's rows, 4 columns each
-    auto rowgroup = [&](const float4 (&m4)[16], const float (&x)[4][D]) {
+    auto rowgroup = [&](const float4 (&m4)[RPT], const float (&x)[4][D]) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float xv = x[gg][16 * rg + u];
+        for (int u = 0; u < RPT; ++u) {
+          const float xv = x[gg][RPT * rg + u];
           acc.x = fmaf(m4[u].x, xv, acc.x);
           acc.y = fmaf(m4[u].y, xv, acc.y);
           acc.z = fmaf(m4[u].z, xv, acc.z);
@@ -306,16 +314,18 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int e = threadIdx.x; e < 4 * D; e += blockDim.x) {
         float v = 0.f;
 #pragma unroll
-        for (int r8 = 0; r8 < 8; ++r8) v += part[r8 * 4 * D + e];
+        for (int r8 = 0; r8 < NRG; ++r8) v += part[r8 * 4 * D + e];
         y[e / D][e % D] = v;
       }
     };
     if (khad) {
-      // wave w transforms query w
-      float lo = sqs[wave][lane] * kc.had_sign[lane], hi = sqs[wave][lane + 64] * kc.had_sign[lane + 64];
-      fwht128_wave(lo, hi, lane);
-      sqr[wave][lane] = lo * kInvSqrt128;
-      sqr[wave][lane + 64] = hi * kInvSqrt128;
+      // wave w < 4 transforms query w
+      if (wave < 4) {
+        float lo = sqs[wave][lane] * kc.had_sign[lane], hi = sqs[wave][lane + 64] * kc.had_sign[lane + 64];
+        fwht128_wave(lo, hi, lane);
+        sqr[wave][lane] = lo * kInvSqrt128;
+        sqr[wave][lane + 64] = hi * kInvSqrt128;
+      }
     } else {
       rowgroup(rc4, sqs);
       __syncthreads();
@@ -340,8 +350,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     __syncthreads();
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {  // consecutive threads write consecutive 16-byte groups
-    const int e4 = k * 256 + threadIdx.x;
+  for (int k = 0; k < 2048 / NT; ++k) {  // consecutive threads write consecutive 16-byte groups
+    const int e4 = k * NT + threadIdx.x;
     const uint32_t v = slut1[e4 >> 3];
     reinterpret_cast<u32x4*>(slut)[e4] = u32x4{v, v, v, v};
   }
@@ -357,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int i = 0; i < 4; ++i) v += ((sb >> i) & 1) ? sqs[gg][i] : -sqs[gg][i];
       sqtab[gg * kSqtab + 4 * 64 + sb] = v;
     }
-    {  // wave w: sum_{i >= 4} mu_i q'_i of query w
+    if (wave < 4) {  // wave w: sum_{i >= 4} mu_i q'_i of query w
       float v = 0.f;
       for (int i = 4 + lane; i < D; i += 64) v += smuv[i] * sqr[wave][i];
 #pragma unroll
@@ -392,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   // byte -> 8 fp16 +-1 values (element k from bit k): the B operands of the
   // score chain are read from this table instead of being expanded on the VALU
   __shared__ u32x4 spm[256];
-  {
+  if (threadIdx.x < 256) {
     const uint32_t e = threadIdx.x;
     u32x4 r;
 #pragma unroll
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       r[j] = (((e >> (2 * j)) & 1u) ? 0x3C00u : 0xBC00u) | ((((e >> (2 * j + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
     spm[e] = r;
   }
-  for (int f = wave; f < NP * 4; f += 4) {
+  for (int f = wave; f < NP * 4; f += NW) {
     const int p = f / 4, c = f % 4;
     const bool sign_part = p == NP - 1;
     const int r = n;
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
 #pragma unroll
   for (int vb = 0; vb < 8; ++vb) accv[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // tiles tile, tile + 4, ... alternate between two register sets (no copies
+  // tiles tile, tile + NW, ... alternate between two register sets (no copies
   // between them, so nothing waits for the next tile's loads early)
   auto process = [&](const TileRegs& R, int tile) {
     uint32_t kw[4][NP], vw[8][2];
@@ -662,12 +672,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
   };
   // the prefetches are unconditional (clamped to the last tile, a harmless
   // re-read) so that the wait counters stay exact across the loop
-  for (int tile = t_begin + wave; tile < t_end; tile += 8) {
-    load_tile(min(tile + 4, t_end - 1), rb);
+  for (int tile = t_begin + wave; tile < t_end; tile += 2 * NW) {
+    load_tile(min(tile + NW, t_end - 1), rb);
     process(ra, tile);
-    if (tile + 4 >= t_end) break;
-    load_tile(min(tile + 8, t_end - 1), ra);
-    process(rb, tile + 4);
+    if (tile + NW >= t_end) break;
+    load_tile(min(tile + 2 * NW, t_end - 1), ra);
+    process(rb, tile + NW);
   }
   // ---- merge the 4 waves: group-0 lanes hold rows (queries) 0..3 of coord 16vb+n
   if (g16 < 2 && n == 0) {
@@ -684,14 +694,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
       for (int q = 0; q < 4; ++q) sacc[wave][q][16 * vb + n] = accv[vb][q];
   }
   __syncthreads();
-  if (a.nsplit > 1) {
+  // partials for decode_combine (the 8-wave form is only launched with
+  // several splits per sequence)
+  if (NW == 8 || a.nsplit > 1) {
     float* out = a.part + ((int64_t(b) * a.Hkv + g) * a.nsplit + split) * (G * (2 + D));
     for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
       const int gg = e / D, i = e % D;
       float M = -INFINITY;
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][gg]);
       float accs = 0.f, l = 0.f;
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = sm_m[w][gg] == -INFINITY ? 0.f : exp2_le0(sm_m[w][gg] - M);
         accs += f * sacc[w][gg][i];
         l += f * sm_l[w][gg];
@@ -701,15 +713,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
     }
     return;
   }
+  if constexpr (NW == 4) {
   // one split per sequence: normalise and rotate back here,
   // out_i = sum_k Pi_v[k][i] y_k with y = acc / l (the query set-up arrays
   // are free again and hold y and the second half's sums)
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int gg = e / D, i = e % D;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][gg]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][gg]);
     float accs = 0.f, l = 0.f;
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = sm_m[w][gg] == -INFINITY ? 0.f : exp2_le0(sm_m[w][gg] - M);
       accs += f * sacc[w][gg][i];
       l += f * sm_l[w][gg];
@@ -756,6 +769,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(CodecView kc, Codec
         a.out[(int64_t(b) * a.Hq + g * G + gg) * D + i] = o[gg] + sqs[gg][i];
     }
   }
+  }
 }
 
 }  // namespace
@@ -786,8 +800,15 @@ bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G) {
 hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
                               hipStream_t s) {
   const int G = a.Hq / a.Hkv;
+  if (a.waves == 8 && a.nsplit < 2) return hipErrorInvalidValue;  // the 8-wave form writes partials only
   dim3 grid(unsigned(a.nsplit), unsigned(a.Hkv), unsigned(a.B));
-#define TQ_LAUNCH(GG, UU) hipLaunchKernelGGL((decode_mfma_kernel<GG, UU>), grid, dim3(256), 0, s, kv, vv, a)
+#define TQ_LAUNCH(GG, UU)                                                                        \
+  do {                                                                                            \
+    if (a.waves == 8)                                                                             \
+      hipLaunchKernelGGL((decode_mfma_kernel<GG, UU, 8>), grid, dim3(512), 0, s, kv, vv, a);      \
+    else                                                                                          \
+      hipLaunchKernelGGL((decode_mfma_kernel<GG, UU, 4>), grid, dim3(256), 0, s, kv, vv, a);      \
+  } while (0)
   if (kv.outl) {
     if (G == 4) TQ_LAUNCH(4, 3); else if (G == 2) TQ_LAUNCH(2, 3); else TQ_LAUNCH(1, 3);
   } else if (!kv.uniform) {

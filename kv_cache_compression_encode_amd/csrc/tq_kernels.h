@@ -126,6 +126,7 @@ struct DecodeArgs {
   float scale;
   int chunk_tiles;     // tiles per split
   int nsplit;
+  int waves;           // MFMA kernel: waves per workgroup, 4 or 8 (8 only with nsplit > 1)
   int len_add;         // tokens attended = min(seq_lens[b] + len_add, max_tokens)
   // paged records (block_table non-NULL): tile t of set (b, g) is tile
   // t % 2^page_shift of page block_table[(b * Hkv + g) * max_pages + (t >> page_shift)]
