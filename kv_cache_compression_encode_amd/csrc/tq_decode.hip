@@ -541,8 +541,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
     constexpr int spl_c[9] = {0, 1, 0, 2, 0, 3, 1, 2, 3};
     constexpr bool spl_o[9] = {true, false, true, false, true, false, false, false, false};
     auto kbyte = [&](int nb, int k) -> uint32_t {
-      if (SPL) return spl_p[k] == 1 ? kw[nb][1] : (kw[nb][spl_p[k]] >> (8 * spl_c[k])) & 0xffu;
-      return (kw[nb][k >> 2] >> (8 * (k & 3))) & 0xffu;
+      if constexpr (SPL) return spl_p[k] == 1 ? kw[nb][1] : (kw[nb][spl_p[k]] >> (8 * spl_c[k])) & 0xffu;
+      else return (kw[nb][k >> 2] >> (8 * (k & 3))) & 0xffu;
     };
     auto afrag = [&](int k) -> u32x4 { return SPL ? sA[spl_p[k] * 4 + spl_c[k]][lane] : sA[k][lane]; };
     f32x4 accs[4], accso[4];
