@@ -1,5 +1,10 @@
 """Plain CPU oracle of the TurboQuant / SpectralQuant codec (fp64).
 
+Its rotations, sketches, scores and quantizer are plain loops in C
+(tq_loops.c, built with gcc by build_loops.py and loaded through ctypes);
+the rest is numpy, with library routines only for the QR and eigensolves
+that construct Pi.
+
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this module: only the tests, the smoke check and the benchmark's
 ``cpu_baseline`` leg use it.  It shares no code, tables or constants with the
@@ -45,12 +50,63 @@ arithmetic.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional
 
 import numpy as np
 from scipy import special
+
+# ---------------------------------------------------------------------------
+# Plain loops (tq_loops.c): the rotations, sketches, scores and the quantizer
+# below run as textbook fp64 loops, one dot product or one count per output
+# in index order, built with gcc by build_loops.py.
+# ---------------------------------------------------------------------------
+_LOOPS = None
+
+
+def _loops():
+    global _LOOPS
+    if _LOOPS is None:
+        from oracle import build_loops
+        lib = ctypes.CDLL(build_loops.build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.tq_oracle_matmul_nt.argtypes = [dp, dp, dp, i64, i64, i64]
+        lib.tq_oracle_matmul_nt.restype = None
+        lib.tq_oracle_count_le.argtypes = [dp, i64, dp, i64, i64, lp, i64]
+        lib.tq_oracle_count_le.restype = None
+        _LOOPS = lib
+    return _LOOPS
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def dot_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """c[i][j] = sum_t a[i][t] b[j][t] (every row of a against every row of b), by plain loops."""
+    a = np.ascontiguousarray(np.atleast_2d(a), dtype=np.float64)
+    b = np.ascontiguousarray(np.atleast_2d(b), dtype=np.float64)
+    if a.shape[1] != b.shape[1]:
+        raise ValueError("rows of different lengths")
+    c = np.empty((a.shape[0], b.shape[0]))
+    if c.size:
+        _loops().tq_oracle_matmul_nt(_dptr(a), _dptr(b), _dptr(c), a.shape[0], b.shape[0], a.shape[1])
+    return c
+
+
+def count_le(t: np.ndarray, y: np.ndarray) -> np.ndarray:
+    """Number of entries of t that are <= y, for every element of the 1-D array y."""
+    t = np.ascontiguousarray(t, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    out = np.empty(y.shape[0], dtype=np.int64)
+    if y.size:
+        _loops().tq_oracle_count_le(_dptr(t), t.shape[0], _dptr(y), y.shape[0], 1,
+                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 1)
+    return out
 
 # ---------------------------------------------------------------------------
 # Counter-based generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
@@ -394,7 +450,7 @@ def spectralquant_codec(calib: np.ndarray, bitmap, m: int, sketch_seed: int,
         p = _f32(rows)
         x = calib[h]
         u = x / np.linalg.norm(x, axis=1, keepdims=True)
-        y = u @ p.T
+        y = dot_rows(u, p)                        # y = P u per row
         rots.append(p)
         sig.append(np.sqrt(np.mean(y * y, axis=0)))
     if bitmap is None:
@@ -428,12 +484,11 @@ class Encoded:
 def quantize(codec: Codec, y: np.ndarray, head: int) -> np.ndarray:
     """idx_i = number of boundaries t with t <= y_i (ties go to the upper cell)."""
     n, d = y.shape
-    idx = np.empty((n, d), dtype=np.int64)
     if codec.uniform:
-        idx[:] = np.searchsorted(codec.boundaries[head][0], y, side="right")
-    else:
-        for i in range(d):
-            idx[:, i] = np.searchsorted(codec.boundaries[head][i], y[:, i], side="right")
+        return count_le(codec.boundaries[head][0], y.reshape(-1)).reshape(n, d)
+    idx = np.empty((n, d), dtype=np.int64)
+    for i in range(d):
+        idx[:, i] = count_le(codec.boundaries[head][i], y[:, i])
     return idx
 
 
@@ -456,7 +511,7 @@ def encode(codec: Codec, x: np.ndarray, head: int = 0, round_norms: bool = True)
     nx = np.sqrt(np.sum(x * x, axis=1))
     safe = np.where(nx > 0, nx, 1.0)
     u = np.where(nx[:, None] > 0, x / safe[:, None], 0.0)
-    y = u @ codec.rot[head].T                     # y = Pi u
+    y = dot_rows(u, codec.rot[head])              # y = Pi u
     idx = quantize(codec, y, head)
     store = (lambda v: v.astype(np.float16)) if round_norms else (lambda v: v)
     if codec.mode == "mse":
@@ -474,7 +529,7 @@ def residual_sketch(codec: Codec, y: np.ndarray, idx: np.ndarray, head: int = 0)
     chat = dequantize(codec, idx, head)
     r = y[:, :m] - chat[:, :m]                   # residual of the mse stage
     nr = np.sqrt(np.sum(r * r, axis=1))
-    z = r @ codec.sketch.T                       # S r
+    z = dot_rows(r, codec.sketch)                # S r
     return nr, z
 
 
@@ -501,8 +556,8 @@ QJL_CONST = math.sqrt(math.pi / 2)
 def prepare_query(codec: Codec, q: np.ndarray, head: int = 0):
     """q' = Pi q and (prod) q_s = S q'[0:m]."""
     q = np.asarray(q, dtype=np.float64)
-    qr = q @ codec.rot[head].T
-    qs = qr[:, :codec.m] @ codec.sketch.T if codec.mode == "prod" else None
+    qr = dot_rows(q, codec.rot[head])
+    qs = dot_rows(qr[:, :codec.m], codec.sketch) if codec.mode == "prod" else None
     return qr, qs
 
 
@@ -513,10 +568,10 @@ def score(codec: Codec, q: np.ndarray, enc: Encoded, head: int = 0) -> np.ndarra
     qr, qs = prepare_query(codec, q, head)
     chat = dequantize(codec, enc.idx, head)
     nx = enc.nx.astype(np.float64)
-    s = qr @ chat.T
+    s = dot_rows(qr, chat)
     if codec.mode == "prod":
         pm = np.where(enc.signs, 1.0, -1.0)
-        s = s + (qs @ pm.T) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[None, :]
+        s = s + dot_rows(qs, pm) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[None, :]
     return s * nx[None, :]
 
 
@@ -525,15 +580,15 @@ def reconstruct(codec: Codec, enc: Encoded, head: int = 0) -> np.ndarray:
     chat = dequantize(codec, enc.idx, head)
     if codec.mode == "prod":
         pm = np.where(enc.signs, 1.0, -1.0)
-        corr = (pm @ codec.sketch) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[:, None]
+        corr = dot_rows(pm, codec.sketch.T) * (enc.nr.astype(np.float64) * QJL_CONST / codec.m)[:, None]
         chat = chat.copy()
         chat[:, :codec.m] += corr
-    return (chat @ codec.rot[head]) * enc.nx.astype(np.float64)[:, None]
+    return dot_rows(chat, codec.rot[head].T) * enc.nx.astype(np.float64)[:, None]
 
 
 def score_via_reconstruction(codec: Codec, q: np.ndarray, enc: Encoded, head: int = 0):
     """Second scoring path: <q, x_hat>."""
-    return np.asarray(q, dtype=np.float64) @ reconstruct(codec, enc, head).T
+    return dot_rows(np.asarray(q, dtype=np.float64), reconstruct(codec, enc, head))
 
 
 def decode_attention(kcodec: Codec, vcodec: Codec, q: np.ndarray, kenc: List[Encoded],
@@ -554,7 +609,7 @@ def decode_attention(kcodec: Codec, vcodec: Codec, q: np.ndarray, kenc: List[Enc
         s = score(kcodec, q[h:h + 1], kenc[g], kh)[0] * scale
         p = np.exp(s - s.max())
         p /= p.sum()
-        out[h] = p @ reconstruct(vcodec, venc[g], vh)
+        out[h] = dot_rows(p, reconstruct(vcodec, venc[g], vh).T)[0]
     return out
 
 
@@ -856,7 +911,7 @@ def split_decode_attention(kcodec, vcodec, q: np.ndarray, kenc: list, venc: list
         s = sc_(kcodec, q[h:h + 1], kenc[g], g)[0] * scale
         p = np.exp(s - s.max())
         p /= p.sum()
-        out[h] = p @ rec_(vcodec, venc[g], g)
+        out[h] = dot_rows(p, rec_(vcodec, venc[g], g).T)[0]
     return out
 
 

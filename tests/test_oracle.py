@@ -194,6 +194,29 @@ def test_mse_falls_with_bits_and_stays_within_bounds(d):
         prev = D
 
 
+def test_loops_match_their_definitions():
+    # The oracle's loop library against the definitions spelled out in Python
+    # on tiny inputs: every output of dot_rows is the sum of the products of
+    # one row of each operand (a swapped or transposed operand, a dropped
+    # term or a stride slip changes some entry), and count_le counts the
+    # boundaries at or below the value (ties included).
+    rng = np.random.default_rng(17)
+    a = rng.normal(size=(5, 7))
+    b = rng.normal(size=(3, 7))
+    c = o.dot_rows(a, b)
+    assert c.shape == (5, 3)
+    for i in range(5):
+        for j in range(3):
+            ref = 0.0
+            for t in range(7):
+                ref += a[i, t] * b[j, t]
+            assert abs(c[i, j] - ref) <= 1e-13
+    assert o.dot_rows(np.zeros((0, 4)), np.ones((2, 4))).shape == (0, 2)
+    t = np.array([-0.5, 0.0, 0.25, 1.0])
+    y = np.array([-1.0, -0.5, -0.1, 0.0, 0.1, 0.25, 0.9, 1.0, 2.0])
+    assert o.count_le(t, y).tolist() == [sum(1 for tk in t if tk <= v) for v in y] == [0, 1, 1, 2, 2, 3, 3, 4, 4]
+
+
 def test_quantize_matches_brute_force_d8():
     codec = o.turboquant_codec(8, 3, "mse", rot_seed=5)
     rng = np.random.default_rng(0)
