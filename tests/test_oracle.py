@@ -395,6 +395,39 @@ def test_prod_estimator_unbiased_over_sketch():
     assert abs(v.var(ddof=1) / var - 1) < 0.1
 
 
+def test_fp16_sketch_rounding_bias_is_bounded():
+    # The stored sketch is the Gaussian draw rounded to fp32 and then to fp16
+    # (a reading of the pages, which fix no precision).  The QJL estimator
+    # n_r sqrt(pi/2)/m sum_j <s_j, q'> sign<s_j, r> is exactly unbiased for
+    # Gaussian rows s_j (paper review, "Results").  Per row, the paired
+    # difference between the rounded and the exact sketch bounds the mean
+    # shift the rounding causes: it stays below 2^-10 |q'| |r| (the spread of
+    # the estimator over one 64-row sketch is about 0.16 |q'| |r|).  Entry by
+    # entry the rounding is to nearest: within half an fp16 ulp, 2^-11
+    # relative (truncation would reach 2^-10), or 2^-25 absolute below the
+    # fp16 normal range.
+    m = 64
+    rng = np.random.default_rng(41)
+    q, r = rng.normal(size=m), rng.normal(size=m)
+    c = math.sqrt(math.pi / 2) * np.linalg.norm(r)
+    est, diff = [], []
+    for s in range(1000):
+        g = o.gaussian_sketch(m, 9000 + s)
+        st = o.stored_sketch(m, 9000 + s)
+        assert np.all(np.abs(st - g) <= np.maximum(np.abs(g) * 2.0 ** -11, 2.0 ** -25))
+        e_g = c * (g @ q) * np.where(g @ r >= 0, 1.0, -1.0)
+        e_s = c * (st @ q) * np.where(st @ r >= 0, 1.0, -1.0)
+        est.append(e_g)
+        diff.append(e_s - e_g)
+    est, diff = np.concatenate(est), np.concatenate(diff)
+    se_est = est.std(ddof=1) / math.sqrt(len(est))
+    assert abs(est.mean() - q @ r) < 4 * se_est          # the exact sketch is unbiased
+    se = diff.std(ddof=1) / math.sqrt(len(diff))
+    bound = 2.0 ** -10 * np.linalg.norm(q) * np.linalg.norm(r)
+    assert 4 * se < bound                                # the check resolves the bound
+    assert abs(diff.mean()) + 4 * se < bound
+
+
 def test_mse_inner_product_is_biased():
     # Paper review, "Problem": mse-optimal quantizers give biased inner products.
     # At 1 bit and large d the mean of <q, x_hat> over random rotations is
