@@ -288,6 +288,25 @@ tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64
                     void* records, int64_t rs_b, int64_t rs_h, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Keys and values of the same tokens encoded together, as a KV cache is
+ * written ([TQ] "Method", KV-cache setting: every new token's key and value
+ * are quantized online, each by its own codec).  The result is that of
+ * tq_encode(kcb, k, ...) followed by tq_encode(vcb, v, ...), byte for byte:
+ *   k, v     device rows of x_dtype with the same sizes and strides
+ *            (xs_b, xs_h, xs_t as for tq_encode);
+ *   k_records, v_records  device records of each codec, set (b, h) at
+ *            k_records + b*kr_b + h*kr_h (likewise v), 16-byte aligned.
+ * Both codecs must be d = 128 (else TQ_EUNSUPPORTED) on one device (else
+ * TQ_EINVAL); the other errors are tq_encode's, checked for both before any
+ * launch.  bf16 rows with a TurboQuant-prod 3-bit ROW key codec and a
+ * TurboQuant-mse 4-bit COL value codec (dense Pi) run as one launch whose
+ * workgroups take the value tiles as soon as the key tiles leave CUs free;
+ * every other pair runs as the two encodes.  No workspace is needed. */
+tq_status tq_encode_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k, const void* v,
+                       int32_t x_dtype, int64_t batch, int64_t heads, int64_t tokens, int64_t xs_b,
+                       int64_t xs_h, int64_t xs_t, void* k_records, int64_t kr_b, int64_t kr_h,
+                       void* v_records, int64_t vr_b, int64_t vr_h, void* stream);
+
 /* Inner-product scores of nq queries against n ROW records of head `head`:
  *   scores[i][t] = n_x (sum_j q'_j c[idx_j] + n_r sqrt(pi/2)/m sum_j qs_j (2 bit_j - 1)),
  *   q' = Pi q, qs = S q'[0:m] ([TQ] "Method"; estimator of <q, x>).

@@ -17,7 +17,7 @@ from . import _lib as L
 from ._lib import (TQ_BF16, TQ_F32, TQ_LAYOUT_COL, TQ_LAYOUT_ROW, TQ_MSE, TQ_PROD,
                    TQ_ROT_CALIBRATE, TQ_ROT_GIVEN, TQ_ROT_HAAR, TQ_ROT_HADAMARD, TQ_TILE, TQError)
 
-__all__ = ["Codebook", "encode", "append", "score", "decode_attend", "decode_step", "search_topk", "water_fill",
+__all__ = ["Codebook", "encode", "encode_kv", "append", "score", "decode_attend", "decode_step", "search_topk", "water_fill",
            "TQError",
            "TQ_MSE", "TQ_PROD", "TQ_LAYOUT_ROW", "TQ_LAYOUT_COL", "TQ_ROT_HAAR",
            "TQ_ROT_GIVEN", "TQ_ROT_CALIBRATE", "TQ_ROT_HADAMARD", "TQ_TILE"]
@@ -189,6 +189,29 @@ def encode(cb: Codebook, x: torch.Tensor, records: Optional[torch.Tensor] = None
                               ws.data_ptr() if ws is not None else None, ws_bytes,
                               _stream(x.device)), "tq_encode")
     return records
+
+
+def encode_kv(kcb: Codebook, vcb: Codebook, k: torch.Tensor, v: torch.Tensor,
+              k_records: Optional[torch.Tensor] = None, v_records: Optional[torch.Tensor] = None):
+    """Keys k and values v of one shape ([T][d], [H][T][d] or [B][H][T][d], same
+    strides, fp32 or bf16) encoded together (tq_encode_kv): the records of
+    encode(kcb, k) and encode(vcb, v).  Returns (k_records, v_records)."""
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("keys and values need one shape, stride and dtype")
+    lead = 4 - k.dim()
+    k4 = k.reshape((1,) * lead + tuple(k.shape)) if lead else k
+    v4 = v.reshape((1,) * lead + tuple(v.shape)) if lead else v
+    B, H, T, d = k4.shape
+    kper, vper = kcb.records_bytes(T), vcb.records_bytes(T)
+    if k_records is None:
+        k_records = torch.empty(B * H * kper, dtype=torch.uint8, device=k.device)
+    if v_records is None:
+        v_records = torch.empty(B * H * vper, dtype=torch.uint8, device=v.device)
+    s = k4.stride()
+    L.check(L.lib().tq_encode_kv(kcb.handle, vcb.handle, k4.data_ptr(), v4.data_ptr(), _dtype_code(k4),
+                                 B, H, T, s[0], s[1], s[2], k_records.data_ptr(), H * kper, kper,
+                                 v_records.data_ptr(), H * vper, vper, _stream(k.device)), "tq_encode_kv")
+    return k_records, v_records
 
 
 def score(cb: Codebook, q: torch.Tensor, records: torch.Tensor, n: int, head: int = 0) -> torch.Tensor:

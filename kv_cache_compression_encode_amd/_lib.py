@@ -17,7 +17,7 @@ TQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 TQ_MAX_LEVELS = 32
 
 EXPORTED = ["tq_codebook_build", "tq_codebook_free", "tq_water_fill", "tq_append", "tq_codebook_get_info", "tq_codebook_export",
-            "tq_records_bytes", "tq_encode", "tq_score", "tq_decode_attend", "tq_decode_attend_noalloc", "tq_decode_step", "tq_search_topk",
+            "tq_records_bytes", "tq_encode", "tq_encode_kv", "tq_score", "tq_decode_attend", "tq_decode_attend_noalloc", "tq_decode_step", "tq_search_topk",
             "tq_workspace_size", "tq_status_string"]
 
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.tq_records_bytes.restype = i64
     L.tq_encode.argtypes = [p, p, i32, i64, i64, i64, i64, i64, i64, p, i64, i64, p, sz, p]
     L.tq_encode.restype = i32
+    L.tq_encode_kv.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p]
+    L.tq_encode_kv.restype = i32
     L.tq_score.argtypes = [p, p, i64, i32, p, i64, p, p, sz, p]
     L.tq_score.restype = i32
     L.tq_decode_attend.argtypes = [p, p, p, i32, i32, i32, i32, ctypes.POINTER(KVView),

@@ -888,37 +888,71 @@ int64_t tq_records_bytes(const tq_codebook* cb, int64_t n) {
   return ((n + kTile - 1) / kTile) * cb->info.tile_bytes;
 }
 
-tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
-                    int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
-                    void* records, int64_t rs_b, int64_t rs_h, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+// The argument checks of one encode (tq_encode's, short of the workspace) and
+// its kernel arguments; *empty when there is nothing to encode.
+static tq_status encode_check(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
+                              int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
+                              void* records, int64_t rs_b, int64_t rs_h, EncodeArgs* a, bool* empty) {
+  *empty = false;
   if (!cb) return TQ_EINVAL;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
   if (batch < 0 || heads < 0 || tokens < 0) return TQ_EINVAL;
-  if (batch == 0 || heads == 0 || tokens == 0) return TQ_OK;  // nothing to encode
+  if (batch == 0 || heads == 0 || tokens == 0) {  // nothing to encode
+    *empty = true;
+    return TQ_OK;
+  }
   if (!x || !records) return TQ_EINVAL;
   if (xs_b < 0 || xs_h < 0 || xs_t < cb->desc.d) return TQ_EINVAL;
   if (batch * heads > int64_t(65535) * 65535) return TQ_EUNSUPPORTED;
   if (!on_device(cb)) return TQ_EINVAL;
   if (cb->info.num_heads > 1 && heads != cb->info.num_heads) return TQ_EINVAL;
   const int d = cb->desc.d;
-  const bool large = d != 128;
-  if (large && (d % 128 || d > 4096 || !cb->uniform || cb->desc.layout != TQ_LAYOUT_ROW ||
-                (cb->desc.mode == TQ_PROD && cb->m != d)))
+  if (d != 128 && (d % 128 || d > 4096 || !cb->uniform || cb->desc.layout != TQ_LAYOUT_ROW ||
+                   (cb->desc.mode == TQ_PROD && cb->m != d)))
     return TQ_EUNSUPPORTED;
   const int64_t esz = x_dtype == TQ_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(records) || (xs_t * esz) % 16 || (xs_h * esz) % 16 ||
       (xs_b * esz) % 16 || rs_b % 16 || rs_h % 16)
     return TQ_EALIGN;
+  *a = EncodeArgs{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
+                  static_cast<uint8_t*>(records), rs_b, rs_h};
+  return TQ_OK;
+}
+
+tq_status tq_encode(const tq_codebook* cb, const void* x, int32_t x_dtype, int64_t batch,
+                    int64_t heads, int64_t tokens, int64_t xs_b, int64_t xs_h, int64_t xs_t,
+                    void* records, int64_t rs_b, int64_t rs_h, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  EncodeArgs a{};
+  bool empty = false;
+  const tq_status st = encode_check(cb, x, x_dtype, batch, heads, tokens, xs_b, xs_h, xs_t, records, rs_b, rs_h,
+                                    &a, &empty);
+  if (st != TQ_OK || empty) return st;
   const size_t need = tq_workspace_size(cb, TQ_OP_ENCODE, 0, 0, 0);
   if (need > 0 && (!workspace || workspace_bytes < need)) return TQ_EWORKSPACE;
   if (need > 0 && !aligned16(workspace)) return TQ_EALIGN;
   if (hipSetDevice(cb->device) != hipSuccess) return TQ_EDEVICE;
-  EncodeArgs a{x, x_dtype == TQ_BF16, batch, heads, tokens, xs_b, xs_h, xs_t,
-               static_cast<uint8_t*>(records), rs_b, rs_h};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (large) return map_hip(launch_encode_wide(make_view(cb), a, workspace, s));
+  if (cb->desc.d != 128) return map_hip(launch_encode_wide(make_view(cb), a, workspace, s));
   return map_hip(launch_encode_d128(make_view(cb), a, s));
+}
+
+tq_status tq_encode_kv(const tq_codebook* kcb, const tq_codebook* vcb, const void* k, const void* v,
+                       int32_t x_dtype, int64_t batch, int64_t heads, int64_t tokens, int64_t xs_b,
+                       int64_t xs_h, int64_t xs_t, void* k_records, int64_t kr_b, int64_t kr_h,
+                       void* v_records, int64_t vr_b, int64_t vr_h, void* stream) {
+  if (!kcb || !vcb) return TQ_EINVAL;
+  EncodeArgs ka{}, va{};
+  bool empty = false;
+  tq_status st = encode_check(kcb, k, x_dtype, batch, heads, tokens, xs_b, xs_h, xs_t, k_records, kr_b, kr_h,
+                              &ka, &empty);
+  if (st != TQ_OK) return st;
+  st = encode_check(vcb, v, x_dtype, batch, heads, tokens, xs_b, xs_h, xs_t, v_records, vr_b, vr_h, &va, &empty);
+  if (st != TQ_OK || empty) return st;
+  if (kcb->device != vcb->device) return TQ_EINVAL;
+  if (kcb->desc.d != 128 || vcb->desc.d != 128) return TQ_EUNSUPPORTED;
+  if (hipSetDevice(kcb->device) != hipSuccess) return TQ_EDEVICE;
+  return map_hip(launch_encode_kv_d128(make_view(kcb), ka, make_view(vcb), va, static_cast<hipStream_t>(stream)));
 }
 
 

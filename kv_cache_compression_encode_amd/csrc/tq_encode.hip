@@ -326,8 +326,12 @@ __device__ __forceinline__ uint32_t group_or(uint32_t w) {
   return w;
 }
 
+// Encode of the tiles of one workgroup: workgroup bx of the gx that share
+// the (sequence, head) set bh.  The kernels below call it with their grid
+// coordinates.
 template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
-__global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
+__device__ __forceinline__ void encode_d128_body(const CodecView& cv, const EncodeArgs& a, const int bx,
+                                                 const int gx, const int64_t bh) {
   // MODE: 0 mse, 1 prod with a full 128-dim MFMA sketch, 2 prod with a small
   // (m <= 4) sketch on rotated dims 0..m-1 (SpectralQuant selective QJL).
   // SPLIT: outlier-channel split codec in stored order, each group
@@ -348,8 +352,6 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   // 16-level COL codes: bucket table of the boundaries (one compare per coordinate)
   __shared__ float2 sQ[UNIFORM && COL && UB == 4 && MODE == 0 ? kQMax : 1];
 
-  // (sequence, head) set: grid y, continued in grid z past 65535 sets
-  const int64_t bh = blockIdx.y + int64_t(blockIdx.z) * gridDim.y;
   if (bh >= a.batch * a.heads) return;
   const int64_t b = bh / a.heads, h = bh % a.heads;
   const int hc = cv.heads > 1 ? int(h) : 0;
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
   const NibT nibc = nib_transpose_consts(int(threadIdx.x & 7));
 
   const int nwaves = blockDim.x >> 6;
-  const int64_t tstep = int64_t(gridDim.x) * nwaves;
+  const int64_t tstep = int64_t(gx) * nwaves;
   // bf16 input: the raw rows of the next sub-tile are loaded while the
   // current one is processed (register double buffer).
   // Loads are unconditional (rows past the end read the last row instead and
@@ -1085,7 +1087,7 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       }
     }
   };
-  // Jobs of this workgroup: job j is tile (j / nwaves) tstep + blockIdx.x
+  // Jobs of this workgroup: job j is tile (j / nwaves) tstep + bx
   // nwaves + j % nwaves (both of its sub-tiles when NSUB = 2, else one
   // sub-tile).  Wave w starts with job w.  When the workgroup has at least
   // 4 jobs per wave, each further job goes to the wave that asks first (a
@@ -1099,9 +1101,9 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
     if (!dyn) return tl + tstep;  // uniform over the workgroup
     const int jb = take_job(&sJob, lane);
     const int r = jb / nwaves;
-    return int64_t(r) * tstep + int64_t(blockIdx.x) * nwaves + (jb - r * nwaves);
+    return int64_t(r) * tstep + int64_t(bx) * nwaves + (jb - r * nwaves);
   };
-  int64_t tile = int64_t(blockIdx.x) * nwaves + wave;
+  int64_t tile = int64_t(bx) * nwaves + wave;
   if (threadIdx.x == 0) sJob = nwaves;
   // the tables' loads go out first, then the first rows; the tables are
   // stored to LDS as soon as they arrive, with the rows still in flight
@@ -1170,6 +1172,30 @@ __global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, Encod
       tile = t1;
     }
   }
+}
+
+// One codec: gx workgroups per (sequence, head) set along grid x; the sets
+// run along grid y, continued in grid z past 65535.
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
+__global__ __launch_bounds__(512, 1) void encode_d128_kernel(CodecView cv, EncodeArgs a) {
+  encode_d128_body<NB, BF16IN, MODE, COL, UNIFORM, UB, SPLIT>(cv, a, int(blockIdx.x), int(gridDim.x),
+                                                              blockIdx.y + int64_t(blockIdx.z) * gridDim.y);
+}
+
+// Keys and values of the same tokens in one launch (bf16 rows, uniform
+// codecs): a 1-D grid whose first nk = kgx x (key sets) workgroups encode the
+// keys and the rest the values.  Workgroups start in grid order, one per CU
+// (the LDS tables), so the value workgroups fill the CUs the key workgroups
+// leave, instead of waiting for the last of them as a second launch would.
+template <int KMODE, int KUB, int VMODE, bool VCOL, int VUB>
+__global__ __launch_bounds__(512, 1) void encode_kv_d128_kernel(CodecView kcv, EncodeArgs ka, int kgx,
+                                                                CodecView vcv, EncodeArgs va, int vgx) {
+  const int64_t nk = int64_t(kgx) * ka.batch * ka.heads;
+  const int64_t wg = blockIdx.x;
+  if (wg < nk)
+    encode_d128_body<1, true, KMODE, false, true, KUB>(kcv, ka, int(wg % kgx), kgx, wg / kgx);
+  else
+    encode_d128_body<1, true, VMODE, VCOL, true, VUB>(vcv, va, int((wg - nk) % vgx), vgx, (wg - nk) / vgx);
 }
 
 // ---------------------------------------------------------------------------
@@ -1484,30 +1510,75 @@ hipError_t launch_had(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
-hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
-  auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB, SPLIT>;
-  size_t lds = size_t(2) * D * LDS_ROW * 2;
-  if (MODE == 1) lds += size_t(D) * LDS_ROW * 2;
-  if (!UNIFORM && SPLIT != 1) lds += size_t(2) * D * kMaxLevels * 4;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (e != hipSuccess) return e;
+// Dynamic LDS of the d = 128 encode: Pi hi and lo, S for a full sketch, the
+// per-dim tables of non-uniform codecs.
+template <int MODE, bool UNIFORM, int SPLIT>
+constexpr size_t encode_lds() {
+  return size_t(2) * D * LDS_ROW * 2 + (MODE == 1 ? size_t(D) * LDS_ROW * 2 : 0) +
+         (!UNIFORM && SPLIT != 1 ? size_t(2) * D * kMaxLevels * 4 : 0);
+}
+
+// Workgroups per (sequence, head) set: one 8-wave workgroup per CU (the LDS
+// copy of Pi/S) each looping over tiles, as many as the sets leave CUs for,
+// and at least 8 tiles each.
+int64_t encode_gx(const EncodeArgs& a) {
   const int64_t ntiles = (a.tokens + kTile - 1) / kTile;
   const int64_t sets = a.batch * a.heads;
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  // one 8-wave workgroup per CU (the LDS copy of Pi/S), each looping over tiles
-  int64_t gx = (ntiles + 7) / 8;
+  const int64_t gx = (ntiles + 7) / 8;
   const int64_t want = std::max<int64_t>(1, (int64_t(cus) + sets - 1) / sets);
-  gx = std::max<int64_t>(1, std::min(gx, want));
-  hipLaunchKernelGGL(kern, set_grid(gx, sets), dim3(512), lds, s, cv, a);
+  return std::max<int64_t>(1, std::min(gx, want));
+}
+
+template <int NB, bool BF16IN, int MODE, bool COL, bool UNIFORM, int UB, int SPLIT = 0>
+hipError_t launch_one(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
+  auto kern = encode_d128_kernel<NB, BF16IN, MODE, COL, UNIFORM, UB, SPLIT>;
+  const size_t lds = encode_lds<MODE, UNIFORM, SPLIT>();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, set_grid(encode_gx(a), a.batch * a.heads), dim3(512), lds, s, cv, a);
+  return hipGetLastError();
+}
+
+template <int KMODE, int KUB, int VMODE, bool VCOL, int VUB>
+hipError_t launch_kv(const CodecView& kcv, const EncodeArgs& ka, const CodecView& vcv, const EncodeArgs& va,
+                     hipStream_t s) {
+  auto kern = encode_kv_d128_kernel<KMODE, KUB, VMODE, VCOL, VUB>;
+  const size_t lds = std::max(encode_lds<KMODE, true, 0>(), encode_lds<VMODE, true, 0>());
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  const int64_t kgx = encode_gx(ka), vgx = encode_gx(va);
+  const int64_t wgs = (kgx + vgx) * ka.batch * ka.heads;
+  if (wgs > INT32_MAX) return hipErrorNotSupported;
+  hipLaunchKernelGGL(kern, dim3(unsigned(wgs)), dim3(512), lds, s, kcv, ka, int(kgx), vcv, va, int(vgx));
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_encode_kv_d128(const CodecView& kcv, const EncodeArgs& ka, const CodecView& vcv,
+                                 const EncodeArgs& va, hipStream_t s) {
+  // one launch for the prod b = 3 ROW keys and mse b = 4 COL values of bf16
+  // rows with a dense Pi (the KV-cache pair the pages quantize); any other
+  // pair as the two launches of launch_encode_d128
+  const bool pair = ka.x_bf16 && va.x_bf16 && ka.batch == va.batch && ka.heads == va.heads &&
+                    ka.tokens == va.tokens && kcv.uniform && vcv.uniform && !kcv.had_mask && !vcv.had_mask &&
+                    !kcv.outl && !vcv.outl && kcv.mode == TQ_PROD && kcv.m == D &&
+                    kcv.layout == TQ_LAYOUT_ROW && kcv.ubits == 2 && vcv.mode == TQ_MSE &&
+                    vcv.layout == TQ_LAYOUT_COL && vcv.ubits == 4 && vcv.qn >= 2 && vcv.qn <= kQMax;
+  if (pair) {
+    const hipError_t e = launch_kv<1, 2, 0, true, 4>(kcv, ka, vcv, va, s);
+    if (e != hipErrorNotSupported) return e;
+  }
+  const hipError_t e = launch_encode_d128(kcv, ka, s);
+  if (e != hipSuccess) return e;
+  return launch_encode_d128(vcv, va, s);
+}
 
 hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s) {
   const bool col = cv.layout == TQ_LAYOUT_COL;

@@ -71,6 +71,9 @@ struct EncodeArgs {
 };
 
 hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStream_t s);
+// keys and values of the same tokens, in one launch where the pair allows it
+hipError_t launch_encode_kv_d128(const CodecView& kcv, const EncodeArgs& ka, const CodecView& vcv,
+                                 const EncodeArgs& va, hipStream_t s);
 
 // One new vector per (sequence, head) written into slot positions[b] of the
 // existing records (d = 128).

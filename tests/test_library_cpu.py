@@ -177,6 +177,20 @@ def test_argument_errors_before_launch():
     st = lib.tq_encode(cb.handle, ctypes.addressof(buf), 5, 1, 1, 4, 0, 0, 128,
                        ctypes.addressof(buf), 0, 0, None, 0, None)
     assert st == L.TQ_EINVAL
+    # tq_encode_kv: tq_encode's checks on both codecs before any launch
+    a = ctypes.addressof(buf)
+    assert lib.tq_encode_kv(None, cb.handle, a, a, L.TQ_BF16, 1, 1, 4, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_EINVAL
+    assert lib.tq_encode_kv(cb.handle, cb.handle, a, a, L.TQ_BF16, 1, 1, 4, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_EINVAL  # host-only codebooks
+    assert lib.tq_encode_kv(cb.handle, cb.handle, a, None, L.TQ_BF16, 1, 1, 4, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_EINVAL
+    assert lib.tq_encode_kv(cb.handle, cb.handle, a, a, 5, 1, 1, 4, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_EINVAL
+    assert lib.tq_encode_kv(cb.handle, cb.handle, a, a, L.TQ_BF16, 1, 1, -1, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_EINVAL
+    assert lib.tq_encode_kv(cb.handle, cb.handle, a, a, L.TQ_BF16, 1, 1, 0, 0, 0, 128, a, 0, 0, a, 0, 0,
+                            None) == L.TQ_OK  # nothing to encode
     assert lib.tq_workspace_size(cb.handle, L.TQ_OP_ENCODE, 0, 0, 0) == 0
     wide = tq.Codebook(1536, tq.TQ_PROD, 2, device=-1)
     assert lib.tq_workspace_size(wide.handle, L.TQ_OP_ENCODE, 0, 0, 0) > 0
