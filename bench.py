@@ -12,7 +12,8 @@ its inputs from HBM.  Reported value: keys per second through the whole step.
 
 Other workloads (--workload): gqa_outlier (the same layer with 2.5-bit
 outlier-split keys: per KV head the 32 largest-RMS channels at 3 bits, the
-other 96 at 2 bits, two TurboQuant instances), small (4096 fp32 vectors, 16 queries),
+other 96 at 2 bits, two TurboQuant instances), gqa_outlier_kv (2.5-bit split
+keys and values), small (4096 fp32 vectors, 16 queries),
 bulk_prefill (32 layers x 8 heads x 131072 tokens), sq_decode (SpectralQuant
 keys, 64 sequences x 8192 tokens), vector_search (1e6 x 1536 database, 1024
 queries, top-10).  Each prints one JSON line of the same shape.
@@ -38,6 +39,7 @@ NLAYERS = 16
 # Algorithmic bytes per vector: input row + record bytes (codes, signs, fp16 norms).
 K_REC, V_REC = 52, 66
 K_REC_SPLIT = 44                     # split keys: 16 + 4 code bytes, 16 sign bytes, 4 fp16 norms
+V_REC_SPLIT = 40                     # split values: 16 + 16 + 4 code bytes, 2 fp16 norms
 K_ENC_BYTES = 2 * D + K_REC          # 308 B per key
 V_ENC_BYTES = 2 * D + V_REC          # 322 B per value
 DEC_BYTES = K_REC + V_REC            # 118 B per cached token-head read by decode
@@ -57,7 +59,8 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=None)
     p.add_argument("--workload", default="gqa_layer",
-                   choices=["gqa_layer", "gqa_outlier", "small", "bulk_prefill", "sq_decode", "vector_search"])
+                   choices=["gqa_layer", "gqa_outlier", "gqa_outlier_kv", "small", "bulk_prefill", "sq_decode",
+                            "vector_search"])
     p.add_argument("--bits", type=int, default=2, help="vector_search: TurboQuant-prod bits (2 or 4)")
     p.add_argument("--rotation", default="haar", choices=["haar", "hadamard"],
                    help="gqa_layer / bulk_prefill: dense seeded Haar Pi (default) or the randomized "
@@ -160,6 +163,29 @@ def cpu_baseline_gqa_outlier():
     reps, el = _time_loop(run)
     return {"value": reps * n / el, "unit": "keys/s", "cores": _cores(), "kind": "oracle",
             "sample": f"1 kv head x {n} tokens (split encode K, encode V, 4-head decode), {reps} reps in {el:.1f} s"}
+
+
+def cpu_baseline_gqa_outlier_kv():
+    """The oracle on a bounded sample: one KV head, 4096 tokens, split encode
+    of K and of V, then the 4 query heads' decode step."""
+    import torch
+    import synth
+    from oracle import tq_oracle as o
+    n = 4096
+    law = synth.KVLaw(1, D, 205)
+    k = synth.kv_cache(1, 1, n, D, 201, law)[0, 0].double().numpy()
+    v = synth.kv_cache(1, 1, n, D, 251, law)[0, 0].double().numpy()
+    q = synth.kv_queries(1, 4, 1, D, 202, law)[0].double().numpy()
+    ch = outlier_channels(torch, law, 1)
+    kc = o.outlier_split_codec(D, ch, 3, 2, "prod", rot_seed=203, sketch_seed=204)
+    vc = o.outlier_split_codec(D, ch, 3, 2, "mse", rot_seed=213)
+
+    def run():
+        ke, ve = o.split_encode(kc, k), o.split_encode(vc, v)
+        o.split_decode_attention(kc, vc, q, [ke], [ve], 1 / math.sqrt(D))
+    reps, el = _time_loop(run)
+    return {"value": reps * n / el, "unit": "keys/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"1 kv head x {n} tokens (split encode K and V, 4-head decode), {reps} reps in {el:.1f} s"}
 
 
 def cpu_baseline_small():
@@ -328,7 +354,7 @@ def hbm_roof(workload, name, ms, nbytes, note=None):
 
 
 # ------------------------------------------------------------ workloads
-def run_gqa_layer(args, torch, tq, synth, split=False):
+def run_gqa_layer(args, torch, tq, synth, split=False, split_values=False):
     dev = torch.device("cuda:0")
     law = synth.KVLaw(HKV, D, 205)
     K = [synth.kv_cache(1, HKV, T, D, 201 + 1000 * l, law, device=dev)[0] for l in range(NLAYERS)]
@@ -340,9 +366,15 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
                           outlier_channels=outlier_channels(torch, law, HKV), outlier_bits=3)
     else:
         kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204, **rot_kw(tq))
-    vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
+    if split_values:
+        # 2.5-bit values as well: the same channel split, mse, row records
+        vcb = tq.Codebook(D, tq.TQ_MSE, 2, seed_rotation=213, outlier_channels=outlier_channels(torch, law, HKV),
+                          outlier_bits=3)
+    else:
+        vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
     k_rec = K_REC_SPLIT if split else K_REC
-    assert kcb.tile_bytes == 64 * k_rec and vcb.tile_bytes == 64 * V_REC
+    v_rec = V_REC_SPLIT if split_values else V_REC
+    assert kcb.tile_bytes == 64 * k_rec and vcb.tile_bytes == 64 * v_rec
     krec = [torch.empty(HKV * kcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
     vrec = [torch.empty(HKV * vcb.records_bytes(T), dtype=torch.uint8, device=dev) for _ in range(NLAYERS)]
     out = torch.empty(1, HQ, D, dtype=torch.float32, device=dev)
@@ -379,8 +411,8 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
                                                      page_tiles=page_tiles),
                        args.steps, args.warmup)
     nk = HKV * T
-    nbytes = {"encode_keys": nk * (2 * D + k_rec), "encode_values": nk * V_ENC_BYTES,
-              "encode_kv": nk * (2 * D + k_rec + V_ENC_BYTES), "decode_attend": nk * (k_rec + V_REC)}
+    nbytes = {"encode_keys": nk * (2 * D + k_rec), "encode_values": nk * (2 * D + v_rec),
+              "encode_kv": nk * (4 * D + k_rec + v_rec), "decode_attend": nk * (k_rec + v_rec)}
     dom = max(t, key=lambda k: t[k])
     tall = {**t, **t1}
     bd = {k: {"ms": tall[k], "GBps": nbytes[k] / (tall[k] * 1e-3) / 1e9,
@@ -388,20 +420,25 @@ def run_gqa_layer(args, torch, tq, synth, split=False):
     keys_desc = ("K outlier-channel split, 2.5 bits (per KV head the 32 largest-RMS channels of a 2048-token "
                  "calibration sample: TurboQuant-prod b=3; the other 96: b=2; row records, 44 B/key)"
                  if split else "K TurboQuant-prod b=3 (row records)")
-    roof = hbm_roof("gqa_outlier" if split else "gqa_layer", dom, t[dom], nbytes[dom])
+    vals_desc = ("V outlier-channel split, 2.5 bits (the same channels: TurboQuant-mse b=3 on them, b=2 "
+                 "on the other 96; row records, 40 B/value; decode on the general kernel)"
+                 if split_values else "V TurboQuant-mse b=4 (col records)")
+    wname = "gqa_outlier_kv" if split_values else ("gqa_outlier" if split else "gqa_layer")
+    roof = hbm_roof(wname, dom, t[dom], nbytes[dom])
     res = result(args, "compressed-key scoring keys/s & KV encode GB/s at d=128, % of HBM roofline",
                  nk / (ms_step * 1e-3), "keys/s", ms_step,
-                 {"workload": rot_note(("gqa_outlier" if split else "gqa_decode_layer") +
+                 {"workload": rot_note(("gqa_decode_layer" if wname == "gqa_layer" else wname) +
                                        ": 32 q / 8 kv heads, d=128, 32768 tokens, batch 1, "
-                                       f"bf16 K/V; {keys_desc}, V TurboQuant-mse b=4 "
-                                       "(col records); step = encode K and V (one tq_encode_kv call) + "
-                                       "decode attention"),
+                                       f"bf16 K/V; {keys_desc}, {vals_desc}; step = encode K and V "
+                                       "(one tq_encode_kv call) + decode attention"),
                   "layers_cycled": NLAYERS},
                  "f32 (split-f16 MFMA)", roof, bd,
                  {"decode_keys_per_s": nk / (t["decode_attend"] * 1e-3),
                   "append_kv_ms": append_ms,
                   "decode_step_paged_ms": step_ms,
                   "encode_GBps": nbytes["encode_kv"] / (t["encode_kv"] * 1e-3) / 1e9})
+    if split_values:
+        return res, cpu_baseline_gqa_outlier_kv
     return res, (cpu_baseline_gqa_outlier if split else cpu_baseline_gqa)
 
 
@@ -598,7 +635,8 @@ def run_search(args, torch, tq, synth):
     return res, lambda: cpu_baseline_search(args.bits)
 
 
-DEFAULT_STEPS = {"gqa_layer": (200, 20), "gqa_outlier": (200, 20), "small": (200, 10), "bulk_prefill": (10, 2),
+DEFAULT_STEPS = {"gqa_layer": (200, 20), "gqa_outlier": (200, 20), "gqa_outlier_kv": (200, 20), "small": (200, 10),
+                 "bulk_prefill": (10, 2),
                  "sq_decode": (200, 20),
                  "vector_search": (3, 1)}
 
@@ -624,7 +662,8 @@ def main():
     import kv_cache_compression_encode_amd as tq
     import synth
     run = {"gqa_layer": run_gqa_layer, "small": run_small,
-           "gqa_outlier": lambda *a: run_gqa_layer(*a, split=True), "bulk_prefill": run_bulk,
+           "gqa_outlier": lambda *a: run_gqa_layer(*a, split=True),
+           "gqa_outlier_kv": lambda *a: run_gqa_layer(*a, split=True, split_values=True), "bulk_prefill": run_bulk,
            "sq_decode": run_sq, "vector_search": run_search}[args.workload]
     res, baseline = run(args, torch, tq, synth)
     if not args.no_cpu_baseline:

@@ -351,7 +351,12 @@ typedef struct {
  *   out_{b,h} = sum_t softmax_t(logit) * v_hat_{b,g,t},
  *   v_hat = n_v Pi_v^T c_v[idx] (mse reconstruction of the value).
  *   kcb      ROW codec of the keys (num_heads 1 or Hkv);
- *   vcb      COL mse codec of the values (num_heads 1 or Hkv); same d = 128.
+ *   vcb      mse codec of the values (num_heads 1 or Hkv), d = 128: COL records
+ *            of a uniform codec with up to 4 index bits, or ROW records of a
+ *            uniform codec or of an outlier-channel split one (each stored
+ *            coordinate scaled by its group's norm; [TQ] "Method": the
+ *            KV-cache experiments split the channels of keys and values);
+ *            other value codecs give TQ_EUNSUPPORTED.
  *   q        device [B][Hq][d] of q_dtype;  out device fp32 [B][Hq][d].
  *   workspace >= tq_workspace_size(kcb, TQ_OP_DECODE, B*Hq, max_tokens, Hkv). */
 /* A sequence with no tokens (seq_lens[b] = 0, or max_tokens = 0) gets an

@@ -1051,8 +1051,10 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || kv->max_tokens < 0) return TQ_EINVAL;
   if (!on_device(kcb) || !on_device(vcb) || kcb->device != vcb->device) return TQ_EINVAL;
   if (kcb->desc.d != 128 || vcb->desc.d != 128) return TQ_EUNSUPPORTED;
-  if (kcb->desc.layout != TQ_LAYOUT_ROW || vcb->desc.layout != TQ_LAYOUT_COL ||
-      vcb->desc.mode != TQ_MSE || !vcb->uniform || vcb->ubits > 4)
+  // values: mse, as COL records of a uniform codec with up to 4 index bits,
+  // or as ROW records of a uniform or an outlier-channel split codec
+  if (kcb->desc.layout != TQ_LAYOUT_ROW || vcb->desc.mode != TQ_MSE) return TQ_EUNSUPPORTED;
+  if (vcb->desc.layout == TQ_LAYOUT_COL ? (!vcb->uniform || vcb->ubits > 4) : !(vcb->uniform || vcb->outlier > 0))
     return TQ_EUNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_EUNSUPPORTED;

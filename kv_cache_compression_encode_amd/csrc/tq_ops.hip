@@ -324,11 +324,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
   __shared__ float sqr[G][D];
   __shared__ float sqs[G][D];
   __shared__ float skcen[D * kMaxLevels];
-  __shared__ float svcen[kMaxLevels];
+  __shared__ float svcen[D * kMaxLevels];  // uniform values: the first kMaxLevels
   __shared__ float spw[4][G][kTile];
+  __shared__ float spwo[4][G][kTile];  // split values: weights times the outlier group's norm
   __shared__ float sm_m[4][G], sm_l[4][G];
   __shared__ float sacc[4][G][D];
   __shared__ int16_t sbp[kMaxBits * D];  // split keys: bit positions of the index bits
+  __shared__ int16_t svbp[kMaxBits * D];  // non-uniform ROW values: bit positions of the index bits
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int mk = kc.mode == TQ_PROD ? kc.m : 0;
@@ -347,8 +349,13 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
     for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x)
       skcen[e] = kc.cen[size_t(hk) * D * kMaxLevels + e];
   }
-  for (int e = threadIdx.x; e < kMaxLevels; e += blockDim.x)
-    svcen[e] = vc.uniform ? vc.ucen[e] : vc.cen[size_t(hv) * D * kMaxLevels + e];
+  if (vc.uniform) {
+    for (int e = threadIdx.x; e < kMaxLevels; e += blockDim.x) svcen[e] = vc.ucen[e];
+  } else {
+    for (int e = threadIdx.x; e < D * kMaxLevels; e += blockDim.x)
+      svcen[e] = vc.cen[size_t(hv) * D * kMaxLevels + e];
+    for (int e = threadIdx.x; e < kMaxBits * D; e += blockDim.x) svbp[e] = vc.bitpos[e];
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -447,6 +454,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
     for (int gg = 0; gg < G; ++gg) sc[gg] = nx * (s[gg] + coef * sg[gg]);
     }
     const float nv = f16_to_f32(*reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * lane));
+    const float nvo = vc.outl ? f16_to_f32(*reinterpret_cast<const uint16_t*>(vt + vc.off_nxo + 2 * lane)) : 0.f;
     // ---- online softmax
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
@@ -460,9 +468,40 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(CodecView kc, Codec
       acc1[gg] *= alpha;
       mrun[gg] = mnew;
       spw[wave][gg][lane] = p * nv;
+      if (vc.outl) spwo[wave][gg][lane] = p * nvo;
     }
     __builtin_amdgcn_wave_barrier();
-    // ---- values (lane = dims lane, lane + 64; index-major col fields)
+    // ---- values (lane = dims lane, lane + 64)
+    if (vc.layout == TQ_LAYOUT_ROW) {
+      // row records (any uniform codec, or a split one): the index of
+      // (token t, stored coordinate i) from the planes of t's row; a split
+      // codec scales each coordinate by its group's norm (stored coordinate
+      // i is an outlier one when i % 32 < o4, the same for i and i + 64)
+      const bool og = vc.outl && (lane & 31) < vc.o4;
+      const float(*w_)[kTile] = og ? spwo[wave] : spw[wave];
+      auto vidx = [&](int t, int dim) -> int {
+        if (vc.uniform) return row_index_uniform(vt, t, dim, D, vc.ubits);
+        int idx = (vt[size_t(t) * 16 + (dim >> 3)] >> (dim & 7)) & 1;
+        for (int p = 1; p < kMaxBits; ++p) {
+          const int pos = svbp[p * D + dim];
+          if (pos >= 0) idx |= row_bit(vt, t, pos, vc.code_bytes) << p;
+        }
+        return idx;
+      };
+      const int l0 = vc.uniform ? 0 : lane * kMaxLevels, l1 = vc.uniform ? 0 : (lane + 64) * kMaxLevels;
+      for (int t = 0; t < kTile; ++t) {
+        const float c0 = svcen[l0 + vidx(t, lane)], c1 = svcen[l1 + vidx(t, lane + 64)];
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          const float w = w_[gg][t];
+          acc0[gg] = fmaf(w, c0, acc0[gg]);
+          acc1[gg] = fmaf(w, c1, acc1[gg]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
+    // index-major col fields
     const int vb = vc.ubits;
     const uint8_t* f0 = vt + size_t(lane) * 8 * vb;
     const uint8_t* f1 = vt + size_t(lane + 64) * 8 * vb;

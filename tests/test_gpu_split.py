@@ -268,3 +268,138 @@ def test_gqa_outlier_full_size():
     err = np.max(np.abs(out - ref)) / nvmax
     say(f"split full layer decode: max |out - ref| / max n_v = {err:.3g}")
     assert err <= 1e-3
+
+
+def _decode_split_values(B, Hq, Hkv, T, seq_lens, kbits=(3, 2), vbits=(3, 2), split_keys=True):
+    """Decode over values of an outlier-split mse codec (ROW records; the
+    paper review's KV-cache setting splits the values' channels too)."""
+    law = synth.KVLaw(Hkv, 128, 955)
+    K = synth.kv_cache(B, Hkv, T, 128, 951, law)
+    V = synth.kv_cache(B, Hkv, T, 128, 952, law)
+    q = synth.kv_queries(B, Hq, Hkv, 128, 953, law)
+    ch = outlier_channels(law, Hkv, seed=960)
+    if split_keys:
+        kcb, kc = codecs(ch, bits=kbits)
+        kenc = lambda x, g: o.split_encode(kc, x, head=g)
+        kpack = lambda e: o.split_pack(kc, e)
+        ktake = lambda e, n: o.SplitEncoded(take(e.o, n), take(e.r, n))
+    else:
+        kcb = tq.Codebook(128, tq.TQ_PROD, kbits[0], seed_rotation=211, seed_sketch=212)
+        kc = o.turboquant_codec(128, kbits[0], "prod", rot_seed=211, sketch_seed=212)
+        kenc = lambda x, g: o.encode(kc, x)
+        kpack = lambda e: o.pack(kc, e)
+        ktake = take
+    vcb, vc = codecs(ch, bits=vbits, mode="mse", seeds=(957, 958))
+    ke = [[kenc(K[b, g].double().numpy(), g) for g in range(Hkv)] for b in range(B)]
+    ve = [[o.split_encode(vc, V[b, g].double().numpy(), head=g) for g in range(Hkv)] for b in range(B)]
+    kbuf = np.concatenate([kpack(e) for row in ke for e in row])
+    vbuf = np.concatenate([o.split_pack(vc, e) for row in ve for e in row])
+    # the value records as the GPU encodes them match the oracle's
+    gv = tq.encode(vcb, V.to(DEV)).cpu().numpy()
+    per = vcb.records_bytes(T)
+    for b in range(B):
+        for g in range(Hkv):
+            got = o.split_unpack(vc, gv[(b * Hkv + g) * per:(b * Hkv + g + 1) * per], T)
+            check_split(vc, ve[b][g], got)
+    scale = 1 / math.sqrt(128)
+    ref = np.zeros((B, Hq, 128))
+    for b in range(B):
+        L_ = seq_lens[b]
+        if L_ == 0:
+            continue
+        kk = [ktake(e, L_) for e in ke[b]]
+        vv = [o.SplitEncoded(take(e.o, L_), take(e.r, L_)) for e in ve[b]]
+        ref[b] = o.split_decode_attention(kc, vc, q[b].double().numpy(), kk, vv, scale)
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), up(kbuf), up(vbuf), T, Hkv, scale,
+                           seq_lens=torch.tensor(seq_lens, dtype=torch.int32, device=DEV)).cpu().numpy()
+    nvmax = max(max(float(np.max(e.o.nx.astype(np.float64))), float(np.max(e.r.nx.astype(np.float64))))
+                for row in ve for e in row)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"split-value decode B={B} Hq={Hq} Hkv={Hkv} T={T} k={kbits} v={vbits} split keys={split_keys}: "
+        f"max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3
+    if any(L_ == 0 for L_ in seq_lens):
+        assert not np.any(out[[b for b in range(B) if seq_lens[b] == 0]])
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens,kbits,vbits,sk", [
+    (2, 8, 2, 700, [700, 129], (3, 2), (3, 2), True),   # 2.5-bit K and V
+    (3, 4, 4, 300, [300, 0, 65], (3, 2), (4, 3), True),  # 3.5-bit values, an empty sequence
+    (1, 2, 1, 1000, [1000], (3, 3), (2, 1), False),      # plain prod keys, 1.5-bit values
+])
+def test_split_value_decode(B, Hq, Hkv, T, lens, kbits, vbits, sk):
+    _decode_split_values(B, Hq, Hkv, T, lens, kbits, vbits, sk)
+
+
+def test_row_value_decode():
+    # values in ROW records of a uniform mse codec (any index bits) on the
+    # general decode kernel
+    B, Hq, Hkv, T = 2, 8, 2, 500
+    lens = [500, 333]
+    law = synth.KVLaw(Hkv, 128, 965)
+    K = synth.kv_cache(B, Hkv, T, 128, 961, law)
+    V = synth.kv_cache(B, Hkv, T, 128, 962, law)
+    q = synth.kv_queries(B, Hq, Hkv, 128, 963, law)
+    kcb = tq.Codebook(128, tq.TQ_PROD, 3, seed_rotation=966, seed_sketch=967)
+    kc = o.turboquant_codec(128, 3, "prod", rot_seed=966, sketch_seed=967)
+    for vb in (3, 4):
+        say(f"row-value decode b={vb}")
+        vcb = tq.Codebook(128, tq.TQ_MSE, vb, seed_rotation=968)
+        vc = o.turboquant_codec(128, vb, "mse", rot_seed=968)
+        kb = tq.encode(kcb, K.to(DEV))
+        vbuf = tq.encode(vcb, V.to(DEV))
+        kper, vper = kcb.records_bytes(T), vcb.records_bytes(T)
+        kcpu, vcpu = kb.cpu().numpy(), vbuf.cpu().numpy()
+        scale = 1 / math.sqrt(128)
+        out = tq.decode_attend(kcb, vcb, q.to(DEV), kb, vbuf, T, Hkv, scale,
+                               seq_lens=torch.tensor(lens, dtype=torch.int32, device=DEV)).cpu().numpy()
+        nvmax, err = 0.0, 0.0
+        for b in range(B):
+            ke = [o.unpack(kc, kcpu[(b * Hkv + g) * kper:(b * Hkv + g + 1) * kper], lens[b]) for g in range(Hkv)]
+            ve = [o.unpack(vc, vcpu[(b * Hkv + g) * vper:(b * Hkv + g + 1) * vper], lens[b]) for g in range(Hkv)]
+            for g in range(Hkv):
+                check_encoded(vc, o.encode(vc, V[b, g, :lens[b]].double().numpy()), ve[g])
+            ref = o.decode_attention(kc, vc, q[b].double().numpy(), ke, ve, scale)
+            nvmax = max(nvmax, max(float(np.max(e.nx.astype(np.float64))) for e in ve))
+            err = max(err, float(np.max(np.abs(out[b] - ref))))
+        say(f"row-value decode b={vb}: max |out - ref| / max n_v = {err / nvmax:.3g}")
+        assert err / nvmax <= 1e-3
+
+
+def test_gqa_outlier_kv_full_size():
+    """2.5-bit keys and values (both split: 32 outlier channels at 3 bits, 96
+    at 2) on the full layer, 32 q / 8 kv heads, 32768 tokens: the GPU value
+    records against the oracle, then the decode step."""
+    Hq, Hkv, T = 32, 8, 32768
+    say("split K+V full layer: generate")
+    law = synth.KVLaw(Hkv, 128, 205)
+    K = synth.kv_cache(1, Hkv, T, 128, 201, law)[0]
+    V = synth.kv_cache(1, Hkv, T, 128, 251, law)[0]
+    q = synth.kv_queries(1, Hq, Hkv, 128, 202, law)
+    ch = outlier_channels(law, Hkv)
+    kcb, kc = codecs(ch, seeds=(203, 204))
+    vcb, vc = codecs(ch, mode="mse", seeds=(213, 214))
+    say("split K+V full layer: encode")
+    kb, vb = tq.encode_kv(kcb, vcb, K.to(torch.bfloat16).to(DEV), V.to(torch.bfloat16).to(DEV))
+    kb, vb = kb.cpu().numpy(), vb.cpu().numpy()
+    kper, vper = kcb.records_bytes(T), vcb.records_bytes(T)
+    ke, ve, tot = [], [], 0
+    for h in range(Hkv):
+        xk = K[h].to(torch.bfloat16).double().numpy()
+        xv = V[h].to(torch.bfloat16).double().numpy()
+        rk, rv = o.split_encode(kc, xk, head=h), o.split_encode(vc, xv, head=h)
+        st = check_split(vc, rv, o.split_unpack(vc, vb[h * vper:(h + 1) * vper], T))
+        tot += sum(v["band_code_flips"] for v in st.values())
+        ke.append(o.split_unpack(kc, kb[h * kper:(h + 1) * kper], T))
+        ve.append(o.split_unpack(vc, vb[h * vper:(h + 1) * vper], T))
+    say("value band flips", tot)
+    say("split K+V full layer: decode parity")
+    scale = 1 / math.sqrt(128)
+    ref = o.split_decode_attention(kc, vc, q[0].double().numpy(), ke, ve, scale)
+    out = tq.decode_attend(kcb, vcb, q.to(DEV), torch.from_numpy(kb).to(DEV), torch.from_numpy(vb).to(DEV),
+                           T, Hkv, scale).cpu().numpy()[0]
+    nvmax = max(max(float(np.max(e.o.nx.astype(np.float64))), float(np.max(e.r.nx.astype(np.float64))))
+                for e in ve)
+    err = np.max(np.abs(out - ref)) / nvmax
+    say(f"split K+V full layer decode: max |out - ref| / max n_v = {err:.3g}")
+    assert err <= 1e-3
