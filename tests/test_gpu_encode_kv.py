@@ -97,3 +97,17 @@ def test_encode_kv_two_launch_pairs(case):
     kr, vr, k1, v1 = both_ways(kcb, vcb, K, V)
     assert np.array_equal(kr, k1)
     assert np.array_equal(vr, v1)
+
+
+def test_encode_kv_many_sets():
+    # 2 x 32800 (sequence, head) sets of one token: the one-launch grid holds
+    # 131200 workgroups along x; every set against the single encodes
+    B, H = 2, 32800
+    say(f"encode_kv: {B} x {H} sets of one token")
+    g = torch.Generator().manual_seed(23)
+    K = torch.randn(B, H, 1, 128, generator=g).to(torch.bfloat16).to(DEV)
+    V = torch.randn(B, H, 1, 128, generator=g).to(torch.bfloat16).to(DEV)
+    kcb, vcb = gqa_codecs()
+    kr, vr, k1, v1 = both_ways(kcb, vcb, K, V)
+    assert np.array_equal(kr, k1)
+    assert np.array_equal(vr, v1)

@@ -403,3 +403,48 @@ def test_gqa_outlier_kv_full_size():
     err = np.max(np.abs(out - ref)) / nvmax
     say(f"split K+V full layer decode: max |out - ref| / max n_v = {err:.3g}")
     assert err <= 1e-3
+
+
+def test_split_kv_decode_step():
+    # append-on-decode with split keys and split values: each step writes the
+    # new key and value into slot seq_lens[b] (split ROW records, tq_append)
+    # and attends over seq_lens[b] + 1 tokens
+    B, H, Hq, cap, steps = 2, 2, 8, 200, 3
+    L0 = [0, 130]
+    law = synth.KVLaw(H, 128, 975)
+    K = synth.kv_cache(B, H, cap, 128, 971, law)
+    V = synth.kv_cache(B, H, cap, 128, 972, law)
+    ch = outlier_channels(law, H, seed=980)
+    kcb, kc = codecs(ch, seeds=(973, 974))
+    vcb, vc = codecs(ch, mode="mse", seeds=(976, 977))
+    kf = {(b, h): o.split_encode(kc, K[b, h].double().numpy(), head=h) for b in range(B) for h in range(H)}
+    vf = {(b, h): o.split_encode(vc, V[b, h].double().numpy(), head=h) for b in range(B) for h in range(H)}
+    kper, vper = kcb.records_bytes(cap), vcb.records_bytes(cap)
+    kr, vr = np.zeros(B * H * kper, np.uint8), np.zeros(B * H * vper, np.uint8)
+    for b in range(B):
+        for h in range(H):
+            if L0[b]:
+                p = o.split_pack(kc, o.SplitEncoded(take(kf[b, h].o, L0[b]), take(kf[b, h].r, L0[b])))
+                kr[(b * H + h) * kper:(b * H + h) * kper + len(p)] = p
+                p = o.split_pack(vc, o.SplitEncoded(take(vf[b, h].o, L0[b]), take(vf[b, h].r, L0[b])))
+                vr[(b * H + h) * vper:(b * H + h) * vper + len(p)] = p
+    kr, vr = up(kr), up(vr)
+    scale = 1 / math.sqrt(128)
+    for s_ in range(steps):
+        lens = [L0[b] + s_ for b in range(B)]
+        q = synth.kv_queries(B, Hq, H, 128, 985 + s_, law)
+        kn = torch.stack([K[b, :, lens[b]] for b in range(B)]).to(DEV)
+        vn = torch.stack([V[b, :, lens[b]] for b in range(B)]).to(DEV)
+        out = tq.decode_step(kcb, vcb, q.to(DEV), kn, vn, kr, vr, cap, H, scale,
+                             torch.tensor(lens, dtype=torch.int32, device=DEV)).cpu().numpy()
+        nvmax, err = 0.0, 0.0
+        for b in range(B):
+            n = lens[b] + 1
+            kk = [o.SplitEncoded(take(kf[b, h].o, n), take(kf[b, h].r, n)) for h in range(H)]
+            vv = [o.SplitEncoded(take(vf[b, h].o, n), take(vf[b, h].r, n)) for h in range(H)]
+            ref = o.split_decode_attention(kc, vc, q[b].double().numpy(), kk, vv, scale)
+            err = max(err, float(np.max(np.abs(out[b] - ref))))
+            nvmax = max(nvmax, max(max(float(np.max(e.o.nx.astype(np.float64))),
+                                       float(np.max(e.r.nx.astype(np.float64)))) for e in vv))
+        say(f"split K+V decode step {s_}: max |out - ref| / max n_v = {err / nvmax:.3g}")
+        assert err / nvmax <= 1e-3
