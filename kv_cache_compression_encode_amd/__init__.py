@@ -198,9 +198,11 @@ def encode_kv(kcb: Codebook, vcb: Codebook, k: torch.Tensor, v: torch.Tensor,
     encode(kcb, k) and encode(vcb, v).  Returns (k_records, v_records)."""
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("keys and values need one shape, stride and dtype")
-    lead = 4 - k.dim()
-    k4 = k.reshape((1,) * lead + tuple(k.shape)) if lead else k
-    v4 = v.reshape((1,) * lead + tuple(v.shape)) if lead else v
+    if not 2 <= k.dim() <= 4:
+        raise ValueError("keys and values need 2 to 4 dims")
+    k4, v4 = k, v
+    while k4.dim() < 4:  # leading size-1 dims: views, never copies
+        k4, v4 = k4.unsqueeze(0), v4.unsqueeze(0)
     B, H, T, d = k4.shape
     kper, vper = kcb.records_bytes(T), vcb.records_bytes(T)
     if k_records is None:
