@@ -830,6 +830,7 @@ class SplitCodec:
     regular: np.ndarray      # [H][d - o] the other channels, ascending
     inst_o: Codec            # TurboQuant instance of dimension o
     inst_r: Codec            # TurboQuant instance of dimension d - o
+    layout: str = "row"      # "col": mse values in 8-token code words (split_col_layout)
 
     @property
     def o(self) -> int:
@@ -847,7 +848,7 @@ class SplitEncoded:
 
 
 def outlier_split_codec(d: int, outlier_channels, bits_outlier: int, bits_regular: int, mode: str,
-                        rot_seed: int, sketch_seed: int = 0) -> SplitCodec:
+                        rot_seed: int, sketch_seed: int = 0, layout: str = "row") -> SplitCodec:
     """Two independent TurboQuant instances over a channel split (paper
     review, "Method", KV-cache setting).  outlier_channels: [o] or [H][o]."""
     ch = np.atleast_2d(np.asarray(outlier_channels, dtype=np.int64))
@@ -860,9 +861,31 @@ def outlier_split_codec(d: int, outlier_channels, bits_outlier: int, bits_regula
         if len(s) != o or min(s) < 0 or max(s) >= d:
             raise ValueError("outlier channels must be distinct and in [0, d)")
         regular.append([c for c in range(d) if c not in s])
+    if layout not in ("row", "col") or (layout == "col" and (mode != "mse" or d != 128)):
+        raise ValueError("the col layout of a split codec holds d = 128 mse values")
     inst_o = turboquant_codec(o, bits_outlier, mode, rot_seed + 1, sketch_seed + 1)
     inst_r = turboquant_codec(d - o, bits_regular, mode, rot_seed, sketch_seed)
-    return SplitCodec(d, mode, ch, np.asarray(regular, dtype=np.int64), inst_o, inst_r)
+    return SplitCodec(d, mode, ch, np.asarray(regular, dtype=np.int64), inst_o, inst_r, layout)
+
+
+# Col layout of split values (d = 128, mse; the library's layout, written
+# out here from its specification): per tile, for each 8-token group g
+# (tokens 8g .. 8g + 7) the 16 lane blocks n = 0..15 in order, block n holding
+# stored coordinates 16 vb + n for vb = 0..7 in that order, coordinate i as a
+# little-endian word of b_i bytes whose bits b_i k .. b_i k + b_i - 1 are the
+# index of token 8g + k (b_i: its index bits).  Then n_x of the regular and
+# of the outlier instance, fp16 x 64 each.
+def split_col_layout(bits):
+    """(offset of coordinate i's word within a token group [d], group bytes)."""
+    bits = np.asarray(bits, dtype=np.int64)
+    off = np.zeros(len(bits), dtype=np.int64)
+    pos = 0
+    for n in range(16):
+        for vb in range(8):
+            i = 16 * vb + n
+            off[i] = pos
+            pos += int(bits[i])
+    return off, pos
 
 
 def split_encode(sc: SplitCodec, x: np.ndarray, head: int = 0, round_norms: bool = True) -> SplitEncoded:
@@ -976,7 +999,11 @@ def _split_stored_encoded(sc: SplitCodec, enc: SplitEncoded) -> Encoded:
 
 
 def split_tile_fields(sc: SplitCodec):
-    """tile_fields of the stored-order codec, then the outlier instance's norms."""
+    """tile_fields of the stored-order codec (col: the code words, then n_x),
+    then the outlier instance's norms."""
+    if sc.layout == "col":
+        _, gbytes = split_col_layout(split_stored_codec(sc).bits)
+        return [("codes", 0, 8 * gbytes), ("nx", 8 * gbytes, 2 * TILE), ("nx_o", 8 * gbytes + 2 * TILE, 2 * TILE)]
     fields = tile_fields(split_stored_codec(sc))
     off = fields[-1][1] + fields[-1][2]
     fields.append(("nx_o", off, 2 * TILE))
@@ -990,8 +1017,70 @@ def split_tile_bytes(sc: SplitCodec) -> int:
     return f[-1][1] + f[-1][2]
 
 
+def _split_col_pack(sc: SplitCodec, enc: SplitEncoded) -> np.ndarray:
+    stored = split_stored_codec(sc)
+    st = _split_stored_encoded(sc, enc)
+    off, gbytes = split_col_layout(stored.bits)
+    n = st.idx.shape[0]
+    ntile = (n + TILE - 1) // TILE
+    tb = split_tile_bytes(sc)
+    fields = dict((f[0], f[1]) for f in split_tile_fields(sc))
+    pad = ntile * TILE - n
+    idx = np.concatenate([st.idx, np.zeros((pad, sc.d), np.int64)])
+    nx = np.concatenate([enc.r.nx, np.zeros(pad, np.float16)])
+    nxo = np.concatenate([enc.o.nx, np.zeros(pad, np.float16)])
+    buf = np.zeros(ntile * tb, dtype=np.uint8)
+    for t in range(ntile):
+        base = t * tb
+        for g in range(8):
+            for i in range(sc.d):
+                b = int(stored.bits[i])
+                word = 0
+                for k in range(8):
+                    word |= int(idx[t * TILE + 8 * g + k, i]) << (b * k)
+                for j in range(b):
+                    buf[base + g * gbytes + off[i] + j] = (word >> (8 * j)) & 0xFF
+        rows = slice(t * TILE, (t + 1) * TILE)
+        buf[base + fields["nx"]: base + fields["nx"] + 2 * TILE] = nx[rows].view(np.uint8)
+        buf[base + fields["nx_o"]: base + fields["nx_o"] + 2 * TILE] = nxo[rows].view(np.uint8)
+    return buf
+
+
+def _split_col_unpack(sc: SplitCodec, buf: np.ndarray, n: int) -> SplitEncoded:
+    stored = split_stored_codec(sc)
+    off, gbytes = split_col_layout(stored.bits)
+    ntile = (n + TILE - 1) // TILE
+    tb = split_tile_bytes(sc)
+    fields = dict((f[0], f[1]) for f in split_tile_fields(sc))
+    idx = np.zeros((ntile * TILE, sc.d), dtype=np.int64)
+    nx = np.zeros(ntile * TILE, np.float16)
+    nxo = np.zeros(ntile * TILE, np.float16)
+    for t in range(ntile):
+        base = t * tb
+        for g in range(8):
+            for i in range(sc.d):
+                b = int(stored.bits[i])
+                word = 0
+                for j in range(b):
+                    word |= int(buf[base + g * gbytes + off[i] + j]) << (8 * j)
+                for k in range(8):
+                    idx[t * TILE + 8 * g + k, i] = (word >> (b * k)) & ((1 << b) - 1)
+        nx[t * TILE:(t + 1) * TILE] = buf[base + fields["nx"]: base + fields["nx"] + 2 * TILE].view(np.float16)
+        nxo[t * TILE:(t + 1) * TILE] = buf[base + fields["nx_o"]: base + fields["nx_o"] + 2 * TILE].view(np.float16)
+    group, coord = split_stored_order(sc.d, sc.o)
+    out = []
+    for gsel in (1, 0):
+        cols = np.nonzero(group == gsel)[0]
+        order = cols[np.argsort(coord[cols])]
+        out.append(idx[:n, order])
+    return SplitEncoded(Encoded(out[0], None, nxo[:n], None, None, None),
+                        Encoded(out[1], None, nx[:n], None, None, None))
+
+
 def split_pack(sc: SplitCodec, enc: SplitEncoded) -> np.ndarray:
     """Bytes of the record tiles of a split codec (layout above)."""
+    if sc.layout == "col":
+        return _split_col_pack(sc, enc)
     stored = split_stored_codec(sc)
     inner = pack(stored, _split_stored_encoded(sc, enc))
     tb_in, tb = tile_bytes(stored), split_tile_bytes(sc)
@@ -1014,6 +1103,8 @@ def split_pack(sc: SplitCodec, enc: SplitEncoded) -> np.ndarray:
 def split_unpack(sc: SplitCodec, buf: np.ndarray, n: int) -> SplitEncoded:
     """Inverse of split_pack (y and z come back as None)."""
     buf = np.asarray(buf, dtype=np.uint8)
+    if sc.layout == "col":
+        return _split_col_unpack(sc, buf, n)
     stored = split_stored_codec(sc)
     tb_in, tb = tile_bytes(stored), split_tile_bytes(sc)
     ntile = (n + TILE - 1) // TILE

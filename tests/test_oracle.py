@@ -739,3 +739,45 @@ def test_split_stored_form_gives_same_scores():
             assert np.max(np.abs(st.rot[h] @ st.rot[h].T - np.eye(128))) < 1e-5
             assert not st.sketch[np.ix_(group == 1, group == 0)].any()
 
+
+
+def test_split_col_layout_worked_example():
+    # Col records of 2.5-bit split values (32 outlier channels at 3 index
+    # bits, 96 at 2), worked by hand from the layout: a token group's code
+    # words are ordered by lane block n (coordinates 16 vb + n, vb = 0..7),
+    # so within group 0 stored coordinate 0 (outlier, 3 bytes) sits at byte
+    # 0, stored coordinate 16 (regular, 2 bytes) at byte 3, stored coordinate
+    # 1 (outlier) at byte 20 (block 0: 4 x 3 + 4 x 2 bytes), stored coordinate
+    # 8 (regular: block 8 starts after 8 blocks of 20 bytes) at byte 160; a
+    # group is 8 x 20 + 8 x 16 = 288 bytes, so group 1 starts at 288.
+    # Stored coordinate i = 32 blk + r is outlier coordinate 8 blk + r when
+    # r < 8, else regular coordinate 24 blk + r - 8.
+    sc = o.outlier_split_codec(128, np.arange(32) * 4, 3, 2, "mse", rot_seed=1, layout="col")
+    n = 16
+    io = np.zeros((n, 32), np.int64)
+    ir = np.zeros((n, 96), np.int64)
+    io[:8, 0] = [1, 2, 3, 4, 5, 6, 7, 0]     # stored 0, tokens 0..7
+    ir[:8, 8] = [3, 0, 1, 2, 3, 0, 1, 2]     # stored 16 = regular 8
+    io[:8, 1] = 5                            # stored 1
+    ir[:8, 0] = [1, 1, 1, 1, 0, 0, 0, 0]     # stored 8 = regular 0
+    io[8:, 0] = 7                            # stored 0, tokens 8..15 (group 1)
+    enc = o.SplitEncoded(o.Encoded(io, None, np.full(n, 2.0, np.float16), None, None, None),
+                         o.Encoded(ir, None, np.full(n, 0.5, np.float16), None, None, None))
+    buf = o.split_pack(sc, enc)
+    assert o.split_tile_bytes(sc) == 2560 and len(buf) == 2560
+    # 1 + 2<<3 + 3<<6 + 4<<9 + 5<<12 + 6<<15 + 7<<18 = 0x1F58D1
+    assert buf[0:3].tolist() == [0xD1, 0x58, 0x1F]
+    # 3 + 0<<2 + 1<<4 + 2<<6 + 3<<8 + 0<<10 + 1<<12 + 2<<14 = 0x9393
+    assert buf[3:5].tolist() == [0x93, 0x93]
+    # eight 5s at 3 bits: 0b101 repeated = 0xB6DB6D
+    assert buf[20:23].tolist() == [0x6D, 0xDB, 0xB6]
+    # 1, 1, 1, 1, 0, 0, 0, 0 at 2 bits = 0x0055
+    assert buf[160:162].tolist() == [0x55, 0x00]
+    # group 1, stored 0: eight 7s = 0xFFFFFF
+    assert buf[288:291].tolist() == [0xFF, 0xFF, 0xFF]
+    assert np.count_nonzero(buf[:2304]) == 3 + 2 + 3 + 1 + 3
+    # norms: regular n_x then the outlier n_x, fp16
+    assert np.array_equal(buf[2304:2304 + 2 * n].view(np.float16), np.full(n, 0.5, np.float16))
+    assert np.array_equal(buf[2432:2432 + 2 * n].view(np.float16), np.full(n, 2.0, np.float16))
+    back = o.split_unpack(sc, buf, n)
+    assert np.array_equal(back.o.idx, io) and np.array_equal(back.r.idx, ir)
