@@ -178,7 +178,7 @@ def cpu_baseline_gqa_outlier_kv():
     q = synth.kv_queries(1, 4, 1, D, 202, law)[0].double().numpy()
     ch = outlier_channels(torch, law, 1)
     kc = o.outlier_split_codec(D, ch, 3, 2, "prod", rot_seed=203, sketch_seed=204)
-    vc = o.outlier_split_codec(D, ch, 3, 2, "mse", rot_seed=213)
+    vc = o.outlier_split_codec(D, ch, 3, 2, "mse", rot_seed=213, layout="col")
 
     def run():
         ke, ve = o.split_encode(kc, k), o.split_encode(vc, v)
@@ -367,9 +367,10 @@ def run_gqa_layer(args, torch, tq, synth, split=False, split_values=False):
     else:
         kcb = tq.Codebook(D, tq.TQ_PROD, 3, seed_rotation=203, seed_sketch=204, **rot_kw(tq))
     if split_values:
-        # 2.5-bit values as well: the same channel split, mse, row records
+        # 2.5-bit values as well: the same channel split, mse, col records
+        # (8-token code words that the MFMA decode reads)
         vcb = tq.Codebook(D, tq.TQ_MSE, 2, seed_rotation=213, outlier_channels=outlier_channels(torch, law, HKV),
-                          outlier_bits=3)
+                          outlier_bits=3, layout=tq.TQ_LAYOUT_COL)
     else:
         vcb = tq.Codebook(D, tq.TQ_MSE, 4, seed_rotation=203, layout=tq.TQ_LAYOUT_COL, **rot_kw(tq))
     k_rec = K_REC_SPLIT if split else K_REC
@@ -421,7 +422,7 @@ def run_gqa_layer(args, torch, tq, synth, split=False, split_values=False):
                  "calibration sample: TurboQuant-prod b=3; the other 96: b=2; row records, 44 B/key)"
                  if split else "K TurboQuant-prod b=3 (row records)")
     vals_desc = ("V outlier-channel split, 2.5 bits (the same channels: TurboQuant-mse b=3 on them, b=2 "
-                 "on the other 96; row records, 40 B/value; decode on the general kernel)"
+                 "on the other 96; col records, 40 B/value)"
                  if split_values else "V TurboQuant-mse b=4 (col records)")
     wname = "gqa_outlier_kv" if split_values else ("gqa_outlier" if split else "gqa_layer")
     roof = hbm_roof(wname, dom, t[dom], nbytes[dom])

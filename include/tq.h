@@ -122,7 +122,15 @@ typedef struct tq_codebook tq_codebook;
  *              TQ_ROT_CALIBRATE / TQ_ROT_GIVEN, or per outlier channel list of
  *              a split codec); TQ_ROT_HAAR otherwise uses 1.
  *   layout     TQ_LAYOUT_ROW or TQ_LAYOUT_COL (COL needs a uniform bit map;
- *              the GPU encode writes COL records for 1, 2 or 4 index bits).
+ *              the GPU encode writes COL records for 1, 2 or 4 index bits),
+ *              or, for an outlier-channel split, the 2.5-bit mse split (32
+ *              outlier channels at outlier_bits 3, the others at bits 2):
+ *              per 8-token group, 16 lane blocks (block n: stored
+ *              coordinates 16 vb + n, vb = 0..7, each a little-endian word
+ *              of 8 codes, 3 bytes for the outlier coordinates (n < 8, vb
+ *              even), 2 bytes otherwise), 288 bytes a group, then n_x of the
+ *              regular and of the outlier instance; its decode runs on the
+ *              MFMA kernel.
  *   seed_*     seeds of the Philox4x32-10 streams of Pi (stream 1; the
  *              Hadamard signs use stream 3) and S (stream 2).
  *   device     HIP device ordinal that holds the codebook's tables.
@@ -221,8 +229,8 @@ tq_status tq_codebook_free(tq_codebook* cb);
  *              h * rs_h bytes and hold `capacity` tokens (their tile count).
  *   positions  device int32 [B]; entries outside [0, capacity) are skipped.
  * Supported: ROW records of any bit map (mse, or prod with m <= d), COL
- * records of uniform mse codecs with 1, 2 or 4 index bits; TQ_EUNSUPPORTED
- * otherwise.  Only the new slot's bytes (COL: the new vector's bits in each
+ * records of uniform mse codecs with 1, 2 or 4 index bits and of the 2.5-bit
+ * split mse codec; TQ_EUNSUPPORTED otherwise.  Only the new slot's bytes (COL: the new vector's bits in each
  * dim's field) change.  Calls for the same records must not overlap.
  * Errors: TQ_EINVAL (null pointer, negative size, bad dtype), TQ_EALIGN
  * (records or record strides not 4-byte aligned), TQ_EDEVICE (launch). */

@@ -140,11 +140,16 @@ tq_status build_split(tq_codebook* cb, const tq_codebook_desc& ds) {
   if (o != 32 && o != 64 && o != 96) return TQ_EUNSUPPORTED;
   if (!ds.outlier_channels || ds.bitmap || ds.waterfill_bits > 0 || ds.rotation != TQ_ROT_HAAR)
     return TQ_EINVAL;
-  if (ds.layout != TQ_LAYOUT_ROW || (ds.qjl_dims != 0 && ds.qjl_dims != d)) return TQ_EUNSUPPORTED;
+  if (ds.qjl_dims != 0 && ds.qjl_dims != d) return TQ_EUNSUPPORTED;
   const int heads = std::max(1, ds.num_heads);
   const int ub_r = ds.mode == TQ_PROD ? ds.bits - 1 : ds.bits;
   const int ub_o = ds.mode == TQ_PROD ? ds.outlier_bits - 1 : ds.outlier_bits;
   if (ub_r < 1 || ub_r > kMaxBits || ub_o < 1 || ub_o > kMaxBits) return TQ_EINVAL;
+  // col records: the 2.5-bit split of mse values only (32 outlier channels
+  // at 3 index bits, 96 at 2), whose 8-token code words the MFMA decode reads
+  if (ds.layout == TQ_LAYOUT_COL && (ds.mode != TQ_MSE || o != 32 || ub_o != 3 || ub_r != 2))
+    return TQ_EUNSUPPORTED;
+  if (ds.layout != TQ_LAYOUT_ROW && ds.layout != TQ_LAYOUT_COL) return TQ_EINVAL;
   // channel lists: outlier channels in list order, the others ascending
   std::vector<int> och(size_t(heads) * o), rch(size_t(heads) * (d - o));
   for (int h = 0; h < heads; ++h) {
@@ -1051,10 +1056,15 @@ tq_status decode_impl(const tq_codebook* kcb, const tq_codebook* vcb, const void
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || kv->max_tokens < 0) return TQ_EINVAL;
   if (!on_device(kcb) || !on_device(vcb) || kcb->device != vcb->device) return TQ_EINVAL;
   if (kcb->desc.d != 128 || vcb->desc.d != 128) return TQ_EUNSUPPORTED;
-  // values: mse, as COL records of a uniform codec with up to 4 index bits,
-  // or as ROW records of a uniform or an outlier-channel split codec
+  // values: mse, as COL records of a uniform codec with up to 4 index bits
+  // or of the 2.5-bit split (MFMA kernel only), or as ROW records of a
+  // uniform or an outlier-channel split codec
   if (kcb->desc.layout != TQ_LAYOUT_ROW || vcb->desc.mode != TQ_MSE) return TQ_EUNSUPPORTED;
-  if (vcb->desc.layout == TQ_LAYOUT_COL ? (!vcb->uniform || vcb->ubits > 4) : !(vcb->uniform || vcb->outlier > 0))
+  if (vcb->desc.layout == TQ_LAYOUT_COL ? (!vcb->uniform || vcb->ubits > 4) && vcb->outlier == 0
+                                        : !(vcb->uniform || vcb->outlier > 0))
+    return TQ_EUNSUPPORTED;
+  if (vcb->desc.layout == TQ_LAYOUT_COL && vcb->outlier > 0 &&
+      !decode_mfma_supported(make_view(kcb), make_view(vcb), Hq / Hkv))
     return TQ_EUNSUPPORTED;
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return TQ_EUNSUPPORTED;

@@ -187,6 +187,21 @@ __device__ __forceinline__ void append_one(const CodecView& cv, const AppendArgs
           const int P = bpos[p];
           atomicOr(&sbits[P >> 5], 1u << (P & 31));
         }
+  } else if (t < D && cv.outl) {
+    // col records of the 2.5-bit split: bits b k .. b k + b - 1 of
+    // coordinate i's b-byte word in the slot's 8-token group (k = slot % 8),
+    // the word at byte 5 (vb / 2) + 3 (vb % 2) of lane block n < 8 (20 bytes)
+    // or 2 vb of block n >= 8 (16 bytes; n = i % 16, vb = i / 16), 288 bytes a
+    // group; the other tokens' bits are kept
+    const int n = i & 15, vb = i >> 4;
+    const int off = n < 8 ? 20 * n + 5 * (vb >> 1) + 3 * (vb & 1) : 160 + 16 * (n - 8) + 2 * vb;
+    uint8_t* wb = trec + (slot >> 3) * 288 + off;
+    const int ub = nbits, sh = ub * (slot & 7);
+    uint32_t w = 0u;
+    for (int q = 0; q < ub; ++q) w |= uint32_t(wb[q]) << (8 * q);
+    const uint32_t mask = ((1u << ub) - 1u) << sh;
+    w = (w & ~mask) | ((uint32_t(idx) << sh) & mask);
+    for (int q = 0; q < ub; ++q) wb[q] = uint8_t(w >> (8 * q));
   } else if (t < D) {
     // col: bit (b v + k) of dim i's 8b-byte field is bit k of vector v's index
     const int ub = nbits;  // uniform codec: the same on every dim
@@ -256,8 +271,10 @@ __global__ __launch_bounds__(256) void append_pair_kernel(CodecView kc, AppendAr
 
 bool append_supported(const CodecView& cv) {
   if (cv.d != D || !cv.rot_t) return false;
-  if (cv.layout == TQ_LAYOUT_COL)
+  if (cv.layout == TQ_LAYOUT_COL) {
+    if (cv.outl) return cv.mode == TQ_MSE && cv.o4 == 8 && cv.split_ub_o == 3 && cv.split_ub_r == 2;
     return cv.uniform && cv.mode == TQ_MSE && (cv.ubits == 1 || cv.ubits == 2 || cv.ubits == 4);
+  }
   return cv.mode == TQ_MSE || (cv.sketch_t && cv.m >= 1 && cv.m <= D);
 }
 

@@ -46,6 +46,7 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr float kQjl = 1.2533141373155001f;  // sqrt(pi / 2)
@@ -112,7 +113,16 @@ __device__ __forceinline__ float xor16(float v, int lane) {
 // NW waves per workgroup: 4 (two workgroups per CU), or 8 (one per CU, for
 // small batches split into many workgroups: the set-up, which loads the
 // columns of Pi and S, then runs once per CU)
-template <int G, int UB, int NW>
+// VK: the value records.  0: TurboQuant-mse col records with 4 index bits.
+// 1: 2.5-bit outlier-split mse values in col records: for each 8-token group
+// the 16 lane blocks (block n: coordinates 16 vb + n, vb = 0..7; 3-byte slots
+// of 3-bit codes for the outlier coordinates, vb even and n < 8, 2-byte slots
+// of 2-bit codes otherwise), 288 bytes a group, then the two groups' norms.
+// Lane (n, g16) loads its block of token groups g16 and 4 + g16, which hold
+// exactly its B operands; each token pair's codes index a 2-token LUT of its
+// group (16 regular, 64 outlier entries) and the pair's group norms are
+// multiplied in, so P carries the softmax weights alone.
+template <int G, int UB, int NW, int VK = 0>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView kc, CodecView vc, DecodeArgs a) {
   static_assert(G >= 1 && G <= 4, "up to 4 query heads per KV head");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
@@ -169,6 +179,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
   struct TileRegs {
     u32x4 kw4[NP], vw4[4];
     uint32_t nx, nr, nv, tl, sg, xo, ro;
+    uint32_t vcw[2][5];   // VK 1: the lane block of token groups g16, 4 + g16
+    u32x4 vnr[2], vno[2];  // VK 1: fp16 norm pairs of those tokens (regular, outlier)
   };
   TileRegs cur, nxt;
   auto load_tile = [&](int tile, TileRegs& R) {
@@ -192,13 +204,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
       const int off = SQ ? 0 : (p < (SPL ? 2 : UB) ? p * kTile * 16 : kc.off_signs);  // SQ: plane 0 only
       R.kw4[p] = *reinterpret_cast<const u32x4*>(kt + off + tok * 16);
     }
-    // load j: dim 16 (2j + g16/2) + n, bytes 16 (g16 % 2) .. + 15 of its field
+    if constexpr (VK == 0) {
+      // load j: dim 16 (2j + g16/2) + n, bytes 16 (g16 % 2) .. + 15 of its field
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      R.vw4[j] = *reinterpret_cast<const u32x4*>(vt + (16 * (2 * j + (g16 >> 1)) + n) * 32 + 16 * (g16 & 1));
+      for (int j = 0; j < 4; ++j)
+        R.vw4[j] = *reinterpret_cast<const u32x4*>(vt + (16 * (2 * j + (g16 >> 1)) + n) * 32 + 16 * (g16 & 1));
+      R.nv = *reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok);
+    } else {
+      const int boff = n < 8 ? 20 * n : 160 + 16 * (n - 8);
+#pragma unroll
+      for (int kc2 = 0; kc2 < 2; ++kc2) {
+        const uint32_t* blk = reinterpret_cast<const uint32_t*>(vt + (4 * kc2 + g16) * 288 + boff);
+#pragma unroll
+        for (int u = 0; u < 5; ++u) R.vcw[kc2][u] = blk[u];  // the fifth word of an n >= 8 block goes unused
+        R.vnr[kc2] = *reinterpret_cast<const u32x4*>(vt + vc.off_nx + 2 * (32 * kc2 + 8 * g16));
+        R.vno[kc2] = *reinterpret_cast<const u32x4*>(vt + vc.off_nxo + 2 * (32 * kc2 + 8 * g16));
+      }
+      R.nv = 0x3C00u;  // 1.0: the norms are in the B operand
+    }
     R.nx = *reinterpret_cast<const uint16_t*>(kt + kc.off_nx + 2 * tok);
     R.nr = *reinterpret_cast<const uint16_t*>(kt + kc.off_nr + 2 * tok);
-    R.nv = *reinterpret_cast<const uint16_t*>(vt + vc.off_nx + 2 * tok);
     if (SQ) {
       R.tl = kt[kTile * 16 + tok];
       R.sg = kt[kc.off_signs + tok];
@@ -268,7 +293,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
   const float* kcen = kc.cen + size_t(hk) * D * kMaxLevels;
   if (threadIdx.x < 256) {
     const int t = threadIdx.x;  // one value-table entry per thread
-    slut1[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+    if constexpr (VK == 0) {
+      slut1[t] = f16b(vc.ucen[t & 15]) | (f16b(vc.ucen[t >> 4]) << 16);
+    } else {
+      // entries 0..15: regular token pairs (i0 | i1 << 2, levels of stored
+      // dim 8); 16..79: outlier pairs (i0 | i1 << 3, levels of stored dim 0)
+      const float* ce = vc.cen + size_t(vc.heads > 1 ? g : 0) * D * kMaxLevels;
+      uint32_t v = 0u;
+      if (t < 16) v = f16b(ce[8 * kMaxLevels + (t & 3)]) | (f16b(ce[8 * kMaxLevels + (t >> 2)]) << 16);
+      else if (t < 80) v = f16b(ce[(t - 16) & 7]) | (f16b(ce[(t - 16) >> 3]) << 16);
+      slut1[t] = v;
+    }
   }
   for (int e = threadIdx.x; e < NW * 16 * PROW / 8; e += blockDim.x)
     reinterpret_cast<u32x4*>(&sP[0][0][0])[e] = u32x4{0u, 0u, 0u, 0u};
@@ -498,13 +533,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) kw[nb][p] = t[nb];  // dword g16 of token 16 nb + n
     }
+    if constexpr (VK == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 t = transpose4(R.vw4[j], lane);
-      vw[2 * j][0] = t[0];
-      vw[2 * j][1] = t[1];
-      vw[2 * j + 1][0] = t[2];
-      vw[2 * j + 1][1] = t[3];
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 t = transpose4(R.vw4[j], lane);
+        vw[2 * j][0] = t[0];
+        vw[2 * j][1] = t[1];
+        vw[2 * j + 1][0] = t[2];
+        vw[2 * j + 1][1] = t[3];
+      }
     }
     float nx[4], nr[4], nv[4], nxo[4], nro[4];
     // SQ, per token before the exchange (once per token instead of once per
@@ -609,17 +646,54 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void decode_mfma_kernel(CodecView 
     // value B fragments: table lookups issued before the softmax, whose
     // arithmetic covers their latency
     u32x4 Bv[8][2];
+    if constexpr (VK == 0) {
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
+      for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+        for (int kc2 = 0; kc2 < 2; ++kc2) {
+          const uint32_t w = vw[vb][kc2];
+          const uint32_t* lut = slut + (lane & 31);
+          Bv[vb][kc2][0] = lut[(w & 0xffu) << 5];
+          Bv[vb][kc2][1] = lut[((w >> 8) & 0xffu) << 5];
+          Bv[vb][kc2][2] = lut[((w >> 16) & 0xffu) << 5];
+          Bv[vb][kc2][3] = lut[(w >> 24) << 5];
+        }
+    } else {
+      // slot vb of the lane block: bytes 5 (vb / 2) + 3 (vb % 2) (n < 8) or
+      // 2 vb (n >= 8); 3-bit codes in the outlier slots (n < 8, vb even)
+      const bool lo8 = n < 8;
+      const uint32_t* lut = slut + (lane & 31);
 #pragma unroll
       for (int kc2 = 0; kc2 < 2; ++kc2) {
-        const uint32_t w = vw[vb][kc2];
-        const uint32_t* lut = slut + (lane & 31);
-        Bv[vb][kc2][0] = lut[(w & 0xffu) << 5];
-        Bv[vb][kc2][1] = lut[((w >> 8) & 0xffu) << 5];
-        Bv[vb][kc2][2] = lut[((w >> 16) & 0xffu) << 5];
-        Bv[vb][kc2][3] = lut[(w >> 24) << 5];
+        uint32_t c[6];
+#pragma unroll
+        for (int u = 0; u < 5; ++u) c[u] = R.vcw[kc2][u];
+        c[5] = 0u;
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb) {
+          const int obo = 5 * (vb >> 1) + 3 * (vb & 1), obr = 2 * vb;
+          const uint32_t wo = __builtin_amdgcn_alignbyte(c[obo / 4 + 1], c[obo / 4], obo % 4);
+          const uint32_t wr = __builtin_amdgcn_alignbyte(c[obr / 4 + 1], c[obr / 4], obr % 4);
+          const bool three = lo8 && !(vb & 1);
+          const uint32_t w = lo8 ? wo : wr;
+          const uint32_t bs2 = three ? 6u : 4u;       // bits per token pair
+          const uint32_t base = three ? (16u << 5) : 0u;
+          // the norm words go through scalars: a bit cast straight from a
+          // vector element has read element 0
+          uint32_t nw[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) nw[k] = three ? R.vno[kc2][k] : R.vnr[kc2][k];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t e = __builtin_amdgcn_ubfe(w, bs2 * k, bs2);
+            const uint32_t lv = lut[base + (e << 5)];
+            const uint32_t nk = nw[k];
+            const h2_t prod = __builtin_bit_cast(h2_t, lv) * __builtin_bit_cast(h2_t, nk);
+            Bv[vb][kc2][k] = __builtin_bit_cast(uint32_t, prod);
+          }
+        }
       }
+    }
     // ---- online softmax (lanes of group 0: queries 0,1; group 1: queries 2,3)
     float alpha[2];
 #pragma unroll
@@ -793,8 +867,13 @@ bool decode_mfma_supported(const CodecView& kv, const CodecView& vv, int G) {
   const bool keys = kv.d == D && kv.layout == TQ_LAYOUT_ROW &&
                     ((kv.uniform && kv.mode == TQ_PROD && kv.m == D && (kv.ubits == 1 || kv.ubits == 2)) ||
                      sq_keys(kv) || split_keys(kv));
-  return keys && vv.d == D && vv.uniform && vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL &&
-         vv.ubits == 4 && (G == 1 || G == 2 || G == 4);
+  // values: 4-bit col records, or the 2.5-bit split in col records (with split
+  // keys or 2-bit TurboQuant-prod keys)
+  const bool sv = vv.outl && vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL && vv.o4 == 8 &&
+                  vv.split_ub_o == 3 && vv.split_ub_r == 2 &&
+                  (split_keys(kv) || (kv.uniform && kv.mode == TQ_PROD && kv.m == D && kv.ubits == 2));
+  const bool v4 = vv.uniform && vv.mode == TQ_MSE && vv.layout == TQ_LAYOUT_COL && vv.ubits == 4;
+  return keys && vv.d == D && (v4 || sv) && (G == 1 || G == 2 || G == 4);
 }
 
 hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const DecodeArgs& a,
@@ -809,7 +888,21 @@ hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const De
     else                                                                                          \
       hipLaunchKernelGGL((decode_mfma_kernel<GG, UU, 4>), grid, dim3(256), 0, s, kv, vv, a);      \
   } while (0)
-  if (kv.outl) {
+#define TQ_LAUNCH_SV(GG, UU)                                                                     \
+  do {                                                                                            \
+    if (a.waves == 8)                                                                             \
+      hipLaunchKernelGGL((decode_mfma_kernel<GG, UU, 8, 1>), grid, dim3(512), 0, s, kv, vv, a);   \
+    else                                                                                          \
+      hipLaunchKernelGGL((decode_mfma_kernel<GG, UU, 4, 1>), grid, dim3(256), 0, s, kv, vv, a);   \
+  } while (0)
+  if (vv.outl) {
+    // split values: split keys or 2-bit TurboQuant-prod keys
+    if (kv.outl) {
+      if (G == 4) TQ_LAUNCH_SV(4, 3); else if (G == 2) TQ_LAUNCH_SV(2, 3); else TQ_LAUNCH_SV(1, 3);
+    } else {
+      if (G == 4) TQ_LAUNCH_SV(4, 2); else if (G == 2) TQ_LAUNCH_SV(2, 2); else TQ_LAUNCH_SV(1, 2);
+    }
+  } else if (kv.outl) {
     if (G == 4) TQ_LAUNCH(4, 3); else if (G == 2) TQ_LAUNCH(2, 3); else TQ_LAUNCH(1, 3);
   } else if (!kv.uniform) {
     if (G == 4) TQ_LAUNCH(4, 0); else if (G == 2) TQ_LAUNCH(2, 0); else TQ_LAUNCH(1, 0);
@@ -819,6 +912,7 @@ hipError_t launch_decode_mfma(const CodecView& kv, const CodecView& vv, const De
     if (G == 4) TQ_LAUNCH(4, 1); else if (G == 2) TQ_LAUNCH(2, 1); else TQ_LAUNCH(1, 1);
   }
 #undef TQ_LAUNCH
+#undef TQ_LAUNCH_SV
   return hipGetLastError();
 }
 

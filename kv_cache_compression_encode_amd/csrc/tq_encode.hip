@@ -843,6 +843,21 @@ __device__ __forceinline__ void encode_d128_body(const CodecView& cv, const Enco
                   if (pos >= 0) tailw[nb] |= uint32_t((idx >> p) & 1) << (pos - D);
                 }
               }
+            } else if constexpr (SPLIT == 2) {
+              // split values in col records (32 outlier coordinates at 3
+              // index bits, the others at 2): the 8 tokens of a group (8
+              // consecutive lanes) form one word of b-bit codes, stored as b
+              // bytes in slot vb = dim / 16 of lane block n = dim % 16 of the
+              // group (block n < 8: 3- and 2-byte slots alternating, 20
+              // bytes; n >= 8: 2-byte slots, 16 bytes; 288 bytes a group)
+              const bool og = (16 * hh + r) < cv.o4;
+              const int b = og ? 3 : 2;
+              const uint32_t w = group_or<8>(uint32_t(idx) << (b * (j & 7)));
+              const int n = dim & 15, vb = dim >> 4;
+              const int off = n < 8 ? 20 * n + 5 * (vb >> 1) + 3 * (vb & 1) : 160 + 16 * (n - 8) + 2 * vb;
+              const int grp = (sub * 32 + j) >> 3;
+              const int k = j & 7;
+              if (k < b) trec[grp * 288 + off + k] = uint8_t(w >> (8 * k));
             } else if (SYM4) {
               // packed and transposed after the block
             } else if (UB == 1) {
@@ -939,7 +954,7 @@ __device__ __forceinline__ void encode_d128_body(const CodecView& cv, const Enco
               *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 32 + 4 * word) = w;
             }
           }
-          if (COL && UB > 1 && !SYM4) {
+          if (COL && UB > 1 && !SYM4 && !SPLIT) {
             // lane j holds, for r = k*VPD + (j % VPD), the dword of dim
             // 32mb + 16hh + r covering vectors (j / VPD)*VPD ..
             constexpr int VPD = 32 / UB;
@@ -951,7 +966,7 @@ __device__ __forceinline__ void encode_d128_body(const CodecView& cv, const Enco
               *reinterpret_cast<uint32_t*>(trec + size_t(dim) * 8 * UB + 4 * word) = colkeep[nb][k];
             }
           }
-          if (COL && UB == 1) {
+          if (COL && UB == 1 && !SPLIT) {
             // store the 32 dims x 32 vectors of this block: lane k < 32 holds dim 32mb+k
             if (lane < 32) {
               uint8_t* w = trec + (size_t(32) * mb + lane) * 8;
@@ -1593,8 +1608,14 @@ hipError_t launch_encode_d128(const CodecView& cv, const EncodeArgs& a, hipStrea
     // outlier-channel split, row layout, full block sketch: the 2.5-bit KV
     // setting (32 outlier coordinates at 2 index bits, the others at 1) on
     // its specialised path, any other outlier count and bits on the general
-    // one
-    if (col || !cv.omask) return hipErrorNotSupported;
+    // one; col layout: 2.5-bit mse values (32 outlier coordinates at 3 index
+    // bits, the others at 2) on the general path
+    if (!cv.omask) return hipErrorNotSupported;
+    if (col) {
+      if (cv.mode != TQ_MSE || cv.o4 != 8 || cv.split_ub_o != 3 || cv.split_ub_r != 2) return hipErrorNotSupported;
+      return a.x_bf16 ? launch_one<1, true, 0, true, false, 1, 2>(cv, a, s)
+                      : launch_one<1, false, 0, true, false, 1, 2>(cv, a, s);
+    }
     const bool fast = cv.o4 == 8 && cv.split_ub_o == 2 && cv.split_ub_r == 1;
     if (cv.mode == TQ_PROD) {
       if (cv.m != D) return hipErrorNotSupported;

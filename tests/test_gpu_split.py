@@ -39,11 +39,12 @@ def outlier_channels(law, heads, o_=32, n=2048, seed=900):
     return np.stack(out).astype(np.int32)
 
 
-def codecs(ch, bits=(3, 2), mode="prod", seeds=(211, 212)):
+def codecs(ch, bits=(3, 2), mode="prod", seeds=(211, 212), layout="row"):
     m = tq.TQ_PROD if mode == "prod" else tq.TQ_MSE
     cb = tq.Codebook(128, m, bits[1], seed_rotation=seeds[0], seed_sketch=seeds[1], outlier_channels=ch,
-                     outlier_bits=bits[0])
-    sc = o.outlier_split_codec(128, ch, bits[0], bits[1], mode, rot_seed=seeds[0], sketch_seed=seeds[1])
+                     outlier_bits=bits[0], layout=tq.TQ_LAYOUT_COL if layout == "col" else tq.TQ_LAYOUT_ROW)
+    sc = o.outlier_split_codec(128, ch, bits[0], bits[1], mode, rot_seed=seeds[0], sketch_seed=seeds[1],
+                               layout=layout)
     return cb, sc
 
 
@@ -270,7 +271,7 @@ def test_gqa_outlier_full_size():
     assert err <= 1e-3
 
 
-def _decode_split_values(B, Hq, Hkv, T, seq_lens, kbits=(3, 2), vbits=(3, 2), split_keys=True):
+def _decode_split_values(B, Hq, Hkv, T, seq_lens, kbits=(3, 2), vbits=(3, 2), split_keys=True, vlayout="row"):
     """Decode over values of an outlier-split mse codec (ROW records; the
     paper review's KV-cache setting splits the values' channels too)."""
     law = synth.KVLaw(Hkv, 128, 955)
@@ -289,7 +290,7 @@ def _decode_split_values(B, Hq, Hkv, T, seq_lens, kbits=(3, 2), vbits=(3, 2), sp
         kenc = lambda x, g: o.encode(kc, x)
         kpack = lambda e: o.pack(kc, e)
         ktake = take
-    vcb, vc = codecs(ch, bits=vbits, mode="mse", seeds=(957, 958))
+    vcb, vc = codecs(ch, bits=vbits, mode="mse", seeds=(957, 958), layout=vlayout)
     ke = [[kenc(K[b, g].double().numpy(), g) for g in range(Hkv)] for b in range(B)]
     ve = [[o.split_encode(vc, V[b, g].double().numpy(), head=g) for g in range(Hkv)] for b in range(B)]
     kbuf = np.concatenate([kpack(e) for row in ke for e in row])
@@ -315,7 +316,7 @@ def _decode_split_values(B, Hq, Hkv, T, seq_lens, kbits=(3, 2), vbits=(3, 2), sp
     nvmax = max(max(float(np.max(e.o.nx.astype(np.float64))), float(np.max(e.r.nx.astype(np.float64))))
                 for row in ve for e in row)
     err = np.max(np.abs(out - ref)) / nvmax
-    say(f"split-value decode B={B} Hq={Hq} Hkv={Hkv} T={T} k={kbits} v={vbits} split keys={split_keys}: "
+    say(f"split-value decode B={B} Hq={Hq} Hkv={Hkv} T={T} k={kbits} v={vbits} {vlayout} split keys={split_keys}: "
         f"max |out - ref| / max n_v = {err:.3g}")
     assert err <= 1e-3
     if any(L_ == 0 for L_ in seq_lens):
@@ -366,10 +367,12 @@ def test_row_value_decode():
         assert err / nvmax <= 1e-3
 
 
-def test_gqa_outlier_kv_full_size():
+@pytest.mark.parametrize("vlayout", ["row", "col"])
+def test_gqa_outlier_kv_full_size(vlayout):
     """2.5-bit keys and values (both split: 32 outlier channels at 3 bits, 96
     at 2) on the full layer, 32 q / 8 kv heads, 32768 tokens: the GPU value
-    records against the oracle, then the decode step."""
+    records (row records: general decode kernel; col: MFMA decode) against
+    the oracle, then the decode step."""
     Hq, Hkv, T = 32, 8, 32768
     say("split K+V full layer: generate")
     law = synth.KVLaw(Hkv, 128, 205)
@@ -378,7 +381,7 @@ def test_gqa_outlier_kv_full_size():
     q = synth.kv_queries(1, Hq, Hkv, 128, 202, law)
     ch = outlier_channels(law, Hkv)
     kcb, kc = codecs(ch, seeds=(203, 204))
-    vcb, vc = codecs(ch, mode="mse", seeds=(213, 214))
+    vcb, vc = codecs(ch, mode="mse", seeds=(213, 214), layout=vlayout)
     say("split K+V full layer: encode")
     kb, vb = tq.encode_kv(kcb, vcb, K.to(torch.bfloat16).to(DEV), V.to(torch.bfloat16).to(DEV))
     kb, vb = kb.cpu().numpy(), vb.cpu().numpy()
@@ -401,11 +404,12 @@ def test_gqa_outlier_kv_full_size():
     nvmax = max(max(float(np.max(e.o.nx.astype(np.float64))), float(np.max(e.r.nx.astype(np.float64))))
                 for e in ve)
     err = np.max(np.abs(out - ref)) / nvmax
-    say(f"split K+V full layer decode: max |out - ref| / max n_v = {err:.3g}")
+    say(f"split K+V full layer ({vlayout} values) decode: max |out - ref| / max n_v = {err:.3g}")
     assert err <= 1e-3
 
 
-def test_split_kv_decode_step():
+@pytest.mark.parametrize("vlayout", ["row", "col"])
+def test_split_kv_decode_step(vlayout):
     # append-on-decode with split keys and split values: each step writes the
     # new key and value into slot seq_lens[b] (split ROW records, tq_append)
     # and attends over seq_lens[b] + 1 tokens
@@ -416,7 +420,7 @@ def test_split_kv_decode_step():
     V = synth.kv_cache(B, H, cap, 128, 972, law)
     ch = outlier_channels(law, H, seed=980)
     kcb, kc = codecs(ch, seeds=(973, 974))
-    vcb, vc = codecs(ch, mode="mse", seeds=(976, 977))
+    vcb, vc = codecs(ch, mode="mse", seeds=(976, 977), layout=vlayout)
     kf = {(b, h): o.split_encode(kc, K[b, h].double().numpy(), head=h) for b in range(B) for h in range(H)}
     vf = {(b, h): o.split_encode(vc, V[b, h].double().numpy(), head=h) for b in range(B) for h in range(H)}
     kper, vper = kcb.records_bytes(cap), vcb.records_bytes(cap)
@@ -446,5 +450,25 @@ def test_split_kv_decode_step():
             err = max(err, float(np.max(np.abs(out[b] - ref))))
             nvmax = max(nvmax, max(max(float(np.max(e.o.nx.astype(np.float64))),
                                        float(np.max(e.r.nx.astype(np.float64)))) for e in vv))
-        say(f"split K+V decode step {s_}: max |out - ref| / max n_v = {err / nvmax:.3g}")
+        say(f"split K+V ({vlayout} values) decode step {s_}: max |out - ref| / max n_v = {err / nvmax:.3g}")
         assert err / nvmax <= 1e-3
+    # the value records now hold L0 + steps tokens each, as the oracle encodes them
+    vall = vr.cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            n = L0[b] + steps
+            got = o.split_unpack(vc, vall[(b * H + h) * vper:(b * H + h + 1) * vper], n)
+            check_split(vc, o.SplitEncoded(take(vf[b, h].o, n), take(vf[b, h].r, n)), got)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,lens,kbits,sk", [
+    (2, 8, 2, 700, [700, 129], (3, 2), True),     # split keys, several splits per sequence
+    (3, 4, 4, 300, [300, 0, 65], (3, 2), True),   # an empty sequence, group size 1
+    (1, 2, 1, 1000, [1000], (3, 3), False),       # 2-bit TurboQuant-prod keys, group size 2
+    (66, 4, 4, 129, [129] * 66, (3, 2), True),    # one split per sequence (4-wave form)
+    (1, 4, 1, 2500, [2500], (3, 2), True),        # 8-wave workgroups over 16-tile splits
+])
+def test_split_col_value_decode(B, Hq, Hkv, T, lens, kbits, sk):
+    # 2.5-bit split values in col records: the GPU encode of the records
+    # against the oracle, then the MFMA decode
+    _decode_split_values(B, Hq, Hkv, T, lens, kbits, (3, 2), sk, vlayout="col")
