@@ -249,8 +249,17 @@ def test_outlier_split_argument_errors():
         tq.Codebook(128, tq.TQ_PROD, 2, outlier_channels=np.r_[ch[:31], 128], outlier_bits=3, device=-1)
     with pytest.raises(tq.TQError):      # o must be 32, 64 or 96
         tq.Codebook(128, tq.TQ_PROD, 2, outlier_channels=ch[:16], outlier_bits=3, device=-1)
-    with pytest.raises(tq.TQError):      # col layout
-        tq.Codebook(128, tq.TQ_MSE, 2, outlier_channels=ch, outlier_bits=3, layout=tq.TQ_LAYOUT_COL, device=-1)
+    # col records: the 2.5-bit mse split only (32 channels at 3 index bits, the others at 2)
+    cb = tq.Codebook(128, tq.TQ_MSE, 2, outlier_channels=ch, outlier_bits=3, layout=tq.TQ_LAYOUT_COL, device=-1)
+    assert cb.tile_bytes == 2560  # 8 groups x 288 bytes of code words, two fp16 norms x 64
+    for kw in (dict(mode=tq.TQ_PROD, bits=3, outlier_bits=4), dict(mode=tq.TQ_MSE, bits=2, outlier_bits=4),
+               dict(mode=tq.TQ_MSE, bits=3, outlier_bits=3)):
+        with pytest.raises(tq.TQError):  # other col splits
+            tq.Codebook(128, kw["mode"], kw["bits"], outlier_channels=ch, outlier_bits=kw["outlier_bits"],
+                        layout=tq.TQ_LAYOUT_COL, device=-1)
+    with pytest.raises(tq.TQError):      # col split with 64 outlier channels
+        tq.Codebook(128, tq.TQ_MSE, 2, outlier_channels=np.arange(64) * 2, outlier_bits=3,
+                    layout=tq.TQ_LAYOUT_COL, device=-1)
     with pytest.raises(tq.TQError):      # d = 128 only
         tq.Codebook(256, tq.TQ_PROD, 2, outlier_channels=ch, outlier_bits=3, device=-1)
 
