@@ -672,6 +672,20 @@ __device__ __forceinline__ void encode_d128_body(const CodecView& cv, const Enco
           p1w[nb] = 0u;
         }
       }
+      // 2.5-bit split values (col records): the 7 outlier boundaries (3 index
+      // bits, stored dim 0) and the 3 regular ones (2 bits, stored dim 8),
+      // scaled to the accumulator by each group's factor, in registers
+      constexpr bool SCOL = SPLIT == 2 && COL && MODE == 0;
+      f32x16v Tso[NB], Tsr[NB];
+      if constexpr (SCOL) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int k = 0; k < 7; ++k) Tso[nb][k] = sThr[k] * wso_[nb];
+#pragma unroll
+          for (int k = 0; k < 3; ++k) Tsr[nb][k] = sThr[8 * kMaxLevels + k] * wsr_[nb];
+        }
+      }
 
       // ------------------------------------------------ rotation block
       // one accumulation chain per 32-vector block: Pi_hi x_hi, Pi_lo x_hi
@@ -748,6 +762,12 @@ __device__ __forceinline__ void encode_d128_body(const CodecView& cv, const Enco
                 cw[nb][0] = __builtin_amdgcn_alignbit(cw[nb][0], vb, 31);
                 chat = __uint_as_float(__float_as_uint(spl_c1) | (vb & 0x80000000u));
               }
+            } else if constexpr (SCOL) {
+              // idx = #{t_k <= y} by the register search of the coordinate's
+              // group (the same products t_k w as the general search below)
+              const bool og = 16 * hh + r < cv.o4;
+              const int io = quant_tree<3>(v, Tso[nb]), ir = quant_tree<2>(v, Tsr[nb]);
+              idx = og ? io : ir;
             } else if constexpr (SPLIT == 2) {
               // the coordinate's group codebook (boundaries +inf past its
               // levels), against the group's scale: idx = #{t_k <= y}
